@@ -1,0 +1,280 @@
+"""Plain CPU oracle for prefill-end KV-cache importance scoring and selection.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import or call this package. The library's
+own path never does, and shares no code with it (inputs come from the
+separate `synth` generator).
+
+Everything is float64 numpy, written as the plain definition: no blocking,
+fusion or reordering beyond what the definition states. Library primitives
+used as steps: matrix product, exp, sort.
+
+Sources (cited by page title and section):
+  [CriticalKV]  the sumin.im Korean translation of "CriticalKV: Optimizing
+                KV Cache Eviction from an Output Perturbation Perspective"
+  [KVzip]       the manon006.tistory.com review of "KVzip: Query-Agnostic KV
+                Cache Compression with Context Reconstruction"
+
+Readings taken where the pages are silent (each repeated where it is used):
+  scale     logits are scale * <q, k> with scale an argument (the model's
+            1/sqrt(d)); the pages print softmax(QK^T) with no scale.
+  causal    window query i (of W) sits at cache position n-W+i and sees
+            keys 0..n-W+i; external queries see all n keys.
+  sum       window scores sum (not average) over the W queries and the G
+            query heads of a KV head; the mean only rescales by 1/(W*G).
+  window    candidates are positions [0, n-W); the W window positions are
+            always kept and count toward the budget.
+  pool      max-pooling: kernel `pool`, stride 1, centred, over candidates
+            only; out-of-range neighbours are ignored.
+  weight    value weight of KV head h at position j:
+            mean over g of || W_O[:, slice(h*G+g)] v_j ||_1, in fp64.
+  key       two-stage key = (pooled * score_norm + eps) * weight, applied
+            after pooling; stage 1 takes floor(alpha*k) by pooled score.
+  ties      larger key first; equal keys go to the lower index (adaptive:
+            lower head, then lower position). Output positions ascending.
+  max mode  KVzip's max over queries, softmax over the n cached keys only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "window_raw_scores", "external_raw_scores", "maxpool", "value_weight",
+    "topk_indices", "select_layer", "compact_layer",
+]
+
+
+# --------------------------------------------------------------- scoring ----
+
+def _softmax_rows(logits: np.ndarray) -> np.ndarray:
+    """Row softmax; -inf entries (masked) get weight 0."""
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def window_raw_scores(q: np.ndarray, k: np.ndarray, G: int, scale: float,
+                      agg: str = "sum") -> np.ndarray:
+    """Observation-window attention scores of every cached key.
+
+    [CriticalKV, §3.3 Algorithm 2, steps 2-3]: Q_hat = the last n' queries,
+    A = softmax(Q_hat K^T), then aggregated over the window queries.
+    GQA grouping (query head h*G+g reads KV head h) follows [KVzip, §2.2].
+    Readings: causal window, explicit scale, sum over W and G (or max over
+    them when agg='max'; masked entries contribute nothing).
+
+    q: [H_kv*G][W][d], k: [H_kv][n][d] (float64). Returns raw [H_kv][n].
+    """
+    H, n, d = k.shape
+    Hq, W, _ = q.shape
+    assert Hq == H * G and 0 < W < n
+    pos = n - W + np.arange(W)                       # cache position of query i
+    visible = np.arange(n)[None, :] <= pos[:, None]  # causal mask [W][n]
+    raw = np.zeros((H, n))
+    for h in range(H):
+        for g in range(G):
+            logits = scale * (q[h * G + g] @ k[h].T)  # [W][n]
+            logits = np.where(visible, logits, -np.inf)
+            p = _softmax_rows(logits)
+            if agg == "sum":
+                raw[h] += p.sum(axis=0)
+            else:
+                raw[h] = np.maximum(raw[h], p.max(axis=0))
+    return raw
+
+
+def external_raw_scores(q: np.ndarray, k: np.ndarray, G: int, scale: float,
+                        agg: str = "max", q_chunk: int = 512) -> np.ndarray:
+    """Scores from queries outside the cache (KVzip's reconstruction queries).
+
+    [KVzip, §3.2]: A = Softmax(Q K^T) for the G x n_in group queries, then
+    S = max over g and i of the slice of A on the cached keys. Reading: the
+    softmax runs over the n cached keys only (synthetic queries have no
+    self-keys). agg='sum' sums over g and i instead. Queries are processed
+    q_chunk at a time ([KVzip, §3.4] processes the input in chunks); max and
+    sum over queries do not depend on the chunking.
+
+    q: [H_kv*G][Q_s][d], k: [H_kv][n][d]. Returns raw [H_kv][n].
+    """
+    H, n, d = k.shape
+    Hq, Qs, _ = q.shape
+    assert Hq == H * G
+    raw = np.zeros((H, n))
+    for h in range(H):
+        for g in range(G):
+            for c0 in range(0, Qs, q_chunk):
+                p = _softmax_rows(scale * (q[h * G + g, c0:c0 + q_chunk] @ k[h].T))
+                if agg == "max":
+                    raw[h] = np.maximum(raw[h], p.max(axis=0))
+                else:
+                    raw[h] += p.sum(axis=0)
+    return raw
+
+
+def maxpool(raw: np.ndarray, n_cand: int, pool: int) -> np.ndarray:
+    """[CriticalKV, §3.3 Algorithm 2, step 4] (SnapKV's max-pooling, kernel 7
+    in [CriticalKV, §4.1]). Reading: stride 1, centred, over candidate
+    positions [0, n_cand) only; neighbours outside that range are ignored.
+
+    raw: [..., n] with n >= n_cand. Returns pooled [..., n_cand].
+    """
+    assert pool >= 1 and pool % 2 == 1
+    r = pool // 2
+    src = raw[..., :n_cand]
+    out = src.copy()
+    for off in range(1, r + 1):
+        if off >= n_cand:
+            break
+        out[..., off:] = np.maximum(out[..., off:], src[..., :n_cand - off])
+        out[..., :n_cand - off] = np.maximum(out[..., :n_cand - off], src[..., off:])
+    return out
+
+
+# ---------------------------------------------------------- value weight ----
+
+def value_weight(v: np.ndarray, w_o: np.ndarray, G: int,
+                 positions: np.ndarray | None = None) -> np.ndarray:
+    """CriticalKV's projected-value norm.
+
+    [CriticalKV, §3.3 Algorithm 1, steps 2-3]: V_proj = V W^O and the L1 norm
+    of each row of V_proj (Theorem 3.3 bounds the output perturbation by
+    attention weight times this norm; the L1 distance is the paper's choice,
+    footnote 1 and §C.3). Reading under GQA: query head hq = h*G+g projects
+    KV head h's values through its own d columns of W_O, and the weight of
+    KV head h is the mean over its G query heads.
+
+    v: [H_kv][n][d], w_o: [D][H_kv*G*d] (torch Linear layout).
+    positions: optional subset of positions. Returns [H_kv][len(positions)].
+    """
+    H, n, d = v.shape
+    if positions is None:
+        positions = np.arange(n)
+    out = np.zeros((H, len(positions)))
+    for h in range(H):
+        vh = v[h, positions]                           # [m][d]
+        for g in range(G):
+            hq = h * G + g
+            w_slice = w_o[:, hq * d:(hq + 1) * d]      # [D][d]
+            proj = vh @ w_slice.T                      # [m][D] rows of V W^O
+            out[h] += np.abs(proj).sum(axis=1)
+        out[h] /= G
+    return out
+
+
+# -------------------------------------------------------------- selection ----
+
+def topk_indices(key: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest entries, equal keys to the lower index,
+    returned ascending. ([CriticalKV, §3.3] Top_k; tie rule is a reading.)"""
+    order = np.lexsort((np.arange(key.shape[0]), -key))
+    return np.sort(order[:k])
+
+
+def _stage_key(score, weight, score_norm, eps, dtype):
+    """Integrated score (A*score_norm + eps) * weight, in `dtype`.
+
+    [CriticalKV, §3.3 Algorithm 1, step 3 and footnote 3 (eps = 1E-4)].
+    With dtype float32 each operation rounds once, in this order:
+    mul, add, mul (the precision a float32 kernel decides in)."""
+    if dtype == np.float32:
+        s = np.asarray(score, np.float32)
+        t = s * np.float32(score_norm)
+        t = t + np.float32(eps)
+        return t * np.asarray(weight, np.float32)
+    return (np.asarray(score, np.float64) * score_norm + eps) * np.asarray(weight, np.float64)
+
+
+def _two_stage(score, weight, k, alpha, score_norm, eps, dtype):
+    """[CriticalKV, §3.3 Algorithm 1, steps 4-9]: b' = floor(alpha*b) picked by
+    attention score (stage 1); the remaining b - b' picked among the rest by
+    the integrated score (stage 2). Returns (ascending indices, stage 1|2)."""
+    k1 = int(np.floor(alpha * k))
+    s1 = topk_indices(score, k1)
+    rest = np.ones(score.shape[0], dtype=bool)
+    rest[s1] = False
+    cand = np.nonzero(rest)[0]
+    key = _stage_key(score, weight, score_norm, eps, dtype)
+    s2 = cand[topk_indices(key[cand], k - k1)]
+    idx = np.concatenate([s1, s2])
+    stage = np.concatenate([np.ones(len(s1), np.uint8), np.full(len(s2), 2, np.uint8)])
+    o = np.argsort(idx, kind="stable")
+    return idx[o], stage[o]
+
+
+def select_layer(scores: np.ndarray, budget: int, W: int, n: int,
+                 adaptive: bool = False, weight: np.ndarray | None = None,
+                 alpha: float = 0.5, score_norm: float = 1.0, eps: float = 1e-4,
+                 dtype=np.float64):
+    """Kept positions of one layer.
+
+    scores: pooled [H][n_cand] (n_cand = n - W). weight: optional [H][n_cand].
+    budget: kept entries incl. the W window positions, per head, or per layer
+    when adaptive (reading: the window counts toward the budget, so
+    k = budget - W per head, or budget - H*W per layer).
+    adaptive: one top-k over all heads' candidates of the layer — the
+    non-uniform head budget of [KVzip, §4.2] / AdaKV in [CriticalKV, §3.3
+    Algorithm 2, step 1], ties by (head, position).
+    weight given: CriticalKV two-stage selection [CriticalKV, Algorithm 1].
+
+    Returns (idx, head_offsets, stage): uniform -> idx [H][budget],
+    head_offsets None; adaptive -> idx [budget] packed by head and
+    head_offsets [H+1]. Per head: candidates ascending, then the window
+    n-W..n-1. stage: 0 window, 1 stage 1 / single stage, 2 stage 2.
+    """
+    H, n_cand = scores.shape
+    assert n_cand == n - W
+    window = np.arange(n - W, n)
+    if not adaptive:
+        k = budget - W
+        assert 0 <= k <= n_cand
+        idx = np.empty((H, budget), np.int64)
+        stage = np.empty((H, budget), np.uint8)
+        for h in range(H):
+            if weight is None:
+                pick, st = topk_indices(scores[h], k), None
+                st = np.ones(k, np.uint8)
+            else:
+                pick, st = _two_stage(scores[h], weight[h], k, alpha, score_norm, eps, dtype)
+            idx[h] = np.concatenate([pick, window])
+            stage[h] = np.concatenate([st, np.zeros(W, np.uint8)])
+        return idx, None, stage
+    k = budget - H * W
+    assert 0 <= k <= H * n_cand
+    flat = scores.reshape(-1)
+    if weight is None:
+        pick = topk_indices(flat, k)
+        st = np.ones(k, np.uint8)
+    else:
+        pick, st = _two_stage(flat, weight.reshape(-1), k, alpha, score_norm, eps, dtype)
+    heads, pos = np.divmod(pick, n_cand)
+    idx_parts, st_parts, offs = [], [], [0]
+    for h in range(H):
+        sel = heads == h
+        idx_parts += [pos[sel], window]
+        st_parts += [st[sel], np.zeros(W, np.uint8)]
+        offs.append(offs[-1] + int(sel.sum()) + W)
+    return np.concatenate(idx_parts), np.asarray(offs, np.int64), np.concatenate(st_parts)
+
+
+# -------------------------------------------------------------- compaction ----
+
+def compact_layer(k: np.ndarray, v: np.ndarray, idx: np.ndarray,
+                  head_offsets: np.ndarray | None = None):
+    """Gather the kept rows from the un-replicated KV cache.
+
+    [KVzip, §4.2]: eviction acts on the original cache before GQA
+    replication, so the kept rows of KV head h come from k[h], v[h].
+    Bit copies: works on any dtype (bf16 bit patterns included).
+    Uniform: idx [H][B] -> [H][B][d]; packed: idx [B_layer] with
+    head_offsets [H+1] -> [B_layer][d].
+    """
+    if head_offsets is None:
+        H = k.shape[0]
+        return (np.stack([k[h, idx[h]] for h in range(H)]),
+                np.stack([v[h, idx[h]] for h in range(H)]))
+    ko, vo = [], []
+    for h in range(len(head_offsets) - 1):
+        sl = idx[head_offsets[h]:head_offsets[h + 1]]
+        ko.append(k[h, sl])
+        vo.append(v[h, sl])
+    return np.concatenate(ko), np.concatenate(vo)

@@ -1,0 +1,399 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each check takes an oracle module `o` and raises AssertionError (or any
+exception) when the oracle disagrees with:
+  - brute force: explicit Python loops over tiny inputs (full causal n x n
+    attention, triple-loop projections, pairwise top-k conditions);
+  - closed forms and hand-worked examples (tests/golden/*.txt, each with its
+    derivation and citation);
+  - special cases that reduce to a library routine (scipy softmax,
+    torch max_pool1d, torch index_select);
+  - invariants (scores of a head sum to W*G, max-mode scores in [1/n, 1]).
+The mutation tests run the same checks against copies of the oracle with a
+planted mistake and require each copy to fail at least one check.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_golden(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = (s.strip() for s in line.split("=", 1))
+            out[key] = [float(x) for x in val.split()]
+    return out
+
+
+def _embed_1d(vals, d=4):
+    """d=1 vectors embedded as (x, 0, ..., 0) in d dims."""
+    a = np.zeros((len(vals), d))
+    a[:, 0] = vals
+    return a
+
+
+# ------------------------------------------------------- window scoring ----
+
+def _bruteforce_window(q, k, G, scale, extra_queries):
+    """Full causal attention over all n positions with explicit loops; keeps
+    the last W rows and sums them per KV head."""
+    H, n, d = k.shape
+    Hq, W, _ = q.shape
+    raw = [[0.0] * n for _ in range(H)]
+    for hq in range(Hq):
+        h = hq // G
+        # queries for every position: earlier ones arbitrary, last W = window
+        qfull = [list(extra_queries[hq][p]) for p in range(n - W)] + \
+                [list(q[hq][i]) for i in range(W)]
+        for p in range(n):
+            logits = []
+            for j in range(p + 1):
+                s = 0.0
+                for e in range(d):
+                    s += qfull[p][e] * k[h][j][e]
+                logits.append(scale * s)
+            mx = max(logits)
+            z = sum(math.exp(x - mx) for x in logits)
+            if p >= n - W:
+                for j in range(p + 1):
+                    raw[h][j] += math.exp(logits[j] - mx) / z
+    return np.array(raw)
+
+
+def check_window_bruteforce(o):
+    rng = np.random.default_rng(11)
+    for (H, G, d, n, W) in [(2, 3, 3, 7, 2), (1, 1, 2, 5, 1), (2, 2, 4, 9, 4), (3, 2, 3, 6, 5)]:
+        q = rng.standard_normal((H * G, W, d)) * 1.5
+        k = rng.standard_normal((H, n, d)) * 1.5
+        extra = rng.standard_normal((H * G, n, d))
+        scale = 0.7
+        ref = _bruteforce_window(q, k, G, scale, extra)
+        got = o.window_raw_scores(q, k, G, scale)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def check_window_sum_invariant(o):
+    rng = np.random.default_rng(12)
+    H, G, d, n, W = 3, 4, 16, 300, 32
+    q = rng.standard_normal((H * G, W, d))
+    k = rng.standard_normal((H, n, d)) * rng.uniform(0.5, 4, size=(H, n, 1))
+    raw = o.window_raw_scores(q, k, G, 1 / math.sqrt(d))
+    np.testing.assert_allclose(raw.sum(axis=1), W * G, rtol=1e-12)
+    assert (raw >= 0).all()
+
+
+def check_window_equal_keys(o):
+    g = load_golden("window_equal_keys.txt")
+    n, W, G = int(g["n"][0]), int(g["W"][0]), int(g["G"][0])
+    rng = np.random.default_rng(13)
+    d = 8
+    q = rng.standard_normal((G, W, d))
+    k = np.tile(rng.standard_normal(d), (1, n, 1))
+    raw = o.window_raw_scores(q, k, G, 0.3)[0]
+    np.testing.assert_allclose(raw, g["raw"], rtol=1e-12)
+    # general (n, W, G) against exact harmonic sums
+    for (n, W, G) in [(40, 7, 3), (17, 16, 1), (64, 32, 4)]:
+        q = rng.standard_normal((2 * G, W, d))
+        k = np.tile(rng.standard_normal(d), (2, n, 1))
+        raw = o.window_raw_scores(q, k, G, 0.25)
+        pre = G * sum(Fraction(1, n - W + i + 1) for i in range(W))
+        win = [G * sum(Fraction(1, n - W + i + 1) for i in range(t, W)) for t in range(W)]
+        exp = np.array([float(pre)] * (n - W) + [float(x) for x in win])
+        for h in range(2):
+            np.testing.assert_allclose(raw[h], exp, rtol=1e-12)
+
+
+def check_window_hand_example(o):
+    g = load_golden("window_hand_example.txt")
+    q = _embed_1d(g["q"])[None]              # [1][W=2][d]
+    k = _embed_1d(g["k"])[None]              # [1][n=4][d]
+    raw = o.window_raw_scores(q, k, 1, 1.0)[0]
+    np.testing.assert_allclose(raw, g["raw"], rtol=1e-12)
+    # the same closed form written out here
+    e = math.e
+    z2, z3 = 2 + e, 2 + 2 * e
+    np.testing.assert_allclose(raw, [1 / z2 + 1 / z3, e / z2 + e / z3, 1 / z2 + 1 / z3, e / z3],
+                               rtol=1e-13)
+
+
+def check_window_single_query_softmax(o):
+    """W = 1, G = 1: the last query sees every key -> one softmax row."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(14)
+    for n, d, scale in [(50, 8, 0.35), (257, 16, 1.0)]:
+        q = rng.standard_normal((1, 1, d))
+        k = rng.standard_normal((1, n, d))
+        raw = o.window_raw_scores(q, k, 1, scale)[0]
+        np.testing.assert_allclose(raw, softmax(scale * (k[0] @ q[0, 0])), rtol=1e-12)
+
+
+def check_window_max_agg(o):
+    rng = np.random.default_rng(15)
+    H, G, d, n, W = 2, 2, 3, 8, 3
+    q = rng.standard_normal((H * G, W, d))
+    k = rng.standard_normal((H, n, d))
+    scale = 0.8
+    got = o.window_raw_scores(q, k, G, scale, agg="max")
+    ref = np.zeros((H, n))
+    for hq in range(H * G):
+        h = hq // G
+        for i in range(W):
+            p = n - W + i
+            lg = [scale * sum(q[hq, i, e] * k[h, j, e] for e in range(d)) for j in range(p + 1)]
+            mx = max(lg)
+            z = sum(math.exp(x - mx) for x in lg)
+            for j in range(p + 1):
+                ref[h, j] = max(ref[h, j], math.exp(lg[j] - mx) / z)
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
+
+
+# ----------------------------------------------------- external scoring ----
+
+def check_external(o):
+    from scipy.special import softmax
+    g = load_golden("external_hand_example.txt")
+    q = _embed_1d(g["q"])[None]
+    k = _embed_1d(g["k"])[None]
+    raw = o.external_raw_scores(q, k, 1, 1.0, agg="max")[0]
+    np.testing.assert_allclose(raw, g["raw"], rtol=1e-12)
+    rng = np.random.default_rng(16)
+    # one query, G = 1 -> one softmax row over all n keys
+    n, d = 77, 8
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, n, d))
+    np.testing.assert_allclose(o.external_raw_scores(q, k, 1, 0.5)[0],
+                               softmax(0.5 * (k[0] @ q[0, 0])), rtol=1e-12)
+    # brute force (loops), ranges, and chunk independence
+    H, G, Qs, n, d = 2, 3, 5, 9, 3
+    q = rng.standard_normal((H * G, Qs, d)) * 2
+    k = rng.standard_normal((H, n, d)) * 2
+    scale = 0.6
+    ref = np.zeros((H, n))
+    refsum = np.zeros((H, n))
+    for hq in range(H * G):
+        h = hq // G
+        for i in range(Qs):
+            lg = [scale * sum(q[hq, i, e] * k[h, j, e] for e in range(d)) for j in range(n)]
+            mx = max(lg)
+            z = sum(math.exp(x - mx) for x in lg)
+            for j in range(n):
+                pj = math.exp(lg[j] - mx) / z
+                ref[h, j] = max(ref[h, j], pj)
+                refsum[h, j] += pj
+    for ch in (1, 2, 512):
+        np.testing.assert_allclose(o.external_raw_scores(q, k, G, scale, "max", ch), ref, rtol=1e-12)
+    np.testing.assert_allclose(o.external_raw_scores(q, k, G, scale, "sum", 2), refsum, rtol=1e-12)
+    np.testing.assert_allclose(refsum.sum(axis=1), G * Qs, rtol=1e-12)
+    big = o.external_raw_scores(rng.standard_normal((4, 64, 16)), rng.standard_normal((2, 300, 16)), 2, 0.25)
+    assert (big <= 1 + 1e-15).all() and (big.max(axis=1) >= 1 / 300).all()
+
+
+# ---------------------------------------------------------------- pool ----
+
+def check_maxpool(o):
+    import torch
+    rng = np.random.default_rng(17)
+    raw = rng.random((3, 103))
+    for pool in (1, 3, 7, 9):
+        for n_cand in (103, 96, 5, 1):
+            got = o.maxpool(raw, n_cand, pool)
+            t = torch.from_numpy(raw[:, :n_cand].copy())[:, None, :]
+            ref = torch.nn.functional.max_pool1d(t, pool, stride=1, padding=pool // 2)[:, 0, :].numpy()
+            np.testing.assert_array_equal(got, ref)
+            assert (got >= raw[:, :n_cand]).all()
+    np.testing.assert_array_equal(o.maxpool(raw, 50, 1), raw[:, :50])
+    # hand example: a single spike spreads 3 positions each way, clipped
+    x = np.zeros((1, 12))
+    x[0, 1] = 5.0
+    np.testing.assert_array_equal(o.maxpool(x, 10, 7)[0], [5, 5, 5, 5, 5, 0, 0, 0, 0, 0])
+
+
+# -------------------------------------------------------- value weight ----
+
+def check_value_weight(o):
+    rng = np.random.default_rng(18)
+    # brute force with explicit loops
+    H, G, d, n, D = 2, 3, 3, 5, 4
+    v = rng.standard_normal((H, n, d))
+    w_o = rng.standard_normal((D, H * G * d))
+    ref = np.zeros((H, n))
+    for h in range(H):
+        for j in range(n):
+            tot = 0.0
+            for g in range(G):
+                for c in range(D):
+                    s = 0.0
+                    for e in range(d):
+                        s += w_o[c, (h * G + g) * d + e] * v[h, j, e]
+                    tot += abs(s)
+            ref[h, j] = tot / G
+    np.testing.assert_allclose(o.value_weight(v, w_o, G), ref, rtol=1e-12)
+    pos = np.array([4, 0, 2])
+    np.testing.assert_allclose(o.value_weight(v, w_o, G, pos), ref[:, pos], rtol=1e-12)
+    # identity slices -> plain L1 norm of v
+    H, G, d, n = 2, 2, 6, 11
+    D = 2 * d
+    v = rng.standard_normal((H, n, d))
+    w_o = np.zeros((D, H * G * d))
+    for hq in range(H * G):
+        w_o[:d, hq * d:(hq + 1) * d] = np.eye(d)
+    np.testing.assert_allclose(o.value_weight(v, w_o, G), np.abs(v).sum(axis=2), rtol=1e-12)
+    # homogeneity and linearity in |c|
+    w_o = rng.standard_normal((D, H * G * d))
+    base = o.value_weight(v, w_o, G)
+    np.testing.assert_allclose(o.value_weight(-2.5 * v, w_o, G), 2.5 * base, rtol=1e-12)
+    # only the group's own columns matter: zero them for head 1, head 0 unchanged
+    w2 = w_o.copy()
+    w2[:, G * d:] = 0
+    got = o.value_weight(v, w2, G)
+    np.testing.assert_allclose(got[0], base[0], rtol=1e-12)
+    np.testing.assert_array_equal(got[1], 0)
+    # rank-one slice u e_0^T -> ||u||_1 |v_0|, averaged over the group
+    w3 = np.zeros((D, H * G * d))
+    u = rng.standard_normal((H * G, D))
+    for hq in range(H * G):
+        w3[:, hq * d] = u[hq]
+    exp = np.stack([np.mean([np.abs(u[h * G + g]).sum() for g in range(G)]) * np.abs(v[h, :, 0])
+                    for h in range(H)])
+    np.testing.assert_allclose(o.value_weight(v, w3, G), exp, rtol=1e-12)
+
+
+# ----------------------------------------------------------- selection ----
+
+def _assert_topk_property(key, picked, k):
+    """Every picked entry beats every unpicked one: larger key, or equal key
+    and lower index. Checked pairwise with loops."""
+    picked = list(picked)
+    assert len(picked) == k and len(set(picked)) == k
+    ps = set(picked)
+    for i in picked:
+        for j in range(len(key)):
+            if j in ps:
+                continue
+            assert key[i] > key[j] or (key[i] == key[j] and i < j), (i, j)
+
+
+def check_select_examples(o):
+    g = load_golden("select_examples.txt")
+    ties_pooled = np.array([g["ties.pooled"]])
+    idx, _, st = o.select_layer(ties_pooled, int(g["ties.budget"][0]), int(g["ties.W"][0]),
+                                int(g["ties.n"][0]))
+    np.testing.assert_array_equal(idx[0], g["ties.kept"])
+    for name in ("two_stage", "odd_k", "eps"):
+        idx, _, st = o.select_layer(np.array([g[name + ".pooled"]]), int(g[name + ".budget"][0]),
+                                    int(g[name + ".W"][0]), int(g[name + ".n"][0]),
+                                    weight=np.array([g[name + ".weight"]]),
+                                    alpha=g[name + ".alpha"][0], score_norm=1.0,
+                                    eps=g[name + ".eps"][0])
+        np.testing.assert_array_equal(idx[0], g[name + ".kept"], err_msg=name)
+        np.testing.assert_array_equal(st[0], g[name + ".stage"], err_msg=name)
+
+
+def check_select_bruteforce(o):
+    rng = np.random.default_rng(19)
+    for trial in range(20):
+        H, n, W = 3, 40, 4
+        n_cand = n - W
+        # few distinct values -> many ties
+        scores = rng.integers(0, 6, size=(H, n_cand)).astype(np.float64)
+        budget = int(rng.integers(W, n + 1))
+        idx, _, st = o.select_layer(scores, budget, W, n)
+        for h in range(H):
+            row = list(idx[h])
+            assert row == sorted(row)
+            assert row[-W:] == list(range(n - W, n))
+            _assert_topk_property(scores[h], row[:budget - W], budget - W)
+            assert (st[h][-W:] == 0).all() and (st[h][:budget - W] == 1).all()
+        # adaptive: one flattened top-k, ties by (head, position)
+        budget = int(rng.integers(H * W, H * n + 1))
+        idx, offs, st = o.select_layer(scores, budget, W, n, adaptive=True)
+        assert offs[0] == 0 and offs[-1] == budget == len(idx)
+        flat_pick = []
+        for h in range(H):
+            seg = list(idx[offs[h]:offs[h + 1]])
+            assert seg == sorted(seg) and seg[-W:] == list(range(n - W, n))
+            flat_pick += [h * n_cand + p for p in seg[:-W]]
+        _assert_topk_property(scores.reshape(-1), flat_pick, budget - H * W)
+        # two-stage: stage-1 set is a top-k1 by score; stage-2 set a top-k2
+        # of the rest by (score*norm + eps)*w
+        w = rng.integers(0, 4, size=(H, n_cand)).astype(np.float64)
+        budget = int(rng.integers(W, n + 1))
+        alpha = float(rng.choice([0.0, 0.25, 0.5, 1.0]))
+        idx, _, st = o.select_layer(scores, budget, W, n, weight=w, alpha=alpha,
+                                    score_norm=0.5, eps=0.01)
+        k = budget - W
+        k1 = int(math.floor(alpha * k))
+        for h in range(H):
+            s1 = [int(i) for i, s in zip(idx[h], st[h]) if s == 1]
+            s2 = [int(i) for i, s in zip(idx[h], st[h]) if s == 2]
+            _assert_topk_property(scores[h], s1, k1)
+            rest = [j for j in range(n_cand) if j not in set(s1)]
+            key = (scores[h] * 0.5 + 0.01) * w[h]
+            sub = np.array([key[j] for j in rest])
+            _assert_topk_property(sub, [rest.index(j) for j in s2], k - k1)
+
+
+def check_select_reductions(o):
+    rng = np.random.default_rng(20)
+    H, n, W = 4, 64, 8
+    scores = rng.random((H, n - W))
+    w = rng.random((H, n - W)) + 0.1
+    budget = 30
+    plain, _, _ = o.select_layer(scores, budget, W, n)
+    # alpha = 1: two-stage collapses to plain top-k by score
+    a1, _, _ = o.select_layer(scores, budget, W, n, weight=w, alpha=1.0)
+    np.testing.assert_array_equal(a1, plain)
+    # alpha = 0, eps = 0, weight = 1, norm = 1: top-k by score again
+    a0, _, _ = o.select_layer(scores, budget, W, n, weight=np.ones_like(w), alpha=0.0,
+                              eps=0.0, score_norm=1.0)
+    np.testing.assert_array_equal(a0, plain)
+    # adaptive with identical heads and k divisible by H -> per-head k/H
+    same = np.tile(rng.random(n - W), (H, 1))
+    per_head, _, _ = o.select_layer(same, W + 5, W, n)
+    ada, offs, _ = o.select_layer(same, H * (W + 5), W, n, adaptive=True)
+    np.testing.assert_array_equal(ada, per_head.reshape(-1))
+    np.testing.assert_array_equal(offs, np.arange(H + 1) * (W + 5))
+    # budget = W keeps only the window; budget = n keeps everything
+    only_w, _, _ = o.select_layer(scores, W, W, n)
+    np.testing.assert_array_equal(only_w, np.tile(np.arange(n - W, n), (H, 1)))
+    full, _, _ = o.select_layer(scores, n, W, n)
+    np.testing.assert_array_equal(full, np.tile(np.arange(n), (H, 1)))
+
+
+# ----------------------------------------------------------- compaction ----
+
+def check_compact(o):
+    import torch
+    rng = np.random.default_rng(21)
+    H, n, d, B = 3, 50, 8, 7
+    k = rng.integers(0, 65535, size=(H, n, d)).astype(np.uint16)
+    v = rng.integers(0, 65535, size=(H, n, d)).astype(np.uint16)
+    idx = np.stack([np.sort(rng.choice(n, B, replace=False)) for _ in range(H)])
+    ko, vo = o.compact_layer(k, v, idx)
+    for h in range(H):
+        ti = torch.from_numpy(idx[h])
+        np.testing.assert_array_equal(ko[h], torch.index_select(torch.from_numpy(k[h].astype(np.int32)), 0, ti).numpy())
+        np.testing.assert_array_equal(vo[h], torch.index_select(torch.from_numpy(v[h].astype(np.int32)), 0, ti).numpy())
+    offs = np.array([0, 2, 2, 9])
+    flat = np.concatenate([idx[0][:2], idx[2]])
+    ko, vo = o.compact_layer(k, v, flat, offs)
+    np.testing.assert_array_equal(ko, np.concatenate([k[0, idx[0][:2]], k[2, idx[2]]]))
+    np.testing.assert_array_equal(vo, np.concatenate([v[0, idx[0][:2]], v[2, idx[2]]]))
+
+
+ALL_CHECKS = [
+    check_window_bruteforce, check_window_sum_invariant, check_window_equal_keys,
+    check_window_hand_example, check_window_single_query_softmax, check_window_max_agg,
+    check_external, check_maxpool, check_value_weight, check_select_examples,
+    check_select_bruteforce, check_select_reductions, check_compact,
+]

@@ -1,0 +1,62 @@
+"""Plant plausible mistakes in copies of the oracle and require the pins to
+catch every one of them. CPU only; the real oracle is never modified."""
+import importlib.util
+import os
+import sys
+
+import pytest
+
+from oracle_pins import ALL_CHECKS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "__init__.py")
+
+MUTANTS = {
+    "causal_off_by_one": ("pos = n - W + np.arange(W)", "pos = n - W - 1 + np.arange(W)"),
+    "causal_off_by_one_late": ("pos = n - W + np.arange(W)", "pos = n - W + 1 + np.minimum(np.arange(W), W - 2)"),
+    "non_causal": ("logits = np.where(visible, logits, -np.inf)", "logits = logits"),
+    "no_scale": ("logits = scale * (q[h * G + g] @ k[h].T)", "logits = (q[h * G + g] @ k[h].T)"),
+    "gqa_interleaved": ("logits = scale * (q[h * G + g] @ k[h].T)", "logits = scale * (q[g * H + h] @ k[h].T)"),
+    "softmax_wrong_axis": ("m = logits.max(axis=1, keepdims=True)\n    e = np.exp(logits - m)\n    return e / e.sum(axis=1, keepdims=True)",
+                           "m = logits.max(axis=0, keepdims=True)\n    e = np.exp(logits - m)\n    return e / e.sum(axis=0, keepdims=True)"),
+    "mean_instead_of_sum": ("raw[h] += p.sum(axis=0)\n            else:", "raw[h] += p.mean(axis=0)\n            else:"),
+    "external_sum_for_max": ("                if agg == \"max\":", "                if agg == \"sum\":"),
+    "external_causal": ("p = _softmax_rows(scale * (q[h * G + g, c0:c0 + q_chunk] @ k[h].T))",
+                        "p = _softmax_rows(np.where(np.tri(min(q_chunk, Qs - c0), n, n - min(q_chunk, Qs - c0), bool), scale * (q[h * G + g, c0:c0 + q_chunk] @ k[h].T), -np.inf))"),
+    "pool_radius": ("r = pool // 2\n", "r = max(pool // 2 - 1, 0)\n"),
+    "pool_one_sided": ("out[..., :n_cand - off] = np.maximum(out[..., :n_cand - off], src[..., off:])", "pass"),
+    "pool_over_all_n": ("src = raw[..., :n_cand]\n    out = src.copy()", "src = raw\n    out = src.copy()[..., :n_cand]"),
+    "weight_no_abs": ("out[h] += np.abs(proj).sum(axis=1)", "out[h] += proj.sum(axis=1)"),
+    "weight_l2": ("out[h] += np.abs(proj).sum(axis=1)", "out[h] += np.sqrt((proj ** 2).sum(axis=1))"),
+    "weight_no_mean": ("out[h] /= G", "out[h] /= 1"),
+    "weight_wrong_slice": ("w_slice = w_o[:, hq * d:(hq + 1) * d]", "w_slice = w_o[:, h * d:(h + 1) * d]"),
+    "ties_to_higher_index": ("order = np.lexsort((np.arange(key.shape[0]), -key))", "order = np.lexsort((-np.arange(key.shape[0]), -key))"),
+    "k1_ceil": ("k1 = int(np.floor(alpha * k))", "k1 = int(np.ceil(alpha * k))"),
+    "no_eps_f64": ("(np.asarray(score, np.float64) * score_norm + eps)", "(np.asarray(score, np.float64) * score_norm)"),
+    "stage2_from_all": ("cand = np.nonzero(rest)[0]", "cand = np.arange(score.shape[0])"),
+    "adaptive_transposed": ("flat = scores.reshape(-1)", "flat = scores.T.reshape(-1)"),
+    "window_not_counted": ("        k = budget - W\n        assert 0 <= k <= n_cand", "        k = max(budget - 2 * W, 0)\n        assert 0 <= k <= n_cand"),
+    "compact_wrong_head": ("return (np.stack([k[h, idx[h]] for h in range(H)]),", "return (np.stack([k[0, idx[h]] for h in range(H)]),"),
+}
+
+
+def _load_mutant(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} must occur exactly once"
+    mod_name = f"oracle_mutant_{name}"
+    spec = importlib.util.spec_from_loader(mod_name, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src.replace(old, new), f"<{mod_name}>", "exec"), mod.__dict__)
+    sys.modules.pop(mod_name, None)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mod = _load_mutant(name, *MUTANTS[name])
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:
+            failed.append(check.__name__)
+    assert failed, f"no pin caught the planted mistake '{name}'"
