@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the prefill-end KV-cache scoring -> selection -> compaction
+path on one MI355X.
+
+One step = the whole hot path over one synthetic cache, all layers at once:
+kvsel_score (window attention scores + max-pool), kvsel_value_weight (only
+for the value-weighted workload), kvsel_select and kvsel_compact. Inputs are
+seeded synthetic bf16 tensors from `synth`, resident in HBM before timing.
+
+Prints ONE JSON line. `value` = KV entries (KV head x cached token) scored,
+selected and compacted per second over the whole step, which equals the
+per-layer rate (n*H_kv per layer / time per layer). `roofline` is for the
+dominant kernel (the scoring call), timed with HIP events on the stream it
+runs on, over the timed steps. `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+METRIC = "KV entries scored+selected/sec per layer at n=32K; % of HBM roofline"
+SCORE_SOURCES = ["score_dispatch.hip", "score_twopass.hip", "kvsel_internal.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "eviction_importance_scoring_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(key, sha):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(key)
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def cpu_baseline(wl, host, seconds):
+    """Oracle (fp64 numpy) on whole layers of the same inputs, one after the
+    other, until `seconds` of CPU work; reported in entries/s."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    done = 0
+    t0 = time.perf_counter()
+    for l in range(wl.L):
+        q = synth.bf16_to_f64(host["q"][l])
+        k = synth.bf16_to_f64(host["k"][l])
+        if wl.q_mode == "window":
+            raw = oracle.window_raw_scores(q, k, wl.G, wl.scale, wl.agg)
+        else:
+            raw = oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg)
+        pooled = oracle.maxpool(raw, wl.n_cand, wl.pool)
+        oracle.select_layer(pooled, wl.budget, wl.W_kept, wl.n, adaptive=wl.adaptive)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done * wl.H_kv * wl.n / dt, "unit": "entries/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {wl.L} layers of {wl.name}: window scores, max-pool and "
+                      f"top-k selection in fp64 numpy ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_n32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "bench.py measures one GPU only: the scoring path shards "
+                                   "by layer / KV head with no communication, and this build "
+                                   "runs and reports a single GPU",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import eviction_importance_scoring_amd as kv
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {wl.name} (seed {args.seed})")
+    which = ("q", "k", "v", "w_o") if wl.value_weight else ("q", "k", "v")
+    t0 = time.time()
+    host = synth.gen_all(wl, args.seed, which)
+    log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
+
+    def up(u):
+        return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t = {name: up(a) for name, a in host.items()}
+    q, k, v = t["q"], t["k"], t["v"]
+    w_o = t.get("w_o")
+    mode = kv.Q_WINDOW if wl.q_mode == "window" else kv.Q_EXTERNAL
+    agg = kv.AGG_SUM if wl.agg == "sum" else kv.AGG_MAX
+    W_kept = wl.W_kept
+    scores = torch.empty((wl.L, wl.H_kv, wl.n_cand), dtype=torch.float32, device=dev)
+    weight = (torch.empty((wl.L, wl.H_kv, wl.n_cand), dtype=torch.float32, device=dev)
+              if wl.value_weight else None)
+    ws_s = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    _, _ = kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
+                          scores=scores)  # sizes the workspace once
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record()
+        kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
+                       scores=scores)
+        if marks is not None:
+            marks[1].record()
+        if weight is not None:
+            kv.kvsel_value_weight(v, w_o, G=wl.G, n_cand=wl.n_cand, weight=weight)
+        if marks is not None:
+            marks[2].record()
+        idx, offs, _ = kv.kvsel_select(scores, n=wl.n, W=W_kept, budget=wl.budget,
+                                       adaptive=wl.adaptive, weight=weight,
+                                       score_norm=1.0 / (wl.W * wl.G), eps=wl.eps,
+                                       alpha=wl.alpha)
+        if marks is not None:
+            marks[3].record()
+        kv.kvsel_compact(k, v, idx, offs)
+        if marks is not None:
+            marks[4].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    start, end = ev(), ev()
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(marks[s])
+    end.record()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    part = lambda a, b: float(np.mean([m[a].elapsed_time(m[b]) for m in marks]))
+    ms_score, ms_vw, ms_sel, ms_cmp = part(0, 1), part(1, 2), part(2, 3), part(3, 4)
+
+    entries = wl.L * wl.H_kv * wl.n
+    # algorithmic bytes of one scoring call: K read once, Q read once,
+    # pooled scores written once
+    score_bytes = (wl.L * wl.H_kv * wl.n * wl.d * 2 + wl.L * wl.H_q * wl.W * wl.d * 2
+                   + wl.L * wl.H_kv * wl.n_cand * 4)
+    achieved = score_bytes / (ms_score * 1e-3) / 1e9
+    sha = source_sha(SCORE_SOURCES)
+    traffic = traffic_from_profiles(f"kvsel_score:{wl.name}", sha)
+    out = {
+        "metric": METRIC,
+        "value": entries / (ms_step * 1e-3),
+        "unit": "entries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "L": wl.L, "H_kv": wl.H_kv, "G": wl.G, "d": wl.d,
+                   "n": wl.n, "W": wl.W, "q_mode": wl.q_mode, "agg": wl.agg, "pool": wl.pool,
+                   "budget": wl.budget, "adaptive": wl.adaptive,
+                   "value_weight": wl.value_weight, "seed": args.seed,
+                   "step": "score+value_weight+select+compact" if wl.value_weight
+                           else "score+select+compact"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "kvsel_score", "bytes_per_launch": score_bytes,
+                     "ms_per_launch": ms_score, "source_sha": sha},
+        "per_call_ms": {"score": ms_score, "value_weight": ms_vw, "select": ms_sel,
+                        "compact": ms_cmp},
+        "scored_selected_entries_per_s": entries / ((ms_score + ms_sel) * 1e-3),
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

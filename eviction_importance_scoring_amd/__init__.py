@@ -1,0 +1,211 @@
+"""Python binding of libkvsel: prefill-end KV-cache importance scoring,
+selection and compaction on MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI declared in include/kvsel.h: each
+function below checks tensor dtypes / shapes / devices, allocates outputs
+and the workspace with torch on the inputs' device, and calls the C entry
+point of the same name on the current torch stream. Every step of the
+computation runs in the HIP kernels of libkvsel.so. There is no fallback:
+if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "lib", "library_path", "KvselError", "kvsel_score", "kvsel_value_weight",
+    "kvsel_select", "kvsel_compact", "kvsel_status_str", "kvsel_abi_version",
+    "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX",
+]
+
+Q_WINDOW, Q_EXTERNAL = 0, 1
+AGG_SUM, AGG_MAX = 0, 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libkvsel.so")
+
+_c_void_p = ctypes.c_void_p
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_c_f32 = ctypes.c_float
+_c_size_p = ctypes.POINTER(ctypes.c_size_t)
+
+_SIGNATURES = {
+    "kvsel_score": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                    _c_i32, _c_i32, _c_f32, _c_i32, _c_void_p, _c_void_p, _c_void_p,
+                    _c_size_p, _c_void_p],
+    "kvsel_value_weight": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                           _c_i32, _c_i32, _c_void_p, _c_void_p],
+    "kvsel_select": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                     _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                     _c_size_p, _c_void_p],
+    "kvsel_compact": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
+                      _c_void_p, _c_i64, _c_void_p, _c_void_p, _c_void_p],
+    "kvsel_status_str": [_c_i32],
+    "kvsel_abi_version": [],
+}
+
+_LIB = None
+
+
+class KvselError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvsel.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise KvselError(f"{library_path} is missing: build it with __graft_entry__.build()")
+        l = ctypes.CDLL(library_path)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = _c_i32
+        l.kvsel_status_str.restype = ctypes.c_char_p
+        _LIB = l
+    return _LIB
+
+
+def kvsel_status_str(status: int) -> str:
+    return lib().kvsel_status_str(status).decode()
+
+
+def kvsel_abi_version() -> int:
+    return lib().kvsel_abi_version()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise KvselError(kvsel_status_str(rc))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def kvsel_score(q, k, *, G: int, q_mode: int = Q_WINDOW, agg: int = AGG_SUM,
+                scale: float | None = None, pool: int = 7, return_raw: bool = False,
+                scores=None, raw=None, workspace=None):
+    """Pooled attention scores [L][H_kv][n_cand] (and raw [L][H_kv][n]).
+
+    q bf16 [L][H_kv*G][W][d], k bf16 [L][H_kv][n][d]."""
+    _need(q, torch.bfloat16, "q", 4)
+    _need(k, torch.bfloat16, "k", 4)
+    L, Hq, W, d = q.shape
+    L2, H, n, d2 = k.shape
+    if L2 != L or d2 != d or Hq != H * G:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, G={G}")
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    n_cand = n - W if q_mode == Q_WINDOW else n
+    dev = q.device
+    if scores is None:
+        scores = torch.empty((L, H, max(n_cand, 0)), dtype=torch.float32, device=dev)
+    if return_raw and raw is None:
+        raw = torch.empty((L, H, n), dtype=torch.float32, device=dev)
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_score
+    args = (L, H, G, d, n, W, q_mode, agg, float(scale), pool)
+    _check(f(None, None, *args, None, _ptr(raw), None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(q), _ptr(k), *args, _ptr(scores), _ptr(raw), _ptr(ws), ctypes.byref(nbytes),
+             _stream(dev)))
+    return scores, raw
+
+
+def kvsel_value_weight(v, w_o, *, G: int, n_cand: int | None = None, weight=None):
+    """CriticalKV value weight [L][H_kv][n_cand]. v bf16 [L][H_kv][n][d],
+    w_o bf16 [L][D][H_kv*G*d]."""
+    _need(v, torch.bfloat16, "v", 4)
+    _need(w_o, torch.bfloat16, "w_o", 3)
+    L, H, n, d = v.shape
+    if w_o.shape[0] != L or w_o.shape[2] != H * G * d:
+        raise ValueError(f"shape mismatch: v {tuple(v.shape)}, w_o {tuple(w_o.shape)}, G={G}")
+    D = w_o.shape[1]
+    n_cand = n if n_cand is None else n_cand
+    if weight is None:
+        weight = torch.empty((L, H, n_cand), dtype=torch.float32, device=v.device)
+    _check(lib().kvsel_value_weight(_ptr(v), _ptr(w_o), L, H, G, d, n, D, n_cand,
+                                    _ptr(weight), _stream(v.device)))
+    return weight
+
+
+def kvsel_select(scores, *, n: int, W: int, budget: int, adaptive: bool = False,
+                 weight=None, score_norm: float = 1.0, eps: float = 1e-4,
+                 alpha: float = 0.5, return_stage: bool = False, workspace=None):
+    """Kept positions. scores f32 [L][H_kv][n-W]; returns (idx, head_offsets,
+    stage): idx [L][H_kv][budget] (uniform) or [L][budget] with
+    head_offsets [L][H_kv+1] (adaptive)."""
+    _need(scores, torch.float32, "scores", 3)
+    if weight is not None:
+        _need(weight, torch.float32, "weight", 3)
+        if weight.shape != scores.shape:
+            raise ValueError("weight must match scores")
+    L, H, n_cand = scores.shape
+    if n_cand != n - W:
+        raise ValueError(f"scores has {n_cand} candidates, expected n-W={n - W}")
+    dev = scores.device
+    shape = (L, budget) if adaptive else (L, H, budget)
+    idx = torch.empty(shape, dtype=torch.int32, device=dev)
+    offs = torch.empty((L, H + 1), dtype=torch.int32, device=dev) if adaptive else None
+    stage = torch.empty(shape, dtype=torch.uint8, device=dev) if return_stage else None
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_select
+    args = (L, H, n, W, int(budget), int(adaptive), float(score_norm), float(eps), float(alpha))
+    _check(f(None, _ptr(weight), *args, None, None, None, None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(scores), _ptr(weight), *args, _ptr(idx), _ptr(offs), _ptr(stage), _ptr(ws),
+             ctypes.byref(nbytes), _stream(dev)))
+    return idx, offs, stage
+
+
+def kvsel_compact(k, v, idx, head_offsets=None):
+    """Gather kept rows: returns (k_out, v_out) bf16 [L][kept_per_layer][d]."""
+    _need(k, torch.bfloat16, "k", 4)
+    _need(v, torch.bfloat16, "v", 4)
+    _need(idx, torch.int32, "idx")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    L, H, n, d = k.shape
+    kept = idx[0].numel()
+    if idx.shape[0] != L:
+        raise ValueError("idx must have a leading L axis")
+    if head_offsets is not None:
+        _need(head_offsets, torch.int32, "head_offsets", 2)
+    k_out = torch.empty((L, kept, d), dtype=k.dtype, device=k.device)
+    v_out = torch.empty((L, kept, d), dtype=v.dtype, device=v.device)
+    _check(lib().kvsel_compact(_ptr(k), _ptr(v), L, H, d, n, _ptr(idx), _ptr(head_offsets),
+                               kept, _ptr(k_out), _ptr(v_out), _stream(k.device)))
+    return k_out, v_out

@@ -1,0 +1,151 @@
+// C ABI of libkvsel: argument checks, workspace sizing, dispatch.
+// Every check runs before the first HIP call, so a rejected call touches
+// neither the device nor the outputs (and works on a host without a GPU).
+#include <cmath>
+#include <cstdint>
+
+#include "kvsel.h"
+#include "kvsel_kernels.h"
+
+namespace kvsel {
+hipError_t score_launch(const ScorePlan& p, const void* q, const void* k, float* scores,
+                        float* raw, void* ws, size_t ws_bytes, hipStream_t st);
+size_t score_ws_bytes(const ScorePlan& p);
+bool select_groups_ok(int groups);
+}  // namespace kvsel
+
+using namespace kvsel;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvsel_abi_version(void) { return 1; }
+
+const char* kvsel_status_str(int32_t status) {
+  switch (status) {
+    case KVSEL_OK: return "KVSEL_OK";
+    case KVSEL_ERR_ARG: return "KVSEL_ERR_ARG: invalid argument";
+    case KVSEL_ERR_UNSUPPORTED: return "KVSEL_ERR_UNSUPPORTED: request outside what this build covers";
+    case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE: workspace too small";
+    case KVSEL_ERR_HIP: return "KVSEL_ERR_HIP: HIP launch failed";
+    default: return "KVSEL: unknown status";
+  }
+}
+
+int32_t kvsel_score(const void* q, const void* k, int32_t L, int32_t H_kv, int32_t G,
+                    int32_t d, int32_t n, int32_t W, int32_t q_mode, int32_t agg, float scale,
+                    int32_t pool, float* scores, float* raw, void* ws, size_t* ws_bytes,
+                    void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || G < 1 || d < 1 || n < 1 || W < 1) return KVSEL_ERR_ARG;
+  if (q_mode != KVSEL_Q_WINDOW && q_mode != KVSEL_Q_EXTERNAL) return KVSEL_ERR_ARG;
+  if (agg != KVSEL_AGG_SUM && agg != KVSEL_AGG_MAX) return KVSEL_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return KVSEL_ERR_ARG;
+  if (pool < 1 || pool % 2 == 0) return KVSEL_ERR_ARG;
+  if (q_mode == KVSEL_Q_WINDOW && W >= n) return KVSEL_ERR_ARG;
+  if (d != kHeadDimPublic) return KVSEL_ERR_UNSUPPORTED;
+  if (pool > 65) return KVSEL_ERR_UNSUPPORTED;
+  if ((int64_t)G * W > kMaxIndex || (int64_t)H_kv * n > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  ScorePlan p;
+  p.L = L; p.H = H_kv; p.G = G; p.n = n; p.W = W;
+  p.R = G * W;
+  p.causal = q_mode == KVSEL_Q_WINDOW;
+  p.n_cand = p.causal ? n - W : n;
+  p.pool = pool;
+  p.max_agg = agg == KVSEL_AGG_MAX;
+  p.need_raw_tmp = raw == nullptr;
+  p.scale = scale;
+  const size_t need = score_ws_bytes(p);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!q || !k || !scores) return KVSEL_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(scores) || !aligned16(ws) ||
+      (raw && !aligned16(raw)))
+    return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  const hipError_t e = score_launch(p, q, k, scores, raw, ws, *ws_bytes,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_value_weight(const void* v, const void* w_o, int32_t L, int32_t H_kv, int32_t G,
+                           int32_t d, int32_t n, int32_t D, int32_t n_cand, float* weight,
+                           void* stream) {
+  if (!v || !w_o || !weight) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || G < 1 || d < 1 || n < 1 || D < 1) return KVSEL_ERR_ARG;
+  if (n_cand < 1 || n_cand > n) return KVSEL_ERR_ARG;
+  if (!aligned16(v) || !aligned16(w_o) || !aligned16(weight)) return KVSEL_ERR_ARG;
+  if (d != kHeadDimPublic || D % 32 != 0) return KVSEL_ERR_UNSUPPORTED;
+  if ((int64_t)H_kv * G * d > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  const hipError_t e = value_weight_launch(v, w_o, L, H_kv, G, n, D, n_cand, weight,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_select(const float* scores, const float* weight, int32_t L, int32_t H_kv,
+                     int32_t n, int32_t W, int64_t budget, int32_t adaptive, float score_norm,
+                     float eps, float alpha, int32_t* idx, int32_t* head_offsets,
+                     uint8_t* stage, void* ws, size_t* ws_bytes, void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || n < 1 || W < 0 || W >= n) return KVSEL_ERR_ARG;
+  if (adaptive != 0 && adaptive != 1) return KVSEL_ERR_ARG;
+  const int64_t n_cand = (int64_t)n - W;
+  const int64_t groups = adaptive ? H_kv : 1;
+  if (budget < groups * W || budget > groups * (int64_t)n) return KVSEL_ERR_ARG;
+  if (weight) {
+    if (!(alpha >= 0.f && alpha <= 1.f)) return KVSEL_ERR_ARG;
+    if (!(score_norm > 0.f) || !std::isfinite(score_norm)) return KVSEL_ERR_ARG;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return KVSEL_ERR_ARG;
+  }
+  if (groups * n_cand > kMaxIndex || budget > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  if (adaptive && !select_groups_ok(H_kv)) return KVSEL_ERR_UNSUPPORTED;
+  SelectPlan p;
+  p.L = L; p.H = H_kv; p.n = n; p.W = W; p.n_cand = (int)n_cand;
+  p.budget = budget;
+  p.adaptive = adaptive != 0;
+  p.two_stage = weight != nullptr;
+  p.score_norm = score_norm;
+  p.eps = eps;
+  p.k = budget - groups * W;
+  p.k1 = p.two_stage ? (int64_t)std::floor((double)alpha * (double)p.k) : 0;
+  p.segments = adaptive ? L : L * H_kv;
+  p.seg_len = groups * n_cand;
+  p.resident = false;
+  const size_t need = select_ws_bytes(p);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!scores || (budget > 0 && !idx) || (adaptive && !head_offsets)) return KVSEL_ERR_ARG;
+  if (!aligned16(scores) || (weight && !aligned16(weight))) return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  const hipError_t e = select_launch(p, scores, weight, idx, head_offsets, stage, ws,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_compact(const void* k, const void* v, int32_t L, int32_t H_kv, int32_t d,
+                      int32_t n, const int32_t* idx, const int32_t* head_offsets,
+                      int64_t kept_per_layer, void* k_out, void* v_out, void* stream) {
+  if (!k || !v || !idx || !k_out || !v_out) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || d < 1 || n < 1 || kept_per_layer < 1) return KVSEL_ERR_ARG;
+  if (d % 8 != 0) return KVSEL_ERR_UNSUPPORTED;
+  if (!head_offsets && kept_per_layer % H_kv != 0) return KVSEL_ERR_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out))
+    return KVSEL_ERR_ARG;
+  if (kept_per_layer > (int64_t)H_kv * n) return KVSEL_ERR_ARG;
+  const hipError_t e = compact_launch(k, v, L, H_kv, d, n, idx, head_offsets, kept_per_layer,
+                                      k_out, v_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+}  // extern "C"

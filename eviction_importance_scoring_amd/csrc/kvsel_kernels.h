@@ -1,0 +1,60 @@
+// Host-side interfaces between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+constexpr int kHeadDimPublic = 128;   // the head dimension the library accepts
+
+// ------------------------------------------------------------- scoring ----
+struct ScorePlan {
+  int L, H, G, n, W;      // W = queries per query head
+  int R;                  // rows per KV head = G*W
+  int n_cand;             // n-W (window) or n (external)
+  int pool;
+  bool causal;            // window mode
+  bool max_agg;
+  bool need_raw_tmp;      // caller passed raw == NULL
+  float scale;
+};
+
+struct TwoPassLayout {
+  int row_blocks, splits, keys_per_split;
+  size_t part_off, stat_off, raw_off, bytes;
+};
+
+void twopass_plan(const ScorePlan& p, TwoPassLayout* o);
+hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void* q,
+                          const void* k, float* scores, float* raw, void* ws,
+                          hipStream_t st);
+
+// ------------------------------------------------------------ selection ----
+struct SelectPlan {
+  int L, H, n, W, n_cand;
+  int64_t budget;
+  bool adaptive, two_stage;
+  float score_norm, eps;
+  int64_t k, k1;          // candidates kept (all stages), stage-1 share
+  int segments;           // L*H (uniform) or L (adaptive)
+  int64_t seg_len;        // n_cand or H*n_cand
+  bool resident;          // segment fits in LDS
+};
+
+size_t select_ws_bytes(const SelectPlan& p);
+hipError_t select_launch(const SelectPlan& p, const float* scores, const float* weight,
+                         int32_t* idx, int32_t* head_offsets, uint8_t* stage, void* ws,
+                         hipStream_t st);
+
+// ----------------------------------------------------------- compaction ----
+hipError_t compact_launch(const void* k, const void* v, int L, int H, int d, int n,
+                          const int32_t* idx, const int32_t* head_offsets,
+                          int64_t kept, void* k_out, void* v_out, hipStream_t st);
+
+// --------------------------------------------------------- value weight ----
+hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int G, int n,
+                               int D, int n_cand, float* weight, hipStream_t st);
+
+}  // namespace kvsel

@@ -1,0 +1,197 @@
+/*
+ * kvsel.h -- prefill-end KV-cache importance scoring, selection and
+ * compaction on AMD Instinct MI355X (gfx950). C ABI.
+ *
+ * Sources, cited below by page title and section:
+ *   [CriticalKV] "CriticalKV: Optimizing KV Cache Eviction from an Output
+ *                Perturbation Perspective" (Korean translation, sumin.im)
+ *   [KVzip]      review of "KVzip: Query-Agnostic KV Cache Compression with
+ *                Context Reconstruction" (manon006.tistory.com)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *    keeps no pointer after a call returns. bf16 tensors are passed as
+ *    `const void*` (IEEE bfloat16, 2 bytes); other types are as declared.
+ *    Every tensor is dense, row-major, in the layout documented per call,
+ *    and must be 16-byte aligned.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream). Outputs are valid once the stream has been
+ *    synchronised. No call allocates device memory or synchronises.
+ *  - Every argument check runs before anything is launched: a call that
+ *    returns non-zero has launched nothing and written nothing.
+ *  - Workspace protocol (kvsel_score, kvsel_select): with ws == NULL the
+ *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
+ *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
+ *    Workspace contents need no initialisation and are scratch afterwards.
+ *    Two calls in flight at once must use different workspaces.
+ *  - Floating-point inputs must be finite; results are unspecified
+ *    otherwise. Results are bitwise reproducible for identical inputs
+ *    (no floating-point atomics anywhere).
+ *  - Calls are thread-safe when they use distinct outputs and workspaces.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KVSEL_OK = 0,
+  KVSEL_ERR_ARG = 1,          /* null required pointer, bad size, bad range */
+  KVSEL_ERR_UNSUPPORTED = 2,  /* valid request this build does not cover    */
+  KVSEL_ERR_WORKSPACE = 3,    /* ws given but *ws_bytes is too small        */
+  KVSEL_ERR_HIP = 4           /* a HIP launch failed; outputs undefined     */
+};
+
+/* Which queries score the cache. */
+enum {
+  /* The W queries are the cache's own last W tokens ([CriticalKV] §3.3,
+     Algorithm 2, step 2: Q_hat = Q[-n':]). Query i sits at position n-W+i
+     and sees keys 0..n-W+i (causal). Candidates are positions [0, n-W); the
+     window itself is always kept by kvsel_select. */
+  KVSEL_Q_WINDOW = 0,
+  /* The W queries come from outside the cache (KVzip's reconstruction
+     queries, [KVzip] §3.2) and see all n keys. Candidates are [0, n). */
+  KVSEL_Q_EXTERNAL = 1
+};
+
+/* How the per-query softmax weights of one key are aggregated. */
+enum {
+  /* Sum over the W queries and the G query heads of the KV head
+     ([CriticalKV] §3.3, Algorithm 2, step 3, as a sum: the mean only
+     rescales by 1/(W*G)). The raw scores of one head sum to W*G. */
+  KVSEL_AGG_SUM = 0,
+  /* Max over the W queries and the G query heads ([KVzip] §3.2). */
+  KVSEL_AGG_MAX = 1
+};
+
+/*
+ * kvsel_score -- attention-based importance of every cached key.
+ *
+ * Per layer l and KV head h, with query head hq = h*G + g (GQA grouping,
+ * [KVzip] §2.2): logits s = scale * <q[l][hq][i], k[l][h][j]>, a softmax
+ * over the keys each query sees (all n, or causal in window mode), the
+ * aggregate over (g, i) chosen by `agg`, then 1-D max-pooling of width
+ * `pool` along the candidate positions ([CriticalKV] §3.3, Algorithm 2,
+ * step 4; stride 1, centred, neighbours outside [0, n_cand) ignored).
+ *
+ *   q      bf16 [L][H_kv*G][W][d]
+ *   k      bf16 [L][H_kv][n][d]
+ *   scores f32  [L][H_kv][n_cand]  pooled scores, n_cand = n-W (window)
+ *                                  or n (external)
+ *   raw    f32  [L][H_kv][n]       optional (NULL): pre-pool aggregate over
+ *                                  all n keys, window keys included
+ *   scale  softmax temperature (the model's 1/sqrt(d)), > 0
+ *   pool   odd, >= 1 (1 = no pooling)
+ *
+ * Limits: d == 128 (else KVSEL_ERR_UNSUPPORTED); window mode needs
+ * 1 <= W < n. Needs a workspace (protocol above).
+ */
+int32_t kvsel_score(const void* q, const void* k,
+                    int32_t L, int32_t H_kv, int32_t G, int32_t d, int32_t n,
+                    int32_t W, int32_t q_mode, int32_t agg, float scale,
+                    int32_t pool, float* scores, float* raw,
+                    void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_value_weight -- CriticalKV's projected-value norm.
+ *
+ * [CriticalKV] §3.3, Algorithm 1, steps 2-3: V_proj = V W^O and the L1
+ * norm of each row of V_proj (Theorem 3.3: the output perturbation is
+ * bounded by attention weight times this norm). Under GQA the weight of
+ * KV head h at position j is the mean over its G query heads:
+ *   weight[l][h][j] = (1/G) sum_g sum_{c<D} | sum_{e<d}
+ *                        w_o[l][c][(h*G+g)*d + e] * v[l][h][j][e] |
+ * for j < n_cand. The projection is accumulated in fp32 from bf16 and is
+ * never written out.
+ *
+ *   v      bf16 [L][H_kv][n][d]
+ *   w_o    bf16 [L][D][H_kv*G*d]     output projection, (out, in) layout
+ *   weight f32  [L][H_kv][n_cand]    1 <= n_cand <= n
+ *
+ * Limits: d == 128, D % 32 == 0 (else KVSEL_ERR_UNSUPPORTED).
+ */
+int32_t kvsel_value_weight(const void* v, const void* w_o,
+                           int32_t L, int32_t H_kv, int32_t G, int32_t d,
+                           int32_t n, int32_t D, int32_t n_cand,
+                           float* weight, void* stream);
+
+/*
+ * kvsel_select -- which cache entries to keep.
+ *
+ * Candidates are positions [0, n-W) of every head; the W window positions
+ * [n-W, n) are always kept and count toward the budget. Among candidates
+ * the k = budget - W (per head) or k = budget - H_kv*W (per layer, when
+ * adaptive) largest keys are kept; equal keys go to the lower index
+ * (adaptive: lower head, then lower position).
+ *
+ *  - weight == NULL: key = scores ([CriticalKV] §3.3, Algorithm 2, step 6).
+ *  - weight != NULL: CriticalKV's two-stage selection ([CriticalKV] §3.3,
+ *    Algorithm 1, steps 3-9): stage 1 keeps k1 = floor(alpha*k) entries by
+ *    score; stage 2 keeps k - k1 of the rest by the integrated score
+ *      (score*score_norm + eps) * weight
+ *    computed in fp32 as mul, add, mul, each rounded once.
+ *  - adaptive == 0: one budget per head. adaptive == 1: one budget per
+ *    layer shared by its heads, selected over the flattened candidates of
+ *    all heads (the non-uniform head budget of [KVzip] §4.2 / AdaKV).
+ *
+ *   scores       f32 [L][H_kv][n-W]
+ *   weight       f32 [L][H_kv][n-W]    optional
+ *   idx          i32 adaptive == 0: [L][H_kv][budget]  (may be NULL if budget == 0)
+ *                    adaptive == 1: [L][budget], grouped by head
+ *                Per head: kept candidates ascending, then n-W..n-1.
+ *   head_offsets i32 [L][H_kv+1]  adaptive == 1 only (required there):
+ *                head h of layer l owns idx[l][head_offsets[l][h] ..
+ *                head_offsets[l][h+1]).
+ *   stage        u8 same shape as idx, optional: 0 window, 1 stage 1 (or
+ *                the single stage), 2 stage 2.
+ *
+ * Ranges: 0 <= W < n; W <= budget <= n (per head) or
+ * H_kv*W <= budget <= H_kv*n (per layer); 0 <= alpha <= 1;
+ * score_norm > 0, eps >= 0. Needs a workspace (protocol above).
+ */
+int32_t kvsel_select(const float* scores, const float* weight,
+                     int32_t L, int32_t H_kv, int32_t n, int32_t W,
+                     int64_t budget, int32_t adaptive,
+                     float score_norm, float eps, float alpha,
+                     int32_t* idx, int32_t* head_offsets, uint8_t* stage,
+                     void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_compact -- gather the kept rows of K and V.
+ *
+ * Eviction acts on the un-replicated cache ([KVzip] §4.2): kept row t of
+ * layer l, head h, is a bit copy of k[l][h][idx[...]][:] (same for v).
+ *
+ *   k, v         bf16 [L][H_kv][n][d]
+ *   idx          i32  as written by kvsel_select: head_offsets == NULL ->
+ *                     [L][H_kv][B] with B = kept_per_layer / H_kv;
+ *                     otherwise [L][kept_per_layer] grouped by head
+ *   head_offsets i32  [L][H_kv+1] or NULL
+ *   k_out, v_out bf16 [L][kept_per_layer][d]  (uniform: = [L][H_kv][B][d])
+ *
+ * Every idx entry must lie in [0, n); out-of-range entries are not read
+ * (their rows are written as zeros). d % 8 == 0.
+ */
+int32_t kvsel_compact(const void* k, const void* v,
+                      int32_t L, int32_t H_kv, int32_t d, int32_t n,
+                      const int32_t* idx, const int32_t* head_offsets,
+                      int64_t kept_per_layer, void* k_out, void* v_out,
+                      void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* kvsel_status_str(int32_t status);
+
+/* ABI version of this header: 1. */
+int32_t kvsel_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

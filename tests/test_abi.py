@@ -1,0 +1,146 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/kvsel.h declares, answers workspace queries and rejects
+bad arguments before any HIP call (nothing is launched on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import eviction_importance_scoring_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvsel.h")
+
+OK, ARG, UNSUP, WS = 0, 1, 2, 3
+
+# Tests that pass made-up non-null pointers only ever hit argument checks;
+# they are not run where a GPU is visible, so that a validation bug could
+# never launch a kernel on a bogus address.
+no_gpu_only = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(),
+    reason="passes fake device pointers; CPU-only contract test")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvsel_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kv.library_path):
+        pytest.fail("libkvsel.so not built (run __graft_entry__.build())")
+    return kv.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"kvsel_score", "kvsel_value_weight", "kvsel_select", "kvsel_compact",
+                          "kvsel_status_str", "kvsel_abi_version"}
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in kvsel.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvsel_abi_version() == 1
+    for code in (OK, ARG, UNSUP, WS, 4):
+        assert kv.kvsel_status_str(code).startswith("KVSEL")
+    assert "unknown" in kv.kvsel_status_str(99)
+
+
+def _score(lib, **kw):
+    a = dict(L=1, H=8, G=4, d=128, n=4096, W=32, mode=0, agg=0, scale=0.088, pool=7)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    rc = lib.kvsel_score(None, None, a["L"], a["H"], a["G"], a["d"], a["n"], a["W"], a["mode"],
+                         a["agg"], a["scale"], a["pool"], None, None, None, ctypes.byref(nb), None)
+    return rc, nb.value
+
+
+def test_score_workspace_query(lib):
+    rc, nb = _score(lib)
+    assert rc == OK and nb > 0
+    rc2, nb2 = _score(lib, L=32, n=32768)
+    assert rc2 == OK and nb2 >= nb
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), ARG), (dict(H=0), ARG), (dict(G=0), ARG), (dict(n=0), ARG), (dict(W=0), ARG),
+    (dict(W=4096), ARG), (dict(W=5000), ARG), (dict(mode=2), ARG), (dict(agg=3), ARG),
+    (dict(scale=0.0), ARG), (dict(scale=-1.0), ARG), (dict(scale=float("inf")), ARG),
+    (dict(scale=float("nan")), ARG), (dict(pool=0), ARG), (dict(pool=4), ARG),
+    (dict(d=64), UNSUP), (dict(pool=67), UNSUP),
+])
+def test_score_rejects(lib, kw, code):
+    assert _score(lib, **kw)[0] == code
+
+
+def test_score_external_allows_w_ge_n(lib):
+    assert _score(lib, mode=1, W=8192, n=4096)[0] == OK
+
+
+@no_gpu_only
+def test_score_null_and_workspace_checks(lib):
+    nb = ctypes.c_size_t(0)
+    assert lib.kvsel_score(None, None, 1, 8, 4, 128, 4096, 32, 0, 0, 0.088, 7, None, None, None,
+                           None, None) == ARG
+    # non-null workspace but null inputs -> ARG; too small -> WORKSPACE (pointers unused)
+    fake = ctypes.c_void_p(1 << 20)
+    nb.value = 1 << 30
+    assert lib.kvsel_score(None, None, 1, 8, 4, 128, 4096, 32, 0, 0, 0.088, 7, None, None, fake,
+                           ctypes.byref(nb), None) == ARG
+    nb.value = 16
+    assert lib.kvsel_score(fake, fake, 1, 8, 4, 128, 4096, 32, 0, 0, 0.088, 7, fake, None, fake,
+                           ctypes.byref(nb), None) == WS
+    nb.value = 1 << 30
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.kvsel_score(odd, fake, 1, 8, 4, 128, 4096, 32, 0, 0, 0.088, 7, fake, None, fake,
+                           ctypes.byref(nb), None) == ARG
+
+
+def _select(lib, weight=False, **kw):
+    a = dict(L=1, H=8, n=4096, W=32, budget=819, adaptive=0, norm=1.0, eps=1e-4, alpha=0.5)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    w = ctypes.c_void_p(1 << 20) if weight else None
+    return lib.kvsel_select(None, w, a["L"], a["H"], a["n"], a["W"], a["budget"], a["adaptive"],
+                            a["norm"], a["eps"], a["alpha"], None, None, None, None,
+                            ctypes.byref(nb), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(budget=32), OK), (dict(budget=4096), OK), (dict(W=0, budget=0), OK),
+    (dict(budget=31), ARG), (dict(budget=4097), ARG), (dict(W=4096), ARG), (dict(W=-1), ARG),
+    (dict(adaptive=2), ARG), (dict(adaptive=1, budget=255), ARG), (dict(adaptive=1, budget=256), OK),
+    (dict(adaptive=1, budget=8 * 4096), OK), (dict(adaptive=1, budget=8 * 4096 + 1), ARG),
+    (dict(L=0), ARG), (dict(H=0), ARG), (dict(n=0), ARG),
+])
+def test_select_ranges(lib, kw, code):
+    assert _select(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(alpha=-0.1), ARG), (dict(alpha=1.5), ARG), (dict(alpha=float("nan")), ARG),
+    (dict(norm=0.0), ARG), (dict(eps=-1.0), ARG), (dict(eps=float("inf")), ARG), (dict(), OK),
+])
+@no_gpu_only
+def test_select_two_stage_ranges(lib, kw, code):
+    assert _select(lib, weight=True, **kw) == code
+
+
+@no_gpu_only
+def test_value_weight_and_compact_reject(lib):
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.kvsel_value_weight
+    assert f(None, p, 1, 8, 4, 128, 100, 4096, 68, p, None) == ARG
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 101, p, None) == ARG    # n_cand > n
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 0, p, None) == ARG
+    assert f(p, p, 1, 8, 4, 64, 100, 4096, 68, p, None) == UNSUP
+    assert f(p, p, 1, 8, 4, 128, 100, 4010, 68, p, None) == UNSUP   # D % 32
+    c = lib.kvsel_compact
+    assert c(None, p, 1, 8, 128, 100, p, None, 16, p, p, None) == ARG
+    assert c(p, p, 1, 8, 128, 100, p, None, 12, p, p, None) == ARG  # not divisible by H
+    assert c(p, p, 1, 8, 128, 100, p, None, 808, p, p, None) == ARG  # more rows than the cache
+    assert c(p, p, 1, 8, 12, 100, p, None, 16, p, p, None) == UNSUP

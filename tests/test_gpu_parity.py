@@ -1,0 +1,212 @@
+"""GPU parity against the oracle at small sizes (several tiles, ragged
+tails, edge cases). Every call goes through the C ABI via the ctypes
+binding; nothing here falls back to a CPU path."""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import eviction_importance_scoring_amd as kv
+import oracle
+import synth
+from harness import (assert_scores_close, assert_topk_within_band, gen, oracle_scores_layer,
+                     split_heads, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(**kw):
+    base = dict(name="t", L=1, H_kv=2, G=4, d=128, n=100, W=8, pool=7, heavy="zipf")
+    base.update(kw)
+    base["name"] = "t_" + "_".join(f"{k}{v}" for k, v in sorted(kw.items()))
+    return synth.Workload(**base)
+
+
+def _run_scores(wl, data, return_raw=True):
+    q, k = to_dev(data["q"]), to_dev(data["k"])
+    mode = kv.Q_WINDOW if wl.q_mode == "window" else kv.Q_EXTERNAL
+    agg = kv.AGG_SUM if wl.agg == "sum" else kv.AGG_MAX
+    print(f"[gpu] kvsel_score {wl.name} L={wl.L} H={wl.H_kv} G={wl.G} n={wl.n} W={wl.W}",
+          flush=True)
+    scores, raw = kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale,
+                                 pool=wl.pool, return_raw=return_raw)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), (raw.cpu().numpy() if raw is not None else None)
+
+
+WINDOW_CASES = [
+    dict(n=100, W=8),
+    dict(L=2, H_kv=3, n=257, W=32),
+    dict(G=1, n=1000, W=1, pool=3),
+    dict(H_kv=1, G=7, n=4097, W=32, pool=1),
+    dict(n=33, W=32),                      # a single candidate
+    dict(n=2, W=1, G=2),                   # smallest cache
+    dict(n=300, W=16, pool=5, agg="max"),
+    dict(n=1500, W=40, G=4),               # R = 160 rows: more than one row block
+    dict(n=4096, W=32, heavy="uniform1pct"),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_window_scores(case):
+    wl = _wl(**case)
+    data = gen(wl, seed=1, which=("q", "k"))
+    scores, raw = _run_scores(wl, data)
+    for l in range(wl.L):
+        ref_raw, ref_pool = oracle_scores_layer(wl, data["q"][l], data["k"][l])
+        assert_scores_close(raw[l], ref_raw, "raw")
+        assert_scores_close(scores[l], ref_pool, "pooled")
+        if wl.agg == "sum":
+            np.testing.assert_allclose(raw[l].astype(np.float64).sum(axis=1), wl.W * wl.G, rtol=1e-5)
+
+
+EXTERNAL_CASES = [
+    dict(n=300, W=50, G=3, agg="max"),
+    dict(H_kv=1, G=7, n=1000, W=129, agg="max"),
+    dict(L=2, n=33, W=1, G=2, agg="max"),
+    dict(n=700, W=64, G=2, agg="sum"),
+    dict(n=5000, W=300, G=1, agg="max", pool=3),
+]
+
+
+@pytest.mark.parametrize("case", EXTERNAL_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_external_scores(case):
+    wl = _wl(q_mode="external", pool=case.pop("pool", 1), **case)
+    data = gen(wl, seed=2, which=("q", "k"))
+    scores, raw = _run_scores(wl, data)
+    for l in range(wl.L):
+        ref_raw, ref_pool = oracle_scores_layer(wl, data["q"][l], data["k"][l])
+        assert_scores_close(raw[l], ref_raw, "raw")
+        assert_scores_close(scores[l], ref_pool, "pooled")
+        if wl.agg == "max":
+            assert (raw[l] <= 1.0 + 1e-6).all()
+
+
+def test_scores_deterministic():
+    wl = _wl(L=2, n=3000, W=32)
+    data = gen(wl, seed=3, which=("q", "k"))
+    a = _run_scores(wl, data)
+    b = _run_scores(wl, data)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# --------------------------------------------------------------- selection ----
+
+def _quantised_scores(rng, shape, levels):
+    """Scores with many exact ties (few distinct levels)."""
+    return (rng.integers(0, levels, size=shape) / levels).astype(np.float32)
+
+
+SELECT_CASES = [
+    # (L, H, n, W, budget_frac, adaptive, two_stage, alpha, levels)
+    (1, 2, 100, 8, 0.5, False, False, 0.5, 7),
+    (2, 3, 1000, 32, 0.2, False, False, 0.5, 1000000),
+    (1, 4, 3000, 32, 0.4, True, False, 0.5, 50),
+    (2, 2, 2000, 16, 0.3, False, True, 0.5, 30),
+    (1, 3, 1500, 8, 0.25, True, True, 0.5, 1000000),
+    (1, 2, 500, 4, 0.3, False, True, 0.0, 10),
+    (1, 2, 500, 4, 0.3, False, True, 1.0, 10),
+    (1, 1, 50000, 32, 0.1, False, False, 0.5, 1000),      # longer than LDS: streamed
+    (1, 2, 40000, 32, 0.1, True, True, 0.5, 100000),      # streamed, two-stage, adaptive
+    (1, 2, 64, 32, 1.0, False, False, 0.5, 3),            # keep everything
+    (1, 2, 64, 32, 0.5, False, False, 0.5, 3),            # keep only the window
+    (1, 2, 64, 0, 0.0, False, False, 0.5, 3),             # external: nothing kept
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: "L{}H{}n{}W{}b{}a{}t{}al{}lv{}".format(*c))
+def test_select_exact_on_same_fp32_scores(case):
+    L, H, n, W, frac, adaptive, two_stage, alpha, levels = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    n_cand = n - W
+    sc = _quantised_scores(rng, (L, H, n_cand), levels)
+    wt = (rng.random((L, H, n_cand)).astype(np.float32) * 3 + 0.01) if two_stage else None
+    groups = H if adaptive else 1
+    budget = max(groups * W, int(np.floor(frac * groups * n)))
+    print(f"[gpu] kvsel_select case={case} budget={budget}", flush=True)
+    idx, offs, stage = kv.kvsel_select(torch.from_numpy(sc).cuda(), n=n, W=W, budget=budget,
+                                       adaptive=adaptive,
+                                       weight=None if wt is None else torch.from_numpy(wt).cuda(),
+                                       score_norm=1.0 / 128, eps=1e-4, alpha=alpha,
+                                       return_stage=True)
+    torch.cuda.synchronize()
+    idx, stage = idx.cpu().numpy(), stage.cpu().numpy()
+    offs = None if offs is None else offs.cpu().numpy()
+    for l in range(L):
+        ri, ro, rs = oracle.select_layer(sc[l].astype(np.float64), budget, W, n, adaptive=adaptive,
+                                         weight=None if wt is None else wt[l].astype(np.float64),
+                                         alpha=float(np.float32(alpha)), score_norm=float(np.float32(1 / 128)),
+                                         eps=float(np.float32(1e-4)), dtype=np.float32)
+        np.testing.assert_array_equal(idx[l], ri)
+        np.testing.assert_array_equal(stage[l], rs)
+        if adaptive:
+            np.testing.assert_array_equal(offs[l], ro)
+
+
+def test_select_end_to_end_band():
+    """GPU scores + GPU select against the fp64 oracle's selection."""
+    wl = _wl(L=2, H_kv=2, n=3000, W=32)
+    data = gen(wl, seed=4, which=("q", "k"))
+    q, k = to_dev(data["q"]), to_dev(data["k"])
+    scores, _ = kv.kvsel_score(q, k, G=wl.G, pool=7)
+    budget = int(0.3 * wl.n)
+    idx, _, _ = kv.kvsel_select(scores, n=wl.n, W=wl.W, budget=budget)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for l in range(wl.L):
+        _, pooled = oracle_scores_layer(wl, data["q"][l], data["k"][l])
+        picks = split_heads(idx[l], None, wl.H_kv, wl.W, wl.n)
+        for h in range(wl.H_kv):
+            assert_topk_within_band(picks[h], pooled[h], budget - wl.W, f"l{l}h{h}")
+
+
+# -------------------------------------------------------------- compaction ----
+
+@pytest.mark.parametrize("adaptive", [False, True])
+def test_compact_bit_exact(adaptive):
+    rng = np.random.default_rng(5)
+    L, H, n, d = 2, 3, 777, 128
+    k = rng.integers(0, 65536, size=(L, H, n, d), dtype=np.uint16)
+    v = rng.integers(0, 65536, size=(L, H, n, d), dtype=np.uint16)
+    if adaptive:
+        counts = [[5, 0, 40], [17, 3, 25]]
+        kept = 45
+        idx = np.zeros((L, kept), np.int32)
+        offs = np.zeros((L, H + 1), np.int32)
+        for l in range(L):
+            parts = [np.sort(rng.choice(n, c, replace=False)) for c in counts[l]]
+            idx[l] = np.concatenate(parts)
+            offs[l] = np.concatenate([[0], np.cumsum(counts[l])])
+    else:
+        B = 31
+        idx = np.stack([np.stack([np.sort(rng.choice(n, B, replace=False)) for _ in range(H)])
+                        for _ in range(L)]).astype(np.int32)
+        offs = None
+    ko, vo = kv.kvsel_compact(to_dev(k), to_dev(v), torch.from_numpy(idx).cuda(),
+                              None if offs is None else torch.from_numpy(offs).cuda())
+    torch.cuda.synchronize()
+    ko = ko.cpu().view(torch.int16).numpy().view(np.uint16)
+    vo = vo.cpu().view(torch.int16).numpy().view(np.uint16)
+    for l in range(L):
+        rk, rv = oracle.compact_layer(k[l], v[l], idx[l], None if offs is None else offs[l])
+        np.testing.assert_array_equal(ko[l].reshape(rk.shape), rk)
+        np.testing.assert_array_equal(vo[l].reshape(rv.shape), rv)
+
+
+# ------------------------------------------------------------ value weight ----
+
+@pytest.mark.parametrize("H,G,n,D,n_cand", [(2, 4, 300, 256, 290), (1, 7, 97, 64, 97), (3, 1, 1000, 32, 999)])
+def test_value_weight(H, G, n, D, n_cand):
+    wl = _wl(H_kv=H, G=G, n=n, W=n - n_cand if n_cand < n else 1, value_weight=True, D=D)
+    data = gen(wl, seed=6, which=("v", "w_o"))
+    print(f"[gpu] kvsel_value_weight H={H} G={G} n={n} D={D}", flush=True)
+    w = kv.kvsel_value_weight(to_dev(data["v"]), to_dev(data["w_o"]), G=G, n_cand=n_cand)
+    torch.cuda.synchronize()
+    w = w.cpu().numpy()
+    ref = oracle.value_weight(synth.bf16_to_f64(data["v"][0]), synth.bf16_to_f64(data["w_o"][0]), G,
+                              np.arange(n_cand))
+    assert_scores_close(w[0], ref, "value weight")
