@@ -47,6 +47,13 @@ __device__ __forceinline__ void load_half_row(const void* row, int hf, bf16x8 (&
   for (int s = 0; s < 8; ++s) x[s] = ld16(p + 16 * s);
 }
 
+// Same, for data read exactly once (non-temporal: not kept in the caches).
+__device__ __forceinline__ void load_half_row_stream(const void* row, int hf, bf16x8 (&x)[8]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(row) + hf * 128);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) x[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(p + s));
+}
+
 __device__ __forceinline__ void zero_ops(bf16x8 (&x)[8]) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) x[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});

@@ -31,6 +31,16 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
                           const void* k, float* scores, float* raw, void* ws,
                           hipStream_t st);
 
+struct WindowLayout {
+  int kpb, blocks;          // keys per workgroup, workgroups per head
+  size_t part_off, stat_off, raw_off, bytes;
+};
+
+bool window_applicable(const ScorePlan& p);
+void window_plan(const ScorePlan& p, WindowLayout* o);
+hipError_t window_launch(const ScorePlan& p, const WindowLayout& o, const void* q, const void* k,
+                         float* scores, float* raw, void* ws, hipStream_t st);
+
 // ------------------------------------------------------------ selection ----
 struct SelectPlan {
   int L, H, n, W, n_cand;

@@ -1,20 +1,32 @@
 // kvsel_score dispatch: workspace sizing and the choice of score kernels.
+//
+// Window mode with R = G*W <= 128 query rows per KV head uses the streaming
+// window kernels (score_window.hip); external queries and larger R use the
+// general two-pass kernels (score_twopass.hip). The workspace is the larger
+// of the two layouts, so a size query needs no device.
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
 
 namespace kvsel {
 
 size_t score_ws_bytes(const ScorePlan& p) {
-  TwoPassLayout o;
-  twopass_plan(p, &o);
-  return o.bytes;
+  TwoPassLayout t;
+  twopass_plan(p, &t);
+  WindowLayout w;
+  window_plan(p, &w);
+  return t.bytes > w.bytes ? t.bytes : w.bytes;
 }
 
 hipError_t score_launch(const ScorePlan& p, const void* q, const void* k, float* scores,
                         float* raw, void* ws, size_t, hipStream_t st) {
-  TwoPassLayout o;
-  twopass_plan(p, &o);
-  return twopass_launch(p, o, q, k, scores, raw, ws, st);
+  if (window_applicable(p)) {
+    WindowLayout w;
+    window_plan(p, &w);
+    return window_launch(p, w, q, k, scores, raw, ws, st);
+  }
+  TwoPassLayout t;
+  twopass_plan(p, &t);
+  return twopass_launch(p, t, q, k, scores, raw, ws, st);
 }
 
 }  // namespace kvsel

@@ -163,6 +163,20 @@ __global__ __launch_bounds__(256) void k_pool(const float* __restrict__ raw, int
 
 // ------------------------------------------------------------------ host ----
 
+hipError_t combine_launch(const float2* part, int L, int H, int R, int splits, float* stat,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_combine, dim3((R + 255) / 256, H, L), dim3(256), 0, st, part, H, R,
+                     splits, stat);
+  return hipGetLastError();
+}
+
+hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r, float* scores,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(k_pool, dim3((n_cand + 255) / 256, L * H), dim3(256), 0, st, raw, n,
+                     n_cand, r, scores);
+  return hipGetLastError();
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 void twopass_plan(const ScorePlan& p, TwoPassLayout* o) {

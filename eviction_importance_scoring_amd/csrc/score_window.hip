@@ -1,0 +1,286 @@
+// Window-mode scoring, two streaming passes over K ([CriticalKV] §3.3
+// Algorithm 2 steps 2-3; the row softmax runs along keys and the aggregate
+// along queries, [KVzip] §3.4, so the normaliser of every row is needed
+// before any key's weight).
+//
+// Both kernels serve R = G*W <= 128 query rows per KV head. A workgroup
+// owns a range of keys of one (layer, KV head); its 4 waves split the rows
+// (wave w: rows 32w..32w+31, held as MFMA operands in registers for the
+// whole kernel) and all consume the same K tiles. K streams from HBM once
+// per pass through a ring of kSlots LDS slots of kTile keys each, filled by
+// direct global->LDS loads (global_load_lds_dwordx4): each instruction reads
+// 4 whole 256-byte rows, and the 16-byte pieces of row r are stored XOR-
+// swizzled by (r & 15), so the MFMA operand reads (one half row per lane)
+// are free of bank conflicts. kSlots-1 tiles are in flight at any time.
+// MFMA is 32x32x16 bf16 with fp32 accumulation.
+//
+//   pass 1 (k_win_stats): keys on the MFMA M side, rows on lanes; every lane
+//     keeps an online (max, sum of 2^(x - max)) for its row over the keys.
+//   pass 2 (k_win_colsum): rows on the M side, keys on lanes; every lane sums
+//     2^(x - c_r) (or takes the max of x - c_r) over its 16 rows of each key,
+//     then lane halves and waves are added in a fixed order through LDS.
+// Tiles whose keys every window query sees (all but the last tile or two of
+// a head) skip the causal mask.
+#include "kvsel_internal.h"
+#include "kvsel_kernels.h"
+
+namespace kvsel {
+
+constexpr int kTile = 64;                     // keys per ring slot (16 KB)
+constexpr int kSlots = 4;                     // ring depth
+constexpr int kLoadsPerTile = kTile * kRowBytes / (4 * 1024);   // per wave: 4
+constexpr float kNegBig = -1.0e30f;           // "no key seen yet"
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) const void* glb_ptr;
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
+// Workgroup barrier without a memory fence: the ring's LDS-DMA writes are
+// waited for explicitly (s_waitcnt vmcnt) before it, so the tiles still in
+// flight are not drained.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wait until at most (kSlots-2) tiles of this wave's loads are outstanding
+__device__ __forceinline__ void wait_ring() {
+  constexpr int n = (kSlots - 2) * kLoadsPerTile;
+  static_assert(n < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(n | (7 << 4) | (15 << 8));
+}
+
+// Issue this wave's share (kLoadsPerTile instructions of 1 KB) of the tile
+// of keys [key0, key0 + kTile) into `slot`. Keys >= n read row n-1 (never
+// used). LDS layout: row r at r*256, piece p at ((p ^ (r & 15)) * 16).
+__device__ __forceinline__ void load_tile(const __bf16* kh, int key0, int n, unsigned char* slot) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kLoadsPerTile; ++i) {
+    const int chunk = wave * kLoadsPerTile + i;          // 1 KB = 4 rows
+    const int r = chunk * 4 + (lane >> 4);
+    const int piece = (lane & 15) ^ (r & 15);
+    const int key = min(key0 + r, n - 1);
+    const char* src = reinterpret_cast<const char*>(kh + (size_t)key * kHeadDim) + piece * 16;
+    __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(slot + chunk * 1024), 16, 0, 0);
+  }
+}
+
+// MFMA operand (step s) of key row r (0..kTile-1) for lane half hf.
+__device__ __forceinline__ bf16x8 tile_op(const unsigned char* slot, int r, int hf, int s) {
+  return ld16(slot + r * kRowBytes + (((hf * 8 + s) ^ (r & 15)) << 4));
+}
+
+struct RingShared {
+  unsigned char ring[kSlots][kTile * kRowBytes];
+};
+
+// ---------------------------------------------------------------- pass 1 ----
+// grid (blocks, H, L); keys [b*kpb, min(n, (b+1)*kpb)); part[lh][b][row].
+__global__ __launch_bounds__(256) void k_win_stats(const __bf16* __restrict__ q,
+                                                   const __bf16* __restrict__ k, int H, int R,
+                                                   int W, int n, float alpha, int blocks,
+                                                   int kpb, float2* __restrict__ part) {
+  __shared__ __align__(16) RingShared sm;
+  const int b = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+  const size_t lh = (size_t)l * H + h;
+  const __bf16* kh = k + lh * (size_t)n * kHeadDim;
+  const int j0 = b * kpb, j1 = min(n, j0 + kpb);
+  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+
+#pragma unroll
+  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
+
+  const int row = wave * 32 + col;
+  const bool active = wave * 32 < R;       // wave has rows (uniform)
+  bf16x8 qb[8];
+  if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qb);
+  else zero_ops(qb);
+  const int last = row < R ? n - W + row % W : -1;   // last key this row sees
+  const int open_end = n - W;                        // every row sees keys <= this
+  float m = kNegBig, s = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_ring();
+    ring_barrier();
+    load_tile(kh, j0 + min(t + kSlots - 1, ntiles - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
+    if (!active) continue;
+    const unsigned char* slot = sm.ring[t % kSlots];
+    const int kt = j0 + t * kTile;
+    f32x16 acc0 = zero16(), acc1 = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      acc0 = mfma32(tile_op(slot, col, hf, st), qb[st], acc0);
+      acc1 = mfma32(tile_op(slot, 32 + col, hf, st), qb[st], acc1);
+    }
+    if (!(kt + kTile - 1 <= open_end && kt + kTile <= j1)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k0 = kt + acc_row(i, lane), k1 = k0 + 32;
+        if (!(k0 <= last && k0 < j1)) acc0[i] = -__builtin_inff();
+        if (!(k1 <= last && k1 < j1)) acc1[i] = -__builtin_inff();
+      }
+    }
+    float tm = max3f(acc0[0], acc0[1], acc0[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) tm = max3f(tm, acc0[i], acc0[i + 1]);
+    tm = max3f(tm, acc0[15], acc1[0]);
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) tm = max3f(tm, acc1[i], acc1[i + 1]);
+    tm = __builtin_fmaxf(tm, acc1[15]);
+    const float mn = __builtin_fmaxf(m, tm * alpha);
+    float sum = s * fast_exp2(m - mn);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sum += fast_exp2(__builtin_fmaf(acc0[i], alpha, -mn));
+      sum += fast_exp2(__builtin_fmaf(acc1[i], alpha, -mn));
+    }
+    s = sum;
+    m = mn;
+  }
+  // the other lane half saw the other 16 keys of every 32-key sub-tile
+  const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(s, 32);
+  lse_merge(m, s, m2, s2);
+  if (hf == 0 && row < R) part[(lh * blocks + b) * (size_t)R + row] = make_float2(m, s);
+}
+
+// ---------------------------------------------------------------- pass 2 ----
+// grid (blocks, H, L); raw[lh][key] = sum_r 2^(x - c_r), or 2^(max_r (x - c_r)).
+template <bool MAXAGG>
+__global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q,
+                                                    const __bf16* __restrict__ k, int H, int R,
+                                                    int W, int n, float alpha,
+                                                    const float* __restrict__ stat, int kpb,
+                                                    float* __restrict__ raw) {
+  __shared__ __align__(16) RingShared sm;
+  __shared__ float colbuf[2][4][kTile];
+  const int b = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const size_t lh = (size_t)l * H + h;
+  const __bf16* kh = k + lh * (size_t)n * kHeadDim;
+  const int j0 = b * kpb, j1 = min(n, j0 + kpb);
+  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+
+#pragma unroll
+  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
+
+  const bool active = wave * 32 < R;
+  bf16x8 qa[8];
+  {
+    const int row = wave * 32 + col;
+    if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qa);
+    else zero_ops(qa);
+  }
+  float cr[16];
+  int wq[16];            // window index of each of this lane's 16 rows
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = wave * 32 + acc_row(i, lane);
+    cr[i] = row < R ? stat[lh * R + row] : __builtin_inff();   // padded rows weigh 0
+    wq[i] = row % W;
+  }
+  const int open_end = n - W;
+  const float ident = MAXAGG ? -__builtin_inff() : 0.f;
+
+  for (int t = 0; t <= ntiles; ++t) {
+    if (t < ntiles) wait_ring();
+    ring_barrier();
+    // reduce the previous tile's per-wave column partials
+    if (t > 0 && tid < kTile) {
+      const int key = j0 + (t - 1) * kTile + tid;
+      const float* cb = &colbuf[(t - 1) & 1][0][0];
+      float v;
+      if (MAXAGG) v = fast_exp2(__builtin_fmaxf(__builtin_fmaxf(cb[tid], cb[kTile + tid]),
+                                                __builtin_fmaxf(cb[2 * kTile + tid], cb[3 * kTile + tid])));
+      else v = (cb[tid] + cb[kTile + tid]) + (cb[2 * kTile + tid] + cb[3 * kTile + tid]);
+      if (key < j1) raw[lh * n + key] = v;
+    }
+    if (t == ntiles) break;
+    load_tile(kh, j0 + min(t + kSlots - 1, ntiles - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
+    const unsigned char* slot = sm.ring[t % kSlots];
+    const int kt = j0 + t * kTile;
+    const bool open = kt + kTile - 1 <= open_end;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float agg = ident;
+      if (active) {
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int st = 0; st < 8; ++st) acc = mfma32(qa[st], tile_op(slot, nt * 32 + col, hf, st), acc);
+        const int key = kt + nt * 32 + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = __builtin_fmaf(acc[i], alpha, -cr[i]);
+          if (!open && key > n - W + wq[i]) x = -__builtin_inff();
+          if (MAXAGG) agg = __builtin_fmaxf(agg, x);
+          else agg += fast_exp2(x);
+        }
+      }
+      const float o = __shfl_xor(agg, 32);
+      if (hf == 0) colbuf[t & 1][wave][nt * 32 + col] = MAXAGG ? __builtin_fmaxf(agg, o) : agg + o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host ----
+
+static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool window_applicable(const ScorePlan& p) { return p.causal && p.R <= 128; }
+
+static int win_keys_per_block(const ScorePlan& p) {
+  // >= ~2048 workgroups per pass when the cache is large; kTile granularity
+  const long long heads = (long long)p.L * p.H;
+  long long kpb = ((long long)p.n * heads + 2047) / 2048;
+  kpb = (kpb + kTile - 1) / kTile * kTile;
+  if (kpb < 2 * kTile) kpb = 2 * kTile;
+  if (kpb > 4096) kpb = 4096;
+  return (int)kpb;
+}
+
+void window_plan(const ScorePlan& p, WindowLayout* o) {
+  const int kpb = win_keys_per_block(p);
+  o->kpb = kpb;
+  o->blocks = (p.n + kpb - 1) / kpb;
+  const size_t LH = (size_t)p.L * p.H;
+  o->part_off = 0;
+  o->stat_off = al256(LH * o->blocks * p.R * sizeof(float2));
+  o->raw_off = o->stat_off + al256(LH * p.R * sizeof(float));
+  o->bytes = o->raw_off + (p.need_raw_tmp ? al256(LH * p.n * sizeof(float)) : 0);
+}
+
+hipError_t combine_launch(const float2* part, int L, int H, int R, int splits, float* stat,
+                          hipStream_t st);
+hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r, float* scores,
+                       hipStream_t st);
+
+hipError_t window_launch(const ScorePlan& p, const WindowLayout& o, const void* q, const void* k,
+                         float* scores, float* raw, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  float2* part = reinterpret_cast<float2*>(w + o.part_off);
+  float* stat = reinterpret_cast<float*>(w + o.stat_off);
+  float* rawbuf = raw ? raw : reinterpret_cast<float*>(w + o.raw_off);
+  const __bf16* qb = static_cast<const __bf16*>(q);
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  const float alpha = p.scale * kLog2e;
+  dim3 grid(o.blocks, p.H, p.L);
+  hipLaunchKernelGGL(k_win_stats, grid, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n, alpha,
+                     o.blocks, o.kpb, part);
+  (void)combine_launch(part, p.L, p.H, p.R, o.blocks, stat, st);
+  if (p.max_agg)
+    hipLaunchKernelGGL(k_win_colsum<true>, grid, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n,
+                       alpha, stat, o.kpb, rawbuf);
+  else
+    hipLaunchKernelGGL(k_win_colsum<false>, grid, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n,
+                       alpha, stat, o.kpb, rawbuf);
+  (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -47,6 +47,12 @@ WINDOW_CASES = [
     dict(n=300, W=16, pool=5, agg="max"),
     dict(n=1500, W=40, G=4),               # R = 160 rows: more than one row block
     dict(n=4096, W=32, heavy="uniform1pct"),
+    # one-pass kernel: chunk boundaries (256 keys) against pool halos
+    dict(n=513, W=1, G=1, pool=17),
+    dict(n=768, W=32, pool=7),             # candidates end inside a chunk
+    dict(n=771, W=3, G=4, pool=9),         # 4 chunks, last chunk 3 keys
+    dict(L=3, H_kv=2, n=2048, W=8, G=8),   # R = 64
+    dict(n=1000, W=30, G=3, pool=1),       # R = 90, no pooling
 ]
 
 
