@@ -60,34 +60,46 @@ def traffic_from_profiles(key, sha):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(wl, host, seconds):
-    """Oracle (fp64 numpy) on whole layers of the same inputs, one after the
-    other, until `seconds` of CPU work; reported in entries/s."""
+def cpu_baseline(wl, host, seconds, w_host=None):
+    """The oracle (fp64 numpy) on the same inputs, one (layer, KV head) at a
+    time in order, until `seconds` of CPU work: attention scores, max-pool,
+    the value weight when the workload uses it, and top-k selection.
+    Reported in KV entries per second."""
     import numpy as np
 
     import oracle
     import synth
     from threadpoolctl import threadpool_info
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    done = 0
+    units = 0
     t0 = time.perf_counter()
-    for l in range(wl.L):
-        q = synth.bf16_to_f64(host["q"][l])
-        k = synth.bf16_to_f64(host["k"][l])
-        if wl.q_mode == "window":
-            raw = oracle.window_raw_scores(q, k, wl.G, wl.scale, wl.agg)
-        else:
-            raw = oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg)
-        pooled = oracle.maxpool(raw, wl.n_cand, wl.pool)
-        oracle.select_layer(pooled, wl.budget, wl.W_kept, wl.n, adaptive=wl.adaptive)
-        done += 1
+    for l in range(min(wl.L, host["q"].shape[0])):
+        for h in range(wl.H_kv):
+            q = synth.bf16_to_f64(host["q"][l][h * wl.G:(h + 1) * wl.G])
+            k = synth.bf16_to_f64(host["k"][l][h:h + 1])
+            if wl.q_mode == "window":
+                raw = oracle.window_raw_scores(q, k, wl.G, wl.scale, wl.agg)
+            else:
+                raw = oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg)
+            pooled = oracle.maxpool(raw, wl.n_cand, wl.pool)
+            weight = None
+            if wl.value_weight and w_host is not None:
+                v = synth.bf16_to_f64(host["v"][l][h:h + 1])
+                wo = synth.bf16_to_f64(w_host[l][:, h * wl.G * wl.d:(h + 1) * wl.G * wl.d])
+                weight = oracle.value_weight(v, wo, wl.G, np.arange(wl.n_cand))
+            oracle.select_layer(pooled, wl.budget if not wl.adaptive else wl.budget // wl.H_kv,
+                                wl.W_kept, wl.n, weight=weight, alpha=wl.alpha,
+                                score_norm=1.0 / (wl.W * wl.G), eps=wl.eps)
+            units += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": done * wl.H_kv * wl.n / dt, "unit": "entries/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} of {wl.L} layers of {wl.name}: window scores, max-pool and "
-                      f"top-k selection in fp64 numpy ({dt:.1f} s)"}
+    what = "scores, max-pool" + (", value weight" if wl.value_weight else "") + " and top-k selection"
+    return {"value": units * wl.n / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{units} (layer, KV head) pairs of {wl.name} in order from layer 0: "
+                      f"{what} in fp64 numpy ({dt:.1f} s)"}
 
 
 def main():
@@ -99,6 +111,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw the inputs on the GPU (default for caches above 4 GB)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -114,18 +130,31 @@ def main():
     import eviction_importance_scoring_amd as kv
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    log(f"[bench] generating {wl.name} (seed {args.seed})")
+    if args.copy_calibration:
+        # a plain copy of known size: reads and writes exactly 1 GiB each
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}), flush=True)
+        return
+    wl = synth.WORKLOADS[args.workload]
     which = ("q", "k", "v", "w_o") if wl.value_weight else ("q", "k", "v")
+    cache_bytes = wl.L * wl.H_kv * wl.n * wl.d * 2 * 2
     t0 = time.time()
-    host = synth.gen_all(wl, args.seed, which)
-    log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
-
-    def up(u):
-        return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    t = {name: up(a) for name, a in host.items()}
+    if args.device_inputs or cache_bytes > (4 << 30):
+        log(f"[bench] drawing {wl.name} on the GPU (seed {args.seed})")
+        t = synth.gen_all_device(wl, args.seed, which, dev)
+        host = None
+    else:
+        log(f"[bench] generating {wl.name} on the host (seed {args.seed})")
+        host = synth.gen_all(wl, args.seed, which)
+        t = {name: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+             for name, a in host.items()}
+    torch.cuda.synchronize(dev)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
     q, k, v = t["q"], t["k"], t["v"]
     w_o = t.get("w_o")
     mode = kv.Q_WINDOW if wl.q_mode == "window" else kv.Q_EXTERNAL
@@ -216,9 +245,25 @@ def main():
         "scored_selected_entries_per_s": entries / ((ms_score + ms_sel) * 1e-3),
         "wall_s_timed": wall,
     }
+    if wl.value_weight:
+        vw_flops = 2.0 * wl.L * wl.H_kv * wl.n_cand * wl.G * wl.D * wl.d
+        out["value_weight_mfma"] = {"tflops": vw_flops / (ms_vw * 1e-3) / 1e12,
+                                    "peak": MFMA_BF16_PEAK_TFS,
+                                    "frac": vw_flops / (ms_vw * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
+    if wl.q_mode == "external":
+        sc_flops = 2 * 2.0 * wl.L * wl.H_q * wl.W * wl.n * wl.d   # two passes of Q K^T
+        out["score_mfma"] = {"tflops": sc_flops / (ms_score * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFS,
+                             "frac": sc_flops / (ms_score * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
+        if host is None:   # bring back the first layers, which the sample uses
+            nl = min(wl.L, 2)
+            host = {name: t[name][:nl].cpu().view(torch.int16).numpy().view(np.uint16)
+                    for name in t if name != "w_o"}
+        w_host = None
+        if wl.value_weight:
+            w_host = t["w_o"][:2].cpu().view(torch.int16).numpy().view(np.uint16)
+        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds, w_host)
     print(json.dumps(out), flush=True)
 
 

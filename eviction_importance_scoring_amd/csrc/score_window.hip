@@ -27,9 +27,11 @@
 namespace kvsel {
 
 constexpr int kTile = 64;                     // keys per ring slot (16 KB)
-constexpr int kSlots = 4;                     // ring depth
-constexpr int kLoadsPerTile = kTile * kRowBytes / (4 * 1024);   // per wave: 4
+constexpr int kSlots = 3;                     // ring depth (3 keeps 3 workgroups per CU)
+constexpr int kSub = kTile / 32;              // 32-key MFMA sub-tiles per slot
+constexpr int kLoadsPerTile = kTile * kRowBytes / (4 * 1024);   // per wave
 constexpr float kNegBig = -1.0e30f;           // "no key seen yet"
+constexpr int kNonTemporal = 2;               // cache-policy bit: K is read once per pass
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) const void* glb_ptr;
@@ -66,7 +68,7 @@ __device__ __forceinline__ void load_tile(const __bf16* kh, int key0, int n, uns
     const int piece = (lane & 15) ^ (r & 15);
     const int key = min(key0 + r, n - 1);
     const char* src = reinterpret_cast<const char*>(kh + (size_t)key * kHeadDim) + piece * 16;
-    __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(slot + chunk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(slot + chunk * 1024), 16, 0, kNonTemporal);
   }
 }
 
@@ -112,34 +114,33 @@ __global__ __launch_bounds__(256) void k_win_stats(const __bf16* __restrict__ q,
     if (!active) continue;
     const unsigned char* slot = sm.ring[t % kSlots];
     const int kt = j0 + t * kTile;
-    f32x16 acc0 = zero16(), acc1 = zero16();
+    f32x16 acc[kSub];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      acc0 = mfma32(tile_op(slot, col, hf, st), qb[st], acc0);
-      acc1 = mfma32(tile_op(slot, 32 + col, hf, st), qb[st], acc1);
-    }
+    for (int u = 0; u < kSub; ++u) acc[u] = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) acc[u] = mfma32(tile_op(slot, u * 32 + col, hf, st), qb[st], acc[u]);
     if (!(kt + kTile - 1 <= open_end && kt + kTile <= j1)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int k0 = kt + acc_row(i, lane), k1 = k0 + 32;
-        if (!(k0 <= last && k0 < j1)) acc0[i] = -__builtin_inff();
-        if (!(k1 <= last && k1 < j1)) acc1[i] = -__builtin_inff();
-      }
+      for (int u = 0; u < kSub; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = kt + u * 32 + acc_row(i, lane);
+          if (!(kk <= last && kk < j1)) acc[u][i] = -__builtin_inff();
+        }
     }
-    float tm = max3f(acc0[0], acc0[1], acc0[2]);
+    float tm = -__builtin_inff();
 #pragma unroll
-    for (int i = 3; i < 15; i += 2) tm = max3f(tm, acc0[i], acc0[i + 1]);
-    tm = max3f(tm, acc0[15], acc1[0]);
+    for (int u = 0; u < kSub; ++u)
 #pragma unroll
-    for (int i = 1; i < 15; i += 2) tm = max3f(tm, acc1[i], acc1[i + 1]);
-    tm = __builtin_fmaxf(tm, acc1[15]);
+      for (int i = 0; i < 16; i += 2) tm = max3f(tm, acc[u][i], acc[u][i + 1]);
     const float mn = __builtin_fmaxf(m, tm * alpha);
     float sum = s * fast_exp2(m - mn);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sum += fast_exp2(__builtin_fmaf(acc0[i], alpha, -mn));
-      sum += fast_exp2(__builtin_fmaf(acc1[i], alpha, -mn));
-    }
+    for (int u = 0; u < kSub; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(acc[u][i], alpha, -mn));
     s = sum;
     m = mn;
   }
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q
     const int kt = j0 + t * kTile;
     const bool open = kt + kTile - 1 <= open_end;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kSub; ++nt) {
       float agg = ident;
       if (active) {
         f32x16 acc = zero16();

@@ -195,3 +195,46 @@ def gen_all(wl: Workload, seed: int, which=("q", "k", "v", "w_o")) -> dict:
     """All layers stacked on a leading L axis (uint16 bf16 bit patterns)."""
     per = [gen_layer(wl, seed, l, which) for l in range(wl.L)]
     return {key: np.stack([p[key] for p in per]) for key in per[0]}
+
+
+# ------------------------------------------------------- device generator ----
+
+def gen_all_device(wl: Workload, seed: int, which=("q", "k", "v", "w_o"), device="cuda"):
+    """Same shapes and distributions as gen_all, drawn on the GPU with torch's
+    seeded generator (not bit-identical to the host draws). For workloads
+    too large to draw on the host in reasonable time."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + (zlib.crc32(wl.name.encode()) & 0xFFFF))
+    out = {}
+
+    def normal(shape, std=1.0):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        for l in range(shape[0]):
+            t[l] = (torch.randn(shape[1:], generator=g, device=device) * std).to(torch.bfloat16)
+        return t
+
+    if "q" in which:
+        out["q"] = normal((wl.L, wl.H_q, wl.W, wl.d))
+    if "k" in which:
+        k = torch.empty((wl.L, wl.H_kv, wl.n, wl.d), dtype=torch.bfloat16, device=device)
+        n_pool = wl.n - wl.W if wl.q_mode == "window" else wl.n
+        for l in range(wl.L):
+            x = torch.randn((wl.H_kv, wl.n, wl.d), generator=g, device=device)
+            f = torch.ones((wl.H_kv, wl.n), device=device)
+            for h in range(wl.H_kv):
+                if wl.heavy == "uniform1pct":
+                    pos = torch.randperm(n_pool, generator=g, device=device)[: int(0.01 * wl.n)]
+                    f[h, pos] = 4.0
+                elif wl.heavy == "zipf":
+                    perm = torch.randperm(n_pool, generator=g, device=device)
+                    rank = torch.arange(1, n_pool + 1, device=device, dtype=torch.float64)
+                    f[h, perm] = (1.0 + 3.0 * rank ** -1.1).to(torch.float32)
+            k[l] = (x * f[:, :, None]).to(torch.bfloat16)
+        out["k"] = k
+    if "v" in which and (wl.value_weight or wl.compact):
+        out["v"] = normal((wl.L, wl.H_kv, wl.n, wl.d))
+    if "w_o" in which and wl.value_weight:
+        out["w_o"] = normal((wl.L, wl.D, wl.H_q * wl.d), 0.02)
+    return out
