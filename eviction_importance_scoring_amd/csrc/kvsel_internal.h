@@ -66,6 +66,20 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// ----------------------------------------------------------- dispatch ----
+//
+// The command processor hands workgroup w of a 1-D grid to XCD w % 8, and
+// each XCD has its own L2. Workgroups that re-read the same operand should
+// share an L2, so a kernel works on the logical index returned here: the
+// workgroups of one XCD take one contiguous logical range (a bijection on
+// [0, total)).
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int q = total / kXcds, r = total % kXcds, x = w % kXcds;
+  return x * q + min(x, r) + w / kXcds;
+}
+
 // ---------------------------------------------------------------- math ----
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

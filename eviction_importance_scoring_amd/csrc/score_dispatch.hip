@@ -2,19 +2,23 @@
 //
 // Window mode with R = G*W <= 128 query rows per KV head uses the streaming
 // window kernels (score_window.hip); external queries and larger R use the
-// general two-pass kernels (score_twopass.hip). The workspace is the larger
-// of the two layouts, so a size query needs no device.
+// general two-pass kernels (score_twopass.hip). The choice depends on the
+// shapes alone, so the workspace is sized for the chosen kernels and a size
+// query needs no device.
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
 
 namespace kvsel {
 
 size_t score_ws_bytes(const ScorePlan& p) {
+  if (window_applicable(p)) {
+    WindowLayout w;
+    window_plan(p, &w);
+    return w.bytes;
+  }
   TwoPassLayout t;
   twopass_plan(p, &t);
-  WindowLayout w;
-  window_plan(p, &w);
-  return t.bytes > w.bytes ? t.bytes : w.bytes;
+  return t.bytes;
 }
 
 hipError_t score_launch(const ScorePlan& p, const void* q, const void* k, float* scores,

@@ -1,83 +1,325 @@
-// Two-pass attention scoring: exact softmax weights aggregated per key.
-//
-// [CriticalKV] §3.3 Algorithm 2 steps 2-4 (window scores, then max-pool) and
-// [KVzip] §3.2 (max over the group queries of the softmax weight). The row
-// softmax runs over keys while the aggregate runs over queries ([KVzip] §3.4
-// names this cross-dimension dependence), so the exact weight needs each
-// row's normaliser over all keys before any column can be summed:
-//   pass 1  per query row r: m_r = max_j x_rj, l_r = sum_j 2^(x_rj - m_r),
-//           with x = log2(e) * scale * <q_r, k_j>; split over key ranges.
-//   combine c_r = m_r + log2(l_r) over the key ranges (fixed order).
-//   pass 2  per key j: sum_r 2^(x_rj - c_r)  or  2^(max_r (x_rj - c_r)).
+// General two-pass attention scoring for any number R of query rows per KV
+// head: KVzip's many external queries ([KVzip] §3.2, max over the group
+// queries of the softmax weight), and window scoring with R = G*W > 128
+// ([CriticalKV] §3.3 Algorithm 2 steps 2-4). The row softmax runs along the
+// keys while the aggregate runs along the queries ([KVzip] §3.4 names this
+// cross-dimension dependence), so every row's normaliser is needed before
+// any key's aggregate:
+//   pass 1  k_gen_stats   per row r: m_r = max_j x_rj, l_r = sum_j 2^(x_rj - m_r),
+//                         x = log2(e) * scale * <q_r, k_j>; c_r = m_r + log2 l_r.
+//   pass 2  k_gen_colagg  per key j: sum_r 2^(x_rj - c_r), or 2^(max_r (x_rj - c_r)).
 //   pool    max over +-pool/2 neighbours inside the candidate range.
-// Both passes run the Q K^T products on MFMA (32x32x16 bf16, fp32 accum).
-// Pass 1 puts queries on lanes so the per-row max/sum stays in-lane; pass 2
-// puts keys on lanes so the per-key sum/max over rows stays in-lane.
+// Both passes are dense Q K^T contractions on MFMA (32x32x16 bf16, fp32
+// accumulation) built for operand reuse:
+//   pass 1: a workgroup of 8 waves owns 512 rows (a wave: 64 rows, two MFMA
+//     N tiles, Q operands in registers) and streams K in 64-key tiles
+//     through an LDS ring shared by the 8 waves. Rows sit on lanes, so the
+//     online max / sum stays in-lane.
+//   pass 2: a workgroup owns 512 keys (a wave: 64 keys in registers) and
+//     streams Q in 64-row tiles through the ring, each with its 64 c_r.
+//     The accumulators start at -c_r / (log2(e) * scale), so the MFMA
+//     itself subtracts the normaliser and max aggregation costs one max
+//     per element.
+// Ring slots are filled by direct global->LDS loads, the 16-byte pieces of
+// row r XOR-swizzled by (r & 15); fence-free barriers keep the loads of the
+// next gSlots-1 tiles in flight. Workgroups are ordered so that those that
+// re-read one head's operand run on one XCD (one L2). Every row's and key's
+// result comes from one lane and a fixed-order merge: deterministic.
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
 
 namespace kvsel {
 
-// ---------------------------------------------------------------- pass 1 ----
-// grid (row_blocks * splits, H, L), block 256: 4 waves x 32 query rows.
-// Each wave streams 32-key tiles of its split; lane l owns query row
-// rb*128 + wave*32 + l%32 and, per tile, 16 of the 32 keys (by lane half).
-template <bool CAUSAL>
-__global__ __launch_bounds__(256) void k_rowstats(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, int H, int R,
-    int W, int n, float alpha, int splits, int keys_per_split,
-    float2* __restrict__ part) {
-  const int rb = blockIdx.x / splits, sp = blockIdx.x % splits;
-  const int h = blockIdx.y, l = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hf = lane >> 5, col = lane & 31;
-  const int row = rb * 128 + wave * 32 + col;
-  const size_t lh = (size_t)l * H + h;
-  const __bf16* qh = q + lh * (size_t)R * kHeadDim;
-  const __bf16* kh = k + lh * (size_t)n * kHeadDim;
+constexpr int gTile = 64;                                     // rows per ring slot (16 KB)
+constexpr int gSlots = 3;
+constexpr int gWaves = 8;
+constexpr int gBlock = gWaves * 64;                           // rows / keys per workgroup
+constexpr int gLoads = gTile * kRowBytes / (gWaves * 1024);   // 16-byte loads per lane per tile
+constexpr int gRowsBytes = gTile * kRowBytes;
+constexpr int gSlotBytes = gRowsBytes + gTile * 4;             // pass 2: rows + normalisers
+constexpr float gNegBig = -1.0e30f;
+static_assert(gSlots >= 2, "ring depth");
 
-  bf16x8 b[8];
-  if (row < R) load_half_row(qh + (size_t)row * kHeadDim, hf, b);
-  else zero_ops(b);
-  // last key this row sees
-  const int vis = CAUSAL ? (n - W + (row % W)) : (n - 1);
-  const int j0 = sp * keys_per_split;
-  const int j1 = min(n, j0 + keys_per_split);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) const void* glb_ptr_t;
 
-  float m = neg_inf(), s = 0.f;
-  for (int kt = j0; kt < j1; kt += 32) {
-    bf16x8 a[8];
-    const int key = kt + col;
-    if (key < n) load_half_row(kh + (size_t)key * kHeadDim, hf, a);
-    else zero_ops(a);
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int st = 0; st < 8; ++st) acc = mfma32(a[st], b[st], acc);
-    float x[16];
-    float tmax = neg_inf();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kj = kt + acc_row(i, lane);
-      const bool ok = kj < j1 && kj <= vis;
-      x[i] = ok ? acc[i] * alpha : neg_inf();
-      tmax = fmaxf(tmax, x[i]);
-    }
-    const float mn = fmaxf(m, tmax);
-    if (mn != neg_inf()) {
-      float t = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) t += fast_exp2(x[i] - mn);
-      s = s * fast_exp2(m - mn) + t;
-      m = mn;
-    }
-  }
-  // the other lane half holds the other 16 keys of every tile
-  const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(s, 32);
-  lse_merge(m, s, m2, s2);
-  if (hf == 0 && row < R) part[(lh * splits + sp) * (size_t)R + row] = make_float2(m, s);
+// Workgroup barrier without the vmcnt(0) that __syncthreads implies (the
+// ring's loads stay in flight across it); LDS visibility comes from the
+// explicit waits below.
+__device__ __forceinline__ void gen_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// c_r = m_r + log2(l_r) over the splits, in split order.
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (vmcnt is 6 bits: low 4 in [3:0], high 2 in [15:14]).
+template <int N>
+__device__ __forceinline__ void gen_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int PER, int A>
+__device__ __forceinline__ void gen_wait_ahead(int ahead) {
+  if constexpr (A == 0) {
+    gen_wait<0>();
+  } else {
+    if (ahead >= A) gen_wait<A * PER>();
+    else gen_wait_ahead<PER, A - 1>(ahead);
+  }
+}
+
+// Wait for this wave's loads of tile t (PER loads per tile). The prologue
+// issues gSlots-1 tile loads (repeating the last tile when there are fewer
+// tiles) and iteration t' issues tile t'+gSlots-1 when it exists, all in
+// order; the loads issued after tile t's may stay in flight.
+template <int PER>
+__device__ __forceinline__ void gen_wait_tile(int t, int ntiles) {
+  const int issued = gSlots - 1 + max(0, min(t, ntiles - gSlots + 1));
+  gen_wait_ahead<PER, gSlots - 2>(issued - (t + 1));
+}
+
+// This wave's share of rows [row0, row0 + 64) of a [rows][128] bf16 matrix
+// into `slot` (rows past the end repeat row rows-1 and are never used).
+__device__ __forceinline__ void gen_load_tile(const __bf16* base, int row0, int rows,
+                                              unsigned char* slot) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < gLoads; ++i) {
+    const int chunk = wave * gLoads + i;
+    const int r = chunk * 4 + (lane >> 4);
+    const int piece = (lane & 15) ^ (r & 15);
+    const int row = min(row0 + r, rows - 1);
+    const char* src = reinterpret_cast<const char*>(base + (size_t)row * kHeadDim) + piece * 16;
+    __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(slot + chunk * 1024), 16, 0, 0);
+  }
+}
+
+// MFMA operand of step s, lane half hf, for row r of a ring slot.
+__device__ __forceinline__ bf16x8 gen_op(const unsigned char* slot, int r, int hf, int s) {
+  return ld16(slot + r * kRowBytes + (((hf * 8 + s) ^ (r & 15)) << 4));
+}
+
+__device__ __forceinline__ float gmax3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
+// MFMA step st of one 64-row ring tile against this wave's two 32-column
+// operand sets: acc[mt][nt] += (slot rows [32mt, 32mt + 32)) x b[nt], over
+// head-dim slice st. a[] holds the step's two row operands.
+__device__ __forceinline__ void tile_step(const bf16x8 (&a)[2], const bf16x8 (&b)[2][8], int st,
+                                          f32x16 (&acc)[2][2]) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    acc[0][nt] = mfma32(a[0], b[nt][st], acc[0][nt]);
+    acc[1][nt] = mfma32(a[1], b[nt][st], acc[1][nt]);
+  }
+}
+
+__device__ __forceinline__ void read_step(const unsigned char* slot, int col, int hf, int st,
+                                          bf16x8 (&a)[2]) {
+  a[0] = gen_op(slot, col, hf, st);
+  a[1] = gen_op(slot, 32 + col, hf, st);
+}
+
+// ---------------------------------------------------------------- pass 1 ----
+// 1-D grid of row_blocks * splits * H * L workgroups, block 512.
+// part[lh][sp][row] = (m, l) of the row over split sp's keys.
+//
+// Software pipelined: the 8 MFMA steps of tile t are interleaved with the
+// vector work of tile t-1 (two accumulator sets in turn), an eighth of it
+// after each step, so the matrix and vector units run side by side.
+// The vector work is the bound here (an exponential costs a quarter-rate
+// issue slot), so it is kept to one FMA, one exp2 and one add per logit:
+// a tile's exponentials use the running offset m from before the tile, and
+// the tile's max is only found (and the sum redone with a new offset) when
+// the tile's partial sum passes 2^64: on the first tile of a row, or when
+// its max jumps. A partial sum of at most 2^64 bounds every term, so the
+// kept sums stay far below fp32's limit (at most n * 2^64).
+constexpr float kHeadroomPow2 = 1.8446744e19f;   // 2^64
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
+                                                   const __bf16* __restrict__ k, int H, int R,
+                                                   int W, int n, float alpha, int row_blocks,
+                                                   int splits, int kps,
+                                                   float2* __restrict__ part) {
+  __shared__ __align__(16) unsigned char ring[gSlots][gTile * kRowBytes];
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int rb = id % row_blocks;
+  id /= row_blocks;
+  const int sp = id % splits;
+  id /= splits;
+  const int h = id % H, l = id / H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+  const size_t lh = (size_t)l * H + h;
+  const __bf16* kh = k + lh * (size_t)n * kHeadDim;
+  const int j0 = sp * kps, j1 = min(n, j0 + kps);
+  const int ntiles = (j1 - j0 + gTile - 1) / gTile;
+
+  const int row0 = rb * gBlock + wave * 64;
+  const bool active = row0 < R;
+  bf16x8 qb[2][8];
+  int last[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = row0 + nt * 32 + col;
+    if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qb[nt]);
+    else zero_ops(qb[nt]);
+    last[nt] = row < R ? (CAUSAL ? n - W + row % W : n - 1) : -1;   // last visible key
+  }
+  asm volatile("" ::: "memory");
+  // the first gSlots-1 tiles (repeating the last one if there are fewer)
+#pragma unroll
+  for (int t = 0; t < gSlots - 1; ++t)
+    gen_load_tile(kh, j0 + min(t, ntiles - 1) * gTile, n, ring[t]);
+  // Q is in registers once at most the prologue's loads are in flight; an
+  // explicit wait here keeps the compiler from waiting inside the loop
+  gen_wait<(gSlots - 1) * gLoads>();
+  // keys every row sees
+  const int open_end = CAUSAL ? n - W : n - 1;
+  float m[2] = {gNegBig, gNegBig}, s[2] = {0.f, 0.f};
+
+  // hide the keys a row does not see (tiles at the causal edge or the split end)
+  auto mask = [&](f32x16 (&acc)[2][2], int t) {
+    const int kt = j0 + t * gTile;
+    if (kt + gTile - 1 <= open_end && kt + gTile <= j1) return;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt + mt * 32 + acc_row(i, lane);
+          if (!(key <= last[nt] && key < j1)) acc[mt][nt][i] = neg_inf();
+        }
+  };
+  // part c (of 8) of a tile: 8 logits of row set nt = c / 4 into the
+  // tile's partial sum at offset m
+  auto fold_part = [&](const f32x16 (&acc)[2][2], int c, float (&ps)[2]) {
+    const int nt = c >> 2, mt = (c >> 1) & 1, i0 = (c & 1) * 8;
+    float sum = ps[nt];
+    const float off = -m[nt];
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) sum += fast_exp2(__builtin_fmaf(acc[mt][nt][i], alpha, off));
+    ps[nt] = sum;
+  };
+  // close a tile: accept its partial sums, or redo a row with a new offset
+  auto fold_end = [&](const f32x16 (&acc)[2][2], const float (&ps)[2]) {
+    // both rows' sums are taken unconditionally (before any branch), so the
+    // partial sums are computed where they were written, beside the MFMAs,
+    // rather than sunk towards a branch
+    const float s_old[2] = {s[0], s[1]};
+    s[0] = s_old[0] + ps[0];
+    s[1] = s_old[1] + ps[1];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (!(ps[nt] <= kHeadroomPow2)) {   // also catches an overflow to inf
+        float tm = neg_inf();
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) tm = gmax3(tm, acc[mt][nt][i], acc[mt][nt][i + 1]);
+        const float mn = __builtin_fmaxf(m[nt], tm * alpha);   // alpha > 0
+        float sum = s_old[nt] * fast_exp2(m[nt] - mn);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(acc[mt][nt][i], alpha, -mn));
+        s[nt] = sum;
+        m[nt] = mn;
+      }
+    }
+  };
+  auto begin_tile = [&](int t) -> const unsigned char* {
+    gen_wait_tile<gLoads>(t, ntiles);
+    gen_barrier();
+    if (t + gSlots - 1 < ntiles)
+      gen_load_tile(kh, j0 + (t + gSlots - 1) * gTile, n, ring[(t + gSlots - 1) % gSlots]);
+    // opaque offset: keeps the compiler from moving LDS reads across tiles
+    int qoff = 0;
+    asm volatile("" : "+v"(qoff));
+    return ring[t % gSlots] + qoff;
+  };
+  auto zero_acc = [&](f32x16 (&acc)[2][2]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+  };
+  // tile t into cur, interleaved with folding tile t-1 (prev)
+  auto step = [&](int t, f32x16 (&cur)[2][2], f32x16 (&prev)[2][2]) {
+    const unsigned char* slot = begin_tile(t);
+    if (!active) return;
+    mask(prev, t - 1);
+    float ps[2] = {0.f, 0.f};
+    zero_acc(cur);
+    bf16x8 a[2][2];
+    read_step(slot, col, hf, 0, a[0]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
+      tile_step(a[st & 1], qb, st, cur);
+      fold_part(prev, st, ps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // pin the partial sums here: otherwise the compiler sinks the second
+    // row set's folds past the first row set's branch, behind the MFMAs
+    asm volatile("" : "+v"(ps[0]), "+v"(ps[1]));
+    fold_end(prev, ps);
+  };
+  // fold a tile with no MFMA work beside it
+  auto fold_all = [&](f32x16 (&acc)[2][2], int t) {
+    mask(acc, t);
+    float ps[2] = {0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fold_part(acc, c, ps);
+    fold_end(acc, ps);
+  };
+
+  f32x16 A[2][2], B[2][2];
+  {
+    const unsigned char* slot = begin_tile(0);
+    if (active) {
+      zero_acc(A);
+      bf16x8 a[2][2];
+      read_step(slot, col, hf, 0, a[0]);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
+        tile_step(a[st & 1], qb, st, A);
+      }
+    }
+  }
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B, A);
+    step(t + 1, A, B);
+  }
+  if (t < ntiles) {
+    step(t, B, A);
+    if (active) fold_all(B, t);
+  } else if (active) {
+    fold_all(A, t - 1);
+  }
+  // with fewer tiles than the prologue's loads, repeats of the last tile may
+  // still be landing in LDS: let them finish before the workgroup ends
+  gen_wait<0>();
+  // the other lane half holds the other 16 keys of every 32-key block
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float m2 = __shfl_xor(m[nt], 32), s2 = __shfl_xor(s[nt], 32);
+    lse_merge(m[nt], s[nt], m2, s2);
+    const int row = row0 + nt * 32 + col;
+    if (hf == 0 && row < R) part[(lh * splits + sp) * (size_t)R + row] = make_float2(m[nt], s[nt]);
+  }
+}
+
+// c_r = m_r + log2(l_r) over the splits, in split order (the window
+// kernels' normaliser).
 __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part,
                                                  int H, int R, int splits,
                                                  float* __restrict__ stat) {
@@ -85,7 +327,7 @@ __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part
   const int h = blockIdx.y, l = blockIdx.z;
   if (r >= R) return;
   const size_t lh = (size_t)l * H + h;
-  float m = neg_inf(), s = 0.f;
+  float m = gNegBig, s = 0.f;
   for (int sp = 0; sp < splits; ++sp) {
     const float2 p = part[(lh * splits + sp) * (size_t)R + r];
     lse_merge(m, s, p.x, p.y);
@@ -93,51 +335,190 @@ __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part
   stat[lh * R + r] = m + __log2f(s);
 }
 
+// Pass 2's form of the normaliser: -c_r / alpha in rows of Rpad (a multiple
+// of the tile), padding rows -inf so they drop out of every aggregate.
+__global__ __launch_bounds__(256) void k_combine_neg(const float2* __restrict__ part,
+                                                     int H, int R, int Rpad, int splits,
+                                                     float inv_alpha,
+                                                     float* __restrict__ stat) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y, l = blockIdx.z;
+  if (r >= Rpad) return;
+  const size_t lh = (size_t)l * H + h;
+  if (r >= R) {
+    stat[lh * Rpad + r] = neg_inf();
+    return;
+  }
+  float m = gNegBig, s = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float2 p = part[(lh * splits + sp) * (size_t)R + r];
+    lse_merge(m, s, p.x, p.y);
+  }
+  stat[lh * Rpad + r] = -(m + __log2f(s)) * inv_alpha;
+}
+
 // ---------------------------------------------------------------- pass 2 ----
-// grid (ceil(n/128), H, L), block 256: 4 waves x 32 keys. Lane l owns key
-// kb*128 + wave*32 + l%32 and loops over all R query rows in tiles of 32;
-// per tile it holds 16 of the 32 rows (by lane half).
+// 1-D grid of key_blocks * H * L workgroups, block 512. raw[lh][key].
+// Pipelined like pass 1: the MFMAs of row tile t run beside the aggregation
+// of tile t-1, so the matrix pipe does not wait for the per-tile max / sum.
 template <bool CAUSAL, bool MAXAGG>
-__global__ __launch_bounds__(256) void k_colagg(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, int H, int R,
-    int W, int n, float alpha, const float* __restrict__ stat,
-    float* __restrict__ raw) {
-  const int kb = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hf = lane >> 5, col = lane & 31;
-  const int key = kb * 128 + wave * 32 + col;
+__global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q,
+                                                    const __bf16* __restrict__ k, int H, int R,
+                                                    int W, int n, float alpha, int key_blocks,
+                                                    const float* __restrict__ stat,
+                                                    float* __restrict__ raw) {
+  // one LDS object: slot = 64 Q rows, then their 64 normalisers (with two
+  // objects the compiler waits for every direct-to-LDS load before any read)
+  __shared__ __align__(16) unsigned char ring[gSlots][gSlotBytes];
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = id % key_blocks;
+  id /= key_blocks;
+  const int h = id % H, l = id / H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
   const size_t lh = (size_t)l * H + h;
   const __bf16* qh = q + lh * (size_t)R * kHeadDim;
-  const __bf16* kh = k + lh * (size_t)n * kHeadDim;
-  const float* sh = stat + lh * R;
+  const int ntiles = (R + gTile - 1) / gTile;
+  const float* sh = stat + lh * (size_t)ntiles * gTile;
 
-  bf16x8 b[8];
-  if (key < n) load_half_row(kh + (size_t)key * kHeadDim, hf, b);
-  else zero_ops(b);
-  float agg = MAXAGG ? neg_inf() : 0.f;
-  for (int rt = 0; rt < R; rt += 32) {
-    bf16x8 a[8];
-    const int qrow = rt + col;
-    if (qrow < R) load_half_row(qh + (size_t)qrow * kHeadDim, hf, a);
-    else zero_ops(a);
-    f32x16 acc = zero16();
+  // this wave's 64 keys: MFMA B operands for the whole kernel
+  const int key0 = kb * gBlock + wave * 64;
+  bf16x8 kop[2][8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) acc = mfma32(a[st], b[st], acc);
+  for (int nt = 0; nt < 2; ++nt) {
+    const int key = key0 + nt * 32 + col;
+    if (key < n) load_half_row(k + (lh * n + key) * (size_t)kHeadDim, hf, kop[nt]);
+    else zero_ops(kop[nt]);
+  }
+  // a row tile: the Q rows (all waves) and their -c_r / alpha (wave 0)
+  auto issue = [&](int t, int slot) {
+    gen_load_tile(qh, t * gTile, R, ring[slot]);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(sh + t * gTile + lane),
+                                       (lds_ptr_t)(ring[slot] + gRowsBytes), 4, 0, 0);
+  };
+  asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = rt + acc_row(i, lane);
-      bool ok = r < R;
-      if (CAUSAL) ok = ok && key <= n - W + (r % W);
-      const float c = sh[min(r, R - 1)];
-      const float x = acc[i] * alpha - c;
-      if (MAXAGG) agg = ok ? fmaxf(agg, x) : agg;
-      else agg += ok ? fast_exp2(x) : 0.f;
+  for (int t = 0; t < gSlots - 1; ++t) issue(min(t, ntiles - 1), t);
+  // K operands are in registers once at most the prologue's loads remain
+  if (wave == 0) gen_wait<(gSlots - 1) * (gLoads + 1)>();
+  else gen_wait<(gSlots - 1) * gLoads>();
+
+  float agg[2];
+  agg[0] = agg[1] = MAXAGG ? neg_inf() : 0.f;
+  const bool any_key = key0 < n;
+
+  auto begin_tile = [&](int t) -> const unsigned char* {
+    if (wave == 0) gen_wait_tile<gLoads + 1>(t, ntiles);
+    else gen_wait_tile<gLoads>(t, ntiles);
+    gen_barrier();
+    if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
+    int qoff = 0;
+    asm volatile("" : "+v"(qoff));
+    return ring[t % gSlots] + qoff;
+  };
+  // acc = <q_r, k> - c_r / alpha: start from the tile's normalisers
+  // (padding rows: -inf)
+  auto init_acc = [&](const unsigned char* slot, f32x16 (&acc)[2][2]) {
+    const float* cs = reinterpret_cast<const float*>(slot + gRowsBytes);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16 init;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(cs + mt * 32 + 8 * j + 4 * hf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) init[4 * j + u] = c4[u];
+      }
+      acc[mt][0] = init;
+      acc[mt][1] = init;
+    }
+  };
+  // window rows: row r sees keys up to n - W + r % W (only keys past n - W
+  // can be hidden)
+  auto mask = [&](f32x16 (&acc)[2][2], int t) {
+    if (!CAUSAL) return;
+    const int rt = t * gTile;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int key = key0 + nt * 32 + col;
+      if (key > n - W) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = rt + mt * 32 + acc_row(i, lane);
+            if (key > n - W + row % W) acc[mt][nt][i] = neg_inf();
+          }
+      }
+    }
+  };
+  // part c (of 8) of a tile: 8 values of key set nt = c / 4
+  auto fold_part = [&](const f32x16 (&acc)[2][2], int c, float (&pa)[2]) {
+    const int nt = c >> 2, mt = (c >> 1) & 1, i0 = (c & 1) * 8;
+    float a = pa[nt];
+#pragma unroll
+    for (int i = i0; i < i0 + 8; i += 2) {
+      if (MAXAGG) a = gmax3(a, acc[mt][nt][i], acc[mt][nt][i + 1]);
+      else a += fast_exp2(acc[mt][nt][i] * alpha) + fast_exp2(acc[mt][nt][i + 1] * alpha);
+    }
+    pa[nt] = a;
+  };
+  auto step = [&](int t, f32x16 (&cur)[2][2], f32x16 (&prev)[2][2]) {
+    const unsigned char* slot = begin_tile(t);
+    if (!any_key) return;
+    mask(prev, t - 1);
+    init_acc(slot, cur);
+    bf16x8 a[2][2];
+    read_step(slot, col, hf, 0, a[0]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
+      tile_step(a[st & 1], kop, st, cur);
+      fold_part(prev, st, agg);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto fold_all = [&](f32x16 (&acc)[2][2], int t) {
+    mask(acc, t);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fold_part(acc, c, agg);
+  };
+
+  f32x16 A[2][2], B[2][2];
+  {
+    const unsigned char* slot = begin_tile(0);
+    if (any_key) {
+      init_acc(slot, A);
+      bf16x8 a[2][2];
+      read_step(slot, col, hf, 0, a[0]);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
+        tile_step(a[st & 1], kop, st, A);
+      }
     }
   }
-  const float o = __shfl_xor(agg, 32);
-  if (MAXAGG) agg = fast_exp2(fmaxf(agg, o));
-  else agg += o;
-  if (hf == 0 && key < n) raw[lh * n + key] = agg;
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B, A);
+    step(t + 1, A, B);
+  }
+  if (t < ntiles) {
+    step(t, B, A);
+    if (any_key) fold_all(B, t);
+  } else if (any_key) {
+    fold_all(A, t - 1);
+  }
+  gen_wait<0>();   // repeats of the last tile (fewer tiles than the prologue's)
+  // the other lane half holds the other 16 rows of every 32-row block
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float o = __shfl_xor(agg[nt], 32);
+    const float tot = MAXAGG ? fast_exp2(__builtin_fmaxf(agg[nt], o) * alpha) : agg[nt] + o;
+    const int key = key0 + nt * 32 + col;
+    if (hf == 0 && key < n) raw[lh * n + key] = tot;
+  }
 }
 
 // ------------------------------------------------------------------ pool ----
@@ -180,22 +561,24 @@ hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r,
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 void twopass_plan(const ScorePlan& p, TwoPassLayout* o) {
-  const int row_blocks = (p.R + 127) / 128;
+  const int row_blocks = (p.R + gBlock - 1) / gBlock;
   const long long base = (long long)row_blocks * p.H * p.L;
-  int splits = (int)((2048 + base - 1) / base);
-  const int max_splits = (p.n + 255) / 256;
+  // split the keys only when the row blocks alone cannot fill the GPU
+  int splits = (int)((1024 + base - 1) / base);
+  const int max_splits = (p.n + 4 * gTile - 1) / (4 * gTile);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int kps = (p.n + splits - 1) / splits;
-  kps = (kps + 31) / 32 * 32;
+  kps = (kps + gTile - 1) / gTile * gTile;
   splits = (p.n + kps - 1) / kps;
   o->row_blocks = row_blocks;
   o->splits = splits;
   o->keys_per_split = kps;
   const size_t LH = (size_t)p.L * p.H;
   o->part_off = 0;
+  const size_t Rpad = (size_t)(p.R + gTile - 1) / gTile * gTile;
   o->stat_off = align256(LH * splits * p.R * sizeof(float2));
-  o->raw_off = o->stat_off + align256(LH * p.R * sizeof(float));
+  o->raw_off = o->stat_off + align256(LH * Rpad * sizeof(float));
   o->bytes = o->raw_off + (p.need_raw_tmp ? align256(LH * p.n * sizeof(float)) : 0);
 }
 
@@ -209,33 +592,36 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
   const __bf16* qb = static_cast<const __bf16*>(q);
   const __bf16* kb = static_cast<const __bf16*>(k);
   const float alpha = p.scale * kLog2e;
-  dim3 g1(o.row_blocks * o.splits, p.H, p.L);
+  const long long g1 = (long long)o.row_blocks * o.splits * p.H * p.L;
+  const int key_blocks = (p.n + gBlock - 1) / gBlock;
+  const long long g2 = (long long)key_blocks * p.H * p.L;
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.causal)
-    hipLaunchKernelGGL(k_rowstats<true>, g1, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n,
-                       alpha, o.splits, o.keys_per_split, part);
+    hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
+                       p.R, p.W, p.n, alpha, o.row_blocks, o.splits, o.keys_per_split, part);
   else
-    hipLaunchKernelGGL(k_rowstats<false>, g1, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n,
-                       alpha, o.splits, o.keys_per_split, part);
-  hipLaunchKernelGGL(k_combine, dim3((p.R + 255) / 256, p.H, p.L), dim3(256), 0, st, part,
-                     p.H, p.R, o.splits, stat);
-  dim3 g2((p.n + 127) / 128, p.H, p.L);
+    hipLaunchKernelGGL(k_gen_stats<false>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
+                       p.R, p.W, p.n, alpha, o.row_blocks, o.splits, o.keys_per_split, part);
+  const int Rpad = (p.R + gTile - 1) / gTile * gTile;
+  hipLaunchKernelGGL(k_combine_neg, dim3((Rpad + 255) / 256, p.H, p.L), dim3(256), 0, st, part,
+                     p.H, p.R, Rpad, o.splits, 1.0f / alpha, stat);
+  const dim3 grid2((unsigned)g2);
   if (p.causal) {
     if (p.max_agg)
-      hipLaunchKernelGGL((k_colagg<true, true>), g2, dim3(256), 0, st, qb, kb, p.H, p.R, p.W,
-                         p.n, alpha, stat, rawbuf);
+      hipLaunchKernelGGL((k_gen_colagg<true, true>), grid2, dim3(512), 0, st, qb, kb, p.H, p.R,
+                         p.W, p.n, alpha, key_blocks, stat, rawbuf);
     else
-      hipLaunchKernelGGL((k_colagg<true, false>), g2, dim3(256), 0, st, qb, kb, p.H, p.R, p.W,
-                         p.n, alpha, stat, rawbuf);
+      hipLaunchKernelGGL((k_gen_colagg<true, false>), grid2, dim3(512), 0, st, qb, kb, p.H,
+                         p.R, p.W, p.n, alpha, key_blocks, stat, rawbuf);
   } else {
     if (p.max_agg)
-      hipLaunchKernelGGL((k_colagg<false, true>), g2, dim3(256), 0, st, qb, kb, p.H, p.R, p.W,
-                         p.n, alpha, stat, rawbuf);
+      hipLaunchKernelGGL((k_gen_colagg<false, true>), grid2, dim3(512), 0, st, qb, kb, p.H,
+                         p.R, p.W, p.n, alpha, key_blocks, stat, rawbuf);
     else
-      hipLaunchKernelGGL((k_colagg<false, false>), g2, dim3(256), 0, st, qb, kb, p.H, p.R, p.W,
-                         p.n, alpha, stat, rawbuf);
+      hipLaunchKernelGGL((k_gen_colagg<false, false>), grid2, dim3(512), 0, st, qb, kb, p.H,
+                         p.R, p.W, p.n, alpha, key_blocks, stat, rawbuf);
   }
-  hipLaunchKernelGGL(k_pool, dim3((p.n_cand + 255) / 256, p.L * p.H), dim3(256), 0, st,
-                     rawbuf, p.n, p.n_cand, p.pool / 2, scores);
+  (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
   return hipGetLastError();
 }
 

@@ -49,10 +49,26 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// wait until at most (kSlots-2) tiles of this wave's loads are outstanding
-__device__ __forceinline__ void wait_ring() {
-  constexpr int n = (kSlots - 2) * kLoadsPerTile;
+// Wait for this wave's loads of tile t. Tiles are issued in order, kSlots-1
+// ahead, and none past the last, so all but the last tile may leave the
+// next one in flight; the last drains everything (nothing is left in flight
+// when the workgroup ends).
+static_assert(kSlots == 3, "wait_ring assumes one tile in flight behind the current one");
+__device__ __forceinline__ void wait_ring(bool last) {
+  constexpr int n = kLoadsPerTile;
   static_assert(n < 16, "vmcnt field");
+  if (last) __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  else __builtin_amdgcn_s_waitcnt(n | (7 << 4) | (15 << 8));
+}
+
+// Wait until only the prologue's ring loads may still be outstanding: the
+// per-lane operands loaded before them are then in registers, so the loop
+// needs no wait for them (otherwise the compiler waits for every load in
+// flight inside the loop).
+__device__ __forceinline__ void wait_operands() {
+  constexpr int n = (kSlots - 1) * kLoadsPerTile;
+  static_assert(n < 16, "vmcnt field");
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(n | (7 << 4) | (15 << 8));
 }
 
@@ -81,6 +97,14 @@ struct RingShared {
   unsigned char ring[kSlots][kTile * kRowBytes];
 };
 
+// Pass 2 keeps its column partials in the same LDS object as the ring: with
+// two objects the compiler waits for every direct-to-LDS load in flight
+// before each LDS read, which would drain the ring every tile.
+struct ColsumShared {
+  unsigned char ring[kSlots][kTile * kRowBytes];
+  float colbuf[2][4][kTile];
+};
+
 // ---------------------------------------------------------------- pass 1 ----
 // grid (blocks, H, L); keys [b*kpb, min(n, (b+1)*kpb)); part[lh][b][row].
 __global__ __launch_bounds__(256) void k_win_stats(const __bf16* __restrict__ q,
@@ -95,22 +119,24 @@ __global__ __launch_bounds__(256) void k_win_stats(const __bf16* __restrict__ q,
   const int j0 = b * kpb, j1 = min(n, j0 + kpb);
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
 
-#pragma unroll
-  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
-
   const int row = wave * 32 + col;
   const bool active = wave * 32 < R;       // wave has rows (uniform)
   bf16x8 qb[8];
   if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qb);
   else zero_ops(qb);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
+  wait_operands();
   const int last = row < R ? n - W + row % W : -1;   // last key this row sees
   const int open_end = n - W;                        // every row sees keys <= this
   float m = kNegBig, s = 0.f;
 
   for (int t = 0; t < ntiles; ++t) {
-    wait_ring();
+    wait_ring(t + 1 == ntiles);
     ring_barrier();
-    load_tile(kh, j0 + min(t + kSlots - 1, ntiles - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
+    if (t + kSlots - 1 < ntiles)
+      load_tile(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
     if (!active) continue;
     const unsigned char* slot = sm.ring[t % kSlots];
     const int kt = j0 + t * kTile;
@@ -158,8 +184,7 @@ __global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q
                                                     int W, int n, float alpha,
                                                     const float* __restrict__ stat, int kpb,
                                                     float* __restrict__ raw) {
-  __shared__ __align__(16) RingShared sm;
-  __shared__ float colbuf[2][4][kTile];
+  __shared__ __align__(16) ColsumShared sm;
   const int b = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
@@ -167,9 +192,6 @@ __global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q
   const __bf16* kh = k + lh * (size_t)n * kHeadDim;
   const int j0 = b * kpb, j1 = min(n, j0 + kpb);
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-
-#pragma unroll
-  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
 
   const bool active = wave * 32 < R;
   bf16x8 qa[8];
@@ -186,16 +208,20 @@ __global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q
     cr[i] = row < R ? stat[lh * R + row] : __builtin_inff();   // padded rows weigh 0
     wq[i] = row % W;
   }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
+  wait_operands();
   const int open_end = n - W;
   const float ident = MAXAGG ? -__builtin_inff() : 0.f;
 
   for (int t = 0; t <= ntiles; ++t) {
-    if (t < ntiles) wait_ring();
+    if (t < ntiles) wait_ring(t + 1 == ntiles);
     ring_barrier();
     // reduce the previous tile's per-wave column partials
     if (t > 0 && tid < kTile) {
       const int key = j0 + (t - 1) * kTile + tid;
-      const float* cb = &colbuf[(t - 1) & 1][0][0];
+      const float* cb = &sm.colbuf[(t - 1) & 1][0][0];
       float v;
       if (MAXAGG) v = fast_exp2(__builtin_fmaxf(__builtin_fmaxf(cb[tid], cb[kTile + tid]),
                                                 __builtin_fmaxf(cb[2 * kTile + tid], cb[3 * kTile + tid])));
@@ -203,7 +229,8 @@ __global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q
       if (key < j1) raw[lh * n + key] = v;
     }
     if (t == ntiles) break;
-    load_tile(kh, j0 + min(t + kSlots - 1, ntiles - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
+    if (t + kSlots - 1 < ntiles)
+      load_tile(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
     const unsigned char* slot = sm.ring[t % kSlots];
     const int kt = j0 + t * kTile;
     const bool open = kt + kTile - 1 <= open_end;
@@ -224,7 +251,7 @@ __global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q
         }
       }
       const float o = __shfl_xor(agg, 32);
-      if (hf == 0) colbuf[t & 1][wave][nt * 32 + col] = MAXAGG ? __builtin_fmaxf(agg, o) : agg + o;
+      if (hf == 0) sm.colbuf[t & 1][wave][nt * 32 + col] = MAXAGG ? __builtin_fmaxf(agg, o) : agg + o;
     }
   }
 }

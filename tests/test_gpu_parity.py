@@ -53,6 +53,9 @@ WINDOW_CASES = [
     dict(n=771, W=3, G=4, pool=9),         # 4 chunks, last chunk 3 keys
     dict(L=3, H_kv=2, n=2048, W=8, G=8),   # R = 64
     dict(n=1000, W=30, G=3, pool=1),       # R = 90, no pooling
+    # general kernels (R > 128): several 512-row blocks, ragged row / key tails
+    dict(n=2000, W=160, G=4),              # R = 640
+    dict(n=1537, W=130, G=5, agg="max"),   # R = 650
 ]
 
 
@@ -75,6 +78,8 @@ EXTERNAL_CASES = [
     dict(L=2, n=33, W=1, G=2, agg="max"),
     dict(n=700, W=64, G=2, agg="sum"),
     dict(n=5000, W=300, G=1, agg="max", pool=3),
+    dict(H_kv=1, G=7, n=1100, W=600, agg="max"),   # R = 4200: many row blocks
+    dict(n=2049, W=520, G=1, agg="sum"),           # R = 520, keys split
 ]
 
 
