@@ -27,102 +27,12 @@
 // result comes from one lane and a fixed-order merge: deterministic.
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
+#include "kvsel_ring.h"
 
 namespace kvsel {
 
-constexpr int gTile = 64;                                     // rows per ring slot (16 KB)
-constexpr int gSlots = 3;
-constexpr int gWaves = 8;
-constexpr int gBlock = gWaves * 64;                           // rows / keys per workgroup
-constexpr int gLoads = gTile * kRowBytes / (gWaves * 1024);   // 16-byte loads per lane per tile
-constexpr int gRowsBytes = gTile * kRowBytes;
 constexpr int gSlotBytes = gRowsBytes + gTile * 4;             // pass 2: rows + normalisers
 constexpr float gNegBig = -1.0e30f;
-static_assert(gSlots >= 2, "ring depth");
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) const void* glb_ptr_t;
-
-// Workgroup barrier without the vmcnt(0) that __syncthreads implies (the
-// ring's loads stay in flight across it); LDS visibility comes from the
-// explicit waits below.
-__device__ __forceinline__ void gen_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Wait until at most N of this wave's vector-memory loads are outstanding
-// (vmcnt is 6 bits: low 4 in [3:0], high 2 in [15:14]).
-template <int N>
-__device__ __forceinline__ void gen_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <int PER, int A>
-__device__ __forceinline__ void gen_wait_ahead(int ahead) {
-  if constexpr (A == 0) {
-    gen_wait<0>();
-  } else {
-    if (ahead >= A) gen_wait<A * PER>();
-    else gen_wait_ahead<PER, A - 1>(ahead);
-  }
-}
-
-// Wait for this wave's loads of tile t (PER loads per tile). The prologue
-// issues gSlots-1 tile loads (repeating the last tile when there are fewer
-// tiles) and iteration t' issues tile t'+gSlots-1 when it exists, all in
-// order; the loads issued after tile t's may stay in flight.
-template <int PER>
-__device__ __forceinline__ void gen_wait_tile(int t, int ntiles) {
-  const int issued = gSlots - 1 + max(0, min(t, ntiles - gSlots + 1));
-  gen_wait_ahead<PER, gSlots - 2>(issued - (t + 1));
-}
-
-// This wave's share of rows [row0, row0 + 64) of a [rows][128] bf16 matrix
-// into `slot` (rows past the end repeat row rows-1 and are never used).
-__device__ __forceinline__ void gen_load_tile(const __bf16* base, int row0, int rows,
-                                              unsigned char* slot) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < gLoads; ++i) {
-    const int chunk = wave * gLoads + i;
-    const int r = chunk * 4 + (lane >> 4);
-    const int piece = (lane & 15) ^ (r & 15);
-    const int row = min(row0 + r, rows - 1);
-    const char* src = reinterpret_cast<const char*>(base + (size_t)row * kHeadDim) + piece * 16;
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(slot + chunk * 1024), 16, 0, 0);
-  }
-}
-
-// MFMA operand of step s, lane half hf, for row r of a ring slot.
-__device__ __forceinline__ bf16x8 gen_op(const unsigned char* slot, int r, int hf, int s) {
-  return ld16(slot + r * kRowBytes + (((hf * 8 + s) ^ (r & 15)) << 4));
-}
-
-__device__ __forceinline__ float gmax3(float a, float b, float c) {
-  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
-}
-
-// MFMA step st of one 64-row ring tile against this wave's two 32-column
-// operand sets: acc[mt][nt] += (slot rows [32mt, 32mt + 32)) x b[nt], over
-// head-dim slice st. a[] holds the step's two row operands.
-__device__ __forceinline__ void tile_step(const bf16x8 (&a)[2], const bf16x8 (&b)[2][8], int st,
-                                          f32x16 (&acc)[2][2]) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    acc[0][nt] = mfma32(a[0], b[nt][st], acc[0][nt]);
-    acc[1][nt] = mfma32(a[1], b[nt][st], acc[1][nt]);
-  }
-}
-
-__device__ __forceinline__ void read_step(const unsigned char* slot, int col, int hf, int st,
-                                          bf16x8 (&a)[2]) {
-  a[0] = gen_op(slot, col, hf, st);
-  a[1] = gen_op(slot, 32 + col, hf, st);
-}
 
 // ---------------------------------------------------------------- pass 1 ----
 // 1-D grid of row_blocks * splits * H * L workgroups, block 512.
@@ -175,7 +85,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
   // the first gSlots-1 tiles (repeating the last one if there are fewer)
 #pragma unroll
   for (int t = 0; t < gSlots - 1; ++t)
-    gen_load_tile(kh, j0 + min(t, ntiles - 1) * gTile, n, ring[t]);
+    gen_load_tile(kh, j0 + min(t, ntiles - 1) * gTile, n, kHeadDim, ring[t]);
   // Q is in registers once at most the prologue's loads are in flight; an
   // explicit wait here keeps the compiler from waiting inside the loop
   gen_wait<(gSlots - 1) * gLoads>();
@@ -238,7 +148,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     gen_wait_tile<gLoads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles)
-      gen_load_tile(kh, j0 + (t + gSlots - 1) * gTile, n, ring[(t + gSlots - 1) % gSlots]);
+      gen_load_tile(kh, j0 + (t + gSlots - 1) * gTile, n, kHeadDim, ring[(t + gSlots - 1) % gSlots]);
     // opaque offset: keeps the compiler from moving LDS reads across tiles
     int qoff = 0;
     asm volatile("" : "+v"(qoff));
@@ -392,7 +302,7 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
   }
   // a row tile: the Q rows (all waves) and their -c_r / alpha (wave 0)
   auto issue = [&](int t, int slot) {
-    gen_load_tile(qh, t * gTile, R, ring[slot]);
+    gen_load_tile(qh, t * gTile, R, kHeadDim, ring[slot]);
     if (wave == 0)
       __builtin_amdgcn_global_load_lds((glb_ptr_t)(sh + t * gTile + lane),
                                        (lds_ptr_t)(ring[slot] + gRowsBytes), 4, 0, 0);

@@ -2,76 +2,171 @@
 // 2-3; Theorem 3.3): weight[l][h][j] = (1/G) sum_g || W_O^(h,g) v_j ||_1
 // where W_O^(h,g) is the D x d column slice of the output projection that
 // query head h*G+g uses. The projection V_proj = V W^O is a bf16 MFMA
-// product accumulated in fp32; each 32 x 32 output tile is folded into
-// per-key |.| sums in registers and never written ([CriticalKV] §D.4 notes
-// the full V_proj would be ~7.8 GB per layer at 7B / 128K).
+// product accumulated in fp32; each output tile is folded into per-key |.|
+// sums in registers and never written ([CriticalKV] §D.4 notes the full
+// V_proj would be ~7.8 GB per layer at 7B / 128K).
 //
-// Tiling: a workgroup owns 256 keys of one (layer, KV head); each of its 4
-// waves holds the bf16 values of 64 keys (2 MFMA N-tiles) in registers for
-// the whole kernel and streams 32-row tiles of W_O^(h,g) (the MFMA A
-// operand) for every g and every 32 of the D output features. Every key's
-// sum is accumulated in one lane in a fixed order: deterministic, no
-// atomics.
+// Tiling (the 8-wave LDS ring of kvsel_ring.h): a workgroup owns 512 keys of
+// one (layer, KV head); each wave holds the values of 64 keys (two MFMA
+// N tiles) in registers for the whole kernel. The A operand, W_O^(h,g), is
+// streamed in 64-row tiles (64 of the D output features, 128 columns each,
+// rows H_q*d elements apart in the [D][H_q*d] matrix) through the ring, for
+// every g: G * ceil(D/64) tiles. Workgroups of one (layer, head) run on one XCD, so
+// the 4 MB slice they all stream stays in that XCD's L2. Software
+// pipelined: the MFMAs of tile t run beside the |.| folding of tile t-1.
+// Every key's sum is accumulated in one lane in a fixed order:
+// deterministic, no atomics.
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
+#include "kvsel_ring.h"
 
 namespace kvsel {
 
-__global__ __launch_bounds__(256) void k_value_weight(const __bf16* __restrict__ v,
+// 1-D grid of key_blocks * H * L workgroups, block 512.
+__global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__ v,
                                                       const __bf16* __restrict__ w_o,
                                                       int H, int G, int n, int D, int n_cand,
+                                                      int key_blocks,
                                                       float* __restrict__ weight) {
-  const int kb = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hf = lane >> 5, col = lane & 31;
+  __shared__ __align__(16) unsigned char ring[gSlots][gRowsBytes];
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = id % key_blocks;
+  id /= key_blocks;
+  const int h = id % H, l = id / H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
   const size_t lh = (size_t)l * H + h;
   const int Hq = H * G;
-  const __bf16* vh = v + lh * (size_t)n * kHeadDim;
-  const __bf16* wl = w_o + (size_t)l * D * (size_t)Hq * kHeadDim;
+  const int stride = Hq * kHeadDim;                        // elements between W_O rows
+  const __bf16* wl = w_o + (size_t)l * D * (size_t)stride;
+  const int dtiles = (D + gTile - 1) / gTile;
+  const int ntiles = G * dtiles;
 
-  bf16x8 b[2][8];
-  int key[2];
+  // this wave's 64 keys: MFMA B operands for the whole kernel
+  const int key0 = kb * gBlock + wave * 64;
+  bf16x8 vop[2][8];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    key[nt] = kb * 256 + wave * 64 + nt * 32 + col;
-    if (key[nt] < n_cand) load_half_row(vh + (size_t)key[nt] * kHeadDim, hf, b[nt]);
-    else zero_ops(b[nt]);
+    const int key = key0 + nt * 32 + col;
+    if (key < n_cand) load_half_row(v + (lh * n + key) * (size_t)kHeadDim, hf, vop[nt]);
+    else zero_ops(vop[nt]);
   }
+  // tile t: output features [64*dt, 64*dt + 64) of query head h*G + g
+  auto issue = [&](int t, int slot) {
+    const int g = t / dtiles, dt = t - g * dtiles;
+    gen_load_tile(wl + (size_t)(h * G + g) * kHeadDim, dt * gTile, D, stride, ring[slot]);
+  };
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < gSlots - 1; ++t) issue(min(t, ntiles - 1), t);
+  // values are in registers once at most the prologue's loads remain
+  gen_wait<(gSlots - 1) * gLoads>();
+
+  const bool any_key = key0 < n_cand;
   float part[2] = {0.f, 0.f};
-  for (int g = 0; g < G; ++g) {
-    const __bf16* wg = wl + (size_t)(h * G + g) * kHeadDim;   // column slice of this query head
-    for (int mt = 0; mt < D; mt += 32) {
-      bf16x8 a[8];
-      load_half_row(wg + (size_t)(mt + col) * Hq * kHeadDim, hf, a);
-      f32x16 acc0 = zero16(), acc1 = zero16();
+
+  auto begin_tile = [&](int t) -> const unsigned char* {
+    gen_wait_tile<gLoads>(t, ntiles);
+    gen_barrier();
+    if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
+    int qoff = 0;
+    asm volatile("" : "+v"(qoff));
+    return ring[t % gSlots] + qoff;
+  };
+  // D % 64 == 32: the last tile of each g has 32 real rows; its other 32
+  // MFMA rows get zero operands (|0| adds nothing)
+  auto half_tile = [&](int t) { return (t % dtiles) * gTile + 32 >= D; };
+  auto read = [&](const unsigned char* slot, int st, bool half, bf16x8 (&a)[2]) {
+    read_step(slot, col, hf, st, a);
+    if (half) a[1] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  };
+  // part c (of 8) of a tile: 8 outputs of key set nt = c / 4
+  auto fold_part = [&](const f32x16 (&acc)[2][2], int c, float (&ps)[2]) {
+    const int nt = c >> 2, mt = (c >> 1) & 1, i0 = (c & 1) * 8;
+    float sum = ps[nt];
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) sum += __builtin_fabsf(acc[mt][nt][i]);
+    ps[nt] = sum;
+  };
+  auto zero_acc = [&](f32x16 (&acc)[2][2]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+  };
+  // tile t into cur while tile t-1 (prev) is folded; per-tile partial sums
+  // keep the fp32 additions short
+  auto step = [&](int t, f32x16 (&cur)[2][2], f32x16 (&prev)[2][2]) {
+    const unsigned char* slot = begin_tile(t);
+    if (!any_key) return;
+    const bool half = half_tile(t);
+    float ps[2] = {0.f, 0.f};
+    zero_acc(cur);
+    bf16x8 a[2][2];
+    read(slot, 0, half, a[0]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) read(slot, st + 1, half, a[(st + 1) & 1]);
+      tile_step(a[st & 1], vop, st, cur);
+      fold_part(prev, st, ps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" : "+v"(ps[0]), "+v"(ps[1]));
+    part[0] += ps[0];
+    part[1] += ps[1];
+  };
+  auto fold_all = [&](const f32x16 (&acc)[2][2]) {
+    float ps[2] = {0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fold_part(acc, c, ps);
+    part[0] += ps[0];
+    part[1] += ps[1];
+  };
+
+  f32x16 A[2][2], B[2][2];
+  {
+    const unsigned char* slot = begin_tile(0);
+    if (any_key) {
+      const bool half = half_tile(0);
+      zero_acc(A);
+      bf16x8 a[2][2];
+      read(slot, 0, half, a[0]);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        acc0 = mfma32(a[st], b[0][st], acc0);
-        acc1 = mfma32(a[st], b[1][st], acc1);
+        if (st + 1 < 8) read(slot, st + 1, half, a[(st + 1) & 1]);
+        tile_step(a[st & 1], vop, st, A);
       }
-      float t0 = 0.f, t1 = 0.f;   // per-tile partials keep the fp32 sums short
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        t0 += fabsf(acc0[i]);
-        t1 += fabsf(acc1[i]);
-      }
-      part[0] += t0;
-      part[1] += t1;
     }
   }
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B, A);
+    step(t + 1, A, B);
+  }
+  if (t < ntiles) {
+    step(t, B, A);
+    if (any_key) fold_all(B);
+  } else if (any_key) {
+    fold_all(A);
+  }
+  gen_wait<0>();   // repeats of the last tile (fewer tiles than the prologue's)
   const float inv_g = 1.0f / (float)G;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float tot = part[nt] + __shfl_xor(part[nt], 32);   // the other 16 output rows
-    if (hf == 0 && key[nt] < n_cand) weight[lh * n_cand + key[nt]] = tot * inv_g;
+    const int key = key0 + nt * 32 + col;
+    if (hf == 0 && key < n_cand) weight[lh * n_cand + key] = tot * inv_g;
   }
 }
 
 hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int G, int n,
                                int D, int n_cand, float* weight, hipStream_t st) {
-  dim3 grid((n_cand + 255) / 256, H, L);
-  hipLaunchKernelGGL(k_value_weight, grid, dim3(256), 0, st, static_cast<const __bf16*>(v),
-                     static_cast<const __bf16*>(w_o), H, G, n, D, n_cand, weight);
+  const int key_blocks = (n_cand + gBlock - 1) / gBlock;
+  const long long blocks = (long long)key_blocks * H * L;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_value_weight, dim3((unsigned)blocks), dim3(512), 0, st,
+                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(w_o), H, G, n, D,
+                     n_cand, key_blocks, weight);
   return hipGetLastError();
 }
 

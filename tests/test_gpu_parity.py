@@ -177,10 +177,10 @@ def test_select_end_to_end_band():
 
 # -------------------------------------------------------------- compaction ----
 
-@pytest.mark.parametrize("adaptive", [False, True])
-def test_compact_bit_exact(adaptive):
+@pytest.mark.parametrize("adaptive,d", [(False, 128), (True, 128), (False, 64), (True, 72)])
+def test_compact_bit_exact(adaptive, d):
     rng = np.random.default_rng(5)
-    L, H, n, d = 2, 3, 777, 128
+    L, H, n = 2, 3, 777
     k = rng.integers(0, 65536, size=(L, H, n, d), dtype=np.uint16)
     v = rng.integers(0, 65536, size=(L, H, n, d), dtype=np.uint16)
     if adaptive:
@@ -210,14 +210,20 @@ def test_compact_bit_exact(adaptive):
 
 # ------------------------------------------------------------ value weight ----
 
-@pytest.mark.parametrize("H,G,n,D,n_cand", [(2, 4, 300, 256, 290), (1, 7, 97, 64, 97), (3, 1, 1000, 32, 999)])
-def test_value_weight(H, G, n, D, n_cand):
-    wl = _wl(H_kv=H, G=G, n=n, W=n - n_cand if n_cand < n else 1, value_weight=True, D=D)
+@pytest.mark.parametrize("L,H,G,n,D,n_cand", [
+    (1, 2, 4, 300, 256, 290),
+    (1, 1, 7, 97, 64, 97),
+    (1, 3, 1, 1000, 32, 999),     # half a W_O tile
+    (2, 2, 3, 1500, 96, 1400),    # several key blocks, ragged, last tile half
+])
+def test_value_weight(L, H, G, n, D, n_cand):
+    wl = _wl(L=L, H_kv=H, G=G, n=n, W=n - n_cand if n_cand < n else 1, value_weight=True, D=D)
     data = gen(wl, seed=6, which=("v", "w_o"))
-    print(f"[gpu] kvsel_value_weight H={H} G={G} n={n} D={D}", flush=True)
+    print(f"[gpu] kvsel_value_weight L={L} H={H} G={G} n={n} D={D}", flush=True)
     w = kv.kvsel_value_weight(to_dev(data["v"]), to_dev(data["w_o"]), G=G, n_cand=n_cand)
     torch.cuda.synchronize()
     w = w.cpu().numpy()
-    ref = oracle.value_weight(synth.bf16_to_f64(data["v"][0]), synth.bf16_to_f64(data["w_o"][0]), G,
-                              np.arange(n_cand))
-    assert_scores_close(w[0], ref, "value weight")
+    for l in range(L):
+        ref = oracle.value_weight(synth.bf16_to_f64(data["v"][l]), synth.bf16_to_f64(data["w_o"][l]),
+                                  G, np.arange(n_cand))
+        assert_scores_close(w[l], ref, "value weight")
