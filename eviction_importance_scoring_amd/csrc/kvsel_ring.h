@@ -32,7 +32,9 @@ typedef __attribute__((address_space(1))) const void* glb_ptr_t;
 
 // Workgroup barrier without the vmcnt(0) that __syncthreads implies (the
 // ring's loads stay in flight across it); LDS visibility comes from the
-// explicit waits below.
+// explicit waits below. It does not wait for the wave's own ds_write
+// operations either, so the kernels built on it write LDS only through the
+// direct global->LDS loads.
 __device__ __forceinline__ void gen_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

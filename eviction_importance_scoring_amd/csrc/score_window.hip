@@ -49,11 +49,23 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The same barrier for a wave that has written LDS with ds_write since the
+// last one (pass 2's column partials and row normalisers): s_barrier by
+// itself does not order LDS writes before other waves' reads after it, so
+// the wave first waits for its own LDS operations (lgkmcnt(0); vmcnt and
+// expcnt left at their maxima).
+__device__ __forceinline__ void ring_barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait for this wave's loads of tile t. Tiles are issued in order, kSlots-1
 // ahead, and none past the last, so all but the last tile may leave the
 // next one in flight; the last drains everything (nothing is left in flight
 // when the workgroup ends).
-static_assert(kSlots == 3, "wait_ring assumes one tile in flight behind the current one");
+static_assert(kSlots == 3 && kSub == 2, "wait_ring and the pass-1 folds assume 3 slots of 64 keys");
 __device__ __forceinline__ void wait_ring(bool last) {
   constexpr int n = kLoadsPerTile;
   static_assert(n < 16, "vmcnt field");
@@ -88,6 +100,47 @@ __device__ __forceinline__ void load_tile(const __bf16* kh, int key0, int n, uns
   }
 }
 
+// Pass 2 leaves wave 0 out of the ring loads: wave 0 stores the finished
+// sums, and a wave's stores share vmcnt with its loads, so a store still in
+// flight would hold up its next ring wait (and with it the barrier). Waves
+// 1..3 load chunks [0,6), [6,11) and [11,16) of each tile's 16 chunks; wave
+// 0 never waits on vmcnt in the loop.
+constexpr int kChunks = kTile * kRowBytes / 1024;
+static_assert(kChunks == 16, "chunk split of the pass-2 loaders");
+__device__ __forceinline__ void load_tile_w123(const __bf16* kh, int key0, int n, int wave,
+                                               unsigned char* slot) {
+  if (wave == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int c0 = wave == 1 ? 0 : 6 + (wave - 2) * 5, cnt = wave == 1 ? 6 : 5;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    if (i < cnt) {
+      const int chunk = c0 + i;
+      const int r = chunk * 4 + (lane >> 4);
+      const int piece = (lane & 15) ^ (r & 15);
+      const int key = min(key0 + r, n - 1);
+      const char* src = reinterpret_cast<const char*>(kh + (size_t)key * kHeadDim) + piece * 16;
+      __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(slot + chunk * 1024), 16, 0, kNonTemporal);
+    }
+  }
+}
+
+// wait_ring for the pass-2 loaders (wave 0 has no ring loads)
+__device__ __forceinline__ void wait_ring_w123(bool last, int wave) {
+  if (wave == 0) return;
+  if (last) __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  else if (wave == 1) __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8));
+  else __builtin_amdgcn_s_waitcnt(5 | (7 << 4) | (15 << 8));
+}
+
+// Before the pass-2 loop every load of the prologue is waited for: with
+// stores in the loop the compiler otherwise re-waits for all loads in
+// flight (vmcnt(0)) at the operands' first use inside the loop.
+__device__ __forceinline__ void wait_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
 // MFMA operand (step s) of key row r (0..kTile-1) for lane half hf.
 __device__ __forceinline__ bf16x8 tile_op(const unsigned char* slot, int r, int hf, int s) {
   return ld16(slot + r * kRowBytes + (((hf * 8 + s) ^ (r & 15)) << 4));
@@ -103,17 +156,30 @@ struct RingShared {
 struct ColsumShared {
   unsigned char ring[kSlots][kTile * kRowBytes];
   float colbuf[2][4][kTile];
+  float crow[128];            // row normalisers c_r (padding rows: +inf)
 };
 
 // ---------------------------------------------------------------- pass 1 ----
 // grid (blocks, H, L); keys [b*kpb, min(n, (b+1)*kpb)); part[lh][b][row].
-__global__ __launch_bounds__(256) void k_win_stats(const __bf16* __restrict__ q,
+//
+// Software pipelined: the MFMAs of tile t are interleaved (one step at a
+// time) with folding tile t-1 into the running (max, sum), two accumulator
+// sets in turn, so the vector work hides behind the matrix work and the
+// tile loads. A tile's exponentials use the running offset m from before
+// the tile; only when the tile's partial sum passes 2^64 (first tile of a
+// row, or a large jump of its max) is the tile's max found and the sum
+// redone at a new offset, which keeps the max off the per-logit path.
+constexpr float kPartialLimit = 1.8446744e19f;   // 2^64
+
+// Three workgroups per CU (LDS) need at most 168 registers a lane.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_win_stats(const __bf16* __restrict__ q,
                                                    const __bf16* __restrict__ k, int H, int R,
                                                    int W, int n, float alpha, int blocks,
                                                    int kpb, float2* __restrict__ part) {
   __shared__ __align__(16) RingShared sm;
   const int b = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
   const size_t lh = (size_t)l * H + h;
   const __bf16* kh = k + lh * (size_t)n * kHeadDim;
   const int j0 = b * kpb, j1 = min(n, j0 + kpb);
@@ -132,43 +198,99 @@ __global__ __launch_bounds__(256) void k_win_stats(const __bf16* __restrict__ q,
   const int open_end = n - W;                        // every row sees keys <= this
   float m = kNegBig, s = 0.f;
 
-  for (int t = 0; t < ntiles; ++t) {
+  auto begin_tile = [&](int t) -> const unsigned char* {
     wait_ring(t + 1 == ntiles);
     ring_barrier();
     if (t + kSlots - 1 < ntiles)
       load_tile(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
-    if (!active) continue;
-    const unsigned char* slot = sm.ring[t % kSlots];
+    int qoff = 0;   // opaque offset: keeps LDS reads from moving across tiles
+    asm volatile("" : "+v"(qoff));
+    return sm.ring[t % kSlots] + qoff;
+  };
+  auto mask = [&](f32x16 (&acc)[kSub], int t) {
     const int kt = j0 + t * kTile;
-    f32x16 acc[kSub];
+    if (kt + kTile - 1 <= open_end && kt + kTile <= j1) return;
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) acc[u] = zero16();
+    for (int u = 0; u < kSub; ++u)
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kt + u * 32 + acc_row(i, lane);
+        if (!(kk <= last && kk < j1)) acc[u][i] = -__builtin_inff();
+      }
+  };
+  // part c (of 8) of a tile: 4 logits into the partial sum at offset m
+  auto fold_part = [&](const f32x16 (&acc)[kSub], int c, float& ps) {
+    const int u = c >> 2, i0 = (c & 3) * 4;
 #pragma unroll
-      for (int u = 0; u < kSub; ++u) acc[u] = mfma32(tile_op(slot, u * 32 + col, hf, st), qb[st], acc[u]);
-    if (!(kt + kTile - 1 <= open_end && kt + kTile <= j1)) {
+    for (int i = i0; i < i0 + 4; ++i) ps += fast_exp2(__builtin_fmaf(acc[u][i], alpha, -m));
+  };
+  auto fold_end = [&](const f32x16 (&acc)[kSub], float ps) {
+    const float s_old = s;
+    s = s_old + ps;            // unconditional: keeps the folds beside the MFMAs
+    if (!(ps <= kPartialLimit)) {
+      float tm = -__builtin_inff();
 #pragma unroll
       for (int u = 0; u < kSub; ++u)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = kt + u * 32 + acc_row(i, lane);
-          if (!(kk <= last && kk < j1)) acc[u][i] = -__builtin_inff();
-        }
+        for (int i = 0; i < 16; i += 2) tm = max3f(tm, acc[u][i], acc[u][i + 1]);
+      const float mn = __builtin_fmaxf(m, tm * alpha);   // alpha > 0
+      float sum = s_old * fast_exp2(m - mn);
+#pragma unroll
+      for (int u = 0; u < kSub; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(acc[u][i], alpha, -mn));
+      s = sum;
+      m = mn;
     }
-    float tm = -__builtin_inff();
+  };
+  auto mfma_step = [&](const unsigned char* slot, int st, f32x16 (&acc)[kSub]) {
 #pragma unroll
-    for (int u = 0; u < kSub; ++u)
+    for (int u = 0; u < kSub; ++u) acc[u] = mfma32(tile_op(slot, u * 32 + col, hf, st), qb[st], acc[u]);
+  };
+  auto step = [&](int t, f32x16 (&cur)[kSub], f32x16 (&prev)[kSub]) {
+    const unsigned char* slot = begin_tile(t);
+    if (!active) return;
+    mask(prev, t - 1);
+    float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) tm = max3f(tm, acc[u][i], acc[u][i + 1]);
-    const float mn = __builtin_fmaxf(m, tm * alpha);
-    float sum = s * fast_exp2(m - mn);
+    for (int u = 0; u < kSub; ++u) cur[u] = zero16();
 #pragma unroll
-    for (int u = 0; u < kSub; ++u)
+    for (int st = 0; st < 8; ++st) {
+      mfma_step(slot, st, cur);
+      fold_part(prev, st, ps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" : "+v"(ps));
+    fold_end(prev, ps);
+  };
+  auto fold_all = [&](f32x16 (&acc)[kSub], int t) {
+    mask(acc, t);
+    float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(acc[u][i], alpha, -mn));
-    s = sum;
-    m = mn;
+    for (int c = 0; c < 8; ++c) fold_part(acc, c, ps);
+    fold_end(acc, ps);
+  };
+
+  f32x16 A[kSub], B[kSub];
+  {
+    const unsigned char* slot = begin_tile(0);
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) A[u] = zero16();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) mfma_step(slot, st, A);
+    }
+  }
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B, A);
+    step(t + 1, A, B);
+  }
+  if (t < ntiles) {
+    step(t, B, A);
+    if (active) fold_all(B, t);
+  } else if (active) {
+    fold_all(A, t - 1);
   }
   // the other lane half saw the other 16 keys of every 32-key sub-tile
   const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(s, 32);
@@ -178,16 +300,21 @@ __global__ __launch_bounds__(256) void k_win_stats(const __bf16* __restrict__ q,
 
 // ---------------------------------------------------------------- pass 2 ----
 // grid (blocks, H, L); raw[lh][key] = sum_r 2^(x - c_r), or 2^(max_r (x - c_r)).
+//
+// Pipelined like pass 1: while the MFMAs of tile t run, tile t-1 is folded
+// into per-key partials over this wave's 32 rows and written to LDS; after
+// the next barrier one wave adds the 4 waves' partials of tile t-1 in
+// fixed order and stores them. Three workgroups per CU (LDS) need at most
+// 168 registers a lane.
 template <bool MAXAGG>
-__global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q,
-                                                    const __bf16* __restrict__ k, int H, int R,
-                                                    int W, int n, float alpha,
-                                                    const float* __restrict__ stat, int kpb,
-                                                    float* __restrict__ raw) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_win_colsum(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, int H, int R, int W, int n,
+    float alpha, const float* __restrict__ stat, int kpb, float* __restrict__ raw) {
   __shared__ __align__(16) ColsumShared sm;
   const int b = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hf = lane >> 5, col = lane & 31;
   const size_t lh = (size_t)l * H + h;
   const __bf16* kh = k + lh * (size_t)n * kHeadDim;
   const int j0 = b * kpb, j1 = min(n, j0 + kpb);
@@ -200,59 +327,128 @@ __global__ __launch_bounds__(256) void k_win_colsum(const __bf16* __restrict__ q
     if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qa);
     else zero_ops(qa);
   }
-  float cr[16];
-  int wq[16];            // window index of each of this lane's 16 rows
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = wave * 32 + acc_row(i, lane);
-    cr[i] = row < R ? stat[lh * R + row] : __builtin_inff();   // padded rows weigh 0
-    wq[i] = row % W;
-  }
+  // the row normalisers live in LDS (read 4 at a time by the folds), which
+  // keeps three workgroups' registers per CU; visible after the first barrier
+  if (tid < 128) sm.crow[tid] = tid < R ? stat[lh * R + tid] : __builtin_inff();   // padded rows weigh 0
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
-  wait_operands();
+  for (int t = 0; t < kSlots - 1; ++t) load_tile_w123(kh, j0 + min(t, ntiles - 1) * kTile, n, wave, sm.ring[t]);
+  wait_all();
   const int open_end = n - W;
   const float ident = MAXAGG ? -__builtin_inff() : 0.f;
 
-  for (int t = 0; t <= ntiles; ++t) {
-    if (t < ntiles) wait_ring(t + 1 == ntiles);
-    ring_barrier();
-    // reduce the previous tile's per-wave column partials
-    if (t > 0 && tid < kTile) {
-      const int key = j0 + (t - 1) * kTile + tid;
-      const float* cb = &sm.colbuf[(t - 1) & 1][0][0];
-      float v;
-      if (MAXAGG) v = fast_exp2(__builtin_fmaxf(__builtin_fmaxf(cb[tid], cb[kTile + tid]),
-                                                __builtin_fmaxf(cb[2 * kTile + tid], cb[3 * kTile + tid])));
-      else v = (cb[tid] + cb[kTile + tid]) + (cb[2 * kTile + tid] + cb[3 * kTile + tid]);
-      if (key < j1) raw[lh * n + key] = v;
-    }
-    if (t == ntiles) break;
+  // one wave adds the 4 waves' partials of tile tt (written before the
+  // last barrier) in a fixed order
+  auto reduce = [&](int tt) {
+    if (tid >= kTile) return;
+    const int key = j0 + tt * kTile + tid;
+    const float* cb = &sm.colbuf[tt & 1][0][0];
+    float v;
+    if (MAXAGG) v = fast_exp2(__builtin_fmaxf(__builtin_fmaxf(cb[tid], cb[kTile + tid]),
+                                              __builtin_fmaxf(cb[2 * kTile + tid], cb[3 * kTile + tid])));
+    else v = (cb[tid] + cb[kTile + tid]) + (cb[2 * kTile + tid] + cb[3 * kTile + tid]);
+    if (key < j1) raw[lh * n + key] = v;
+  };
+  // tile t-2's sums are stored by wave 0, which loads no ring tiles
+  auto begin_tile = [&](int t) -> const unsigned char* {
+    wait_ring_w123(t + 1 == ntiles, wave);
+    ring_barrier_lds();
+    if (t >= 2) reduce(t - 2);
     if (t + kSlots - 1 < ntiles)
-      load_tile(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
-    const unsigned char* slot = sm.ring[t % kSlots];
+      load_tile_w123(kh, j0 + (t + kSlots - 1) * kTile, n, wave, sm.ring[(t + kSlots - 1) % kSlots]);
+    int qoff = 0;   // opaque offset: keeps LDS reads from moving across tiles
+    asm volatile("" : "+v"(qoff));
+    return sm.ring[t % kSlots] + qoff;
+  };
+  // window rows hide keys past n - W + (row % W)
+  auto mask = [&](f32x16 (&acc)[kSub], int t) {
     const int kt = j0 + t * kTile;
-    const bool open = kt + kTile - 1 <= open_end;
+    if (kt + kTile - 1 <= open_end) return;
 #pragma unroll
     for (int nt = 0; nt < kSub; ++nt) {
-      float agg = ident;
-      if (active) {
-        f32x16 acc = zero16();
+      const int key = kt + nt * 32 + col;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) acc = mfma32(qa[st], tile_op(slot, nt * 32 + col, hf, st), acc);
-        const int key = kt + nt * 32 + col;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = __builtin_fmaf(acc[i], alpha, -cr[i]);
-          if (!open && key > n - W + wq[i]) x = -__builtin_inff();
-          if (MAXAGG) agg = __builtin_fmaxf(agg, x);
-          else agg += fast_exp2(x);
-        }
-      }
-      const float o = __shfl_xor(agg, 32);
-      if (hf == 0) sm.colbuf[t & 1][wave][nt * 32 + col] = MAXAGG ? __builtin_fmaxf(agg, o) : agg + o;
+      for (int i = 0; i < 16; ++i)
+        if (key > n - W + (wave * 32 + acc_row(i, lane)) % W) acc[nt][i] = -__builtin_inff();
     }
+  };
+  // part c (of 8): 4 rows of key set nt = c / 4 into the per-key partial
+  auto fold_part = [&](const f32x16 (&acc)[kSub], int c, float (&pa)[kSub]) {
+    const int nt = c >> 2, i0 = (c & 3) * 4;
+    // rows wave*32 + 8*(c&3) + 4*hf + u of registers i0 + u
+    const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.crow[wave * 32 + 2 * i0 + 4 * hf]);
+#pragma unroll
+    for (int i = i0; i < i0 + 4; ++i) {
+      const float x = __builtin_fmaf(acc[nt][i], alpha, -c4[i - i0]);
+      if (MAXAGG) pa[nt] = __builtin_fmaxf(pa[nt], x);
+      else pa[nt] += fast_exp2(x);
+    }
+  };
+  // this wave's per-key partials of tile tt (other lane half: other 16 rows)
+  auto fold_end = [&](const float (&pa)[kSub], int tt) {
+#pragma unroll
+    for (int nt = 0; nt < kSub; ++nt) {
+      const float o = __shfl_xor(pa[nt], 32);
+      if (hf == 0)
+        sm.colbuf[tt & 1][wave][nt * 32 + col] = MAXAGG ? __builtin_fmaxf(pa[nt], o) : pa[nt] + o;
+    }
+  };
+  auto mfma_step = [&](const unsigned char* slot, int st, f32x16 (&acc)[kSub]) {
+#pragma unroll
+    for (int nt = 0; nt < kSub; ++nt) acc[nt] = mfma32(qa[st], tile_op(slot, nt * 32 + col, hf, st), acc[nt]);
+  };
+  // tile t into cur while tile t-1 (prev) is folded; tile t-2 is reduced
+  auto step = [&](int t, f32x16 (&cur)[kSub], f32x16 (&prev)[kSub]) {
+    const unsigned char* slot = begin_tile(t);
+    float pa[kSub] = {ident, ident};
+    if (active) {
+      mask(prev, t - 1);
+#pragma unroll
+      for (int nt = 0; nt < kSub; ++nt) cur[nt] = zero16();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        mfma_step(slot, st, cur);
+        fold_part(prev, st, pa);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    fold_end(pa, t - 1);
+  };
+
+  f32x16 A[kSub], B[kSub];
+  {
+    const unsigned char* slot = begin_tile(0);
+    if (active) {
+#pragma unroll
+      for (int nt = 0; nt < kSub; ++nt) A[nt] = zero16();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) mfma_step(slot, st, A);
+    }
+  }
+  int t = 1;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B, A);
+    step(t + 1, A, B);
+  }
+  // the last tile's accumulators: B if one more step runs, else A
+  auto finish = [&](f32x16 (&acc)[kSub], int tl) {
+    ring_barrier_lds();            // partials of tile tl-1 are in LDS
+    if (tl >= 1) reduce(tl - 1);
+    float pa[kSub] = {ident, ident};
+    if (active) {
+      mask(acc, tl);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) fold_part(acc, c, pa);
+    }
+    fold_end(pa, tl);
+    ring_barrier_lds();
+    reduce(tl);
+  };
+  if (t < ntiles) {
+    step(t, B, A);
+    finish(B, t);
+  } else {
+    finish(A, t - 1);
   }
 }
 

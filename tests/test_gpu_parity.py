@@ -96,13 +96,32 @@ def test_external_scores(case):
             assert (raw[l] <= 1.0 + 1e-6).all()
 
 
-def test_scores_deterministic():
-    wl = _wl(L=2, n=3000, W=32)
+@pytest.mark.parametrize("case", [
+    dict(L=2, n=3000, W=32),
+    # many tiles per workgroup, all heads busy: cross-wave LDS hand-offs
+    dict(L=4, H_kv=8, n=20000, W=32),
+    dict(L=2, H_kv=2, G=7, n=4000, W=600, q_mode="external", agg="max", pool=1),
+    dict(n=2000, W=160, G=4),
+])
+def test_scores_deterministic(case):
+    """Bit-identical results on repeated calls (no atomics, fixed orders)."""
+    wl = _wl(**case)
     data = gen(wl, seed=3, which=("q", "k"))
     a = _run_scores(wl, data)
-    b = _run_scores(wl, data)
-    np.testing.assert_array_equal(a[0], b[0])
-    np.testing.assert_array_equal(a[1], b[1])
+    for _ in range(2):
+        b = _run_scores(wl, data)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_value_weight_deterministic():
+    wl = _wl(L=1, H_kv=2, G=4, n=3000, W=1, value_weight=True, D=512)
+    data = gen(wl, seed=7, which=("v", "w_o"))
+    v, w_o = to_dev(data["v"]), to_dev(data["w_o"])
+    a = kv.kvsel_value_weight(v, w_o, G=wl.G, n_cand=wl.n).cpu().numpy()
+    for _ in range(2):
+        b = kv.kvsel_value_weight(v, w_o, G=wl.G, n_cand=wl.n).cpu().numpy()
+        np.testing.assert_array_equal(a, b)
 
 
 # --------------------------------------------------------------- selection ----
