@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 METRIC = "KV entries scored+selected/sec per layer at n=32K; % of HBM roofline"
-SCORE_SOURCES = ["score_dispatch.hip", "score_window.hip", "score_twopass.hip", "kvsel_internal.h"]
+SCORE_SOURCES = ["score_dispatch.hip", "score_window.hip", "score_twopass.hip", "kvsel_internal.h",
+                 "kvsel_ring.h"]
 
 
 def log(msg):
