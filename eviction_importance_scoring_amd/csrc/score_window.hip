@@ -243,9 +243,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       m = mn;
     }
   };
-  auto mfma_step = [&](const unsigned char* slot, int st, f32x16 (&acc)[kSub]) {
+  // operand reads run one step ahead of the MFMAs that use them
+  auto read_ops = [&](const unsigned char* slot, int st, bf16x8 (&o)[kSub]) {
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) acc[u] = mfma32(tile_op(slot, u * 32 + col, hf, st), qb[st], acc[u]);
+    for (int u = 0; u < kSub; ++u) o[u] = tile_op(slot, u * 32 + col, hf, st);
+  };
+  auto mfma_step = [&](const bf16x8 (&o)[kSub], int st, f32x16 (&acc)[kSub]) {
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) acc[u] = mfma32(o[u], qb[st], acc[u]);
   };
   auto step = [&](int t, f32x16 (&cur)[kSub], f32x16 (&prev)[kSub]) {
     const unsigned char* slot = begin_tile(t);
@@ -254,9 +259,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     float ps = 0.f;
 #pragma unroll
     for (int u = 0; u < kSub; ++u) cur[u] = zero16();
+    bf16x8 o[2][kSub];
+    read_ops(slot, 0, o[0]);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      mfma_step(slot, st, cur);
+      if (st + 1 < 8) read_ops(slot, st + 1, o[(st + 1) & 1]);
+      mfma_step(o[st & 1], st, cur);
       fold_part(prev, st, ps);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -277,8 +285,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     if (active) {
 #pragma unroll
       for (int u = 0; u < kSub; ++u) A[u] = zero16();
+      bf16x8 o[2][kSub];
+      read_ops(slot, 0, o[0]);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) mfma_step(slot, st, A);
+      for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) read_ops(slot, st + 1, o[(st + 1) & 1]);
+        mfma_step(o[st & 1], st, A);
+      }
     }
   }
   int t = 1;
@@ -364,12 +377,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   auto mask = [&](f32x16 (&acc)[kSub], int t) {
     const int kt = j0 + t * kTile;
     if (kt + kTile - 1 <= open_end) return;
+    // opaque row base: keeps the 16 row % W values from being hoisted out
+    // of the tile loop into registers (this branch runs on edge tiles only)
+    int rbase = wave * 32 + 4 * hf;
+    asm volatile("" : "+v"(rbase));
 #pragma unroll
     for (int nt = 0; nt < kSub; ++nt) {
       const int key = kt + nt * 32 + col;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key > n - W + (wave * 32 + acc_row(i, lane)) % W) acc[nt][i] = -__builtin_inff();
+        if (key > n - W + (rbase + 8 * (i >> 2) + (i & 3)) % W) acc[nt][i] = -__builtin_inff();
     }
   };
   // part c (of 8): 4 rows of key set nt = c / 4 into the per-key partial
@@ -393,9 +410,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         sm.colbuf[tt & 1][wave][nt * 32 + col] = MAXAGG ? __builtin_fmaxf(pa[nt], o) : pa[nt] + o;
     }
   };
-  auto mfma_step = [&](const unsigned char* slot, int st, f32x16 (&acc)[kSub]) {
+  // operand reads run one step ahead of the MFMAs that use them
+  auto read_ops = [&](const unsigned char* slot, int st, bf16x8 (&o)[kSub]) {
 #pragma unroll
-    for (int nt = 0; nt < kSub; ++nt) acc[nt] = mfma32(qa[st], tile_op(slot, nt * 32 + col, hf, st), acc[nt]);
+    for (int nt = 0; nt < kSub; ++nt) o[nt] = tile_op(slot, nt * 32 + col, hf, st);
+  };
+  auto mfma_step = [&](const bf16x8 (&o)[kSub], int st, f32x16 (&acc)[kSub]) {
+#pragma unroll
+    for (int nt = 0; nt < kSub; ++nt) acc[nt] = mfma32(qa[st], o[nt], acc[nt]);
   };
   // tile t into cur while tile t-1 (prev) is folded; tile t-2 is reduced
   auto step = [&](int t, f32x16 (&cur)[kSub], f32x16 (&prev)[kSub]) {
@@ -405,9 +427,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       mask(prev, t - 1);
 #pragma unroll
       for (int nt = 0; nt < kSub; ++nt) cur[nt] = zero16();
+      bf16x8 o[2][kSub];
+      read_ops(slot, 0, o[0]);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        mfma_step(slot, st, cur);
+        if (st + 1 < 8) read_ops(slot, st + 1, o[(st + 1) & 1]);
+        mfma_step(o[st & 1], st, cur);
         fold_part(prev, st, pa);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -421,8 +446,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     if (active) {
 #pragma unroll
       for (int nt = 0; nt < kSub; ++nt) A[nt] = zero16();
+      bf16x8 o[2][kSub];
+      read_ops(slot, 0, o[0]);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) mfma_step(slot, st, A);
+      for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) read_ops(slot, st + 1, o[(st + 1) & 1]);
+        mfma_step(o[st & 1], st, A);
+      }
     }
   }
   int t = 1;
