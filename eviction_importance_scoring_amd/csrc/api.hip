@@ -128,6 +128,7 @@ int32_t kvsel_select(const float* scores, const float* weight, int32_t L, int32_
   if (!scores || (budget > 0 && !idx) || (adaptive && !head_offsets)) return KVSEL_ERR_ARG;
   if (!aligned16(scores) || (weight && !aligned16(weight))) return KVSEL_ERR_ARG;
   if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return KVSEL_ERR_ARG;
   const hipError_t e = select_launch(p, scores, weight, idx, head_offsets, stage, ws,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;

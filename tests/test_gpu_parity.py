@@ -142,6 +142,13 @@ SELECT_CASES = [
     (1, 2, 500, 4, 0.3, False, True, 1.0, 10),
     (1, 1, 50000, 32, 0.1, False, False, 0.5, 1000),      # longer than LDS: streamed
     (1, 2, 40000, 32, 0.1, True, True, 0.5, 100000),      # streamed, two-stage, adaptive
+    # segments over the LDS size run on many workgroups (chunks of 8192)
+    (2, 8, 9032, 32, 0.2, True, False, 0.5, 50),          # adaptive, 8 heads, ties
+    (1, 3, 20000, 0, 0.3, True, False, 0.5, 5),           # adaptive, no window, heavy ties
+    (1, 1, 36000, 16, 1.0, False, False, 0.5, 3),         # keep everything
+    (1, 2, 50000, 32, 0.3, False, True, 0.0, 1000),       # two-stage, alpha 0
+    (1, 2, 50000, 32, 0.3, False, True, 1.0, 1000),       # two-stage, alpha 1
+    (1, 4, 12000, 8, 0.25, True, True, 0.5, 7),           # adaptive two-stage, ties
     (1, 2, 64, 32, 1.0, False, False, 0.5, 3),            # keep everything
     (1, 2, 64, 32, 0.5, False, False, 0.5, 3),            # keep only the window
     (1, 2, 64, 0, 0.0, False, False, 0.5, 3),             # external: nothing kept
