@@ -31,7 +31,7 @@ constexpr int kSlots = 3;                     // ring depth (3 keeps 3 workgroup
 constexpr int kSub = kTile / 32;              // 32-key MFMA sub-tiles per slot
 constexpr int kLoadsPerTile = kTile * kRowBytes / (4 * 1024);   // per wave
 constexpr float kNegBig = -1.0e30f;           // "no key seen yet"
-constexpr int kNonTemporal = 2;               // cache-policy bit: K is read once per pass
+[[maybe_unused]] constexpr int kNonTemporal = 2;              // cache-policy bit: K is read once per pass
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) const void* glb_ptr;
@@ -84,45 +84,54 @@ __device__ __forceinline__ void wait_operands() {
   __builtin_amdgcn_s_waitcnt(n | (7 << 4) | (15 << 8));
 }
 
-// Issue this wave's share (kLoadsPerTile instructions of 1 KB) of the tile
-// of keys [key0, key0 + kTile) into `slot`. Keys >= n read row n-1 (never
-// used). LDS layout: row r at r*256, piece p at ((p ^ (r & 15)) * 16).
-__device__ __forceinline__ void load_tile(const __bf16* kh, int key0, int n, unsigned char* slot) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// A wave's share of the ring loads: chunks [c0, c0 + cnt) of a tile's 16
+// chunks of 1 KB (chunk c = key rows 4c..4c+3), cnt <= MAXC. LDS layout: row
+// r at r*256, piece p at ((p ^ (r & 15)) * 16). Loads go through a buffer
+// resource whose base is the tile's first key and whose size ends at key
+// n-1: the lane offsets (row r = 4c + lane/16, swizzled piece) are fixed
+// for the whole kernel, so issuing a tile costs no vector instructions, and
+// rows past the last key are cut off by the hardware range check (those
+// keys are never used) instead of being clamped.
+constexpr int kChunks = kTile * kRowBytes / 1024;
+static_assert(kChunks == 16, "chunk split of the ring loaders");
+[[maybe_unused]] constexpr int kRawBufferWord3 = 0x00020000;  // untyped 32-bit data format
+template <int MAXC>
+struct RingLoader {
+  uint32_t off[MAXC];
+  int c0, cnt;
+  __device__ __forceinline__ void init(int first, int count) {
+    const int lane = threadIdx.x & 63;
+    c0 = first;
+    cnt = count;
 #pragma unroll
-  for (int i = 0; i < kLoadsPerTile; ++i) {
-    const int chunk = wave * kLoadsPerTile + i;          // 1 KB = 4 rows
-    const int r = chunk * 4 + (lane >> 4);
-    const int piece = (lane & 15) ^ (r & 15);
-    const int key = min(key0 + r, n - 1);
-    const char* src = reinterpret_cast<const char*>(kh + (size_t)key * kHeadDim) + piece * 16;
-    __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(slot + chunk * 1024), 16, 0, kNonTemporal);
+    for (int i = 0; i < MAXC; ++i) {
+      const int r = (first + i) * 4 + (lane >> 4);
+      off[i] = (uint32_t)(r * kRowBytes + (((lane & 15) ^ (r & 15)) << 4));
+    }
   }
-}
+  // key0 < n; n * kRowBytes < 2^31 (window_applicable)
+  __device__ __forceinline__ void issue(const __bf16* kh, int key0, int n, unsigned char* slot) const {
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(kh + (size_t)key0 * kHeadDim), 0, (n - key0) * kRowBytes, kRawBufferWord3);
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+      if (i < cnt)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(slot + (c0 + i) * 1024), 16, off[i], 0, 0,
+                                                 kNonTemporal);
+#endif
+  }
+};
 
 // Pass 2 leaves wave 0 out of the ring loads: wave 0 stores the finished
 // sums, and a wave's stores share vmcnt with its loads, so a store still in
 // flight would hold up its next ring wait (and with it the barrier). Waves
 // 1..3 load chunks [0,6), [6,11) and [11,16) of each tile's 16 chunks; wave
 // 0 never waits on vmcnt in the loop.
-constexpr int kChunks = kTile * kRowBytes / 1024;
-static_assert(kChunks == 16, "chunk split of the pass-2 loaders");
-__device__ __forceinline__ void load_tile_w123(const __bf16* kh, int key0, int n, int wave,
-                                               unsigned char* slot) {
-  if (wave == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int c0 = wave == 1 ? 0 : 6 + (wave - 2) * 5, cnt = wave == 1 ? 6 : 5;
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    if (i < cnt) {
-      const int chunk = c0 + i;
-      const int r = chunk * 4 + (lane >> 4);
-      const int piece = (lane & 15) ^ (r & 15);
-      const int key = min(key0 + r, n - 1);
-      const char* src = reinterpret_cast<const char*>(kh + (size_t)key * kHeadDim) + piece * 16;
-      __builtin_amdgcn_global_load_lds((glb_ptr)src, (lds_ptr)(slot + chunk * 1024), 16, 0, kNonTemporal);
-    }
-  }
+__device__ __forceinline__ void init_loader_w123(RingLoader<6>& ld, int wave) {
+  if (wave == 0) ld.init(0, 0);
+  else if (wave == 1) ld.init(0, 6);
+  else ld.init(6 + (wave - 2) * 5, 5);
 }
 
 // wait_ring for the pass-2 loaders (wave 0 has no ring loads)
@@ -191,8 +200,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qb);
   else zero_ops(qb);
   asm volatile("" ::: "memory");
+  RingLoader<kLoadsPerTile> ld;
+  ld.init(wave * kLoadsPerTile, kLoadsPerTile);
 #pragma unroll
-  for (int t = 0; t < kSlots - 1; ++t) load_tile(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
+  for (int t = 0; t < kSlots - 1; ++t) ld.issue(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
   wait_operands();
   const int last = row < R ? n - W + row % W : -1;   // last key this row sees
   const int open_end = n - W;                        // every row sees keys <= this
@@ -202,10 +213,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     wait_ring(t + 1 == ntiles);
     ring_barrier();
     if (t + kSlots - 1 < ntiles)
-      load_tile(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
-    int qoff = 0;   // opaque offset: keeps LDS reads from moving across tiles
-    asm volatile("" : "+v"(qoff));
-    return sm.ring[t % kSlots] + qoff;
+      ld.issue(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
+    // the slot's offset in an opaque vector register: keeps LDS reads from
+    // moving across tiles, and each operand address is one add
+    int soff = (t % kSlots) * (kTile * kRowBytes);
+    asm volatile("" : "+v"(soff));
+    return sm.ring[0] + soff;
   };
   auto mask = [&](f32x16 (&acc)[kSub], int t) {
     const int kt = j0 + t * kTile;
@@ -344,8 +357,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // keeps three workgroups' registers per CU; visible after the first barrier
   if (tid < 128) sm.crow[tid] = tid < R ? stat[lh * R + tid] : __builtin_inff();   // padded rows weigh 0
   asm volatile("" ::: "memory");
+  RingLoader<6> ld;
+  init_loader_w123(ld, wave);
 #pragma unroll
-  for (int t = 0; t < kSlots - 1; ++t) load_tile_w123(kh, j0 + min(t, ntiles - 1) * kTile, n, wave, sm.ring[t]);
+  for (int t = 0; t < kSlots - 1; ++t) ld.issue(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
   wait_all();
   const int open_end = n - W;
   const float ident = MAXAGG ? -__builtin_inff() : 0.f;
@@ -368,10 +383,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     ring_barrier_lds();
     if (t >= 2) reduce(t - 2);
     if (t + kSlots - 1 < ntiles)
-      load_tile_w123(kh, j0 + (t + kSlots - 1) * kTile, n, wave, sm.ring[(t + kSlots - 1) % kSlots]);
-    int qoff = 0;   // opaque offset: keeps LDS reads from moving across tiles
-    asm volatile("" : "+v"(qoff));
-    return sm.ring[t % kSlots] + qoff;
+      ld.issue(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
+    // the slot's offset in an opaque vector register: keeps LDS reads from
+    // moving across tiles, and each operand address is one add
+    int soff = (t % kSlots) * (kTile * kRowBytes);
+    asm volatile("" : "+v"(soff));
+    return sm.ring[0] + soff;
   };
   // window rows hide keys past n - W + (row % W)
   auto mask = [&](f32x16 (&acc)[kSub], int t) {
@@ -486,7 +503,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-bool window_applicable(const ScorePlan& p) { return p.causal && p.R <= 128; }
+// The ring's buffer resources address a head's K with 31-bit byte offsets.
+bool window_applicable(const ScorePlan& p) {
+  return p.causal && p.R <= 128 && (long long)p.n * kRowBytes <= 0x7fffffffLL;
+}
 
 static int win_keys_per_block(const ScorePlan& p) {
   // >= ~2048 workgroups per pass when the cache is large; kTile granularity
