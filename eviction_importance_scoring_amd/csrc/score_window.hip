@@ -165,7 +165,6 @@ struct RingShared {
 struct ColsumShared {
   unsigned char ring[kSlots][kTile * kRowBytes];
   float colbuf[2][4][kTile];
-  float crow[128];            // row normalisers c_r (padding rows: +inf)
 };
 
 // ---------------------------------------------------------------- pass 1 ----
@@ -353,9 +352,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qa);
     else zero_ops(qa);
   }
-  // the row normalisers live in LDS (read 4 at a time by the folds), which
-  // keeps three workgroups' registers per CU; visible after the first barrier
-  if (tid < 128) sm.crow[tid] = tid < R ? stat[lh * R + tid] : __builtin_inff();   // padded rows weigh 0
+  // row normaliser of each accumulator register's row (padding rows weigh 0)
+  float crow[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = wave * 32 + acc_row(i, lane);
+    crow[i] = r < R ? stat[lh * R + r] : __builtin_inff();
+  }
   asm volatile("" ::: "memory");
   RingLoader<6> ld;
   init_loader_w123(ld, wave);
@@ -409,11 +412,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // part c (of 8): 4 rows of key set nt = c / 4 into the per-key partial
   auto fold_part = [&](const f32x16 (&acc)[kSub], int c, float (&pa)[kSub]) {
     const int nt = c >> 2, i0 = (c & 3) * 4;
-    // rows wave*32 + 8*(c&3) + 4*hf + u of registers i0 + u
-    const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.crow[wave * 32 + 2 * i0 + 4 * hf]);
 #pragma unroll
     for (int i = i0; i < i0 + 4; ++i) {
-      const float x = __builtin_fmaf(acc[nt][i], alpha, -c4[i - i0]);
+      const float x = __builtin_fmaf(acc[nt][i], alpha, -crow[i]);
       if (MAXAGG) pa[nt] = __builtin_fmaxf(pa[nt], x);
       else pa[nt] += fast_exp2(x);
     }

@@ -14,13 +14,19 @@
 // 11/11/9-bit digits over the score bits, then over the index bits, each
 // digit a 2048-bin LDS histogram; it stops as soon as the bucket that holds
 // the k-th key is taken whole. Members are then (key >> shift) >= prefix.
+// The final select stops after the score bits: if the last bucket (keys of
+// one score) is not taken whole, its first `need` entries in index order
+// are members, which the index-order emission counts with one more scan
+// instead of three more rounds over the index bits (max-pooling makes such
+// ties common).
 // Two-stage selection runs the select twice: first on the score (k1
-// entries), then on a key where stage-1 members are +inf and the others
-// carry the integrated score, which keeps exactly the k1 stage-1 members
-// plus the k - k1 best of the rest.
+// entries, down to a single key), then on a key where stage-1 members are
+// +inf and the others carry the integrated score, which keeps exactly the
+// k1 stage-1 members plus the k - k1 best of the rest.
 //
 // Segments of up to kResidentMax candidates are read from HBM once into
-// LDS; longer ones are streamed from memory on every pass.
+// the LDS of one workgroup; longer ones are spread over many workgroups
+// (below).
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
 
@@ -28,9 +34,11 @@ namespace kvsel {
 
 constexpr int kSelThreads = 1024;
 constexpr int kBins = 2048;
-constexpr int kResidentMax = 34816;          // 136 KiB of u32 keys in LDS
+constexpr int kResidentMax = 34816;          // 136 KiB of u32 keys in LDS (< 2^16)
 constexpr int kMaxGroups = 1024;             // heads per segment
 constexpr uint32_t kInfBits = 0x7F800000u;
+constexpr int kLoadUnroll = 8;              // loads in flight per thread
+constexpr int kMaxPer = 35;                  // candidates a thread emits (odd)
 
 struct SelArgs {
   const float* scores;
@@ -45,7 +53,7 @@ struct SelArgs {
   float score_norm, eps;
 };
 
-struct SelShared {
+struct alignas(16) SelShared {   // a multiple of 16 bytes: the keys follow it
   uint32_t hist[kBins];
   uint32_t sbuf[32];
   uint32_t group_start[kMaxGroups];
@@ -73,6 +81,16 @@ __device__ __forceinline__ int digit_width(int shift) {
   return (shift == 40 || shift == 9) ? 9 : 11;   // 62->51->40->31->20->9->0
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global stores (a plain __syncthreads would drain
+// the output stores of every emission round).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Exclusive scan of v over the 1024 threads; returns the block total too.
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,17 +114,25 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf, uint32_t& total)
   return off + x - v;
 }
 
-// One stage of radix select over the segment: finds (prefix, shift) such
-// that exactly k keys satisfy (key >> shift) >= prefix.
-template <typename KeyFn>
-__device__ void radix_select(SelShared& sm, uint32_t len, uint32_t k, KeyFn key_of,
-                             uint64_t& prefix_out, int& shift_out) {
+// Result of one radix-select stage. done: exactly k keys satisfy
+// (key >> shift) >= prefix. Otherwise the rounds stopped at shift 31 (the
+// score bits): the keys with (key >> 31) > prefix are members, and so are
+// the first `need` keys, in index order, of those with (key >> 31) ==
+// prefix (the index part of the key orders equal scores that way).
+struct SelCut {
+  uint64_t prefix;
+  int shift;
+  uint32_t need;
+  bool done;
+};
+
+// One stage of radix select over the segment's resident key bits, down to
+// stop_shift at most (0: to a single key).
+__device__ SelCut radix_select(SelShared& sm, const uint32_t* bits, uint32_t len, uint32_t k,
+                               int stop_shift) {
   const int tid = threadIdx.x;
-  if (k == 0 || k == len) {  // nothing, or everything
-    prefix_out = (k == 0) ? 1 : 0;
-    shift_out = 62;
-    return;
-  }
+  if (k == 0 || k == len)   // nothing, or everything
+    return SelCut{(k == 0) ? uint64_t(1) : uint64_t(0), 62, 0u, true};
   if (tid == 0) {
     sm.prefix = 0;
     sm.shift = 62;
@@ -121,10 +147,23 @@ __device__ void radix_select(SelShared& sm, uint32_t len, uint32_t k, KeyFn key_
     const int nb = 1 << wdt;
     for (int b = tid; b < kBins; b += kSelThreads) sm.hist[b] = 0;
     __syncthreads();
-    for (uint32_t f = tid; f < len; f += kSelThreads) {
-      const uint64_t key = key_of(f);
-      if ((key >> shift) == prefix)
-        atomicAdd(&sm.hist[(uint32_t)(key >> (shift - wdt)) & (nb - 1)], 1u);
+    if (shift - wdt >= 31 && (len & 3u) == 0) {
+      // the digit lies in the score bits: 32-bit compares on 4 keys a read
+      const uint32_t sh = shift - 31, dsh = shift - wdt - 31, p32 = (uint32_t)prefix;
+      const u32x4* b4 = reinterpret_cast<const u32x4*>(bits);
+      for (uint32_t i = tid; i < (len >> 2); i += kSelThreads) {
+        const u32x4 v = b4[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if ((uint32_t)((uint64_t)v[c] >> sh) == p32)   // sh may be 31
+            atomicAdd(&sm.hist[(v[c] >> dsh) & (nb - 1)], 1u);
+      }
+    } else {
+      for (uint32_t f = tid; f < len; f += kSelThreads) {
+        const uint64_t key = make_key(bits[f], f);
+        if ((key >> shift) == prefix)
+          atomicAdd(&sm.hist[(uint32_t)(key >> (shift - wdt)) & (nb - 1)], 1u);
+      }
     }
     __syncthreads();
     // bins in descending order: thread t holds bins nb-1-2t and nb-2-2t
@@ -149,14 +188,15 @@ __device__ void radix_select(SelShared& sm, uint32_t len, uint32_t k, KeyFn key_
       sm.need = need - sm.above;
     }
     __syncthreads();
-    if (sm.need == sm.dcount || sm.shift == 0) break;
+    if (sm.need == sm.dcount || sm.shift <= stop_shift) break;
   }
-  prefix_out = sm.prefix;
-  shift_out = sm.shift;
+  const SelCut cut{sm.prefix, sm.shift, sm.need, sm.need == sm.dcount || sm.shift == 0};
   __syncthreads();
+  return cut;
 }
 
-template <bool RESIDENT>
+// One workgroup per segment of at most kResidentMax candidates: the key
+// bits are read from HBM once into LDS and every pass runs there.
 __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SelShared& sm = *reinterpret_cast<SelShared*>(smem_raw);
@@ -167,92 +207,174 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   const float* wt = a.weight ? a.weight + seg * a.seg_len : nullptr;
   const uint32_t len = a.seg_len;
 
-  if (RESIDENT) {
-    for (uint32_t f = tid; f < len; f += kSelThreads) keys[f] = score_bits(sc[f]);
-    __syncthreads();
-  }
-  auto bits1 = [&](uint32_t f) -> uint32_t {
-    return RESIDENT ? keys[f] : score_bits(sc[f]);
-  };
-
-  // stage 1 (only when two-stage)
-  uint64_t p1 = 1;
-  int s1 = 62;
-  if (a.two_stage) {
-    radix_select(sm, len, a.k1, [&](uint32_t f) { return make_key(bits1(f), f); }, p1, s1);
-  }
-  auto member1 = [&](uint32_t f, uint32_t b1) -> bool {
-    return (make_key(b1, f) >> s1) >= p1;
-  };
-  if (RESIDENT && a.two_stage) {
-    for (uint32_t f = tid; f < len; f += kSelThreads) {
-      const uint32_t b1 = keys[f];
-      keys[f] = member1(f, b1) ? kInfBits : stage2_bits(sc[f], wt[f], a.score_norm, a.eps);
-    }
-    __syncthreads();
-  }
-  auto bits_final = [&](uint32_t f) -> uint32_t {
-    if (RESIDENT || !a.two_stage) return bits1(f);
-    const uint32_t b1 = score_bits(sc[f]);
-    return member1(f, b1) ? kInfBits : stage2_bits(sc[f], wt[f], a.score_norm, a.eps);
-  };
-
-  uint64_t pf;
-  int sf;
-  radix_select(sm, len, a.k, [&](uint32_t f) { return make_key(bits_final(f), f); }, pf, sf);
-
-  // ---- emission, in index order, 1024 candidates per round
-  int32_t* out = a.idx + seg * (size_t)a.budget;
-  uint8_t* st_out = a.stage ? a.stage + seg * (size_t)a.budget : nullptr;
-  const int lane = tid & 63, wave = tid >> 6;
-  uint32_t running = 0;
-  for (uint32_t base = 0; base < len; base += kSelThreads) {
-    const uint32_t f = base + tid;
-    bool mem = false;
-    uint32_t bf = 0;
-    if (f < len) {
-      bf = bits_final(f);
-      mem = (make_key(bf, f) >> sf) >= pf;
-    }
-    const uint64_t ballot = __ballot(mem);
-    const uint32_t lane_rank = __builtin_amdgcn_mbcnt_hi(
-        (uint32_t)(ballot >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
-    if (lane == 0) sm.sbuf[wave] = __popcll(ballot);
-    __syncthreads();
-    uint32_t woff = 0, rtot = 0;
+  // every load of a sweep in flight at once (one wait per sweep)
+  if ((len & 3u) == 0) {
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(sc);
+    u32x4* k4 = reinterpret_cast<u32x4*>(keys);
+    const uint32_t n4 = len >> 2;
+    for (uint32_t base = 0; base < n4; base += kLoadUnroll * kSelThreads) {
+      u32x4 v[kLoadUnroll];
 #pragma unroll
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      const uint32_t t = sm.sbuf[w];
-      woff += (w < wave) ? t : 0u;
-      rtot += t;
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const uint32_t i = base + u * kSelThreads + tid;
+        v[u] = i < n4 ? __builtin_nontemporal_load(s4 + i) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const uint32_t i = base + u * kSelThreads + tid;
+        if (i < n4)
+          k4[i] = u32x4{score_bits(__uint_as_float(v[u].x)), score_bits(__uint_as_float(v[u].y)),
+                        score_bits(__uint_as_float(v[u].z)), score_bits(__uint_as_float(v[u].w))};
+      }
     }
-    const uint32_t before = running + woff + lane_rank;  // members with index < f
-    if (f < len) {
-      const uint32_t g = f / a.n_cand, pos = f - g * a.n_cand;
-      if (pos == 0) sm.group_start[g] = before;
-      if (mem) {
-        const uint32_t o = before + g * a.W;
-        if (o < a.budget) {   // exactly k members: always true; never write past the segment
-          out[o] = (int32_t)pos;
-          if (st_out) st_out[o] = (!a.two_stage || bf == kInfBits) ? 1 : 2;
+  } else {
+    for (uint32_t base = 0; base < len; base += kLoadUnroll * kSelThreads) {
+      float v[kLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const uint32_t f = base + u * kSelThreads + tid;
+        v[u] = f < len ? sc[f] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const uint32_t f = base + u * kSelThreads + tid;
+        if (f < len) keys[f] = score_bits(v[u]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // stage 1 (two-stage only), all the way down: stage-1 membership stays a
+  // test on the key, which stage 2 turns into +inf
+  if (a.two_stage) {
+    const SelCut c1 = radix_select(sm, keys, len, a.k1, 0);
+    for (uint32_t base = 0; base < len; base += kLoadUnroll * kSelThreads) {
+      float sv[kLoadUnroll], wv[kLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const uint32_t f = base + u * kSelThreads + tid;
+        sv[u] = f < len ? sc[f] : 0.f;
+        wv[u] = f < len ? wt[f] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const uint32_t f = base + u * kSelThreads + tid;
+        if (f < len)
+          keys[f] = (make_key(keys[f], f) >> c1.shift) >= c1.prefix
+                        ? kInfBits : stage2_bits(sv[u], wv[u], a.score_norm, a.eps);
+      }
+    }
+    __syncthreads();
+  }
+
+  const SelCut cf = radix_select(sm, keys, len, a.k, 31);
+
+  // ---- emission, in index order. Thread t owns the `per` consecutive
+  // candidates from t*per (per odd, so the LDS reads of a wave fall in
+  // distinct banks); block scans give each thread the members (and tied
+  // bucket entries) before its range. Members are staged by rank in LDS
+  // (over the keys, which are no longer needed) and then written out with
+  // coalesced stores.
+  static_assert(((kResidentMax + kSelThreads - 1) / kSelThreads | 1) <= kMaxPer, "one 64-bit mask a thread");
+  const uint32_t per = ((len + kSelThreads - 1) / kSelThreads) | 1u;
+  const uint32_t f0 = min(len, tid * per), f1 = min(len, f0 + per);
+  // (key >> shift) vs prefix on the score bits alone; prefix 1 at shift 62
+  // (select nothing) stays out of reach of every 31-bit score
+  const uint32_t csh = (uint32_t)cf.shift - 31u;
+  const uint32_t cp = cf.prefix > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)cf.prefix;
+  // every read first (clamped in range), then branch-free tests
+  uint32_t bv[kMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) bv[j] = keys[min(f0 + j, len - 1)];
+  const bool done = cf.done;
+  uint64_t mmask = 0, emask = 0, imask = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const bool valid = f0 + j < f1;
+    const uint32_t top = (uint32_t)((uint64_t)bv[j] >> csh);   // the select stopped at shift >= 31
+    const bool eq = top == cp;
+    const bool mem = valid && (top > cp || (done && eq));
+    const bool tie = valid && !done && eq;
+    mmask |= (uint64_t)mem << j;
+    emask |= (uint64_t)tie << j;
+    imask |= (uint64_t)(bv[j] == kInfBits) << j;
+  }
+  // one scan of (tied entries, members) before each thread's range: the
+  // tied members are the first cf.need tied entries in index order, so the
+  // members before the range are mem_before + min(need, tied_before)
+  uint32_t tot;
+  const uint32_t packed = ((uint32_t)__popcll(emask) << 16) | (uint32_t)__popcll(mmask);
+  const uint32_t before = block_excl_scan(packed, sm.sbuf, tot);   // both sums < 2^16
+  const uint32_t tied_before = before >> 16;
+  const uint32_t need = done ? 0u : cf.need;
+  uint32_t rank = (before & 0xFFFFu) + min(need, tied_before);
+  for (uint64_t e = emask, t = tied_before; e != 0 && t < need; e &= e - 1, ++t)
+    mmask |= e & (~e + 1);
+  // staged[r] = position in its head of the member of rank r, bit 31 set
+  // for a stage-2 member of the two-stage selection
+  uint32_t* staged = keys;
+  if (f0 < f1) {
+    const uint32_t g0 = f0 / a.n_cand, gstart = g0 * a.n_cand;
+    if (gstart == f0) sm.group_start[g0] = rank;   // members before each group
+    for (uint32_t gs = gstart + a.n_cand; gs < f1; gs += a.n_cand)
+      sm.group_start[gs / a.n_cand] = rank + (uint32_t)__popcll(mmask & ((uint64_t(1) << (gs - f0)) - 1));
+    if (a.n_cand >= (uint32_t)kMaxPer) {   // at most one group boundary in the range
+      const uint32_t next = gstart + a.n_cand;
+      uint32_t r = rank;
+#pragma unroll
+      for (int j = 0; j < kMaxPer; ++j) {
+        if ((mmask >> j) & 1u) {
+          const uint32_t f = f0 + j;
+          const uint32_t pos = f - (f >= next ? next : gstart);
+          const bool second = a.two_stage && !((imask >> j) & 1u);
+          if (r < a.k) staged[r] = pos | (second ? 0x80000000u : 0u);   // r < k always
+          ++r;
         }
       }
-    }
-    running += rtot;
-    __syncthreads();
-  }
-  // window entries after each group's members, and the group offsets
-  for (uint32_t g = 0; g < a.groups; ++g) {
-    const uint32_t end_rank = (g + 1 < a.groups) ? sm.group_start[g + 1] : a.k;
-    const uint32_t end = end_rank + (g + 1) * a.W;
-    for (uint32_t t = tid; t < a.W; t += kSelThreads) {
-      if (end - a.W + t < a.budget) {
-        out[end - a.W + t] = (int32_t)(a.n - a.W + t);
-        if (st_out) st_out[end - a.W + t] = 0;
+    } else {
+      uint32_t gs = gstart;
+      for (uint64_t m = mmask; m != 0; m &= m - 1, ++rank) {
+        const uint32_t j = (uint32_t)__builtin_ctzll(m);
+        const uint32_t f = f0 + j;
+        while (f >= gs + a.n_cand) gs += a.n_cand;
+        const bool second = a.two_stage && !((imask >> j) & 1u);
+        if (rank < a.k) staged[rank] = (f - gs) | (second ? 0x80000000u : 0u);   // rank < k always
       }
     }
-    if (a.head_offsets && tid == 0) a.head_offsets[seg * (a.groups + 1) + g] = sm.group_start[g] + g * a.W;
   }
+  lds_barrier();
+  // output slot o: group g's members then its W window entries, groups in
+  // order (slot of group g's first member: group_start[g] + g*W)
+  int32_t* out = a.idx + seg * (size_t)a.budget;
+  uint8_t* st_out = a.stage ? a.stage + seg * (size_t)a.budget : nullptr;
+  for (uint32_t o = tid; o < a.budget; o += kSelThreads) {
+    uint32_t g = 0;
+    if (a.groups > 1) {   // last group whose first slot is <= o
+      uint32_t lo = 0, hi = a.groups - 1;
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (sm.group_start[mid] + mid * a.W <= o) lo = mid; else hi = mid - 1;
+      }
+      g = lo;
+    }
+    const uint32_t first = sm.group_start[g];
+    const uint32_t count = (g + 1 < a.groups ? sm.group_start[g + 1] : a.k) - first;
+    const uint32_t local = o - (first + g * a.W);
+    int32_t v;
+    uint8_t sv;
+    if (local < count) {
+      const uint32_t e = staged[first + local];
+      v = (int32_t)(e & 0x7FFFFFFFu);
+      sv = (e >> 31) ? 2 : 1;
+    } else {
+      v = (int32_t)(a.n - a.W + (local - count));
+      sv = 0;
+    }
+    out[o] = v;
+    if (st_out) st_out[o] = sv;
+  }
+  if (a.head_offsets && tid < (int)a.groups)
+    a.head_offsets[seg * (a.groups + 1) + tid] = (int32_t)(sm.group_start[tid] + tid * a.W);
   if (a.head_offsets && tid == 0) a.head_offsets[seg * (a.groups + 1) + a.groups] = (int32_t)a.budget;
 }
 
@@ -717,9 +839,7 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   return hipGetLastError();
 }
 
-static size_t lds_bytes(bool resident, uint32_t len) {
-  return sizeof(SelShared) + (resident ? (size_t)len * sizeof(uint32_t) : 0);
-}
+static size_t lds_bytes(uint32_t len) { return sizeof(SelShared) + (size_t)len * sizeof(uint32_t); }
 
 size_t select_ws_bytes(const SelectPlan& p) { return use_multi(p) ? msel_layout(p).bytes : 0; }
 
@@ -744,20 +864,11 @@ hipError_t select_launch(const SelectPlan& p, const float* scores, const float* 
   a.score_norm = p.score_norm;
   a.eps = p.eps;
   if (use_multi(p)) return msel_launch(p, scores, weight, idx, head_offsets, stage, ws, st);
-  const bool resident = p.seg_len <= kResidentMax;
-  const size_t lds = lds_bytes(resident, a.seg_len);
-  hipError_t e;
-  if (resident) {
-    e = hipFuncSetAttribute((const void*)k_select<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_select<true>, dim3(p.segments), dim3(kSelThreads), lds, st, a);
-  } else {
-    e = hipFuncSetAttribute((const void*)k_select<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_select<false>, dim3(p.segments), dim3(kSelThreads), lds, st, a);
-  }
+  const size_t lds = lds_bytes(a.seg_len);
+  const hipError_t e =
+      hipFuncSetAttribute((const void*)k_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_select, dim3(p.segments), dim3(kSelThreads), lds, st, a);
   return hipGetLastError();
 }
 

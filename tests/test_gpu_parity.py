@@ -140,8 +140,11 @@ SELECT_CASES = [
     (1, 3, 1500, 8, 0.25, True, True, 0.5, 1000000),
     (1, 2, 500, 4, 0.3, False, True, 0.0, 10),
     (1, 2, 500, 4, 0.3, False, True, 1.0, 10),
-    (1, 1, 50000, 32, 0.1, False, False, 0.5, 1000),      # longer than LDS: streamed
-    (1, 2, 40000, 32, 0.1, True, True, 0.5, 100000),      # streamed, two-stage, adaptive
+    (1, 8, 4000, 8, 0.3, True, False, 0.5, 5),            # one workgroup: 33 candidates a thread, head starts inside ranges
+    (1, 8, 40, 8, 0.5, True, False, 0.5, 3),              # heads shorter than a thread's range
+    (1, 16, 30, 4, 0.5, True, True, 0.5, 3),              # the same, two-stage
+    (1, 1, 50000, 32, 0.1, False, False, 0.5, 1000),      # longer than LDS: many workgroups
+    (1, 2, 40000, 32, 0.1, True, True, 0.5, 100000),      # many workgroups, two-stage, adaptive
     # segments over the LDS size run on many workgroups (chunks of 8192)
     (2, 8, 9032, 32, 0.2, True, False, 0.5, 50),          # adaptive, 8 heads, ties
     (1, 3, 20000, 0, 0.3, True, False, 0.5, 5),           # adaptive, no window, heavy ties
