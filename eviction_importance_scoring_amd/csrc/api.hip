@@ -53,6 +53,10 @@ int32_t kvsel_score(const void* q, const void* k, int32_t L, int32_t H_kv, int32
   if (d != kHeadDimPublic) return KVSEL_ERR_UNSUPPORTED;
   if (pool > 65) return KVSEL_ERR_UNSUPPORTED;
   if ((int64_t)G * W > kMaxIndex || (int64_t)H_kv * n > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  // the kernels address one head's K, and one head's query rows, through
+  // buffer resources with 31-bit byte offsets
+  if ((int64_t)n * kRowBytesPublic > kMaxIndex || (int64_t)G * W * kRowBytesPublic > kMaxIndex)
+    return KVSEL_ERR_UNSUPPORTED;
   ScorePlan p;
   p.L = L; p.H = H_kv; p.G = G; p.n = n; p.W = W;
   p.R = G * W;
@@ -86,6 +90,8 @@ int32_t kvsel_value_weight(const void* v, const void* w_o, int32_t L, int32_t H_
   if (!aligned16(v) || !aligned16(w_o) || !aligned16(weight)) return KVSEL_ERR_ARG;
   if (d != kHeadDimPublic || D % 32 != 0) return KVSEL_ERR_UNSUPPORTED;
   if ((int64_t)H_kv * G * d > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  // w_o is read through buffer resources with 31-bit byte offsets
+  if ((int64_t)D * H_kv * G * d * 2 > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
   const hipError_t e = value_weight_launch(v, w_o, L, H_kv, G, n, D, n_cand, weight,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;

@@ -8,6 +8,7 @@
 namespace kvsel {
 
 constexpr int kHeadDimPublic = 128;   // the head dimension the library accepts
+constexpr int kRowBytesPublic = kHeadDimPublic * 2;   // one bf16 row
 
 // ------------------------------------------------------------- scoring ----
 struct ScorePlan {

@@ -3,7 +3,7 @@
 //
 // A workgroup of gWaves waves streams a shared [rows][128] bf16 operand in
 // 64-row tiles through a ring of gSlots LDS slots. Slots are filled with
-// direct global->LDS loads (global_load_lds_dwordx4): each instruction
+// direct-to-LDS loads (buffer_load_dwordx4 ... lds): each instruction
 // moves 4 whole 256-byte rows, the 16-byte pieces of row r stored XOR-
 // swizzled by (r & 15) so that the MFMA operand reads (one half row per
 // lane) are free of bank conflicts. Each wave multiplies every tile by its
@@ -34,7 +34,7 @@ typedef __attribute__((address_space(1))) const void* glb_ptr_t;
 // ring's loads stay in flight across it); LDS visibility comes from the
 // explicit waits below. It does not wait for the wave's own ds_write
 // operations either, so the kernels built on it write LDS only through the
-// direct global->LDS loads.
+// direct-to-LDS loads.
 __device__ __forceinline__ void gen_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -70,22 +70,40 @@ __device__ __forceinline__ void gen_wait_tile(int t, int ntiles) {
   gen_wait_ahead<PER, gSlots - 2>(issued - (t + 1));
 }
 
-// This wave's share of rows [row0, row0 + 64) of a bf16 matrix with `rows`
-// rows of 128 elements, `stride` elements apart, into `slot` (rows past the
-// end repeat row rows-1; their results are never used).
-__device__ __forceinline__ void gen_load_tile(const __bf16* base, int row0, int rows, int stride,
-                                              unsigned char* slot) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// This wave's share (gLoads chunks of 1 KB, chunk c = tile rows 4c..4c+3)
+// of rows [row0, row0 + 64) of a bf16 matrix with `rows` rows of 128
+// elements, `stride` elements apart, into `slot`. Loads go through a raw
+// buffer resource based at the tile's first row and ending after row
+// rows-1: the lane offsets (row r = 4c + lane/16, swizzled piece) are fixed
+// per kernel, so a tile costs no vector instructions, and rows past the end
+// are cut off by the hardware range check (their results are never used).
+// The whole matrix must span less than 2^31 bytes (checked by the API).
+[[maybe_unused]] constexpr int kRawBufferWord3 = 0x00020000;   // untyped 32-bit data format
+struct GenLoader {
+  uint32_t off[gLoads];
+  __device__ __forceinline__ void init(int stride) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < gLoads; ++i) {
-    const int chunk = wave * gLoads + i;
-    const int r = chunk * 4 + (lane >> 4);
-    const int piece = (lane & 15) ^ (r & 15);
-    const int row = min(row0 + r, rows - 1);
-    const char* src = reinterpret_cast<const char*>(base + (size_t)row * stride) + piece * 16;
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)(slot + chunk * 1024), 16, 0, 0);
+    for (int i = 0; i < gLoads; ++i) {
+      const int r = (wave * gLoads + i) * 4 + (lane >> 4);
+      off[i] = (uint32_t)r * (uint32_t)stride * 2u + (uint32_t)(((lane & 15) ^ (r & 15)) << 4);
+    }
   }
-}
+  // row0 < rows
+  __device__ __forceinline__ void issue(const __bf16* base, int row0, int rows, int stride,
+                                        unsigned char* slot) const {
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bytes = ((rows - 1 - row0) * stride + kHeadDim) * 2;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(base + (size_t)row0 * stride), 0, bytes, kRawBufferWord3);
+#pragma unroll
+    for (int i = 0; i < gLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(slot + (wave * gLoads + i) * 1024), 16,
+                                               off[i], 0, 0, 0);
+#endif
+  }
+};
 
 // MFMA operand of step s, lane half hf, for row r of a ring slot.
 __device__ __forceinline__ bf16x8 gen_op(const unsigned char* slot, int r, int hf, int s) {

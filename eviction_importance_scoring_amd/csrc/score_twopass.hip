@@ -81,11 +81,12 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     else zero_ops(qb[nt]);
     last[nt] = row < R ? (CAUSAL ? n - W + row % W : n - 1) : -1;   // last visible key
   }
+  GenLoader ld;
+  ld.init(kHeadDim);
   asm volatile("" ::: "memory");
   // the first gSlots-1 tiles (repeating the last one if there are fewer)
 #pragma unroll
-  for (int t = 0; t < gSlots - 1; ++t)
-    gen_load_tile(kh, j0 + min(t, ntiles - 1) * gTile, n, kHeadDim, ring[t]);
+  for (int t = 0; t < gSlots - 1; ++t) ld.issue(kh, j0 + min(t, ntiles - 1) * gTile, n, kHeadDim, ring[t]);
   // Q is in registers once at most the prologue's loads are in flight; an
   // explicit wait here keeps the compiler from waiting inside the loop
   gen_wait<(gSlots - 1) * gLoads>();
@@ -148,11 +149,12 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     gen_wait_tile<gLoads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles)
-      gen_load_tile(kh, j0 + (t + gSlots - 1) * gTile, n, kHeadDim, ring[(t + gSlots - 1) % gSlots]);
-    // opaque offset: keeps the compiler from moving LDS reads across tiles
-    int qoff = 0;
-    asm volatile("" : "+v"(qoff));
-    return ring[t % gSlots] + qoff;
+      ld.issue(kh, j0 + (t + gSlots - 1) * gTile, n, kHeadDim, ring[(t + gSlots - 1) % gSlots]);
+    // the slot's offset in an opaque vector register: keeps LDS reads from
+    // moving across tiles, and each operand address is one add
+    int soff = (t % gSlots) * gRowsBytes;
+    asm volatile("" : "+v"(soff));
+    return ring[0] + soff;
   };
   auto zero_acc = [&](f32x16 (&acc)[2][2]) {
 #pragma unroll
@@ -301,8 +303,10 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
     else zero_ops(kop[nt]);
   }
   // a row tile: the Q rows (all waves) and their -c_r / alpha (wave 0)
+  GenLoader ld;
+  ld.init(kHeadDim);
   auto issue = [&](int t, int slot) {
-    gen_load_tile(qh, t * gTile, R, kHeadDim, ring[slot]);
+    ld.issue(qh, t * gTile, R, kHeadDim, ring[slot]);
     if (wave == 0)
       __builtin_amdgcn_global_load_lds((glb_ptr_t)(sh + t * gTile + lane),
                                        (lds_ptr_t)(ring[slot] + gRowsBytes), 4, 0, 0);
@@ -323,9 +327,9 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
     else gen_wait_tile<gLoads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
-    int qoff = 0;
-    asm volatile("" : "+v"(qoff));
-    return ring[t % gSlots] + qoff;
+    int soff = (t % gSlots) * gSlotBytes;   // opaque: LDS reads stay inside the tile
+    asm volatile("" : "+v"(soff));
+    return ring[0] + soff;
   };
   // acc = <q_r, k> - c_r / alpha: start from the tile's normalisers
   // (padding rows: -inf)

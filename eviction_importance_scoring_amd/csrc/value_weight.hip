@@ -52,9 +52,11 @@ __global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__
     else zero_ops(vop[nt]);
   }
   // tile t: output features [64*dt, 64*dt + 64) of query head h*G + g
+  GenLoader ld;
+  ld.init(stride);
   auto issue = [&](int t, int slot) {
     const int g = t / dtiles, dt = t - g * dtiles;
-    gen_load_tile(wl + (size_t)(h * G + g) * kHeadDim, dt * gTile, D, stride, ring[slot]);
+    ld.issue(wl + (size_t)(h * G + g) * kHeadDim, dt * gTile, D, stride, ring[slot]);
   };
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -69,9 +71,9 @@ __global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__
     gen_wait_tile<gLoads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
-    int qoff = 0;
-    asm volatile("" : "+v"(qoff));
-    return ring[t % gSlots] + qoff;
+    int soff = (t % gSlots) * gRowsBytes;   // opaque: LDS reads stay inside the tile
+    asm volatile("" : "+v"(soff));
+    return ring[0] + soff;
   };
   // D % 64 == 32: the last tile of each g has 32 real rows; its other 32
   // MFMA rows get zero operands (|0| adds nothing)

@@ -89,8 +89,10 @@ enum {
  *   scale  softmax temperature (the model's 1/sqrt(d)), > 0
  *   pool   odd, >= 1 (1 = no pooling)
  *
- * Limits: d == 128 (else KVSEL_ERR_UNSUPPORTED); window mode needs
- * 1 <= W < n. Needs a workspace (protocol above).
+ * Limits: d == 128; one head's K and one head's query rows must each span
+ * less than 2^31 bytes (n <= 8388607 and G*W <= 8388607); else
+ * KVSEL_ERR_UNSUPPORTED. Window mode needs 1 <= W < n. Needs a workspace
+ * (protocol above).
  */
 int32_t kvsel_score(const void* q, const void* k,
                     int32_t L, int32_t H_kv, int32_t G, int32_t d, int32_t n,
@@ -114,7 +116,8 @@ int32_t kvsel_score(const void* q, const void* k,
  *   w_o    bf16 [L][D][H_kv*G*d]     output projection, (out, in) layout
  *   weight f32  [L][H_kv][n_cand]    1 <= n_cand <= n
  *
- * Limits: d == 128, D % 32 == 0 (else KVSEL_ERR_UNSUPPORTED).
+ * Limits: d == 128, D % 32 == 0, and one layer's w_o must span less than
+ * 2^31 bytes (D * H_kv*G*d * 2 < 2^31); else KVSEL_ERR_UNSUPPORTED.
  */
 int32_t kvsel_value_weight(const void* v, const void* w_o,
                            int32_t L, int32_t H_kv, int32_t G, int32_t d,
