@@ -72,6 +72,9 @@ def test_score_workspace_query(lib):
     (dict(scale=0.0), ARG), (dict(scale=-1.0), ARG), (dict(scale=float("inf")), ARG),
     (dict(scale=float("nan")), ARG), (dict(pool=0), ARG), (dict(pool=4), ARG),
     (dict(d=64), UNSUP), (dict(pool=67), UNSUP),
+    # one head's K (or query rows) reaching 2^31 bytes: n * 256 >= 2^31
+    (dict(H=1, n=1 << 23), UNSUP), (dict(H=1, G=1, n=1 << 23, W=(1 << 23) - 1), UNSUP),
+    (dict(H=1, n=(1 << 23) - 1), OK), (dict(H=1, G=2, W=1 << 22, n=(1 << 22) + 1), UNSUP),
 ])
 def test_score_rejects(lib, kw, code):
     assert _score(lib, **kw)[0] == code
@@ -139,6 +142,7 @@ def test_value_weight_and_compact_reject(lib):
     assert f(p, p, 1, 8, 4, 128, 100, 4096, 0, p, None) == ARG
     assert f(p, p, 1, 8, 4, 64, 100, 4096, 68, p, None) == UNSUP
     assert f(p, p, 1, 8, 4, 128, 100, 4010, 68, p, None) == UNSUP   # D % 32
+    assert f(p, p, 1, 8, 4, 128, 100, 1 << 18, 68, p, None) == UNSUP  # w_o of 2^31 bytes
     c = lib.kvsel_compact
     assert c(None, p, 1, 8, 128, 100, p, None, 16, p, p, None) == ARG
     assert c(p, p, 1, 8, 128, 100, p, None, 12, p, p, None) == ARG  # not divisible by H
