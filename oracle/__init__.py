@@ -33,6 +33,8 @@ Readings taken where the pages are silent (each repeated where it is used):
   ties      larger key first; equal keys go to the lower index (adaptive:
             lower head, then lower position). Output positions ascending.
   max mode  KVzip's max over queries, softmax over the n cached keys only.
+  decode    attention of one new query per query head over its KV head's
+            kept rows only; an empty head gives zeros.
 """
 from __future__ import annotations
 
@@ -278,3 +280,39 @@ def compact_layer(k: np.ndarray, v: np.ndarray, idx: np.ndarray,
         ko.append(k[h, sl])
         vo.append(v[h, sl])
     return np.concatenate(ko), np.concatenate(vo)
+
+
+# ------------------------------------------------ decode over the kept rows ----
+
+def decode_attention(q: np.ndarray, k_kept: np.ndarray, v_kept: np.ndarray, G: int,
+                     scale: float, head_offsets: np.ndarray | None = None) -> np.ndarray:
+    """One decoding step of attention over the compacted cache of one layer.
+
+    [KVzip, §7.1] (decoding efficiency): after eviction every KV head keeps
+    its own number of rows (non-uniform head budgets), and a new token's
+    attention runs over each head's kept rows with a variable-length kernel.
+    The query of query head h*G+g attends over the kept rows of KV head h:
+        out[h*G+g] = softmax_t(scale * <q[h*G+g], k_t>) . v_t   (t kept in h)
+    Readings: the call covers the kept rows only (the new token's own K/V
+    are the caller's to append); a head with no kept rows gives zeros.
+
+    q [H*G][d]; uniform layout: k_kept, v_kept [H][B][d]; packed layout:
+    [B_layer][d] with head_offsets [H+1] (the kvsel_compact layouts).
+    Returns [H*G][d] float64.
+    """
+    q = np.asarray(q, np.float64)
+    k_kept = np.asarray(k_kept, np.float64)
+    v_kept = np.asarray(v_kept, np.float64)
+    if head_offsets is None:
+        heads = [(k_kept[h], v_kept[h]) for h in range(k_kept.shape[0])]
+    else:
+        heads = [(k_kept[head_offsets[h]:head_offsets[h + 1]], v_kept[head_offsets[h]:head_offsets[h + 1]])
+                 for h in range(len(head_offsets) - 1)]
+    out = np.zeros((len(heads) * G, q.shape[-1]))
+    for h, (kh, vh) in enumerate(heads):
+        if kh.shape[0] == 0:
+            continue
+        for g in range(G):
+            p = _softmax_rows(scale * (q[h * G + g] @ kh.T)[None, :])[0]
+            out[h * G + g] = p @ vh
+    return out

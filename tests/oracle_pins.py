@@ -391,9 +391,84 @@ def check_compact(o):
     np.testing.assert_array_equal(vo, np.concatenate([v[0, idx[0][:2]], v[2, idx[2]]]))
 
 
+# ------------------------------------------------- decode over kept rows ----
+
+def check_decode_hand_example(o):
+    g = load_golden("decode_hand_example.txt")
+    k = np.zeros((1, 3, 4))
+    k[0, :, 0] = g["key_x"]
+    v = np.asarray(g["values"]).reshape(1, 3, 4)
+    q = np.array([[1.0, 0, 0, 0]])
+    np.testing.assert_allclose(o.decode_attention(q, k, v, 1, 1.0)[0], g["out"], rtol=1e-12, atol=1e-14)
+
+
+def check_decode_bruteforce(o):
+    """Explicit loops (exp, sums, no matrix products) on ragged heads,
+    one of them empty."""
+    rng = np.random.default_rng(31)
+    H, G, d, scale = 3, 2, 5, 0.7
+    offs = np.array([0, 4, 4, 11])
+    k = rng.normal(size=(11, d))
+    v = rng.normal(size=(11, d))
+    q = rng.normal(size=(H * G, d))
+    got = o.decode_attention(q, k, v, G, scale, offs)
+    for h in range(H):
+        rows = range(offs[h], offs[h + 1])
+        for g in range(G):
+            hq = h * G + g
+            if not len(rows):
+                np.testing.assert_array_equal(got[hq], np.zeros(d))
+                continue
+            logits = [scale * sum(q[hq, e] * k[t, e] for e in range(d)) for t in rows]
+            mx = max(logits)
+            w = [math.exp(x - mx) for x in logits]
+            z = sum(w)
+            ref = [sum(w[i] / z * v[t, e] for i, t in enumerate(rows)) for e in range(d)]
+            np.testing.assert_allclose(got[hq], ref, rtol=1e-12, atol=1e-14)
+
+
+def check_decode_sdpa(o):
+    """Uniform heads against torch's scaled_dot_product_attention (fp64),
+    the KV heads repeated for their G query heads."""
+    import torch
+    rng = np.random.default_rng(32)
+    H, G, B, d, scale = 2, 3, 9, 8, 0.35
+    k = rng.normal(size=(H, B, d))
+    v = rng.normal(size=(H, B, d))
+    q = rng.normal(size=(H * G, d))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, :], torch.from_numpy(k).repeat_interleave(G, 0),
+        torch.from_numpy(v).repeat_interleave(G, 0), scale=scale)[:, 0].numpy()
+    np.testing.assert_allclose(o.decode_attention(q, k, v, G, scale), ref, rtol=1e-12, atol=1e-14)
+
+
+def check_decode_closed_forms(o):
+    rng = np.random.default_rng(33)
+    d = 6
+    q = rng.normal(size=(2, d))
+    # equal keys: the mean of the values
+    k = np.tile(rng.normal(size=(1, 1, d)), (1, 5, 1))
+    v = rng.normal(size=(1, 5, d))
+    np.testing.assert_allclose(o.decode_attention(q, k, v, 2, 0.5), np.tile(v[0].mean(0), (2, 1)),
+                               rtol=1e-12, atol=1e-14)
+    # one row: its value exactly
+    np.testing.assert_allclose(o.decode_attention(q[:1], k[:, :1], v[:, :1], 1, 0.5)[0], v[0, 0],
+                               rtol=1e-15)
+    # a dominant key: its value
+    k2 = rng.normal(size=(1, 5, d)) * 0.01
+    k2[0, 2] = q[0] * 100
+    np.testing.assert_allclose(o.decode_attention(q[:1], k2, v, 1, 1.0)[0], v[0, 2], rtol=1e-9)
+    # the order of a head's rows does not matter
+    k3 = rng.normal(size=(1, 5, d))
+    perm = rng.permutation(5)
+    np.testing.assert_allclose(o.decode_attention(q, k3, v, 2, 0.3),
+                               o.decode_attention(q, k3[:, perm], v[:, perm], 2, 0.3), rtol=1e-12)
+
+
 ALL_CHECKS = [
     check_window_bruteforce, check_window_sum_invariant, check_window_equal_keys,
     check_window_hand_example, check_window_single_query_softmax, check_window_max_agg,
     check_external, check_maxpool, check_value_weight, check_select_examples,
     check_select_bruteforce, check_select_reductions, check_compact,
+    check_decode_hand_example, check_decode_bruteforce, check_decode_sdpa, check_decode_closed_forms,
 ]

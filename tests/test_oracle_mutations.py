@@ -35,6 +35,14 @@ MUTANTS = {
     "stage2_from_all": ("cand = np.nonzero(rest)[0]", "cand = np.arange(score.shape[0])"),
     "adaptive_transposed": ("flat = scores.reshape(-1)", "flat = scores.T.reshape(-1)"),
     "window_not_counted": ("        k = budget - W\n        assert 0 <= k <= n_cand", "        k = max(budget - 2 * W, 0)\n        assert 0 <= k <= n_cand"),
+    "decode_no_scale": ("p = _softmax_rows(scale * (q[h * G + g] @ kh.T)[None, :])[0]",
+                        "p = _softmax_rows((q[h * G + g] @ kh.T)[None, :])[0]"),
+    "decode_gqa_interleaved": ("p = _softmax_rows(scale * (q[h * G + g] @ kh.T)[None, :])[0]",
+                               "p = _softmax_rows(scale * (q[g * len(heads) + h] @ kh.T)[None, :])[0]"),
+    "decode_values_from_keys": ("out[h * G + g] = p @ vh", "out[h * G + g] = p @ kh"),
+    "decode_offsets_shifted": ("heads = [(k_kept[head_offsets[h]:head_offsets[h + 1]], v_kept[head_offsets[h]:head_offsets[h + 1]])",
+                               "heads = [(k_kept[head_offsets[h]:head_offsets[h + 1]], v_kept[head_offsets[h] + 1:head_offsets[h + 1] + 1])"),
+    "decode_uniform_weights": ("out[h * G + g] = p @ vh", "out[h * G + g] = vh.mean(axis=0)"),
     "compact_wrong_head": ("return (np.stack([k[h, idx[h]] for h in range(H)]),", "return (np.stack([k[0, idx[h]] for h in range(H)]),"),
 }
 
