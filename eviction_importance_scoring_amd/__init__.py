@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_value_weight",
-    "kvsel_select", "kvsel_compact", "kvsel_status_str", "kvsel_abi_version",
+    "kvsel_select", "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
+    "kvsel_abi_version",
     "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX",
 ]
 
@@ -44,6 +45,9 @@ _SIGNATURES = {
                      _c_size_p, _c_void_p],
     "kvsel_compact": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                       _c_void_p, _c_i64, _c_void_p, _c_void_p, _c_void_p],
+    "kvsel_decode_attention": [_c_void_p, _c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32,
+                               _c_i64, _c_void_p, _c_f32, _c_void_p, _c_void_p, _c_size_p,
+                               _c_void_p],
     "kvsel_status_str": [_c_i32],
     "kvsel_abi_version": [],
 }
@@ -209,3 +213,45 @@ def kvsel_compact(k, v, idx, head_offsets=None):
     _check(lib().kvsel_compact(_ptr(k), _ptr(v), L, H, d, n, _ptr(idx), _ptr(head_offsets),
                                kept, _ptr(k_out), _ptr(v_out), _stream(k.device)))
     return k_out, v_out
+
+
+def kvsel_decode_attention(q, k_kept, v_kept, *, G: int, scale: float | None = None,
+                           head_offsets=None, out=None, workspace=None):
+    """One decoding step over the kept rows. q bf16 [L][H_kv*G][d];
+    k_kept, v_kept bf16 [L][kept_per_layer][d] (kvsel_compact's output);
+    head_offsets i32 [L][H_kv+1] or None (uniform heads). Returns out f32
+    [L][H_kv*G][d]."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(k_kept, torch.bfloat16, "k_kept", 3)
+    _need(v_kept, torch.bfloat16, "v_kept", 3)
+    if k_kept.shape != v_kept.shape:
+        raise ValueError("k_kept and v_kept must have the same shape")
+    L, Hq, d = q.shape
+    if Hq % G != 0:
+        raise ValueError("q must hold H_kv*G query heads")
+    H = Hq // G
+    if k_kept.shape[0] != L or k_kept.shape[2] != d:
+        raise ValueError("k_kept must be [L][kept][d]")
+    kept = k_kept.shape[1]
+    if head_offsets is not None:
+        _need(head_offsets, torch.int32, "head_offsets", 2)
+        if tuple(head_offsets.shape) != (L, H + 1):
+            raise ValueError("head_offsets must be [L][H_kv+1]")
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    dev = q.device
+    if out is None:
+        out = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
+    else:
+        _need(out, torch.float32, "out", 3)
+        if tuple(out.shape) != (L, Hq, d):
+            raise ValueError("out must be [L][H_kv*G][d]")
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_decode_attention
+    args = (L, H, G, d, int(kept), _ptr(head_offsets), float(scale))
+    _check(f(None, None, None, *args, None, None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(q), _ptr(k_kept), _ptr(v_kept), *args, _ptr(out), _ptr(ws), ctypes.byref(nbytes),
+             _stream(dev)))
+    return out

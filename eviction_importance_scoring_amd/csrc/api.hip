@@ -155,4 +155,28 @@ int32_t kvsel_compact(const void* k, const void* v, int32_t L, int32_t H_kv, int
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 
+int32_t kvsel_decode_attention(const void* q, const void* k, const void* v, int32_t L,
+                               int32_t H_kv, int32_t G, int32_t d, int64_t kept_per_layer,
+                               const int32_t* head_offsets, float scale, float* out, void* ws,
+                               size_t* ws_bytes, void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || G < 1 || d < 1 || kept_per_layer < 1) return KVSEL_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return KVSEL_ERR_ARG;
+  if (!head_offsets && kept_per_layer % H_kv != 0) return KVSEL_ERR_ARG;
+  if (d != kHeadDimPublic || G > 8 || H_kv > 1024) return KVSEL_ERR_UNSUPPORTED;
+  if (kept_per_layer > kMaxIndex || (int64_t)L * H_kv * G > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  const size_t need = decode_ws_bytes(L, H_kv, G, kept_per_layer, head_offsets != nullptr);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!q || !k || !v || !out) return KVSEL_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws))
+    return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  const hipError_t e = decode_launch(q, k, v, L, H_kv, G, kept_per_layer, head_offsets, scale, out,
+                                     ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
 }  // extern "C"

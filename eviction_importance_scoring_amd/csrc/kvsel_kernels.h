@@ -68,4 +68,10 @@ hipError_t compact_launch(const void* k, const void* v, int L, int H, int d, int
 hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int G, int n,
                                int D, int n_cand, float* weight, hipStream_t st);
 
+// -------------------------------------------------------------- decoding ----
+size_t decode_ws_bytes(int L, int H, int G, int64_t kept, bool ragged);
+hipError_t decode_launch(const void* q, const void* k, const void* v, int L, int H, int G,
+                         int64_t kept, const int32_t* head_offsets, float scale, float* out,
+                         void* ws, hipStream_t st);
+
 }  // namespace kvsel

@@ -20,7 +20,8 @@
  *    synchronised. No call allocates device memory or synchronises.
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
- *  - Workspace protocol (kvsel_score, kvsel_select): with ws == NULL the
+ *  - Workspace protocol (kvsel_score, kvsel_select, kvsel_decode_attention):
+ *    with ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
  *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
  *    Workspace contents need no initialisation and are scratch afterwards.
@@ -186,6 +187,41 @@ int32_t kvsel_compact(const void* k, const void* v,
                       const int32_t* idx, const int32_t* head_offsets,
                       int64_t kept_per_layer, void* k_out, void* v_out,
                       void* stream);
+
+/*
+ * kvsel_decode_attention -- one decoding step over the kept rows.
+ *
+ * [KVzip] §7.1 (decoding efficiency): after eviction every KV head keeps
+ * its own number of rows, and a new token's attention runs over each
+ * head's kept rows with a variable-length kernel. The query of query head
+ * h*G+g attends over the kept rows of KV head h:
+ *   out[l][h*G+g] = sum_t softmax_t(scale * <q[l][h*G+g], k_t>) * v_t
+ * over the rows t that kvsel_compact wrote for head h. A head with no kept
+ * rows gives zeros. The new token's own key and value are not part of the
+ * call (append them to the kept rows to include them).
+ *
+ *   q            bf16 [L][H_kv*G][d]          the new token's queries
+ *   k, v         bf16 [L][kept_per_layer][d]  kept rows (kvsel_compact's
+ *                                             output layouts)
+ *   head_offsets i32  [L][H_kv+1] or NULL: head h of layer l owns rows
+ *                [head_offsets[l][h], head_offsets[l][h+1]) (as written by
+ *                kvsel_select); NULL: every head owns kept_per_layer/H_kv
+ *                consecutive rows. Offsets are clamped into
+ *                [0, kept_per_layer]; a head whose end is not past its start
+ *                is empty.
+ *   out          f32  [L][H_kv*G][d]
+ *   scale        softmax temperature (the model's 1/sqrt(d)), > 0
+ *
+ * fp32 from bf16: exact products, fp32 sums, base-2 exponentials with the
+ * scale folded in. Limits: d == 128, 1 <= G <= 8, H_kv <= 1024 (else
+ * KVSEL_ERR_UNSUPPORTED); kept_per_layer >= 1, divisible by H_kv when
+ * head_offsets is NULL. Needs a workspace (protocol above).
+ */
+int32_t kvsel_decode_attention(const void* q, const void* k, const void* v,
+                               int32_t L, int32_t H_kv, int32_t G, int32_t d,
+                               int64_t kept_per_layer, const int32_t* head_offsets,
+                               float scale, float* out,
+                               void* ws, size_t* ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* kvsel_status_str(int32_t status);

@@ -148,3 +148,29 @@ def test_value_weight_and_compact_reject(lib):
     assert c(p, p, 1, 8, 128, 100, p, None, 12, p, p, None) == ARG  # not divisible by H
     assert c(p, p, 1, 8, 128, 100, p, None, 808, p, p, None) == ARG  # more rows than the cache
     assert c(p, p, 1, 8, 12, 100, p, None, 16, p, p, None) == UNSUP
+
+
+def _decode(lib, **kw):
+    a = dict(L=2, H=8, G=4, d=128, kept=800, offs=None, scale=0.088)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    return lib.kvsel_decode_attention(None, None, None, a["L"], a["H"], a["G"], a["d"], a["kept"],
+                                      a["offs"], a["scale"], None, None, ctypes.byref(nb), None), nb.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(G=8), OK), (dict(G=1), OK), (dict(L=0), ARG), (dict(H=0), ARG),
+    (dict(G=0), ARG), (dict(kept=0), ARG), (dict(kept=801), ARG), (dict(scale=0.0), ARG),
+    (dict(scale=float("nan")), ARG), (dict(G=9), UNSUP), (dict(d=64), UNSUP),
+    (dict(H=1025, kept=1025 * 4), UNSUP),
+])
+def test_decode_ranges(lib, kw, code):
+    assert _decode(lib, **kw)[0] == code
+
+
+def test_decode_workspace_query(lib):
+    rc, nb = _decode(lib)
+    assert rc == OK and nb > 0
+    # ragged heads (offsets given) size for the worst split of the rows
+    rc2, nb2 = _decode(lib, kept=801, offs=ctypes.c_void_p(1 << 20))
+    assert rc2 == OK and nb2 >= nb

@@ -256,3 +256,83 @@ def test_value_weight(L, H, G, n, D, n_cand):
         ref = oracle.value_weight(synth.bf16_to_f64(data["v"][l]), synth.bf16_to_f64(data["w_o"][l]),
                                   G, np.arange(n_cand))
         assert_scores_close(w[l], ref, "value weight")
+
+
+# ------------------------------------------------- decode over kept rows ----
+#
+# Tolerance: outputs are weighted means of v rows, so their error is
+# measured against the head's largest |v|: |gpu - ref| <= 1e-4 * max|v| +
+# 1e-4 * |ref|. fp32 logits from exact bf16 products (|error| ~ 1e-5 of a
+# logit of magnitude ~10), base-2 exponentials and fp32 sums over <= 10^4
+# rows keep the weights within ~1e-5 relative.
+
+DECODE_CASES = [
+    # (L, H_kv, G, head lengths per layer (None: uniform B), B)
+    (1, 2, 4, None, 300),        # two items per head, the second ragged
+    (2, 8, 4, None, 13),         # tiny heads
+    (1, 1, 8, None, 1000),       # G = 8, four items
+    (1, 3, 7, None, 256),        # exactly one item
+    (1, 4, 1, None, 512),
+    (2, 4, 4, [[0, 1, 600, 257], [300, 0, 0, 5]], None),   # ragged, empty heads
+    (1, 3, 2, [[2000, 3, 513]], None),
+]
+
+
+def _decode_inputs(rng, L, H, G, lengths, B):
+    if lengths is None:
+        lengths = [[B] * H for _ in range(L)]
+    kept = max(sum(x) for x in lengths)
+    offs = np.zeros((L, H + 1), np.int32)
+    for l in range(L):
+        offs[l, 1:] = np.cumsum(lengths[l])
+    q = synth.bf16_bits(rng.normal(size=(L, H * G, 128)).astype(np.float32))
+    k = synth.bf16_bits((rng.normal(size=(L, kept, 128)) * 1.5).astype(np.float32))
+    v = synth.bf16_bits(rng.normal(size=(L, kept, 128)).astype(np.float32))
+    return q, k, v, offs, kept
+
+
+def _assert_decode_close(got, ref, vmax, what):
+    bad = np.abs(got - ref) > 1e-4 * vmax + 1e-4 * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} entries off; max err {np.abs(got - ref).max():.3g}"
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"L{c[0]}H{c[1]}G{c[2]}{'r' if c[3] else 'u'}")
+def test_decode_attention(case):
+    L, H, G, lengths, B = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    q, k, v, offs, kept = _decode_inputs(rng, L, H, G, lengths, B)
+    scale = 1.0 / np.sqrt(128.0)
+    ragged = lengths is not None
+    print(f"[gpu] kvsel_decode_attention L={L} H={H} G={G} kept={kept} ragged={ragged}", flush=True)
+    out = kv.kvsel_decode_attention(to_dev(q), to_dev(k), to_dev(v), G=G, scale=scale,
+                                    head_offsets=torch.from_numpy(offs).cuda() if ragged else None)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for l in range(L):
+        kl, vl = synth.bf16_to_f64(k[l]), synth.bf16_to_f64(v[l])
+        if ragged:
+            ref = oracle.decode_attention(synth.bf16_to_f64(q[l]), kl, vl, G, scale, offs[l])
+        else:
+            ref = oracle.decode_attention(synth.bf16_to_f64(q[l]), kl.reshape(H, B, 128),
+                                          vl.reshape(H, B, 128), G, scale)
+        _assert_decode_close(out[l], ref, np.abs(vl).max(), f"decode layer {l}")
+
+
+def test_decode_attention_clamps_offsets():
+    """Offsets outside [0, kept] are clamped and a head ending before its
+    start is empty: nothing outside the layer's rows is read."""
+    rng = np.random.default_rng(77)
+    L, H, G, kept = 1, 4, 2, 300
+    q = synth.bf16_bits(rng.normal(size=(L, H * G, 128)).astype(np.float32))
+    k = synth.bf16_bits(rng.normal(size=(L, kept, 128)).astype(np.float32))
+    v = synth.bf16_bits(rng.normal(size=(L, kept, 128)).astype(np.float32))
+    offs = np.array([[-5, 100, 40, 290, 9999]], np.int32)
+    out = kv.kvsel_decode_attention(to_dev(q), to_dev(k), to_dev(v), G=G, scale=0.09,
+                                    head_offsets=torch.from_numpy(offs).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()[0]
+    # each offset clamped into [0, kept]: head 1 = [100, 40) is empty, head 2 = [40, 290)
+    eff = np.clip(offs[0], 0, kept)
+    ref = oracle.decode_attention(synth.bf16_to_f64(q[0]), synth.bf16_to_f64(k[0]),
+                                  synth.bf16_to_f64(v[0]), G, 0.09, eff)
+    _assert_decode_close(out, ref, np.abs(synth.bf16_to_f64(v[0])).max(), "clamped offsets")
