@@ -185,9 +185,10 @@ def main():
                                        alpha=wl.alpha)
         if marks is not None:
             marks[3].record()
-        kv.kvsel_compact(k, v, idx, offs)
+        kept = kv.kvsel_compact(k, v, idx, offs)
         if marks is not None:
             marks[4].record()
+        return kept, offs
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -200,7 +201,7 @@ def main():
     wall0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        step(marks[s])
+        kept_kv, kept_offs = step(marks[s])
     end.record()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
@@ -270,6 +271,33 @@ def main():
     out["roofline"] = calls[0][1]
     if len(calls) > 1:
         out["other_rooflines"] = [c[1] for c in calls[1:]]
+    # the next step after eviction: one decoding step over the kept rows of
+    # every layer (not part of `value`), on the last step's compacted cache
+    if wl.G <= 8:
+        gq = torch.Generator(device=dev)
+        gq.manual_seed(args.seed + 7)
+        q_dec = torch.randn((wl.L, wl.H_q, wl.d), generator=gq, device=dev).to(torch.bfloat16)
+        ko, vo = kept_kv
+        out_dec = torch.empty((wl.L, wl.H_q, wl.d), dtype=torch.float32, device=dev)
+        dec = lambda: kv.kvsel_decode_attention(q_dec, ko, vo, G=wl.G, scale=wl.scale,
+                                                head_offsets=kept_offs, out=out_dec)
+        for _ in range(3):
+            dec()
+        torch.cuda.synchronize(dev)
+        d0, d1 = ev(), ev()
+        reps = 10
+        d0.record()
+        for _ in range(reps):
+            dec()
+        d1.record()
+        torch.cuda.synchronize(dev)
+        ms_dec = d0.elapsed_time(d1) / reps
+        dec_bytes = 2 * ko.numel() * 2 + q_dec.numel() * 2 + out_dec.numel() * 4
+        out["next_rows"] = {"decode_attention": {
+            "bound": "hbm", "ms_per_call": ms_dec, "bytes_per_launch": dec_bytes,
+            "achieved": dec_bytes / (ms_dec * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dec_bytes / (ms_dec * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kept_rows_per_layer": int(ko.shape[1])}}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         if host is None:   # bring back the first layers, which the sample uses

@@ -11,7 +11,9 @@ they do not affect the sampled results). Checks:
   - selection: bit-exact against the oracle run in fp32 on the GPU's own
     scores (same precision decides), and within the tolerance band of the
     fp64 oracle's selection where that is affordable;
-  - compaction: bit-exact given the GPU's index set.
+  - compaction: bit-exact given the GPU's index set;
+  - one decoding step over the compacted cache of a sampled layer against
+    the fp64 oracle.
 """
 from __future__ import annotations
 
@@ -90,6 +92,28 @@ def _check_compact(dev, host, idx, offs, l, wl):
                                   None if offs is None else offs[l].cpu().numpy())
     np.testing.assert_array_equal(ko[l].cpu().view(torch.int16).numpy().view(np.uint16).reshape(rk.shape), rk)
     np.testing.assert_array_equal(vo[l].cpu().view(torch.int16).numpy().view(np.uint16).reshape(rv.shape), rv)
+    _check_decode(wl, ko, vo, offs, l)
+
+
+def _check_decode(wl, ko, vo, offs, l):
+    """One decoding step over the compacted cache of every layer; layer l
+    against the fp64 oracle (|err| <= 1e-4 * max|v| + 1e-4 * |ref|)."""
+    rng = np.random.default_rng(99)
+    qd = synth.bf16_bits(rng.normal(size=(wl.L, wl.H_q, wl.d)).astype(np.float32))
+    print(f"[gpu] kvsel_decode_attention {wl.name}", flush=True)
+    out = kv.kvsel_decode_attention(to_dev(qd), ko, vo, G=wl.G, scale=wl.scale, head_offsets=offs)
+    torch.cuda.synchronize()
+    k_l = synth.bf16_to_f64(ko[l].cpu().view(torch.int16).numpy().view(np.uint16))
+    v_l = synth.bf16_to_f64(vo[l].cpu().view(torch.int16).numpy().view(np.uint16))
+    if offs is None:
+        ref = oracle.decode_attention(synth.bf16_to_f64(qd[l]), k_l.reshape(wl.H_kv, -1, wl.d),
+                                      v_l.reshape(wl.H_kv, -1, wl.d), wl.G, wl.scale)
+    else:
+        ref = oracle.decode_attention(synth.bf16_to_f64(qd[l]), k_l, v_l, wl.G, wl.scale,
+                                      offs[l].cpu().numpy())
+    got = out[l].cpu().numpy()
+    bad = np.abs(got - ref) > 1e-4 * np.abs(v_l).max() + 1e-4 * np.abs(ref)
+    assert not bad.any(), f"decode layer {l}: {bad.sum()} entries off, max err {np.abs(got - ref).max():.3g}"
 
 
 def test_snapkv_L1_n4k_full():
