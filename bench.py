@@ -250,8 +250,10 @@ def main():
                  "kernel": "kvsel_score", "bytes_per_launch": score_bytes,
                  "ms_per_launch": ms_score, "source_sha": sha}
     calls = []
-    if wl.q_mode == "external":
-        sc_flops = 2 * 2.0 * wl.L * wl.H_q * wl.W * wl.n * wl.d
+    # two passes of Q K^T (R = G*W rows per KV head against n keys); the
+    # call is MFMA-bound when those flops take longer at peak than its bytes
+    sc_flops = 2 * 2.0 * wl.L * wl.H_q * wl.W * wl.n * wl.d
+    if sc_flops / (MFMA_BF16_PEAK_TFS * 1e12) > score_bytes / (HBM_PEAK_GBS * 1e9):
         tfs = sc_flops / (ms_score * 1e-3) / 1e12
         calls.append((ms_score, {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,
                                  "unit": "TFLOP/s", "frac": tfs / MFMA_BF16_PEAK_TFS, "traffic": None,

@@ -116,6 +116,13 @@ WORKLOADS = {
         Workload("criticalkv_llama8b_n128k", L=32, H_kv=8, G=4, d=128,
                  n=131072, W=32, pool=7, beta=0.10, value_weight=True,
                  D=4096),
+        # CriticalAdaKV: value-norm weighted two-stage selection over one
+        # budget per layer (the flattened candidates of its heads), n = 32K, 20%
+        Workload("criticaladakv_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768,
+                 W=32, pool=7, beta=0.20, adaptive=True, value_weight=True, D=4096),
+        # H2O-style accumulated attention: window scoring with W = 256, 20%
+        Workload("h2o_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=256,
+                 pool=7, beta=0.20),
         # many external queries, max aggregation, Qwen2.5-7B GQA shape
         Workload("kvzip_qwen7b_n32k", L=28, H_kv=4, G=7, d=128, n=32768,
                  W=4096, q_mode="external", agg="max", pool=1, beta=0.25,

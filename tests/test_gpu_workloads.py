@@ -131,7 +131,7 @@ def test_snapkv_L1_n4k_full():
     _check_compact(dev, host, idx, offs, 0, wl)
 
 
-@pytest.mark.parametrize("name", ["llama8b_n32k", "adakv_llama8b_n64k"])
+@pytest.mark.parametrize("name", ["llama8b_n32k", "adakv_llama8b_n64k", "h2o_llama8b_n32k"])
 def test_window_workload_full(name):
     wl = synth.WORKLOADS[name]
     sampled = [0, wl.L - 1]
@@ -158,8 +158,9 @@ def test_window_workload_full(name):
     _check_compact(dev, host, idx, offs, 0, wl)
 
 
-def test_criticalkv_n128k_full():
-    wl = synth.WORKLOADS["criticalkv_llama8b_n128k"]
+@pytest.mark.parametrize("name", ["criticalkv_llama8b_n128k", "criticaladakv_llama8b_n32k"])
+def test_criticalkv_full(name):
+    wl = synth.WORKLOADS[name]
     sampled = [0, wl.L - 1]
     dev, host = device_inputs(wl, set(sampled), ("q", "k", "v", "w_o"))
     s, r = _score(wl, dev)
@@ -174,14 +175,14 @@ def test_criticalkv_n128k_full():
                                   wl.G, pos)
         assert_scores_close(w[l].cpu().numpy()[:, pos], ref, f"value weight l{l}")
     idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=wl.W, budget=wl.budget, weight=w,
-                                       score_norm=1.0 / (wl.W * wl.G), eps=wl.eps, alpha=wl.alpha,
-                                       return_stage=True)
+                                       adaptive=wl.adaptive, score_norm=1.0 / (wl.W * wl.G),
+                                       eps=wl.eps, alpha=wl.alpha, return_stage=True)
     torch.cuda.synchronize()
     _check_select_exact(wl, s, w, idx, offs, stage, sampled)
     st = stage[0].cpu().numpy()
-    k = wl.budget - wl.W
-    assert ((st == 1).sum(axis=1) == int(np.floor(wl.alpha * k))).all()
-    assert ((st == 2).sum(axis=1) == k - int(np.floor(wl.alpha * k))).all()
+    k = wl.budget - (wl.H_kv * wl.W if wl.adaptive else wl.W)
+    assert ((st == 1).sum(axis=-1) == int(np.floor(wl.alpha * k))).all()
+    assert ((st == 2).sum(axis=-1) == k - int(np.floor(wl.alpha * k))).all()
     _check_compact(dev, host, idx, offs, 0, wl)
 
 
