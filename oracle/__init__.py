@@ -27,7 +27,8 @@ Readings taken where the pages are silent (each repeated where it is used):
   pool      max-pooling: kernel `pool`, stride 1, centred, over candidates
             only; out-of-range neighbours are ignored.
   weight    value weight of KV head h at position j:
-            mean over g of || W_O[:, slice(h*G+g)] v_j ||_1, in fp64.
+            mean over g of || W_O[:, slice(h*G+g)] v_j ||_1, in fp64
+            (|| . ||_2 for the L2 variant).
   key       two-stage key = (pooled * score_norm + eps) * weight, applied
             after pooling; stage 1 takes floor(alpha*k) by pooled score.
   ties      larger key first; equal keys go to the lower index (adaptive:
@@ -159,6 +160,31 @@ def value_weight(v: np.ndarray, w_o: np.ndarray, G: int,
             w_slice = w_o[:, hq * d:(hq + 1) * d]      # [D][d]
             proj = vh @ w_slice.T                      # [m][D] rows of V W^O
             out[h] += np.abs(proj).sum(axis=1)
+        out[h] /= G
+    return out
+
+
+def value_weight_l2(v: np.ndarray, w_o: np.ndarray, G: int,
+                    positions: np.ndarray | None = None) -> np.ndarray:
+    """The L2 variant of CriticalKV's projected-value norm.
+
+    [CriticalKV, §C.3 and footnote 1]: the L1 and L2 distances are compared
+    and the L2 one gives similar gains. Weight of KV head h at position j:
+    mean over its G query heads of || W_O^(h,g) v_j ||_2, with the same
+    column slices and GQA reading as value_weight.
+
+    v: [H_kv][n][d], w_o: [D][H_kv*G*d]. Returns [H_kv][len(positions)].
+    """
+    H, n, d = v.shape
+    if positions is None:
+        positions = np.arange(n)
+    out = np.zeros((H, len(positions)))
+    for h in range(H):
+        vh = v[h, positions]
+        for g in range(G):
+            hq = h * G + g
+            proj = vh @ w_o[:, hq * d:(hq + 1) * d].T      # [m][D]
+            out[h] += np.sqrt((proj * proj).sum(axis=1))
         out[h] /= G
     return out
 

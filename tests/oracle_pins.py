@@ -391,6 +391,44 @@ def check_compact(o):
     np.testing.assert_array_equal(vo, np.concatenate([v[0, idx[0][:2]], v[2, idx[2]]]))
 
 
+# ------------------------------------------------------- value weight, L2 ----
+
+def check_value_weight_l2(o):
+    rng = np.random.default_rng(41)
+    H, G, n, d = 2, 3, 7, 4
+    v = rng.normal(size=(H, n, d))
+    # identity slices: the L2 norm of v itself
+    w_id = np.tile(np.eye(d), (1, H * G))
+    np.testing.assert_allclose(o.value_weight_l2(v, w_id, G), np.linalg.norm(v, axis=2), rtol=1e-13)
+    # brute force with loops
+    D = 5
+    w = rng.normal(size=(D, H * G * d))
+    got = o.value_weight_l2(v, w, G)
+    for h in range(H):
+        for j in range(n):
+            acc = 0.0
+            for g in range(G):
+                hq = h * G + g
+                ss = 0.0
+                for c in range(D):
+                    x = sum(w[c, hq * d + e] * v[h, j, e] for e in range(d))
+                    ss += x * x
+                acc += math.sqrt(ss)
+            assert abs(got[h, j] - acc / G) <= 1e-12 * max(1.0, acc)
+    # a rotation of the output space changes nothing (true of L2, not of L1)
+    qm, _ = np.linalg.qr(rng.normal(size=(D, D)))
+    np.testing.assert_allclose(o.value_weight_l2(v, qm @ w, G), got, rtol=1e-12)
+    # homogeneity in v, and a rank-one slice: ||a||_2 |b . v|
+    np.testing.assert_allclose(o.value_weight_l2(-2.5 * v, w, G), 2.5 * got, rtol=1e-13)
+    a_vec, b_vec = rng.normal(size=D), rng.normal(size=d)
+    w1 = np.tile(np.outer(a_vec, b_vec), (1, H * G))
+    np.testing.assert_allclose(o.value_weight_l2(v, w1, G),
+                               np.linalg.norm(a_vec) * np.abs(v @ b_vec), rtol=1e-12)
+    # positions select columns of the full result
+    pos = np.array([5, 0, 3])
+    np.testing.assert_allclose(o.value_weight_l2(v, w, G, pos), got[:, pos], rtol=1e-15)
+
+
 # ------------------------------------------------- decode over kept rows ----
 
 def check_decode_hand_example(o):
@@ -471,4 +509,5 @@ ALL_CHECKS = [
     check_external, check_maxpool, check_value_weight, check_select_examples,
     check_select_bruteforce, check_select_reductions, check_compact,
     check_decode_hand_example, check_decode_bruteforce, check_decode_sdpa, check_decode_closed_forms,
+    check_value_weight_l2,
 ]

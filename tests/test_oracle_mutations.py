@@ -27,7 +27,8 @@ MUTANTS = {
     "pool_over_all_n": ("src = raw[..., :n_cand]\n    out = src.copy()", "src = raw\n    out = src.copy()[..., :n_cand]"),
     "weight_no_abs": ("out[h] += np.abs(proj).sum(axis=1)", "out[h] += proj.sum(axis=1)"),
     "weight_l2": ("out[h] += np.abs(proj).sum(axis=1)", "out[h] += np.sqrt((proj ** 2).sum(axis=1))"),
-    "weight_no_mean": ("out[h] /= G", "out[h] /= 1"),
+    "weight_no_mean": ("            out[h] += np.abs(proj).sum(axis=1)\n        out[h] /= G",
+                       "            out[h] += np.abs(proj).sum(axis=1)\n        out[h] /= 1"),
     "weight_wrong_slice": ("w_slice = w_o[:, hq * d:(hq + 1) * d]", "w_slice = w_o[:, h * d:(h + 1) * d]"),
     "ties_to_higher_index": ("order = np.lexsort((np.arange(key.shape[0]), -key))", "order = np.lexsort((-np.arange(key.shape[0]), -key))"),
     "k1_ceil": ("k1 = int(np.floor(alpha * k))", "k1 = int(np.ceil(alpha * k))"),
@@ -43,6 +44,11 @@ MUTANTS = {
     "decode_offsets_shifted": ("heads = [(k_kept[head_offsets[h]:head_offsets[h + 1]], v_kept[head_offsets[h]:head_offsets[h + 1]])",
                                "heads = [(k_kept[head_offsets[h]:head_offsets[h + 1]], v_kept[head_offsets[h] + 1:head_offsets[h + 1] + 1])"),
     "decode_uniform_weights": ("out[h * G + g] = p @ vh", "out[h * G + g] = vh.mean(axis=0)"),
+    "l2_no_sqrt": ("out[h] += np.sqrt((proj * proj).sum(axis=1))", "out[h] += (proj * proj).sum(axis=1)"),
+    "l2_is_l1": ("out[h] += np.sqrt((proj * proj).sum(axis=1))", "out[h] += np.abs(proj).sum(axis=1) * 1.0"),
+    "l2_no_mean": ("            out[h] += np.sqrt((proj * proj).sum(axis=1))\n        out[h] /= G",
+                   "            out[h] += np.sqrt((proj * proj).sum(axis=1))\n        out[h] /= 1"),
+    "l2_wrong_slice": ("proj = vh @ w_o[:, hq * d:(hq + 1) * d].T      # [m][D]", "proj = vh @ w_o[:, h * d:(h + 1) * d].T      # [m][D]"),
     "compact_wrong_head": ("return (np.stack([k[h, idx[h]] for h in range(H)]),", "return (np.stack([k[0, idx[h]] for h in range(H)]),"),
 }
 
