@@ -17,6 +17,7 @@ import torch
 
 __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_value_weight",
+    "kvsel_value_weight_l2",
     "kvsel_select", "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
     "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX",
@@ -40,6 +41,8 @@ _SIGNATURES = {
                     _c_size_p, _c_void_p],
     "kvsel_value_weight": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_void_p, _c_void_p],
+    "kvsel_value_weight_l2": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                              _c_i32, _c_i32, _c_void_p, _c_void_p, _c_size_p, _c_void_p],
     "kvsel_select": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                      _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                      _c_size_p, _c_void_p],
@@ -162,6 +165,31 @@ def kvsel_value_weight(v, w_o, *, G: int, n_cand: int | None = None, weight=None
         weight = torch.empty((L, H, n_cand), dtype=torch.float32, device=v.device)
     _check(lib().kvsel_value_weight(_ptr(v), _ptr(w_o), L, H, G, d, n, D, n_cand,
                                     _ptr(weight), _stream(v.device)))
+    return weight
+
+
+def kvsel_value_weight_l2(v, w_o, *, G: int, n_cand: int | None = None, weight=None,
+                          workspace=None):
+    """L2 form of the CriticalKV value weight [L][H_kv][n_cand]. v bf16
+    [L][H_kv][n][d], w_o bf16 [L][D][H_kv*G*d]."""
+    _need(v, torch.bfloat16, "v", 4)
+    _need(w_o, torch.bfloat16, "w_o", 3)
+    L, H, n, d = v.shape
+    if w_o.shape[0] != L or w_o.shape[2] != H * G * d:
+        raise ValueError(f"shape mismatch: v {tuple(v.shape)}, w_o {tuple(w_o.shape)}, G={G}")
+    D = w_o.shape[1]
+    n_cand = n if n_cand is None else n_cand
+    dev = v.device
+    if weight is None:
+        weight = torch.empty((L, H, n_cand), dtype=torch.float32, device=dev)
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_value_weight_l2
+    args = (L, H, G, d, n, D, n_cand)
+    _check(f(None, None, *args, None, None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(v), _ptr(w_o), *args, _ptr(weight), _ptr(ws), ctypes.byref(nbytes),
+             _stream(dev)))
     return weight
 
 

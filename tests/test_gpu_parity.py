@@ -258,6 +258,40 @@ def test_value_weight(L, H, G, n, D, n_cand):
         assert_scores_close(w[l], ref, "value weight")
 
 
+# L2 form: the kernel factors each query head's W^T W (Cholesky, fp32) and
+# projects by the factor held as bf16 hi + lo (~2^-17 relative), so the
+# weight meets the same rel 1e-3 bar as the L1 form. D < d (rank-deficient
+# W^T W) exercises the dropped pivots.
+@pytest.mark.parametrize("L,H,G,n,D,n_cand", [
+    (1, 2, 4, 300, 256, 290),
+    (1, 1, 7, 97, 4096, 97),
+    (1, 3, 1, 1000, 32, 999),     # rank 32 of 128
+    (2, 2, 3, 1500, 100, 1400),   # several key blocks, ragged, D not a multiple of 64
+    (1, 1, 2, 600, 128, 513),     # square slice
+])
+def test_value_weight_l2(L, H, G, n, D, n_cand):
+    wl = _wl(L=L, H_kv=H, G=G, n=n, W=n - n_cand if n_cand < n else 1, value_weight=True, D=D)
+    data = gen(wl, seed=8, which=("v", "w_o"))
+    print(f"[gpu] kvsel_value_weight_l2 L={L} H={H} G={G} n={n} D={D}", flush=True)
+    w = kv.kvsel_value_weight_l2(to_dev(data["v"]), to_dev(data["w_o"]), G=G, n_cand=n_cand)
+    torch.cuda.synchronize()
+    w = w.cpu().numpy()
+    for l in range(L):
+        ref = oracle.value_weight_l2(synth.bf16_to_f64(data["v"][l]),
+                                     synth.bf16_to_f64(data["w_o"][l]), G, np.arange(n_cand))
+        assert_scores_close(w[l], ref, "value weight l2")
+
+
+def test_value_weight_l2_deterministic():
+    wl = _wl(L=1, H_kv=2, G=4, n=3000, W=1, value_weight=True, D=512)
+    data = gen(wl, seed=9, which=("v", "w_o"))
+    v, w_o = to_dev(data["v"]), to_dev(data["w_o"])
+    a = kv.kvsel_value_weight_l2(v, w_o, G=wl.G, n_cand=wl.n).cpu().numpy()
+    for _ in range(2):
+        b = kv.kvsel_value_weight_l2(v, w_o, G=wl.G, n_cand=wl.n).cpu().numpy()
+        np.testing.assert_array_equal(a, b)
+
+
 # ------------------------------------------------- decode over kept rows ----
 #
 # Tolerance: outputs are weighted means of v rows, so their error is

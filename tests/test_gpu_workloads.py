@@ -174,6 +174,16 @@ def test_criticalkv_full(name):
         ref = oracle.value_weight(synth.bf16_to_f64(host[("v", l)]), synth.bf16_to_f64(host[("w_o", l)]),
                                   wl.G, pos)
         assert_scores_close(w[l].cpu().numpy()[:, pos], ref, f"value weight l{l}")
+    if name == "criticalkv_llama8b_n128k":
+        print("[gpu] kvsel_value_weight_l2 full", flush=True)
+        w2 = kv.kvsel_value_weight_l2(dev["v"], dev["w_o"], G=wl.G, n_cand=wl.n_cand)
+        torch.cuda.synchronize()
+        for l in sampled:
+            pos = np.sort(rng.choice(wl.n_cand, 64, replace=False))
+            ref = oracle.value_weight_l2(synth.bf16_to_f64(host[("v", l)]),
+                                         synth.bf16_to_f64(host[("w_o", l)]), wl.G, pos)
+            assert_scores_close(w2[l].cpu().numpy()[:, pos], ref, f"value weight l2 l{l}")
+        del w2
     idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=wl.W, budget=wl.budget, weight=w,
                                        adaptive=wl.adaptive, score_norm=1.0 / (wl.W * wl.G),
                                        eps=wl.eps, alpha=wl.alpha, return_stage=True)
