@@ -89,7 +89,8 @@ def cpu_baseline(wl, host, seconds, w_host=None):
         if wl.value_weight and w_host is not None:
             v = synth.bf16_to_f64(host["v"][l][h:h + 1])
             wo = synth.bf16_to_f64(w_host[l][:, h * wl.G * wl.d:(h + 1) * wl.G * wl.d])
-            weight = oracle.value_weight(v, wo, wl.G, np.arange(wl.n_cand))
+            norm = oracle.value_weight_l2 if wl.value_norm == "l2" else oracle.value_weight
+            weight = norm(v, wo, wl.G, np.arange(wl.n_cand))
         oracle.select_layer(pooled, wl.budget if not wl.adaptive else wl.budget // wl.H_kv,
                             wl.W_kept, wl.n, weight=weight, alpha=wl.alpha,
                             score_norm=1.0 / (wl.W * wl.G), eps=wl.eps)
@@ -167,6 +168,19 @@ def main():
     _, _ = kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
                           scores=scores)  # sizes the workspace once
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    l2 = wl.value_weight and wl.value_norm == "l2"
+    factor, ms_factor = None, None
+    if l2:
+        # the L2 norm's per-query-head factor depends on the model weights
+        # only: computed once, outside the timed steps (timed on its own)
+        factor = kv.kvsel_value_l2_factor(w_o, G=wl.G, H_kv=wl.H_kv)
+        torch.cuda.synchronize(dev)
+        f0, f1 = ev(), ev()
+        f0.record()
+        kv.kvsel_value_l2_factor(w_o, G=wl.G, H_kv=wl.H_kv, factor=factor)
+        f1.record()
+        torch.cuda.synchronize(dev)
+        ms_factor = f0.elapsed_time(f1)
 
     def step(marks=None):
         if marks is not None:
@@ -175,7 +189,9 @@ def main():
                        scores=scores)
         if marks is not None:
             marks[1].record()
-        if weight is not None:
+        if l2:
+            kv.kvsel_value_weight_l2(v, factor, G=wl.G, n_cand=wl.n_cand, weight=weight)
+        elif weight is not None:
             kv.kvsel_value_weight(v, w_o, G=wl.G, n_cand=wl.n_cand, weight=weight)
         if marks is not None:
             marks[2].record()
@@ -233,7 +249,9 @@ def main():
         "config": {"workload": wl.name, "L": wl.L, "H_kv": wl.H_kv, "G": wl.G, "d": wl.d,
                    "n": wl.n, "W": wl.W, "q_mode": wl.q_mode, "agg": wl.agg, "pool": wl.pool,
                    "budget": wl.budget, "adaptive": wl.adaptive,
-                   "value_weight": wl.value_weight, "seed": args.seed,
+                   "value_weight": wl.value_weight,
+                   **({"value_norm": wl.value_norm} if wl.value_weight else {}),
+                   "seed": args.seed,
                    "step": "score+value_weight+select+compact" if wl.value_weight
                            else "score+select+compact"},
         "roofline": None,   # the dominant call's, set below
@@ -262,13 +280,23 @@ def main():
         out["score_hbm"] = score_hbm
     else:
         calls.append((ms_score, score_hbm))
-    if wl.value_weight:
+    if wl.value_weight and not l2:
         vw_flops = 2.0 * wl.L * wl.H_kv * wl.n_cand * wl.G * wl.D * wl.d
         tfs = vw_flops / (ms_vw * 1e-3) / 1e12
         calls.append((ms_vw, {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,
                               "unit": "TFLOP/s", "frac": tfs / MFMA_BF16_PEAK_TFS, "traffic": None,
                               "kernel": "kvsel_value_weight", "flops_per_launch": vw_flops,
                               "ms_per_launch": ms_vw}))
+    elif l2:
+        # R v with R upper triangular (d(d+1)/2 products per key and query
+        # head), once for R_hi and once for R_lo
+        vw_flops = 2.0 * 2.0 * wl.L * wl.H_kv * wl.n_cand * wl.G * (wl.d * (wl.d + 1) // 2)
+        tfs = vw_flops / (ms_vw * 1e-3) / 1e12
+        calls.append((ms_vw, {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,
+                              "unit": "TFLOP/s", "frac": tfs / MFMA_BF16_PEAK_TFS, "traffic": None,
+                              "kernel": "kvsel_value_weight_l2", "flops_per_launch": vw_flops,
+                              "ms_per_launch": ms_vw,
+                              "factor_ms_once": ms_factor}))
     calls.sort(key=lambda c: -c[0])
     out["roofline"] = calls[0][1]
     if len(calls) > 1:

@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_value_weight",
-    "kvsel_value_weight_l2",
+    "kvsel_value_l2_factor", "kvsel_value_weight_l2",
     "kvsel_select", "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
     "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX",
@@ -41,8 +41,10 @@ _SIGNATURES = {
                     _c_size_p, _c_void_p],
     "kvsel_value_weight": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_void_p, _c_void_p],
+    "kvsel_value_l2_factor": [_c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
+                              _c_void_p],
     "kvsel_value_weight_l2": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                              _c_i32, _c_i32, _c_void_p, _c_void_p, _c_size_p, _c_void_p],
+                              _c_i32, _c_void_p, _c_void_p],
     "kvsel_select": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                      _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                      _c_size_p, _c_void_p],
@@ -168,28 +170,39 @@ def kvsel_value_weight(v, w_o, *, G: int, n_cand: int | None = None, weight=None
     return weight
 
 
-def kvsel_value_weight_l2(v, w_o, *, G: int, n_cand: int | None = None, weight=None,
-                          workspace=None):
-    """L2 form of the CriticalKV value weight [L][H_kv][n_cand]. v bf16
-    [L][H_kv][n][d], w_o bf16 [L][D][H_kv*G*d]."""
-    _need(v, torch.bfloat16, "v", 4)
+def kvsel_value_l2_factor(w_o, *, G: int, H_kv: int, factor=None):
+    """Per-(layer, query head) factor R (R^T R = W^T W) for the L2 value
+    weight: bf16 [L][H_kv*G][2][d][d] (R_hi, R_lo). w_o bf16 [L][D][H_kv*G*d]."""
     _need(w_o, torch.bfloat16, "w_o", 3)
+    L, D, cols = w_o.shape
+    Hq = H_kv * G
+    if cols % Hq:
+        raise ValueError(f"w_o has {cols} input columns, not a multiple of H_kv*G={Hq}")
+    d = cols // Hq
+    if factor is None:
+        factor = torch.empty((L, Hq, 2, d, d), dtype=torch.bfloat16, device=w_o.device)
+    else:
+        _need(factor, torch.bfloat16, "factor", 5)
+        if tuple(factor.shape) != (L, Hq, 2, d, d):
+            raise ValueError(f"factor must be {(L, Hq, 2, d, d)}, got {tuple(factor.shape)}")
+    _check(lib().kvsel_value_l2_factor(_ptr(w_o), L, H_kv, G, d, D, _ptr(factor),
+                                       _stream(w_o.device)))
+    return factor
+
+
+def kvsel_value_weight_l2(v, factor, *, G: int, n_cand: int | None = None, weight=None):
+    """L2 form of the CriticalKV value weight [L][H_kv][n_cand]. v bf16
+    [L][H_kv][n][d], factor from kvsel_value_l2_factor."""
+    _need(v, torch.bfloat16, "v", 4)
+    _need(factor, torch.bfloat16, "factor", 5)
     L, H, n, d = v.shape
-    if w_o.shape[0] != L or w_o.shape[2] != H * G * d:
-        raise ValueError(f"shape mismatch: v {tuple(v.shape)}, w_o {tuple(w_o.shape)}, G={G}")
-    D = w_o.shape[1]
+    if tuple(factor.shape) != (L, H * G, 2, d, d):
+        raise ValueError(f"shape mismatch: v {tuple(v.shape)}, factor {tuple(factor.shape)}, G={G}")
     n_cand = n if n_cand is None else n_cand
-    dev = v.device
     if weight is None:
-        weight = torch.empty((L, H, n_cand), dtype=torch.float32, device=dev)
-    nbytes = ctypes.c_size_t(0)
-    f = lib().kvsel_value_weight_l2
-    args = (L, H, G, d, n, D, n_cand)
-    _check(f(None, None, *args, None, None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
-    _check(f(_ptr(v), _ptr(w_o), *args, _ptr(weight), _ptr(ws), ctypes.byref(nbytes),
-             _stream(dev)))
+        weight = torch.empty((L, H, n_cand), dtype=torch.float32, device=v.device)
+    _check(lib().kvsel_value_weight_l2(_ptr(v), _ptr(factor), L, H, G, d, n, n_cand,
+                                       _ptr(weight), _stream(v.device)))
     return weight
 
 

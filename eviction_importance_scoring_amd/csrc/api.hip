@@ -97,25 +97,30 @@ int32_t kvsel_value_weight(const void* v, const void* w_o, int32_t L, int32_t H_
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 
-int32_t kvsel_value_weight_l2(const void* v, const void* w_o, int32_t L, int32_t H_kv,
-                              int32_t G, int32_t d, int32_t n, int32_t D, int32_t n_cand,
-                              float* weight, void* ws, size_t* ws_bytes, void* stream) {
-  if (!ws_bytes) return KVSEL_ERR_ARG;
-  if (L < 1 || H_kv < 1 || G < 1 || d < 1 || n < 1 || D < 1) return KVSEL_ERR_ARG;
-  if (n_cand < 1 || n_cand > n) return KVSEL_ERR_ARG;
+int32_t kvsel_value_l2_factor(const void* w_o, int32_t L, int32_t H_kv, int32_t G, int32_t d,
+                              int32_t D, void* factor, void* stream) {
+  if (!w_o || !factor) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || G < 1 || d < 1 || D < 1) return KVSEL_ERR_ARG;
+  if (!aligned16(w_o) || !aligned16(factor)) return KVSEL_ERR_ARG;
   if (d != kHeadDimPublic) return KVSEL_ERR_UNSUPPORTED;
   if ((int64_t)H_kv * G * d > kMaxIndex || (int64_t)L * H_kv * G > kMaxIndex)
     return KVSEL_ERR_UNSUPPORTED;
-  const size_t need = value_weight_l2_ws_bytes(L, H_kv * G);
-  if (!ws) {
-    *ws_bytes = need;
-    return KVSEL_OK;
-  }
-  if (!v || !w_o || !weight) return KVSEL_ERR_ARG;
-  if (!aligned16(v) || !aligned16(w_o) || !aligned16(weight) || !aligned16(ws))
-    return KVSEL_ERR_ARG;
-  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
-  const hipError_t e = value_weight_l2_launch(v, w_o, L, H_kv, G, n, D, n_cand, weight, ws,
+  const hipError_t e = value_l2_factor_launch(w_o, L, H_kv, G, D, factor,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_value_weight_l2(const void* v, const void* factor, int32_t L, int32_t H_kv,
+                              int32_t G, int32_t d, int32_t n, int32_t n_cand, float* weight,
+                              void* stream) {
+  if (!v || !factor || !weight) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || G < 1 || d < 1 || n < 1) return KVSEL_ERR_ARG;
+  if (n_cand < 1 || n_cand > n) return KVSEL_ERR_ARG;
+  if (!aligned16(v) || !aligned16(factor) || !aligned16(weight)) return KVSEL_ERR_ARG;
+  if (d != kHeadDimPublic) return KVSEL_ERR_UNSUPPORTED;
+  if ((int64_t)L * H_kv * G > kMaxIndex || (int64_t)H_kv * n > kMaxIndex)
+    return KVSEL_ERR_UNSUPPORTED;
+  const hipError_t e = value_weight_l2_launch(v, factor, L, H_kv, G, n, n_cand, weight,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }

@@ -67,9 +67,10 @@ hipError_t compact_launch(const void* k, const void* v, int L, int H, int d, int
 // --------------------------------------------------------- value weight ----
 hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int G, int n,
                                int D, int n_cand, float* weight, hipStream_t st);
-size_t value_weight_l2_ws_bytes(int L, int Hq);
-hipError_t value_weight_l2_launch(const void* v, const void* w_o, int L, int H, int G, int n,
-                                  int D, int n_cand, float* weight, void* ws, hipStream_t st);
+hipError_t value_l2_factor_launch(const void* w_o, int L, int H, int G, int D, void* factor,
+                                  hipStream_t st);
+hipError_t value_weight_l2_launch(const void* v, const void* factor, int L, int H, int G, int n,
+                                  int n_cand, float* weight, hipStream_t st);
 
 // -------------------------------------------------------------- decoding ----
 size_t decode_ws_bytes(int L, int H, int G, int64_t kept, bool ragged);

@@ -70,22 +70,25 @@ __device__ __forceinline__ void gen_wait_tile(int t, int ntiles) {
   gen_wait_ahead<PER, gSlots - 2>(issued - (t + 1));
 }
 
-// This wave's share (gLoads chunks of 1 KB, chunk c = tile rows 4c..4c+3)
+// This wave's share (kLoads chunks of 1 KB, chunk c = tile rows 4c..4c+3)
 // of rows [row0, row0 + 64) of a bf16 matrix with `rows` rows of 128
-// elements, `stride` elements apart, into `slot`. Loads go through a raw
-// buffer resource based at the tile's first row and ending after row
-// rows-1: the lane offsets (row r = 4c + lane/16, swizzled piece) are fixed
-// per kernel, so a tile costs no vector instructions, and rows past the end
-// are cut off by the hardware range check (their results are never used).
-// The whole matrix must span less than 2^31 bytes (checked by the API).
+// elements, `stride` elements apart, into `slot`, for a workgroup of NW
+// waves. Loads go through a raw buffer resource based at the tile's first
+// row and ending after row rows-1: the lane offsets (row r = 4c + lane/16,
+// swizzled piece) are fixed per kernel, so a tile costs no vector
+// instructions, and rows past the end are cut off by the hardware range
+// check (their results are never used). The whole matrix must span less
+// than 2^31 bytes (checked by the API).
 [[maybe_unused]] constexpr int kRawBufferWord3 = 0x00020000;   // untyped 32-bit data format
-struct GenLoader {
-  uint32_t off[gLoads];
+template <int NW>
+struct RingLoader {
+  static constexpr int kLoads = gTile * kRowBytes / (NW * 1024);
+  uint32_t off[kLoads];
   __device__ __forceinline__ void init(int stride) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < gLoads; ++i) {
-      const int r = (wave * gLoads + i) * 4 + (lane >> 4);
+    for (int i = 0; i < kLoads; ++i) {
+      const int r = (wave * kLoads + i) * 4 + (lane >> 4);
       off[i] = (uint32_t)r * (uint32_t)stride * 2u + (uint32_t)(((lane & 15) ^ (r & 15)) << 4);
     }
   }
@@ -98,12 +101,14 @@ struct GenLoader {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16*>(base + (size_t)row0 * stride), 0, bytes, kRawBufferWord3);
 #pragma unroll
-    for (int i = 0; i < gLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(slot + (wave * gLoads + i) * 1024), 16,
+    for (int i = 0; i < kLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(slot + (wave * kLoads + i) * 1024), 16,
                                                off[i], 0, 0, 0);
 #endif
   }
 };
+using GenLoader = RingLoader<gWaves>;
+static_assert(GenLoader::kLoads == gLoads, "loads per lane per tile");
 
 // MFMA operand of step s, lane half hf, for row r of a ring slot.
 __device__ __forceinline__ bf16x8 gen_op(const unsigned char* slot, int r, int hf, int s) {

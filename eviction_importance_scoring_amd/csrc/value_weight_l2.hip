@@ -5,28 +5,35 @@
 // head h*G+g uses (the slices and GQA reading of the L1 weight).
 //
 // ||W v||_2^2 = v^T (W^T W) v = ||R v||_2^2 for any R with R^T R = W^T W.
-// So each query head's D x d slice is replaced by the d x d factor R = L^T
-// of the Cholesky factorisation W^T W = L L^T, and the weight becomes a
-// d-row projection instead of a D-row one (D / d = 32 times fewer MFMA
-// flops at D = 4096):
-//   k_gram_chol  per (layer, query head): W^T W by bf16 MFMA (fp32
+// So each query head's D x d slice is replaced by the d x d upper-triangular
+// factor R = L^T of the Cholesky factorisation W^T W = L L^T, and the weight
+// becomes a triangular d-row projection instead of a D-row one. R depends
+// on the model weights only, so it is computed once (kvsel_value_l2_factor)
+// and reused by every call of the projection (kvsel_value_weight_l2):
+//   k_l2_factor  per (layer, query head): W^T W by bf16 MFMA (fp32
 //                accumulation, exact products) over W staged transposed in
 //                LDS, then an in-LDS Cholesky in fp32; R is written as two
 //                bf16 matrices R_hi + R_lo (R_lo = R - R_hi rounded), which
 //                together carry R to about 2^-17 relative.
-//   k_value_weight_l2  the 8-wave ring of kvsel_ring.h: a workgroup owns 512
-//                keys of one (layer, KV head), each wave the values of 64
-//                keys in registers; the ring streams, for every g and each
-//                64-row half of R, the R_hi tile then the R_lo tile into the
-//                same accumulators, so the MFMA forms (R_hi + R_lo) v. Each
-//                pair of tiles is folded into per-key sums of squares beside
-//                the next pair's MFMAs; after both halves of g, sqrt.
+//   k_value_weight_l2  4-wave workgroups (three per CU, so one block's value
+//                loads overlap the others' MFMAs) own 256 keys of one
+//                (layer, KV head), each wave the values of 64 keys in
+//                registers. An LDS ring (kvsel_ring.h) streams, for every g
+//                and each 64-row half of R, the R_hi tile then the R_lo tile
+//                into the same accumulators, so the MFMA forms
+//                (R_hi + R_lo) v. Each MFMA step covers 16 consecutive
+//                columns of R, so the 32 x 16 blocks below the diagonal
+//                (all zero) are skipped: 20 of 32 block-steps remain. Each
+//                pair of tiles is folded into per-key sums of squares; after
+//                both halves of g, sqrt.
 // The factorisation assumes W^T W has full rank (D >= d and independent
 // columns, as for a model's projection): a pivot below 1e-6 of the largest
 // diagonal entry is taken as 0 (its direction dropped).
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
 #include "kvsel_ring.h"
+
+#include <type_traits>
 
 namespace kvsel {
 
@@ -40,9 +47,9 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);   // finite inputs
 }
 
-// grid L * Hq, block 256 (4 waves). rfac[l][hq][2][d][d] bf16: R_hi, R_lo.
-__global__ __launch_bounds__(256) void k_gram_chol(const __bf16* __restrict__ w_o, int D, int Hq,
-                                                   uint16_t* __restrict__ rfac) {
+// grid L * Hq, block 256 (4 waves). factor[l][hq][2][d][d] bf16: R_hi, R_lo.
+__global__ __launch_bounds__(256) void k_l2_factor(const __bf16* __restrict__ w_o, int D, int Hq,
+                                                   uint16_t* __restrict__ factor) {
   __shared__ __align__(16) uint16_t wt[kHeadDim][kWtStride];   // W chunk, transposed: wt[e][c]
   __shared__ float a[kHeadDim][kChStride];                     // W^T W, then L (lower)
   __shared__ float s_piv;
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(256) void k_gram_chol(const __bf16* __restrict__ w_
     __syncthreads();
   }
   // ---- R = L^T as bf16 hi + lo: R[i][j] = L[j][i] for j >= i
-  uint16_t* rh = rfac + (((size_t)l * Hq + hq) * 2) * kHeadDim * kHeadDim;
+  uint16_t* rh = factor + (((size_t)l * Hq + hq) * 2) * kHeadDim * kHeadDim;
   uint16_t* rl = rh + kHeadDim * kHeadDim;
   for (int e = tid; e < kHeadDim * kHeadDim; e += 256) {
     const int i = e >> 7, j = e & (kHeadDim - 1);
@@ -120,11 +127,24 @@ __global__ __launch_bounds__(256) void k_gram_chol(const __bf16* __restrict__ w_
   }
 }
 
-// 1-D grid of key_blocks * H * L workgroups, block 512.
-__global__ __launch_bounds__(512) void k_value_weight_l2(const __bf16* __restrict__ v,
-                                                         const __bf16* __restrict__ rfac, int H,
-                                                         int G, int n, int n_cand, int key_blocks,
-                                                         float* __restrict__ weight) {
+constexpr int kL2Waves = 4;
+constexpr int kL2Block = kL2Waves * 64;   // keys per workgroup
+using L2Loader = RingLoader<kL2Waves>;
+constexpr int kL2Loads = L2Loader::kLoads;
+
+// MFMA operand of step s for lane half hf: the 16-byte piece 2s + hf of row
+// r (columns 16s + 8hf .. +8) of a ring slot, whose pieces are stored
+// XOR-swizzled by r & 15.
+__device__ __forceinline__ bf16x8 tri_op(const unsigned char* slot, int r, int hf, int s) {
+  return ld16(slot + r * kRowBytes + (((2 * s + hf) ^ (r & 15)) << 4));
+}
+
+// 1-D grid of key_blocks * H * L workgroups, block 256.
+__global__ __launch_bounds__(256, 3) void k_value_weight_l2(const __bf16* __restrict__ v,
+                                                            const __bf16* __restrict__ factor,
+                                                            int H, int G, int n, int n_cand,
+                                                            int key_blocks,
+                                                            float* __restrict__ weight) {
   __shared__ __align__(16) unsigned char ring[gSlots][gRowsBytes];
   int id = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = id % key_blocks;
@@ -138,104 +158,109 @@ __global__ __launch_bounds__(512) void k_value_weight_l2(const __bf16* __restric
   // R_hi tile then the R_lo tile
   const int ntiles = 4 * G;
 
-  const int key0 = kb * gBlock + wave * 64;
+  // this wave's 64 keys as MFMA B operands: step s, lane half hf holds
+  // columns 16s + 8hf .. +8 of the key's value row
+  const int key0 = kb * kL2Block + wave * 64;
   bf16x8 vop[2][8];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int key = key0 + nt * 32 + col;
-    if (key < n_cand) load_half_row(v + (lh * n + key) * (size_t)kHeadDim, hf, vop[nt]);
-    else zero_ops(vop[nt]);
+    if (key < n_cand) {
+      const unsigned char* row =
+          reinterpret_cast<const unsigned char*>(v + (lh * n + key) * (size_t)kHeadDim);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) vop[nt][s] = ld16(row + (2 * s + hf) * 16);
+    } else {
+      zero_ops(vop[nt]);
+    }
   }
-  GenLoader ld;
+  L2Loader ld;
   ld.init(kHeadDim);
   auto issue = [&](int t, int slot) {
     const int g = t >> 2, dt = (t >> 1) & 1, lo = t & 1;
-    const __bf16* base = rfac + ((((size_t)l * Hq + h * G + g) * 2 + lo) * kHeadDim) * kHeadDim;
+    const __bf16* base = factor + ((((size_t)l * Hq + h * G + g) * 2 + lo) * kHeadDim) * kHeadDim;
     ld.issue(base, dt * gTile, kHeadDim, kHeadDim, ring[slot]);
   };
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int t = 0; t < gSlots - 1; ++t) issue(min(t, ntiles - 1), t);
-  gen_wait<(gSlots - 1) * gLoads>();
+  // values are in registers once at most the prologue's loads remain
+  gen_wait<(gSlots - 1) * kL2Loads>();
 
   const bool any_key = key0 < n_cand;
   float ss[2] = {0.f, 0.f}, wsum[2] = {0.f, 0.f};
 
   auto begin_tile = [&](int t) -> const unsigned char* {
-    gen_wait_tile<gLoads>(t, ntiles);
+    gen_wait_tile<kL2Loads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
     int soff = (t % gSlots) * gRowsBytes;   // opaque: LDS reads stay inside the tile
     asm volatile("" : "+v"(soff));
     return ring[0] + soff;
   };
-  // part c (of 8) of a tile pair's accumulators: squares of 8 outputs of key set c / 4
-  auto fold_part = [&](const f32x16 (&acc)[2][2], int c, float (&ps)[2]) {
-    const int nt = c >> 2, mt = (c >> 1) & 1, i0 = (c & 1) * 8;
-    float sum = ps[nt];
-#pragma unroll
-    for (int i = i0; i < i0 + 8; ++i) sum = __builtin_fmaf(acc[mt][nt][i], acc[mt][nt][i], sum);
-    ps[nt] = sum;
-  };
-  // after the pair of rows [64, 128) of g: ||R v||_2 of both key sets
-  auto close_g = [&]() {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float tot = ss[nt] + __shfl_xor(ss[nt], 32);   // the other 16 output rows
-      wsum[nt] += __builtin_sqrtf(tot);
-      ss[nt] = 0.f;
-    }
-  };
-  auto mfma_tile = [&](const unsigned char* slot, f32x16 (&cur)[2][2], const f32x16 (&prev)[2][2],
-                       int part0, bool fold, float (&ps)[2]) {
+  // One ring tile of rows [64 DT, 64 DT + 64) of R. Row block mt (32 rows
+  // starting at 64 DT + 32 mt) is zero left of column 64 DT + 32 mt, so its
+  // steps start at 4 DT + 2 mt.
+  auto mfma_tile = [&](auto dtc, const unsigned char* slot, f32x16 (&cur)[2][2]) {
+    constexpr int DT = decltype(dtc)::value;
+    constexpr int s0 = 4 * DT, s1 = 4 * DT + 2;
     bf16x8 av[2][2];
-    read_step(slot, col, hf, 0, av[0]);
+    av[s0 & 1][0] = tri_op(slot, col, hf, s0);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (st + 1 < 8) read_step(slot, col, hf, st + 1, av[(st + 1) & 1]);
-      tile_step(av[st & 1], vop, st, cur);
-      if (fold && (st & 1)) fold_part(prev, part0 + (st >> 1), ps);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int st = s0; st < 8; ++st) {
+      if (st + 1 < 8) {
+        av[(st + 1) & 1][0] = tri_op(slot, col, hf, st + 1);
+        if (st + 1 >= s1) av[(st + 1) & 1][1] = tri_op(slot, 32 + col, hf, st + 1);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        cur[0][nt] = mfma32(av[st & 1][0], vop[nt][st], cur[0][nt]);
+        if (st >= s1) cur[1][nt] = mfma32(av[st & 1][1], vop[nt][st], cur[1][nt]);
+      }
     }
   };
-  // pair p (tiles 2p, 2p+1) into cur while pair p-1 (prev) is folded
-  auto step = [&](int p, f32x16 (&cur)[2][2], f32x16 (&prev)[2][2], bool fold) {
-    float ps[2] = {0.f, 0.f};
+  using D0 = std::integral_constant<int, 0>;
+  using D1 = std::integral_constant<int, 1>;
+  // pair p (tiles 2p, 2p+1: R_hi then R_lo of rows [64 DT, 64 DT + 64),
+  // DT = p & 1) into fresh accumulators, folded into the sums of squares;
+  // after rows [64, 128) of a g, its norm joins the sum over g
+  auto pair = [&](auto dtc, int p) {
+    constexpr int DT = decltype(dtc)::value;
+    f32x16 acc[2][2];
     const unsigned char* slot = begin_tile(2 * p);
     if (any_key) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) cur[mt][nt] = zero16();
-      mfma_tile(slot, cur, prev, 0, fold, ps);
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+      mfma_tile(dtc, slot, acc);
     }
     slot = begin_tile(2 * p + 1);
-    if (any_key) mfma_tile(slot, cur, prev, 4, fold, ps);
-    asm volatile("" : "+v"(ps[0]), "+v"(ps[1]));
-    if (fold) {
-      ss[0] += ps[0];
-      ss[1] += ps[1];
-      if ((p - 1) & 1) close_g();   // pair p-1 held rows [64, 128) of its g
+    if (any_key) {
+      mfma_tile(dtc, slot, acc);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float sum = ss[nt];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum = __builtin_fmaf(acc[mt][nt][i], acc[mt][nt][i], sum);
+        ss[nt] = sum;
+      }
+    }
+    if (DT == 1) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float tot = ss[nt] + __shfl_xor(ss[nt], 32);   // the other 16 output rows
+        wsum[nt] += __builtin_sqrtf(tot);
+        ss[nt] = 0.f;
+      }
     }
   };
-  auto fold_all = [&](const f32x16 (&acc)[2][2]) {
-    float ps[2] = {0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) fold_part(acc, c, ps);
-    ss[0] += ps[0];
-    ss[1] += ps[1];
-    close_g();   // the last pair always holds rows [64, 128)
-  };
-
-  f32x16 A[2][2], B[2][2];
-  const int npairs = 2 * G;   // even
-  step(0, A, B, false);
-  for (int p = 1; p + 1 < npairs; p += 2) {
-    step(p, B, A, true);
-    step(p + 1, A, B, true);
+  for (int g = 0; g < G; ++g) {
+    pair(D0{}, 2 * g);
+    pair(D1{}, 2 * g + 1);
   }
-  step(npairs - 1, B, A, true);
-  fold_all(B);
   gen_wait<0>();
   const float inv_g = 1.0f / (float)G;
 #pragma unroll
@@ -245,22 +270,22 @@ __global__ __launch_bounds__(512) void k_value_weight_l2(const __bf16* __restric
   }
 }
 
-size_t value_weight_l2_ws_bytes(int L, int Hq) {
-  return (size_t)L * Hq * 2 * kHeadDim * kHeadDim * sizeof(uint16_t);
+hipError_t value_l2_factor_launch(const void* w_o, int L, int H, int G, int D, void* factor,
+                                  hipStream_t st) {
+  const long long gc = (long long)L * H * G;
+  if (gc > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_l2_factor, dim3((unsigned)gc), dim3(256), 0, st,
+                     static_cast<const __bf16*>(w_o), D, H * G, static_cast<uint16_t*>(factor));
+  return hipGetLastError();
 }
 
-hipError_t value_weight_l2_launch(const void* v, const void* w_o, int L, int H, int G, int n,
-                                  int D, int n_cand, float* weight, void* ws, hipStream_t st) {
-  const int Hq = H * G;
-  const long long gc = (long long)L * Hq;
-  const int key_blocks = (n_cand + gBlock - 1) / gBlock;
+hipError_t value_weight_l2_launch(const void* v, const void* factor, int L, int H, int G, int n,
+                                  int n_cand, float* weight, hipStream_t st) {
+  const int key_blocks = (n_cand + kL2Block - 1) / kL2Block;
   const long long blocks = (long long)key_blocks * H * L;
-  if (gc > 0x7fffffffLL || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  uint16_t* rfac = static_cast<uint16_t*>(ws);
-  hipLaunchKernelGGL(k_gram_chol, dim3((unsigned)gc), dim3(256), 0, st, static_cast<const __bf16*>(w_o),
-                     D, Hq, rfac);
-  hipLaunchKernelGGL(k_value_weight_l2, dim3((unsigned)blocks), dim3(512), 0, st,
-                     static_cast<const __bf16*>(v), reinterpret_cast<const __bf16*>(rfac), H, G, n,
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_value_weight_l2, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(factor), H, G, n,
                      n_cand, key_blocks, weight);
   return hipGetLastError();
 }

@@ -20,8 +20,8 @@
  *    synchronised. No call allocates device memory or synchronises.
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
- *  - Workspace protocol (kvsel_score, kvsel_value_weight_l2, kvsel_select,
- *    kvsel_decode_attention): with ws == NULL the
+ *  - Workspace protocol (kvsel_score, kvsel_select, kvsel_decode_attention):
+ *    with ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
  *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
  *    Workspace contents need no initialisation and are scratch afterwards.
@@ -126,31 +126,45 @@ int32_t kvsel_value_weight(const void* v, const void* w_o,
                            float* weight, void* stream);
 
 /*
- * kvsel_value_weight_l2 -- the L2 form of the projected-value norm.
+ * kvsel_value_l2_factor, kvsel_value_weight_l2 -- the L2 form of the
+ * projected-value norm.
  *
  * [CriticalKV] §C.3 and footnote 1 (the L1 and L2 distances of the output
  * perturbation give similar gains), with the GQA mean of kvsel_value_weight:
  *   weight[l][h][j] = (1/G) sum_g sqrt( sum_{c<D} ( sum_{e<d}
  *                        w_o[l][c][(h*G+g)*d + e] * v[l][h][j][e] )^2 )
- * for j < n_cand. Computed as ||R v||_2 with R^T R = W^T W (the Cholesky
- * factor of each query head's d x d Gram matrix, formed in fp32 in the
- * workspace and held as two bf16 matrices), so the cost is independent of
- * D. The factorisation treats W^T W as positive definite: a pivot below
- * 1e-6 of the largest diagonal entry is dropped as zero, which is exact
- * for a rank-deficient slice (D < d, or dependent columns) only up to
+ * for j < n_cand. Since ||W v||_2^2 = v^T (W^T W) v = ||R v||_2^2 for the
+ * Cholesky factor R (upper triangular, R^T R = W^T W) of each query head's
+ * d x d Gram matrix, the weight is computed in two calls:
+ *
+ * kvsel_value_l2_factor: R for every (layer, query head), from the model's
+ * output projection alone, so it is computed once per model and reused.
+ * The Gram matrix is accumulated in fp32 from bf16 and factored in fp32;
+ * R is stored as two bf16 matrices whose sum carries it to ~2^-17
+ * relative. W^T W is treated as positive definite: a pivot below 1e-6 of
+ * the largest diagonal entry is taken as zero (its direction dropped), so
+ * a rank-deficient slice (D < d, or dependent columns) is factored up to
  * that threshold.
  *
- *   v      bf16 [L][H_kv][n][d]
- *   w_o    bf16 [L][D][H_kv*G*d]     output projection, (out, in) layout
- *   weight f32  [L][H_kv][n_cand]    1 <= n_cand <= n
+ *   w_o    bf16 [L][D][H_kv*G*d]          output projection, (out, in) layout
+ *   factor bf16 [L][H_kv*G][2][d][d]      out: R_hi, R_lo (zero below the
+ *                                         diagonal); L*H_kv*G*4*d*d bytes
  *
- * Limits: d == 128, else KVSEL_ERR_UNSUPPORTED. Needs a workspace
- * (protocol above): L * H_kv*G * 64 KiB.
+ * kvsel_value_weight_l2: the weight from the values and the factor.
+ *
+ *   v      bf16 [L][H_kv][n][d]
+ *   factor bf16 [L][H_kv*G][2][d][d]      as written by kvsel_value_l2_factor
+ *   weight f32  [L][H_kv][n_cand]         1 <= n_cand <= n
+ *
+ * Limits: d == 128, else KVSEL_ERR_UNSUPPORTED.
  */
-int32_t kvsel_value_weight_l2(const void* v, const void* w_o,
+int32_t kvsel_value_l2_factor(const void* w_o, int32_t L, int32_t H_kv,
+                              int32_t G, int32_t d, int32_t D,
+                              void* factor, void* stream);
+
+int32_t kvsel_value_weight_l2(const void* v, const void* factor,
                               int32_t L, int32_t H_kv, int32_t G, int32_t d,
-                              int32_t n, int32_t D, int32_t n_cand,
-                              float* weight, void* ws, size_t* ws_bytes,
+                              int32_t n, int32_t n_cand, float* weight,
                               void* stream);
 
 /*

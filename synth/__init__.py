@@ -67,6 +67,7 @@ class Workload:
     beta: float = 0.2            # kept fraction (window included)
     adaptive: bool = False       # one budget per layer shared by all heads
     value_weight: bool = False   # value-norm weighted two-stage selection
+    value_norm: str = "l1"       # norm of the projected value: 'l1' or 'l2'
     D: int = 0                   # model width for w_o
     alpha: float = 0.5
     eps: float = 1e-4
@@ -116,6 +117,10 @@ WORKLOADS = {
         Workload("criticalkv_llama8b_n128k", L=32, H_kv=8, G=4, d=128,
                  n=131072, W=32, pool=7, beta=0.10, value_weight=True,
                  D=4096),
+        # the same with the L2 norm of the projected value
+        Workload("criticalkv_l2_llama8b_n128k", L=32, H_kv=8, G=4, d=128,
+                 n=131072, W=32, pool=7, beta=0.10, value_weight=True,
+                 value_norm="l2", D=4096),
         # CriticalAdaKV: value-norm weighted two-stage selection over one
         # budget per layer (the flattened candidates of its heads), n = 32K, 20%
         Workload("criticaladakv_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768,

@@ -176,41 +176,49 @@ def test_decode_workspace_query(lib):
     assert rc2 == OK and nb2 >= nb
 
 
-def _vw_l2(lib, **kw):
+def _l2_args(**kw):
     a = dict(L=2, H=8, G=4, d=128, n=100, D=4096, n_cand=68)
     a.update(kw)
-    nb = ctypes.c_size_t(0)
-    rc = lib.kvsel_value_weight_l2(None, None, a["L"], a["H"], a["G"], a["d"], a["n"], a["D"],
-                                   a["n_cand"], None, None, ctypes.byref(nb), None)
-    return rc, nb.value
+    return a
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(), OK), (dict(D=100), OK), (dict(D=1), OK), (dict(n_cand=100), OK),
-    (dict(L=0), ARG), (dict(G=0), ARG), (dict(D=0), ARG), (dict(n_cand=0), ARG),
-    (dict(n_cand=101), ARG), (dict(d=64), UNSUP),
+    (dict(L=0), ARG), (dict(G=0), ARG), (dict(D=0), ARG), (dict(d=64), UNSUP),
+    (dict(H=1 << 20, G=16), UNSUP),
 ])
-def test_value_weight_l2_ranges(lib, kw, code):
-    assert _vw_l2(lib, **kw)[0] == code
-
-
-def test_value_weight_l2_workspace_query(lib):
-    rc, nb = _vw_l2(lib)
-    # one 128 x 128 factor, as two bf16 matrices, per (layer, query head)
-    assert rc == OK and nb == 2 * 8 * 4 * 2 * 128 * 128 * 2
-    assert lib.kvsel_value_weight_l2(None, None, 2, 8, 4, 128, 100, 4096, 68, None, None, None,
-                                     None) == ARG
+@no_gpu_only
+def test_value_l2_factor_reject(lib, kw, code):
+    p = ctypes.c_void_p(1 << 20)
+    a = _l2_args(**kw)
+    assert lib.kvsel_value_l2_factor(p, a["L"], a["H"], a["G"], a["d"], a["D"], p, None) == code
 
 
 @no_gpu_only
-def test_value_weight_l2_reject(lib):
+def test_value_l2_factor_pointers(lib):
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.kvsel_value_l2_factor
+    assert f(None, 2, 8, 4, 128, 4096, p, None) == ARG
+    assert f(p, 2, 8, 4, 128, 4096, None, None) == ARG
+    assert f(p, 2, 8, 4, 128, 4096, ctypes.c_void_p((1 << 20) + 8), None) == ARG   # misaligned
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), ARG), (dict(G=0), ARG), (dict(n_cand=0), ARG), (dict(n_cand=101), ARG),
+    (dict(n=0), ARG), (dict(d=64), UNSUP),
+])
+@no_gpu_only
+def test_value_weight_l2_reject(lib, kw, code):
+    p = ctypes.c_void_p(1 << 20)
+    a = _l2_args(**kw)
+    assert lib.kvsel_value_weight_l2(p, p, a["L"], a["H"], a["G"], a["d"], a["n"], a["n_cand"],
+                                     p, None) == code
+
+
+@no_gpu_only
+def test_value_weight_l2_pointers(lib):
     p = ctypes.c_void_p(1 << 20)
     f = lib.kvsel_value_weight_l2
-    need = _vw_l2(lib)[1]
-    nb = ctypes.c_size_t(need - 1)
-    assert f(p, p, 2, 8, 4, 128, 100, 4096, 68, p, p, ctypes.byref(nb), None) == WS
-    nb = ctypes.c_size_t(need)
-    assert f(None, p, 2, 8, 4, 128, 100, 4096, 68, p, p, ctypes.byref(nb), None) == ARG
-    assert f(p, p, 2, 8, 4, 128, 100, 4096, 68, None, p, ctypes.byref(nb), None) == ARG
-    assert f(p, ctypes.c_void_p((1 << 20) + 8), 2, 8, 4, 128, 100, 4096, 68, p, p,
-             ctypes.byref(nb), None) == ARG   # misaligned
+    assert f(None, p, 2, 8, 4, 128, 100, 68, p, None) == ARG
+    assert f(p, None, 2, 8, 4, 128, 100, 68, p, None) == ARG
+    assert f(p, p, 2, 8, 4, 128, 100, 68, None, None) == ARG
+    assert f(p, ctypes.c_void_p((1 << 20) + 8), 2, 8, 4, 128, 100, 68, p, None) == ARG

@@ -273,7 +273,8 @@ def test_value_weight_l2(L, H, G, n, D, n_cand):
     wl = _wl(L=L, H_kv=H, G=G, n=n, W=n - n_cand if n_cand < n else 1, value_weight=True, D=D)
     data = gen(wl, seed=8, which=("v", "w_o"))
     print(f"[gpu] kvsel_value_weight_l2 L={L} H={H} G={G} n={n} D={D}", flush=True)
-    w = kv.kvsel_value_weight_l2(to_dev(data["v"]), to_dev(data["w_o"]), G=G, n_cand=n_cand)
+    fac = kv.kvsel_value_l2_factor(to_dev(data["w_o"]), G=G, H_kv=H)
+    w = kv.kvsel_value_weight_l2(to_dev(data["v"]), fac, G=G, n_cand=n_cand)
     torch.cuda.synchronize()
     w = w.cpu().numpy()
     for l in range(L):
@@ -286,10 +287,35 @@ def test_value_weight_l2_deterministic():
     wl = _wl(L=1, H_kv=2, G=4, n=3000, W=1, value_weight=True, D=512)
     data = gen(wl, seed=9, which=("v", "w_o"))
     v, w_o = to_dev(data["v"]), to_dev(data["w_o"])
-    a = kv.kvsel_value_weight_l2(v, w_o, G=wl.G, n_cand=wl.n).cpu().numpy()
+    fac = kv.kvsel_value_l2_factor(w_o, G=wl.G, H_kv=wl.H_kv)
+    a = kv.kvsel_value_weight_l2(v, fac, G=wl.G, n_cand=wl.n).cpu().numpy()
+    f0 = fac.cpu().view(torch.int16).numpy()
     for _ in range(2):
-        b = kv.kvsel_value_weight_l2(v, w_o, G=wl.G, n_cand=wl.n).cpu().numpy()
+        fac = kv.kvsel_value_l2_factor(w_o, G=wl.G, H_kv=wl.H_kv)
+        np.testing.assert_array_equal(fac.cpu().view(torch.int16).numpy(), f0)
+        b = kv.kvsel_value_weight_l2(v, fac, G=wl.G, n_cand=wl.n).cpu().numpy()
         np.testing.assert_array_equal(a, b)
+
+
+def test_value_l2_factor_properties():
+    """The factor is upper triangular with a non-negative diagonal, and
+    (R_hi + R_lo)^T (R_hi + R_lo) reproduces the fp64 Gram matrix W^T W of
+    each query head's slice."""
+    wl = _wl(L=2, H_kv=2, G=3, n=64, W=1, value_weight=True, D=700)
+    data = gen(wl, seed=10, which=("w_o",))
+    fac = kv.kvsel_value_l2_factor(to_dev(data["w_o"]), G=wl.G, H_kv=wl.H_kv)
+    torch.cuda.synchronize()
+    r = fac.float().cpu().numpy().astype(np.float64)
+    for l in range(wl.L):
+        w = synth.bf16_to_f64(data["w_o"][l])
+        for hq in range(wl.H_kv * wl.G):
+            hi, lo = r[l, hq, 0], r[l, hq, 1]
+            assert not np.tril(hi, -1).any() and not np.tril(lo, -1).any()
+            assert (np.diag(hi) >= 0).all()
+            R = hi + lo
+            M = w[:, hq * 128:(hq + 1) * 128].T @ w[:, hq * 128:(hq + 1) * 128]
+            err = np.abs(R.T @ R - M).max()
+            assert err <= 1e-4 * np.abs(M).max(), (l, hq, err)
 
 
 # ------------------------------------------------- decode over kept rows ----

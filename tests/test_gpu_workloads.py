@@ -158,32 +158,30 @@ def test_window_workload_full(name):
     _check_compact(dev, host, idx, offs, 0, wl)
 
 
-@pytest.mark.parametrize("name", ["criticalkv_llama8b_n128k", "criticaladakv_llama8b_n32k"])
+@pytest.mark.parametrize("name", ["criticalkv_llama8b_n128k", "criticaladakv_llama8b_n32k",
+                                  "criticalkv_l2_llama8b_n128k"])
 def test_criticalkv_full(name):
     wl = synth.WORKLOADS[name]
     sampled = [0, wl.L - 1]
     dev, host = device_inputs(wl, set(sampled), ("q", "k", "v", "w_o"))
     s, r = _score(wl, dev)
     _check_scores(wl, s, r, host, [0])
-    print("[gpu] kvsel_value_weight full", flush=True)
-    w = kv.kvsel_value_weight(dev["v"], dev["w_o"], G=wl.G, n_cand=wl.n_cand)
+    if wl.value_norm == "l2":
+        print("[gpu] kvsel_value_l2_factor + kvsel_value_weight_l2 full", flush=True)
+        fac = kv.kvsel_value_l2_factor(dev["w_o"], G=wl.G, H_kv=wl.H_kv)
+        w = kv.kvsel_value_weight_l2(dev["v"], fac, G=wl.G, n_cand=wl.n_cand)
+        del fac
+        norm = oracle.value_weight_l2
+    else:
+        print("[gpu] kvsel_value_weight full", flush=True)
+        w = kv.kvsel_value_weight(dev["v"], dev["w_o"], G=wl.G, n_cand=wl.n_cand)
+        norm = oracle.value_weight
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
     for l in sampled:
         pos = np.sort(rng.choice(wl.n_cand, 96, replace=False))
-        ref = oracle.value_weight(synth.bf16_to_f64(host[("v", l)]), synth.bf16_to_f64(host[("w_o", l)]),
-                                  wl.G, pos)
+        ref = norm(synth.bf16_to_f64(host[("v", l)]), synth.bf16_to_f64(host[("w_o", l)]), wl.G, pos)
         assert_scores_close(w[l].cpu().numpy()[:, pos], ref, f"value weight l{l}")
-    if name == "criticalkv_llama8b_n128k":
-        print("[gpu] kvsel_value_weight_l2 full", flush=True)
-        w2 = kv.kvsel_value_weight_l2(dev["v"], dev["w_o"], G=wl.G, n_cand=wl.n_cand)
-        torch.cuda.synchronize()
-        for l in sampled:
-            pos = np.sort(rng.choice(wl.n_cand, 64, replace=False))
-            ref = oracle.value_weight_l2(synth.bf16_to_f64(host[("v", l)]),
-                                         synth.bf16_to_f64(host[("w_o", l)]), wl.G, pos)
-            assert_scores_close(w2[l].cpu().numpy()[:, pos], ref, f"value weight l2 l{l}")
-        del w2
     idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=wl.W, budget=wl.budget, weight=w,
                                        adaptive=wl.adaptive, score_norm=1.0 / (wl.W * wl.G),
                                        eps=wl.eps, alpha=wl.alpha, return_stage=True)
