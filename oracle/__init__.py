@@ -284,6 +284,41 @@ def select_layer(scores: np.ndarray, budget: int, W: int, n: int,
     return np.concatenate(idx_parts), np.asarray(offs, np.int64), np.concatenate(st_parts)
 
 
+def select_budgets(scores: np.ndarray, budgets, W: int, n: int,
+                   weight: np.ndarray | None = None, alpha: float = 0.5,
+                   score_norm: float = 1.0, eps: float = 1e-4, dtype=np.float64):
+    """Kept positions of one layer under a per-head budget vector.
+
+    [CriticalKV, §4.1]: the method is combined with HeadKV, whose offline
+    budget allocation gives every head of every layer its own budget.
+    Reading: budgets[h] counts head h's W window positions, as the uniform
+    budget does, and is clamped into [W, n] (a head keeps at least its window
+    and at most everything). Each head is then selected on its own, exactly
+    as by select_layer with a uniform budget: the top k_h = budgets[h] - W
+    candidates (two-stage when weight is given), then the window.
+
+    scores, weight: [H][n_cand], n_cand = n - W. budgets: [H].
+    Returns (idx [sum of clamped budgets] packed by head, head_offsets [H+1],
+    stage), the packing of the adaptive layout.
+    """
+    H, n_cand = scores.shape
+    assert n_cand == n - W
+    b = np.clip(np.asarray(budgets, np.int64), W, n)
+    window = np.arange(n - W, n)
+    idx_parts, st_parts, offs = [], [], [0]
+    for h in range(H):
+        k = int(b[h]) - W
+        if weight is None:
+            pick = topk_indices(scores[h], k)
+            st = np.ones(k, np.uint8)
+        else:
+            pick, st = _two_stage(scores[h], weight[h], k, alpha, score_norm, eps, dtype)
+        idx_parts += [pick, window]
+        st_parts += [st, np.zeros(W, np.uint8)]
+        offs.append(offs[-1] + k + W)
+    return np.concatenate(idx_parts), np.asarray(offs, np.int64), np.concatenate(st_parts)
+
+
 # -------------------------------------------------------------- compaction ----
 
 def compact_layer(k: np.ndarray, v: np.ndarray, idx: np.ndarray,

@@ -429,6 +429,72 @@ def check_value_weight_l2(o):
     np.testing.assert_allclose(o.value_weight_l2(v, w, G, pos), got[:, pos], rtol=1e-15)
 
 
+# ---------------------------------------------------- per-head budgets ----
+
+def check_select_budgets_example(o):
+    g = load_golden("select_budgets_example.txt")
+    n, W = int(g["n"][0]), int(g["W"][0])
+    scores = np.array([g[f"pooled{h}"] for h in range(4)])
+    idx, offs, st = o.select_budgets(scores, [int(b) for b in g["budgets"]], W, n)
+    np.testing.assert_array_equal(idx, g["kept"])
+    np.testing.assert_array_equal(offs, g["head_offsets"])
+    np.testing.assert_array_equal(st == 0, np.isin(np.arange(len(idx)), np.concatenate(
+        [np.arange(offs[h + 1] - W, offs[h + 1]) for h in range(4)])))
+
+
+def check_select_budgets_bruteforce(o):
+    rng = np.random.default_rng(43)
+    for trial in range(15):
+        H, n, W = 4, 30, 3
+        n_cand = n - W
+        scores = rng.integers(0, 5, size=(H, n_cand)).astype(np.float64)
+        budgets = rng.integers(W - 2, n + 3, size=H)      # some outside [W, n]
+        idx, offs, st = o.select_budgets(scores, budgets, W, n)
+        eff = [min(max(int(b), W), n) for b in budgets]
+        assert list(offs) == [sum(eff[:h]) for h in range(H + 1)] and len(idx) == offs[-1]
+        for h in range(H):
+            seg = [int(x) for x in idx[offs[h]:offs[h + 1]]]
+            assert seg == sorted(seg) and seg[len(seg) - W:] == list(range(n - W, n))
+            _assert_topk_property(scores[h], seg[:len(seg) - W], eff[h] - W)
+            assert (st[offs[h]:offs[h + 1] - W] == 1).all() and (st[offs[h + 1] - W:offs[h + 1]] == 0).all()
+        # two-stage, per head with its own k: stage-1 a top-floor(alpha k) by
+        # score, stage-2 a top of the rest by (score*norm + eps)*w
+        w = rng.integers(0, 4, size=(H, n_cand)).astype(np.float64)
+        alpha = float(rng.choice([0.0, 0.5, 1.0]))
+        idx, offs, st = o.select_budgets(scores, budgets, W, n, weight=w, alpha=alpha,
+                                         score_norm=0.5, eps=0.01)
+        for h in range(H):
+            k = eff[h] - W
+            k1 = int(math.floor(alpha * k))
+            seg, sst = idx[offs[h]:offs[h + 1]], st[offs[h]:offs[h + 1]]
+            s1 = [int(i) for i, s in zip(seg, sst) if s == 1]
+            s2 = [int(i) for i, s in zip(seg, sst) if s == 2]
+            _assert_topk_property(scores[h], s1, k1)
+            rest = [j for j in range(n_cand) if j not in set(s1)]
+            key = (scores[h] * 0.5 + 0.01) * w[h]
+            _assert_topk_property(np.array([key[j] for j in rest]), [rest.index(j) for j in s2], k - k1)
+
+
+def check_select_budgets_reductions(o):
+    rng = np.random.default_rng(44)
+    H, n, W = 4, 50, 5
+    scores = rng.random((H, n - W))
+    w = rng.random((H, n - W)) + 0.1
+    # one budget for every head: the uniform selection, packed
+    for weight in (None, w):
+        uni, _, ust = o.select_layer(scores, 20, W, n, weight=weight)
+        idx, offs, st = o.select_budgets(scores, [20] * H, W, n, weight=weight)
+        np.testing.assert_array_equal(idx, uni.reshape(-1))
+        np.testing.assert_array_equal(st, ust.reshape(-1))
+        np.testing.assert_array_equal(offs, 20 * np.arange(H + 1))
+    # each head alone: the one-head uniform selection with its own budget
+    budgets = [W, 7, 31, n]
+    idx, offs, _ = o.select_budgets(scores, budgets, W, n)
+    for h in range(H):
+        one, _, _ = o.select_layer(scores[h:h + 1], budgets[h], W, n)
+        np.testing.assert_array_equal(idx[offs[h]:offs[h + 1]], one[0])
+
+
 # ------------------------------------------------- decode over kept rows ----
 
 def check_decode_hand_example(o):
@@ -509,5 +575,6 @@ ALL_CHECKS = [
     check_external, check_maxpool, check_value_weight, check_select_examples,
     check_select_bruteforce, check_select_reductions, check_compact,
     check_decode_hand_example, check_decode_bruteforce, check_decode_sdpa, check_decode_closed_forms,
-    check_value_weight_l2,
+    check_value_weight_l2, check_select_budgets_example, check_select_budgets_bruteforce,
+    check_select_budgets_reductions,
 ]

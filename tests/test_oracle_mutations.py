@@ -49,6 +49,10 @@ MUTANTS = {
     "l2_no_mean": ("            out[h] += np.sqrt((proj * proj).sum(axis=1))\n        out[h] /= G",
                    "            out[h] += np.sqrt((proj * proj).sum(axis=1))\n        out[h] /= 1"),
     "l2_wrong_slice": ("proj = vh @ w_o[:, hq * d:(hq + 1) * d].T      # [m][D]", "proj = vh @ w_o[:, h * d:(h + 1) * d].T      # [m][D]"),
+    "budgets_no_clamp": ("b = np.clip(np.asarray(budgets, np.int64), W, n)", "b = np.asarray(budgets, np.int64)"),
+    "budgets_window_not_counted": ("        k = int(b[h]) - W\n", "        k = max(int(b[h]) - 2 * W, 0)\n"),
+    "budgets_head_shifted": ("        k = int(b[h]) - W\n", "        k = int(b[(h + 1) % H]) - W\n"),
+    "budgets_offsets_no_window": ("offs.append(offs[-1] + k + W)", "offs.append(offs[-1] + k)"),
     "compact_wrong_head": ("return (np.stack([k[h, idx[h]] for h in range(H)]),", "return (np.stack([k[0, idx[h]] for h in range(H)]),"),
 }
 
