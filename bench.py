@@ -61,7 +61,7 @@ def traffic_from_profiles(key, sha):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(wl, host, seconds, w_host=None):
+def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
     """The oracle (fp64 numpy) on the same inputs, one (layer, KV head) at a
     time in order, until `seconds` of CPU work: attention scores, max-pool,
     the value weight when the workload uses it, and top-k selection.
@@ -91,9 +91,13 @@ def cpu_baseline(wl, host, seconds, w_host=None):
             wo = synth.bf16_to_f64(w_host[l][:, h * wl.G * wl.d:(h + 1) * wl.G * wl.d])
             norm = oracle.value_weight_l2 if wl.value_norm == "l2" else oracle.value_weight
             weight = norm(v, wo, wl.G, np.arange(wl.n_cand))
-        oracle.select_layer(pooled, wl.budget if not wl.adaptive else wl.budget // wl.H_kv,
-                            wl.W_kept, wl.n, weight=weight, alpha=wl.alpha,
-                            score_norm=1.0 / (wl.W * wl.G), eps=wl.eps)
+        if budgets is not None:
+            oracle.select_budgets(pooled, budgets[l, h:h + 1], wl.W_kept, wl.n, weight=weight,
+                                  alpha=wl.alpha, score_norm=1.0 / (wl.W * wl.G), eps=wl.eps)
+        else:
+            oracle.select_layer(pooled, wl.budget if not wl.adaptive else wl.budget // wl.H_kv,
+                                wl.W_kept, wl.n, weight=weight, alpha=wl.alpha,
+                                score_norm=1.0 / (wl.W * wl.G), eps=wl.eps)
         units += 1
     dt = time.perf_counter() - t0
     what = "scores, max-pool" + (", value weight" if wl.value_weight else "") + " and top-k selection"
@@ -182,6 +186,12 @@ def main():
         torch.cuda.synchronize(dev)
         ms_factor = f0.elapsed_time(f1)
 
+    budgets, b_host, stride = None, None, None
+    if wl.budget_vector:
+        b_host = synth.gen_budgets(wl, args.seed)
+        budgets = torch.from_numpy(b_host).to(dev)
+        stride = int(np.clip(b_host, W_kept, wl.n).astype(np.int64).sum(axis=1).max())
+
     def step(marks=None):
         if marks is not None:
             marks[0].record()
@@ -195,10 +205,16 @@ def main():
             kv.kvsel_value_weight(v, w_o, G=wl.G, n_cand=wl.n_cand, weight=weight)
         if marks is not None:
             marks[2].record()
-        idx, offs, _ = kv.kvsel_select(scores, n=wl.n, W=W_kept, budget=wl.budget,
-                                       adaptive=wl.adaptive, weight=weight,
-                                       score_norm=1.0 / (wl.W * wl.G), eps=wl.eps,
-                                       alpha=wl.alpha)
+        if budgets is not None:
+            idx, offs, _ = kv.kvsel_select_budgets(scores, budgets, n=wl.n, W=W_kept,
+                                                   layer_stride=stride, weight=weight,
+                                                   score_norm=1.0 / (wl.W * wl.G), eps=wl.eps,
+                                                   alpha=wl.alpha)
+        else:
+            idx, offs, _ = kv.kvsel_select(scores, n=wl.n, W=W_kept, budget=wl.budget,
+                                           adaptive=wl.adaptive, weight=weight,
+                                           score_norm=1.0 / (wl.W * wl.G), eps=wl.eps,
+                                           alpha=wl.alpha)
         if marks is not None:
             marks[3].record()
         kept = kv.kvsel_compact(k, v, idx, offs)
@@ -249,6 +265,7 @@ def main():
         "config": {"workload": wl.name, "L": wl.L, "H_kv": wl.H_kv, "G": wl.G, "d": wl.d,
                    "n": wl.n, "W": wl.W, "q_mode": wl.q_mode, "agg": wl.agg, "pool": wl.pool,
                    "budget": wl.budget, "adaptive": wl.adaptive,
+                   **({"budget_vector": True, "layer_stride": stride} if wl.budget_vector else {}),
                    "value_weight": wl.value_weight,
                    **({"value_norm": wl.value_norm} if wl.value_weight else {}),
                    "seed": args.seed,
@@ -322,12 +339,16 @@ def main():
         d1.record()
         torch.cuda.synchronize(dev)
         ms_dec = d0.elapsed_time(d1) / reps
-        dec_bytes = 2 * ko.numel() * 2 + q_dec.numel() * 2 + out_dec.numel() * 4
+        # kept rows actually read: the packed rows before each layer's last
+        # head offset (a budget-vector row may end before its stride)
+        rows = (int(kept_offs[:, -1].sum().item()) if kept_offs is not None
+                else ko.shape[0] * ko.shape[1])
+        dec_bytes = 2 * rows * wl.d * 2 + q_dec.numel() * 2 + out_dec.numel() * 4
         out["next_rows"] = {"decode_attention": {
             "bound": "hbm", "ms_per_call": ms_dec, "bytes_per_launch": dec_bytes,
             "achieved": dec_bytes / (ms_dec * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": dec_bytes / (ms_dec * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kept_rows_per_layer": int(ko.shape[1])}}
+            "kept_rows": rows}}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         if host is None:   # bring back the first layers, which the sample uses
@@ -337,7 +358,7 @@ def main():
         w_host = None
         if wl.value_weight:
             w_host = t["w_o"][:2].cpu().view(torch.int16).numpy().view(np.uint16)
-        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds, w_host)
+        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds, w_host, b_host)
     print(json.dumps(out), flush=True)
 
 

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_value_weight",
     "kvsel_value_l2_factor", "kvsel_value_weight_l2",
-    "kvsel_select", "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
+    "kvsel_select", "kvsel_select_budgets", "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
     "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX",
 ]
@@ -48,6 +48,9 @@ _SIGNATURES = {
     "kvsel_select": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                      _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                      _c_size_p, _c_void_p],
+    "kvsel_select_budgets": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
+                             _c_i64, _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p,
+                             _c_void_p, _c_size_p, _c_void_p],
     "kvsel_compact": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                       _c_void_p, _c_i64, _c_void_p, _c_void_p, _c_void_p],
     "kvsel_decode_attention": [_c_void_p, _c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -236,8 +239,47 @@ def kvsel_select(scores, *, n: int, W: int, budget: int, adaptive: bool = False,
     return idx, offs, stage
 
 
-def kvsel_compact(k, v, idx, head_offsets=None):
-    """Gather kept rows: returns (k_out, v_out) bf16 [L][kept_per_layer][d]."""
+def kvsel_select_budgets(scores, budgets, *, n: int, W: int, layer_stride: int | None = None,
+                         weight=None, score_norm: float = 1.0, eps: float = 1e-4,
+                         alpha: float = 0.5, return_stage: bool = False, workspace=None):
+    """Kept positions under a per-head budget vector. scores f32 [L][H_kv][n-W];
+    budgets i32 [L][H_kv] on the device. Returns (idx [L][layer_stride],
+    head_offsets [L][H_kv+1], stage). layer_stride defaults to the largest
+    per-layer sum of the budgets clamped into [W, n] (read back from the
+    device: a synchronising copy; pass it to avoid that)."""
+    _need(scores, torch.float32, "scores", 3)
+    _need(budgets, torch.int32, "budgets", 2)
+    if weight is not None:
+        _need(weight, torch.float32, "weight", 3)
+        if weight.shape != scores.shape:
+            raise ValueError("weight must match scores")
+    L, H, n_cand = scores.shape
+    if n_cand != n - W:
+        raise ValueError(f"scores has {n_cand} candidates, expected n-W={n - W}")
+    if tuple(budgets.shape) != (L, H):
+        raise ValueError(f"budgets must be {(L, H)}, got {tuple(budgets.shape)}")
+    if layer_stride is None:
+        layer_stride = int(budgets.clamp(W, n).sum(dim=1).max().item())
+    dev = scores.device
+    idx = torch.empty((L, layer_stride), dtype=torch.int32, device=dev)
+    offs = torch.empty((L, H + 1), dtype=torch.int32, device=dev)
+    stage = torch.empty((L, layer_stride), dtype=torch.uint8, device=dev) if return_stage else None
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_select_budgets
+    args = (L, H, n, W)
+    tail = (float(score_norm), float(eps), float(alpha))
+    _check(f(None, _ptr(weight), *args, None, int(layer_stride), *tail, None, None, None, None,
+             ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(scores), _ptr(weight), *args, _ptr(budgets), int(layer_stride), *tail, _ptr(idx),
+             _ptr(offs), _ptr(stage), _ptr(ws), ctypes.byref(nbytes), _stream(dev)))
+    return idx, offs, stage
+
+
+def kvsel_compact(k, v, idx, head_offsets=None, k_out=None, v_out=None):
+    """Gather kept rows: returns (k_out, v_out) bf16 [L][kept_per_layer][d]
+    (allocated unless given)."""
     _need(k, torch.bfloat16, "k", 4)
     _need(v, torch.bfloat16, "v", 4)
     _need(idx, torch.int32, "idx")
@@ -249,8 +291,15 @@ def kvsel_compact(k, v, idx, head_offsets=None):
         raise ValueError("idx must have a leading L axis")
     if head_offsets is not None:
         _need(head_offsets, torch.int32, "head_offsets", 2)
-    k_out = torch.empty((L, kept, d), dtype=k.dtype, device=k.device)
-    v_out = torch.empty((L, kept, d), dtype=v.dtype, device=v.device)
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        if t is not None:
+            _need(t, torch.bfloat16, name, 3)
+            if tuple(t.shape) != (L, kept, d):
+                raise ValueError(f"{name} must be {(L, kept, d)}, got {tuple(t.shape)}")
+    if k_out is None:
+        k_out = torch.empty((L, kept, d), dtype=k.dtype, device=k.device)
+    if v_out is None:
+        v_out = torch.empty((L, kept, d), dtype=v.dtype, device=v.device)
     _check(lib().kvsel_compact(_ptr(k), _ptr(v), L, H, d, n, _ptr(idx), _ptr(head_offsets),
                                kept, _ptr(k_out), _ptr(v_out), _stream(k.device)))
     return k_out, v_out

@@ -168,6 +168,50 @@ int32_t kvsel_select(const float* scores, const float* weight, int32_t L, int32_
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 
+int32_t kvsel_select_budgets(const float* scores, const float* weight, int32_t L, int32_t H_kv,
+                             int32_t n, int32_t W, const int32_t* budgets, int64_t layer_stride,
+                             float score_norm, float eps, float alpha, int32_t* idx,
+                             int32_t* head_offsets, uint8_t* stage, void* ws, size_t* ws_bytes,
+                             void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || n < 1 || W < 0 || W >= n) return KVSEL_ERR_ARG;
+  if (layer_stride < 1 || layer_stride > (int64_t)H_kv * n) return KVSEL_ERR_ARG;
+  if (weight) {
+    if (!(alpha >= 0.f && alpha <= 1.f)) return KVSEL_ERR_ARG;
+    if (!(score_norm > 0.f) || !std::isfinite(score_norm)) return KVSEL_ERR_ARG;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return KVSEL_ERR_ARG;
+  }
+  const int64_t n_cand = (int64_t)n - W;
+  if ((int64_t)H_kv * n > kMaxIndex || layer_stride > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  SelectPlan p;
+  p.L = L; p.H = H_kv; p.n = n; p.W = W; p.n_cand = (int)n_cand;
+  p.budget = 0;           // per segment, from the budget vector
+  p.adaptive = false;
+  p.two_stage = weight != nullptr;
+  p.score_norm = score_norm;
+  p.eps = eps;
+  p.k = 0;
+  p.k1 = 0;
+  p.segments = L * H_kv;
+  p.seg_len = n_cand;
+  p.resident = false;
+  p.budgets = budgets;
+  p.stride = layer_stride;
+  p.alpha = alpha;
+  const size_t need = select_ws_bytes(p);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!scores || !budgets || !idx || !head_offsets) return KVSEL_ERR_ARG;
+  if (!aligned16(scores) || (weight && !aligned16(weight))) return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return KVSEL_ERR_ARG;
+  const hipError_t e = select_launch(p, scores, weight, idx, head_offsets, stage, ws,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
 int32_t kvsel_compact(const void* k, const void* v, int32_t L, int32_t H_kv, int32_t d,
                       int32_t n, const int32_t* idx, const int32_t* head_offsets,
                       int64_t kept_per_layer, void* k_out, void* v_out, void* stream) {

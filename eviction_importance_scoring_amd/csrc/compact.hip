@@ -30,6 +30,14 @@ __global__ __launch_bounds__(256) void k_compact(const u32x4* __restrict__ k,
   const int64_t base = (int64_t)blockIdx.x * kItems * kCompactThreads + threadIdx.x;
   const int32_t* il = idx + (size_t)l * kept;
   const int32_t* o = offs ? offs + (size_t)l * (H + 1) : nullptr;
+  // packed rows: only those before the last head's end (clamped into the
+  // layer) are written; a budget-vector row may end well before `kept`
+  int64_t lim = total;
+  if (o) {
+    const int64_t e = o[H];
+    lim = (e < 0 ? 0 : (e > kept ? kept : e)) * vecs;
+  }
+  if (base >= lim) return;   // no barriers below
 
   int64_t row[kItems];
   int c[kItems];
@@ -39,7 +47,7 @@ __global__ __launch_bounds__(256) void k_compact(const u32x4* __restrict__ k,
     const int64_t item = base + (int64_t)j * kCompactThreads;
     row[j] = item / vecs;
     c[j] = (int)(item - row[j] * vecs);
-    pos[j] = item < total ? il[row[j]] : -1;
+    pos[j] = item < lim ? il[row[j]] : -1;
   }
   u32x4 kv[kItems], vv[kItems];
 #pragma unroll
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(256) void k_compact(const u32x4* __restrict__ k,
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int64_t item = base + (int64_t)j * kCompactThreads;
-    if (item < total) {
+    if (item < lim) {
       const size_t dst = (size_t)l * total + item;
       __builtin_nontemporal_store(kv[j], ko + dst);
       __builtin_nontemporal_store(vv[j], vo + dst);

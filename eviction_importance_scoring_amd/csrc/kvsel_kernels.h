@@ -52,6 +52,9 @@ struct SelectPlan {
   int segments;           // L*H (uniform) or L (adaptive)
   int64_t seg_len;        // n_cand or H*n_cand
   bool resident;          // segment fits in LDS
+  const int32_t* budgets = nullptr;   // per-head budgets [L][H] (device), or null
+  int64_t stride = 0;     // layer row of idx when budgets are given
+  float alpha = 0.f;
 };
 
 size_t select_ws_bytes(const SelectPlan& p);

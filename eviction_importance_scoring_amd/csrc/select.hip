@@ -27,6 +27,12 @@
 // Segments of up to kResidentMax candidates are read from HBM once into
 // the LDS of one workgroup; longer ones are spread over many workgroups
 // (below).
+//
+// Per-head budget vector ([CriticalKV] §4.1: HeadKV's offline per-head
+// budgets): segments are heads, each with its own budget b (window
+// included, clamped into [W, n]) and so its own k = b - W (and k1); a
+// layer's heads are packed in order into a row of `stride` entries, and
+// entries that would land at or past the row's end are not written.
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
 
@@ -46,12 +52,65 @@ struct SelArgs {
   int32_t* idx;
   int32_t* head_offsets;
   uint8_t* stage;
-  uint32_t seg_len, n_cand, groups, W, n;
+  const int32_t* budgets;   // [L][H] or null
+  uint32_t seg_len, n_cand, groups, W, n, H;
   uint32_t k, k1;
-  int64_t budget;
+  int64_t budget, stride;
   int two_stage;
-  float score_norm, eps;
+  float score_norm, eps, alpha;
 };
+
+// What segment `seg` selects and where it writes. Without a budget vector:
+// the call's k, k1 and budget, at seg * budget. With one (a segment is a
+// head): the head's clamped budget b, k = b - W, k1 = floor(alpha k) in
+// double (as the host computes it), packed after the layer's earlier heads.
+struct SegSpan {
+  uint32_t k, k1;     // k1 = 0xFFFFFFFF: single stage
+  int64_t base;       // first output entry of the segment
+  int64_t room;       // entries it may write (its budget, cut at the row's end)
+  int64_t off, end;   // budget vector: [off, end) in the layer row, clipped to it
+};
+
+__device__ __forceinline__ int64_t clamp_budget(int32_t b, uint32_t W, uint32_t n) {
+  return b < (int32_t)W ? (int64_t)W : (b > (int32_t)n ? (int64_t)n : (int64_t)b);
+}
+
+template <class A>
+__device__ __forceinline__ SegSpan seg_span(const A& a, size_t seg) {
+  SegSpan s;
+  if (!a.budgets) {
+    s.k = a.k;
+    s.k1 = a.k1;
+    s.base = (int64_t)seg * a.budget;
+    s.room = a.budget;
+    s.off = 0;
+    s.end = a.budget;
+    return s;
+  }
+  const size_t l = seg / a.H;
+  const uint32_t h = (uint32_t)(seg - l * a.H);
+  const int32_t* bl = a.budgets + l * a.H;
+  int64_t off = 0;
+  for (uint32_t j = 0; j < h; ++j) off += clamp_budget(bl[j], a.W, a.n);
+  const int64_t b = clamp_budget(bl[h], a.W, a.n);
+  s.k = (uint32_t)(b - a.W);
+  s.k1 = a.weight ? (uint32_t)floor((double)a.alpha * (double)s.k) : 0xFFFFFFFFu;
+  s.off = min(off, a.stride);
+  s.end = min(off + b, a.stride);
+  s.base = (int64_t)l * a.stride + s.off;
+  s.room = s.end - s.off;
+  return s;
+}
+
+// Budget vector: the layer row past the last head is filled with -1 (a
+// stage byte of 0) by the last head's segment.
+__device__ __forceinline__ void fill_row_tail(int32_t* idx, uint8_t* stage, int64_t row0,
+                                              int64_t from, int64_t stride, int tid, int nthreads) {
+  for (int64_t o = from + tid; o < stride; o += nthreads) {
+    idx[row0 + o] = -1;
+    if (stage) stage[row0 + o] = 0;
+  }
+}
 
 struct alignas(16) SelShared {   // a multiple of 16 bytes: the keys follow it
   uint32_t hist[kBins];
@@ -206,6 +265,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   const float* sc = a.scores + seg * a.seg_len;
   const float* wt = a.weight ? a.weight + seg * a.seg_len : nullptr;
   const uint32_t len = a.seg_len;
+  const SegSpan sp = seg_span(a, seg);
 
   // every load of a sweep in flight at once (one wait per sweep)
   if ((len & 3u) == 0) {
@@ -247,7 +307,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   // stage 1 (two-stage only), all the way down: stage-1 membership stays a
   // test on the key, which stage 2 turns into +inf
   if (a.two_stage) {
-    const SelCut c1 = radix_select(sm, keys, len, a.k1, 0);
+    const SelCut c1 = radix_select(sm, keys, len, sp.k1, 0);
     for (uint32_t base = 0; base < len; base += kLoadUnroll * kSelThreads) {
       float sv[kLoadUnroll], wv[kLoadUnroll];
 #pragma unroll
@@ -267,7 +327,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
     __syncthreads();
   }
 
-  const SelCut cf = radix_select(sm, keys, len, a.k, 31);
+  const SelCut cf = radix_select(sm, keys, len, sp.k, 31);
 
   // ---- emission, in index order. Thread t owns the `per` consecutive
   // candidates from t*per (per odd, so the LDS reads of a wave fall in
@@ -327,7 +387,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
           const uint32_t f = f0 + j;
           const uint32_t pos = f - (f >= next ? next : gstart);
           const bool second = a.two_stage && !((imask >> j) & 1u);
-          if (r < a.k) staged[r] = pos | (second ? 0x80000000u : 0u);   // r < k always
+          if (r < sp.k) staged[r] = pos | (second ? 0x80000000u : 0u);   // r < k always
           ++r;
         }
       }
@@ -338,16 +398,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
         const uint32_t f = f0 + j;
         while (f >= gs + a.n_cand) gs += a.n_cand;
         const bool second = a.two_stage && !((imask >> j) & 1u);
-        if (rank < a.k) staged[rank] = (f - gs) | (second ? 0x80000000u : 0u);   // rank < k always
+        if (rank < sp.k) staged[rank] = (f - gs) | (second ? 0x80000000u : 0u);   // rank < k always
       }
     }
   }
   lds_barrier();
   // output slot o: group g's members then its W window entries, groups in
   // order (slot of group g's first member: group_start[g] + g*W)
-  int32_t* out = a.idx + seg * (size_t)a.budget;
-  uint8_t* st_out = a.stage ? a.stage + seg * (size_t)a.budget : nullptr;
-  for (uint32_t o = tid; o < a.budget; o += kSelThreads) {
+  int32_t* out = a.idx + sp.base;
+  uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
+  for (uint32_t o = tid; o < sp.room; o += kSelThreads) {
     uint32_t g = 0;
     if (a.groups > 1) {   // last group whose first slot is <= o
       uint32_t lo = 0, hi = a.groups - 1;
@@ -358,7 +418,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
       g = lo;
     }
     const uint32_t first = sm.group_start[g];
-    const uint32_t count = (g + 1 < a.groups ? sm.group_start[g + 1] : a.k) - first;
+    const uint32_t count = (g + 1 < a.groups ? sm.group_start[g + 1] : sp.k) - first;
     const uint32_t local = o - (first + g * a.W);
     int32_t v;
     uint8_t sv;
@@ -372,6 +432,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
     }
     out[o] = v;
     if (st_out) st_out[o] = sv;
+  }
+  if (a.budgets) {
+    const size_t l = seg / a.H;
+    const uint32_t h = (uint32_t)(seg - l * a.H);
+    if (tid == 0) a.head_offsets[l * (a.H + 1) + h] = (int32_t)sp.off;
+    if (h + 1 == a.H) {
+      if (tid == 0) a.head_offsets[l * (a.H + 1) + a.H] = (int32_t)sp.end;
+      fill_row_tail(a.idx, a.stage, (int64_t)l * a.stride, sp.end, a.stride, tid, kSelThreads);
+    }
+    return;
   }
   if (a.head_offsets && tid < (int)a.groups)
     a.head_offsets[seg * (a.groups + 1) + tid] = (int32_t)(sm.group_start[tid] + tid * a.W);
@@ -424,10 +494,11 @@ struct MselArgs {
   int32_t* idx;
   int32_t* head_offsets;
   uint8_t* stage;
-  uint32_t seg_len, n_cand, groups, W, n, cpg, chunks;
+  const int32_t* budgets;   // [L][H] or null
+  uint32_t seg_len, n_cand, groups, W, n, cpg, chunks, H;
   uint32_t k, k1;
-  int64_t budget;
-  float score_norm, eps;
+  int64_t budget, stride;
+  float score_norm, eps, alpha;
 };
 
 // Key bits of candidate f for the stage being selected (stage 2 of the
@@ -463,7 +534,8 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int segment
     st.p1 = 1;          // no stage-1 members when single-stage
     st.s1 = 62;
   }
-  const uint32_t k = (stage2 || a.k1 == 0xFFFFFFFFu) ? a.k : a.k1;
+  const SegSpan sp = seg_span(a, (size_t)seg);
+  const uint32_t k = (stage2 || sp.k1 == 0xFFFFFFFFu) ? sp.k : sp.k1;
   st.shift = 62;
   if (k == 0) {          // nothing: (key >> 62) >= 1 holds for no key
     st.prefix = 1;
@@ -681,20 +753,31 @@ __global__ __launch_bounds__(kMThreads) void k_msel_offsets(MselArgs a) {
     run_mem += tot_mem;
   }
   __syncthreads();
-  int32_t* out = a.idx + (size_t)seg * (size_t)a.budget;
-  uint8_t* st_out = a.stage ? a.stage + (size_t)seg * (size_t)a.budget : nullptr;
+  const SegSpan sp = seg_span(a, (size_t)seg);
+  int32_t* out = a.idx + sp.base;
+  uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
   for (uint32_t g = 0; g < a.groups; ++g) {
-    const uint32_t end_rank = (g + 1 < a.groups) ? gstart[g + 1] : a.k;
+    const uint32_t end_rank = (g + 1 < a.groups) ? gstart[g + 1] : sp.k;
     const int64_t end = (int64_t)end_rank + (int64_t)(g + 1) * a.W;
     for (uint32_t t = tid; t < a.W; t += kMThreads) {
       const int64_t o = end - a.W + t;
-      if (o >= 0 && o < a.budget) {
+      if (o >= 0 && o < sp.room) {
         out[o] = (int32_t)(a.n - a.W + t);
         if (st_out) st_out[o] = 0;
       }
     }
-    if (a.head_offsets && tid == 0)
+    if (a.head_offsets && !a.budgets && tid == 0)
       a.head_offsets[(size_t)seg * (a.groups + 1) + g] = (int32_t)(gstart[g] + g * a.W);
+  }
+  if (a.budgets) {
+    const size_t l = seg / a.H;
+    const uint32_t h = (uint32_t)(seg - l * a.H);
+    if (tid == 0) a.head_offsets[l * (a.H + 1) + h] = (int32_t)sp.off;
+    if (h + 1 == a.H) {
+      if (tid == 0) a.head_offsets[l * (a.H + 1) + a.H] = (int32_t)sp.end;
+      fill_row_tail(a.idx, a.stage, (int64_t)l * a.stride, sp.end, a.stride, tid, kMThreads);
+    }
+    return;
   }
   if (a.head_offsets && tid == 0)
     a.head_offsets[(size_t)seg * (a.groups + 1) + a.groups] = (int32_t)a.budget;
@@ -753,13 +836,14 @@ __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2)
     }
   }
   uint32_t rank = cc[0] + block_scan256((uint32_t)__popc(mmask), sbuf, tot);
-  int32_t* out = a.idx + (size_t)seg * (size_t)a.budget;
-  uint8_t* st_out = a.stage ? a.stage + (size_t)seg * (size_t)a.budget : nullptr;
+  const SegSpan sp = seg_span(a, (size_t)seg);
+  int32_t* out = a.idx + sp.base;
+  uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
   const uint32_t pos0 = begin - g * a.n_cand;
   for (int j = 0; j < kPerThread; ++j) {
     if (mmask & (1u << j)) {
       const int64_t o = (int64_t)rank + (int64_t)g * a.W;
-      if (o < a.budget) {   // exactly k members: always true; never write past the segment
+      if (o < sp.room) {   // k members fit the budget; the room may be cut at the row's end
         out[o] = (int32_t)(pos0 + tid * kPerThread + j);
         if (st_out) st_out[o] = (!stage2 || bits[emit_slot(tid * kPerThread + j)] == kInfBits) ? 1 : 2;
       }
@@ -815,6 +899,11 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   a.budget = p.budget;
   a.score_norm = p.score_norm;
   a.eps = p.eps;
+  a.budgets = p.budgets;
+  a.H = (uint32_t)p.H;
+  a.stride = p.stride;
+  a.alpha = p.alpha;
+  if (p.budgets) a.head_offsets = head_offsets;
   const long long blocks = (long long)m.chunks * p.segments;
   if (blocks > 0x7fffffffLL || p.segments > 0x7fffffff) return hipErrorInvalidConfiguration;
   // the global histograms start cleared (a kernel, not a memset, so the
@@ -863,6 +952,11 @@ hipError_t select_launch(const SelectPlan& p, const float* scores, const float* 
   a.two_stage = p.two_stage ? 1 : 0;
   a.score_norm = p.score_norm;
   a.eps = p.eps;
+  a.budgets = p.budgets;
+  a.H = (uint32_t)p.H;
+  a.stride = p.stride;
+  a.alpha = p.alpha;
+  if (p.budgets) a.head_offsets = head_offsets;
   if (use_multi(p)) return msel_launch(p, scores, weight, idx, head_offsets, stage, ws, st);
   const size_t lds = lds_bytes(a.seg_len);
   const hipError_t e =

@@ -20,8 +20,8 @@
  *    synchronised. No call allocates device memory or synchronises.
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
- *  - Workspace protocol (kvsel_score, kvsel_select, kvsel_decode_attention):
- *    with ws == NULL the
+ *  - Workspace protocol (kvsel_score, kvsel_select, kvsel_select_budgets,
+ *    kvsel_decode_attention): with ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
  *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
  *    Workspace contents need no initialisation and are scratch afterwards.
@@ -209,6 +209,45 @@ int32_t kvsel_select(const float* scores, const float* weight,
                      void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * kvsel_select_budgets -- per-head selection under a budget vector.
+ *
+ * [CriticalKV] §4.1 combines the method with HeadKV, whose offline budget
+ * allocation gives every head of every layer its own budget. Head h of
+ * layer l keeps b = budgets[l][h] entries, its W window positions included;
+ * b is clamped into [W, n]. Among its candidates [0, n-W) it keeps the
+ * k = b - W largest keys exactly as kvsel_select does per head (equal keys
+ * to the lower index; two-stage when weight != NULL, with
+ * k1 = floor(alpha*k) computed in double).
+ *
+ *   scores       f32 [L][H_kv][n-W]
+ *   weight       f32 [L][H_kv][n-W]    optional
+ *   budgets      i32 [L][H_kv]         DEVICE memory, read by the kernels
+ *   idx          i32 [L][layer_stride] out: the layer's heads packed in
+ *                order, each as its kept candidates ascending then
+ *                n-W..n-1; entries past the last head hold -1
+ *   head_offsets i32 [L][H_kv+1]       out: head h owns idx[l][head_offsets
+ *                [l][h] .. head_offsets[l][h+1])
+ *   stage        u8 [L][layer_stride]  optional, as for kvsel_select
+ *                (0 also past the last head)
+ *
+ * layer_stride should be at least the largest per-layer sum of the clamped
+ * budgets. If a layer's sum is larger, nothing is written past its row:
+ * its head offsets are clipped to layer_stride and the heads that cross it
+ * lose their trailing entries (a truncated selection for those heads).
+ * The idx rows, the head offsets and kvsel_compact / kvsel_decode_attention
+ * then use kept_per_layer = layer_stride.
+ *
+ * Ranges: 0 <= W < n; 1 <= layer_stride <= H_kv*n; alpha, score_norm and
+ * eps as for kvsel_select. Needs a workspace (protocol above).
+ */
+int32_t kvsel_select_budgets(const float* scores, const float* weight,
+                             int32_t L, int32_t H_kv, int32_t n, int32_t W,
+                             const int32_t* budgets, int64_t layer_stride,
+                             float score_norm, float eps, float alpha,
+                             int32_t* idx, int32_t* head_offsets, uint8_t* stage,
+                             void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * kvsel_compact -- gather the kept rows of K and V.
  *
  * Eviction acts on the un-replicated cache ([KVzip] §4.2): kept row t of
@@ -222,7 +261,10 @@ int32_t kvsel_select(const float* scores, const float* weight,
  *   k_out, v_out bf16 [L][kept_per_layer][d]  (uniform: = [L][H_kv][B][d])
  *
  * Every idx entry must lie in [0, n); out-of-range entries are not read
- * (their rows are written as zeros). d % 8 == 0.
+ * (their rows are written as zeros). With head_offsets, only the rows
+ * before head_offsets[l][H_kv] (clamped into [0, kept_per_layer]) are
+ * written; a layer's later rows (the unused end of a kvsel_select_budgets
+ * row) are left as they were. d % 8 == 0.
  */
 int32_t kvsel_compact(const void* k, const void* v,
                       int32_t L, int32_t H_kv, int32_t d, int32_t n,

@@ -66,6 +66,7 @@ class Workload:
     pool: int = 7
     beta: float = 0.2            # kept fraction (window included)
     adaptive: bool = False       # one budget per layer shared by all heads
+    budget_vector: bool = False  # one budget per (layer, head), from gen_budgets
     value_weight: bool = False   # value-norm weighted two-stage selection
     value_norm: str = "l1"       # norm of the projected value: 'l1' or 'l2'
     D: int = 0                   # model width for w_o
@@ -125,6 +126,10 @@ WORKLOADS = {
         # budget per layer (the flattened candidates of its heads), n = 32K, 20%
         Workload("criticaladakv_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768,
                  W=32, pool=7, beta=0.20, adaptive=True, value_weight=True, D=4096),
+        # per-(layer, head) budgets averaging 20% (a HeadKV-style offline
+        # allocation), n = 32K
+        Workload("headkv_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=32,
+                 pool=7, beta=0.20, budget_vector=True),
         # H2O-style accumulated attention: window scoring with W = 256, 20%
         Workload("h2o_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=256,
                  pool=7, beta=0.20),
@@ -135,7 +140,7 @@ WORKLOADS = {
     ]
 }
 
-_TENSOR = {"q": 1, "k": 2, "v": 3, "w_o": 4, "heavy": 5}
+_TENSOR = {"q": 1, "k": 2, "v": 3, "w_o": 4, "heavy": 5, "budgets": 6}
 
 
 def _rng(seed: int, wl: Workload, tensor: str, layer: int) -> np.random.Generator:
@@ -188,6 +193,20 @@ def gen_w_o(wl: Workload, seed: int, layer: int) -> np.ndarray:
     x = r.standard_normal((wl.D, wl.H_q * wl.d), dtype=np.float32)
     x *= np.float32(0.02)
     return bf16_bits(x)
+
+
+def gen_budgets(wl: Workload, seed: int) -> np.ndarray:
+    """Per-(layer, head) budgets [L][H_kv] int32 for a budget-vector workload.
+
+    A stand-in for an offline allocation: every head draws a log-normal
+    importance (sigma 0.75), and the candidate budget of all heads together,
+    L*H_kv*(floor(beta*n) - W), is shared in proportion to it. Each budget
+    counts its W window entries and is capped at n."""
+    r = _rng(seed, wl, "budgets", 0)
+    imp = r.lognormal(0.0, 0.75, size=(wl.L, wl.H_kv))
+    pool = wl.L * wl.H_kv * (int(np.floor(wl.beta * wl.n)) - wl.W_kept)
+    b = wl.W_kept + np.floor(imp / imp.sum() * pool)
+    return np.minimum(b, wl.n).astype(np.int32)
 
 
 def gen_layer(wl: Workload, seed: int, layer: int, which=("q", "k", "v", "w_o")) -> dict:

@@ -222,3 +222,53 @@ def test_value_weight_l2_pointers(lib):
     assert f(p, None, 2, 8, 4, 128, 100, 68, p, None) == ARG
     assert f(p, p, 2, 8, 4, 128, 100, 68, None, None) == ARG
     assert f(p, ctypes.c_void_p((1 << 20) + 8), 2, 8, 4, 128, 100, 68, p, None) == ARG
+
+
+def _sel_budgets(lib, weight=False, **kw):
+    a = dict(L=2, H=8, n=1000, W=32, stride=4000, alpha=0.5, norm=0.01, eps=1e-4)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    w = ctypes.c_void_p(1 << 20) if weight else None
+    return lib.kvsel_select_budgets(None, w, a["L"], a["H"], a["n"], a["W"], None, a["stride"],
+                                    a["norm"], a["eps"], a["alpha"], None, None, None, None,
+                                    ctypes.byref(nb), None), nb.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(W=0), OK), (dict(stride=1), OK), (dict(stride=8000), OK),
+    (dict(n=50000), OK), (dict(L=0), ARG), (dict(H=0), ARG), (dict(W=1000), ARG),
+    (dict(W=-1), ARG), (dict(stride=0), ARG), (dict(stride=8001), ARG),
+    (dict(H=1 << 16, n=1 << 16, stride=5), UNSUP),
+])
+def test_select_budgets_ranges(lib, kw, code):
+    assert _sel_budgets(lib, **kw)[0] == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(alpha=-0.1), ARG), (dict(alpha=1.5), ARG), (dict(norm=0.0), ARG),
+    (dict(eps=-1.0), ARG), (dict(alpha=1.0), OK),
+])
+def test_select_budgets_two_stage_ranges(lib, kw, code):
+    assert _sel_budgets(lib, weight=True, **kw)[0] == code
+
+
+def test_select_budgets_workspace_like_select(lib):
+    # the same segments as the per-head select: the same workspace
+    rc, nb = _sel_budgets(lib, n=50000, W=32)
+    nb2 = ctypes.c_size_t(0)
+    rc2 = lib.kvsel_select(None, None, 2, 8, 50000, 32, 5000, 0, 1.0, 1e-4, 0.5, None, None, None,
+                           None, ctypes.byref(nb2), None)
+    assert rc == OK and rc2 == OK and nb == nb2.value > 0
+
+
+@no_gpu_only
+def test_select_budgets_pointers(lib):
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.kvsel_select_budgets
+    nb = ctypes.c_size_t(1 << 20)
+    args = lambda sc, bud, idx, offs: (sc, None, 2, 8, 1000, 32, bud, 4000, 0.01, 1e-4, 0.5, idx,
+                                       offs, None, p, ctypes.byref(nb), None)
+    assert f(*args(None, p, p, p)) == ARG
+    assert f(*args(p, None, p, p)) == ARG
+    assert f(*args(p, p, None, p)) == ARG
+    assert f(*args(p, p, p, None)) == ARG

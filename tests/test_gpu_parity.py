@@ -187,6 +187,94 @@ def test_select_exact_on_same_fp32_scores(case):
             np.testing.assert_array_equal(offs[l], ro)
 
 
+BUDGET_CASES = [
+    # (L, H, n, W, two_stage, alpha, levels, stride_extra)
+    (2, 4, 300, 8, False, 0.5, 7, 0),
+    (2, 3, 1000, 32, True, 0.5, 30, 0),
+    (1, 8, 64, 32, False, 0.5, 3, 17),          # budgets W .. n, a padded row
+    (3, 2, 2500, 16, True, 1.0, 1000000, 5),
+    (1, 4, 50000, 32, False, 0.5, 1000, 0),     # longer than LDS: many workgroups per head
+    (1, 2, 40000, 16, True, 0.5, 100, 3),       # many workgroups, two-stage
+    (2, 4, 600, 8, False, 0.5, 5, -40),         # rows shorter than layer 0's budgets: truncated
+]
+
+
+@pytest.mark.parametrize("case", BUDGET_CASES, ids=lambda c: "L{}H{}n{}W{}t{}al{}lv{}s{}".format(*c))
+def test_select_budgets_exact(case):
+    L, H, n, W, two_stage, alpha, levels, extra = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    n_cand = n - W
+    sc = _quantised_scores(rng, (L, H, n_cand), levels)
+    wt = (rng.random((L, H, n_cand)).astype(np.float32) * 3 + 0.01) if two_stage else None
+    budgets = rng.integers(W - 3, n + 4, size=(L, H)).astype(np.int32)   # some outside [W, n]
+    budgets[0, 0] = W                                                      # window only
+    if extra < 0:
+        budgets[0] = n                      # layer 0 needs H*n entries
+        budgets[1:] = W + 3
+    sums = np.clip(budgets, W, n).astype(np.int64).sum(axis=1)
+    stride = int(sums.max()) + extra
+    print(f"[gpu] kvsel_select_budgets case={case} stride={stride}", flush=True)
+    idx, offs, stage = kv.kvsel_select_budgets(
+        torch.from_numpy(sc).cuda(), torch.from_numpy(budgets).cuda(), n=n, W=W,
+        layer_stride=stride, weight=None if wt is None else torch.from_numpy(wt).cuda(),
+        score_norm=1.0 / 128, eps=1e-4, alpha=alpha, return_stage=True)
+    torch.cuda.synchronize()
+    idx, offs, stage = idx.cpu().numpy(), offs.cpu().numpy(), stage.cpu().numpy()
+    assert idx.shape == (L, stride)
+    for l in range(L):
+        ri, ro, rs = oracle.select_budgets(sc[l].astype(np.float64), budgets[l], W, n,
+                                           weight=None if wt is None else wt[l].astype(np.float64),
+                                           alpha=float(np.float32(alpha)),
+                                           score_norm=float(np.float32(1 / 128)),
+                                           eps=float(np.float32(1e-4)), dtype=np.float32)
+        m = min(len(ri), stride)
+        np.testing.assert_array_equal(offs[l], np.minimum(ro, stride))
+        np.testing.assert_array_equal(idx[l, :m], ri[:m])
+        np.testing.assert_array_equal(stage[l, :m], rs[:m])
+        assert (idx[l, m:] == -1).all() and (stage[l, m:] == 0).all()
+
+
+def test_select_budgets_feed_compact_and_decode():
+    """Budget-vector output in the packed layout drives compaction and decode."""
+    rng = np.random.default_rng(12)
+    L, H, G, n, W = 2, 4, 2, 700, 16
+    sc = rng.random((L, H, n - W)).astype(np.float32)
+    budgets = np.array([[16, 100, 700, 40], [300, 16, 17, 5]], np.int32)
+    idx, offs, _ = kv.kvsel_select_budgets(torch.from_numpy(sc).cuda(),
+                                           torch.from_numpy(budgets).cuda(), n=n, W=W,
+                                           layer_stride=900)
+    k = synth.bf16_bits(rng.standard_normal((L, H, n, 128)).astype(np.float32))
+    v = synth.bf16_bits(rng.standard_normal((L, H, n, 128)).astype(np.float32))
+    ko, vo = kv.kvsel_compact(to_dev(k), to_dev(v), idx, offs)
+    torch.cuda.synchronize()
+    idx_h, offs_h = idx.cpu().numpy(), offs.cpu().numpy()
+    ko_h = ko.cpu().view(torch.int16).numpy().view(np.uint16)
+    vo_h = vo.cpu().view(torch.int16).numpy().view(np.uint16)
+    for l in range(L):
+        end = offs_h[l, -1]
+        rk, rv = oracle.compact_layer(k[l], v[l], idx_h[l, :end], offs_h[l])
+        np.testing.assert_array_equal(ko_h[l, :end], rk)
+        np.testing.assert_array_equal(vo_h[l, :end], rv)
+    # rows past each layer's last head are left as they were
+    fill = torch.full((L, 900, 128), 1.5, dtype=torch.bfloat16, device="cuda")
+    ko2, vo2 = kv.kvsel_compact(to_dev(k), to_dev(v), idx, offs, k_out=fill.clone(), v_out=fill.clone())
+    torch.cuda.synchronize()
+    for l in range(L):
+        end = offs_h[l, -1]
+        assert torch.equal(ko2[l, :end], ko[l, :end]) and torch.equal(vo2[l, :end], vo[l, :end])
+        assert (ko2[l, end:] == 1.5).all() and (vo2[l, end:] == 1.5).all()
+    qb = synth.bf16_bits(rng.standard_normal((L, H * G, 128)).astype(np.float32))
+    out = kv.kvsel_decode_attention(to_dev(qb), ko, vo, G=G, scale=0.088, head_offsets=offs)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for l in range(L):
+        end = offs_h[l, -1]   # rows past it were never written
+        vl = synth.bf16_to_f64(vo_h[l, :end])
+        ref = oracle.decode_attention(synth.bf16_to_f64(qb[l]), synth.bf16_to_f64(ko_h[l, :end]), vl,
+                                      G, 0.088, head_offsets=offs_h[l])
+        np.testing.assert_allclose(out[l], ref, rtol=1e-4, atol=1e-4 * np.abs(vl).max())
+
+
 def test_select_end_to_end_band():
     """GPU scores + GPU select against the fp64 oracle's selection."""
     wl = _wl(L=2, H_kv=2, n=3000, W=32)

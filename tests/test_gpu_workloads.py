@@ -109,8 +109,9 @@ def _check_decode(wl, ko, vo, offs, l):
         ref = oracle.decode_attention(synth.bf16_to_f64(qd[l]), k_l.reshape(wl.H_kv, -1, wl.d),
                                       v_l.reshape(wl.H_kv, -1, wl.d), wl.G, wl.scale)
     else:
-        ref = oracle.decode_attention(synth.bf16_to_f64(qd[l]), k_l, v_l, wl.G, wl.scale,
-                                      offs[l].cpu().numpy())
+        o = offs[l].cpu().numpy()
+        k_l, v_l = k_l[:o[-1]], v_l[:o[-1]]   # rows past the last head are not written
+        ref = oracle.decode_attention(synth.bf16_to_f64(qd[l]), k_l, v_l, wl.G, wl.scale, o)
     got = out[l].cpu().numpy()
     bad = np.abs(got - ref) > 1e-4 * np.abs(v_l).max() + 1e-4 * np.abs(ref)
     assert not bad.any(), f"decode layer {l}: {bad.sum()} entries off, max err {np.abs(got - ref).max():.3g}"
@@ -156,6 +157,47 @@ def test_window_workload_full(name):
         for h in range(wl.H_kv):
             assert_topk_within_band(picks[h], ref_pool[h], wl.budget - wl.W, f"h{h}")
     _check_compact(dev, host, idx, offs, 0, wl)
+
+
+def test_headkv_budget_vector_full():
+    wl = synth.WORKLOADS["headkv_llama8b_n32k"]
+    sampled = [0, wl.L - 1]
+    dev, host = device_inputs(wl, set(sampled), ("q", "k", "v"))
+    s, r = _score(wl, dev)
+    _check_scores(wl, s, r, host, [0])
+    budgets = synth.gen_budgets(wl, SEED)
+    print("[gpu] kvsel_select_budgets full", flush=True)
+    idx, offs, stage = kv.kvsel_select_budgets(s, torch.from_numpy(budgets).cuda(), n=wl.n,
+                                               W=wl.W, return_stage=True)
+    torch.cuda.synchronize()
+    eff = np.clip(budgets, wl.W, wl.n).astype(np.int64)
+    assert idx.shape[1] == eff.sum(axis=1).max()
+    for l in sampled:
+        ri, ro, rs = oracle.select_budgets(s[l].cpu().numpy().astype(np.float64), budgets[l], wl.W,
+                                           wl.n, dtype=np.float32)
+        m = len(ri)
+        np.testing.assert_array_equal(offs[l].cpu().numpy(), ro)
+        np.testing.assert_array_equal(idx[l, :m].cpu().numpy(), ri)
+        np.testing.assert_array_equal(stage[l, :m].cpu().numpy(), rs)
+        assert (idx[l, m:].cpu().numpy() == -1).all()
+    # end-to-end band check on layer 0 against the fp64 oracle
+    _, ref_pool = oracle_scores_layer(wl, host[("q", 0)], host[("k", 0)])
+    o = offs[0].cpu().numpy()
+    picks = split_heads(idx[0].cpu().numpy(), o, wl.H_kv, wl.W, wl.n)
+    for h in range(wl.H_kv):
+        assert_topk_within_band(picks[h], ref_pool[h], int(eff[0, h]) - wl.W, f"h{h}")
+    # compaction of layer 0 (rows past the last head are not written), then decode
+    ko, vo = kv.kvsel_compact(dev["k"], dev["v"], idx, offs)
+    torch.cuda.synchronize()
+    end = int(o[-1])
+    k_l = dev["k"][0].cpu().view(torch.int16).numpy().view(np.uint16)
+    v_l = dev["v"][0].cpu().view(torch.int16).numpy().view(np.uint16)
+    rk, rv = oracle.compact_layer(k_l, v_l, idx[0, :end].cpu().numpy(), o)
+    ko0 = ko[0].cpu().view(torch.int16).numpy().view(np.uint16)
+    vo0 = vo[0].cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ko0[:end], rk)
+    np.testing.assert_array_equal(vo0[:end], rv)
+    _check_decode(wl, ko, vo, offs, 0)
 
 
 @pytest.mark.parametrize("name", ["criticalkv_llama8b_n128k", "criticaladakv_llama8b_n32k",
