@@ -114,6 +114,57 @@ def external_raw_scores(q: np.ndarray, k: np.ndarray, G: int, scale: float,
     return raw
 
 
+def external_logit_scores(q: np.ndarray, k: np.ndarray, G: int, scale: float) -> np.ndarray:
+    """The softmax-free scores of KVzip-logit.
+
+    [KVzip, §6.5]: the variant drops the softmax normalisation and scores a
+    cached key by the raw attention logits it receives, aggregated like the
+    softmax scores of §3.2 (max over the group queries and input positions).
+    Reading: the logit is the model's scaled one, scale * <q, k> (the scale
+    is common to every head, so it changes no ordering); scores may be
+    negative.
+
+    q: [H_kv*G][Q_s][d], k: [H_kv][n][d]. Returns [H_kv][n].
+    """
+    H, n, d = k.shape
+    assert q.shape[0] == H * G
+    out = np.full((H, n), -np.inf)
+    for h in range(H):
+        for g in range(G):
+            lg = scale * (q[h * G + g] @ k[h].T)    # [Q_s][n] logits
+            out[h] = np.maximum(out[h], lg.max(axis=0))
+    return out
+
+
+def head_scores(scores: np.ndarray) -> np.ndarray:
+    """Head-level importance.
+
+    [KVzip, §3.4 and §3.6]: the score of a head is the maximum of its
+    per-position scores over the sequence, S_head = max_i S[:, :, i].
+    scores: [..., n_pos]. Returns scores.shape[:-1].
+    """
+    return scores.max(axis=-1)
+
+
+def head_budgets(head_score: np.ndarray, keep: int, n: int, W: int) -> np.ndarray:
+    """Budgets of head-level eviction.
+
+    [KVzip, §3.6 and §5.4]: context-independent eviction keeps or drops
+    whole heads by their head score, in DuoAttention's structure, where the
+    heads not kept hold only a recent window. Readings: `keep` heads with
+    the largest score over all layers and heads keep all n entries (ties to
+    the lower flat (layer, head) index); the others keep the last W entries.
+
+    head_score: [L][H]. Returns budgets [L][H] (n or W), the input of the
+    per-head budget selection.
+    """
+    flat = head_score.reshape(-1)
+    top = topk_indices(flat, keep)
+    b = np.full(flat.shape, W, np.int64)
+    b[top] = n
+    return b.reshape(head_score.shape)
+
+
 def maxpool(raw: np.ndarray, n_cand: int, pool: int) -> np.ndarray:
     """[CriticalKV, §3.3 Algorithm 2, step 4] (SnapKV's max-pooling, kernel 7
     in [CriticalKV, §4.1]). Reading: stride 1, centred, over candidate

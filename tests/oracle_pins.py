@@ -198,6 +198,61 @@ def check_external(o):
     assert (big <= 1 + 1e-15).all() and (big.max(axis=1) >= 1 / 300).all()
 
 
+def check_external_logit(o):
+    g = load_golden("logit_head_example.txt")
+    qv = g["logit.q"]
+    q = _embed_1d(qv).reshape(2, 2, 4)            # query heads of one KV head, 2 queries each
+    k = _embed_1d(g["logit.k"])[None]
+    sc = g["logit.scale"][0]
+    np.testing.assert_allclose(o.external_logit_scores(q, k, 2, sc)[0], g["logit.scores"], rtol=1e-15)
+    q1 = _embed_1d([-1.0])[None]
+    np.testing.assert_allclose(o.external_logit_scores(q1, k, 1, sc)[0], g["logit.one_query_scores"],
+                               rtol=1e-15)
+    rng = np.random.default_rng(45)
+    # brute force with loops
+    H, G, Qs, n, d = 2, 3, 4, 7, 3
+    q = rng.standard_normal((H * G, Qs, d))
+    k = rng.standard_normal((H, n, d))
+    ref = np.full((H, n), -np.inf)
+    for hq in range(H * G):
+        for i in range(Qs):
+            for j in range(n):
+                x = 0.7 * sum(q[hq, i, e] * k[hq // G, j, e] for e in range(d))
+                ref[hq // G, j] = max(ref[hq // G, j], x)
+    got = o.external_logit_scores(q, k, G, 0.7)
+    np.testing.assert_allclose(got, ref, rtol=1e-13)
+    # a positive factor on the scale scales the max
+    np.testing.assert_allclose(o.external_logit_scores(q, k, G, 1.4), 2 * got, rtol=1e-13)
+    # one query: the same order as the softmax scores (softmax is monotonic
+    # along a row)
+    q1 = rng.standard_normal((1, 1, 16))
+    kk = rng.standard_normal((1, 200, 16))
+    a = o.external_logit_scores(q1, kk, 1, 0.25)[0]
+    b = o.external_raw_scores(q1, kk, 1, 0.25)[0]
+    np.testing.assert_array_equal(np.argsort(a), np.argsort(b))
+
+
+def check_head_scores_and_budgets(o):
+    g = load_golden("logit_head_example.txt")
+    sc = np.asarray(g["heads.scores"]).reshape(2, 3, 4)
+    hs = o.head_scores(sc)
+    np.testing.assert_array_equal(hs.reshape(-1), g["heads.head_scores"])
+    np.testing.assert_array_equal(o.head_budgets(hs, 3, 100, 8).reshape(-1), g["heads.budgets_keep3"])
+    np.testing.assert_array_equal(o.head_budgets(hs, 2, 100, 8).reshape(-1), g["heads.budgets_keep2"])
+    rng = np.random.default_rng(46)
+    for trial in range(10):
+        L, H, m = 3, 4, 9
+        sc = rng.integers(0, 4, size=(L, H, m)).astype(np.float64)
+        hs = o.head_scores(sc)
+        for l in range(L):
+            for h in range(H):
+                assert hs[l, h] == max(sc[l, h, i] for i in range(m))
+        keep = int(rng.integers(0, L * H + 1))
+        b = o.head_budgets(hs, keep, 50, 5)
+        assert set(np.unique(b)) <= {5, 50} and (b == 50).sum() == keep
+        _assert_topk_property(hs.reshape(-1), list(np.nonzero(b.reshape(-1) == 50)[0]), keep)
+
+
 # ---------------------------------------------------------------- pool ----
 
 def check_maxpool(o):
@@ -576,5 +631,5 @@ ALL_CHECKS = [
     check_select_bruteforce, check_select_reductions, check_compact,
     check_decode_hand_example, check_decode_bruteforce, check_decode_sdpa, check_decode_closed_forms,
     check_value_weight_l2, check_select_budgets_example, check_select_budgets_bruteforce,
-    check_select_budgets_reductions,
+    check_select_budgets_reductions, check_external_logit, check_head_scores_and_budgets,
 ]

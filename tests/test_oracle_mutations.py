@@ -53,6 +53,13 @@ MUTANTS = {
     "budgets_window_not_counted": ("        k = int(b[h]) - W\n", "        k = max(int(b[h]) - 2 * W, 0)\n"),
     "budgets_head_shifted": ("        k = int(b[h]) - W\n", "        k = int(b[(h + 1) % H]) - W\n"),
     "budgets_offsets_no_window": ("offs.append(offs[-1] + k + W)", "offs.append(offs[-1] + k)"),
+    "logit_softmax": ("lg = scale * (q[h * G + g] @ k[h].T)    # [Q_s][n] logits",
+                      "lg = _softmax_rows(scale * (q[h * G + g] @ k[h].T))    # [Q_s][n] logits"),
+    "logit_no_scale": ("lg = scale * (q[h * G + g] @ k[h].T)    # [Q_s][n] logits", "lg = (q[h * G + g] @ k[h].T)    # [Q_s][n] logits"),
+    "logit_floor_zero": ("out = np.full((H, n), -np.inf)", "out = np.zeros((H, n))"),
+    "head_scores_mean": ("    return scores.max(axis=-1)", "    return scores.mean(axis=-1)"),
+    "head_budgets_ties_high": ("    top = topk_indices(flat, keep)", "    top = len(flat) - 1 - topk_indices(flat[::-1], keep)"),
+    "head_budgets_drop_all": ("    b = np.full(flat.shape, W, np.int64)", "    b = np.full(flat.shape, 0, np.int64)"),
     "compact_wrong_head": ("return (np.stack([k[h, idx[h]] for h in range(H)]),", "return (np.stack([k[0, idx[h]] for h in range(H)]),"),
 }
 
