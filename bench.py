@@ -83,7 +83,8 @@ def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
         if wl.q_mode == "window":
             raw = oracle.window_raw_scores(q, k, wl.G, wl.scale, wl.agg)
         else:
-            raw = oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg)
+            raw = (oracle.external_logit_scores(q, k, wl.G, wl.scale) if wl.agg == "logit"
+                   else oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg))
         pooled = oracle.maxpool(raw, wl.n_cand, wl.pool)
         weight = None
         if wl.value_weight and w_host is not None:
@@ -163,7 +164,7 @@ def main():
     q, k, v = t["q"], t["k"], t["v"]
     w_o = t.get("w_o")
     mode = kv.Q_WINDOW if wl.q_mode == "window" else kv.Q_EXTERNAL
-    agg = kv.AGG_SUM if wl.agg == "sum" else kv.AGG_MAX
+    agg = {"sum": kv.AGG_SUM, "max": kv.AGG_MAX, "logit": kv.AGG_LOGIT_MAX}[wl.agg]
     W_kept = wl.W_kept
     scores = torch.empty((wl.L, wl.H_kv, wl.n_cand), dtype=torch.float32, device=dev)
     weight = (torch.empty((wl.L, wl.H_kv, wl.n_cand), dtype=torch.float32, device=dev)
@@ -285,9 +286,11 @@ def main():
                  "kernel": "kvsel_score", "bytes_per_launch": score_bytes,
                  "ms_per_launch": ms_score, "source_sha": sha}
     calls = []
-    # two passes of Q K^T (R = G*W rows per KV head against n keys); the
-    # call is MFMA-bound when those flops take longer at peak than its bytes
-    sc_flops = 2 * 2.0 * wl.L * wl.H_q * wl.W * wl.n * wl.d
+    # two passes of Q K^T (R = G*W rows per KV head against n keys; one for
+    # the softmax-free logit max); the call is MFMA-bound when those flops
+    # take longer at peak than its bytes
+    passes = 1 if wl.agg == "logit" else 2
+    sc_flops = passes * 2.0 * wl.L * wl.H_q * wl.W * wl.n * wl.d
     if sc_flops / (MFMA_BF16_PEAK_TFS * 1e12) > score_bytes / (HBM_PEAK_GBS * 1e9):
         tfs = sc_flops / (ms_score * 1e-3) / 1e12
         calls.append((ms_score, {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,

@@ -20,11 +20,11 @@ __all__ = [
     "kvsel_value_l2_factor", "kvsel_value_weight_l2",
     "kvsel_select", "kvsel_select_budgets", "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
-    "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX",
+    "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX", "AGG_LOGIT_MAX",
 ]
 
 Q_WINDOW, Q_EXTERNAL = 0, 1
-AGG_SUM, AGG_MAX = 0, 1
+AGG_SUM, AGG_MAX, AGG_LOGIT_MAX = 0, 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libkvsel.so")

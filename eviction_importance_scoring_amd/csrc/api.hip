@@ -46,7 +46,9 @@ int32_t kvsel_score(const void* q, const void* k, int32_t L, int32_t H_kv, int32
   if (!ws_bytes) return KVSEL_ERR_ARG;
   if (L < 1 || H_kv < 1 || G < 1 || d < 1 || n < 1 || W < 1) return KVSEL_ERR_ARG;
   if (q_mode != KVSEL_Q_WINDOW && q_mode != KVSEL_Q_EXTERNAL) return KVSEL_ERR_ARG;
-  if (agg != KVSEL_AGG_SUM && agg != KVSEL_AGG_MAX) return KVSEL_ERR_ARG;
+  if (agg != KVSEL_AGG_SUM && agg != KVSEL_AGG_MAX && agg != KVSEL_AGG_LOGIT_MAX)
+    return KVSEL_ERR_ARG;
+  if (agg == KVSEL_AGG_LOGIT_MAX && q_mode != KVSEL_Q_EXTERNAL) return KVSEL_ERR_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return KVSEL_ERR_ARG;
   if (pool < 1 || pool % 2 == 0) return KVSEL_ERR_ARG;
   if (q_mode == KVSEL_Q_WINDOW && W >= n) return KVSEL_ERR_ARG;
@@ -63,7 +65,8 @@ int32_t kvsel_score(const void* q, const void* k, int32_t L, int32_t H_kv, int32
   p.causal = q_mode == KVSEL_Q_WINDOW;
   p.n_cand = p.causal ? n - W : n;
   p.pool = pool;
-  p.max_agg = agg == KVSEL_AGG_MAX;
+  p.max_agg = agg != KVSEL_AGG_SUM;
+  p.logit = agg == KVSEL_AGG_LOGIT_MAX;
   p.need_raw_tmp = raw == nullptr;
   p.scale = scale;
   const size_t need = score_ws_bytes(p);

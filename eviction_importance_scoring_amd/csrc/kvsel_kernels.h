@@ -18,6 +18,7 @@ struct ScorePlan {
   int pool;
   bool causal;            // window mode
   bool max_agg;
+  bool logit = false;     // max of the scaled logits, no softmax (external only)
   bool need_raw_tmp;      // caller passed raw == NULL
   float scale;
 };

@@ -9,6 +9,8 @@
 //                         x = log2(e) * scale * <q_r, k_j>; c_r = m_r + log2 l_r.
 //   pass 2  k_gen_colagg  per key j: sum_r 2^(x_rj - c_r), or 2^(max_r (x_rj - c_r)).
 //   pool    max over +-pool/2 neighbours inside the candidate range.
+// KVzip-logit ([KVzip] §6.5, no softmax): pass 2 alone, every c_r = 0 and
+// no exponential: per key j, scale * max_r <q_r, k_j>.
 // Both passes are dense Q K^T contractions on MFMA (32x32x16 bf16, fp32
 // accumulation) built for operand reuse:
 //   pass 1: a workgroup of 8 waves owns 512 rows (a wave: 64 rows, two MFMA
@@ -269,11 +271,20 @@ __global__ __launch_bounds__(256) void k_combine_neg(const float2* __restrict__ 
   stat[lh * Rpad + r] = -(m + __log2f(s)) * inv_alpha;
 }
 
+// KVzip-logit: no normaliser, so pass 2 starts every real row at 0 (and
+// padding rows at -inf).
+__global__ __launch_bounds__(256) void k_logit_stat(int R, int Rpad, float* __restrict__ stat) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= Rpad) return;
+  const size_t lh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  stat[lh * Rpad + r] = r < R ? 0.f : neg_inf();
+}
+
 // ---------------------------------------------------------------- pass 2 ----
 // 1-D grid of key_blocks * H * L workgroups, block 512. raw[lh][key].
 // Pipelined like pass 1: the MFMAs of row tile t run beside the aggregation
 // of tile t-1, so the matrix pipe does not wait for the per-tile max / sum.
-template <bool CAUSAL, bool MAXAGG>
+template <bool CAUSAL, bool MAXAGG, bool LOGIT = false>
 __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q,
                                                     const __bf16* __restrict__ k, int H, int R,
                                                     int W, int n, float alpha, int key_blocks,
@@ -429,7 +440,9 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float o = __shfl_xor(agg[nt], 32);
-    const float tot = MAXAGG ? fast_exp2(__builtin_fmaxf(agg[nt], o) * alpha) : agg[nt] + o;
+    // LOGIT: alpha is the plain scale and the max is the logit itself
+    const float tot = LOGIT ? __builtin_fmaxf(agg[nt], o) * alpha
+                    : MAXAGG ? fast_exp2(__builtin_fmaxf(agg[nt], o) * alpha) : agg[nt] + o;
     const int key = key0 + nt * 32 + col;
     if (hf == 0 && key < n) raw[lh * n + key] = tot;
   }
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(256) void k_pool(const float* __restrict__ raw, int
   const float* src = raw + lh * n;
   for (int t = threadIdx.x; t < 256 + 2 * r; t += 256) {
     const int j = j0 - r + t;
-    tile[t] = (j >= 0 && j < n_cand) ? src[j] : 0.f;  // scores are >= 0
+    tile[t] = (j >= 0 && j < n_cand) ? src[j] : neg_inf();  // outside the candidates: no part
   }
   __syncthreads();
   const int j = j0 + threadIdx.x;
@@ -491,7 +504,7 @@ void twopass_plan(const ScorePlan& p, TwoPassLayout* o) {
   const size_t LH = (size_t)p.L * p.H;
   o->part_off = 0;
   const size_t Rpad = (size_t)(p.R + gTile - 1) / gTile * gTile;
-  o->stat_off = align256(LH * splits * p.R * sizeof(float2));
+  o->stat_off = p.logit ? 0 : align256(LH * splits * p.R * sizeof(float2));   // no pass 1
   o->raw_off = o->stat_off + align256(LH * Rpad * sizeof(float));
   o->bytes = o->raw_off + (p.need_raw_tmp ? align256(LH * p.n * sizeof(float)) : 0);
 }
@@ -510,6 +523,15 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
   const int key_blocks = (p.n + gBlock - 1) / gBlock;
   const long long g2 = (long long)key_blocks * p.H * p.L;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (p.logit) {
+    const int Rp = (p.R + gTile - 1) / gTile * gTile;
+    hipLaunchKernelGGL(k_logit_stat, dim3((Rp + 255) / 256, p.H, p.L), dim3(256), 0, st, p.R, Rp,
+                       stat);
+    hipLaunchKernelGGL((k_gen_colagg<false, true, true>), dim3((unsigned)g2), dim3(512), 0, st, qb,
+                       kb, p.H, p.R, p.W, p.n, p.scale, key_blocks, stat, rawbuf);
+    (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
+    return hipGetLastError();
+  }
   if (p.causal)
     hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
                        p.R, p.W, p.n, alpha, o.row_blocks, o.splits, o.keys_per_split, part);

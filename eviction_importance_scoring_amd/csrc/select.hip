@@ -6,14 +6,17 @@
 // remaining entries). [KVzip] §4.2: one budget per layer across its heads.
 //
 // Each segment (a head, or a whole layer when adaptive) is one workgroup of
-// 1024 threads. The order is the 62-bit key (score bits << 31) | (2^31-1-f)
+// 1024 threads. The order is the 63-bit key (score bits << 31) | (2^31-1-f)
 // over the flat candidate index f: a larger score wins, equal scores go to
 // the lower index (lower head first when adaptive), and no two keys tie.
-// Scores are >= 0, so their IEEE bits order like the values; negative or
-// NaN inputs count as 0. The k-th key is found by MSD radix select with
-// 11/11/9-bit digits over the score bits, then over the index bits, each
-// digit a 2048-bin LDS histogram; it stops as soon as the bucket that holds
-// the k-th key is taken whole. Members are then (key >> shift) >= prefix.
+// The score bits are an order-preserving 32-bit image of the float (sign
+// bit flipped for positives, all bits flipped for negatives, -0 as +0), so
+// any finite score orders as its value, negative ones included (the
+// softmax-free logit scores of [KVzip] §6.5); NaN counts as below every
+// number. The k-th key is found by MSD radix select with 11/11/10-bit
+// digits over the score bits, then 11/11/9 over the index bits, each digit
+// a 2048-bin LDS histogram; it stops as soon as the bucket that holds the
+// k-th key is taken whole. Members are then (key >> shift) >= prefix.
 // The final select stops after the score bits: if the last bucket (keys of
 // one score) is not taken whole, its first `need` entries in index order
 // are members, which the index-order emission counts with one more scan
@@ -42,7 +45,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kBins = 2048;
 constexpr int kResidentMax = 34816;          // 136 KiB of u32 keys in LDS (< 2^16)
 constexpr int kMaxGroups = 1024;             // heads per segment
-constexpr uint32_t kInfBits = 0x7F800000u;
+constexpr uint32_t kInfBits = 0xFF800000u;     // score bits of +inf
 constexpr int kLoadUnroll = 8;              // loads in flight per thread
 constexpr int kMaxPer = 35;                  // candidates a thread emits (odd)
 
@@ -122,8 +125,12 @@ struct alignas(16) SelShared {   // a multiple of 16 bytes: the keys follow it
   uint32_t digit, above, dcount;
 };
 
+// Order-preserving 32-bit image of a score: larger value, larger bits.
 __device__ __forceinline__ uint32_t score_bits(float x) {
-  return x > 0.f ? __float_as_uint(x) : 0u;
+  if (x != x) return 0u;                      // NaN: below everything
+  if (x == 0.f) return 0x80000000u;           // -0 and +0 alike
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 __device__ __forceinline__ uint64_t make_key(uint32_t bits, uint32_t f) {
@@ -137,7 +144,7 @@ __device__ __forceinline__ uint32_t stage2_bits(float s, float w, float norm, fl
 }
 
 __device__ __forceinline__ int digit_width(int shift) {
-  return (shift == 40 || shift == 9) ? 9 : 11;   // 62->51->40->31->20->9->0
+  return shift == 41 ? 10 : (shift == 9 ? 9 : 11);   // 63->52->41->31->20->9->0
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
@@ -190,11 +197,11 @@ struct SelCut {
 __device__ SelCut radix_select(SelShared& sm, const uint32_t* bits, uint32_t len, uint32_t k,
                                int stop_shift) {
   const int tid = threadIdx.x;
-  if (k == 0 || k == len)   // nothing, or everything
-    return SelCut{(k == 0) ? uint64_t(1) : uint64_t(0), 62, 0u, true};
+  if (k == 0 || k == len)   // nothing ((key >> 63) >= 1 never holds), or everything
+    return SelCut{(k == 0) ? uint64_t(1) : uint64_t(0), 63, 0u, true};
   if (tid == 0) {
     sm.prefix = 0;
-    sm.shift = 62;
+    sm.shift = 63;
     sm.need = k;
   }
   __syncthreads();
@@ -338,8 +345,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   static_assert(((kResidentMax + kSelThreads - 1) / kSelThreads | 1) <= kMaxPer, "one 64-bit mask a thread");
   const uint32_t per = ((len + kSelThreads - 1) / kSelThreads) | 1u;
   const uint32_t f0 = min(len, tid * per), f1 = min(len, f0 + per);
-  // (key >> shift) vs prefix on the score bits alone; prefix 1 at shift 62
-  // (select nothing) stays out of reach of every 31-bit score
+  // (key >> shift) vs prefix on the score bits alone; prefix 1 at shift 63
+  // (select nothing) stays out of reach of every score
   const uint32_t csh = (uint32_t)cf.shift - 31u;
   const uint32_t cp = cf.prefix > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)cf.prefix;
   // every read first (clamped in range), then branch-free tests
@@ -532,12 +539,12 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int segment
     st.s1 = st.shift;
   } else {
     st.p1 = 1;          // no stage-1 members when single-stage
-    st.s1 = 62;
+    st.s1 = 63;
   }
   const SegSpan sp = seg_span(a, (size_t)seg);
   const uint32_t k = (stage2 || sp.k1 == 0xFFFFFFFFu) ? sp.k : sp.k1;
-  st.shift = 62;
-  if (k == 0) {          // nothing: (key >> 62) >= 1 holds for no key
+  st.shift = 63;
+  if (k == 0) {          // nothing: (key >> 63) >= 1 holds for no key
     st.prefix = 1;
     st.need = 0;
     st.done = 1;

@@ -68,7 +68,11 @@ enum {
      rescales by 1/(W*G)). The raw scores of one head sum to W*G. */
   KVSEL_AGG_SUM = 0,
   /* Max over the W queries and the G query heads ([KVzip] §3.2). */
-  KVSEL_AGG_MAX = 1
+  KVSEL_AGG_MAX = 1,
+  /* No softmax: max over the W queries and the G query heads of the logit
+     s itself (KVzip-logit, [KVzip] §6.5). KVSEL_Q_EXTERNAL only. Scores
+     may be negative; kvsel_select orders them as signed values. */
+  KVSEL_AGG_LOGIT_MAX = 2
 };
 
 /*
@@ -76,8 +80,9 @@ enum {
  *
  * Per layer l and KV head h, with query head hq = h*G + g (GQA grouping,
  * [KVzip] §2.2): logits s = scale * <q[l][hq][i], k[l][h][j]>, a softmax
- * over the keys each query sees (all n, or causal in window mode), the
- * aggregate over (g, i) chosen by `agg`, then 1-D max-pooling of width
+ * over the keys each query sees (all n, or causal in window mode; none for
+ * KVSEL_AGG_LOGIT_MAX), the aggregate over (g, i) chosen by `agg`, then
+ * 1-D max-pooling of width
  * `pool` along the candidate positions ([CriticalKV] §3.3, Algorithm 2,
  * step 4; stride 1, centred, neighbours outside [0, n_cand) ignored).
  *
@@ -174,7 +179,8 @@ int32_t kvsel_value_weight_l2(const void* v, const void* factor,
  * [n-W, n) are always kept and count toward the budget. Among candidates
  * the k = budget - W (per head) or k = budget - H_kv*W (per layer, when
  * adaptive) largest keys are kept; equal keys go to the lower index
- * (adaptive: lower head, then lower position).
+ * (adaptive: lower head, then lower position). Keys compare as signed
+ * floats (-0 equal to +0); a NaN key counts as below every number.
  *
  *  - weight == NULL: key = scores ([CriticalKV] §3.3, Algorithm 2, step 6).
  *  - weight != NULL: CriticalKV's two-stage selection ([CriticalKV] §3.3,

@@ -62,7 +62,7 @@ class Workload:
     n: int
     W: int
     q_mode: str = "window"
-    agg: str = "sum"
+    agg: str = "sum"             # 'sum', 'max' (softmax weights) or 'logit' (raw logits, external)
     pool: int = 7
     beta: float = 0.2            # kept fraction (window included)
     adaptive: bool = False       # one budget per layer shared by all heads
@@ -133,6 +133,10 @@ WORKLOADS = {
         # H2O-style accumulated attention: window scoring with W = 256, 20%
         Workload("h2o_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=256,
                  pool=7, beta=0.20),
+        # KVzip-logit: the same queries, max of the raw logits (no softmax)
+        Workload("kvzip_logit_qwen7b_n32k", L=28, H_kv=4, G=7, d=128, n=32768,
+                 W=4096, q_mode="external", agg="logit", pool=1, beta=0.25,
+                 q_chunk=512),
         # many external queries, max aggregation, Qwen2.5-7B GQA shape
         Workload("kvzip_qwen7b_n32k", L=28, H_kv=4, G=7, d=128, n=32768,
                  W=4096, q_mode="external", agg="max", pool=1, beta=0.25,

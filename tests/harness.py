@@ -9,9 +9,15 @@ is below fp32 resolution of that head's softmax terms, e.g. keys whose
 every weight underflows; select_tolerance_ok() checks that no such entry
 sits at a selection boundary.
 
+Logit rule (KVzip-logit scores, any sign): |gpu - ref| <= RTOL * |ref| +
+LOGIT_ATOL_REL * max |ref| of that head. A logit is an fp32 sum of 128
+exact bf16 products: its absolute error scales with the terms, not with
+the (possibly cancelling) sum, so near-zero logits get the floor.
+
 Selection rule: let t be the oracle's k-th largest key of a segment and
-A = {j : |key_j - t| <= RTOL * t + tau}. The GPU keeps exactly as many
-entries as the oracle and the two sets agree outside A.
+A = {j : |key_j - t| <= RTOL * |t| + tau}, tau = ATOL_REL * max(key) (or
+LOGIT_ATOL_REL * max |key| for logit scores). The GPU keeps exactly as
+many entries as the oracle and the two sets agree outside A.
 """
 from __future__ import annotations
 
@@ -23,6 +29,7 @@ import synth
 
 RTOL = 1e-3
 ATOL_REL = 1e-6
+LOGIT_ATOL_REL = 1e-4
 
 
 def to_dev(u16: np.ndarray, device="cuda") -> torch.Tensor:
@@ -47,23 +54,33 @@ def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, what: str = "scores"):
     return float((err / np.maximum(np.abs(ref), 1e-30)).max())
 
 
-def _band(key: np.ndarray, k: int):
+def _band(key: np.ndarray, k: int, logit: bool = False):
     """Oracle's k-th key t and the tolerance band around it (a boolean mask)."""
     if k == 0 or k == key.size:
         return None, np.zeros(key.shape, bool)
     order = np.lexsort((np.arange(key.size), -key))
     t = key[order[k - 1]]
-    tau = ATOL_REL * key.max()
+    tau = LOGIT_ATOL_REL * np.abs(key).max() if logit else ATOL_REL * key.max()
     return t, np.abs(key - t) <= RTOL * abs(t) + tau
 
 
-def assert_topk_within_band(gpu_pick, ref_key: np.ndarray, k: int, what: str):
+def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, what: str = "logit scores"):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    tol = RTOL * np.abs(ref) + LOGIT_ATOL_REL * np.abs(ref).max(axis=-1, keepdims=True)
+    bad = np.abs(gpu - ref) > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} entries outside tolerance, "
+                           f"max err {np.abs(gpu - ref).max():.3g}")
+
+
+def assert_topk_within_band(gpu_pick, ref_key: np.ndarray, k: int, what: str, logit: bool = False):
     """gpu_pick: candidate indices the GPU kept (any order)."""
     gpu_pick = np.asarray(gpu_pick)
     assert gpu_pick.size == k, f"{what}: kept {gpu_pick.size}, expected {k}"
     assert np.unique(gpu_pick).size == k, f"{what}: duplicate indices"
     ref_pick = oracle.topk_indices(ref_key, k)
-    t, band = _band(ref_key, k)
+    t, band = _band(ref_key, k, logit)
     g = np.zeros(ref_key.size, bool)
     g[gpu_pick] = True
     r = np.zeros(ref_key.size, bool)
@@ -98,6 +115,8 @@ def oracle_scores_layer(wl: synth.Workload, q_u16, k_u16):
     k = synth.bf16_to_f64(k_u16)
     if wl.q_mode == "window":
         raw = oracle.window_raw_scores(q, k, wl.G, wl.scale, wl.agg)
+    elif wl.agg == "logit":
+        raw = oracle.external_logit_scores(q, k, wl.G, wl.scale)
     else:
         raw = oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg)
     return raw, oracle.maxpool(raw, wl.n_cand, wl.pool)

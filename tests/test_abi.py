@@ -272,3 +272,11 @@ def test_select_budgets_pointers(lib):
     assert f(*args(p, None, p, p)) == ARG
     assert f(*args(p, p, None, p)) == ARG
     assert f(*args(p, p, p, None)) == ARG
+
+
+def test_score_logit_mode(lib):
+    assert _score(lib, mode=1, agg=2)[0] == OK
+    assert _score(lib, mode=0, agg=2)[0] == ARG      # external queries only
+    assert _score(lib, mode=1, agg=3)[0] == ARG
+    # no pass 1: a smaller workspace than the softmax max of the same shape
+    assert _score(lib, mode=1, agg=2, W=4096)[1] < _score(lib, mode=1, agg=1, W=4096)[1]

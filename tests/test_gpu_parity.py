@@ -12,8 +12,8 @@ import torch
 import eviction_importance_scoring_amd as kv
 import oracle
 import synth
-from harness import (assert_scores_close, assert_topk_within_band, gen, oracle_scores_layer,
-                     split_heads, to_dev)
+from harness import (assert_logits_close, assert_scores_close, assert_topk_within_band, gen,
+                     oracle_scores_layer, split_heads, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -273,6 +273,78 @@ def test_select_budgets_feed_compact_and_decode():
         ref = oracle.decode_attention(synth.bf16_to_f64(qb[l]), synth.bf16_to_f64(ko_h[l, :end]), vl,
                                       G, 0.088, head_offsets=offs_h[l])
         np.testing.assert_allclose(out[l], ref, rtol=1e-4, atol=1e-4 * np.abs(vl).max())
+
+
+# KVzip-logit: scale * max <q, k> in fp32 from bf16 (exact products, fp32
+# sums of 128 terms), checked with the logit rule of harness.py.
+LOGIT_CASES = [
+    # (L, H, G, n, Q per query head, pool)
+    (1, 2, 3, 1000, 70, 1),
+    (2, 1, 7, 4097, 130, 5),      # several key blocks, ragged, pooled negatives
+    (1, 2, 1, 300, 600, 1),       # more queries than keys
+    (1, 4, 4, 2048, 512, 3),
+    (1, 2, 1, 777, 1, 5),         # one query: about half the scores negative, pooled
+]
+
+
+@pytest.mark.parametrize("case", LOGIT_CASES, ids=lambda c: "L{}H{}G{}n{}Q{}p{}".format(*c))
+def test_logit_scores(case):
+    L, H, G, n, Qn, pool = case
+    wl = _wl(L=L, H_kv=H, G=G, n=n, W=Qn, q_mode="external", agg="max", pool=pool)
+    data = gen(wl, seed=11, which=("q", "k"))
+    print(f"[gpu] kvsel_score logit {case}", flush=True)
+    s, r = kv.kvsel_score(to_dev(data["q"]), to_dev(data["k"]), G=G, q_mode=kv.Q_EXTERNAL,
+                          agg=kv.AGG_LOGIT_MAX, scale=wl.scale, pool=pool, return_raw=True)
+    torch.cuda.synchronize()
+    s, r = s.cpu().numpy(), r.cpu().numpy()
+    for l in range(L):
+        ref = oracle.external_logit_scores(synth.bf16_to_f64(data["q"][l]),
+                                           synth.bf16_to_f64(data["k"][l]), G, wl.scale)
+        refp = oracle.maxpool(ref, n, pool)
+        assert_logits_close(r[l], ref, f"logit raw l{l}")
+        assert_logits_close(s[l], refp, f"logit pooled l{l}")
+
+
+SIGNED_CASES = [
+    # (L, H, n, W, frac, adaptive, two_stage)
+    (1, 3, 2000, 0, 0.3, False, False),
+    (2, 2, 1000, 8, 0.2, True, False),
+    (1, 2, 3000, 16, 0.4, False, True),
+    (1, 1, 50000, 0, 0.1, False, False),      # many workgroups
+    (1, 2, 40000, 8, 0.3, True, True),        # many workgroups, adaptive two-stage
+]
+
+
+@pytest.mark.parametrize("case", SIGNED_CASES, ids=lambda c: "L{}H{}n{}W{}b{}a{}t{}".format(*c))
+def test_select_signed_scores(case):
+    """Negative scores (logit scores), -0 beside +0, and infinities."""
+    L, H, n, W, frac, adaptive, two_stage = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    n_cand = n - W
+    sc = (rng.integers(-40, 40, size=(L, H, n_cand)) * 0.125).astype(np.float32)
+    sc[sc == 0] = np.where(rng.random((sc == 0).sum()) < 0.5, -0.0, 0.0)
+    flat = sc.reshape(-1)
+    flat[rng.choice(flat.size, 5, replace=False)] = np.inf
+    flat[rng.choice(flat.size, 5, replace=False)] = -np.inf
+    wt = (rng.random((L, H, n_cand)).astype(np.float32) * 3 + 0.01) if two_stage else None
+    groups = H if adaptive else 1
+    budget = max(groups * W, int(np.floor(frac * groups * n)))
+    print(f"[gpu] kvsel_select signed case={case}", flush=True)
+    idx, offs, stage = kv.kvsel_select(torch.from_numpy(sc).cuda(), n=n, W=W, budget=budget,
+                                       adaptive=adaptive,
+                                       weight=None if wt is None else torch.from_numpy(wt).cuda(),
+                                       score_norm=1.0 / 128, eps=1e-4, alpha=0.5, return_stage=True)
+    torch.cuda.synchronize()
+    idx, stage = idx.cpu().numpy(), stage.cpu().numpy()
+    for l in range(L):
+        ri, ro, rs = oracle.select_layer(sc[l].astype(np.float64), budget, W, n, adaptive=adaptive,
+                                         weight=None if wt is None else wt[l].astype(np.float64),
+                                         alpha=0.5, score_norm=float(np.float32(1 / 128)),
+                                         eps=float(np.float32(1e-4)), dtype=np.float32)
+        np.testing.assert_array_equal(idx[l], ri)
+        np.testing.assert_array_equal(stage[l], rs)
+        if adaptive:
+            np.testing.assert_array_equal(offs[l].cpu().numpy(), ro)
 
 
 def test_select_end_to_end_band():

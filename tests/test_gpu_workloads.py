@@ -24,8 +24,8 @@ import torch
 import eviction_importance_scoring_amd as kv
 import oracle
 import synth
-from harness import (assert_scores_close, assert_topk_within_band, oracle_scores_layer,
-                     split_heads, to_dev)
+from harness import (assert_logits_close, assert_scores_close, assert_topk_within_band,
+                     oracle_scores_layer, split_heads, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def device_inputs(wl: synth.Workload, sampled, which):
 
 def _score(wl, dev):
     mode = kv.Q_WINDOW if wl.q_mode == "window" else kv.Q_EXTERNAL
-    agg = kv.AGG_SUM if wl.agg == "sum" else kv.AGG_MAX
+    agg = {"sum": kv.AGG_SUM, "max": kv.AGG_MAX, "logit": kv.AGG_LOGIT_MAX}[wl.agg]
     print(f"[gpu] kvsel_score {wl.name}", flush=True)
     s, r = kv.kvsel_score(dev["q"], dev["k"], G=wl.G, q_mode=mode, agg=agg, scale=wl.scale,
                           pool=wl.pool, return_raw=True)
@@ -236,18 +236,25 @@ def test_criticalkv_full(name):
     _check_compact(dev, host, idx, offs, 0, wl)
 
 
-def test_kvzip_many_query_full():
-    wl = synth.WORKLOADS["kvzip_qwen7b_n32k"]
+@pytest.mark.parametrize("name", ["kvzip_qwen7b_n32k", "kvzip_logit_qwen7b_n32k"])
+def test_kvzip_many_query_full(name):
+    wl = synth.WORKLOADS[name]
+    logit = wl.agg == "logit"
     dev, host = device_inputs(wl, {0}, ("q", "k"))
     s, r = _score(wl, dev)
     # oracle on one KV head of layer 0 (28672 query rows x 32768 keys)
     h = 1
     q = synth.bf16_to_f64(host[("q", 0)][h * wl.G:(h + 1) * wl.G])
     k = synth.bf16_to_f64(host[("k", 0)][h:h + 1])
-    ref = oracle.external_raw_scores(q, k, wl.G, wl.scale, "max", q_chunk=512)[0]
-    assert_scores_close(r[0, h].cpu().numpy()[None], ref[None], "kvzip raw")
-    assert_scores_close(s[0, h].cpu().numpy()[None], ref[None], "kvzip scores")
+    if logit:
+        ref = oracle.external_logit_scores(q, k, wl.G, wl.scale)[0]
+        close = assert_logits_close
+    else:
+        ref = oracle.external_raw_scores(q, k, wl.G, wl.scale, "max", q_chunk=512)[0]
+        close = assert_scores_close
+    close(r[0, h].cpu().numpy()[None], ref[None], "kvzip raw")
+    close(s[0, h].cpu().numpy()[None], ref[None], "kvzip scores")
     idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=0, budget=wl.budget, return_stage=True)
     torch.cuda.synchronize()
     _check_select_exact(wl, s, None, idx, offs, stage, [0, wl.L - 1])
-    assert_topk_within_band(idx[0, h].cpu().numpy(), ref, wl.budget, "kvzip select")
+    assert_topk_within_band(idx[0, h].cpu().numpy(), ref, wl.budget, "kvzip select", logit)
