@@ -73,6 +73,7 @@ def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
     from threadpoolctl import threadpool_info
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     units = 0
+    head_rows = []
     pairs = [(l, h) for l in range(min(wl.L, host["q"].shape[0])) for h in range(wl.H_kv)]
     t0 = time.perf_counter()
     # the sample's pairs in order, repeated until `seconds` of CPU work
@@ -86,6 +87,10 @@ def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
             raw = (oracle.external_logit_scores(q, k, wl.G, wl.scale) if wl.agg == "logit"
                    else oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg))
         pooled = oracle.maxpool(raw, wl.n_cand, wl.pool)
+        if wl.head_keep > 0:   # selected below, once the sample's head scores are known
+            head_rows.append(pooled)
+            units += 1
+            continue
         weight = None
         if wl.value_weight and w_host is not None:
             v = synth.bf16_to_f64(host["v"][l][h:h + 1])
@@ -100,8 +105,16 @@ def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
                                 wl.W_kept, wl.n, weight=weight, alpha=wl.alpha,
                                 score_norm=1.0 / (wl.W * wl.G), eps=wl.eps)
         units += 1
+    if head_rows:
+        # head-level eviction over the sample's heads: head score, keep the
+        # same fraction whole, select each head under its budget
+        hs = oracle.head_scores(np.concatenate(head_rows))[None]
+        b = oracle.head_budgets(hs, int(round(wl.head_keep * hs.size)), wl.n, wl.W_kept)
+        for i, row in enumerate(head_rows):
+            oracle.select_budgets(row, b[0, i:i + 1], wl.W_kept, wl.n)
     dt = time.perf_counter() - t0
-    what = "scores, max-pool" + (", value weight" if wl.value_weight else "") + " and top-k selection"
+    what = ("scores, max-pool" + (", value weight" if wl.value_weight else "")
+            + (", head scores and head budgets" if head_rows else "") + " and top-k selection")
     return {"value": units * wl.n / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
             "sample": f"{units} (layer, KV head) pairs of {wl.name} in order from layer 0"
                       f"{' (the sample repeated)' if units > len(pairs) else ''}: "
@@ -192,6 +205,15 @@ def main():
         b_host = synth.gen_budgets(wl, args.seed)
         budgets = torch.from_numpy(b_host).to(dev)
         stride = int(np.clip(b_host, W_kept, wl.n).astype(np.int64).sum(axis=1).max())
+    keep = 0
+    if wl.head_keep > 0:
+        # head-level eviction: the budgets come from the head scores inside
+        # the step; a layer holds at most min(H, keep) whole heads
+        keep = int(round(wl.head_keep * wl.L * wl.H_kv))
+        full = min(wl.H_kv, keep)
+        stride = full * wl.n + (wl.H_kv - full) * W_kept
+        head_sc = torch.empty((wl.L, wl.H_kv), dtype=torch.float32, device=dev)
+        budgets = torch.empty((wl.L, wl.H_kv), dtype=torch.int32, device=dev)
 
     def step(marks=None):
         if marks is not None:
@@ -200,6 +222,9 @@ def main():
                        scores=scores)
         if marks is not None:
             marks[1].record()
+        if keep:
+            kv.kvsel_head_score(scores, out=head_sc)
+            kv.kvsel_head_budgets(head_sc, keep=keep, n=wl.n, W=W_kept, out=budgets)
         if l2:
             kv.kvsel_value_weight_l2(v, factor, G=wl.G, n_cand=wl.n_cand, weight=weight)
         elif weight is not None:
@@ -267,13 +292,18 @@ def main():
                    "n": wl.n, "W": wl.W, "q_mode": wl.q_mode, "agg": wl.agg, "pool": wl.pool,
                    "budget": wl.budget, "adaptive": wl.adaptive,
                    **({"budget_vector": True, "layer_stride": stride} if wl.budget_vector else {}),
+                   **({"head_keep": wl.head_keep, "heads_kept": keep, "layer_stride": stride}
+                      if keep else {}),
                    "value_weight": wl.value_weight,
                    **({"value_norm": wl.value_norm} if wl.value_weight else {}),
                    "seed": args.seed,
-                   "step": "score+value_weight+select+compact" if wl.value_weight
-                           else "score+select+compact"},
+                   "step": ("score+head_score+head_budgets+select_budgets+compact" if keep
+                            else "score+select_budgets+compact" if wl.budget_vector
+                            else "score+value_weight+select+compact" if wl.value_weight
+                            else "score+select+compact")},
         "roofline": None,   # the dominant call's, set below
         "per_call_ms": {"score": ms_score, **({"value_weight": ms_vw} if wl.value_weight else {}),
+                        **({"head_score+head_budgets": ms_vw} if keep else {}),
                         "select": ms_sel, "compact": ms_cmp},
         "scored_selected_entries_per_s": entries / ((ms_score + ms_sel) * 1e-3),
         "wall_s_timed": wall,

@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_value_weight",
     "kvsel_value_l2_factor", "kvsel_value_weight_l2",
-    "kvsel_select", "kvsel_select_budgets", "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
+    "kvsel_select", "kvsel_select_budgets", "kvsel_head_score", "kvsel_head_budgets",
+    "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
     "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX", "AGG_LOGIT_MAX",
 ]
@@ -51,6 +52,9 @@ _SIGNATURES = {
     "kvsel_select_budgets": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                              _c_i64, _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p,
                              _c_void_p, _c_size_p, _c_void_p],
+    "kvsel_head_score": [_c_void_p, _c_i32, _c_i32, _c_i32, _c_void_p, _c_void_p],
+    "kvsel_head_budgets": [_c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
+                           _c_void_p, _c_size_p, _c_void_p],
     "kvsel_compact": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                       _c_void_p, _c_i64, _c_void_p, _c_void_p, _c_void_p],
     "kvsel_decode_attention": [_c_void_p, _c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -275,6 +279,34 @@ def kvsel_select_budgets(scores, budgets, *, n: int, W: int, layer_stride: int |
     _check(f(_ptr(scores), _ptr(weight), *args, _ptr(budgets), int(layer_stride), *tail, _ptr(idx),
              _ptr(offs), _ptr(stage), _ptr(ws), ctypes.byref(nbytes), _stream(dev)))
     return idx, offs, stage
+
+
+def kvsel_head_score(scores, *, out=None):
+    """Head scores [L][H_kv]: max over positions of scores f32 [L][H_kv][n_pos]."""
+    _need(scores, torch.float32, "scores", 3)
+    L, H, n_pos = scores.shape
+    if out is None:
+        out = torch.empty((L, H), dtype=torch.float32, device=scores.device)
+    _check(lib().kvsel_head_score(_ptr(scores), L, H, n_pos, _ptr(out), _stream(scores.device)))
+    return out
+
+
+def kvsel_head_budgets(head_score, *, keep: int, n: int, W: int, out=None, workspace=None):
+    """Budgets i32 [L][H_kv] of head-level eviction: n for the `keep` heads
+    with the largest head score, W for the others."""
+    _need(head_score, torch.float32, "head_score", 2)
+    L, H = head_score.shape
+    dev = head_score.device
+    if out is None:
+        out = torch.empty((L, H), dtype=torch.int32, device=dev)
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_head_budgets
+    _check(f(None, L, H, int(keep), n, W, None, None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(head_score), L, H, int(keep), n, W, _ptr(out), _ptr(ws), ctypes.byref(nbytes),
+             _stream(dev)))
+    return out
 
 
 def kvsel_compact(k, v, idx, head_offsets=None, k_out=None, v_out=None):

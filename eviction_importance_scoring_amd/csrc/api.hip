@@ -215,6 +215,37 @@ int32_t kvsel_select_budgets(const float* scores, const float* weight, int32_t L
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 
+int32_t kvsel_head_score(const float* scores, int32_t L, int32_t H_kv, int32_t n_pos,
+                         float* head_score, void* stream) {
+  if (!scores || !head_score) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || n_pos < 1) return KVSEL_ERR_ARG;
+  if ((int64_t)L * H_kv > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  const hipError_t e = head_score_launch(scores, L, H_kv, n_pos, head_score,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_head_budgets(const float* head_score, int32_t L, int32_t H_kv, int32_t keep,
+                           int32_t n, int32_t W, int32_t* budgets, void* ws, size_t* ws_bytes,
+                           void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || n < 1 || W < 0 || W > n) return KVSEL_ERR_ARG;
+  const int64_t count = (int64_t)L * H_kv;
+  if (count > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  if (keep < 0 || keep > count) return KVSEL_ERR_ARG;
+  const size_t need = head_budgets_ws_bytes((int)count, keep);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!head_score || !budgets) return KVSEL_ERR_ARG;
+  if (!aligned16(head_score) || !aligned16(ws)) return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  const hipError_t e = head_budgets_launch(head_score, (int)count, keep, n, W, budgets, ws,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
 int32_t kvsel_compact(const void* k, const void* v, int32_t L, int32_t H_kv, int32_t d,
                       int32_t n, const int32_t* idx, const int32_t* head_offsets,
                       int64_t kept_per_layer, void* k_out, void* v_out, void* stream) {

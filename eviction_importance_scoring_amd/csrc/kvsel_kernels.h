@@ -76,6 +76,13 @@ hipError_t value_l2_factor_launch(const void* w_o, int L, int H, int G, int D, v
 hipError_t value_weight_l2_launch(const void* v, const void* factor, int L, int H, int G, int n,
                                   int n_cand, float* weight, hipStream_t st);
 
+// ------------------------------------------------------------ head level ----
+hipError_t head_score_launch(const float* scores, int L, int H, int n_pos, float* out,
+                             hipStream_t st);
+size_t head_budgets_ws_bytes(int count, int keep);
+hipError_t head_budgets_launch(const float* head_score, int count, int keep, int n, int W,
+                               int32_t* budgets, void* ws, hipStream_t st);
+
 // -------------------------------------------------------------- decoding ----
 size_t decode_ws_bytes(int L, int H, int G, int64_t kept, bool ragged);
 hipError_t decode_launch(const void* q, const void* k, const void* v, int L, int H, int G,

@@ -21,7 +21,7 @@
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
  *  - Workspace protocol (kvsel_score, kvsel_select, kvsel_select_budgets,
- *    kvsel_decode_attention): with ws == NULL the
+ *    kvsel_head_budgets, kvsel_decode_attention): with ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
  *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
  *    Workspace contents need no initialisation and are scratch afterwards.
@@ -252,6 +252,40 @@ int32_t kvsel_select_budgets(const float* scores, const float* weight,
                              float score_norm, float eps, float alpha,
                              int32_t* idx, int32_t* head_offsets, uint8_t* stage,
                              void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_head_score -- head-level importance.
+ *
+ * [KVzip] §3.4: the score of a head is the maximum of its per-position
+ * scores over the sequence, head_score[l][h] = max_i scores[l][h][i].
+ *
+ *   scores     f32 [L][H_kv][n_pos]   e.g. kvsel_score's scores or raw
+ *   head_score f32 [L][H_kv]
+ *
+ * NaN entries are ignored (a row of NaN gives -inf).
+ */
+int32_t kvsel_head_score(const float* scores, int32_t L, int32_t H_kv,
+                         int32_t n_pos, float* head_score, void* stream);
+
+/*
+ * kvsel_head_budgets -- budgets of head-level eviction.
+ *
+ * [KVzip] §3.6 / §5.4: context-independent eviction keeps or drops whole
+ * heads by their head score, in DuoAttention's structure where a dropped
+ * head holds only a recent window. The `keep` heads with the largest
+ * head_score over all layers and heads (equal scores to the lower flat
+ * index l*H_kv + h; scores ordered as by kvsel_select) get budget n, the
+ * others budget W: the budget vector kvsel_select_budgets takes.
+ *
+ *   head_score f32 [L][H_kv]
+ *   budgets    i32 [L][H_kv]   out
+ *
+ * Ranges: 0 <= keep <= L*H_kv; 0 <= W <= n. Needs a workspace (protocol
+ * above).
+ */
+int32_t kvsel_head_budgets(const float* head_score, int32_t L, int32_t H_kv,
+                           int32_t keep, int32_t n, int32_t W, int32_t* budgets,
+                           void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * kvsel_compact -- gather the kept rows of K and V.

@@ -67,6 +67,7 @@ class Workload:
     beta: float = 0.2            # kept fraction (window included)
     adaptive: bool = False       # one budget per layer shared by all heads
     budget_vector: bool = False  # one budget per (layer, head), from gen_budgets
+    head_keep: float = 0.0       # > 0: head-level eviction keeping this fraction of heads
     value_weight: bool = False   # value-norm weighted two-stage selection
     value_norm: str = "l1"       # norm of the projected value: 'l1' or 'l2'
     D: int = 0                   # model width for w_o
@@ -130,6 +131,10 @@ WORKLOADS = {
         # allocation), n = 32K
         Workload("headkv_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=32,
                  pool=7, beta=0.20, budget_vector=True),
+        # head-level eviction: head score = max over positions of the window
+        # score, half of all heads kept whole, the others their window
+        Workload("headlevel_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=32,
+                 pool=7, head_keep=0.5),
         # H2O-style accumulated attention: window scoring with W = 256, 20%
         Workload("h2o_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=256,
                  pool=7, beta=0.20),

@@ -280,3 +280,37 @@ def test_score_logit_mode(lib):
     assert _score(lib, mode=1, agg=3)[0] == ARG
     # no pass 1: a smaller workspace than the softmax max of the same shape
     assert _score(lib, mode=1, agg=2, W=4096)[1] < _score(lib, mode=1, agg=1, W=4096)[1]
+
+
+def _head_budgets(lib, **kw):
+    a = dict(L=4, H=8, keep=10, n=1000, W=32)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    rc = lib.kvsel_head_budgets(None, a["L"], a["H"], a["keep"], a["n"], a["W"], None, None,
+                                ctypes.byref(nb), None)
+    return rc, nb.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(keep=0), OK), (dict(keep=32), OK), (dict(W=0), OK), (dict(W=1000), OK),
+    (dict(L=100, H=400, keep=20000), OK),   # more heads than one workgroup holds
+    (dict(keep=33), ARG), (dict(keep=-1), ARG), (dict(W=1001), ARG), (dict(W=-1), ARG),
+    (dict(L=0), ARG), (dict(n=0), ARG),
+])
+def test_head_budgets_ranges(lib, kw, code):
+    assert _head_budgets(lib, **kw)[0] == code
+
+
+@no_gpu_only
+def test_head_score_and_budgets_pointers(lib):
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.kvsel_head_score(None, 2, 8, 100, p, None) == ARG
+    assert lib.kvsel_head_score(p, 2, 8, 100, None, None) == ARG
+    assert lib.kvsel_head_score(p, 0, 8, 100, p, None) == ARG
+    assert lib.kvsel_head_score(p, 2, 8, 0, p, None) == ARG
+    nb = ctypes.c_size_t(1 << 20)
+    f = lib.kvsel_head_budgets
+    assert f(None, 2, 8, 3, 100, 8, p, p, ctypes.byref(nb), None) == ARG
+    assert f(p, 2, 8, 3, 100, 8, None, p, ctypes.byref(nb), None) == ARG
+    small = ctypes.c_size_t(1)
+    assert f(p, 2, 8, 3, 100, 8, p, p, ctypes.byref(small), None) == WS

@@ -347,6 +347,51 @@ def test_select_signed_scores(case):
             np.testing.assert_array_equal(offs[l].cpu().numpy(), ro)
 
 
+@pytest.mark.parametrize("L,H,n_pos", [(2, 3, 1), (1, 4, 3), (3, 8, 4096), (2, 2, 33333)])
+def test_head_score_exact(L, H, n_pos):
+    """The max is exact: bit-equal to the oracle on signed scores."""
+    rng = np.random.default_rng(L * 1000 + n_pos)
+    sc = (rng.standard_normal((L, H, n_pos)) * 5 - 2).astype(np.float32)
+    print(f"[gpu] kvsel_head_score L={L} H={H} n_pos={n_pos}", flush=True)
+    got = kv.kvsel_head_score(torch.from_numpy(sc).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.head_scores(sc.astype(np.float64)).astype(np.float32))
+
+
+@pytest.mark.parametrize("L,H,keep,levels", [
+    (2, 3, 3, 4), (4, 8, 0, 10), (4, 8, 32, 10), (32, 8, 128, 7),
+    (100, 400, 20000, 50),    # 40000 heads: the many-workgroup selection
+])
+def test_head_budgets_exact(L, H, keep, levels):
+    rng = np.random.default_rng(keep + L)
+    hs = _quantised_scores(rng, (L, H), levels) - 0.5
+    n, W = 5000, 16
+    print(f"[gpu] kvsel_head_budgets L={L} H={H} keep={keep}", flush=True)
+    got = kv.kvsel_head_budgets(torch.from_numpy(hs).cuda(), keep=keep, n=n, W=W).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.head_budgets(hs.astype(np.float64), keep, n, W))
+
+
+def test_head_level_eviction_pipeline():
+    """Head score -> head budgets -> budget-vector select -> compaction: the
+    kept heads keep every entry, the others their last W."""
+    L, H, n, W, keep = 2, 4, 900, 24, 3
+    rng = np.random.default_rng(77)
+    sc = rng.random((L, H, n - W)).astype(np.float32)
+    hs = kv.kvsel_head_score(torch.from_numpy(sc).cuda())
+    b = kv.kvsel_head_budgets(hs, keep=keep, n=n, W=W)
+    idx, offs, _ = kv.kvsel_select_budgets(torch.from_numpy(sc).cuda(), b, n=n, W=W)
+    torch.cuda.synchronize()
+    rb = oracle.head_budgets(oracle.head_scores(sc.astype(np.float64)), keep, n, W)
+    np.testing.assert_array_equal(b.cpu().numpy(), rb)
+    idx, offs = idx.cpu().numpy(), offs.cpu().numpy()
+    for l in range(L):
+        ri, ro, _ = oracle.select_budgets(sc[l].astype(np.float64), rb[l], W, n, dtype=np.float32)
+        np.testing.assert_array_equal(offs[l], ro)
+        np.testing.assert_array_equal(idx[l, :len(ri)], ri)
+        for h in range(H):
+            want = np.arange(n) if rb[l, h] == n else np.arange(n - W, n)
+            np.testing.assert_array_equal(idx[l, offs[l, h]:offs[l, h + 1]], want)
+
+
 def test_select_end_to_end_band():
     """GPU scores + GPU select against the fp64 oracle's selection."""
     wl = _wl(L=2, H_kv=2, n=3000, W=32)

@@ -200,6 +200,46 @@ def test_headkv_budget_vector_full():
     _check_decode(wl, ko, vo, offs, 0)
 
 
+def test_headlevel_eviction_full():
+    wl = synth.WORKLOADS["headlevel_llama8b_n32k"]
+    sampled = [0, wl.L - 1]
+    dev, host = device_inputs(wl, set(sampled), ("q", "k", "v"))
+    s, r = _score(wl, dev)
+    _check_scores(wl, s, r, host, [0])
+    keep = int(round(wl.head_keep * wl.L * wl.H_kv))
+    print("[gpu] kvsel_head_score + kvsel_head_budgets full", flush=True)
+    hs = kv.kvsel_head_score(s)
+    b = kv.kvsel_head_budgets(hs, keep=keep, n=wl.n, W=wl.W)
+    torch.cuda.synchronize()
+    s_h = s.cpu().numpy()
+    # exact on the GPU's own scores; within the score tolerance of the fp64 oracle
+    np.testing.assert_array_equal(hs.cpu().numpy(), oracle.head_scores(s_h.astype(np.float64)).astype(np.float32))
+    _, ref_pool = oracle_scores_layer(wl, host[("q", 0)], host[("k", 0)])
+    assert_scores_close(hs[0].cpu().numpy(), oracle.head_scores(ref_pool), "head score l0")
+    bh = b.cpu().numpy()
+    np.testing.assert_array_equal(bh, oracle.head_budgets(hs.cpu().numpy().astype(np.float64), keep,
+                                                          wl.n, wl.W))
+    full = min(wl.H_kv, keep)
+    stride = full * wl.n + (wl.H_kv - full) * wl.W
+    idx, offs, _ = kv.kvsel_select_budgets(s, b, n=wl.n, W=wl.W, layer_stride=stride)
+    torch.cuda.synchronize()
+    for l in sampled:
+        o = offs[l].cpu().numpy()
+        ri, ro, _ = oracle.select_budgets(s_h[l].astype(np.float64), bh[l], wl.W, wl.n, dtype=np.float32)
+        np.testing.assert_array_equal(o, ro)
+        np.testing.assert_array_equal(idx[l, :len(ri)].cpu().numpy(), ri)
+    ko, vo = kv.kvsel_compact(dev["k"], dev["v"], idx, offs)
+    torch.cuda.synchronize()
+    o = offs[0].cpu().numpy()
+    end = int(o[-1])
+    k_l = dev["k"][0].cpu().view(torch.int16).numpy().view(np.uint16)
+    v_l = dev["v"][0].cpu().view(torch.int16).numpy().view(np.uint16)
+    rk, rv = oracle.compact_layer(k_l, v_l, idx[0, :end].cpu().numpy(), o)
+    np.testing.assert_array_equal(ko[0, :end].cpu().view(torch.int16).numpy().view(np.uint16), rk)
+    np.testing.assert_array_equal(vo[0, :end].cpu().view(torch.int16).numpy().view(np.uint16), rv)
+    _check_decode(wl, ko, vo, offs, 0)
+
+
 @pytest.mark.parametrize("name", ["criticalkv_llama8b_n128k", "criticaladakv_llama8b_n32k",
                                   "criticalkv_l2_llama8b_n128k"])
 def test_criticalkv_full(name):
