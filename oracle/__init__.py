@@ -114,6 +114,45 @@ def external_raw_scores(q: np.ndarray, k: np.ndarray, G: int, scale: float,
     return raw
 
 
+def chunked_scores(q: np.ndarray, k_cache: np.ndarray, k_self: np.ndarray, G: int,
+                   scale: float, m: int, n_prompt: int) -> np.ndarray:
+    """KVzip's chunked scoring, with the input's own keys in the softmax.
+
+    [KVzip, §3.4]: the context's n cached keys are split into T = ceil(n/m)
+    chunks of m. Chunk t is reconstructed on its own from an input of
+    n_in = n_prompt + m_t tokens (the repeat prompt, then the chunk), whose
+    queries attend over the chunk's cached keys followed by the input's own
+    n_in keys: A = Softmax(Q [K_chunk; K_self]^T), an n_in x (m_t + n_in)
+    matrix per query head. The slice of A on the cached keys, maxed over the
+    group queries and input positions, scores the chunk's keys.
+    Readings: the logits carry the model's scale; the input's own keys are
+    causal (input position i sees its keys 0..i), the cached keys all
+    visible (the context precedes the input); the last chunk may be shorter
+    (m_t = n - t*m), its input then n_prompt + m_t tokens long.
+
+    q: [T][H_kv*G][n_in_max][d], k_cache: [H_kv][n][d],
+    k_self: [T][H_kv][n_in_max][d] with n_in_max = n_prompt + m (rows past a
+    chunk's own n_in are ignored). Returns [H_kv][n].
+    """
+    H, n, d = k_cache.shape
+    T = (n + m - 1) // m
+    assert q.shape[0] == T and q.shape[1] == H * G and k_self.shape[0] == T
+    S = np.zeros((H, n))
+    for t in range(T):
+        c0 = t * m
+        mt = min(m, n - c0)
+        nin = n_prompt + mt
+        for h in range(H):
+            keys = np.concatenate([k_cache[h, c0:c0 + mt], k_self[t, h, :nin]])   # [mt + nin][d]
+            hidden = np.zeros((nin, mt + nin), bool)
+            hidden[:, mt:] = np.triu(np.ones((nin, nin), bool), 1)   # self key j > position i
+            for g in range(G):
+                logits = scale * (q[t, h * G + g, :nin] @ keys.T)
+                a = _softmax_rows(np.where(hidden, -np.inf, logits))
+                S[h, c0:c0 + mt] = np.maximum(S[h, c0:c0 + mt], a[:, :mt].max(axis=0))
+    return S
+
+
 def external_logit_scores(q: np.ndarray, k: np.ndarray, G: int, scale: float) -> np.ndarray:
     """The softmax-free scores of KVzip-logit.
 

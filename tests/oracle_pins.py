@@ -253,6 +253,48 @@ def check_head_scores_and_budgets(o):
         _assert_topk_property(hs.reshape(-1), list(np.nonzero(b.reshape(-1) == 50)[0]), keep)
 
 
+def check_chunked(o):
+    g = load_golden("chunked_example.txt")
+    m, npr = int(g["m"][0]), int(g["n_prompt"][0])
+    k = _embed_1d(g["k_cache"])[None]
+    q = np.stack([_embed_1d(g["q_chunk0"]), _embed_1d(g["q_chunk1"])])[:, None]     # [T][1][3][4]
+    ks = np.stack([_embed_1d(g["kself_chunk0"]), _embed_1d(g["kself_chunk1"])])[:, None]
+    np.testing.assert_allclose(o.chunked_scores(q, k, ks, 1, 1.0, m, npr)[0], g["scores"], rtol=1e-14)
+    rng = np.random.default_rng(47)
+    # brute force with loops: H = 2, G = 2, n = 7, m = 3 (chunks 3, 3, 1)
+    H, G, n, m, npr, d, sc = 2, 2, 7, 3, 2, 3, 0.8
+    T, nin_max = 3, npr + m
+    q = rng.standard_normal((T, H * G, nin_max, d))
+    k = rng.standard_normal((H, n, d))
+    ks = rng.standard_normal((T, H, nin_max, d))
+    ref = np.zeros((H, n))
+    for t in range(T):
+        mt = min(m, n - t * m)
+        nin = npr + mt
+        for hq in range(H * G):
+            h = hq // G
+            for i in range(nin):
+                lg = [sc * sum(q[t, hq, i, e] * k[h, t * m + j, e] for e in range(d)) for j in range(mt)]
+                own = [sc * sum(q[t, hq, i, e] * ks[t, h, j, e] for e in range(d)) for j in range(i + 1)]
+                mx = max(lg + own)
+                z = sum(math.exp(x - mx) for x in lg + own)
+                for j in range(mt):
+                    ref[h, t * m + j] = max(ref[h, t * m + j], math.exp(lg[j] - mx) / z)
+    got = o.chunked_scores(q, k, ks, G, sc, m, npr)
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
+    # a chunk's scores depend on its own inputs only; rows past a chunk's
+    # input (the last chunk's padding) are ignored; every weight is <= 1
+    q2, ks2 = q.copy(), ks.copy()
+    q2[0] += 1.0
+    ks2[0] -= 1.0
+    q2[2, :, npr + 1:] = 50.0
+    ks2[2, :, npr + 1:] = -3.0
+    got2 = o.chunked_scores(q2, k, ks2, G, sc, m, npr)
+    np.testing.assert_allclose(got2[:, m:], got[:, m:], rtol=1e-15)
+    assert not np.allclose(got2[:, :m], got[:, :m])
+    assert (got <= 1).all() and (got > 0).all()
+
+
 # ---------------------------------------------------------------- pool ----
 
 def check_maxpool(o):
@@ -632,4 +674,5 @@ ALL_CHECKS = [
     check_decode_hand_example, check_decode_bruteforce, check_decode_sdpa, check_decode_closed_forms,
     check_value_weight_l2, check_select_budgets_example, check_select_budgets_bruteforce,
     check_select_budgets_reductions, check_external_logit, check_head_scores_and_budgets,
+    check_chunked,
 ]

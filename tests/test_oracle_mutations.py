@@ -60,6 +60,11 @@ MUTANTS = {
     "head_scores_mean": ("    return scores.max(axis=-1)", "    return scores.mean(axis=-1)"),
     "head_budgets_ties_high": ("    top = topk_indices(flat, keep)", "    top = len(flat) - 1 - topk_indices(flat[::-1], keep)"),
     "head_budgets_drop_all": ("    b = np.full(flat.shape, W, np.int64)", "    b = np.full(flat.shape, 0, np.int64)"),
+    "chunked_self_not_causal": ("hidden[:, mt:] = np.triu(np.ones((nin, nin), bool), 1)", "hidden[:, mt:] = False"),
+    "chunked_self_excluded": ("hidden[:, mt:] = np.triu(np.ones((nin, nin), bool), 1)", "hidden[:, mt:] = True"),
+    "chunked_padding_rows": ("        nin = n_prompt + mt\n", "        nin = n_prompt + m\n"),
+    "chunked_offset": ("        c0 = t * m\n", "        c0 = min(t * m + 1, n - 1)\n"),
+    "chunked_no_scale": ("logits = scale * (q[t, h * G + g, :nin] @ keys.T)", "logits = (q[t, h * G + g, :nin] @ keys.T)"),
     "compact_wrong_head": ("return (np.stack([k[h, idx[h]] for h in range(H)]),", "return (np.stack([k[0, idx[h]] for h in range(H)]),"),
 }
 
