@@ -79,9 +79,13 @@ def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
     # the sample's pairs in order, repeated until `seconds` of CPU work
     while time.perf_counter() - t0 < seconds:
         l, h = pairs[units % len(pairs)]
-        q = synth.bf16_to_f64(host["q"][l][h * wl.G:(h + 1) * wl.G])
+        q = None if wl.chunk else synth.bf16_to_f64(host["q"][l][h * wl.G:(h + 1) * wl.G])
         k = synth.bf16_to_f64(host["k"][l][h:h + 1])
-        if wl.q_mode == "window":
+        if wl.chunk:
+            qc = synth.bf16_to_f64(host["q"][l][:, h * wl.G:(h + 1) * wl.G])
+            ks = synth.bf16_to_f64(host["kself"][l][:, h:h + 1])
+            raw = oracle.chunked_scores(qc, k, ks, wl.G, wl.scale, wl.chunk, wl.n_prompt)
+        elif wl.q_mode == "window":
             raw = oracle.window_raw_scores(q, k, wl.G, wl.scale, wl.agg)
         else:
             raw = (oracle.external_logit_scores(q, k, wl.G, wl.scale) if wl.agg == "logit"
@@ -161,9 +165,12 @@ def main():
         return
     wl = synth.WORKLOADS[args.workload]
     which = ("q", "k", "v", "w_o") if wl.value_weight else ("q", "k", "v")
-    cache_bytes = wl.L * wl.H_kv * wl.n * wl.d * 2 * 2
+    if wl.chunk:
+        which = which + ("kself",)
+    input_bytes = sum(wl.L * int(np.prod(wl.shape(name))) * 2 for name in which
+                      if name != "w_o" or wl.value_weight)
     t0 = time.time()
-    if args.device_inputs or cache_bytes > (4 << 30):
+    if args.device_inputs or input_bytes > (4 << 30):
         log(f"[bench] drawing {wl.name} on the GPU (seed {args.seed})")
         t = synth.gen_all_device(wl, args.seed, which, dev)
         host = None
@@ -183,8 +190,9 @@ def main():
     weight = (torch.empty((wl.L, wl.H_kv, wl.n_cand), dtype=torch.float32, device=dev)
               if wl.value_weight else None)
     ws_s = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-    _, _ = kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
-                          scores=scores)  # sizes the workspace once
+    if not wl.chunk:
+        _, _ = kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
+                              scores=scores)  # sizes the workspace once
     ev = lambda: torch.cuda.Event(enable_timing=True)
     l2 = wl.value_weight and wl.value_norm == "l2"
     factor, ms_factor = None, None
@@ -215,11 +223,18 @@ def main():
         head_sc = torch.empty((wl.L, wl.H_kv), dtype=torch.float32, device=dev)
         budgets = torch.empty((wl.L, wl.H_kv), dtype=torch.int32, device=dev)
 
+    def score():
+        if wl.chunk:
+            kv.kvsel_score_chunked(q, k, t["kself"], G=wl.G, m=wl.chunk, n_prompt=wl.n_prompt,
+                                   scale=wl.scale, pool=wl.pool, scores=scores)
+        else:
+            kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
+                           scores=scores)
+
     def step(marks=None):
         if marks is not None:
             marks[0].record()
-        kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
-                       scores=scores)
+        score()
         if marks is not None:
             marks[1].record()
         if keep:
@@ -272,6 +287,9 @@ def main():
     # pooled scores written once
     score_bytes = (wl.L * wl.H_kv * wl.n * wl.d * 2 + wl.L * wl.H_q * wl.W * wl.d * 2
                    + wl.L * wl.H_kv * wl.n_cand * 4)
+    if wl.chunk:   # every chunk's queries and own keys
+        score_bytes = (wl.L * wl.H_kv * wl.n * wl.d * 2 + wl.L * wl.T * (wl.H_q + wl.H_kv) * wl.n_in * wl.d * 2
+                       + wl.L * wl.H_kv * wl.n_cand * 4)
     achieved = score_bytes / (ms_score * 1e-3) / 1e9
     sha = source_sha(SCORE_SOURCES)
     traffic = traffic_from_profiles(f"kvsel_score:{wl.name}", sha)
@@ -291,6 +309,7 @@ def main():
         "config": {"workload": wl.name, "L": wl.L, "H_kv": wl.H_kv, "G": wl.G, "d": wl.d,
                    "n": wl.n, "W": wl.W, "q_mode": wl.q_mode, "agg": wl.agg, "pool": wl.pool,
                    "budget": wl.budget, "adaptive": wl.adaptive,
+                   **({"chunk": wl.chunk, "n_prompt": wl.n_prompt} if wl.chunk else {}),
                    **({"budget_vector": True, "layer_stride": stride} if wl.budget_vector else {}),
                    **({"head_keep": wl.head_keep, "heads_kept": keep, "layer_stride": stride}
                       if keep else {}),
@@ -321,6 +340,11 @@ def main():
     # take longer at peak than its bytes
     passes = 1 if wl.agg == "logit" else 2
     sc_flops = passes * 2.0 * wl.L * wl.H_q * wl.W * wl.n * wl.d
+    if wl.chunk:
+        # per (layer, chunk, KV head): pass 1 over the chunk's m cached keys
+        # and the n_in own keys, pass 2 over the m cached keys (own keys as
+        # whole tiles, the MFMA work issued)
+        sc_flops = 2.0 * wl.L * wl.T * wl.H_q * wl.n_in * wl.d * (2 * wl.chunk + wl.n_in)
     if sc_flops / (MFMA_BF16_PEAK_TFS * 1e12) > score_bytes / (HBM_PEAK_GBS * 1e9):
         tfs = sc_flops / (ms_score * 1e-3) / 1e12
         calls.append((ms_score, {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,

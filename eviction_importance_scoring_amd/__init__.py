@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = [
-    "lib", "library_path", "KvselError", "kvsel_score", "kvsel_value_weight",
+    "lib", "library_path", "KvselError", "kvsel_score", "kvsel_score_chunked", "kvsel_value_weight",
     "kvsel_value_l2_factor", "kvsel_value_weight_l2",
     "kvsel_select", "kvsel_select_budgets", "kvsel_head_score", "kvsel_head_budgets",
     "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
@@ -40,6 +40,9 @@ _SIGNATURES = {
     "kvsel_score": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                     _c_i32, _c_i32, _c_f32, _c_i32, _c_void_p, _c_void_p, _c_void_p,
                     _c_size_p, _c_void_p],
+    "kvsel_score_chunked": [_c_void_p, _c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32,
+                            _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_void_p, _c_void_p,
+                            _c_void_p, _c_size_p, _c_void_p],
     "kvsel_value_weight": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_void_p, _c_void_p],
     "kvsel_value_l2_factor": [_c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
@@ -157,6 +160,38 @@ def kvsel_score(q, k, *, G: int, q_mode: int = Q_WINDOW, agg: int = AGG_SUM,
     nbytes = ctypes.c_size_t(ws.numel())
     _check(f(_ptr(q), _ptr(k), *args, _ptr(scores), _ptr(raw), _ptr(ws), ctypes.byref(nbytes),
              _stream(dev)))
+    return scores, raw
+
+
+def kvsel_score_chunked(q, k, k_self, *, G: int, m: int, n_prompt: int,
+                        scale: float | None = None, pool: int = 1, return_raw: bool = False,
+                        scores=None, raw=None, workspace=None):
+    """KVzip chunked scores [L][H_kv][n] (and raw). q bf16 [L][T][H_kv*G][n_in][d],
+    k bf16 [L][H_kv][n][d], k_self bf16 [L][T][H_kv][n_in][d], n_in = n_prompt + m."""
+    _need(q, torch.bfloat16, "q", 5)
+    _need(k, torch.bfloat16, "k", 4)
+    _need(k_self, torch.bfloat16, "k_self", 5)
+    L, H, n, d = k.shape
+    me = min(m, n)
+    T, n_in = (n + me - 1) // me, n_prompt + me
+    if tuple(q.shape) != (L, T, H * G, n_in, d) or tuple(k_self.shape) != (L, T, H, n_in, d):
+        raise ValueError(f"chunked shapes: q {tuple(q.shape)}, k_self {tuple(k_self.shape)}; "
+                         f"expected {(L, T, H * G, n_in, d)} and {(L, T, H, n_in, d)}")
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    dev = k.device
+    if scores is None:
+        scores = torch.empty((L, H, n), dtype=torch.float32, device=dev)
+    if return_raw and raw is None:
+        raw = torch.empty((L, H, n), dtype=torch.float32, device=dev)
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_score_chunked
+    args = (L, H, G, d, n, m, n_prompt, float(scale), pool)
+    _check(f(None, None, None, *args, None, _ptr(raw), None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(q), _ptr(k), _ptr(k_self), *args, _ptr(scores), _ptr(raw), _ptr(ws),
+             ctypes.byref(nbytes), _stream(dev)))
     return scores, raw
 
 

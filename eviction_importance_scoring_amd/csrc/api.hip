@@ -10,6 +10,9 @@
 namespace kvsel {
 hipError_t score_launch(const ScorePlan& p, const void* q, const void* k, float* scores,
                         float* raw, void* ws, size_t ws_bytes, hipStream_t st);
+hipError_t score_chunked_launch(const ScorePlan& p, const void* q, const void* k,
+                                const void* k_self, float* scores, float* raw, void* ws,
+                                hipStream_t st);
 size_t score_ws_bytes(const ScorePlan& p);
 bool select_groups_ok(int groups);
 }  // namespace kvsel
@@ -81,6 +84,50 @@ int32_t kvsel_score(const void* q, const void* k, int32_t L, int32_t H_kv, int32
   if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
   const hipError_t e = score_launch(p, q, k, scores, raw, ws, *ws_bytes,
                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_score_chunked(const void* q, const void* k, const void* k_self, int32_t L,
+                            int32_t H_kv, int32_t G, int32_t d, int32_t n, int32_t m,
+                            int32_t n_prompt, float scale, int32_t pool, float* scores, float* raw,
+                            void* ws, size_t* ws_bytes, void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || G < 1 || d < 1 || n < 1 || m < 1 || n_prompt < 0) return KVSEL_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return KVSEL_ERR_ARG;
+  if (pool < 1 || pool % 2 == 0) return KVSEL_ERR_ARG;
+  if (d != kHeadDimPublic || pool > 65) return KVSEL_ERR_UNSUPPORTED;
+  const int64_t m_eff = m < n ? m : n;          // one chunk holds at most the whole cache
+  const int64_t n_in = (int64_t)n_prompt + m_eff;
+  const int64_t T = ((int64_t)n + m_eff - 1) / m_eff;
+  const int64_t R = (int64_t)G * n_in;
+  if (R > kMaxIndex || (int64_t)H_kv * n > kMaxIndex || L * T * H_kv > kMaxIndex)
+    return KVSEL_ERR_UNSUPPORTED;
+  // one head's keys, query rows and own keys each span < 2^31 bytes
+  if ((int64_t)n * kRowBytesPublic > kMaxIndex || R * kRowBytesPublic > kMaxIndex)
+    return KVSEL_ERR_UNSUPPORTED;
+  ScorePlan p;
+  p.L = L; p.H = H_kv; p.G = G; p.n = n; p.W = (int)n_in;
+  p.R = (int)R;
+  p.causal = false;
+  p.n_cand = n;
+  p.pool = pool;
+  p.max_agg = true;
+  p.need_raw_tmp = raw == nullptr;
+  p.scale = scale;
+  p.chunk_m = (int)m_eff;
+  p.n_prompt = n_prompt;
+  const size_t need = score_ws_bytes(p);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!q || !k || !k_self || !scores) return KVSEL_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(k_self) || !aligned16(scores) ||
+      !aligned16(ws) || (raw && !aligned16(raw)))
+    return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  const hipError_t e = score_chunked_launch(p, q, k, k_self, scores, raw, ws,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 

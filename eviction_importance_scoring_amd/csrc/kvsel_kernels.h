@@ -19,19 +19,23 @@ struct ScorePlan {
   bool causal;            // window mode
   bool max_agg;
   bool logit = false;     // max of the scaled logits, no softmax (external only)
+  int chunk_m = 0;        // chunked scoring: cached keys per chunk (0: not chunked)
+  int n_prompt = 0;       // chunked scoring: prompt tokens before each chunk
   bool need_raw_tmp;      // caller passed raw == NULL
   float scale;
 };
 
 struct TwoPassLayout {
   int row_blocks, splits, keys_per_split;
+  int sp_stride;          // statistics slots per row (splits, or 2 when chunked)
+  int Lv;                 // grid layers: L, or L * chunks
   size_t part_off, stat_off, raw_off, bytes;
 };
 
 void twopass_plan(const ScorePlan& p, TwoPassLayout* o);
 hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void* q,
-                          const void* k, float* scores, float* raw, void* ws,
-                          hipStream_t st);
+                          const void* k, const void* k_self, float* scores, float* raw,
+                          void* ws, hipStream_t st);
 
 struct WindowLayout {
   int kpb, blocks;          // keys per workgroup, workgroups per head

@@ -23,6 +23,7 @@ size_t score_ws_bytes(const ScorePlan& p) {
 
 hipError_t score_launch(const ScorePlan& p, const void* q, const void* k, float* scores,
                         float* raw, void* ws, size_t, hipStream_t st) {
+  if (p.chunk_m > 0) return hipErrorInvalidValue;   // chunked: score_chunked_launch
   if (window_applicable(p)) {
     WindowLayout w;
     window_plan(p, &w);
@@ -30,7 +31,16 @@ hipError_t score_launch(const ScorePlan& p, const void* q, const void* k, float*
   }
   TwoPassLayout t;
   twopass_plan(p, &t);
-  return twopass_launch(p, t, q, k, scores, raw, ws, st);
+  return twopass_launch(p, t, q, k, nullptr, scores, raw, ws, st);
+}
+
+// KVzip's chunked scoring always runs on the general kernels.
+hipError_t score_chunked_launch(const ScorePlan& p, const void* q, const void* k,
+                                const void* k_self, float* scores, float* raw, void* ws,
+                                hipStream_t st) {
+  TwoPassLayout t;
+  twopass_plan(p, &t);
+  return twopass_launch(p, t, q, k, k_self, scores, raw, ws, st);
 }
 
 }  // namespace kvsel

@@ -11,6 +11,13 @@
 //   pool    max over +-pool/2 neighbours inside the candidate range.
 // KVzip-logit ([KVzip] §6.5, no softmax): pass 2 alone, every c_r = 0 and
 // no exponential: per key j, scale * max_r <q_r, k_j>.
+// Chunked scoring ([KVzip] §3.4): a "layer" of the grid is a (layer,
+// chunk) pair whose keys are the chunk's m cached keys (a KeyMap says where
+// they sit in the cache). Pass 1 runs twice into two statistics slots per
+// row: over the chunk's cached keys, and causally over the input's own
+// keys (the window rule with n = W = n_in); the combine merges both and
+// gives the rows past a short last chunk's input -inf; pass 2 maxes over
+// the chunk's cached keys.
 // Both passes are dense Q K^T contractions on MFMA (32x32x16 bf16, fp32
 // accumulation) built for operand reuse:
 //   pass 1: a workgroup of 8 waves owns 512 rows (a wave: 64 rows, two MFMA
@@ -36,6 +43,21 @@ namespace kvsel {
 constexpr int gSlotBytes = gRowsBytes + gTile * 4;             // pass 2: rows + normalisers
 constexpr float gNegBig = -1.0e30f;
 
+// The keys of grid layer lv (layer lv / T, chunk lv % T) and head h: rows
+// [row0, row0 + nk) of a [L][H][n_total][d] array, chunk t holding keys
+// [t*m, t*m + m) of its (layer, head) (the last chunk may be shorter).
+// Unchunked: T = 1, m = n_total.
+struct KeyMap {
+  int T, m, n_total;
+};
+
+__device__ __forceinline__ void key_span(const KeyMap& km, int lv, int H, int h, size_t& row0,
+                                         int& nk) {
+  const int l = lv / km.T, t = lv - l * km.T;
+  row0 = ((size_t)l * H + h) * km.n_total + (size_t)t * km.m;
+  nk = min(km.m, km.n_total - t * km.m);
+}
+
 // ---------------------------------------------------------------- pass 1 ----
 // 1-D grid of row_blocks * splits * H * L workgroups, block 512.
 // part[lh][sp][row] = (m, l) of the row over split sp's keys.
@@ -52,11 +74,12 @@ constexpr float gNegBig = -1.0e30f;
 // kept sums stay far below fp32's limit (at most n * 2^64).
 constexpr float kHeadroomPow2 = 1.8446744e19f;   // 2^64
 
+// part[lh][sp_off + sp] (of sp_stride slots per row block) for split sp.
 template <bool CAUSAL>
 __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
                                                    const __bf16* __restrict__ k, int H, int R,
-                                                   int W, int n, float alpha, int row_blocks,
-                                                   int splits, int kps,
+                                                   int W, KeyMap km, float alpha, int row_blocks,
+                                                   int splits, int kps, int sp_off, int sp_stride,
                                                    float2* __restrict__ part) {
   __shared__ __align__(16) unsigned char ring[gSlots][gTile * kRowBytes];
   int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -68,8 +91,25 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
   const size_t lh = (size_t)l * H + h;
-  const __bf16* kh = k + lh * (size_t)n * kHeadDim;
-  const int j0 = sp * kps, j1 = min(n, j0 + kps);
+  size_t krow0;
+  int n;
+  key_span(km, l, H, h, krow0, n);
+  const __bf16* kh = k + krow0 * kHeadDim;
+  // causal: no row of this workgroup sees past its largest r % W, so the
+  // keys after it are skipped (the window rule's rows are [G][W]; a chunk's
+  // own keys have n = W, where this halves the work)
+  int vis_end = n;
+  if (CAUSAL) {
+    const int r0 = rb * gBlock, r1 = min(R, r0 + gBlock);
+    const int top = (r1 - 1) / W != r0 / W ? W - 1 : (r1 - 1) % W;
+    vis_end = n - W + top + 1;
+  }
+  const int j0 = sp * kps, j1 = min(min(n, vis_end), j0 + kps);
+  if (j1 <= j0) {   // a split past every visible key: neutral statistics
+    const int row = rb * gBlock + threadIdx.x;
+    if (row < R) part[(lh * sp_stride + sp_off + sp) * (size_t)R + row] = make_float2(gNegBig, 0.f);
+    return;         // every wave returns here: no barrier is left waiting
+  }
   const int ntiles = (j1 - j0 + gTile - 1) / gTile;
 
   const int row0 = rb * gBlock + wave * 64;
@@ -228,7 +268,8 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     const float m2 = __shfl_xor(m[nt], 32), s2 = __shfl_xor(s[nt], 32);
     lse_merge(m[nt], s[nt], m2, s2);
     const int row = row0 + nt * 32 + col;
-    if (hf == 0 && row < R) part[(lh * splits + sp) * (size_t)R + row] = make_float2(m[nt], s[nt]);
+    if (hf == 0 && row < R)
+      part[(lh * sp_stride + sp_off + sp) * (size_t)R + row] = make_float2(m[nt], s[nt]);
   }
 }
 
@@ -251,15 +292,23 @@ __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part
 
 // Pass 2's form of the normaliser: -c_r / alpha in rows of Rpad (a multiple
 // of the tile), padding rows -inf so they drop out of every aggregate.
+// Chunked (T > 0): rows are [G][n_in] per head, and row i of a g block is
+// padding past the chunk's input of n_prompt + m_t tokens.
 __global__ __launch_bounds__(256) void k_combine_neg(const float2* __restrict__ part,
                                                      int H, int R, int Rpad, int splits,
-                                                     float inv_alpha,
+                                                     float inv_alpha, int T, int n_in,
+                                                     int n_prompt, KeyMap km,
                                                      float* __restrict__ stat) {
   const int r = blockIdx.x * 256 + threadIdx.x;
   const int h = blockIdx.y, l = blockIdx.z;
   if (r >= Rpad) return;
   const size_t lh = (size_t)l * H + h;
-  if (r >= R) {
+  bool pad = r >= R;
+  if (T > 0 && !pad) {
+    const int t = l % T;
+    pad = r % n_in >= n_prompt + min(km.m, km.n_total - t * km.m);
+  }
+  if (pad) {
     stat[lh * Rpad + r] = neg_inf();
     return;
   }
@@ -287,7 +336,7 @@ __global__ __launch_bounds__(256) void k_logit_stat(int R, int Rpad, float* __re
 template <bool CAUSAL, bool MAXAGG, bool LOGIT = false>
 __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q,
                                                     const __bf16* __restrict__ k, int H, int R,
-                                                    int W, int n, float alpha, int key_blocks,
+                                                    int W, KeyMap km, float alpha, int key_blocks,
                                                     const float* __restrict__ stat,
                                                     float* __restrict__ raw) {
   // one LDS object: slot = 64 Q rows, then their 64 normalisers (with two
@@ -303,6 +352,9 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
   const __bf16* qh = q + lh * (size_t)R * kHeadDim;
   const int ntiles = (R + gTile - 1) / gTile;
   const float* sh = stat + lh * (size_t)ntiles * gTile;
+  size_t krow0;
+  int n;
+  key_span(km, l, H, h, krow0, n);
 
   // this wave's 64 keys: MFMA B operands for the whole kernel
   const int key0 = kb * gBlock + wave * 64;
@@ -310,7 +362,7 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int key = key0 + nt * 32 + col;
-    if (key < n) load_half_row(k + (lh * n + key) * (size_t)kHeadDim, hf, kop[nt]);
+    if (key < n) load_half_row(k + (krow0 + key) * (size_t)kHeadDim, hf, kop[nt]);
     else zero_ops(kop[nt]);
   }
   // a row tile: the Q rows (all waves) and their -c_r / alpha (wave 0)
@@ -444,7 +496,7 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
     const float tot = LOGIT ? __builtin_fmaxf(agg[nt], o) * alpha
                     : MAXAGG ? fast_exp2(__builtin_fmaxf(agg[nt], o) * alpha) : agg[nt] + o;
     const int key = key0 + nt * 32 + col;
-    if (hf == 0 && key < n) raw[lh * n + key] = tot;
+    if (hf == 0 && key < n) raw[krow0 + key] = tot;
   }
 }
 
@@ -488,30 +540,44 @@ hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r,
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 void twopass_plan(const ScorePlan& p, TwoPassLayout* o) {
+  const int Lv = p.chunk_m > 0 ? p.L * ((p.n + p.chunk_m - 1) / p.chunk_m) : p.L;
   const int row_blocks = (p.R + gBlock - 1) / gBlock;
-  const long long base = (long long)row_blocks * p.H * p.L;
-  // split the keys only when the row blocks alone cannot fill the GPU
-  int splits = (int)((1024 + base - 1) / base);
-  const int max_splits = (p.n + 4 * gTile - 1) / (4 * gTile);
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int kps = (p.n + splits - 1) / splits;
-  kps = (kps + gTile - 1) / gTile * gTile;
-  splits = (p.n + kps - 1) / kps;
+  int splits, kps, stride;
+  if (p.chunk_m > 0) {
+    // chunked: (layer, chunk) pairs fill the GPU; one split over the chunk's
+    // cached keys and one over the input's own keys
+    splits = 1;
+    kps = (p.chunk_m + gTile - 1) / gTile * gTile;
+    stride = 2;
+  } else {
+    const long long base = (long long)row_blocks * p.H * p.L;
+    // split the keys only when the row blocks alone cannot fill the GPU
+    splits = (int)((1024 + base - 1) / base);
+    const int max_splits = (p.n + 4 * gTile - 1) / (4 * gTile);
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    kps = (p.n + splits - 1) / splits;
+    kps = (kps + gTile - 1) / gTile * gTile;
+    splits = (p.n + kps - 1) / kps;
+    stride = splits;
+  }
   o->row_blocks = row_blocks;
   o->splits = splits;
+  o->sp_stride = stride;
   o->keys_per_split = kps;
-  const size_t LH = (size_t)p.L * p.H;
+  o->Lv = Lv;
+  const size_t LHv = (size_t)Lv * p.H;
   o->part_off = 0;
   const size_t Rpad = (size_t)(p.R + gTile - 1) / gTile * gTile;
-  o->stat_off = p.logit ? 0 : align256(LH * splits * p.R * sizeof(float2));   // no pass 1
-  o->raw_off = o->stat_off + align256(LH * Rpad * sizeof(float));
-  o->bytes = o->raw_off + (p.need_raw_tmp ? align256(LH * p.n * sizeof(float)) : 0);
+  o->stat_off = p.logit ? 0 : align256(LHv * stride * p.R * sizeof(float2));   // no pass 1
+  o->raw_off = o->stat_off + align256(LHv * Rpad * sizeof(float));
+  o->bytes = o->raw_off +
+             (p.need_raw_tmp ? align256((size_t)p.L * p.H * p.n * sizeof(float)) : 0);
 }
 
 hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void* q,
-                          const void* k, float* scores, float* raw, void* ws,
-                          hipStream_t st) {
+                          const void* k, const void* k_self, float* scores, float* raw,
+                          void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   float2* part = reinterpret_cast<float2*>(w + o.part_off);
   float* stat = reinterpret_cast<float*>(w + o.stat_off);
@@ -519,43 +585,60 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
   const __bf16* qb = static_cast<const __bf16*>(q);
   const __bf16* kb = static_cast<const __bf16*>(k);
   const float alpha = p.scale * kLog2e;
-  const long long g1 = (long long)o.row_blocks * o.splits * p.H * p.L;
-  const int key_blocks = (p.n + gBlock - 1) / gBlock;
-  const long long g2 = (long long)key_blocks * p.H * p.L;
+  const bool chunked = p.chunk_m > 0;
+  const int T = chunked ? (p.n + p.chunk_m - 1) / p.chunk_m : 1;
+  const KeyMap km{T, chunked ? p.chunk_m : p.n, p.n};
+  const int kmax = km.m;                      // keys a grid layer holds at most
+  const long long g1 = (long long)o.row_blocks * o.splits * p.H * o.Lv;
+  const int key_blocks = (kmax + gBlock - 1) / gBlock;
+  const long long g2 = (long long)key_blocks * p.H * o.Lv;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int Rpad = (p.R + gTile - 1) / gTile * gTile;
   if (p.logit) {
-    const int Rp = (p.R + gTile - 1) / gTile * gTile;
-    hipLaunchKernelGGL(k_logit_stat, dim3((Rp + 255) / 256, p.H, p.L), dim3(256), 0, st, p.R, Rp,
-                       stat);
+    hipLaunchKernelGGL(k_logit_stat, dim3((Rpad + 255) / 256, p.H, o.Lv), dim3(256), 0, st, p.R,
+                       Rpad, stat);
     hipLaunchKernelGGL((k_gen_colagg<false, true, true>), dim3((unsigned)g2), dim3(512), 0, st, qb,
-                       kb, p.H, p.R, p.W, p.n, p.scale, key_blocks, stat, rawbuf);
+                       kb, p.H, p.R, p.W, km, p.scale, key_blocks, stat, rawbuf);
     (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
     return hipGetLastError();
   }
   if (p.causal)
     hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
-                       p.R, p.W, p.n, alpha, o.row_blocks, o.splits, o.keys_per_split, part);
+                       p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
+                       o.sp_stride, part);
   else
     hipLaunchKernelGGL(k_gen_stats<false>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
-                       p.R, p.W, p.n, alpha, o.row_blocks, o.splits, o.keys_per_split, part);
-  const int Rpad = (p.R + gTile - 1) / gTile * gTile;
-  hipLaunchKernelGGL(k_combine_neg, dim3((Rpad + 255) / 256, p.H, p.L), dim3(256), 0, st, part,
-                     p.H, p.R, Rpad, o.splits, 1.0f / alpha, stat);
+                       p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
+                       o.sp_stride, part);
+  int n_in = 0;
+  if (chunked) {
+    // the input's own keys, causally: the window rule with n = W = n_in
+    // (rows are [G][n_in], row r sees own keys 0 .. r % n_in)
+    n_in = p.n_prompt + p.chunk_m;
+    const KeyMap kms{1, n_in, n_in};
+    const int kps_self = (n_in + gTile - 1) / gTile * gTile;
+    hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb,
+                       static_cast<const __bf16*>(k_self), p.H, p.R, n_in, kms, alpha,
+                       o.row_blocks, 1, kps_self, 1, o.sp_stride, part);
+  }
+  hipLaunchKernelGGL(k_combine_neg, dim3((Rpad + 255) / 256, p.H, o.Lv), dim3(256), 0, st, part,
+                     p.H, p.R, Rpad, o.sp_stride, 1.0f / alpha, chunked ? T : 0, n_in, p.n_prompt,
+                     km, stat);
   const dim3 grid2((unsigned)g2);
   if (p.causal) {
     if (p.max_agg)
       hipLaunchKernelGGL((k_gen_colagg<true, true>), grid2, dim3(512), 0, st, qb, kb, p.H, p.R,
-                         p.W, p.n, alpha, key_blocks, stat, rawbuf);
+                         p.W, km, alpha, key_blocks, stat, rawbuf);
     else
       hipLaunchKernelGGL((k_gen_colagg<true, false>), grid2, dim3(512), 0, st, qb, kb, p.H,
-                         p.R, p.W, p.n, alpha, key_blocks, stat, rawbuf);
+                         p.R, p.W, km, alpha, key_blocks, stat, rawbuf);
   } else {
     if (p.max_agg)
       hipLaunchKernelGGL((k_gen_colagg<false, true>), grid2, dim3(512), 0, st, qb, kb, p.H,
-                         p.R, p.W, p.n, alpha, key_blocks, stat, rawbuf);
+                         p.R, p.W, km, alpha, key_blocks, stat, rawbuf);
     else
       hipLaunchKernelGGL((k_gen_colagg<false, false>), grid2, dim3(512), 0, st, qb, kb, p.H,
-                         p.R, p.W, p.n, alpha, key_blocks, stat, rawbuf);
+                         p.R, p.W, km, alpha, key_blocks, stat, rawbuf);
   }
   (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
   return hipGetLastError();

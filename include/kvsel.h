@@ -20,8 +20,9 @@
  *    synchronised. No call allocates device memory or synchronises.
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
- *  - Workspace protocol (kvsel_score, kvsel_select, kvsel_select_budgets,
- *    kvsel_head_budgets, kvsel_decode_attention): with ws == NULL the
+ *  - Workspace protocol (kvsel_score, kvsel_score_chunked, kvsel_select,
+ *    kvsel_select_budgets, kvsel_head_budgets, kvsel_decode_attention): with
+ *    ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
  *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
  *    Workspace contents need no initialisation and are scratch afterwards.
@@ -105,6 +106,37 @@ int32_t kvsel_score(const void* q, const void* k,
                     int32_t W, int32_t q_mode, int32_t agg, float scale,
                     int32_t pool, float* scores, float* raw,
                     void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_score_chunked -- KVzip's chunked scoring with the input's own keys.
+ *
+ * [KVzip] §3.4: the n cached keys of each (layer, head) are split into
+ * T = ceil(n/m) chunks of m (the last one m_T = n - (T-1)*m long). Chunk t
+ * is reconstructed from an input of n_in_t = n_prompt + m_t tokens whose
+ * queries attend over the chunk's cached keys (all visible) and the
+ * input's own keys (causal: input position i sees own keys 0..i):
+ *   A = softmax_j(scale * <q[l][t][hq][i], [k_chunk ; k_self][j]>)
+ * and the chunk's keys score max over g < G and i < n_in_t of the cached
+ * part of A, then max-pooling of width `pool` over all n positions as in
+ * kvsel_score. Inputs hold every chunk at the full n_in = n_prompt + m:
+ *
+ *   q      bf16 [L][T][H_kv*G][n_in][d]  chunk t's queries (rows past n_in_t
+ *                                        are ignored)
+ *   k      bf16 [L][H_kv][n][d]          the cache
+ *   k_self bf16 [L][T][H_kv][n_in][d]    chunk t's own keys (rows past n_in_t
+ *                                        are ignored)
+ *   scores f32  [L][H_kv][n]             pooled
+ *   raw    f32  [L][H_kv][n]             optional (NULL): before pooling
+ *
+ * m larger than n is taken as n (one chunk). Limits: d == 128;
+ * G*n_in*d*2 and n*d*2 each below 2^31 bytes; pool odd <= 65. Needs a
+ * workspace (protocol above).
+ */
+int32_t kvsel_score_chunked(const void* q, const void* k, const void* k_self,
+                            int32_t L, int32_t H_kv, int32_t G, int32_t d,
+                            int32_t n, int32_t m, int32_t n_prompt, float scale,
+                            int32_t pool, float* scores, float* raw,
+                            void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * kvsel_value_weight -- CriticalKV's projected-value norm.

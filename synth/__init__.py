@@ -68,6 +68,8 @@ class Workload:
     adaptive: bool = False       # one budget per layer shared by all heads
     budget_vector: bool = False  # one budget per (layer, head), from gen_budgets
     head_keep: float = 0.0       # > 0: head-level eviction keeping this fraction of heads
+    chunk: int = 0               # > 0: KVzip chunked scoring, cached keys per chunk
+    n_prompt: int = 0            # chunked scoring: repeat-prompt tokens before each chunk
     value_weight: bool = False   # value-norm weighted two-stage selection
     value_norm: str = "l1"       # norm of the projected value: 'l1' or 'l2'
     D: int = 0                   # model width for w_o
@@ -80,6 +82,30 @@ class Workload:
     @property
     def H_q(self) -> int:
         return self.H_kv * self.G
+
+    @property
+    def T(self) -> int:
+        """Chunks per layer (chunked scoring)."""
+        return (self.n + self.chunk - 1) // self.chunk if self.chunk else 1
+
+    @property
+    def n_in(self) -> int:
+        """Input tokens per chunk (chunked scoring)."""
+        return self.n_prompt + min(self.chunk, self.n)
+
+    def shape(self, tensor: str) -> tuple:
+        """Per-layer shape of an input tensor."""
+        if tensor == "q":
+            if self.chunk:
+                return (self.T, self.H_q, self.n_in, self.d)
+            return (self.H_q, self.W, self.d)
+        if tensor == "kself":
+            return (self.T, self.H_kv, self.n_in, self.d)
+        if tensor in ("k", "v"):
+            return (self.H_kv, self.n, self.d)
+        if tensor == "w_o":
+            return (self.D, self.H_q * self.d)
+        raise ValueError(tensor)
 
     @property
     def n_cand(self) -> int:
@@ -142,6 +168,12 @@ WORKLOADS = {
         Workload("kvzip_logit_qwen7b_n32k", L=28, H_kv=4, G=7, d=128, n=32768,
                  W=4096, q_mode="external", agg="logit", pool=1, beta=0.25,
                  q_chunk=512),
+        # KVzip's chunked scoring: chunks of 2048 cached keys, each scored by
+        # a 32-token repeat prompt plus the chunk (own keys in the softmax);
+        # W = the 2080 queries of a chunk's input
+        Workload("kvzip_chunked_qwen7b_n32k", L=28, H_kv=4, G=7, d=128, n=32768,
+                 W=2080, q_mode="external", agg="max", pool=1, beta=0.25, chunk=2048,
+                 n_prompt=32),
         # many external queries, max aggregation, Qwen2.5-7B GQA shape
         Workload("kvzip_qwen7b_n32k", L=28, H_kv=4, G=7, d=128, n=32768,
                  W=4096, q_mode="external", agg="max", pool=1, beta=0.25,
@@ -149,7 +181,7 @@ WORKLOADS = {
     ]
 }
 
-_TENSOR = {"q": 1, "k": 2, "v": 3, "w_o": 4, "heavy": 5, "budgets": 6}
+_TENSOR = {"q": 1, "k": 2, "v": 3, "w_o": 4, "heavy": 5, "budgets": 6, "kself": 7}
 
 
 def _rng(seed: int, wl: Workload, tensor: str, layer: int) -> np.random.Generator:
@@ -180,8 +212,14 @@ def _heavy_factors(wl: Workload, rng: np.random.Generator) -> np.ndarray:
 
 def gen_q(wl: Workload, seed: int, layer: int) -> np.ndarray:
     r = _rng(seed, wl, "q", layer)
-    x = r.standard_normal((wl.H_q, wl.W, wl.d), dtype=np.float32)
+    x = r.standard_normal(wl.shape("q"), dtype=np.float32)
     return bf16_bits(x)
+
+
+def gen_kself(wl: Workload, seed: int, layer: int) -> np.ndarray:
+    """Chunked scoring: each chunk's own input keys, N(0, 1)."""
+    r = _rng(seed, wl, "kself", layer)
+    return bf16_bits(r.standard_normal(wl.shape("kself"), dtype=np.float32))
 
 
 def gen_k(wl: Workload, seed: int, layer: int) -> np.ndarray:
@@ -228,6 +266,8 @@ def gen_layer(wl: Workload, seed: int, layer: int, which=("q", "k", "v", "w_o"))
         out["v"] = gen_v(wl, seed, layer)
     if "w_o" in which and wl.value_weight:
         out["w_o"] = gen_w_o(wl, seed, layer)
+    if "kself" in which and wl.chunk:
+        out["kself"] = gen_kself(wl, seed, layer)
     return out
 
 
@@ -256,7 +296,9 @@ def gen_all_device(wl: Workload, seed: int, which=("q", "k", "v", "w_o"), device
         return t
 
     if "q" in which:
-        out["q"] = normal((wl.L, wl.H_q, wl.W, wl.d))
+        out["q"] = normal((wl.L, *wl.shape("q")))
+    if "kself" in which and wl.chunk:
+        out["kself"] = normal((wl.L, *wl.shape("kself")))
     if "k" in which:
         k = torch.empty((wl.L, wl.H_kv, wl.n, wl.d), dtype=torch.bfloat16, device=device)
         n_pool = wl.n - wl.W if wl.q_mode == "window" else wl.n

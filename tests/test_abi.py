@@ -314,3 +314,39 @@ def test_head_score_and_budgets_pointers(lib):
     assert f(p, 2, 8, 3, 100, 8, None, p, ctypes.byref(nb), None) == ARG
     small = ctypes.c_size_t(1)
     assert f(p, 2, 8, 3, 100, 8, p, p, ctypes.byref(small), None) == WS
+
+
+def _chunked(lib, **kw):
+    a = dict(L=2, H=4, G=7, d=128, n=32768, m=2048, npr=32, scale=0.088, pool=1)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    rc = lib.kvsel_score_chunked(None, None, None, a["L"], a["H"], a["G"], a["d"], a["n"], a["m"],
+                                 a["npr"], a["scale"], a["pool"], None, None, None,
+                                 ctypes.byref(nb), None)
+    return rc, nb.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(npr=0), OK), (dict(m=1), OK), (dict(m=100000), OK), (dict(pool=5), OK),
+    (dict(m=0), ARG), (dict(npr=-1), ARG), (dict(pool=2), ARG), (dict(scale=0.0), ARG),
+    (dict(L=0), ARG), (dict(d=64), UNSUP), (dict(pool=67), UNSUP),
+    (dict(G=64, m=32768, npr=100000), UNSUP),   # a head's query rows past 2^31 bytes
+])
+def test_score_chunked_ranges(lib, kw, code):
+    assert _chunked(lib, **kw)[0] == code
+
+
+def test_score_chunked_workspace(lib):
+    # m past n is one chunk: the same plan as m == n
+    assert _chunked(lib, n=5000, m=100000)[1] == _chunked(lib, n=5000, m=5000)[1]
+
+
+@no_gpu_only
+def test_score_chunked_pointers(lib):
+    p = ctypes.c_void_p(1 << 20)
+    nb = ctypes.c_size_t(1 << 30)
+    f = lib.kvsel_score_chunked
+    base = (2, 4, 7, 128, 32768, 2048, 32, 0.088, 1)
+    assert f(p, p, None, *base, p, None, p, ctypes.byref(nb), None) == ARG
+    assert f(None, p, p, *base, p, None, p, ctypes.byref(nb), None) == ARG
+    assert f(p, p, p, *base, None, None, p, ctypes.byref(nb), None) == ARG

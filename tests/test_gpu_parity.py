@@ -305,6 +305,43 @@ def test_logit_scores(case):
         assert_logits_close(s[l], refp, f"logit pooled l{l}")
 
 
+CHUNKED_CASES = [
+    # (L, H, G, n, m, n_prompt, pool)
+    (1, 2, 2, 1000, 256, 8, 1),       # 4 chunks, the last 232 keys
+    (2, 1, 7, 3000, 1024, 40, 3),     # pooled
+    (1, 1, 1, 100, 500, 0, 1),        # m past n: one chunk, no prompt
+    (1, 2, 4, 2048, 512, 100, 1),     # an exact multiple
+    (1, 1, 3, 700, 64, 200, 5),       # chunks shorter than the prompt
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED_CASES, ids=lambda c: "L{}H{}G{}n{}m{}p{}pool{}".format(*c))
+def test_score_chunked(case):
+    L, H, G, n, m, npr, pool = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    me = min(m, n)
+    T, n_in = (n + me - 1) // me, npr + me
+    q = rng.standard_normal((L, T, H * G, n_in, 128)).astype(np.float32)
+    ks = rng.standard_normal((L, T, H, n_in, 128)).astype(np.float32)
+    k = rng.standard_normal((L, H, n, 128)).astype(np.float32)
+    k[..., :8, :] *= 3.0          # a few heavy keys
+    last = npr + (n - (T - 1) * me)
+    q[:, T - 1, :, last:] = 30.0  # rows past the last chunk's input: ignored
+    ks[:, T - 1, :, last:] = -7.0
+    qb, kb, kb_self = synth.bf16_bits(q), synth.bf16_bits(k), synth.bf16_bits(ks)
+    scale = 1 / np.sqrt(128)
+    print(f"[gpu] kvsel_score_chunked case={case}", flush=True)
+    s, r = kv.kvsel_score_chunked(to_dev(qb), to_dev(kb), to_dev(kb_self), G=G, m=m, n_prompt=npr,
+                                  scale=scale, pool=pool, return_raw=True)
+    torch.cuda.synchronize()
+    s, r = s.cpu().numpy(), r.cpu().numpy()
+    for l in range(L):
+        ref = oracle.chunked_scores(synth.bf16_to_f64(qb[l]), synth.bf16_to_f64(kb[l]),
+                                    synth.bf16_to_f64(kb_self[l]), G, scale, me, npr)
+        assert_scores_close(r[l], ref, f"chunked raw l{l}")
+        assert_scores_close(s[l], oracle.maxpool(ref, n, pool), f"chunked pooled l{l}")
+
+
 SIGNED_CASES = [
     # (L, H, n, W, frac, adaptive, two_stage)
     (1, 3, 2000, 0, 0.3, False, False),

@@ -33,9 +33,8 @@ SEED = 0
 
 
 def device_inputs(wl: synth.Workload, sampled, which):
-    shapes = {"q": (wl.H_q, wl.W, wl.d), "k": (wl.H_kv, wl.n, wl.d),
-              "v": (wl.H_kv, wl.n, wl.d), "w_o": (wl.D, wl.H_q * wl.d)}
-    std = {"q": 1.0, "k": 1.0, "v": 1.0, "w_o": 0.02}
+    shapes = {name: wl.shape(name) for name in which}
+    std = {"q": 1.0, "k": 1.0, "v": 1.0, "w_o": 0.02, "kself": 1.0}
     g = torch.Generator(device="cuda")
     g.manual_seed(1234)
     dev, host = {}, {}
@@ -274,6 +273,28 @@ def test_criticalkv_full(name):
     assert ((st == 1).sum(axis=-1) == int(np.floor(wl.alpha * k))).all()
     assert ((st == 2).sum(axis=-1) == k - int(np.floor(wl.alpha * k))).all()
     _check_compact(dev, host, idx, offs, 0, wl)
+
+
+def test_kvzip_chunked_full():
+    wl = synth.WORKLOADS["kvzip_chunked_qwen7b_n32k"]
+    dev, host = device_inputs(wl, {0}, ("q", "k", "kself"))
+    print(f"[gpu] kvsel_score_chunked {wl.name}", flush=True)
+    s, r = kv.kvsel_score_chunked(dev["q"], dev["k"], dev["kself"], G=wl.G, m=wl.chunk,
+                                  n_prompt=wl.n_prompt, scale=wl.scale, pool=wl.pool,
+                                  return_raw=True)
+    torch.cuda.synchronize()
+    # oracle on one KV head of layer 0: 16 chunks of 2080 x 7 query rows
+    h = 1
+    q = synth.bf16_to_f64(host[("q", 0)][:, h * wl.G:(h + 1) * wl.G])
+    k = synth.bf16_to_f64(host[("k", 0)][h:h + 1])
+    ks = synth.bf16_to_f64(host[("kself", 0)][:, h:h + 1])
+    ref = oracle.chunked_scores(q, k, ks, wl.G, wl.scale, wl.chunk, wl.n_prompt)[0]
+    assert_scores_close(r[0, h].cpu().numpy()[None], ref[None], "chunked raw")
+    assert_scores_close(s[0, h].cpu().numpy()[None], ref[None], "chunked scores")
+    idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=0, budget=wl.budget, return_stage=True)
+    torch.cuda.synchronize()
+    _check_select_exact(wl, s, None, idx, offs, stage, [0, wl.L - 1])
+    assert_topk_within_band(idx[0, h].cpu().numpy(), ref, wl.budget, "chunked select")
 
 
 @pytest.mark.parametrize("name", ["kvzip_qwen7b_n32k", "kvzip_logit_qwen7b_n32k"])
