@@ -409,6 +409,67 @@ def select_budgets(scores: np.ndarray, budgets, W: int, n: int,
     return np.concatenate(idx_parts), np.asarray(offs, np.int64), np.concatenate(st_parts)
 
 
+def anchor_select(pooled: np.ndarray, rand: np.ndarray, n: int, W: int, k: int,
+                  rho: float) -> np.ndarray:
+    """AnchorKV's anchor positions of one layer.
+
+    [AnchorKV, §3.2, anchor selection]: each KV head keeps k anchors. The
+    W most recent positions are always anchors and count toward k; of the
+    remaining k - W slots a fraction rho goes to the best positions by the
+    pooled SnapKV score, the rest to positions drawn uniformly at random
+    from the context. Readings: floor(rho * (k - W)) slots by score (ties to
+    the lower position); the random ones are drawn without replacement from
+    the candidates not already taken, as the largest of per-position uniform
+    draws `rand` (the draws are an input: equal draws to the lower position).
+
+    pooled, rand: [H][n - W]. Returns anchors [H][k]: ascending positions.
+    """
+    H, n_cand = pooled.shape
+    assert n_cand == n - W and W <= k <= n
+    k1 = int(np.floor(rho * (k - W)))
+    out = np.empty((H, k), np.int64)
+    for h in range(H):
+        by_score = topk_indices(pooled[h], k1)
+        rest = np.setdiff1d(np.arange(n_cand), by_score)
+        drawn = rest[topk_indices(rand[h][rest], k - W - k1)]
+        out[h] = np.sort(np.concatenate([by_score, drawn, np.arange(n - W, n)]))
+    return out
+
+
+def anchor_assign(x: np.ndarray, anchors: np.ndarray):
+    """AnchorKV's anchor-residual representation of one layer (no residual).
+
+    [AnchorKV, §3.1]: anchors are stored exactly; every other vector is
+    projected orthogonally onto the span of the single anchor with the
+    largest cosine similarity, kept as that anchor's index and the scalar
+    coefficient gamma = <x, a> / <a, a>. Readings: keys and values are
+    assigned separately (call once per tensor); equal cosines go to the
+    lower anchor slot; an anchor with zero norm is never chosen; an anchor
+    position is its own slot with gamma = 1.
+
+    x: [H][n][d]; anchors: [H][k] positions. Returns (slot [H][n] indices
+    into anchors[h], gamma [H][n]).
+    """
+    H, n, d = x.shape
+    k = anchors.shape[1]
+    slot = np.empty((H, n), np.int64)
+    gamma = np.empty((H, n))
+    for h in range(H):
+        A = x[h, anchors[h]]                                  # [k][d]
+        na = np.sqrt((A * A).sum(axis=1))
+        nx = np.sqrt((x[h] * x[h]).sum(axis=1))
+        dots = x[h] @ A.T                                     # [n][k]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            cos = dots / (nx[:, None] * na[None, :])
+        cos = np.where(na[None, :] > 0, np.nan_to_num(cos, nan=0.0), -np.inf)
+        best = np.argmax(cos, axis=1)                         # first of equal maxima
+        slot[h] = best
+        gamma[h] = dots[np.arange(n), best] / np.where(na[best] > 0, na[best] ** 2, 1.0)
+        slot[h, anchors[h]] = np.arange(k)
+        gamma[h, anchors[h]] = 1.0
+    return slot, gamma
+
+
 # -------------------------------------------------------------- compaction ----
 
 def compact_layer(k: np.ndarray, v: np.ndarray, idx: np.ndarray,

@@ -295,6 +295,79 @@ def check_chunked(o):
     assert (got <= 1).all() and (got > 0).all()
 
 
+def check_anchor_select(o):
+    g = load_golden("anchor_example.txt")
+    n, W, k = int(g["select.n"][0]), int(g["select.W"][0]), int(g["select.k"][0])
+    got = o.anchor_select(np.array([g["select.pooled"]]), np.array([g["select.rand"]]), n, W, k,
+                          g["select.rho"][0])
+    np.testing.assert_array_equal(got[0], g["select.anchors"])
+    rng = np.random.default_rng(48)
+    for trial in range(10):
+        H, n, W = 3, 60, 4
+        k = int(rng.integers(W, n + 1))
+        rho = float(rng.choice([0.0, 0.3, 0.7, 1.0]))
+        pooled = rng.integers(0, 5, size=(H, n - W)).astype(np.float64)
+        rand = rng.random((H, n - W))
+        got = o.anchor_select(pooled, rand, n, W, k, rho)
+        k1 = int(math.floor(rho * (k - W)))
+        for h in range(H):
+            row = list(got[h])
+            assert row == sorted(row) and len(set(row)) == k and row[-W:] == list(range(n - W, n))
+            cand = [p for p in row if p < n - W]
+            # some k1 of them are a top-k1 by score; the others a top by the
+            # draws among what the score part left
+            by_score = [int(p) for p in o.topk_indices(pooled[h], k1)]
+            _assert_topk_property(pooled[h], by_score, k1)
+            assert set(by_score) <= set(cand)
+            rest = [p for p in range(n - W) if p not in set(by_score)]
+            drawn = [rest.index(p) for p in cand if p not in set(by_score)]
+            _assert_topk_property(np.array([rand[h][p] for p in rest]), drawn, k - W - k1)
+        # the same as the two-stage selection with stage 2 keyed by the draws:
+        # (score * 0 + 1) * rand
+        idx, _, _ = o.select_layer(pooled, k, W, n, weight=rand, alpha=rho, score_norm=0.0, eps=1.0)
+        np.testing.assert_array_equal(np.sort(idx, axis=1), got)
+
+
+def check_anchor_assign(o):
+    g = load_golden("anchor_example.txt")
+    x = np.asarray(g["assign.x"]).reshape(1, -1, 2)
+    anchors = np.asarray(g["assign.anchors"], np.int64)[None]
+    slot, gamma = o.anchor_assign(x, anchors)
+    np.testing.assert_array_equal(slot[0], g["assign.slot"])
+    np.testing.assert_allclose(gamma[0], g["assign.gamma"], rtol=1e-15, atol=1e-15)
+    rng = np.random.default_rng(49)
+    H, n, d, k = 2, 40, 5, 6
+    x = rng.standard_normal((H, n, d))
+    anchors = np.sort(np.stack([rng.choice(n, k, replace=False) for _ in range(H)]), axis=1)
+    slot, gamma = o.anchor_assign(x, anchors)
+    for h in range(H):
+        for j in range(n):
+            if j in set(anchors[h]):
+                assert anchors[h][slot[h, j]] == j and gamma[h, j] == 1.0
+                continue
+            best, bs = -2.0, -1
+            for s_ in range(k):
+                a = x[h, anchors[h][s_]]
+                c = sum(a[e] * x[h, j, e] for e in range(d)) / (
+                    math.sqrt(sum(v * v for v in a)) * math.sqrt(sum(v * v for v in x[h, j])))
+                if c > best:
+                    best, bs = c, s_
+            assert slot[h, j] == bs
+            a = x[h, anchors[h][bs]]
+            gm = sum(a[e] * x[h, j, e] for e in range(d)) / sum(v * v for v in a)
+            assert abs(gamma[h, j] - gm) <= 1e-12 * max(1.0, abs(gm))
+            # gamma * a is the orthogonal projection onto the anchor's span
+            r = x[h, j] - gamma[h, j] * a
+            assert abs(r @ a) <= 1e-10 * (a @ a)
+    # scaling an anchor by c > 0 keeps the slots and divides its gammas by c
+    x2 = x.copy()
+    x2[0, anchors[0][2]] *= 4.0
+    slot2, gamma2 = o.anchor_assign(x2, anchors)
+    np.testing.assert_array_equal(slot2, slot)
+    m = (slot[0] == 2) & ~np.isin(np.arange(n), anchors[0])
+    np.testing.assert_allclose(gamma2[0][m], gamma[0][m] / 4.0, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- pool ----
 
 def check_maxpool(o):
@@ -674,5 +747,5 @@ ALL_CHECKS = [
     check_decode_hand_example, check_decode_bruteforce, check_decode_sdpa, check_decode_closed_forms,
     check_value_weight_l2, check_select_budgets_example, check_select_budgets_bruteforce,
     check_select_budgets_reductions, check_external_logit, check_head_scores_and_budgets,
-    check_chunked,
+    check_chunked, check_anchor_select, check_anchor_assign,
 ]

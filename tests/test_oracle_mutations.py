@@ -65,6 +65,17 @@ MUTANTS = {
     "chunked_padding_rows": ("        nin = n_prompt + mt\n", "        nin = n_prompt + m\n"),
     "chunked_offset": ("        c0 = t * m\n", "        c0 = min(t * m + 1, n - 1)\n"),
     "chunked_no_scale": ("logits = scale * (q[t, h * G + g, :nin] @ keys.T)", "logits = (q[t, h * G + g, :nin] @ keys.T)"),
+    "anchor_rho_of_k": ("    k1 = int(np.floor(rho * (k - W)))\n    out = np.empty((H, k), np.int64)",
+                        "    k1 = min(int(np.floor(rho * k)), k - W)\n    out = np.empty((H, k), np.int64)"),
+    "anchor_no_window": ("out[h] = np.sort(np.concatenate([by_score, drawn, np.arange(n - W, n)]))",
+                         "out[h] = np.sort(np.concatenate([by_score, drawn, np.arange(n - W - 1, n - 1)]))"),
+    "anchor_random_from_all": ("drawn = rest[topk_indices(rand[h][rest], k - W - k1)]",
+                               "drawn = rest[topk_indices(rand[h][:len(rest)], k - W - k1)]"),
+    "assign_dot_not_cos": ("cos = dots / (nx[:, None] * na[None, :])", "cos = dots / (nx[:, None] * 1.0)"),
+    "assign_gamma_unnormed": ("gamma[h] = dots[np.arange(n), best] / np.where(na[best] > 0, na[best] ** 2, 1.0)",
+                              "gamma[h] = dots[np.arange(n), best] / np.where(na[best] > 0, na[best], 1.0)"),
+    "assign_ties_high": ("best = np.argmax(cos, axis=1)                         # first of equal maxima",
+                         "best = k - 1 - np.argmax(cos[:, ::-1], axis=1)     # first of equal maxima"),
     "compact_wrong_head": ("return (np.stack([k[h, idx[h]] for h in range(H)]),", "return (np.stack([k[0, idx[h]] for h in range(H)]),"),
 }
 
