@@ -61,7 +61,7 @@ def traffic_from_profiles(key, sha):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
+def cpu_baseline(wl, host, seconds, w_host=None, budgets=None, rand=None):
     """The oracle (fp64 numpy) on the same inputs, one (layer, KV head) at a
     time in order, until `seconds` of CPU work: attention scores, max-pool,
     the value weight when the workload uses it, and top-k selection.
@@ -91,6 +91,13 @@ def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
             raw = (oracle.external_logit_scores(q, k, wl.G, wl.scale) if wl.agg == "logit"
                    else oracle.external_raw_scores(q, k, wl.G, wl.scale, wl.agg))
         pooled = oracle.maxpool(raw, wl.n_cand, wl.pool)
+        if wl.anchor_k:        # AnchorKV's anchor stage for this head
+            anchors = oracle.anchor_select(pooled, rand[l, h:h + 1], wl.n, wl.W_kept, wl.anchor_k,
+                                           wl.rho)
+            oracle.anchor_assign(k, anchors)
+            oracle.anchor_assign(synth.bf16_to_f64(host["v"][l][h:h + 1]), anchors)
+            units += 1
+            continue
         if wl.head_keep > 0:   # selected below, once the sample's head scores are known
             head_rows.append(pooled)
             units += 1
@@ -118,7 +125,8 @@ def cpu_baseline(wl, host, seconds, w_host=None, budgets=None):
             oracle.select_budgets(row, b[0, i:i + 1], wl.W_kept, wl.n)
     dt = time.perf_counter() - t0
     what = ("scores, max-pool" + (", value weight" if wl.value_weight else "")
-            + (", head scores and head budgets" if head_rows else "") + " and top-k selection")
+            + (", head scores and head budgets" if head_rows else "")
+            + (", anchor selection and key/value assignment" if wl.anchor_k else " and top-k selection"))
     return {"value": units * wl.n / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
             "sample": f"{units} (layer, KV head) pairs of {wl.name} in order from layer 0"
                       f"{' (the sample repeated)' if units > len(pairs) else ''}: "
@@ -231,7 +239,34 @@ def main():
             kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
                            scores=scores)
 
+    if wl.anchor_k:
+        rand = torch.from_numpy(synth.gen_rand(wl, args.seed)).to(dev)
+        anchors = torch.empty((wl.L, wl.H_kv, wl.anchor_k), dtype=torch.int32, device=dev)
+        a_slot = [torch.empty((wl.L, wl.H_kv, wl.n), dtype=torch.int32, device=dev) for _ in range(2)]
+        a_gamma = [torch.empty((wl.L, wl.H_kv, wl.n), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def anchor_step(marks=None):
+        # AnchorKV's anchor stage: score, anchors, keys and values assigned
+        if marks is not None:
+            marks[0].record()
+        score()
+        if marks is not None:
+            marks[1].record()
+        kv.kvsel_anchor_select(scores, rand, n=wl.n, W=W_kept, k=wl.anchor_k, rho=wl.rho,
+                               out=anchors)
+        if marks is not None:
+            marks[2].record()
+        kv.kvsel_anchor_assign(k, anchors, slot=a_slot[0], gamma=a_gamma[0])
+        if marks is not None:
+            marks[3].record()
+        kv.kvsel_anchor_assign(v, anchors, slot=a_slot[1], gamma=a_gamma[1])
+        if marks is not None:
+            marks[4].record()
+        return None, None
+
     def step(marks=None):
+        if wl.anchor_k:
+            return anchor_step(marks)
         if marks is not None:
             marks[0].record()
         score()
@@ -316,14 +351,18 @@ def main():
                    "value_weight": wl.value_weight,
                    **({"value_norm": wl.value_norm} if wl.value_weight else {}),
                    "seed": args.seed,
-                   "step": ("score+head_score+head_budgets+select_budgets+compact" if keep
+                   **({"anchor_k": wl.anchor_k, "rho": wl.rho} if wl.anchor_k else {}),
+                   "step": ("score+anchor_select+anchor_assign(K)+anchor_assign(V)" if wl.anchor_k
+                            else "score+head_score+head_budgets+select_budgets+compact" if keep
                             else "score+select_budgets+compact" if wl.budget_vector
                             else "score+value_weight+select+compact" if wl.value_weight
                             else "score+select+compact")},
         "roofline": None,   # the dominant call's, set below
-        "per_call_ms": {"score": ms_score, **({"value_weight": ms_vw} if wl.value_weight else {}),
-                        **({"head_score+head_budgets": ms_vw} if keep else {}),
-                        "select": ms_sel, "compact": ms_cmp},
+        "per_call_ms": ({"score": ms_score, "anchor_select": ms_vw, "anchor_assign_k": ms_sel,
+                         "anchor_assign_v": ms_cmp} if wl.anchor_k else
+                        {"score": ms_score, **({"value_weight": ms_vw} if wl.value_weight else {}),
+                         **({"head_score+head_budgets": ms_vw} if keep else {}),
+                         "select": ms_sel, "compact": ms_cmp}),
         "scored_selected_entries_per_s": entries / ((ms_score + ms_sel) * 1e-3),
         "wall_s_timed": wall,
     }
@@ -377,7 +416,19 @@ def main():
         out["other_rooflines"] = [c[1] for c in calls[1:]]
     # the next step after eviction: one decoding step over the kept rows of
     # every layer (not part of `value`), on the last step's compacted cache
-    if wl.G <= 8:
+    if wl.anchor_k:
+        # assignment: each vector read once (256 B) and its slot and gamma
+        # written (8 B); 2 * kpad * d MFMA flops per vector
+        kpad = (wl.anchor_k + 63) // 64 * 64
+        a_bytes = wl.L * wl.H_kv * wl.n * (wl.d * 2 + 8)
+        a_flops = 2.0 * wl.L * wl.H_kv * wl.n * kpad * wl.d
+        a_ms = (ms_sel + ms_cmp) / 2
+        out["anchor_assign"] = {
+            "bound": "hbm", "ms_per_call": a_ms, "bytes_per_launch": a_bytes,
+            "achieved": a_bytes / (a_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a_bytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_tflops": a_flops / (a_ms * 1e-3) / 1e12}
+    if wl.G <= 8 and kept_kv is not None:
         gq = torch.Generator(device=dev)
         gq.manual_seed(args.seed + 7)
         q_dec = torch.randn((wl.L, wl.H_q, wl.d), generator=gq, device=dev).to(torch.bfloat16)
@@ -415,7 +466,8 @@ def main():
         w_host = None
         if wl.value_weight:
             w_host = t["w_o"][:2].cpu().view(torch.int16).numpy().view(np.uint16)
-        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds, w_host, b_host)
+        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds, w_host, b_host,
+                                           synth.gen_rand(wl, args.seed) if wl.anchor_k else None)
     print(json.dumps(out), flush=True)
 
 

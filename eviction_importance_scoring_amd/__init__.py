@@ -19,6 +19,7 @@ __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_score_chunked", "kvsel_value_weight",
     "kvsel_value_l2_factor", "kvsel_value_weight_l2",
     "kvsel_select", "kvsel_select_budgets", "kvsel_head_score", "kvsel_head_budgets",
+    "kvsel_anchor_select", "kvsel_anchor_assign",
     "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
     "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX", "AGG_LOGIT_MAX",
@@ -58,6 +59,10 @@ _SIGNATURES = {
     "kvsel_head_score": [_c_void_p, _c_i32, _c_i32, _c_i32, _c_void_p, _c_void_p],
     "kvsel_head_budgets": [_c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                            _c_void_p, _c_size_p, _c_void_p],
+    "kvsel_anchor_select": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                            _c_void_p, _c_void_p, _c_size_p, _c_void_p],
+    "kvsel_anchor_assign": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                            _c_void_p, _c_void_p, _c_void_p, _c_size_p, _c_void_p],
     "kvsel_compact": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                       _c_void_p, _c_i64, _c_void_p, _c_void_p, _c_void_p],
     "kvsel_decode_attention": [_c_void_p, _c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -342,6 +347,55 @@ def kvsel_head_budgets(head_score, *, keep: int, n: int, W: int, out=None, works
     _check(f(_ptr(head_score), L, H, int(keep), n, W, _ptr(out), _ptr(ws), ctypes.byref(nbytes),
              _stream(dev)))
     return out
+
+
+def kvsel_anchor_select(scores, rand, *, n: int, W: int, k: int, rho: float = 0.7,
+                        out=None, workspace=None):
+    """AnchorKV anchor positions i32 [L][H_kv][k] (ascending). scores, rand
+    f32 [L][H_kv][n-W]."""
+    _need(scores, torch.float32, "scores", 3)
+    _need(rand, torch.float32, "rand", 3)
+    if rand.shape != scores.shape:
+        raise ValueError("rand must match scores")
+    L, H, n_cand = scores.shape
+    if n_cand != n - W:
+        raise ValueError(f"scores has {n_cand} candidates, expected n-W={n - W}")
+    dev = scores.device
+    if out is None:
+        out = torch.empty((L, H, k), dtype=torch.int32, device=dev)
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_anchor_select
+    args = (L, H, n, W, int(k), float(rho))
+    _check(f(None, None, *args, None, None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(scores), _ptr(rand), *args, _ptr(out), _ptr(ws), ctypes.byref(nbytes),
+             _stream(dev)))
+    return out
+
+
+def kvsel_anchor_assign(x, anchors, *, slot=None, gamma=None, workspace=None):
+    """Nearest-anchor slot i32 and gamma f32 [L][H_kv][n] of x bf16
+    [L][H_kv][n][d] for anchors i32 [L][H_kv][k]."""
+    _need(x, torch.bfloat16, "x", 4)
+    _need(anchors, torch.int32, "anchors", 3)
+    L, H, n, d = x.shape
+    if anchors.shape[:2] != (L, H):
+        raise ValueError(f"anchors must be [L][H_kv][k], got {tuple(anchors.shape)}")
+    k = anchors.shape[2]
+    dev = x.device
+    if slot is None:
+        slot = torch.empty((L, H, n), dtype=torch.int32, device=dev)
+    if gamma is None:
+        gamma = torch.empty((L, H, n), dtype=torch.float32, device=dev)
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_anchor_assign
+    _check(f(None, None, L, H, d, n, k, None, None, None, ctypes.byref(nbytes), None))
+    ws = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(f(_ptr(x), _ptr(anchors), L, H, d, n, k, _ptr(slot), _ptr(gamma), _ptr(ws),
+             ctypes.byref(nbytes), _stream(dev)))
+    return slot, gamma
 
 
 def kvsel_compact(k, v, idx, head_offsets=None, k_out=None, v_out=None):

@@ -1,0 +1,221 @@
+// AnchorKV's anchor stage ([AnchorKV] §3.1-3.2).
+//
+// Anchor selection is the two-stage selection of select.hip with stage 2
+// keyed by uniform draws: (score * 0 + 1) * draw is the draw itself, so
+// stage 1 takes floor(rho * (k - W)) positions by pooled score and stage 2
+// the largest draws among the rest (uniform sampling without replacement);
+// the W recent positions are the window. See kvsel_anchor_select in api.hip.
+//
+// Assignment: every vector of a head goes to the anchor of largest cosine
+// similarity, kept as the anchor's slot and gamma = <x, a> / <a, a>:
+//   k_anchor_gather  the head's anchor rows into a contiguous [kpad][128]
+//                    block (zero rows past k) and 1/|a| per slot (0 for a
+//                    zero or padding anchor, which is never chosen)
+//   k_anchor_assign  4-wave workgroups, 256 vectors of one (layer, head),
+//                    each wave 64 of them in registers as MFMA operands;
+//                    the anchor block streams through the LDS ring of
+//                    kvsel_ring.h in 64-row tiles. Per tile the MFMA gives
+//                    <x, a> for 64 anchors x 64 vectors; each lane keeps,
+//                    per vector, the best <x, a> / |a| (the cosine up to
+//                    the vector's own norm) over its anchor rows, visited
+//                    in increasing slot order with a strict compare, so the
+//                    lower slot wins ties; the two lane halves merge the
+//                    same way.
+//   k_anchor_self    every anchor position to its own slot, gamma 1.
+// Dot products are fp32 sums of exact bf16 products.
+#include "kvsel_internal.h"
+#include "kvsel_kernels.h"
+#include "kvsel_ring.h"
+
+namespace kvsel {
+
+constexpr int kAsWaves = 4;
+constexpr int kMaxAnchorPad = 2048;        // anchors per head (LDS for their 1/|a|)
+constexpr int kAsBlock = kAsWaves * 64;    // vectors per workgroup
+using AsLoader = RingLoader<kAsWaves>;
+constexpr int kAsLoads = AsLoader::kLoads;
+
+int anchor_kpad(int k) { return (k + gTile - 1) / gTile * gTile; }
+
+// grid (kpad, L*H), block 64: one anchor row per workgroup, its 16-byte
+// pieces on 16 lanes (the other 48 idle; the gather is tiny)
+__global__ __launch_bounds__(64) void k_anchor_gather(const u32x4* __restrict__ x,
+                                                      const int32_t* __restrict__ anchors, int n,
+                                                      int k, int kpad, u32x4* __restrict__ arows,
+                                                      float* __restrict__ rinv) {
+  const int s = blockIdx.x;
+  const size_t lh = blockIdx.y;
+  const int lane = threadIdx.x;
+  constexpr int kPieces = kRowBytes / 16;
+  int pos = -1;
+  if (s < k) pos = anchors[lh * k + s];
+  const bool valid = pos >= 0 && pos < n;
+  float ss = 0.f;
+  if (lane < kPieces) {
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (valid) v = x[(lh * n + pos) * kPieces + lane];
+    arows[((size_t)lh * kpad + s) * kPieces + lane] = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __uint_as_float(v[e] << 16), hi = __uint_as_float(v[e] & 0xFFFF0000u);
+      ss = __builtin_fmaf(lo, lo, ss);
+      ss = __builtin_fmaf(hi, hi, ss);
+    }
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) rinv[lh * kpad + s] = ss > 0.f ? 1.0f / __builtin_sqrtf(ss) : 0.f;
+}
+
+// 1-D grid of key_blocks * H * L workgroups, block 256.
+__global__ __launch_bounds__(256, 2) void k_anchor_assign(const __bf16* __restrict__ x,
+                                                          const __bf16* __restrict__ arows,
+                                                          const float* __restrict__ rinv_g, int H,
+                                                          int n, int kpad, int key_blocks,
+                                                          int32_t* __restrict__ slot_out,
+                                                          float* __restrict__ gamma_out) {
+  __shared__ __align__(16) unsigned char ring[gSlots][gRowsBytes];
+  // per slot: 1/|a|, and 0 or -inf (an anchor never chosen) added to its score
+  __shared__ __align__(16) float rinv[kMaxAnchorPad];
+  __shared__ __align__(16) float pen[kMaxAnchorPad];
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = id % key_blocks;
+  id /= key_blocks;
+  const int h = id % H, l = id / H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+  const size_t lh = (size_t)l * H + h;
+  const int ntiles = kpad / gTile;
+  const __bf16* ah = arows + lh * (size_t)kpad * kHeadDim;
+
+  const int key0 = kb * kAsBlock + wave * 64;
+  bf16x8 vop[2][8];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int key = key0 + nt * 32 + col;
+    if (key < n) load_half_row(x + (lh * n + key) * (size_t)kHeadDim, hf, vop[nt]);
+    else zero_ops(vop[nt]);
+  }
+  for (int s = threadIdx.x; s < kpad; s += 256) {
+    const float r = rinv_g[lh * kpad + s];
+    rinv[s] = r;
+    pen[s] = r > 0.f ? 0.f : neg_inf();
+  }
+  AsLoader ld;
+  ld.init(kHeadDim);
+  auto issue = [&](int t, int slot) { ld.issue(ah, t * gTile, kpad, kHeadDim, ring[slot]); };
+  // the rinv stores and the operand loads complete before the ring starts
+  __syncthreads();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < gSlots - 1; ++t) issue(min(t, ntiles - 1), t);
+
+  const bool any_key = key0 < n;
+  // best <x, a> / |a| per vector so far, and its slot (gamma = best / |a|)
+  float best[2] = {neg_inf(), neg_inf()};
+  int bslot[2] = {0, 0};
+
+  auto begin_tile = [&](int t) -> const unsigned char* {
+    gen_wait_tile<kAsLoads>(t, ntiles);
+    gen_barrier();
+    if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
+    int soff = (t % gSlots) * gRowsBytes;   // opaque: LDS reads stay inside the tile
+    asm volatile("" : "+v"(soff));
+    return ring[0] + soff;
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    const unsigned char* slot = begin_tile(t);
+    if (!any_key) continue;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+    bf16x8 a[2][2];
+    read_step(slot, col, hf, 0, a[0]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
+      tile_step(a[st & 1], vop, st, acc);
+    }
+    // anchor rows of this lane, in increasing slot order; rows 4j..4j+3 of
+    // an accumulator are consecutive slots (one 16-byte read each)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s0 = t * gTile + mt * 32 + acc_row(4 * j, lane);
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rinv[s0]);
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&pen[s0]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const float sc = __builtin_fmaf(acc[mt][nt][4 * j + u], r4[u], p4[u]);
+            if (sc > best[nt]) {
+              best[nt] = sc;
+              bslot[nt] = s0 + u;
+            }
+          }
+      }
+  }
+  gen_wait<0>();
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    // the other lane half holds the other 16 anchor rows of every block
+    const float ob = __shfl_xor(best[nt], 32);
+    const int os = __shfl_xor(bslot[nt], 32);
+    if (ob > best[nt] || (ob == best[nt] && os < bslot[nt])) {
+      best[nt] = ob;
+      bslot[nt] = os;
+    }
+    const int key = key0 + nt * 32 + col;
+    if (hf == 0 && key < n) {
+      // <x, a> / <a, a> = (<x, a> / |a|) / |a|; no valid anchor: 0
+      const float g = best[nt] * rinv[bslot[nt]];
+      slot_out[lh * n + key] = bslot[nt];
+      gamma_out[lh * n + key] = best[nt] > neg_inf() ? g : 0.f;
+    }
+  }
+}
+
+// grid (ceil(k/256), L*H): anchor positions to their own slot
+__global__ __launch_bounds__(256) void k_anchor_self(const int32_t* __restrict__ anchors, int n,
+                                                     int k, int32_t* __restrict__ slot_out,
+                                                     float* __restrict__ gamma_out) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  const size_t lh = blockIdx.y;
+  if (s >= k) return;
+  const int pos = anchors[lh * k + s];
+  if (pos < 0 || pos >= n) return;
+  slot_out[lh * n + pos] = s;
+  gamma_out[lh * n + pos] = 1.0f;
+}
+
+size_t anchor_ws_bytes(int L, int H, int k) {
+  const size_t kpad = anchor_kpad(k);
+  const size_t rows = ((size_t)L * H * kpad * kRowBytes + 255) & ~size_t(255);
+  return rows + (size_t)L * H * kpad * sizeof(float);
+}
+
+hipError_t anchor_assign_launch(const void* x, const int32_t* anchors, int L, int H, int n, int k,
+                                int32_t* slot, float* gamma, void* ws, hipStream_t st) {
+  const int kpad = anchor_kpad(k);
+  const size_t LH = (size_t)L * H;
+  char* w = static_cast<char*>(ws);
+  u32x4* arows = reinterpret_cast<u32x4*>(w);
+  float* rinv = reinterpret_cast<float*>(w + ((LH * kpad * kRowBytes + 255) & ~size_t(255)));
+  const int key_blocks = (n + kAsBlock - 1) / kAsBlock;
+  const long long blocks = (long long)key_blocks * H * L;
+  if (blocks > 0x7fffffffLL || LH > 65535u) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_anchor_gather, dim3(kpad, (unsigned)LH), dim3(64), 0, st,
+                     static_cast<const u32x4*>(x), anchors, n, k, kpad, arows, rinv);
+  hipLaunchKernelGGL(k_anchor_assign, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const __bf16*>(x), reinterpret_cast<const __bf16*>(arows), rinv, H,
+                     n, kpad, key_blocks, slot, gamma);
+  hipLaunchKernelGGL(k_anchor_self, dim3((k + 255) / 256, (unsigned)LH), dim3(256), 0, st, anchors,
+                     n, k, slot, gamma);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -293,6 +293,61 @@ int32_t kvsel_head_budgets(const float* head_score, int32_t L, int32_t H_kv, int
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 
+int32_t kvsel_anchor_select(const float* scores, const float* rand, int32_t L, int32_t H_kv,
+                            int32_t n, int32_t W, int32_t k, float rho, int32_t* anchors,
+                            void* ws, size_t* ws_bytes, void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || n < 1 || W < 0 || W >= n || k < W || k > n) return KVSEL_ERR_ARG;
+  if (!(rho >= 0.f && rho <= 1.f)) return KVSEL_ERR_ARG;
+  const int64_t n_cand = (int64_t)n - W;
+  if (n_cand > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  // the two-stage selection with stage 2 keyed (score * 0 + 1) * draw
+  SelectPlan p;
+  p.L = L; p.H = H_kv; p.n = n; p.W = W; p.n_cand = (int)n_cand;
+  p.budget = k;
+  p.adaptive = false;
+  p.two_stage = true;
+  p.score_norm = 0.f;
+  p.eps = 1.f;
+  p.k = k - W;
+  p.k1 = (int64_t)std::floor((double)rho * (double)p.k);
+  p.segments = L * H_kv;
+  p.seg_len = n_cand;
+  p.resident = false;
+  const size_t need = select_ws_bytes(p);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!scores || !rand || !anchors) return KVSEL_ERR_ARG;
+  if (!aligned16(scores) || !aligned16(rand)) return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return KVSEL_ERR_ARG;
+  const hipError_t e = select_launch(p, scores, rand, anchors, nullptr, nullptr, ws,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_anchor_assign(const void* x, const int32_t* anchors, int32_t L, int32_t H_kv,
+                            int32_t d, int32_t n, int32_t k, int32_t* slot, float* gamma,
+                            void* ws, size_t* ws_bytes, void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (L < 1 || H_kv < 1 || d < 1 || n < 1 || k < 1 || k > n) return KVSEL_ERR_ARG;
+  if (d != kHeadDimPublic || k > kMaxAnchorsPublic) return KVSEL_ERR_UNSUPPORTED;
+  if ((int64_t)L * H_kv > 65535 || (int64_t)H_kv * n > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  const size_t need = anchor_ws_bytes(L, H_kv, k);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!x || !anchors || !slot || !gamma) return KVSEL_ERR_ARG;
+  if (!aligned16(x) || !aligned16(ws)) return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  const hipError_t e = anchor_assign_launch(x, anchors, L, H_kv, n, k, slot, gamma, ws,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
 int32_t kvsel_compact(const void* k, const void* v, int32_t L, int32_t H_kv, int32_t d,
                       int32_t n, const int32_t* idx, const int32_t* head_offsets,
                       int64_t kept_per_layer, void* k_out, void* v_out, void* stream) {

@@ -80,6 +80,12 @@ hipError_t value_l2_factor_launch(const void* w_o, int L, int H, int G, int D, v
 hipError_t value_weight_l2_launch(const void* v, const void* factor, int L, int H, int G, int n,
                                   int n_cand, float* weight, hipStream_t st);
 
+// ---------------------------------------------------------------- anchors ----
+constexpr int kMaxAnchorsPublic = 2048;
+size_t anchor_ws_bytes(int L, int H, int k);
+hipError_t anchor_assign_launch(const void* x, const int32_t* anchors, int L, int H, int n, int k,
+                                int32_t* slot, float* gamma, void* ws, hipStream_t st);
+
 // ------------------------------------------------------------ head level ----
 hipError_t head_score_launch(const float* scores, int L, int H, int n_pos, float* out,
                              hipStream_t st);

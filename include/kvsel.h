@@ -21,8 +21,8 @@
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
  *  - Workspace protocol (kvsel_score, kvsel_score_chunked, kvsel_select,
- *    kvsel_select_budgets, kvsel_head_budgets, kvsel_decode_attention): with
- *    ws == NULL the
+ *    kvsel_select_budgets, kvsel_head_budgets, kvsel_anchor_select,
+ *    kvsel_anchor_assign, kvsel_decode_attention): with ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
  *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
  *    Workspace contents need no initialisation and are scratch afterwards.
@@ -318,6 +318,58 @@ int32_t kvsel_head_score(const float* scores, int32_t L, int32_t H_kv,
 int32_t kvsel_head_budgets(const float* head_score, int32_t L, int32_t H_kv,
                            int32_t keep, int32_t n, int32_t W, int32_t* budgets,
                            void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_anchor_select -- AnchorKV's anchor positions.
+ *
+ * [AnchorKV] §3.2 (anchor selection): each KV head keeps k anchors. The W
+ * most recent positions [n-W, n) are always anchors and count toward k;
+ * of the remaining k - W slots, k1 = floor(rho * (k - W)) (computed in
+ * double) go to the candidates [0, n-W) with the largest pooled score
+ * (equal scores to the lower position), the rest are drawn uniformly
+ * without replacement among the other candidates: the ones with the
+ * largest draws rand[l][h][j] (equal draws to the lower position). The
+ * draws are the caller's (e.g. uniform in [0, 1)). The page's settings
+ * are k = n/128, W = 32, rho = 0.7.
+ *
+ *   scores  f32 [L][H_kv][n-W]   pooled (kvsel_score)
+ *   rand    f32 [L][H_kv][n-W]   finite draws
+ *   anchors i32 [L][H_kv][k]     out: ascending positions
+ *
+ * Ranges: 0 <= W < n; W <= k <= n; 0 <= rho <= 1. Needs a workspace
+ * (protocol above).
+ */
+int32_t kvsel_anchor_select(const float* scores, const float* rand,
+                            int32_t L, int32_t H_kv, int32_t n, int32_t W,
+                            int32_t k, float rho, int32_t* anchors,
+                            void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_anchor_assign -- AnchorKV's nearest-anchor representation.
+ *
+ * [AnchorKV] §3.1: anchors are stored exactly; every other vector of the
+ * head is projected onto the span of the single anchor with the largest
+ * cosine similarity and kept as that anchor's slot and the coefficient
+ *   gamma = <x, a> / <a, a>.
+ * Equal cosines go to the lower slot; an anchor of zero norm is never
+ * chosen; an anchor position is its own slot with gamma = 1. Call once for
+ * the keys (the page projects pre-RoPE keys) and once for the values.
+ * Dot products are fp32 sums of exact bf16 products, so two anchors whose
+ * cosines agree to ~1e-6 may be chosen either way.
+ *
+ *   x       bf16 [L][H_kv][n][d]
+ *   anchors i32  [L][H_kv][k]    positions (kvsel_anchor_select)
+ *   slot    i32  [L][H_kv][n]    out: index into anchors[l][h]
+ *   gamma   f32  [L][H_kv][n]    out
+ *
+ * Limits: d == 128, k <= 2048, L*H_kv <= 65535 (else
+ * KVSEL_ERR_UNSUPPORTED). Anchor positions outside [0, n) count as zero
+ * vectors. Needs a workspace (protocol above).
+ */
+int32_t kvsel_anchor_assign(const void* x, const int32_t* anchors,
+                            int32_t L, int32_t H_kv, int32_t d, int32_t n,
+                            int32_t k, int32_t* slot, float* gamma,
+                            void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * kvsel_compact -- gather the kept rows of K and V.

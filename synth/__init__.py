@@ -68,6 +68,8 @@ class Workload:
     adaptive: bool = False       # one budget per layer shared by all heads
     budget_vector: bool = False  # one budget per (layer, head), from gen_budgets
     head_keep: float = 0.0       # > 0: head-level eviction keeping this fraction of heads
+    anchor_k: int = 0            # > 0: AnchorKV anchor stage with this many anchors per head
+    rho: float = 0.7             # AnchorKV: share of the non-window anchors taken by score
     chunk: int = 0               # > 0: KVzip chunked scoring, cached keys per chunk
     n_prompt: int = 0            # chunked scoring: repeat-prompt tokens before each chunk
     value_weight: bool = False   # value-norm weighted two-stage selection
@@ -161,6 +163,11 @@ WORKLOADS = {
         # score, half of all heads kept whole, the others their window
         Workload("headlevel_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=32,
                  pool=7, head_keep=0.5),
+        # AnchorKV's anchor stage: k = n/128 anchors per head (W = 32 recent,
+        # 70% of the rest by pooled score, 30% uniform), every key and value
+        # assigned to its most cosine-similar anchor
+        Workload("anchorkv_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=32,
+                 pool=7, anchor_k=256, rho=0.7),
         # H2O-style accumulated attention: window scoring with W = 256, 20%
         Workload("h2o_llama8b_n32k", L=32, H_kv=8, G=4, d=128, n=32768, W=256,
                  pool=7, beta=0.20),
@@ -181,7 +188,7 @@ WORKLOADS = {
     ]
 }
 
-_TENSOR = {"q": 1, "k": 2, "v": 3, "w_o": 4, "heavy": 5, "budgets": 6, "kself": 7}
+_TENSOR = {"q": 1, "k": 2, "v": 3, "w_o": 4, "heavy": 5, "budgets": 6, "kself": 7, "rand": 8}
 
 
 def _rng(seed: int, wl: Workload, tensor: str, layer: int) -> np.random.Generator:
@@ -254,6 +261,13 @@ def gen_budgets(wl: Workload, seed: int) -> np.ndarray:
     pool = wl.L * wl.H_kv * (int(np.floor(wl.beta * wl.n)) - wl.W_kept)
     b = wl.W_kept + np.floor(imp / imp.sum() * pool)
     return np.minimum(b, wl.n).astype(np.int32)
+
+
+def gen_rand(wl: Workload, seed: int) -> np.ndarray:
+    """Uniform draws in [0, 1) per candidate, [L][H_kv][n_cand] float32 (the
+    random anchors of AnchorKV are the candidates with the largest draws)."""
+    r = _rng(seed, wl, "rand", 0)
+    return r.random((wl.L, wl.H_kv, wl.n_cand), dtype=np.float32)
 
 
 def gen_layer(wl: Workload, seed: int, layer: int, which=("q", "k", "v", "w_o")) -> dict:

@@ -350,3 +350,61 @@ def test_score_chunked_pointers(lib):
     assert f(p, p, None, *base, p, None, p, ctypes.byref(nb), None) == ARG
     assert f(None, p, p, *base, p, None, p, ctypes.byref(nb), None) == ARG
     assert f(p, p, p, *base, None, None, p, ctypes.byref(nb), None) == ARG
+
+
+def _anchor_sel(lib, **kw):
+    a = dict(L=2, H=8, n=4096, W=32, k=64, rho=0.7)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    return lib.kvsel_anchor_select(None, None, a["L"], a["H"], a["n"], a["W"], a["k"], a["rho"],
+                                   None, None, ctypes.byref(nb), None), nb.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(k=32), OK), (dict(k=4096), OK), (dict(rho=0.0), OK), (dict(rho=1.0), OK),
+    (dict(W=0, k=0), OK), (dict(n=50000, k=390), OK),
+    (dict(k=31), ARG), (dict(k=4097), ARG), (dict(rho=1.5), ARG), (dict(rho=-0.1), ARG),
+    (dict(W=4096), ARG), (dict(L=0), ARG),
+])
+def test_anchor_select_ranges(lib, kw, code):
+    assert _anchor_sel(lib, **kw)[0] == code
+
+
+def _anchor_asg(lib, **kw):
+    a = dict(L=2, H=8, d=128, n=4096, k=32)
+    a.update(kw)
+    nb = ctypes.c_size_t(0)
+    return lib.kvsel_anchor_assign(None, None, a["L"], a["H"], a["d"], a["n"], a["k"], None, None,
+                                   None, ctypes.byref(nb), None), nb.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), OK), (dict(k=1), OK), (dict(k=2048, n=300000), OK), (dict(k=4096), UNSUP),
+    (dict(k=0), ARG), (dict(k=5000), ARG), (dict(n=0), ARG), (dict(d=64), UNSUP),
+    (dict(k=2049, n=300000), UNSUP), (dict(L=300, H=300), UNSUP),
+])
+def test_anchor_assign_ranges(lib, kw, code):
+    rc, nb = _anchor_asg(lib, **kw)
+    assert rc == code
+
+
+def test_anchor_assign_workspace(lib):
+    # the gathered anchor rows (k rounded up to 64) and one float per anchor
+    rc, nb = _anchor_asg(lib, L=2, H=8, k=100)
+    assert rc == OK and nb >= 2 * 8 * 128 * (256 + 4)
+
+
+@no_gpu_only
+def test_anchor_pointers(lib):
+    p = ctypes.c_void_p(1 << 20)
+    nb = ctypes.c_size_t(1 << 30)
+    f = lib.kvsel_anchor_select
+    assert f(None, p, 2, 8, 4096, 32, 64, 0.7, p, p, ctypes.byref(nb), None) == ARG
+    assert f(p, None, 2, 8, 4096, 32, 64, 0.7, p, p, ctypes.byref(nb), None) == ARG
+    assert f(p, p, 2, 8, 4096, 32, 64, 0.7, None, p, ctypes.byref(nb), None) == ARG
+    g = lib.kvsel_anchor_assign
+    assert g(None, p, 2, 8, 128, 4096, 32, p, p, p, ctypes.byref(nb), None) == ARG
+    assert g(p, None, 2, 8, 128, 4096, 32, p, p, p, ctypes.byref(nb), None) == ARG
+    assert g(p, p, 2, 8, 128, 4096, 32, None, p, p, ctypes.byref(nb), None) == ARG
+    small = ctypes.c_size_t(16)
+    assert g(p, p, 2, 8, 128, 4096, 32, p, p, p, ctypes.byref(small), None) == WS

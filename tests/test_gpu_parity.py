@@ -342,6 +342,91 @@ def test_score_chunked(case):
         assert_scores_close(s[l], oracle.maxpool(ref, n, pool), f"chunked pooled l{l}")
 
 
+ANCHOR_SELECT_CASES = [
+    # (L, H, n, W, k, rho, levels)
+    (1, 2, 1000, 8, 32, 0.7, 5),
+    (2, 3, 4096, 32, 32, 0.7, 1000),      # window only
+    (1, 2, 3000, 16, 3000, 0.5, 3),       # everything
+    (1, 4, 50000, 32, 390, 0.7, 100),     # many workgroups per head
+    (1, 1, 700, 0, 100, 0.0, 7),          # no window, all random
+    (1, 1, 700, 4, 100, 1.0, 7),          # no random
+]
+
+
+@pytest.mark.parametrize("case", ANCHOR_SELECT_CASES, ids=lambda c: "L{}H{}n{}W{}k{}r{}lv{}".format(*c))
+def test_anchor_select_exact(case):
+    L, H, n, W, k, rho, levels = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    sc = _quantised_scores(rng, (L, H, n - W), levels)
+    rd = (rng.integers(0, 1000, size=(L, H, n - W)) / 1000).astype(np.float32)   # ties in the draws too
+    print(f"[gpu] kvsel_anchor_select case={case}", flush=True)
+    got = kv.kvsel_anchor_select(torch.from_numpy(sc).cuda(), torch.from_numpy(rd).cuda(), n=n, W=W,
+                                 k=k, rho=float(np.float32(rho))).cpu().numpy()
+    for l in range(L):
+        ref = oracle.anchor_select(sc[l].astype(np.float64), rd[l].astype(np.float64), n, W, k,
+                                   float(np.float32(rho)))
+        np.testing.assert_array_equal(got[l], ref)
+
+
+ANCHOR_ASSIGN_CASES = [
+    # (L, H, n, k)
+    (1, 2, 1000, 8),
+    (2, 3, 3000, 24),
+    (1, 1, 5000, 100),       # two anchor tiles, the second partly padding
+    (1, 2, 300, 300),        # every position an anchor
+    (1, 1, 777, 1),
+    (1, 1, 2100, 130),       # three tiles, ragged vectors
+]
+
+
+@pytest.mark.parametrize("case", ANCHOR_ASSIGN_CASES, ids=lambda c: "L{}H{}n{}k{}".format(*c))
+def test_anchor_assign(case):
+    """Exact slot where the fp64 best cosine leads by more than 1e-5; within
+    1e-5 of it otherwise (fp32 dot products decide near-ties). gamma against
+    <x, a>/<a, a> for the chosen anchor in fp64."""
+    L, H, n, k = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    x = rng.standard_normal((L, H, n, 128)).astype(np.float32)
+    anchors = np.sort(np.stack([[rng.choice(n, k, replace=False) for _ in range(H)] for _ in range(L)]),
+                      axis=-1).astype(np.int32)
+    if k >= 4:
+        x[0, 0, anchors[0, 0, 3]] = x[0, 0, anchors[0, 0, 1]]   # a duplicate anchor: ties to slot 1
+        x[0, 0, anchors[0, 0, 2]] = 0.0                         # a zero anchor: never chosen
+        x[0, 0, (anchors[0, 0, 0] + 1) % n] = 0.0               # a zero vector (unless an anchor)
+    xb = synth.bf16_bits(x)
+    print(f"[gpu] kvsel_anchor_assign case={case}", flush=True)
+    slot, gamma = kv.kvsel_anchor_assign(to_dev(xb), torch.from_numpy(anchors).cuda())
+    torch.cuda.synchronize()
+    slot, gamma = slot.cpu().numpy(), gamma.cpu().numpy()
+    xf = synth.bf16_to_f64(xb)
+    for l in range(L):
+        for h in range(H):
+            A = xf[l, h, anchors[l, h]]
+            na = np.sqrt((A * A).sum(1))
+            nx = np.sqrt((xf[l, h] ** 2).sum(1))
+            dots = xf[l, h] @ A.T
+            with np.errstate(divide="ignore", invalid="ignore"):
+                cos = np.where(na > 0, np.nan_to_num(dots / (nx[:, None] * na[None, :])), -np.inf)
+            is_anchor = np.zeros(n, bool)
+            is_anchor[anchors[l, h]] = True
+            np.testing.assert_array_equal(slot[l, h, anchors[l, h]], np.arange(k))
+            np.testing.assert_array_equal(gamma[l, h, anchors[l, h]], 1.0)
+            j = np.nonzero(~is_anchor)[0]
+            s = slot[l, h, j]
+            assert ((s >= 0) & (s < k)).all()
+            best = cos[j].max(axis=1)
+            assert (cos[j, s] >= best - 1e-5).all(), "a chosen anchor is not among the most similar"
+            ref_slot, _ = oracle.anchor_assign(xf[l, h][None], anchors[l, h][None].astype(np.int64))
+            second = np.sort(cos[j], axis=1)[:, -2] if k > 1 else np.full(len(j), -np.inf)
+            clear = best - second > 1e-5
+            np.testing.assert_array_equal(s[clear], ref_slot[0, j][clear])
+            g_ref = dots[j, s] / np.where(na[s] > 0, na[s] ** 2, 1.0)
+            tol = 1e-3 * np.abs(g_ref) + 1e-5 * nx[j] / np.where(na[s] > 0, na[s], 1.0)
+            assert (np.abs(gamma[l, h, j] - g_ref) <= tol).all()
+            if l == 0 and h == 0 and k >= 4:
+                assert not (s == 3).any() and not (s == 2).any()   # duplicate and zero anchors
+
+
 SIGNED_CASES = [
     # (L, H, n, W, frac, adaptive, two_stage)
     (1, 3, 2000, 0, 0.3, False, False),

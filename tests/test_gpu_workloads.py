@@ -239,6 +239,51 @@ def test_headlevel_eviction_full():
     _check_decode(wl, ko, vo, offs, 0)
 
 
+def _check_assign(x_u16, anchors, slot, gamma, what):
+    """Anchors exact; elsewhere the chosen anchor within 1e-5 of the best
+    fp64 cosine (fp32 dot products decide near-ties) and gamma within 1e-3
+    of <x, a>/<a, a> for it (plus 1e-5 |x|/|a| for near-zero gamma)."""
+    xf = synth.bf16_to_f64(x_u16)
+    H, n, _ = xf.shape
+    for h in range(H):
+        a_pos = anchors[h]
+        A = xf[h, a_pos]
+        na = np.sqrt((A * A).sum(1))
+        nx = np.sqrt((xf[h] ** 2).sum(1))
+        dots = xf[h] @ A.T
+        cos = dots / (nx[:, None] * na[None, :])
+        np.testing.assert_array_equal(slot[h, a_pos], np.arange(len(a_pos)), err_msg=what)
+        np.testing.assert_array_equal(gamma[h, a_pos], 1.0, err_msg=what)
+        j = np.setdiff1d(np.arange(n), a_pos)
+        s = slot[h, j]
+        assert (cos[j, s] >= cos[j].max(axis=1) - 1e-5).all(), f"{what} h{h}: slots"
+        g_ref = dots[j, s] / na[s] ** 2
+        assert (np.abs(gamma[h, j] - g_ref) <= 1e-3 * np.abs(g_ref) + 1e-5 * nx[j] / na[s]).all(), \
+            f"{what} h{h}: gamma"
+
+
+def test_anchorkv_full():
+    wl = synth.WORKLOADS["anchorkv_llama8b_n32k"]
+    sampled = [0, wl.L - 1]
+    dev, host = device_inputs(wl, set(sampled), ("q", "k", "v"))
+    s, r = _score(wl, dev)
+    _check_scores(wl, s, r, host, [0])
+    rand = synth.gen_rand(wl, SEED)
+    print("[gpu] kvsel_anchor_select + kvsel_anchor_assign full", flush=True)
+    anchors = kv.kvsel_anchor_select(s, torch.from_numpy(rand).cuda(), n=wl.n, W=wl.W,
+                                     k=wl.anchor_k, rho=wl.rho)
+    ks, kg = kv.kvsel_anchor_assign(dev["k"], anchors)
+    vs, vg = kv.kvsel_anchor_assign(dev["v"], anchors)
+    torch.cuda.synchronize()
+    s_h, a_h = s.cpu().numpy(), anchors.cpu().numpy()
+    for l in sampled:
+        ref = oracle.anchor_select(s_h[l].astype(np.float64), rand[l].astype(np.float64), wl.n, wl.W,
+                                   wl.anchor_k, float(np.float32(wl.rho)))
+        np.testing.assert_array_equal(a_h[l], ref)
+        _check_assign(host[("k", l)], a_h[l], ks[l].cpu().numpy(), kg[l].cpu().numpy(), f"keys l{l}")
+        _check_assign(host[("v", l)], a_h[l], vs[l].cpu().numpy(), vg[l].cpu().numpy(), f"values l{l}")
+
+
 @pytest.mark.parametrize("name", ["criticalkv_llama8b_n128k", "criticaladakv_llama8b_n32k",
                                   "criticalkv_l2_llama8b_n128k"])
 def test_criticalkv_full(name):
