@@ -179,6 +179,122 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign(const __bf16* __restri
   }
 }
 
+// Up to kResAnchors anchors per head: the whole anchor block stays in LDS
+// (filled once by direct-to-LDS loads, swizzled like a ring slot) and a
+// workgroup streams kResBlocks blocks of 256 vectors of its head through
+// it, the next block's vectors loading into registers while the current
+// block is compared against every anchor.
+constexpr int kResAnchors = 256;            // 64 KB of anchor rows
+constexpr int kResBlocks = 16;              // vector blocks per workgroup
+
+// 1-D grid of groups * H * L workgroups (groups = ceil(key_blocks /
+// kResBlocks)), block 256.
+__global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __restrict__ x,
+                                                              const __bf16* __restrict__ arows,
+                                                              const float* __restrict__ rinv_g,
+                                                              int H, int n, int kpad,
+                                                              int key_blocks, int groups,
+                                                              int32_t* __restrict__ slot_out,
+                                                              float* __restrict__ gamma_out) {
+  __shared__ __align__(16) unsigned char abuf[kResAnchors / gTile][gRowsBytes];
+  __shared__ __align__(16) float rinv[kResAnchors];
+  __shared__ __align__(16) float pen[kResAnchors];
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = id % groups;
+  id /= groups;
+  const int h = id % H, l = id / H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+  const size_t lh = (size_t)l * H + h;
+  const int ntiles = kpad / gTile;
+  const int b0 = grp * kResBlocks, b1 = min(key_blocks, b0 + kResBlocks);
+
+  // every anchor tile into LDS once
+  {
+    AsLoader ld;
+    ld.init(kHeadDim);
+    const __bf16* ah = arows + lh * (size_t)kpad * kHeadDim;
+    for (int t = 0; t < ntiles; ++t) ld.issue(ah, t * gTile, kpad, kHeadDim, abuf[t]);
+  }
+  for (int s = threadIdx.x; s < kpad; s += 256) {
+    const float r = rinv_g[lh * kpad + s];
+    rinv[s] = r;
+    pen[s] = r > 0.f ? 0.f : neg_inf();
+  }
+  auto load_vecs = [&](int b, bf16x8 (&v)[2][8]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int key = b * kAsBlock + wave * 64 + nt * 32 + col;
+      if (key < n) load_half_row(x + (lh * n + key) * (size_t)kHeadDim, hf, v[nt]);
+      else zero_ops(v[nt]);
+    }
+  };
+  bf16x8 vcur[2][8], vnext[2][8];
+  load_vecs(b0, vcur);
+  __syncthreads();   // the anchors, their table and the first vectors are in place
+
+  for (int b = b0; b < b1; ++b) {
+    if (b + 1 < b1) load_vecs(b + 1, vnext);   // in flight during this block
+    const int key0 = b * kAsBlock + wave * 64;
+    float best[2] = {neg_inf(), neg_inf()};
+    int bslot[2] = {0, 0};
+    if (key0 < n) {
+      for (int t = 0; t < ntiles; ++t) {
+        const unsigned char* slot = abuf[t];
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+        bf16x8 a[2][2];
+        read_step(slot, col, hf, 0, a[0]);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
+          tile_step(a[st & 1], vcur, st, acc);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int s0 = t * gTile + mt * 32 + acc_row(4 * j, lane);
+            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rinv[s0]);
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&pen[s0]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int nt = 0; nt < 2; ++nt) {
+                const float sc = __builtin_fmaf(acc[mt][nt][4 * j + u], r4[u], p4[u]);
+                if (sc > best[nt]) {
+                  best[nt] = sc;
+                  bslot[nt] = s0 + u;
+                }
+              }
+          }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float ob = __shfl_xor(best[nt], 32);
+        const int os = __shfl_xor(bslot[nt], 32);
+        if (ob > best[nt] || (ob == best[nt] && os < bslot[nt])) {
+          best[nt] = ob;
+          bslot[nt] = os;
+        }
+        const int key = key0 + nt * 32 + col;
+        if (hf == 0 && key < n) {
+          const float g = best[nt] * rinv[bslot[nt]];
+          slot_out[lh * n + key] = bslot[nt];
+          gamma_out[lh * n + key] = best[nt] > neg_inf() ? g : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) vcur[nt][s8] = vnext[nt][s8];
+  }
+}
+
 // grid (ceil(k/256), L*H): anchor positions to their own slot
 __global__ __launch_bounds__(256) void k_anchor_self(const int32_t* __restrict__ anchors, int n,
                                                      int k, int32_t* __restrict__ slot_out,
@@ -210,9 +326,16 @@ hipError_t anchor_assign_launch(const void* x, const int32_t* anchors, int L, in
   if (blocks > 0x7fffffffLL || LH > 65535u) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_anchor_gather, dim3(kpad, (unsigned)LH), dim3(64), 0, st,
                      static_cast<const u32x4*>(x), anchors, n, k, kpad, arows, rinv);
-  hipLaunchKernelGGL(k_anchor_assign, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const __bf16*>(x), reinterpret_cast<const __bf16*>(arows), rinv, H,
-                     n, kpad, key_blocks, slot, gamma);
+  if (kpad <= kResAnchors) {
+    const int groups = (key_blocks + kResBlocks - 1) / kResBlocks;
+    hipLaunchKernelGGL(k_anchor_assign_res, dim3((unsigned)((long long)groups * H * L)), dim3(256),
+                       0, st, static_cast<const __bf16*>(x), reinterpret_cast<const __bf16*>(arows),
+                       rinv, H, n, kpad, key_blocks, groups, slot, gamma);
+  } else {
+    hipLaunchKernelGGL(k_anchor_assign, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const __bf16*>(x), reinterpret_cast<const __bf16*>(arows), rinv,
+                       H, n, kpad, key_blocks, slot, gamma);
+  }
   hipLaunchKernelGGL(k_anchor_self, dim3((k + 255) / 256, (unsigned)LH), dim3(256), 0, st, anchors,
                      n, k, slot, gamma);
   return hipGetLastError();
