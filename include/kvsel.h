@@ -83,9 +83,9 @@ enum {
  * [KVzip] §2.2): logits s = scale * <q[l][hq][i], k[l][h][j]>, a softmax
  * over the keys each query sees (all n, or causal in window mode; none for
  * KVSEL_AGG_LOGIT_MAX), the aggregate over (g, i) chosen by `agg`, then
- * 1-D max-pooling of width
- * `pool` along the candidate positions ([CriticalKV] §3.3, Algorithm 2,
- * step 4; stride 1, centred, neighbours outside [0, n_cand) ignored).
+ * 1-D max-pooling of width `pool` along the candidate positions
+ * ([CriticalKV] §3.3, Algorithm 2, step 4; stride 1, centred, neighbours
+ * outside [0, n_cand) ignored).
  *
  *   q      bf16 [L][H_kv*G][W][d]
  *   k      bf16 [L][H_kv][n][d]
@@ -121,7 +121,7 @@ int32_t kvsel_score(const void* q, const void* k,
  * kvsel_score. Inputs hold every chunk at the full n_in = n_prompt + m:
  *
  *   q      bf16 [L][T][H_kv*G][n_in][d]  chunk t's queries (rows past n_in_t
- *                                        are ignored)
+ *                                        are ignored but must be finite)
  *   k      bf16 [L][H_kv][n][d]          the cache
  *   k_self bf16 [L][T][H_kv][n_in][d]    chunk t's own keys (rows past n_in_t
  *                                        are ignored)
