@@ -501,24 +501,44 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
 }
 
 // ------------------------------------------------------------------ pool ----
-// scores[j] = max raw[t], |t - j| <= r, 0 <= t < n_cand.   grid (.., L*H)
+// scores[j] = max raw[t], |t - j| <= r, 0 <= t < n_cand.
+// grid (ceil(n_cand / kPoolSpan), L*H), block 256. A block stages its
+// kPoolSpan + 2r raw values in LDS with all of a thread's loads in flight,
+// then each thread writes kPoolOut outputs 256 apart (conflict-free LDS
+// reads, coalesced stores).
+constexpr int kPoolOut = 4;
+constexpr int kPoolSpan = 256 * kPoolOut;
+
 __global__ __launch_bounds__(256) void k_pool(const float* __restrict__ raw, int n,
                                               int n_cand, int r,
                                               float* __restrict__ scores) {
-  __shared__ float tile[256 + 2 * 32];
+  __shared__ float tile[kPoolSpan + 2 * 32];
   const size_t lh = blockIdx.y;
-  const int j0 = blockIdx.x * 256;
+  const int j0 = blockIdx.x * kPoolSpan;
   const float* src = raw + lh * n;
-  for (int t = threadIdx.x; t < 256 + 2 * r; t += 256) {
+  const int tid = threadIdx.x;
+  const int span = kPoolSpan + 2 * r;
+  float v[kPoolOut + 1];
+#pragma unroll
+  for (int u = 0; u <= kPoolOut; ++u) {
+    const int t = tid + u * 256;
     const int j = j0 - r + t;
-    tile[t] = (j >= 0 && j < n_cand) ? src[j] : neg_inf();  // outside the candidates: no part
+    // outside the candidates: no part
+    v[u] = (t < span && j >= 0 && j < n_cand) ? src[j] : neg_inf();
   }
+#pragma unroll
+  for (int u = 0; u <= kPoolOut; ++u)
+    if (tid + u * 256 < span) tile[tid + u * 256] = v[u];
   __syncthreads();
-  const int j = j0 + threadIdx.x;
-  if (j >= n_cand) return;
-  float m = tile[threadIdx.x + r];
-  for (int o = 1; o <= r; ++o) m = fmaxf(m, fmaxf(tile[threadIdx.x + r - o], tile[threadIdx.x + r + o]));
-  scores[lh * n_cand + j] = m;
+#pragma unroll
+  for (int u = 0; u < kPoolOut; ++u) {
+    const int c = tid + u * 256;
+    if (j0 + c < n_cand) {
+      float m = tile[c + r];
+      for (int o = 1; o <= r; ++o) m = fmaxf(m, fmaxf(tile[c + r - o], tile[c + r + o]));
+      scores[lh * n_cand + j0 + c] = m;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ host ----
@@ -532,8 +552,8 @@ hipError_t combine_launch(const float2* part, int L, int H, int R, int splits, f
 
 hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r, float* scores,
                        hipStream_t st) {
-  hipLaunchKernelGGL(k_pool, dim3((n_cand + 255) / 256, L * H), dim3(256), 0, st, raw, n,
-                     n_cand, r, scores);
+  hipLaunchKernelGGL(k_pool, dim3((n_cand + kPoolSpan - 1) / kPoolSpan, L * H), dim3(256), 0,
+                     st, raw, n, n_cand, r, scores);
   return hipGetLastError();
 }
 

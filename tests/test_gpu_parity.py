@@ -47,10 +47,10 @@ WINDOW_CASES = [
     dict(n=300, W=16, pool=5, agg="max"),
     dict(n=1500, W=40, G=4),               # R = 160 rows: more than one row block
     dict(n=4096, W=32, heavy="uniform1pct"),
-    # one-pass kernel: chunk boundaries (256 keys) against pool halos
+    # workgroup key ranges (128 keys at these sizes) against pool halos
     dict(n=513, W=1, G=1, pool=17),
-    dict(n=768, W=32, pool=7),             # candidates end inside a chunk
-    dict(n=771, W=3, G=4, pool=9),         # 4 chunks, last chunk 3 keys
+    dict(n=768, W=32, pool=7),             # candidates end inside a range
+    dict(n=771, W=3, G=4, pool=9),         # 7 ranges, the last one 3 keys
     dict(L=3, H_kv=2, n=2048, W=8, G=8),   # R = 64
     dict(n=1000, W=30, G=3, pool=1),       # R = 90, no pooling
     # general kernels (R > 128): several 512-row blocks, ragged row / key tails
@@ -70,6 +70,31 @@ def test_window_scores(case):
         assert_scores_close(scores[l], ref_pool, "pooled")
         if wl.agg == "sum":
             np.testing.assert_allclose(raw[l].astype(np.float64).sum(axis=1), wl.W * wl.G, rtol=1e-5)
+
+
+POOL_CASES = WINDOW_CASES + [
+    dict(n=3000, W=32, pool=65),                   # r = 32: the widest halo
+    dict(L=2, H_kv=2, n=5000, W=7, pool=33, agg="max"),
+    dict(n=4160, W=100, G=1, pool=63),             # candidates end before the last range
+    dict(L=4, H_kv=8, n=20000, W=32, pool=7),      # many pooling blocks per head
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES,
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_pool_with_and_without_raw(case):
+    """The pooled scores are the same bits whether the raw sums are returned
+    or kept in the workspace, on every call, and match the oracle."""
+    wl = _wl(**case)
+    data = gen(wl, seed=4, which=("q", "k"))
+    with_raw, _ = _run_scores(wl, data, return_raw=True)
+    alone, raw = _run_scores(wl, data, return_raw=False)
+    assert raw is None
+    np.testing.assert_array_equal(alone, with_raw)
+    again, _ = _run_scores(wl, data, return_raw=False)
+    np.testing.assert_array_equal(again, alone)
+    _, ref_pool = oracle_scores_layer(wl, data["q"][0], data["k"][0])
+    assert_scores_close(alone[0], ref_pool, "pooled")
 
 
 EXTERNAL_CASES = [

@@ -52,12 +52,18 @@ def device_inputs(wl: synth.Workload, sampled, which):
     return dev, host
 
 
+def _mode(wl):
+    return kv.Q_WINDOW if wl.q_mode == "window" else kv.Q_EXTERNAL
+
+
+def _agg(wl):
+    return {"sum": kv.AGG_SUM, "max": kv.AGG_MAX, "logit": kv.AGG_LOGIT_MAX}[wl.agg]
+
+
 def _score(wl, dev):
-    mode = kv.Q_WINDOW if wl.q_mode == "window" else kv.Q_EXTERNAL
-    agg = {"sum": kv.AGG_SUM, "max": kv.AGG_MAX, "logit": kv.AGG_LOGIT_MAX}[wl.agg]
     print(f"[gpu] kvsel_score {wl.name}", flush=True)
-    s, r = kv.kvsel_score(dev["q"], dev["k"], G=wl.G, q_mode=mode, agg=agg, scale=wl.scale,
-                          pool=wl.pool, return_raw=True)
+    s, r = kv.kvsel_score(dev["q"], dev["k"], G=wl.G, q_mode=_mode(wl), agg=_agg(wl),
+                          scale=wl.scale, pool=wl.pool, return_raw=True)
     torch.cuda.synchronize()
     return s, r
 
@@ -138,6 +144,14 @@ def test_window_workload_full(name):
     dev, host = device_inputs(wl, set(sampled), ("q", "k", "v"))
     s, r = _score(wl, dev)
     _check_scores(wl, s, r, host, sampled)
+    # without a raw output (the call the bench times) the pooled scores are
+    # the same bits
+    print(f"[gpu] kvsel_score {wl.name} (no raw output)", flush=True)
+    s2, _ = kv.kvsel_score(dev["q"], dev["k"], G=wl.G, q_mode=_mode(wl), agg=_agg(wl),
+                           scale=wl.scale, pool=wl.pool)
+    torch.cuda.synchronize()
+    assert torch.equal(s2, s), "pooled scores depend on whether raw sums are returned"
+    del s2
     idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=wl.W, budget=wl.budget, adaptive=wl.adaptive,
                                        return_stage=True)
     torch.cuda.synchronize()
