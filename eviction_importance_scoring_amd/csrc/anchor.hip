@@ -37,6 +37,14 @@ constexpr int kAsLoads = AsLoader::kLoads;
 
 int anchor_kpad(int k) { return (k + gTile - 1) / gTile * gTile; }
 
+// A slot's score is <x, a> * scale. The scale is 1/|a|, or NaN for a zero
+// or padding anchor: its score compares greater than nothing, so it is
+// never chosen (and a real anchor's score is the same single rounding of
+// <x, a> / |a| as before).
+__device__ __forceinline__ float score_scale(float r) {
+  return r > 0.f ? r : __builtin_nanf("");
+}
+
 // grid (kpad, L*H), block 64: one anchor row per workgroup, its 16-byte
 // pieces on 16 lanes (the other 48 idle; the gather is tiny)
 __global__ __launch_bounds__(64) void k_anchor_gather(const u32x4* __restrict__ x,
@@ -75,9 +83,7 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign(const __bf16* __restri
                                                           int32_t* __restrict__ slot_out,
                                                           float* __restrict__ gamma_out) {
   __shared__ __align__(16) unsigned char ring[gSlots][gRowsBytes];
-  // per slot: 1/|a|, and 0 or -inf (an anchor never chosen) added to its score
-  __shared__ __align__(16) float rinv[kMaxAnchorPad];
-  __shared__ __align__(16) float pen[kMaxAnchorPad];
+  __shared__ __align__(16) float rinv[kMaxAnchorPad];   // score_scale per slot
   int id = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = id % key_blocks;
   id /= key_blocks;
@@ -96,11 +102,7 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign(const __bf16* __restri
     if (key < n) load_half_row(x + (lh * n + key) * (size_t)kHeadDim, hf, vop[nt]);
     else zero_ops(vop[nt]);
   }
-  for (int s = threadIdx.x; s < kpad; s += 256) {
-    const float r = rinv_g[lh * kpad + s];
-    rinv[s] = r;
-    pen[s] = r > 0.f ? 0.f : neg_inf();
-  }
+  for (int s = threadIdx.x; s < kpad; s += 256) rinv[s] = score_scale(rinv_g[lh * kpad + s]);
   AsLoader ld;
   ld.init(kHeadDim);
   auto issue = [&](int t, int slot) { ld.issue(ah, t * gTile, kpad, kHeadDim, ring[slot]); };
@@ -146,12 +148,11 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign(const __bf16* __restri
       for (int j = 0; j < 4; ++j) {
         const int s0 = t * gTile + mt * 32 + acc_row(4 * j, lane);
         const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rinv[s0]);
-        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&pen[s0]);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
-            const float sc = __builtin_fmaf(acc[mt][nt][4 * j + u], r4[u], p4[u]);
+            const float sc = acc[mt][nt][4 * j + u] * r4[u];
             if (sc > best[nt]) {
               best[nt] = sc;
               bslot[nt] = s0 + u;
@@ -197,8 +198,7 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
                                                               int32_t* __restrict__ slot_out,
                                                               float* __restrict__ gamma_out) {
   __shared__ __align__(16) unsigned char abuf[kResAnchors / gTile][gRowsBytes];
-  __shared__ __align__(16) float rinv[kResAnchors];
-  __shared__ __align__(16) float pen[kResAnchors];
+  __shared__ __align__(16) float rinv[kResAnchors];   // score_scale per slot
   int id = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = id % groups;
   id /= groups;
@@ -216,11 +216,7 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
     const __bf16* ah = arows + lh * (size_t)kpad * kHeadDim;
     for (int t = 0; t < ntiles; ++t) ld.issue(ah, t * gTile, kpad, kHeadDim, abuf[t]);
   }
-  for (int s = threadIdx.x; s < kpad; s += 256) {
-    const float r = rinv_g[lh * kpad + s];
-    rinv[s] = r;
-    pen[s] = r > 0.f ? 0.f : neg_inf();
-  }
+  for (int s = threadIdx.x; s < kpad; s += 256) rinv[s] = score_scale(rinv_g[lh * kpad + s]);
   auto load_vecs = [&](int b, bf16x8 (&v)[2][8]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -233,44 +229,81 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
   load_vecs(b0, vcur);
   __syncthreads();   // the anchors, their table and the first vectors are in place
 
+  // Half-tile u covers anchor slots [32u, 32u + 32): its 16 MFMAs (8 head-
+  // dim steps x 2 vector sets) run while the argmax of half-tile u-1 is
+  // done in eight parts between them, two accumulator pairs in turn.
+  const int nh = 2 * ntiles;
+  auto half_op = [&](int u, int st) -> bf16x8 {
+    return gen_op(abuf[u >> 1], (u & 1) * 32 + col, hf, st);
+  };
+  float best[2];
+  int bslot[2];
+  int bcode[2];   // 8j + e of this half-tile's best row so far, -1 if none
+  // the four scales of rows 4j..4j+3 of half-tile u (consecutive slots)
+  auto scales = [&](int u, int j) -> f32x4 {
+    return *reinterpret_cast<const f32x4*>(&rinv[u * 32 + acc_row(4 * j, lane)]);
+  };
+  // part c of the argmax of half-tile u: slots 32u + 8j + 4hf + e (e < 4),
+  // j = c / 2, of vector set c % 2 (slots rise with j for each set)
+  auto arg_part = [&](int u, const f32x16 (&acc)[2], int c, const f32x4& r4) {
+    const int j = c >> 1, nt = c & 1;
+    if (j == 0) bcode[nt] = -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sc = acc[nt][4 * j + e] * r4[e];
+      if (sc > best[nt]) {
+        best[nt] = sc;
+        bcode[nt] = 8 * j + e;
+      }
+    }
+    if (j == 3 && bcode[nt] >= 0) bslot[nt] = u * 32 + 4 * hf + bcode[nt];
+  };
+  // MFMAs of half-tile u into cur, argmax of half-tile u-1 from prev
+  auto half = [&](int u, f32x16 (&cur)[2], const f32x16 (&prev)[2]) {
+    bf16x8 op[2];
+    f32x4 r4;
+    op[0] = half_op(u, 0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) op[(st + 1) & 1] = half_op(u, st + 1);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        cur[nt] = mfma32(op[st & 1], vcur[nt][st], st == 0 ? zero16() : cur[nt]);
+      if ((st & 1) == 0) r4 = scales(u - 1, st >> 1);   // shared by both vector sets
+      arg_part(u - 1, prev, st, r4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   for (int b = b0; b < b1; ++b) {
     if (b + 1 < b1) load_vecs(b + 1, vnext);   // in flight during this block
     const int key0 = b * kAsBlock + wave * 64;
-    float best[2] = {neg_inf(), neg_inf()};
-    int bslot[2] = {0, 0};
+    best[0] = best[1] = neg_inf();
+    bslot[0] = bslot[1] = 0;
     if (key0 < n) {
-      for (int t = 0; t < ntiles; ++t) {
-        const unsigned char* slot = abuf[t];
-        f32x16 acc[2][2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
-        bf16x8 a[2][2];
-        read_step(slot, col, hf, 0, a[0]);
+      f32x16 A[2], B[2];
+      {
+        bf16x8 op[2];
+        op[0] = half_op(0, 0);
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-          if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
-          tile_step(a[st & 1], vcur, st, acc);
+          if (st + 1 < 8) op[(st + 1) & 1] = half_op(0, st + 1);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            A[nt] = mfma32(op[st & 1], vcur[nt][st], st == 0 ? zero16() : A[nt]);
         }
+      }
+      int u = 1;
+      for (; u + 1 < nh; u += 2) {
+        half(u, B, A);
+        half(u + 1, A, B);
+      }
+      half(u, B, A);   // nh is even: the last half-tile is odd
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int s0 = t * gTile + mt * 32 + acc_row(4 * j, lane);
-            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rinv[s0]);
-            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&pen[s0]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-              for (int nt = 0; nt < 2; ++nt) {
-                const float sc = __builtin_fmaf(acc[mt][nt][4 * j + u], r4[u], p4[u]);
-                if (sc > best[nt]) {
-                  best[nt] = sc;
-                  bslot[nt] = s0 + u;
-                }
-              }
-          }
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 r4 = scales(u, j);
+        arg_part(u, B, 2 * j, r4);
+        arg_part(u, B, 2 * j + 1, r4);
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {

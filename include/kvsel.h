@@ -364,7 +364,9 @@ int32_t kvsel_anchor_select(const float* scores, const float* rand,
  *
  * Limits: d == 128, k <= 2048, L*H_kv <= 65535 (else
  * KVSEL_ERR_UNSUPPORTED). Anchor positions outside [0, n) count as zero
- * vectors. Needs a workspace (protocol above).
+ * vectors. Positions are expected to be distinct (kvsel_anchor_select's
+ * are); a position listed twice maps to one of its slots, which one is
+ * unspecified. Needs a workspace (protocol above).
  */
 int32_t kvsel_anchor_assign(const void* x, const int32_t* anchors,
                             int32_t L, int32_t H_kv, int32_t d, int32_t n,
