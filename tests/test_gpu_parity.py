@@ -539,6 +539,45 @@ def test_head_level_eviction_pipeline():
             np.testing.assert_array_equal(idx[l, offs[l, h]:offs[l, h + 1]], want)
 
 
+def test_largest_head():
+    """The largest head the scoring accepts (n * 256 B just under 2^31), with
+    every key equal: each window row's softmax is then uniform over the keys
+    it sees, so every score has a closed form; all candidates tie, so the
+    selection (many workgroups at this size) keeps the lowest ones; the
+    compaction copies the value rows they name."""
+    n, W, G, budget = 8_388_607, 32, 4, 1000
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    row = torch.randn(128, device=dev, generator=g).to(torch.bfloat16)
+    k = row.expand(1, 1, n, 128).contiguous()
+    q = torch.randn((1, G, W, 128), device=dev, generator=g).to(torch.bfloat16)
+    print(f"[gpu] kvsel_score largest head n={n}", flush=True)
+    scores, raw = kv.kvsel_score(q, k, G=G, pool=7, return_raw=True)
+    torch.cuda.synchronize()
+    # window row i (query position n - W + i) sees keys 0 .. n - W + i
+    inv = 1.0 / (n - W + np.arange(W) + 1.0)
+    tail = G * np.cumsum(inv[::-1])[::-1]            # key n - W + t: rows t .. W - 1
+    ref_raw = np.full(n, G * inv.sum())
+    ref_raw[n - W:] = tail
+    assert_scores_close(raw.cpu().numpy()[0], ref_raw[None], "raw")
+    assert_scores_close(scores.cpu().numpy()[0], np.full((1, n - W), G * inv.sum()), "pooled")
+    del raw
+    print("[gpu] kvsel_select largest head", flush=True)
+    idx, _, _ = kv.kvsel_select(scores, n=n, W=W, budget=budget)
+    torch.cuda.synchronize()
+    want = np.concatenate([np.arange(budget - W), np.arange(n - W, n)])
+    np.testing.assert_array_equal(idx.cpu().numpy()[0, 0], want)
+    del scores, k
+    v = torch.randn((1, 1, n, 128), device=dev, generator=g).to(torch.bfloat16)
+    print("[gpu] kvsel_compact largest head", flush=True)
+    k_out, v_out = kv.kvsel_compact(v, v, idx)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(want).to(dev)
+    assert torch.equal(v_out.reshape(-1, 128), v[0, 0, sel])
+    assert torch.equal(k_out, v_out)
+
+
 def test_select_end_to_end_band():
     """GPU scores + GPU select against the fp64 oracle's selection."""
     wl = _wl(L=2, H_kv=2, n=3000, W=32)
