@@ -115,8 +115,20 @@ __device__ __forceinline__ void fill_row_tail(int32_t* idx, uint8_t* stage, int6
   }
 }
 
+// The resident select's digit histogram: kHistCopies copies of 16-bit
+// counters, two bins a word (bin 2w in the low half of word w, 2w+1 in the
+// high half). Lane l adds to copy l % kHistCopies, so the lanes of one
+// atomic instruction that hit the same bin (common on the first digit,
+// where keys crowd a few exponent bins) are spread over that many words;
+// copies lie kCopyWords apart, an odd count, so those words sit in
+// different banks. A copy sees at most ceil(len / kHistCopies) keys, which
+// keeps every counter below 2^16.
+constexpr int kHistCopies = 4;
+constexpr int kCopyWords = kBins / 2 + 1;
+static_assert((kResidentMax + kHistCopies * kSelThreads) / kHistCopies < 65536, "16-bit counters");
+
 struct alignas(16) SelShared {   // a multiple of 16 bytes: the keys follow it
-  uint32_t hist[kBins];
+  uint32_t hist[kHistCopies * kCopyWords];
   uint32_t sbuf[32];
   uint32_t group_start[kMaxGroups];
   uint64_t prefix;
@@ -211,8 +223,9 @@ __device__ SelCut radix_select(SelShared& sm, const uint32_t* bits, uint32_t len
     const uint32_t need = sm.need;
     const int wdt = digit_width(shift);
     const int nb = 1 << wdt;
-    for (int b = tid; b < kBins; b += kSelThreads) sm.hist[b] = 0;
+    for (int w = tid; w < kHistCopies * kCopyWords; w += kSelThreads) sm.hist[w] = 0;
     __syncthreads();
+    const uint32_t cbase = (uint32_t)(tid & (kHistCopies - 1)) * kCopyWords;
     if (shift - wdt >= 31 && (len & 3u) == 0) {
       // the digit lies in the score bits: 32-bit compares on 4 keys a read
       const uint32_t sh = shift - 31, dsh = shift - wdt - 31, p32 = (uint32_t)prefix;
@@ -221,21 +234,33 @@ __device__ SelCut radix_select(SelShared& sm, const uint32_t* bits, uint32_t len
         const u32x4 v = b4[i];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if ((uint32_t)((uint64_t)v[c] >> sh) == p32)   // sh may be 31
-            atomicAdd(&sm.hist[(v[c] >> dsh) & (nb - 1)], 1u);
+          if ((uint32_t)((uint64_t)v[c] >> sh) == p32) {   // sh may be 31
+            const uint32_t bin = (v[c] >> dsh) & (nb - 1);
+            atomicAdd(&sm.hist[cbase + (bin >> 1)], 1u << ((bin & 1u) << 4));
+          }
       }
     } else {
       for (uint32_t f = tid; f < len; f += kSelThreads) {
         const uint64_t key = make_key(bits[f], f);
-        if ((key >> shift) == prefix)
-          atomicAdd(&sm.hist[(uint32_t)(key >> (shift - wdt)) & (nb - 1)], 1u);
+        if ((key >> shift) == prefix) {
+          const uint32_t bin = (uint32_t)(key >> (shift - wdt)) & (nb - 1);
+          atomicAdd(&sm.hist[cbase + (bin >> 1)], 1u << ((bin & 1u) << 4));
+        }
       }
     }
     __syncthreads();
-    // bins in descending order: thread t holds bins nb-1-2t and nb-2-2t
+    // bins in descending order: thread t holds bins nb-1-2t and nb-2-2t,
+    // the high and low halves of word nb/2-1-t in every copy
     const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
-    const uint32_t h0 = b0 >= 0 ? sm.hist[b0] : 0u;
-    const uint32_t h1 = b1 >= 0 ? sm.hist[b1] : 0u;
+    uint32_t h0 = 0u, h1 = 0u;
+    if (b0 >= 0) {
+#pragma unroll
+      for (int c = 0; c < kHistCopies; ++c) {
+        const uint32_t x = sm.hist[c * kCopyWords + (b0 >> 1)];
+        h0 += x >> 16;
+        h1 += x & 0xFFFFu;
+      }
+    }
     uint32_t tot;
     const uint32_t above = block_excl_scan(h0 + h1, sm.sbuf, tot);
     if (above < need && need <= above + h0) {
@@ -936,6 +961,8 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
 }
 
 static size_t lds_bytes(uint32_t len) { return sizeof(SelShared) + (size_t)len * sizeof(uint32_t); }
+static_assert(sizeof(SelShared) + (size_t)kResidentMax * sizeof(uint32_t) <= 160 * 1024,
+              "a resident segment and the shared state fit the CU's LDS");
 
 size_t select_ws_bytes(const SelectPlan& p) { return use_multi(p) ? msel_layout(p).bytes : 0; }
 
