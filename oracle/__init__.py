@@ -28,7 +28,8 @@ Readings taken where the pages are silent (each repeated where it is used):
             only; out-of-range neighbours are ignored.
   weight    value weight of KV head h at position j:
             mean over g of || W_O[:, slice(h*G+g)] v_j ||_1, in fp64
-            (|| . ||_2 for the L2 variant).
+            (|| . ||_2 for the L2 variant); or, summed over the group,
+            || sum_g W_O[:, slice(h*G+g)] v_j ||_1.
   key       two-stage key = (pooled * score_norm + eps) * weight, applied
             after pooling; stage 1 takes floor(alpha*k) by pooled score.
   ties      larger key first; equal keys go to the lower index (adaptive:
@@ -43,6 +44,7 @@ import numpy as np
 
 __all__ = [
     "window_raw_scores", "external_raw_scores", "maxpool", "value_weight",
+    "value_weight_group_sum",
     "topk_indices", "select_layer", "compact_layer",
 ]
 
@@ -251,6 +253,35 @@ def value_weight(v: np.ndarray, w_o: np.ndarray, G: int,
             proj = vh @ w_slice.T                      # [m][D] rows of V W^O
             out[h] += np.abs(proj).sum(axis=1)
         out[h] /= G
+    return out
+
+
+def value_weight_group_sum(v: np.ndarray, w_o: np.ndarray, G: int,
+                           positions: np.ndarray | None = None) -> np.ndarray:
+    """CriticalKV's projected-value norm with the GQA group summed first.
+
+    [CriticalKV, §3.3 Algorithm 1, steps 2-3]: V_proj = V W^O, then the L1
+    norm of each row. The alternative GQA reading: the G query heads that
+    share KV head h see the same value row, and their attention outputs
+    enter the output projection side by side, so one projected row per KV
+    head is (sum_g W_O^(h,g)) v_j, with W_O^(h,g) the D x d column slice of
+    query head h*G+g. This is the size of the V W^O intermediate that
+    [CriticalKV, §D.4] quotes (one D-vector per KV head and position).
+    Weight = || (sum_g W_O^(h,g)) v_j ||_1, the slices summed exactly.
+
+    v: [H_kv][n][d], w_o: [D][H_kv*G*d]. Returns [H_kv][len(positions)].
+    """
+    H, n, d = v.shape
+    if positions is None:
+        positions = np.arange(n)
+    out = np.zeros((H, len(positions)))
+    for h in range(H):
+        w_sum = np.zeros((w_o.shape[0], d))
+        for g in range(G):
+            hq = h * G + g
+            w_sum += w_o[:, hq * d:(hq + 1) * d]      # [D][d]
+        proj = v[h, positions] @ w_sum.T              # [m][D]
+        out[h] = np.abs(proj).sum(axis=1)
     return out
 
 

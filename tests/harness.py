@@ -4,10 +4,9 @@ comparison rules between the HIP path and the oracle.
 Score rule (fp32 accumulation from bf16 inputs against the fp64 oracle):
     |gpu - ref| <= RTOL * |ref| + ATOL_REL * max(ref of that head)
 RTOL = 1e-3 is the relative error the scores must meet. The absolute floor
-(1e-6 of the head's largest score) only covers entries whose exact value
-is below fp32 resolution of that head's softmax terms, e.g. keys whose
-every weight underflows; select_tolerance_ok() checks that no such entry
-sits at a selection boundary.
+tau = ATOL_REL * max (1e-6 of the head's largest score) only covers entries
+whose exact value is below fp32 resolution of that head's softmax terms,
+e.g. keys whose every weight underflows.
 
 Logit rule (KVzip-logit scores, any sign): |gpu - ref| <= RTOL * |ref| +
 LOGIT_ATOL_REL * max |ref| of that head. A logit is an fp32 sum of 128
@@ -15,9 +14,12 @@ exact bf16 products: its absolute error scales with the terms, not with
 the (possibly cancelling) sum, so near-zero logits get the floor.
 
 Selection rule: let t be the oracle's k-th largest key of a segment and
-A = {j : |key_j - t| <= RTOL * |t| + tau}, tau = ATOL_REL * max(key) (or
-LOGIT_ATOL_REL * max |key| for logit scores). The GPU keeps exactly as
-many entries as the oracle and the two sets agree outside A.
+A = {j : |key_j - t| <= RTOL * |t|}, the relative band alone. The GPU keeps
+exactly as many entries as the oracle and the two sets agree outside A.
+Guard: |t| > 100 * tau (tau as above, LOGIT_ATOL_REL * max |key| for
+logits), so the absolute floor of the score rule is at most 1 % of the
+band at the selection boundary and never decides which side of it an
+entry falls on; a segment that fails the guard fails the check.
 """
 from __future__ import annotations
 
@@ -54,14 +56,17 @@ def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, what: str = "scores"):
     return float((err / np.maximum(np.abs(ref), 1e-30)).max())
 
 
-def _band(key: np.ndarray, k: int, logit: bool = False):
-    """Oracle's k-th key t and the tolerance band around it (a boolean mask)."""
+def _band(key: np.ndarray, k: int, logit: bool = False, what: str = ""):
+    """Oracle's k-th key t and the relative tolerance band around it (a
+    boolean mask). Asserts the guard |t| > 100 * tau."""
     if k == 0 or k == key.size:
         return None, np.zeros(key.shape, bool)
     order = np.lexsort((np.arange(key.size), -key))
     t = key[order[k - 1]]
     tau = LOGIT_ATOL_REL * np.abs(key).max() if logit else ATOL_REL * key.max()
-    return t, np.abs(key - t) <= RTOL * abs(t) + tau
+    assert abs(t) > 100 * tau, (f"{what}: k-th key {t!r} is within 100x the absolute score floor "
+                                f"{tau!r}; the selection band would depend on it")
+    return t, np.abs(key - t) <= RTOL * abs(t)
 
 
 def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, what: str = "logit scores"):
@@ -80,7 +85,7 @@ def assert_topk_within_band(gpu_pick, ref_key: np.ndarray, k: int, what: str, lo
     assert gpu_pick.size == k, f"{what}: kept {gpu_pick.size}, expected {k}"
     assert np.unique(gpu_pick).size == k, f"{what}: duplicate indices"
     ref_pick = oracle.topk_indices(ref_key, k)
-    t, band = _band(ref_key, k, logit)
+    t, band = _band(ref_key, k, logit, what)
     g = np.zeros(ref_key.size, bool)
     g[gpu_pick] = True
     r = np.zeros(ref_key.size, bool)

@@ -438,6 +438,58 @@ def check_value_weight(o):
     np.testing.assert_allclose(o.value_weight(v, w3, G), exp, rtol=1e-12)
 
 
+def check_value_weight_group_sum(o):
+    g = load_golden("value_weight_group_example.txt")
+    w_o = np.array([g["w_o.row0"], g["w_o.row1"]])
+    v = np.array([[g["v.pos0"], g["v.pos1"]]])
+    np.testing.assert_allclose(o.value_weight(v, w_o, 2)[0], g["mean_of_norms"], rtol=1e-15)
+    np.testing.assert_allclose(o.value_weight_group_sum(v, w_o, 2)[0], g["norm_of_sum"], rtol=1e-15)
+    rng = np.random.default_rng(28)
+    # brute force with explicit loops: the slices summed inside the |.|
+    H, G, d, n, D = 2, 3, 3, 5, 4
+    v = rng.standard_normal((H, n, d))
+    w_o = rng.standard_normal((D, H * G * d))
+    ref = np.zeros((H, n))
+    for h in range(H):
+        for j in range(n):
+            tot = 0.0
+            for c in range(D):
+                s = 0.0
+                for gg in range(G):
+                    for e in range(d):
+                        s += w_o[c, (h * G + gg) * d + e] * v[h, j, e]
+                tot += abs(s)
+            ref[h, j] = tot
+    np.testing.assert_allclose(o.value_weight_group_sum(v, w_o, G), ref, rtol=1e-12)
+    pos = np.array([3, 1])
+    np.testing.assert_allclose(o.value_weight_group_sum(v, w_o, G, pos), ref[:, pos], rtol=1e-12)
+    # one query head per KV head: both group modes are the same norm
+    w1 = rng.standard_normal((D, H * d))
+    np.testing.assert_allclose(o.value_weight_group_sum(v, w1, 1), o.value_weight(v, w1, 1),
+                               rtol=1e-12)
+    # triangle inequality: || sum_g W_g v ||_1 <= sum_g || W_g v ||_1 = G * mode 0,
+    # with equality when every slice of the group is the same
+    assert (o.value_weight_group_sum(v, w_o, G) <= G * o.value_weight(v, w_o, G) + 1e-12).all()
+    same = np.concatenate([np.tile(w1[:, h * d:(h + 1) * d], (1, G)) for h in range(H)], axis=1)
+    np.testing.assert_allclose(o.value_weight_group_sum(v, same, G),
+                               G * o.value_weight(v, same, G), rtol=1e-12)
+    # scaled identity slices a_g [I; 0] -> |sum_g a_g| * ||v||_1 (0 when they cancel)
+    H, G, d, n = 2, 3, 4, 6
+    D = 2 * d
+    v = rng.standard_normal((H, n, d))
+    a = np.array([[1.5, -0.5, 2.0], [1.0, -1.0, 0.0]])
+    w_o = np.zeros((D, H * G * d))
+    for h in range(H):
+        for gg in range(G):
+            w_o[:d, (h * G + gg) * d:(h * G + gg + 1) * d] = a[h, gg] * np.eye(d)
+    exp = np.abs(a.sum(axis=1))[:, None] * np.abs(v).sum(axis=2)
+    np.testing.assert_allclose(o.value_weight_group_sum(v, w_o, G), exp, rtol=1e-12, atol=1e-15)
+    # homogeneity
+    w_o = rng.standard_normal((D, H * G * d))
+    np.testing.assert_allclose(o.value_weight_group_sum(-3.0 * v, w_o, G),
+                               3.0 * o.value_weight_group_sum(v, w_o, G), rtol=1e-12)
+
+
 # ----------------------------------------------------------- selection ----
 
 def _assert_topk_property(key, picked, k):
@@ -467,6 +519,74 @@ def check_select_examples(o):
                                     eps=g[name + ".eps"][0])
         np.testing.assert_array_equal(idx[0], g[name + ".kept"], err_msg=name)
         np.testing.assert_array_equal(st[0], g[name + ".stage"], err_msg=name)
+
+
+def check_select_examples_f32(o):
+    """The float32 two-stage key, worked by hand (select_examples.txt): the
+    rounding of mul, add, mul decides a pick that float64 makes the other
+    way, with eps and score_norm both non-trivial."""
+    g = load_golden("select_examples.txt")
+    for name in ("f32_tie", "f32_even", "f32_fma"):
+        args = (np.array([g[name + ".pooled"]]), int(g[name + ".budget"][0]),
+                int(g[name + ".W"][0]), int(g[name + ".n"][0]))
+        kw = dict(weight=np.array([g[name + ".weight"]]), alpha=g[name + ".alpha"][0],
+                  score_norm=g[name + ".score_norm"][0], eps=g[name + ".eps"][0])
+        idx, _, st = o.select_layer(*args, dtype=np.float32, **kw)
+        np.testing.assert_array_equal(idx[0], g[name + ".kept"], err_msg=name)
+        np.testing.assert_array_equal(st[0], g[name + ".stage"], err_msg=name)
+        idx64, _, _ = o.select_layer(*args, dtype=np.float64, **kw)
+        np.testing.assert_array_equal(idx64[0], g[name + ".kept64"], err_msg=name + " (float64)")
+
+
+def _f32_key_by_hand(s, w, norm, eps):
+    """(s*norm + eps)*w with each operation rounded to float32: the exact
+    result of every product and sum is formed as a Fraction and rounded to
+    the nearest float32, ties to even."""
+    def rnd(x: Fraction) -> Fraction:
+        if x == 0:
+            return Fraction(0)
+        sign = -1 if x < 0 else 1
+        a = abs(x)
+        e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+        while Fraction(2) ** e > a:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= a:
+            e += 1
+        e = max(e, -126)                     # subnormal spacing below 2^-126
+        ulp = Fraction(2) ** (e - 23)
+        q, r = divmod(a, ulp)
+        if r * 2 > ulp or (r * 2 == ulp and q % 2 == 1):
+            q += 1
+        return sign * q * ulp
+    f = lambda v: Fraction(float(np.float32(v)))
+    return float(rnd(rnd(rnd(f(s) * f(norm)) + f(eps)) * f(w)))
+
+
+def check_select_two_stage_f32_bruteforce(o):
+    """Two-stage selection in float32 on random tied inputs: stage 1 is a
+    top-k1 by score, stage 2 a top-(k-k1) of the rest by the key rounded as
+    mul, add, mul to float32 (computed here with exact rationals and
+    explicit round-to-nearest-even, not with float32 arithmetic)."""
+    rng = np.random.default_rng(23)
+    for trial in range(6):
+        H, n, W = 2, 24, 3
+        n_cand = n - W
+        scores = rng.integers(0, 5, size=(H, n_cand)).astype(np.float64) * 0.37
+        w = rng.integers(1, 4, size=(H, n_cand)).astype(np.float64) * 1.3
+        budget = int(rng.integers(W, n + 1))
+        alpha = float(rng.choice([0.0, 0.5, 1.0]))
+        norm, eps = 1.0 / 96, 1e-4
+        idx, _, st = o.select_layer(scores, budget, W, n, weight=w, alpha=alpha,
+                                    score_norm=norm, eps=eps, dtype=np.float32)
+        k = budget - W
+        k1 = int(math.floor(alpha * k))
+        for h in range(H):
+            s1 = [int(i) for i, s in zip(idx[h], st[h]) if s == 1]
+            s2 = [int(i) for i, s in zip(idx[h], st[h]) if s == 2]
+            _assert_topk_property(scores[h], s1, k1)
+            rest = [j for j in range(n_cand) if j not in set(s1)]
+            sub = np.array([_f32_key_by_hand(scores[h][j], w[h][j], norm, eps) for j in rest])
+            _assert_topk_property(sub, [rest.index(j) for j in s2], k - k1)
 
 
 def check_select_bruteforce(o):
@@ -748,4 +868,5 @@ ALL_CHECKS = [
     check_value_weight_l2, check_select_budgets_example, check_select_budgets_bruteforce,
     check_select_budgets_reductions, check_external_logit, check_head_scores_and_budgets,
     check_chunked, check_anchor_select, check_anchor_assign,
+    check_select_examples_f32, check_select_two_stage_f32_bruteforce, check_value_weight_group_sum,
 ]

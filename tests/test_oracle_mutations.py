@@ -33,6 +33,20 @@ MUTANTS = {
     "ties_to_higher_index": ("order = np.lexsort((np.arange(key.shape[0]), -key))", "order = np.lexsort((-np.arange(key.shape[0]), -key))"),
     "k1_ceil": ("k1 = int(np.floor(alpha * k))", "k1 = int(np.ceil(alpha * k))"),
     "no_eps_f64": ("(np.asarray(score, np.float64) * score_norm + eps)", "(np.asarray(score, np.float64) * score_norm)"),
+    "no_eps_f32": ("        t = t + np.float32(eps)\n", "        t = t + np.float32(0.0)\n"),
+    "no_norm_f32": ("        t = s * np.float32(score_norm)\n", "        t = s * np.float32(1.0)\n"),
+    "f32_reassociated": ("        t = t + np.float32(eps)\n        return t * np.asarray(weight, np.float32)",
+                         "        wf = np.asarray(weight, np.float32)\n        return t * wf + np.float32(eps) * wf"),
+    "f32_fused_add": ("        t = s * np.float32(score_norm)\n        t = t + np.float32(eps)\n",
+                      "        t = np.float32(np.asarray(score, np.float64) * np.float32(score_norm) + np.float64(np.float32(eps)))\n"),
+    "grpsum_mean_of_norms": ("        proj = v[h, positions] @ w_sum.T              # [m][D]\n        out[h] = np.abs(proj).sum(axis=1)",
+                             "        proj = v[h, positions] @ w_sum.T              # [m][D]\n        out[h] = np.abs(proj).sum(axis=1) / G"),
+    "grpsum_abs_inside": ("            w_sum += w_o[:, hq * d:(hq + 1) * d]      # [D][d]",
+                          "            w_sum += np.abs(w_o[:, hq * d:(hq + 1) * d])      # [D][d]"),
+    "grpsum_first_slice_only": ("            w_sum += w_o[:, hq * d:(hq + 1) * d]      # [D][d]",
+                                "            w_sum += w_o[:, h * G * d:(h * G + 1) * d]      # [D][d]"),
+    "grpsum_wrong_head": ("        proj = v[h, positions] @ w_sum.T              # [m][D]",
+                          "        proj = v[0, positions] @ w_sum.T              # [m][D]"),
     "stage2_from_all": ("cand = np.nonzero(rest)[0]", "cand = np.arange(score.shape[0])"),
     "adaptive_transposed": ("flat = scores.reshape(-1)", "flat = scores.T.reshape(-1)"),
     "window_not_counted": ("        k = budget - W\n        assert 0 <= k <= n_cand", "        k = max(budget - 2 * W, 0)\n        assert 0 <= k <= n_cand"),
