@@ -150,9 +150,15 @@ __device__ __forceinline__ uint64_t make_key(uint32_t bits, uint32_t f) {
 }
 
 // Integrated score of [CriticalKV] Algorithm 1 step 3 in fp32: mul, add,
-// mul, each rounded once (no contraction).
+// mul, each rounded once to nearest-even. HIP's __fmul_rn / __fadd_rn are
+// plain operators, which the compiler's default contraction would fuse
+// into one fma (a single rounding of s*norm + eps); the pragma keeps the
+// three operations separate.
 __device__ __forceinline__ uint32_t stage2_bits(float s, float w, float norm, float eps) {
-  return score_bits(__fmul_rn(__fadd_rn(__fmul_rn(s, norm), eps), w));
+#pragma clang fp contract(off)
+  const float t = s * norm;
+  const float u = t + eps;
+  return score_bits(u * w);
 }
 
 __device__ __forceinline__ int digit_width(int shift) {
