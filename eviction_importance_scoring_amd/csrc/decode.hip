@@ -32,31 +32,49 @@ constexpr int kDecMaxG = 8;
 constexpr int kDecMaxHeads = 1024;
 constexpr int kDecRec = kHeadDim + 2;   // partial of one query head: o[128], m, l
 
-// kept rows [start, start + len) of head h in layer l (clamped into the
-// layer, so no offsets can lead outside it)
+// kept rows [start, start + len) of head h in layer l, from the effective
+// offsets eo[0..H] that dec_prefix leaves in LDS
 struct DecHead {
   int start, len;
 };
 
-__device__ __forceinline__ DecHead dec_head(const int32_t* offs, int l, int H, int kept, int h) {
-  if (!offs) {
-    const int b = kept / H;
-    return DecHead{h * b, b};
-  }
-  const int32_t* o = offs + (size_t)l * (H + 1);
-  const int a = min(max(o[h], 0), kept), e = min(max(o[h + 1], 0), kept);
-  return DecHead{a, max(e - a, 0)};
+__device__ __forceinline__ DecHead dec_head(const int* eo, int h) {
+  return DecHead{eo[h], eo[h + 1] - eo[h]};
 }
 
-// pre[h] = work items of the layer's heads before h, pre[H] = all of them;
-// wave 0 writes them to LDS (visible after the caller's barrier)
-__device__ __forceinline__ void dec_prefix(const int32_t* offs, int l, int H, int kept, int* pre) {
-  if (threadIdx.x >= 64) return;
+// Called by every thread of the block; wave 0 does the work.
+// eo[h] (h <= H): the head offsets clamped into [0, kept] and raised to the
+// largest earlier one, so the heads are disjoint ranges inside the layer
+// whose lengths sum to at most kept (the grid and workspace are sized for
+// that; valid offsets are unchanged). Uniform layout: eo[h] = h * (kept/H).
+// pre[h] = work items of the layer's heads before h, pre[H] = all of them.
+// Both are visible after the caller's barrier.
+__device__ __forceinline__ void dec_prefix(const int32_t* offs, int l, int H, int kept, int* eo,
+                                           int* pre) {
   const int lane = threadIdx.x;
+  if (threadIdx.x < 64) {
+    const int32_t* o = offs ? offs + (size_t)l * (H + 1) : nullptr;
+    int run = 0;
+    for (int base = 0; base <= H; base += 64) {
+      const int h = base + lane;
+      int x = 0;
+      if (h <= H) x = o ? min(max(o[h], 0), kept) : h * (kept / H);
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) {
+        const int y = __shfl_up(x, s);
+        if (lane >= s) x = max(x, y);
+      }
+      x = max(x, run);
+      if (h <= H) eo[h] = x;
+      run = __shfl(x, 63);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
   int carry = 0;
   for (int base = 0; base < H; base += 64) {
     const int h = base + lane;
-    const int cnt = h < H ? (dec_head(offs, l, H, kept, h).len + kDecChunk - 1) / kDecChunk : 0;
+    const int cnt = h < H ? (dec_head(eo, h).len + kDecChunk - 1) / kDecChunk : 0;
     int x = cnt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -127,6 +145,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const __bf16* __restrict
                                                         float alpha, int items,
                                                         float* __restrict__ part) {
   __shared__ int pre[kDecMaxHeads + 1];
+  __shared__ int eo[kDecMaxHeads + 1];
   __shared__ __align__(16) float pr[kDecChunk][kDecMaxG];   // logits, then exponentials
   __shared__ float red[2][4][kDecMaxG];
   __shared__ float osum[4][G][kHeadDim];
@@ -135,11 +154,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const __bf16* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot = lane >> 4, piece = lane & 15;
 
-  dec_prefix(offs, l, H, kept, pre);
+  dec_prefix(offs, l, H, kept, eo, pre);
   __syncthreads();
   if (it >= pre[H]) return;   // uniform: past the layer's items
   const int h = dec_find(pre, H, it);
-  const DecHead hd = dec_head(offs, l, H, kept, h);
+  const DecHead hd = dec_head(eo, h);
   const int r0 = hd.start + (it - pre[h]) * kDecChunk;
   const int r1 = min(hd.start + hd.len, r0 + kDecChunk);   // r0 < r1
 
@@ -258,10 +277,11 @@ __global__ __launch_bounds__(kHeadDim) void k_decode_merge(int H, int G, int kep
                                                            int items, const float* __restrict__ part,
                                                            float* __restrict__ out) {
   __shared__ int pre[kDecMaxHeads + 1];
+  __shared__ int eo[kDecMaxHeads + 1];
   __shared__ float wmax[kHeadDim / 64];
   const int g = blockIdx.x % G, lh = blockIdx.x / G;
   const int h = lh % H, l = lh / H;
-  dec_prefix(offs, l, H, kept, pre);
+  dec_prefix(offs, l, H, kept, eo, pre);
   __syncthreads();
   const int d = threadIdx.x;
   const int i0 = pre[h], i1 = pre[h + 1];
