@@ -2,8 +2,9 @@
 selection and compaction on MI355X (gfx950).
 
 Thin ctypes marshalling over the C ABI declared in include/kvsel.h: each
-function below checks tensor dtypes / shapes / devices, allocates outputs
-and the workspace with torch on the inputs' device, and calls the C entry
+function below checks tensor dtypes / shapes / devices (caller-supplied
+outputs included), allocates missing outputs and the workspace with torch
+on the inputs' device, and calls the C entry
 point of the same name on the current torch stream. Every step of the
 computation runs in the HIP kernels of libkvsel.so. There is no fallback:
 if the library is missing, every call raises.
@@ -23,10 +24,12 @@ __all__ = [
     "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
     "Q_WINDOW", "Q_EXTERNAL", "AGG_SUM", "AGG_MAX", "AGG_LOGIT_MAX",
+    "GROUP_MEAN_OF_NORMS", "GROUP_NORM_OF_SUM",
 ]
 
 Q_WINDOW, Q_EXTERNAL = 0, 1
 AGG_SUM, AGG_MAX, AGG_LOGIT_MAX = 0, 1, 2
+GROUP_MEAN_OF_NORMS, GROUP_NORM_OF_SUM = 0, 1
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libkvsel.so")
@@ -45,7 +48,7 @@ _SIGNATURES = {
                             _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_void_p, _c_void_p,
                             _c_void_p, _c_size_p, _c_void_p],
     "kvsel_value_weight": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                           _c_i32, _c_i32, _c_void_p, _c_void_p],
+                           _c_i32, _c_i32, _c_i32, _c_void_p, _c_void_p, _c_size_p, _c_void_p],
     "kvsel_value_l2_factor": [_c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                               _c_void_p],
     "kvsel_value_weight_l2": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -116,25 +119,49 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, dtype, name, dims=None):
+def _need(t, dtype, name, dims=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
 
 
+def _out(t, dtype, name, shape, device):
+    """A caller-supplied output is checked (dtype, device, contiguity and the
+    exact shape the kernels write); None allocates one."""
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, dtype, name, len(shape), device)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
+    return t
+
+
 def _workspace(nbytes: int, device, workspace=None):
+    """A caller-supplied workspace (any dtype, contiguous, on the device) or a
+    new one. Returns (tensor, size in bytes)."""
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError("workspace too small")
-        return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+            raise ValueError("workspace must be a GPU tensor")
+        if workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, expected {device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        size = workspace.numel() * workspace.element_size()
+        if size < nbytes:
+            raise ValueError(f"workspace too small: {size} < {nbytes} bytes")
+        return workspace, size
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel()
 
 
 def kvsel_score(q, k, *, G: int, q_mode: int = Q_WINDOW, agg: int = AGG_SUM,
@@ -153,16 +180,16 @@ def kvsel_score(q, k, *, G: int, q_mode: int = Q_WINDOW, agg: int = AGG_SUM,
         scale = 1.0 / d ** 0.5
     n_cand = n - W if q_mode == Q_WINDOW else n
     dev = q.device
-    if scores is None:
-        scores = torch.empty((L, H, max(n_cand, 0)), dtype=torch.float32, device=dev)
-    if return_raw and raw is None:
-        raw = torch.empty((L, H, n), dtype=torch.float32, device=dev)
+    _need(k, torch.bfloat16, "k", 4, dev)
+    scores = _out(scores, torch.float32, "scores", (L, H, max(n_cand, 0)), dev)
+    if return_raw or raw is not None:
+        raw = _out(raw, torch.float32, "raw", (L, H, n), dev)
     nbytes = ctypes.c_size_t(0)
     f = lib().kvsel_score
     args = (L, H, G, d, n, W, q_mode, agg, float(scale), pool)
     _check(f(None, None, *args, None, _ptr(raw), None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(q), _ptr(k), *args, _ptr(scores), _ptr(raw), _ptr(ws), ctypes.byref(nbytes),
              _stream(dev)))
     return scores, raw
@@ -185,35 +212,45 @@ def kvsel_score_chunked(q, k, k_self, *, G: int, m: int, n_prompt: int,
     if scale is None:
         scale = 1.0 / d ** 0.5
     dev = k.device
-    if scores is None:
-        scores = torch.empty((L, H, n), dtype=torch.float32, device=dev)
-    if return_raw and raw is None:
-        raw = torch.empty((L, H, n), dtype=torch.float32, device=dev)
+    _need(q, torch.bfloat16, "q", 5, dev)
+    _need(k_self, torch.bfloat16, "k_self", 5, dev)
+    scores = _out(scores, torch.float32, "scores", (L, H, n), dev)
+    if return_raw or raw is not None:
+        raw = _out(raw, torch.float32, "raw", (L, H, n), dev)
     nbytes = ctypes.c_size_t(0)
     f = lib().kvsel_score_chunked
     args = (L, H, G, d, n, m, n_prompt, float(scale), pool)
     _check(f(None, None, None, *args, None, _ptr(raw), None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(q), _ptr(k), _ptr(k_self), *args, _ptr(scores), _ptr(raw), _ptr(ws),
              ctypes.byref(nbytes), _stream(dev)))
     return scores, raw
 
 
-def kvsel_value_weight(v, w_o, *, G: int, n_cand: int | None = None, weight=None):
+def kvsel_value_weight(v, w_o, *, G: int, n_cand: int | None = None,
+                       group_mode: int = GROUP_MEAN_OF_NORMS, weight=None, workspace=None):
     """CriticalKV value weight [L][H_kv][n_cand]. v bf16 [L][H_kv][n][d],
-    w_o bf16 [L][D][H_kv*G*d]."""
+    w_o bf16 [L][D][H_kv*G*d]. group_mode: GROUP_MEAN_OF_NORMS (mean over
+    the group of each query head's L1 norm) or GROUP_NORM_OF_SUM (L1 norm of
+    the group-summed projection)."""
     _need(v, torch.bfloat16, "v", 4)
-    _need(w_o, torch.bfloat16, "w_o", 3)
+    dev = v.device
+    _need(w_o, torch.bfloat16, "w_o", 3, dev)
     L, H, n, d = v.shape
     if w_o.shape[0] != L or w_o.shape[2] != H * G * d:
         raise ValueError(f"shape mismatch: v {tuple(v.shape)}, w_o {tuple(w_o.shape)}, G={G}")
     D = w_o.shape[1]
     n_cand = n if n_cand is None else n_cand
-    if weight is None:
-        weight = torch.empty((L, H, n_cand), dtype=torch.float32, device=v.device)
-    _check(lib().kvsel_value_weight(_ptr(v), _ptr(w_o), L, H, G, d, n, D, n_cand,
-                                    _ptr(weight), _stream(v.device)))
+    weight = _out(weight, torch.float32, "weight", (L, H, n_cand), dev)
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_value_weight
+    args = (L, H, G, d, n, D, n_cand, int(group_mode))
+    _check(f(None, None, *args, None, None, ctypes.byref(nbytes), None))
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
+    _check(f(_ptr(v), _ptr(w_o), *args, _ptr(weight), _ptr(ws), ctypes.byref(nbytes),
+             _stream(dev)))
     return weight
 
 
@@ -226,12 +263,7 @@ def kvsel_value_l2_factor(w_o, *, G: int, H_kv: int, factor=None):
     if cols % Hq:
         raise ValueError(f"w_o has {cols} input columns, not a multiple of H_kv*G={Hq}")
     d = cols // Hq
-    if factor is None:
-        factor = torch.empty((L, Hq, 2, d, d), dtype=torch.bfloat16, device=w_o.device)
-    else:
-        _need(factor, torch.bfloat16, "factor", 5)
-        if tuple(factor.shape) != (L, Hq, 2, d, d):
-            raise ValueError(f"factor must be {(L, Hq, 2, d, d)}, got {tuple(factor.shape)}")
+    factor = _out(factor, torch.bfloat16, "factor", (L, Hq, 2, d, d), w_o.device)
     _check(lib().kvsel_value_l2_factor(_ptr(w_o), L, H_kv, G, d, D, _ptr(factor),
                                        _stream(w_o.device)))
     return factor
@@ -241,13 +273,12 @@ def kvsel_value_weight_l2(v, factor, *, G: int, n_cand: int | None = None, weigh
     """L2 form of the CriticalKV value weight [L][H_kv][n_cand]. v bf16
     [L][H_kv][n][d], factor from kvsel_value_l2_factor."""
     _need(v, torch.bfloat16, "v", 4)
-    _need(factor, torch.bfloat16, "factor", 5)
+    _need(factor, torch.bfloat16, "factor", 5, v.device)
     L, H, n, d = v.shape
     if tuple(factor.shape) != (L, H * G, 2, d, d):
         raise ValueError(f"shape mismatch: v {tuple(v.shape)}, factor {tuple(factor.shape)}, G={G}")
     n_cand = n if n_cand is None else n_cand
-    if weight is None:
-        weight = torch.empty((L, H, n_cand), dtype=torch.float32, device=v.device)
+    weight = _out(weight, torch.float32, "weight", (L, H, n_cand), v.device)
     _check(lib().kvsel_value_weight_l2(_ptr(v), _ptr(factor), L, H, G, d, n, n_cand,
                                        _ptr(weight), _stream(v.device)))
     return weight
@@ -260,14 +291,14 @@ def kvsel_select(scores, *, n: int, W: int, budget: int, adaptive: bool = False,
     stage): idx [L][H_kv][budget] (uniform) or [L][budget] with
     head_offsets [L][H_kv+1] (adaptive)."""
     _need(scores, torch.float32, "scores", 3)
+    dev = scores.device
     if weight is not None:
-        _need(weight, torch.float32, "weight", 3)
+        _need(weight, torch.float32, "weight", 3, dev)
         if weight.shape != scores.shape:
             raise ValueError("weight must match scores")
     L, H, n_cand = scores.shape
     if n_cand != n - W:
         raise ValueError(f"scores has {n_cand} candidates, expected n-W={n - W}")
-    dev = scores.device
     shape = (L, budget) if adaptive else (L, H, budget)
     idx = torch.empty(shape, dtype=torch.int32, device=dev)
     offs = torch.empty((L, H + 1), dtype=torch.int32, device=dev) if adaptive else None
@@ -276,8 +307,8 @@ def kvsel_select(scores, *, n: int, W: int, budget: int, adaptive: bool = False,
     f = lib().kvsel_select
     args = (L, H, n, W, int(budget), int(adaptive), float(score_norm), float(eps), float(alpha))
     _check(f(None, _ptr(weight), *args, None, None, None, None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(scores), _ptr(weight), *args, _ptr(idx), _ptr(offs), _ptr(stage), _ptr(ws),
              ctypes.byref(nbytes), _stream(dev)))
     return idx, offs, stage
@@ -292,9 +323,9 @@ def kvsel_select_budgets(scores, budgets, *, n: int, W: int, layer_stride: int |
     per-layer sum of the budgets clamped into [W, n] (read back from the
     device: a synchronising copy; pass it to avoid that)."""
     _need(scores, torch.float32, "scores", 3)
-    _need(budgets, torch.int32, "budgets", 2)
+    _need(budgets, torch.int32, "budgets", 2, scores.device)
     if weight is not None:
-        _need(weight, torch.float32, "weight", 3)
+        _need(weight, torch.float32, "weight", 3, scores.device)
         if weight.shape != scores.shape:
             raise ValueError("weight must match scores")
     L, H, n_cand = scores.shape
@@ -314,8 +345,8 @@ def kvsel_select_budgets(scores, budgets, *, n: int, W: int, layer_stride: int |
     tail = (float(score_norm), float(eps), float(alpha))
     _check(f(None, _ptr(weight), *args, None, int(layer_stride), *tail, None, None, None, None,
              ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(scores), _ptr(weight), *args, _ptr(budgets), int(layer_stride), *tail, _ptr(idx),
              _ptr(offs), _ptr(stage), _ptr(ws), ctypes.byref(nbytes), _stream(dev)))
     return idx, offs, stage
@@ -325,8 +356,7 @@ def kvsel_head_score(scores, *, out=None):
     """Head scores [L][H_kv]: max over positions of scores f32 [L][H_kv][n_pos]."""
     _need(scores, torch.float32, "scores", 3)
     L, H, n_pos = scores.shape
-    if out is None:
-        out = torch.empty((L, H), dtype=torch.float32, device=scores.device)
+    out = _out(out, torch.float32, "out", (L, H), scores.device)
     _check(lib().kvsel_head_score(_ptr(scores), L, H, n_pos, _ptr(out), _stream(scores.device)))
     return out
 
@@ -337,13 +367,12 @@ def kvsel_head_budgets(head_score, *, keep: int, n: int, W: int, out=None, works
     _need(head_score, torch.float32, "head_score", 2)
     L, H = head_score.shape
     dev = head_score.device
-    if out is None:
-        out = torch.empty((L, H), dtype=torch.int32, device=dev)
+    out = _out(out, torch.int32, "out", (L, H), dev)
     nbytes = ctypes.c_size_t(0)
     f = lib().kvsel_head_budgets
     _check(f(None, L, H, int(keep), n, W, None, None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(head_score), L, H, int(keep), n, W, _ptr(out), _ptr(ws), ctypes.byref(nbytes),
              _stream(dev)))
     return out
@@ -354,21 +383,20 @@ def kvsel_anchor_select(scores, rand, *, n: int, W: int, k: int, rho: float = 0.
     """AnchorKV anchor positions i32 [L][H_kv][k] (ascending). scores, rand
     f32 [L][H_kv][n-W]."""
     _need(scores, torch.float32, "scores", 3)
-    _need(rand, torch.float32, "rand", 3)
+    dev = scores.device
+    _need(rand, torch.float32, "rand", 3, dev)
     if rand.shape != scores.shape:
         raise ValueError("rand must match scores")
     L, H, n_cand = scores.shape
     if n_cand != n - W:
         raise ValueError(f"scores has {n_cand} candidates, expected n-W={n - W}")
-    dev = scores.device
-    if out is None:
-        out = torch.empty((L, H, k), dtype=torch.int32, device=dev)
+    out = _out(out, torch.int32, "out", (L, H, k), dev)
     nbytes = ctypes.c_size_t(0)
     f = lib().kvsel_anchor_select
     args = (L, H, n, W, int(k), float(rho))
     _check(f(None, None, *args, None, None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(scores), _ptr(rand), *args, _ptr(out), _ptr(ws), ctypes.byref(nbytes),
              _stream(dev)))
     return out
@@ -378,21 +406,19 @@ def kvsel_anchor_assign(x, anchors, *, slot=None, gamma=None, workspace=None):
     """Nearest-anchor slot i32 and gamma f32 [L][H_kv][n] of x bf16
     [L][H_kv][n][d] for anchors i32 [L][H_kv][k]."""
     _need(x, torch.bfloat16, "x", 4)
-    _need(anchors, torch.int32, "anchors", 3)
+    dev = x.device
+    _need(anchors, torch.int32, "anchors", 3, dev)
     L, H, n, d = x.shape
     if anchors.shape[:2] != (L, H):
         raise ValueError(f"anchors must be [L][H_kv][k], got {tuple(anchors.shape)}")
     k = anchors.shape[2]
-    dev = x.device
-    if slot is None:
-        slot = torch.empty((L, H, n), dtype=torch.int32, device=dev)
-    if gamma is None:
-        gamma = torch.empty((L, H, n), dtype=torch.float32, device=dev)
+    slot = _out(slot, torch.int32, "slot", (L, H, n), dev)
+    gamma = _out(gamma, torch.float32, "gamma", (L, H, n), dev)
     nbytes = ctypes.c_size_t(0)
     f = lib().kvsel_anchor_assign
     _check(f(None, None, L, H, d, n, k, None, None, None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(x), _ptr(anchors), L, H, d, n, k, _ptr(slot), _ptr(gamma), _ptr(ws),
              ctypes.byref(nbytes), _stream(dev)))
     return slot, gamma
@@ -402,25 +428,23 @@ def kvsel_compact(k, v, idx, head_offsets=None, k_out=None, v_out=None):
     """Gather kept rows: returns (k_out, v_out) bf16 [L][kept_per_layer][d]
     (allocated unless given)."""
     _need(k, torch.bfloat16, "k", 4)
-    _need(v, torch.bfloat16, "v", 4)
-    _need(idx, torch.int32, "idx")
+    dev = k.device
+    _need(v, torch.bfloat16, "v", 4, dev)
+    _need(idx, torch.int32, "idx", None, dev)
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
     L, H, n, d = k.shape
-    kept = idx[0].numel()
-    if idx.shape[0] != L:
+    if idx.dim() < 2 or idx.shape[0] != L:
         raise ValueError("idx must have a leading L axis")
+    kept = idx[0].numel()
     if head_offsets is not None:
-        _need(head_offsets, torch.int32, "head_offsets", 2)
-    for name, t in (("k_out", k_out), ("v_out", v_out)):
-        if t is not None:
-            _need(t, torch.bfloat16, name, 3)
-            if tuple(t.shape) != (L, kept, d):
-                raise ValueError(f"{name} must be {(L, kept, d)}, got {tuple(t.shape)}")
-    if k_out is None:
-        k_out = torch.empty((L, kept, d), dtype=k.dtype, device=k.device)
-    if v_out is None:
-        v_out = torch.empty((L, kept, d), dtype=v.dtype, device=v.device)
+        _need(head_offsets, torch.int32, "head_offsets", 2, dev)
+        if tuple(head_offsets.shape) != (L, H + 1):
+            raise ValueError(f"head_offsets must be {(L, H + 1)}, got {tuple(head_offsets.shape)}")
+    elif idx.dim() != 3 or idx.shape[1] != H:
+        raise ValueError(f"without head_offsets idx must be [L][H_kv][B], got {tuple(idx.shape)}")
+    k_out = _out(k_out, torch.bfloat16, "k_out", (L, kept, d), dev)
+    v_out = _out(v_out, torch.bfloat16, "v_out", (L, kept, d), dev)
     _check(lib().kvsel_compact(_ptr(k), _ptr(v), L, H, d, n, _ptr(idx), _ptr(head_offsets),
                                kept, _ptr(k_out), _ptr(v_out), _stream(k.device)))
     return k_out, v_out
@@ -433,8 +457,8 @@ def kvsel_decode_attention(q, k_kept, v_kept, *, G: int, scale: float | None = N
     head_offsets i32 [L][H_kv+1] or None (uniform heads). Returns out f32
     [L][H_kv*G][d]."""
     _need(q, torch.bfloat16, "q", 3)
-    _need(k_kept, torch.bfloat16, "k_kept", 3)
-    _need(v_kept, torch.bfloat16, "v_kept", 3)
+    _need(k_kept, torch.bfloat16, "k_kept", 3, q.device)
+    _need(v_kept, torch.bfloat16, "v_kept", 3, q.device)
     if k_kept.shape != v_kept.shape:
         raise ValueError("k_kept and v_kept must have the same shape")
     L, Hq, d = q.shape
@@ -445,24 +469,19 @@ def kvsel_decode_attention(q, k_kept, v_kept, *, G: int, scale: float | None = N
         raise ValueError("k_kept must be [L][kept][d]")
     kept = k_kept.shape[1]
     if head_offsets is not None:
-        _need(head_offsets, torch.int32, "head_offsets", 2)
+        _need(head_offsets, torch.int32, "head_offsets", 2, q.device)
         if tuple(head_offsets.shape) != (L, H + 1):
             raise ValueError("head_offsets must be [L][H_kv+1]")
     if scale is None:
         scale = 1.0 / d ** 0.5
     dev = q.device
-    if out is None:
-        out = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
-    else:
-        _need(out, torch.float32, "out", 3)
-        if tuple(out.shape) != (L, Hq, d):
-            raise ValueError("out must be [L][H_kv*G][d]")
+    out = _out(out, torch.float32, "out", (L, Hq, d), dev)
     nbytes = ctypes.c_size_t(0)
     f = lib().kvsel_decode_attention
     args = (L, H, G, d, int(kept), _ptr(head_offsets), float(scale))
     _check(f(None, None, None, *args, None, None, ctypes.byref(nbytes), None))
-    ws = _workspace(nbytes.value, dev, workspace)
-    nbytes = ctypes.c_size_t(ws.numel())
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
     _check(f(_ptr(q), _ptr(k_kept), _ptr(v_kept), *args, _ptr(out), _ptr(ws), ctypes.byref(nbytes),
              _stream(dev)))
     return out

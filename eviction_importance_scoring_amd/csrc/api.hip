@@ -29,7 +29,7 @@ constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 extern "C" {
 
-int32_t kvsel_abi_version(void) { return 1; }
+int32_t kvsel_abi_version(void) { return 2; }
 
 const char* kvsel_status_str(int32_t status) {
   switch (status) {
@@ -132,18 +132,28 @@ int32_t kvsel_score_chunked(const void* q, const void* k, const void* k_self, in
 }
 
 int32_t kvsel_value_weight(const void* v, const void* w_o, int32_t L, int32_t H_kv, int32_t G,
-                           int32_t d, int32_t n, int32_t D, int32_t n_cand, float* weight,
-                           void* stream) {
-  if (!v || !w_o || !weight) return KVSEL_ERR_ARG;
+                           int32_t d, int32_t n, int32_t D, int32_t n_cand, int32_t group_mode,
+                           float* weight, void* ws, size_t* ws_bytes, void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
   if (L < 1 || H_kv < 1 || G < 1 || d < 1 || n < 1 || D < 1) return KVSEL_ERR_ARG;
   if (n_cand < 1 || n_cand > n) return KVSEL_ERR_ARG;
-  if (!aligned16(v) || !aligned16(w_o) || !aligned16(weight)) return KVSEL_ERR_ARG;
+  if (group_mode != KVSEL_GROUP_MEAN_OF_NORMS && group_mode != KVSEL_GROUP_NORM_OF_SUM)
+    return KVSEL_ERR_ARG;
   if (d != kHeadDimPublic || D % 32 != 0) return KVSEL_ERR_UNSUPPORTED;
   if ((int64_t)H_kv * G * d > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
   // w_o is read through buffer resources with 31-bit byte offsets
   if ((int64_t)D * H_kv * G * d * 2 > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
-  const hipError_t e = value_weight_launch(v, w_o, L, H_kv, G, n, D, n_cand, weight,
-                                           static_cast<hipStream_t>(stream));
+  const size_t need = value_weight_ws_bytes(L, H_kv, D, group_mode);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  if (!v || !w_o || !weight) return KVSEL_ERR_ARG;
+  if (!aligned16(v) || !aligned16(w_o) || !aligned16(weight) || !aligned16(ws))
+    return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  const hipError_t e = value_weight_launch(v, w_o, L, H_kv, G, n, D, n_cand, group_mode, weight,
+                                           ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 

@@ -73,8 +73,10 @@ hipError_t compact_launch(const void* k, const void* v, int L, int H, int d, int
                           int64_t kept, void* k_out, void* v_out, hipStream_t st);
 
 // --------------------------------------------------------- value weight ----
+size_t value_weight_ws_bytes(int L, int H, int D, int group_mode);
 hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int G, int n,
-                               int D, int n_cand, float* weight, hipStream_t st);
+                               int D, int n_cand, int group_mode, float* weight, void* ws,
+                               hipStream_t st);
 hipError_t value_l2_factor_launch(const void* w_o, int L, int H, int G, int D, void* factor,
                                   hipStream_t st);
 hipError_t value_weight_l2_launch(const void* v, const void* factor, int L, int H, int G, int n,

@@ -1,10 +1,12 @@
 // CriticalKV's projected-value norm ([CriticalKV] §3.3 Algorithm 1 steps
 // 2-3; Theorem 3.3): weight[l][h][j] = (1/G) sum_g || W_O^(h,g) v_j ||_1
 // where W_O^(h,g) is the D x d column slice of the output projection that
-// query head h*G+g uses. The projection V_proj = V W^O is a bf16 MFMA
-// product accumulated in fp32; each output tile is folded into per-key |.|
-// sums in registers and never written ([CriticalKV] §D.4 notes the full
-// V_proj would be ~7.8 GB per layer at 7B / 128K).
+// query head h*G+g uses (group mode 0), or || (sum_g W_O^(h,g)) v_j ||_1
+// (group mode 1: the slices are summed into a bf16 copy first, then the
+// same kernel runs with one slice per KV head). The projection V W^O is a
+// bf16 MFMA product accumulated in fp32; each output tile is folded into
+// per-key |.| sums in registers and never written ([CriticalKV] §D.4 notes
+// the full V W^O would be ~7.8 GB per layer at 7B / 128K).
 //
 // Tiling (the 8-wave LDS ring of kvsel_ring.h): a workgroup owns 512 keys of
 // one (layer, KV head); each wave holds the values of 64 keys (two MFMA
@@ -161,14 +163,70 @@ __global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__
   }
 }
 
+// Group-summed projection (group mode 1): wsum[l][c][h*d + e] =
+// bf16(sum_g w_o[l][c][(h*G + g)*d + e]), the G column slices of KV head
+// h added in fp32 in order g = 0..G-1 and rounded once to nearest-even.
+// 1-D grid over the L*D*H*d/8 16-byte pieces of wsum, block 256.
+__global__ __launch_bounds__(256) void k_wo_group_sum(const __bf16* __restrict__ w_o, int H,
+                                                       int G, long long pieces,
+                                                       __bf16* __restrict__ wsum) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  constexpr int kPer = kHeadDim / 8;                  // pieces per head row slice
+  const long long row = i / ((long long)H * kPer);    // (l, c)
+  const int rem = (int)(i - row * H * kPer);
+  const int h = rem / kPer, p = rem - h * kPer;
+  const u32x4* src = reinterpret_cast<const u32x4*>(w_o + row * (long long)H * G * kHeadDim +
+                                                     (long long)h * G * kHeadDim + p * 8);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int g = 0; g < G; ++g) {
+    const u32x4 x = src[g * kPer];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += __uint_as_float(x[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(x[e] & 0xFFFF0000u);
+    }
+  }
+  u32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t lo = __float_as_uint(acc[2 * e]), hi = __float_as_uint(acc[2 * e + 1]);
+    lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;    // round to nearest-even (finite)
+    hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+    out[e] = lo | (hi << 16);
+  }
+  reinterpret_cast<u32x4*>(wsum)[i] = out;
+}
+
+size_t value_weight_ws_bytes(int L, int H, int D, int group_mode) {
+  if (group_mode == 0) return 0;
+  return (size_t)L * D * H * kHeadDim * sizeof(__bf16);
+}
+
 hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int G, int n,
-                               int D, int n_cand, float* weight, hipStream_t st) {
+                               int D, int n_cand, int group_mode, float* weight, void* ws,
+                               hipStream_t st) {
   const int key_blocks = (n_cand + gBlock - 1) / gBlock;
   const long long blocks = (long long)key_blocks * H * L;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const __bf16* proj = static_cast<const __bf16*>(w_o);
+  int g_eff = G;
+  if (group_mode == 1) {
+    // mode 1 is mode 0 with one query head per KV head on the summed slices
+    __bf16* wsum = static_cast<__bf16*>(ws);
+    const long long pieces = (long long)L * D * H * (kHeadDim / 8);
+    const long long pb = (pieces + 255) / 256;
+    if (pb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_wo_group_sum, dim3((unsigned)pb), dim3(256), 0, st,
+                       static_cast<const __bf16*>(w_o), H, G, pieces, wsum);
+    proj = wsum;
+    g_eff = 1;
+  }
   hipLaunchKernelGGL(k_value_weight, dim3((unsigned)blocks), dim3(512), 0, st,
-                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(w_o), H, G, n, D,
-                     n_cand, key_blocks, weight);
+                     static_cast<const __bf16*>(v), proj, H, g_eff, n, D, n_cand, key_blocks,
+                     weight);
   return hipGetLastError();
 }
 

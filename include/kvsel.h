@@ -7,6 +7,8 @@
  *                Perturbation Perspective" (Korean translation, sumin.im)
  *   [KVzip]      review of "KVzip: Query-Agnostic KV Cache Compression with
  *                Context Reconstruction" (manon006.tistory.com)
+ *   [AnchorKV]   review of "AnchorKV: Anchor-Residual KV Cache Compression"
+ *                (charstring.tistory.com)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -20,9 +22,10 @@
  *    synchronised. No call allocates device memory or synchronises.
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
- *  - Workspace protocol (kvsel_score, kvsel_score_chunked, kvsel_select,
- *    kvsel_select_budgets, kvsel_head_budgets, kvsel_anchor_select,
- *    kvsel_anchor_assign, kvsel_decode_attention): with ws == NULL the
+ *  - Workspace protocol (kvsel_score, kvsel_score_chunked,
+ *    kvsel_value_weight, kvsel_select, kvsel_select_budgets,
+ *    kvsel_head_budgets, kvsel_anchor_select, kvsel_anchor_assign,
+ *    kvsel_decode_attention): with ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
  *    launches nothing. Otherwise *ws_bytes is the size of `ws` (checked).
  *    Workspace contents need no initialisation and are scratch afterwards.
@@ -138,17 +141,32 @@ int32_t kvsel_score_chunked(const void* q, const void* k, const void* k_self,
                             int32_t pool, float* scores, float* raw,
                             void* ws, size_t* ws_bytes, void* stream);
 
+/* How the G query heads of a KV head combine in kvsel_value_weight. */
+enum {
+  /* Mean over g of the L1 norm of each query head's projection (Theorem
+     3.3 of [CriticalKV] is per attention head; the group's attention is
+     summed before pooling). */
+  KVSEL_GROUP_MEAN_OF_NORMS = 0,
+  /* L1 norm of the group-summed projection (sum_g W_O^(h,g)) v: one
+     D-vector per KV head and position, the size of the V W^O intermediate
+     [CriticalKV] §D.4 quotes; G times fewer matrix flops. */
+  KVSEL_GROUP_NORM_OF_SUM = 1
+};
+
 /*
  * kvsel_value_weight -- CriticalKV's projected-value norm.
  *
  * [CriticalKV] §3.3, Algorithm 1, steps 2-3: V_proj = V W^O and the L1
  * norm of each row of V_proj (Theorem 3.3: the output perturbation is
- * bounded by attention weight times this norm). Under GQA the weight of
- * KV head h at position j is the mean over its G query heads:
- *   weight[l][h][j] = (1/G) sum_g sum_{c<D} | sum_{e<d}
- *                        w_o[l][c][(h*G+g)*d + e] * v[l][h][j][e] |
- * for j < n_cand. The projection is accumulated in fp32 from bf16 and is
- * never written out.
+ * bounded by attention weight times this norm). W_O^(h,g) is the D x d
+ * column slice w_o[l][:][(h*G+g)*d .. +d) of query head h*G+g. For j < n_cand:
+ *   group_mode 0 (KVSEL_GROUP_MEAN_OF_NORMS):
+ *     weight[l][h][j] = (1/G) sum_g sum_{c<D} | (W_O^(h,g) v[l][h][j])_c |
+ *   group_mode 1 (KVSEL_GROUP_NORM_OF_SUM):
+ *     weight[l][h][j] = sum_{c<D} | ((sum_g W_O^(h,g)) v[l][h][j])_c |
+ * The projection is accumulated in fp32 from bf16 and is never written
+ * out. In mode 1 the summed slices are formed in fp32 and rounded once to
+ * bf16 (round to nearest-even) in the workspace before the product.
  *
  *   v      bf16 [L][H_kv][n][d]
  *   w_o    bf16 [L][D][H_kv*G*d]     output projection, (out, in) layout
@@ -156,11 +174,13 @@ int32_t kvsel_score_chunked(const void* q, const void* k, const void* k_self,
  *
  * Limits: d == 128, D % 32 == 0, and one layer's w_o must span less than
  * 2^31 bytes (D * H_kv*G*d * 2 < 2^31); else KVSEL_ERR_UNSUPPORTED.
+ * Needs a workspace (protocol above): none for mode 0 (0 bytes; any
+ * 16-byte-aligned non-NULL ws runs the call), L*D*H_kv*d*2 bytes for mode 1.
  */
 int32_t kvsel_value_weight(const void* v, const void* w_o,
                            int32_t L, int32_t H_kv, int32_t G, int32_t d,
-                           int32_t n, int32_t D, int32_t n_cand,
-                           float* weight, void* stream);
+                           int32_t n, int32_t D, int32_t n_cand, int32_t group_mode,
+                           float* weight, void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * kvsel_value_l2_factor, kvsel_value_weight_l2 -- the L2 form of the
@@ -416,9 +436,11 @@ int32_t kvsel_compact(const void* k, const void* v,
  *   head_offsets i32  [L][H_kv+1] or NULL: head h of layer l owns rows
  *                [head_offsets[l][h], head_offsets[l][h+1]) (as written by
  *                kvsel_select); NULL: every head owns kept_per_layer/H_kv
- *                consecutive rows. Offsets are clamped into
- *                [0, kept_per_layer]; a head whose end is not past its start
- *                is empty.
+ *                consecutive rows. Each offset is clamped into
+ *                [0, kept_per_layer] and then raised to the largest offset
+ *                before it in the row, so heads are disjoint ranges of the
+ *                layer's rows (valid offsets are unchanged; a head whose
+ *                end is not past its start is empty).
  *   out          f32  [L][H_kv*G][d]
  *   scale        softmax temperature (the model's 1/sqrt(d)), > 0
  *
@@ -436,7 +458,7 @@ int32_t kvsel_decode_attention(const void* q, const void* k, const void* v,
 /* Human-readable name of a status code (static string). */
 const char* kvsel_status_str(int32_t status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int32_t kvsel_abi_version(void);
 
 #ifdef __cplusplus

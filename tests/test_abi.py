@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvsel_abi_version() == 1
+    assert lib.kvsel_abi_version() == 2
     for code in (OK, ARG, UNSUP, WS, 4):
         assert kv.kvsel_status_str(code).startswith("KVSEL")
     assert "unknown" in kv.kvsel_status_str(99)
@@ -137,17 +137,35 @@ def test_select_two_stage_ranges(lib, kw, code):
 def test_value_weight_and_compact_reject(lib):
     p = ctypes.c_void_p(1 << 20)
     f = lib.kvsel_value_weight
-    assert f(None, p, 1, 8, 4, 128, 100, 4096, 68, p, None) == ARG
-    assert f(p, p, 1, 8, 4, 128, 100, 4096, 101, p, None) == ARG    # n_cand > n
-    assert f(p, p, 1, 8, 4, 128, 100, 4096, 0, p, None) == ARG
-    assert f(p, p, 1, 8, 4, 64, 100, 4096, 68, p, None) == UNSUP
-    assert f(p, p, 1, 8, 4, 128, 100, 4010, 68, p, None) == UNSUP   # D % 32
-    assert f(p, p, 1, 8, 4, 128, 100, 1 << 18, 68, p, None) == UNSUP  # w_o of 2^31 bytes
+    nb = ctypes.c_size_t(1 << 30)
+    ws = ctypes.byref(nb)
+    assert f(None, p, 1, 8, 4, 128, 100, 4096, 68, 0, p, p, ws, None) == ARG
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 101, 0, p, p, ws, None) == ARG    # n_cand > n
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 0, 0, p, p, ws, None) == ARG
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 68, 2, p, p, ws, None) == ARG     # group mode
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 68, -1, p, p, ws, None) == ARG
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 68, 0, p, p, None, None) == ARG   # no ws_bytes
+    assert f(p, p, 1, 8, 4, 64, 100, 4096, 68, 0, p, p, ws, None) == UNSUP
+    assert f(p, p, 1, 8, 4, 128, 100, 4010, 68, 0, p, p, ws, None) == UNSUP   # D % 32
+    assert f(p, p, 1, 8, 4, 128, 100, 1 << 18, 68, 0, p, p, ws, None) == UNSUP  # w_o of 2^31 bytes
+    small = ctypes.c_size_t(1000)
+    assert f(p, p, 2, 8, 4, 128, 100, 4096, 68, 1, p, p, ctypes.byref(small), None) == WS
+    assert f(p, p, 1, 8, 4, 128, 100, 4096, 68, 1, p, ctypes.c_void_p((1 << 20) + 8), ws, None) == ARG
     c = lib.kvsel_compact
     assert c(None, p, 1, 8, 128, 100, p, None, 16, p, p, None) == ARG
     assert c(p, p, 1, 8, 128, 100, p, None, 12, p, p, None) == ARG  # not divisible by H
     assert c(p, p, 1, 8, 128, 100, p, None, 808, p, p, None) == ARG  # more rows than the cache
     assert c(p, p, 1, 8, 12, 100, p, None, 16, p, p, None) == UNSUP
+
+
+def test_value_weight_workspace_query(lib):
+    nb = ctypes.c_size_t(123)
+    f = lib.kvsel_value_weight
+    # group mode 0 needs none; mode 1 holds the group-summed slices of every layer
+    assert f(None, None, 2, 8, 4, 128, 100, 4096, 68, 0, None, None, ctypes.byref(nb), None) == OK
+    assert nb.value == 0
+    assert f(None, None, 2, 8, 4, 128, 100, 4096, 68, 1, None, None, ctypes.byref(nb), None) == OK
+    assert nb.value == 2 * 4096 * 8 * 128 * 2
 
 
 def _decode(lib, **kw):

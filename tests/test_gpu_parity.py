@@ -212,6 +212,34 @@ def test_select_exact_on_same_fp32_scores(case):
             np.testing.assert_array_equal(offs[l], ro)
 
 
+@pytest.mark.parametrize("name", ["f32_tie", "f32_even", "f32_fma"])
+@pytest.mark.parametrize("pad", [0, 40000])
+def test_select_two_stage_f32_hand_examples(name, pad):
+    """The hand-worked float32 stage-2 keys (tests/golden/select_examples.txt):
+    the kernel's mul, add, mul rounding decides the pick exactly as worked
+    out by hand. pad > 0 appends zero-weight candidates after the two, so the
+    segment runs on the many-workgroup path; they never beat the two."""
+    from oracle_pins import load_golden
+    g = load_golden("select_examples.txt")
+    sc = np.zeros((1, 1, 2 + pad), np.float32)
+    wt = np.zeros((1, 1, 2 + pad), np.float32)
+    sc[0, 0, :2] = g[name + ".pooled"]
+    wt[0, 0, :2] = g[name + ".weight"]
+    W = int(g[name + ".W"][0])
+    n = 2 + pad + W
+    budget = int(g[name + ".budget"][0])
+    print(f"[gpu] kvsel_select fp32 hand example {name} pad={pad}", flush=True)
+    idx, _, stage = kv.kvsel_select(torch.from_numpy(sc).cuda(), n=n, W=W, budget=budget,
+                                    weight=torch.from_numpy(wt).cuda(),
+                                    score_norm=g[name + ".score_norm"][0], eps=g[name + ".eps"][0],
+                                    alpha=g[name + ".alpha"][0], return_stage=True)
+    torch.cuda.synchronize()
+    want = [int(x) for x in g[name + ".kept"]]
+    want = want[:1] + list(range(n - W, n))
+    np.testing.assert_array_equal(idx.cpu().numpy()[0, 0], want)
+    np.testing.assert_array_equal(stage.cpu().numpy()[0, 0], [2] + [0] * W)
+
+
 BUDGET_CASES = [
     # (L, H, n, W, two_stage, alpha, levels, stride_extra)
     (2, 4, 300, 8, False, 0.5, 7, 0),
@@ -630,23 +658,44 @@ def test_compact_bit_exact(adaptive, d):
 
 # ------------------------------------------------------------ value weight ----
 
+@pytest.mark.parametrize("group_mode", [kv.GROUP_MEAN_OF_NORMS, kv.GROUP_NORM_OF_SUM])
 @pytest.mark.parametrize("L,H,G,n,D,n_cand", [
     (1, 2, 4, 300, 256, 290),
     (1, 1, 7, 97, 64, 97),
     (1, 3, 1, 1000, 32, 999),     # half a W_O tile
     (2, 2, 3, 1500, 96, 1400),    # several key blocks, ragged, last tile half
+    (2, 3, 8, 700, 4096, 650),    # the model's D, G = 8
 ])
-def test_value_weight(L, H, G, n, D, n_cand):
+def test_value_weight(L, H, G, n, D, n_cand, group_mode):
+    """Mode 0 against the fp64 mean of per-query-head norms; mode 1 against
+    the fp64 norm of the exactly summed slices (the kernel rounds the summed
+    slices to bf16 once, ~2^-9 relative per element, which averages out in
+    the L1 sum far below the 1e-3 bar on these inputs)."""
     wl = _wl(L=L, H_kv=H, G=G, n=n, W=n - n_cand if n_cand < n else 1, value_weight=True, D=D)
     data = gen(wl, seed=6, which=("v", "w_o"))
-    print(f"[gpu] kvsel_value_weight L={L} H={H} G={G} n={n} D={D}", flush=True)
-    w = kv.kvsel_value_weight(to_dev(data["v"]), to_dev(data["w_o"]), G=G, n_cand=n_cand)
+    print(f"[gpu] kvsel_value_weight L={L} H={H} G={G} n={n} D={D} mode={group_mode}", flush=True)
+    w = kv.kvsel_value_weight(to_dev(data["v"]), to_dev(data["w_o"]), G=G, n_cand=n_cand,
+                              group_mode=group_mode)
     torch.cuda.synchronize()
     w = w.cpu().numpy()
+    norm = oracle.value_weight if group_mode == kv.GROUP_MEAN_OF_NORMS else oracle.value_weight_group_sum
     for l in range(L):
-        ref = oracle.value_weight(synth.bf16_to_f64(data["v"][l]), synth.bf16_to_f64(data["w_o"][l]),
-                                  G, np.arange(n_cand))
+        ref = norm(synth.bf16_to_f64(data["v"][l]), synth.bf16_to_f64(data["w_o"][l]), G,
+                   np.arange(n_cand))
         assert_scores_close(w[l], ref, "value weight")
+
+
+def test_value_weight_group_sum_single_head_is_mode0():
+    """With G = 1 the summed slice is the slice itself (no rounding): both
+    group modes give the same bits."""
+    wl = _wl(L=2, H_kv=3, G=1, n=900, W=1, value_weight=True, D=256)
+    data = gen(wl, seed=9, which=("v", "w_o"))
+    v, w_o = to_dev(data["v"]), to_dev(data["w_o"])
+    print("[gpu] kvsel_value_weight G=1 both modes", flush=True)
+    a = kv.kvsel_value_weight(v, w_o, G=1, group_mode=kv.GROUP_MEAN_OF_NORMS)
+    b = kv.kvsel_value_weight(v, w_o, G=1, group_mode=kv.GROUP_NORM_OF_SUM)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 # L2 form: the kernel factors each query head's W^T W (Cholesky, fp32) and
@@ -769,21 +818,31 @@ def test_decode_attention(case):
         _assert_decode_close(out[l], ref, np.abs(vl).max(), f"decode layer {l}")
 
 
-def test_decode_attention_clamps_offsets():
-    """Offsets outside [0, kept] are clamped and a head ending before its
-    start is empty: nothing outside the layer's rows is read."""
+@pytest.mark.parametrize("kept,offsets", [
+    (300, [-5, 100, 40, 290, 9999]),
+    # overlapping heads: each clamped offset alone would give 8 work items
+    # against the 7 the grid and workspace hold (regression test)
+    (1024, [0, 1024, 0, 1024]),
+])
+def test_decode_attention_clamps_offsets(kept, offsets):
+    """Offsets are clamped into [0, kept] and raised to the largest earlier
+    one, so the heads are disjoint ranges inside the layer: nothing outside
+    the layer's rows or the workspace is read."""
     rng = np.random.default_rng(77)
-    L, H, G, kept = 1, 4, 2, 300
+    L, G = 1, 2
+    H = len(offsets) - 1
     q = synth.bf16_bits(rng.normal(size=(L, H * G, 128)).astype(np.float32))
     k = synth.bf16_bits(rng.normal(size=(L, kept, 128)).astype(np.float32))
     v = synth.bf16_bits(rng.normal(size=(L, kept, 128)).astype(np.float32))
-    offs = np.array([[-5, 100, 40, 290, 9999]], np.int32)
+    offs = np.array([offsets], np.int32)
+    print(f"[gpu] kvsel_decode_attention offsets {offsets} kept={kept}", flush=True)
     out = kv.kvsel_decode_attention(to_dev(q), to_dev(k), to_dev(v), G=G, scale=0.09,
                                     head_offsets=torch.from_numpy(offs).cuda())
     torch.cuda.synchronize()
     out = out.cpu().numpy()[0]
-    # each offset clamped into [0, kept]: head 1 = [100, 40) is empty, head 2 = [40, 290)
-    eff = np.clip(offs[0], 0, kept)
+    # [-5, 100, 40, 290, 9999] -> [0, 100, 100, 290, 300]: head 1 empty, head 2 = [100, 290)
+    # [0, 1024, 0, 1024] -> [0, 1024, 1024, 1024]: heads 1 and 2 empty
+    eff = np.maximum.accumulate(np.clip(offs[0], 0, kept))
     ref = oracle.decode_attention(synth.bf16_to_f64(q[0]), synth.bf16_to_f64(k[0]),
                                   synth.bf16_to_f64(v[0]), G, 0.09, eff)
     _assert_decode_close(out, ref, np.abs(synth.bf16_to_f64(v[0])).max(), "clamped offsets")
