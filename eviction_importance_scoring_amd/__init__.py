@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_score_chunked", "kvsel_value_weight",
     "kvsel_value_l2_factor", "kvsel_value_weight_l2",
-    "kvsel_select", "kvsel_select_budgets", "kvsel_head_score", "kvsel_head_budgets",
+    "kvsel_select", "kvsel_select_static", "kvsel_static_scratch_bytes", "kvsel_select_budgets", "kvsel_head_score", "kvsel_head_budgets",
     "kvsel_anchor_select", "kvsel_anchor_assign",
     "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
@@ -71,6 +71,8 @@ _SIGNATURES = {
     "kvsel_decode_attention": [_c_void_p, _c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32,
                                _c_i64, _c_void_p, _c_f32, _c_void_p, _c_void_p, _c_size_p,
                                _c_void_p],
+    "kvsel_select_static": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                            _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "kvsel_status_str": [_c_i32],
     "kvsel_abi_version": [],
 }
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = _c_i32
         l.kvsel_status_str.restype = ctypes.c_char_p
+        l.kvsel_static_scratch_bytes.argtypes = []
+        l.kvsel_static_scratch_bytes.restype = ctypes.c_size_t
         _LIB = l
     return _LIB
 
@@ -312,6 +316,36 @@ def kvsel_select(scores, *, n: int, W: int, budget: int, adaptive: bool = False,
     _check(f(_ptr(scores), _ptr(weight), *args, _ptr(idx), _ptr(offs), _ptr(stage), _ptr(ws),
              ctypes.byref(nbytes), _stream(dev)))
     return idx, offs, stage
+
+
+def kvsel_select_static(scores, *, n: int, W: int, budget: int, adaptive: bool = False,
+                        weight=None, score_norm: float = 1.0, eps: float = 1e-4,
+                        alpha: float = 0.5, idx=None, head_offsets=None, stage=None):
+    """kvsel_select through the entry point that takes its scratch from the
+    library's static device array (no workspace). Outputs as kvsel_select;
+    caller-supplied idx / head_offsets / stage are checked and written."""
+    _need(scores, torch.float32, "scores", 3)
+    dev = scores.device
+    if weight is not None:
+        _need(weight, torch.float32, "weight", 3, dev)
+        if weight.shape != scores.shape:
+            raise ValueError("weight must match scores")
+    L, H, n_cand = scores.shape
+    if n_cand != n - W:
+        raise ValueError(f"scores has {n_cand} candidates, expected n-W={n - W}")
+    shape = (L, budget) if adaptive else (L, H, budget)
+    idx = _out(idx, torch.int32, "idx", shape, dev)
+    offs = _out(head_offsets, torch.int32, "head_offsets", (L, H + 1), dev) if adaptive else None
+    if stage is not None:
+        stage = _out(stage, torch.uint8, "stage", shape, dev)
+    args = (L, H, n, W, int(budget), int(adaptive), float(score_norm), float(eps), float(alpha))
+    _check(lib().kvsel_select_static(_ptr(scores), _ptr(weight), *args, _ptr(idx), _ptr(offs),
+                                     _ptr(stage), _stream(dev)))
+    return idx, offs, stage
+
+
+def kvsel_static_scratch_bytes() -> int:
+    return int(lib().kvsel_static_scratch_bytes())
 
 
 def kvsel_select_budgets(scores, budgets, *, n: int, W: int, layer_stride: int | None = None,

@@ -27,6 +27,48 @@ constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 }  // namespace
 
+namespace kvsel {
+
+// Argument checks and plan of kvsel_select (shared with the entry point
+// that takes its scratch from a static device array).
+int32_t select_plan(bool two_stage, int32_t L, int32_t H_kv, int32_t n, int32_t W, int64_t budget,
+                    int32_t adaptive, float score_norm, float eps, float alpha, SelectPlan* out) {
+  if (L < 1 || H_kv < 1 || n < 1 || W < 0 || W >= n) return KVSEL_ERR_ARG;
+  if (adaptive != 0 && adaptive != 1) return KVSEL_ERR_ARG;
+  const int64_t n_cand = (int64_t)n - W;
+  const int64_t groups = adaptive ? H_kv : 1;
+  if (budget < groups * W || budget > groups * (int64_t)n) return KVSEL_ERR_ARG;
+  if (two_stage) {
+    if (!(alpha >= 0.f && alpha <= 1.f)) return KVSEL_ERR_ARG;
+    if (!(score_norm > 0.f) || !std::isfinite(score_norm)) return KVSEL_ERR_ARG;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return KVSEL_ERR_ARG;
+  }
+  if (groups * n_cand > kMaxIndex || budget > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
+  if (adaptive && !select_groups_ok(H_kv)) return KVSEL_ERR_UNSUPPORTED;
+  SelectPlan& p = *out;
+  p.L = L; p.H = H_kv; p.n = n; p.W = W; p.n_cand = (int)n_cand;
+  p.budget = budget;
+  p.adaptive = adaptive != 0;
+  p.two_stage = two_stage;
+  p.score_norm = score_norm;
+  p.eps = eps;
+  p.k = budget - groups * W;
+  p.k1 = p.two_stage ? (int64_t)std::floor((double)alpha * (double)p.k) : 0;
+  p.segments = adaptive ? L : L * H_kv;
+  p.seg_len = groups * n_cand;
+  p.resident = false;
+  return KVSEL_OK;
+}
+
+int32_t select_pointers_ok(const SelectPlan& p, const float* scores, const float* weight,
+                           const int32_t* idx, const int32_t* head_offsets) {
+  if (!scores || (p.budget > 0 && !idx) || (p.adaptive && !head_offsets)) return KVSEL_ERR_ARG;
+  if (!aligned16(scores) || (weight && !aligned16(weight))) return KVSEL_ERR_ARG;
+  return KVSEL_OK;
+}
+
+}  // namespace kvsel
+
 extern "C" {
 
 int32_t kvsel_abi_version(void) { return 2; }
@@ -38,6 +80,7 @@ const char* kvsel_status_str(int32_t status) {
     case KVSEL_ERR_UNSUPPORTED: return "KVSEL_ERR_UNSUPPORTED: request outside what this build covers";
     case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE: workspace too small";
     case KVSEL_ERR_HIP: return "KVSEL_ERR_HIP: HIP launch failed";
+    case KVSEL_ERR_SCRATCH: return "KVSEL_ERR_SCRATCH: request needs more than the static scratch";
     default: return "KVSEL: unknown status";
   }
 }
@@ -190,37 +233,17 @@ int32_t kvsel_select(const float* scores, const float* weight, int32_t L, int32_
                      float eps, float alpha, int32_t* idx, int32_t* head_offsets,
                      uint8_t* stage, void* ws, size_t* ws_bytes, void* stream) {
   if (!ws_bytes) return KVSEL_ERR_ARG;
-  if (L < 1 || H_kv < 1 || n < 1 || W < 0 || W >= n) return KVSEL_ERR_ARG;
-  if (adaptive != 0 && adaptive != 1) return KVSEL_ERR_ARG;
-  const int64_t n_cand = (int64_t)n - W;
-  const int64_t groups = adaptive ? H_kv : 1;
-  if (budget < groups * W || budget > groups * (int64_t)n) return KVSEL_ERR_ARG;
-  if (weight) {
-    if (!(alpha >= 0.f && alpha <= 1.f)) return KVSEL_ERR_ARG;
-    if (!(score_norm > 0.f) || !std::isfinite(score_norm)) return KVSEL_ERR_ARG;
-    if (!(eps >= 0.f) || !std::isfinite(eps)) return KVSEL_ERR_ARG;
-  }
-  if (groups * n_cand > kMaxIndex || budget > kMaxIndex) return KVSEL_ERR_UNSUPPORTED;
-  if (adaptive && !select_groups_ok(H_kv)) return KVSEL_ERR_UNSUPPORTED;
   SelectPlan p;
-  p.L = L; p.H = H_kv; p.n = n; p.W = W; p.n_cand = (int)n_cand;
-  p.budget = budget;
-  p.adaptive = adaptive != 0;
-  p.two_stage = weight != nullptr;
-  p.score_norm = score_norm;
-  p.eps = eps;
-  p.k = budget - groups * W;
-  p.k1 = p.two_stage ? (int64_t)std::floor((double)alpha * (double)p.k) : 0;
-  p.segments = adaptive ? L : L * H_kv;
-  p.seg_len = groups * n_cand;
-  p.resident = false;
+  const int32_t rc = select_plan(weight != nullptr, L, H_kv, n, W, budget, adaptive, score_norm,
+                                 eps, alpha, &p);
+  if (rc != KVSEL_OK) return rc;
   const size_t need = select_ws_bytes(p);
   if (!ws) {
     *ws_bytes = need;
     return KVSEL_OK;
   }
-  if (!scores || (budget > 0 && !idx) || (adaptive && !head_offsets)) return KVSEL_ERR_ARG;
-  if (!aligned16(scores) || (weight && !aligned16(weight))) return KVSEL_ERR_ARG;
+  const int32_t rp = select_pointers_ok(p, scores, weight, idx, head_offsets);
+  if (rp != KVSEL_OK) return rp;
   if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return KVSEL_ERR_ARG;
   const hipError_t e = select_launch(p, scores, weight, idx, head_offsets, stage, ws,

@@ -63,6 +63,10 @@ struct SelectPlan {
 };
 
 size_t select_ws_bytes(const SelectPlan& p);
+int32_t select_plan(bool two_stage, int32_t L, int32_t H_kv, int32_t n, int32_t W, int64_t budget,
+                    int32_t adaptive, float score_norm, float eps, float alpha, SelectPlan* out);
+int32_t select_pointers_ok(const SelectPlan& p, const float* scores, const float* weight,
+                           const int32_t* idx, const int32_t* head_offsets);
 hipError_t select_launch(const SelectPlan& p, const float* scores, const float* weight,
                          int32_t* idx, int32_t* head_offsets, uint8_t* stage, void* ws,
                          hipStream_t st);

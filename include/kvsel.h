@@ -50,7 +50,8 @@ enum {
   KVSEL_ERR_ARG = 1,          /* null required pointer, bad size, bad range */
   KVSEL_ERR_UNSUPPORTED = 2,  /* valid request this build does not cover    */
   KVSEL_ERR_WORKSPACE = 3,    /* ws given but *ws_bytes is too small        */
-  KVSEL_ERR_HIP = 4           /* a HIP launch failed; outputs undefined     */
+  KVSEL_ERR_HIP = 4,          /* a HIP launch failed; outputs undefined     */
+  KVSEL_ERR_SCRATCH = 5       /* needs more than the static scratch holds   */
 };
 
 /* Which queries score the cache. */
@@ -265,6 +266,32 @@ int32_t kvsel_select(const float* scores, const float* weight,
                      float score_norm, float eps, float alpha,
                      int32_t* idx, int32_t* head_offsets, uint8_t* stage,
                      void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_select_static -- kvsel_select without a workspace argument.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Same
+ * arguments, outputs and results as kvsel_select, bit for bit; the scratch
+ * memory kvsel_select takes from `ws` comes instead from a static device
+ * array of kvsel_static_scratch_bytes() bytes (16 MiB) that each GPU the
+ * library runs on holds until the process ends. The call allocates
+ * nothing. A request whose workspace (kvsel_select's *ws_bytes) exceeds
+ * that size returns KVSEL_ERR_SCRATCH and launches nothing. All calls on
+ * one GPU share its array: calls that overlap on a GPU (concurrent streams
+ * or threads) race and give undefined results; calls ordered on one
+ * stream are safe. The first call on a device looks up that device's copy
+ * of the array (the device current at the call).
+ */
+int32_t kvsel_select_static(const float* scores, const float* weight,
+                            int32_t L, int32_t H_kv, int32_t n, int32_t W,
+                            int64_t budget, int32_t adaptive,
+                            float score_norm, float eps, float alpha,
+                            int32_t* idx, int32_t* head_offsets, uint8_t* stage,
+                            void* stream);
+
+/* Size in bytes of kvsel_select_static's static scratch (per GPU). */
+size_t kvsel_static_scratch_bytes(void);
 
 /*
  * kvsel_select_budgets -- per-head selection under a budget vector.

@@ -43,9 +43,22 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), f"{name} declared in kvsel.h but not exported"
 
 
+def test_select_static_checks(lib):
+    """Checks run before any HIP call: a request needing more than the static
+    scratch is refused with KVSEL_ERR_SCRATCH, missing pointers with ARG."""
+    f = lib.kvsel_select_static
+    assert lib.kvsel_static_scratch_bytes() == 16 << 20
+    # 8000 segments of 50,000 candidates: the many-workgroup state alone is ~66 MB
+    assert f(None, None, 1000, 8, 50000, 32, 1000, 0, 1.0, 1e-4, 0.5, None, None, None,
+             None) == 5
+    assert kv.kvsel_status_str(5).startswith("KVSEL_ERR_SCRATCH")
+    assert f(None, None, 1, 8, 50000, 32, 1000, 0, 1.0, 1e-4, 0.5, None, None, None, None) == ARG
+    assert f(None, None, 1, 8, 50000, 32, 20, 0, 1.0, 1e-4, 0.5, None, None, None, None) == ARG
+
+
 def test_version_and_status_strings(lib):
     assert lib.kvsel_abi_version() == 2
-    for code in (OK, ARG, UNSUP, WS, 4):
+    for code in (OK, ARG, UNSUP, WS, 4, 5):
         assert kv.kvsel_status_str(code).startswith("KVSEL")
     assert "unknown" in kv.kvsel_status_str(99)
 
