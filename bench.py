@@ -61,11 +61,40 @@ def traffic_from_profiles(key, sha):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, host, seconds, w_host=None, budgets=None, rand=None):
+    """The oracle (fp64 numpy) on the same inputs, timed twice: with one BLAS
+    thread, then with the BLAS thread pool as configured for this process
+    (OMP_NUM_THREADS, the host's CPU share). Reported in KV entries per
+    second, the all-thread rate as the value."""
+    from threadpoolctl import threadpool_limits
+    usable = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=1):
+        one = _cpu_baseline_run(wl, host, seconds / 2, w_host, budgets, rand)
+    allt = _cpu_baseline_run(wl, host, seconds, w_host, budgets, rand)
+    allt["value_1thread"] = one["value"]
+    allt["sample_1thread"] = one["sample"]
+    allt["cpu_model"] = cpu_model()
+    allt["logical_cpus_usable"] = usable
+    allt["logical_cpus_host"] = os.cpu_count()
+    return allt
+
+
+def _cpu_baseline_run(wl, host, seconds, w_host=None, budgets=None, rand=None):
     """The oracle (fp64 numpy) on the same inputs, one (layer, KV head) at a
     time in order, until `seconds` of CPU work: attention scores, max-pool,
     the value weight when the workload uses it, and top-k selection.
-    Reported in KV entries per second."""
+    Reported in KV entries per second; `cores` = the BLAS threads in use."""
     import numpy as np
 
     import oracle
@@ -142,6 +171,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not overwrite a 1 GiB buffer between timed steps")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw the inputs on the GPU (default for caches above 4 GB)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -298,8 +329,19 @@ def main():
             marks[4].record()
         return kept, offs
 
+    # Between timed steps a 1 GiB buffer is overwritten, so no step finds its
+    # inputs in the 256 MB memory-side cache (the small workloads' K would
+    # fit there); each step is timed on its own with events, the overwrite
+    # outside them.
+    flush_buf = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(1.0)
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize(dev)
     marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
@@ -309,13 +351,18 @@ def main():
     wall0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
+        flush()
         kept_kv, kept_offs = step(marks[s])
     end.record()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(end) / args.steps
-    part = lambda a, b: float(np.mean([m[a].elapsed_time(m[b]) for m in marks]))
+    per_step = [m[0].elapsed_time(m[4]) for m in marks]
+    ms_step = float(np.mean(per_step))
+    span = lambda a, b: [m[a].elapsed_time(m[b]) for m in marks]
+    part = lambda a, b: float(np.mean(span(a, b)))
     ms_score, ms_vw, ms_sel, ms_cmp = part(0, 1), part(1, 2), part(2, 3), part(3, 4)
+    stats = lambda xs: {"mean": float(np.mean(xs)), "median": float(np.median(xs)),
+                        "min": float(np.min(xs))}
 
     entries = wl.L * wl.H_kv * wl.n
     # algorithmic bytes of one scoring call: K read once, Q read once,
@@ -363,8 +410,17 @@ def main():
                         {"score": ms_score, **({"value_weight": ms_vw} if wl.value_weight else {}),
                          **({"head_score+head_budgets": ms_vw} if keep else {}),
                          "select": ms_sel, "compact": ms_cmp}),
+        "per_call_ms_stats": {
+            "step": stats(per_step), "score": stats(span(0, 1)),
+            **({"value_weight": stats(span(1, 2))} if wl.value_weight else {}),
+            "select" if not wl.anchor_k else "anchor_select": stats(span(2, 3)),
+            "compact" if not wl.anchor_k else "anchor_assign_k": stats(span(3, 4))},
         "scored_selected_entries_per_s": entries / ((ms_score + ms_sel) * 1e-3),
         "wall_s_timed": wall,
+        "timing": ("each step between HIP events on the stream it runs on; a 1 GiB buffer "
+                   "overwritten before every step, outside its events" if flush_buf is not None
+                   else "each step between HIP events on the stream it runs on; no cache flush"),
+        "ms_per_step_incl_flush": start.elapsed_time(end) / args.steps,
     }
     # rooflines of the calls: the window score is HBM-bound (algorithmic bytes:
     # K read once, Q read once, pooled scores written once); the many-query
