@@ -1,0 +1,356 @@
+"""Host replay of the global-memory index arithmetic of the selection,
+compaction and decoding kernels.
+
+Each function below re-states, for every workgroup and thread of a launch,
+the address expressions of one kernel of the HIP library (the kernel named
+in its docstring) and returns the element indices it would read or write in
+each global buffer. The integer buffers the kernels read and trust (index
+lists, head offsets, budget vectors, the many-workgroup select's per-segment
+state and per-chunk counts) are inputs here, so a test can feed arbitrary
+values, including values no correct earlier kernel would leave, and check
+that every access stays inside the buffer the library was given.
+
+Floating-point data never decides an address in these kernels, so only the
+integer inputs are replayed; a membership test on a key is replaced by an
+arbitrary choice where its outcome feeds an index (every outcome is then
+covered). Indices are Python/numpy integers computed with the kernels'
+widths: uint32 arithmetic wraps modulo 2^32 where the kernel's does.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+U32 = 1 << 32
+
+
+def _u32(x):
+    return np.asarray(x, np.int64) % U32
+
+
+class Accesses:
+    """Per buffer: the list of index arrays touched (reads and writes)."""
+
+    def __init__(self):
+        self.by_buffer: dict[str, list[np.ndarray]] = {}
+
+    def add(self, name, idx):
+        a = np.asarray(idx, np.int64).ravel()
+        if a.size:
+            self.by_buffer.setdefault(name, []).append(a)
+
+    def extent(self, name):
+        parts = self.by_buffer.get(name)
+        if not parts:
+            return None
+        a = np.concatenate(parts)
+        return int(a.min()), int(a.max())
+
+    def check(self, sizes: dict):
+        """Asserts every touched index lies in [0, sizes[name])."""
+        for name, parts in self.by_buffer.items():
+            lo, hi = self.extent(name)
+            assert name in sizes, f"untracked buffer {name}"
+            assert lo >= 0 and hi < sizes[name], \
+                f"{name}: touched [{lo}, {hi}] outside [0, {sizes[name]})"
+
+
+# ------------------------------------------------------------- k_compact ----
+
+K_ITEMS, K_COMPACT_THREADS = 4, 256
+
+
+def _search_last_le(table, base, count, value, acc, name):
+    """Binary search of the kernels' 'last h in [0, count-1] with
+    table[base + h] <= value' (vectorised over value); records the reads."""
+    lo = np.zeros(value.shape, np.int64)
+    hi = np.full(value.shape, count - 1, np.int64)
+    while True:
+        act = lo < hi
+        if not act.any():
+            return lo
+        mid = (lo + hi + 1) >> 1
+        acc.add(name, base + mid[act])
+        cond = np.zeros(value.shape, bool)
+        cond[act] = table[base + mid[act]] <= value[act]
+        lo = np.where(act & cond, mid, lo)
+        hi = np.where(act & ~cond, mid - 1, hi)
+
+
+def compact_accesses(L, H, n, vecs, kept, idx, offs):
+    """k_compact (compact.hip): grid (ceil(kept*vecs / 1024), L), block 256,
+    4 items a thread a block-width apart. idx: int32 [L*kept] (arbitrary),
+    offs: int32 [L*(H+1)] (arbitrary) or None (uniform: kept % H == 0, as
+    the library requires)."""
+    acc = Accesses()
+    total = kept * vecs
+    per_block = K_ITEMS * K_COMPACT_THREADS
+    blocks = -(-total // per_block)
+    per_head = 0 if offs is not None else kept // H
+    base_all = (np.arange(blocks, dtype=np.int64)[:, None] * per_block
+                + np.arange(K_COMPACT_THREADS, dtype=np.int64)[None, :]).ravel()
+    for l in range(L):
+        lim = total
+        if offs is not None:
+            acc.add("offs", [l * (H + 1) + H])
+            e = int(offs[l * (H + 1) + H])
+            lim = min(max(e, 0), kept) * vecs
+        base = base_all[base_all < lim]            # the others return at once
+        for j in range(K_ITEMS):
+            item = base + j * K_COMPACT_THREADS
+            row = item // vecs
+            c = item - row * vecs
+            ok = item < lim
+            acc.add("idx", l * kept + row[ok])
+            pos = np.full(item.shape, -1, np.int64)
+            pos[ok] = idx[l * kept + row[ok]]
+            if offs is not None:
+                h = _search_last_le(offs, l * (H + 1), H, row, acc, "offs")
+            else:
+                h = row // per_head
+            load = (pos >= 0) & (pos < n)
+            acc.add("kv", ((l * H + h[load]) * n + pos[load]) * vecs + c[load])
+            acc.add("out", l * total + item[ok])
+    return acc
+
+
+def compact_sizes(L, H, n, vecs, kept, offs):
+    s = {"idx": L * kept, "kv": L * H * n * vecs, "out": L * kept * vecs}
+    if offs is not None:
+        s["offs"] = L * (H + 1)
+    return s
+
+
+# -------------------------------------------------------------- k_decode ----
+
+DEC_CHUNK, DEC_REC, HEAD_DIM = 256, 128 + 2, 128
+
+
+def decode_items(H, kept, ragged):
+    if ragged:
+        return -(-kept // DEC_CHUNK) + H
+    b = kept // H
+    return H * (-(-b // DEC_CHUNK))
+
+
+def _dec_prefix(offs, l, H, kept, acc):
+    """dec_prefix: effective offsets (clamped into [0, kept], then the
+    running maximum) and the per-head work-item prefix."""
+    h = np.arange(H + 1, dtype=np.int64)
+    if offs is not None:
+        acc.add("offs", l * (H + 1) + h)
+        x = np.clip(offs[l * (H + 1) + h].astype(np.int64), 0, kept)
+    else:
+        x = h * (kept // H)
+    eo = np.maximum.accumulate(x)
+    lens = eo[1:] - eo[:-1]
+    cnt = (lens + DEC_CHUNK - 1) // DEC_CHUNK
+    pre = np.concatenate([[0], np.cumsum(cnt)])
+    return eo, pre
+
+
+def decode_accesses(L, H, G, kept, offs):
+    """k_decode (one item of <= 256 kept rows of one head per workgroup) and
+    k_decode_merge (one query head per workgroup), decode.hip. offs: int32
+    [L*(H+1)] (arbitrary) or None (uniform, kept % H == 0)."""
+    acc = Accesses()
+    ragged = offs is not None
+    items = decode_items(H, kept, ragged)
+    rec = G * DEC_REC
+    for l in range(L):
+        eo, pre = _dec_prefix(offs, l, H, kept, acc)
+        its = np.arange(items, dtype=np.int64)
+        its = its[its < pre[H]]                    # the others return at once
+        if its.size:
+            h = _search_last_le(pre, 0, H, its, Accesses(), "lds")
+            r0 = eo[h] + (its - pre[h]) * DEC_CHUNK
+            r1 = np.minimum(eo[h] + (eo[h + 1] - eo[h]), r0 + DEC_CHUNK)
+            assert (r0 < r1).all(), "an item with no rows would clamp its row to r1 - 1 < r0"
+            rows = np.minimum(r0[:, None] + np.arange(DEC_CHUNK)[None, :], (r1 - 1)[:, None])
+            acc.add("kv_rows", l * kept + rows)
+            acc.add("q", ((l * H + h[:, None]) * G + np.arange(G)[None, :]) * HEAD_DIM)
+            acc.add("q", ((l * H + h[:, None]) * G + np.arange(G)[None, :]) * HEAD_DIM + HEAD_DIM - 1)
+            acc.add("part", (l * items + its) * rec)
+            acc.add("part", (l * items + its) * rec + rec - 1)
+        for hh in range(H):
+            i0, i1 = int(pre[hh]), int(pre[hh + 1])
+            for g in range(G):
+                acc.add("out", ((l * H + hh) * G + g) * HEAD_DIM + np.array([0, HEAD_DIM - 1]))
+                if i0 == i1:
+                    continue
+                i = np.arange(i0, i1, dtype=np.int64)
+                acc.add("part", (l * items + i) * rec + g * DEC_REC)
+                acc.add("part", (l * items + i) * rec + g * DEC_REC + HEAD_DIM + 1)
+    return acc
+
+
+def decode_sizes(L, H, G, kept, offs):
+    s = {"kv_rows": L * kept, "q": L * H * G * HEAD_DIM, "out": L * H * G * HEAD_DIM,
+         "part": L * decode_items(H, kept, offs is not None) * G * DEC_REC}
+    if offs is not None:
+        s["offs"] = L * (H + 1)
+    return s
+
+
+# -------------------------------------------------------------- selection ----
+
+SEL_THREADS, M_THREADS, K_CHUNK, K_BINS, K_MAX_GROUPS = 1024, 256, 8192, 2048, 1024
+
+
+def _clamp_budget(b, W, n):
+    b = int(b)
+    return W if b < W else (n if b > n else b)
+
+
+def seg_span(p, seg, budgets):
+    """seg_span (select.hip): what segment `seg` selects and where it writes."""
+    if budgets is None:
+        return dict(k=p["k"], base=seg * p["budget"], room=p["budget"], off=0, end=p["budget"],
+                    reads=[])
+    H, W, n, stride = p["H"], p["W"], p["n"], p["stride"]
+    l, h = divmod(seg, H)
+    off = sum(_clamp_budget(budgets[l * H + j], W, n) for j in range(h))
+    b = _clamp_budget(budgets[l * H + h], W, n)
+    o = min(off, stride)
+    e = min(off + b, stride)
+    return dict(k=(b - W) % U32, base=l * stride + o, room=e - o, off=o, end=e,
+                reads=[l * H + j for j in range(h + 1)])
+
+
+def _segment_writes(p, seg, sp, acc, threads):
+    """The writes every select variant makes after its members are known:
+    the segment's output slots [0, room), head offsets, and (budget vector,
+    last head) the row tail."""
+    o = np.arange(sp["room"], dtype=np.int64)
+    acc.add("idx", sp["base"] + o)
+    if p["budgets"] is not None:
+        H = p["H"]
+        l, h = divmod(seg, H)
+        acc.add("head_offsets", [l * (H + 1) + h])
+        if h + 1 == H:
+            acc.add("head_offsets", [l * (H + 1) + H])
+            acc.add("idx", l * p["stride"] + np.arange(sp["end"], p["stride"], dtype=np.int64))
+    elif p["adaptive"]:
+        acc.add("head_offsets", seg * (p["groups"] + 1) + np.arange(p["groups"] + 1))
+
+
+def select_resident_accesses(p, budgets=None):
+    """k_select (select.hip), global accesses: the score (and weight) loads
+    of the segment, guarded by f < len, and the writes of the emission."""
+    acc = Accesses()
+    length = p["seg_len"]
+    for seg in range(p["segments"]):
+        sp = seg_span(p, seg, budgets)
+        acc.add("budgets", sp["reads"])
+        f = seg * length + np.array([0, length - 1]) if length else np.zeros(0)
+        acc.add("scores", f)
+        if p["two_stage"]:
+            acc.add("weight", f)
+        _segment_writes(p, seg, sp, acc, SEL_THREADS)
+    return acc
+
+
+def msel_chunk(p, c):
+    g = c // p["cpg"]
+    cc = c - g * p["cpg"]
+    begin = g * p["n_cand"] + cc * K_CHUNK
+    end = min(begin + K_CHUNK, (g + 1) * p["n_cand"])
+    return g, begin, end
+
+
+def digit_width(shift):
+    return 10 if shift == 41 else (9 if shift == 9 else 11)
+
+
+def msel_accesses(p, states, ccount, rng, budgets=None):
+    """k_msel_hist, k_msel_pick, k_msel_count, k_msel_offsets, k_msel_emit
+    (select.hip) with arbitrary segment states (shift, need, done) and
+    arbitrary per-chunk counts. Where a membership test decides a rank, each
+    thread's member count is drawn at random within its 32 candidates."""
+    acc = Accesses()
+    S, chunks, W = p["segments"], p["chunks"], p["W"]
+    for seg in range(S):
+        st = states[seg]
+        sp = seg_span(p, seg, budgets)
+        acc.add("budgets", sp["reads"])
+        acc.add("states", [seg])
+        # k_msel_hist / k_msel_pick: the digit's bins, whatever the shift
+        nb = 1 << digit_width(int(st["shift"]))
+        acc.add("ghist", seg * K_BINS + np.arange(nb))
+        tid = np.arange(M_THREADS)[:, None]
+        b = nb - 1 - 8 * tid - np.arange(8)[None, :]
+        acc.add("ghist", seg * K_BINS + b[b >= 0])
+        for c in range(chunks):
+            g, begin, end = msel_chunk(p, c)
+            # k_msel_hist / k_msel_count / k_msel_emit loads: f < end
+            if end > begin:
+                acc.add("scores", seg * p["seg_len"] + np.array([begin, end - 1]))
+                if p["two_stage"]:
+                    acc.add("weight", seg * p["seg_len"] + np.array([begin, end - 1]))
+            acc.add("ccount", (seg * chunks + c) * 2 + np.array([0, 1]))
+        # k_msel_offsets: scans of arbitrary counts (uint32), group starts
+        cc = ccount[seg]
+        need = 0 if st["done"] else int(st["need"])
+        ne, na = _u32(cc[:, 1]), _u32(cc[:, 0])
+        eqoff = _u32(np.concatenate([[0], np.cumsum(ne)[:-1]]))
+        tie = np.where(eqoff >= need, 0, np.minimum(ne, _u32(need - eqoff)))
+        memoff = _u32(np.concatenate([[0], np.cumsum(_u32(na + tie))[:-1]]))
+        gidx = np.arange(chunks)[np.arange(chunks) % p["cpg"] == 0] // p["cpg"]
+        assert gidx.max(initial=0) < K_MAX_GROUPS
+        gstart = memoff[np.arange(chunks) % p["cpg"] == 0]
+        for g in range(p["groups"]):
+            end_rank = int(gstart[g + 1]) if g + 1 < p["groups"] else int(sp["k"])
+            e = end_rank + (g + 1) * W
+            o = e - W + np.arange(W, dtype=np.int64)
+            o = o[(o >= 0) & (o < sp["room"])]
+            acc.add("idx", sp["base"] + o)
+            if p["adaptive"] and budgets is None:
+                acc.add("head_offsets", [seg * (p["groups"] + 1) + g])
+        if budgets is not None:
+            H = p["H"]
+            l, h = divmod(seg, H)
+            acc.add("head_offsets", [l * (H + 1) + h])
+            if h + 1 == H:
+                acc.add("head_offsets", [l * (H + 1) + H])
+                acc.add("idx", l * p["stride"] + np.arange(sp["end"], p["stride"], dtype=np.int64))
+        elif p["adaptive"]:
+            acc.add("head_offsets", [seg * (p["groups"] + 1) + p["groups"]])
+        # k_msel_emit: rank = (arbitrary count) + scan of per-thread members
+        for c in range(chunks):
+            g, begin, end = msel_chunk(p, c)
+            per = rng.integers(0, 33, size=M_THREADS)
+            start = _u32(int(_u32(ccount[seg][c, 0])) + np.concatenate([[0], np.cumsum(per)[:-1]]))
+            r = (start[:, None] + np.arange(32)[None, :])[np.arange(32)[None, :] < per[:, None]]
+            o = r + g * W                                # int64: never negative
+            acc.add("idx", sp["base"] + o[o < sp["room"]])
+    return acc
+
+
+def select_sizes(p):
+    s = {"scores": p["segments"] * p["seg_len"], "budgets": p["L"] * p["H"],
+         "states": p["segments"], "ghist": p["segments"] * K_BINS,
+         "ccount": p["segments"] * p.get("chunks", 0) * 2}
+    if p["two_stage"]:
+        s["weight"] = s["scores"]
+    if p["budgets"] is not None:
+        s["idx"] = p["L"] * p["stride"]
+        s["head_offsets"] = p["L"] * (p["H"] + 1)
+    else:
+        s["idx"] = p["segments"] * p["budget"]
+        if p["adaptive"]:
+            s["head_offsets"] = p["segments"] * (p["groups"] + 1)
+    return s
+
+
+def select_plan(L, H, n, W, budget=0, adaptive=False, two_stage=False, budgets=None, stride=0):
+    """The plan kvsel_select / kvsel_select_budgets build (api.hip), for
+    arguments those calls accept."""
+    n_cand = n - W
+    groups = H if adaptive else 1
+    p = dict(L=L, H=H, n=n, W=W, n_cand=n_cand, groups=groups, adaptive=adaptive,
+             two_stage=two_stage, budgets=budgets, stride=stride,
+             budget=budget if budgets is None else 0,
+             k=(budget - groups * W) if budgets is None else 0,
+             segments=L if adaptive else L * H, seg_len=groups * n_cand)
+    p["cpg"] = -(-n_cand // K_CHUNK)
+    p["chunks"] = groups * p["cpg"]
+    return p

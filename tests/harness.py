@@ -56,7 +56,7 @@ def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, what: str = "scores"):
     return float((err / np.maximum(np.abs(ref), 1e-30)).max())
 
 
-def _band(key: np.ndarray, k: int, logit: bool = False, what: str = ""):
+def _band(key: np.ndarray, k: int, logit: bool = False, what: str = "", rtol: float = RTOL):
     """Oracle's k-th key t and the relative tolerance band around it (a
     boolean mask). Asserts the guard |t| > 100 * tau."""
     if k == 0 or k == key.size:
@@ -66,7 +66,7 @@ def _band(key: np.ndarray, k: int, logit: bool = False, what: str = ""):
     tau = LOGIT_ATOL_REL * np.abs(key).max() if logit else ATOL_REL * key.max()
     assert abs(t) > 100 * tau, (f"{what}: k-th key {t!r} is within 100x the absolute score floor "
                                 f"{tau!r}; the selection band would depend on it")
-    return t, np.abs(key - t) <= RTOL * abs(t)
+    return t, np.abs(key - t) <= rtol * abs(t)
 
 
 def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, what: str = "logit scores"):
@@ -79,13 +79,17 @@ def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, what: str = "logit sco
                            f"max err {np.abs(gpu - ref).max():.3g}")
 
 
-def assert_topk_within_band(gpu_pick, ref_key: np.ndarray, k: int, what: str, logit: bool = False):
-    """gpu_pick: candidate indices the GPU kept (any order)."""
+def assert_topk_within_band(gpu_pick, ref_key: np.ndarray, k: int, what: str, logit: bool = False,
+                            rtol: float = RTOL):
+    """gpu_pick: candidate indices the GPU kept (any order). rtol: the
+    relative error the GPU's keys may carry (RTOL for a score; a product of
+    two quantities each within RTOL, such as CriticalKV's integrated score,
+    carries (1 + RTOL)^2 - 1)."""
     gpu_pick = np.asarray(gpu_pick)
     assert gpu_pick.size == k, f"{what}: kept {gpu_pick.size}, expected {k}"
     assert np.unique(gpu_pick).size == k, f"{what}: duplicate indices"
     ref_pick = oracle.topk_indices(ref_key, k)
-    t, band = _band(ref_key, k, logit, what)
+    t, band = _band(ref_key, k, logit, what, rtol)
     g = np.zeros(ref_key.size, bool)
     g[gpu_pick] = True
     r = np.zeros(ref_key.size, bool)

@@ -6,7 +6,9 @@ exact data so the oracle can recompute them; the other layers are seeded
 device-side Gaussian draws of the same shape (layers are independent, so
 they do not affect the sampled results). Checks:
   - scores (raw and pooled) of sampled layers, all heads, against the fp64
-    oracle (relative 1e-3);
+    oracle (relative 1e-3); window scoring with sum aggregation also checks
+    every head of every layer for sum_j raw_j = W*G (each of the W*G query
+    rows' softmax sums to one);
   - value weights at sampled positions against the fp64 oracle;
   - selection: bit-exact against the oracle run in fp32 on the GPU's own
     scores (same precision decides), and within the tolerance band of the
@@ -17,6 +19,8 @@ they do not affect the sampled results). Checks:
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -24,7 +28,7 @@ import torch
 import eviction_importance_scoring_amd as kv
 import oracle
 import synth
-from harness import (assert_logits_close, assert_scores_close, assert_topk_within_band,
+from harness import (RTOL, assert_logits_close, assert_scores_close, assert_topk_within_band,
                      oracle_scores_layer, split_heads, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -69,6 +73,13 @@ def _score(wl, dev):
 
 
 def _check_scores(wl, s, r, host, layers):
+    if wl.q_mode == "window" and wl.agg == "sum":
+        # [KVzip, §3.2]: the softmax runs along keys, the sum over the W*G
+        # window rows, so a head's raw scores add up to W*G; fp32 sums of
+        # n terms stay within 1e-4 of it
+        tot = r.sum(dim=-1, dtype=torch.float64).cpu().numpy()
+        err = np.abs(tot - wl.W * wl.G).max()
+        assert err <= 1e-4 * wl.W * wl.G, f"{wl.name}: sum of raw scores off W*G by {err:.3g}"
     for l in layers:
         ref_raw, ref_pool = oracle_scores_layer(wl, host[("q", l)], host[("k", l)])
         assert_scores_close(r[l].cpu().numpy(), ref_raw, f"{wl.name} raw l{l}")
@@ -108,14 +119,16 @@ def _check_decode(wl, ko, vo, offs, l):
     print(f"[gpu] kvsel_decode_attention {wl.name}", flush=True)
     out = kv.kvsel_decode_attention(to_dev(qd), ko, vo, G=wl.G, scale=wl.scale, head_offsets=offs)
     torch.cuda.synchronize()
-    k_l = synth.bf16_to_f64(ko[l].cpu().view(torch.int16).numpy().view(np.uint16))
-    v_l = synth.bf16_to_f64(vo[l].cpu().view(torch.int16).numpy().view(np.uint16))
+    k_u = ko[l].cpu().view(torch.int16).numpy().view(np.uint16)
+    v_u = vo[l].cpu().view(torch.int16).numpy().view(np.uint16)
     if offs is None:
+        k_l, v_l = synth.bf16_to_f64(k_u), synth.bf16_to_f64(v_u)
         ref = oracle.decode_attention(synth.bf16_to_f64(qd[l]), k_l.reshape(wl.H_kv, -1, wl.d),
                                       v_l.reshape(wl.H_kv, -1, wl.d), wl.G, wl.scale)
     else:
         o = offs[l].cpu().numpy()
-        k_l, v_l = k_l[:o[-1]], v_l[:o[-1]]   # rows past the last head are not written
+        # rows past the last head are not written: cut before converting
+        k_l, v_l = synth.bf16_to_f64(k_u[:o[-1]]), synth.bf16_to_f64(v_u[:o[-1]])
         ref = oracle.decode_attention(synth.bf16_to_f64(qd[l]), k_l, v_l, wl.G, wl.scale, o)
     got = out[l].cpu().numpy()
     bad = np.abs(got - ref) > 1e-4 * np.abs(v_l).max() + 1e-4 * np.abs(ref)
@@ -318,8 +331,13 @@ def test_criticalkv_full(name):
         norm = oracle.value_weight
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
+    # every head: 96 scattered positions, a contiguous block of 4096 across
+    # several 512-key workgroup boundaries, and the ragged last block
+    block = np.arange(wl.n_cand // 2 - 2048, wl.n_cand // 2 + 2048)
+    tail = np.arange(max(0, (wl.n_cand - 1) // 512 * 512 - 64), wl.n_cand)
     for l in sampled:
-        pos = np.sort(rng.choice(wl.n_cand, 96, replace=False))
+        pos = np.unique(np.concatenate([rng.choice(wl.n_cand, 96, replace=False), block, tail]))
+        print(f"[host] oracle value weight l{l}: {pos.size} positions x {wl.H_kv} heads", flush=True)
         ref = norm(synth.bf16_to_f64(host[("v", l)]), synth.bf16_to_f64(host[("w_o", l)]), wl.G, pos)
         assert_scores_close(w[l].cpu().numpy()[:, pos], ref, f"value weight l{l}")
     idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=wl.W, budget=wl.budget, weight=w,
@@ -331,50 +349,136 @@ def test_criticalkv_full(name):
     k = wl.budget - (wl.H_kv * wl.W if wl.adaptive else wl.W)
     assert ((st == 1).sum(axis=-1) == int(np.floor(wl.alpha * k))).all()
     assert ((st == 2).sum(axis=-1) == k - int(np.floor(wl.alpha * k))).all()
+    if wl.value_norm == "l1":
+        # uniform budgets select per head: two heads; one budget per layer: all
+        heads = list(range(wl.H_kv)) if wl.adaptive else [0, wl.H_kv - 1]
+        _check_two_stage_band(wl, host, idx[0].cpu().numpy(), None if offs is None else offs[0].cpu().numpy(),
+                              stage[0].cpu().numpy(), heads)
     _check_compact(dev, host, idx, offs, 0, wl)
 
 
-def test_kvzip_chunked_full():
+def _ref_weights_head(v64, w64, wl, h, chunk=4096):
+    """fp64 value weight of every candidate of KV head h: the oracle on the
+    head's own values and its G column slices of W_O, in position chunks."""
+    d = wl.d
+    v_h = v64[h:h + 1]
+    w_h = w64[:, h * wl.G * d:(h + 1) * wl.G * d]
+    out = np.empty(wl.n_cand)
+    for c in range(0, wl.n_cand, chunk):
+        pos = np.arange(c, min(c + chunk, wl.n_cand))
+        out[pos] = oracle.value_weight(v_h, w_h, wl.G, pos)[0]
+    return out
+
+
+def _check_two_stage_band(wl, host, idx0, offs0, stage0, heads):
+    """Layer 0's two-stage selection against fp64 oracle keys ([CriticalKV,
+    §3.3 Algorithm 1, steps 4-9]). Stage 1: the GPU's stage-1 picks are the
+    top floor(alpha*k) fp64 pooled scores up to the score band. Stage 2: over
+    the candidates the GPU's own stage 1 left, its stage-2 picks are the top
+    k - k1 of the fp64 integrated score (pooled * score_norm + eps) * weight,
+    up to the band of a product of two quantities within RTOL each.
+    Uniform budgets: each listed head on its own; one budget per layer: the
+    heads' candidates flattened (all heads listed)."""
+    print(f"[host] oracle two-stage keys l0: heads {heads}", flush=True)
+    _, ref_pool = oracle_scores_layer(wl, host[("q", 0)], host[("k", 0)])
+    v64, w64 = synth.bf16_to_f64(host[("v", 0)]), synth.bf16_to_f64(host[("w_o", 0)])
+    ref_w = {h: _ref_weights_head(v64, w64, wl, h) for h in heads}
+    norm = 1.0 / (wl.W * wl.G)
+    rtol2 = (1.0 + RTOL) ** 2 - 1.0
+
+    def check(pool, weight, s1, s2, k, what):
+        k1 = int(np.floor(wl.alpha * k))
+        assert s1.size == k1 and s2.size == k - k1, what
+        assert_topk_within_band(s1, pool, k1, f"{what} stage 1")
+        rest = np.ones(pool.size, bool)
+        rest[s1] = False
+        cand = np.nonzero(rest)[0]
+        assert np.isin(s2, cand).all(), f"{what}: a stage-2 pick was also picked in stage 1"
+        key = (pool[cand] * norm + wl.eps) * weight[cand]
+        assert_topk_within_band(np.searchsorted(cand, s2), key, k - k1, f"{what} stage 2", rtol=rtol2)
+
+    def segment(h):
+        if offs0 is None:
+            return idx0[h], stage0[h]
+        return idx0[offs0[h]:offs0[h + 1]], stage0[offs0[h]:offs0[h + 1]]
+
+    if not wl.adaptive:
+        for h in heads:
+            row, st = segment(h)
+            check(ref_pool[h], ref_w[h], row[st == 1], row[st == 2], wl.budget - wl.W, f"h{h}")
+        return
+    assert heads == list(range(wl.H_kv))
+    s1, s2 = [], []
+    for h in heads:
+        row, st = segment(h)
+        s1.append(h * wl.n_cand + row[st == 1])
+        s2.append(h * wl.n_cand + row[st == 2])
+    check(ref_pool.reshape(-1), np.concatenate([ref_w[h] for h in heads]), np.concatenate(s1),
+          np.concatenate(s2), wl.budget - wl.H_kv * wl.W, "layer 0")
+
+
+@functools.lru_cache(maxsize=None)
+def _chunked_run():
+    """GPU chunked scores and selection of the KVzip chunked workload, kept
+    on the host for the per-head checks (layer 0 carries host data)."""
     wl = synth.WORKLOADS["kvzip_chunked_qwen7b_n32k"]
     dev, host = device_inputs(wl, {0}, ("q", "k", "kself"))
     print(f"[gpu] kvsel_score_chunked {wl.name}", flush=True)
     s, r = kv.kvsel_score_chunked(dev["q"], dev["k"], dev["kself"], G=wl.G, m=wl.chunk,
                                   n_prompt=wl.n_prompt, scale=wl.scale, pool=wl.pool,
                                   return_raw=True)
+    idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=0, budget=wl.budget, return_stage=True)
     torch.cuda.synchronize()
-    # oracle on one KV head of layer 0: 16 chunks of 2080 x 7 query rows
-    h = 1
+    _check_select_exact(wl, s, None, idx, offs, stage, [0, wl.L - 1])
+    return wl, host, r[0].cpu().numpy(), s[0].cpu().numpy(), idx[0].cpu().numpy()
+
+
+@pytest.mark.parametrize("h", [0, 1, 2, 3])
+def test_kvzip_chunked_full(h):
+    wl, host, r0, s0, idx0 = _chunked_run()
+    # oracle on KV head h of layer 0: 16 chunks of 2080 x 7 query rows
+    print(f"[host] oracle chunked scores l0 h{h}", flush=True)
     q = synth.bf16_to_f64(host[("q", 0)][:, h * wl.G:(h + 1) * wl.G])
     k = synth.bf16_to_f64(host[("k", 0)][h:h + 1])
     ks = synth.bf16_to_f64(host[("kself", 0)][:, h:h + 1])
     ref = oracle.chunked_scores(q, k, ks, wl.G, wl.scale, wl.chunk, wl.n_prompt)[0]
-    assert_scores_close(r[0, h].cpu().numpy()[None], ref[None], "chunked raw")
-    assert_scores_close(s[0, h].cpu().numpy()[None], ref[None], "chunked scores")
+    assert_scores_close(r0[h][None], ref[None], "chunked raw")
+    assert_scores_close(s0[h][None], ref[None], "chunked scores")
+    assert_topk_within_band(idx0[h], ref, wl.budget, "chunked select")
+
+
+@functools.lru_cache(maxsize=None)
+def _many_query_run(name):
+    """GPU scores and selection of a many-query KVzip workload, kept on the
+    host for the per-head checks (first and last layer carry host data)."""
+    wl = synth.WORKLOADS[name]
+    last = wl.L - 1
+    dev, host = device_inputs(wl, {0, last}, ("q", "k"))
+    s, r = _score(wl, dev)
     idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=0, budget=wl.budget, return_stage=True)
     torch.cuda.synchronize()
-    _check_select_exact(wl, s, None, idx, offs, stage, [0, wl.L - 1])
-    assert_topk_within_band(idx[0, h].cpu().numpy(), ref, wl.budget, "chunked select")
+    _check_select_exact(wl, s, None, idx, offs, stage, [0, last])
+    keep = (0, last)
+    return (wl, host, {l: r[l].cpu().numpy() for l in keep}, {l: s[l].cpu().numpy() for l in keep},
+            {l: idx[l].cpu().numpy() for l in keep})
 
 
 @pytest.mark.parametrize("name", ["kvzip_qwen7b_n32k", "kvzip_logit_qwen7b_n32k"])
-def test_kvzip_many_query_full(name):
-    wl = synth.WORKLOADS[name]
+@pytest.mark.parametrize("layer,h", [(0, 0), (0, 1), (0, 2), (0, 3), (-1, 1)])
+def test_kvzip_many_query_full(name, layer, h):
+    wl, host, r, s, idx = _many_query_run(name)
+    l = layer % wl.L
     logit = wl.agg == "logit"
-    dev, host = device_inputs(wl, {0}, ("q", "k"))
-    s, r = _score(wl, dev)
-    # oracle on one KV head of layer 0 (28672 query rows x 32768 keys)
-    h = 1
-    q = synth.bf16_to_f64(host[("q", 0)][h * wl.G:(h + 1) * wl.G])
-    k = synth.bf16_to_f64(host[("k", 0)][h:h + 1])
+    # oracle on KV head h of layer l (28672 query rows x 32768 keys)
+    print(f"[host] oracle {wl.agg} scores l{l} h{h}", flush=True)
+    q = synth.bf16_to_f64(host[("q", l)][h * wl.G:(h + 1) * wl.G])
+    k = synth.bf16_to_f64(host[("k", l)][h:h + 1])
     if logit:
         ref = oracle.external_logit_scores(q, k, wl.G, wl.scale)[0]
         close = assert_logits_close
     else:
         ref = oracle.external_raw_scores(q, k, wl.G, wl.scale, "max", q_chunk=512)[0]
         close = assert_scores_close
-    close(r[0, h].cpu().numpy()[None], ref[None], "kvzip raw")
-    close(s[0, h].cpu().numpy()[None], ref[None], "kvzip scores")
-    idx, offs, stage = kv.kvsel_select(s, n=wl.n, W=0, budget=wl.budget, return_stage=True)
-    torch.cuda.synchronize()
-    _check_select_exact(wl, s, None, idx, offs, stage, [0, wl.L - 1])
-    assert_topk_within_band(idx[0, h].cpu().numpy(), ref, wl.budget, "kvzip select", logit)
+    close(r[l][h][None], ref[None], "kvzip raw")
+    close(s[l][h][None], ref[None], "kvzip scores")
+    assert_topk_within_band(idx[l][h], ref, wl.budget, "kvzip select", logit)
