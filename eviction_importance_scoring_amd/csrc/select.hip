@@ -492,9 +492,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
 // long heads) would leave most CUs idle with one workgroup each, so they
 // run the same MSD radix select spread over chunks of kChunk candidates:
 //   k_msel_init    per segment: state (prefix, shift, need) for a stage
-//   k_msel_hist    per chunk: LDS histogram of the current digit among the
-//                  candidates that match the prefix, added to the
-//                  segment's global histogram
+//                  (and, for the first, a cleared global histogram)
+//   k_msel_hist    per chunk: histogram of the current digit among the
+//                  candidates that match the prefix (LDS, kMCopies copies),
+//                  added to the segment's global histogram
 //   k_msel_pick    per segment: the bin holding the need-th largest key
 //                  (bins read in descending order), the next state, and a
 //                  cleared histogram for the next digit
@@ -509,12 +510,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
 //   k_msel_count   per chunk: entries above the bucket, and in it
 //   k_msel_offsets per segment: exclusive scans over its chunks (members
 //                  and bucket entries), head offsets, window entries
-//   k_msel_emit    per chunk: members in index order at their ranks
+//   k_msel_emit    per chunk: members in index order at their ranks,
+//                  staged in LDS and written with coalesced stores
 // Chunks never straddle a head (group), so a group's first chunk offset is
-// the number of members before the group. Everything is deterministic.
+// the number of members before the group. Every sum runs in a fixed order
+// or over integers: the result is deterministic.
+//
+// Every thread issues all of its kPerThread loads before it uses one: a
+// chunk's workgroup then waits for memory once.
 constexpr int kMThreads = 256;
 constexpr int kChunk = 8192;                       // candidates per chunk
 constexpr int kPerThread = kChunk / kMThreads;     // 32
+constexpr int kMCopies = 4;                        // LDS histogram copies
 
 struct alignas(16) SegState {
   uint64_t prefix;      // current stage: key prefix above `shift`
@@ -539,15 +546,14 @@ struct MselArgs {
   float score_norm, eps, alpha;
 };
 
-// Key bits of candidate f for the stage being selected (stage 2 of the
-// two-stage selection: stage-1 members are +inf, the rest the integrated
-// score).
-__device__ __forceinline__ uint32_t msel_bits(const MselArgs& a, const SegState& st,
-                                              const float* sc, const float* wt, bool stage2,
-                                              uint32_t f) {
-  const uint32_t b = score_bits(sc[f]);
+// Key bits of candidate f for the stage being selected, from its score s
+// and weight w (stage 2 of the two-stage selection: stage-1 members are
+// +inf, the rest the integrated score).
+__device__ __forceinline__ uint32_t msel_bits(const MselArgs& a, const SegState& st, float s,
+                                              float w, bool stage2, uint32_t f) {
+  const uint32_t b = score_bits(s);
   if (!stage2) return b;
-  return (make_key(b, f) >> st.s1) >= st.p1 ? kInfBits : stage2_bits(sc[f], wt[f], a.score_norm, a.eps);
+  return (make_key(b, f) >> st.s1) >= st.p1 ? kInfBits : stage2_bits(s, w, a.score_norm, a.eps);
 }
 
 // chunk c of a segment: [begin, end) in flat candidate indices
@@ -559,11 +565,33 @@ __device__ __forceinline__ void msel_chunk(const MselArgs& a, uint32_t c, uint32
   end = min(begin + (uint32_t)kChunk, (g + 1) * a.n_cand);
 }
 
+// The thread's kPerThread candidates f = begin + e(i) (in range: f < end),
+// all loads issued before the first is used; out-of-range slots read 0.
+template <class Index>
+__device__ __forceinline__ void msel_load(const MselArgs& a, uint32_t seg, uint32_t begin,
+                                          uint32_t end, bool stage2, Index e,
+                                          float (&s)[kPerThread], float (&w)[kPerThread]) {
+  const float* sc = a.scores + (size_t)seg * a.seg_len;
+  const float* wt = a.weight ? a.weight + (size_t)seg * a.seg_len : nullptr;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const uint32_t f = begin + e(i);
+    s[i] = f < end ? sc[f] : 0.f;
+    w[i] = (stage2 && f < end) ? wt[f] : 0.f;
+  }
+}
+
 // stage 1 (or the single stage): prefix 0 / need k. stage 2: keep the
-// stage-1 result in (p1, s1) first. grid ceil(segments/256).
-__global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int segments, int stage2) {
-  const int seg = blockIdx.x * kMThreads + threadIdx.x;
-  if (seg >= segments) return;
+// stage-1 result in (p1, s1) first. grid segments, block 256; stage 1 also
+// clears the segment's global histogram (the workspace may hold anything;
+// each pick clears the bins it read).
+__global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2) {
+  const uint32_t seg = blockIdx.x;
+  if (!stage2) {
+    uint32_t* gh = a.ghist + (size_t)seg * kBins;
+    for (int b = threadIdx.x; b < kBins; b += kMThreads) gh[b] = 0u;
+  }
+  if (threadIdx.x != 0) return;
   SegState& st = a.states[seg];
   if (stage2) {
     st.p1 = st.prefix;
@@ -590,42 +618,43 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int segment
   }
 }
 
-// grid segments, block 256: a segment's global histogram to zero
-__global__ __launch_bounds__(kMThreads) void k_msel_clear(MselArgs a) {
-  uint32_t* gh = a.ghist + (size_t)blockIdx.x * kBins;
-  for (int b = threadIdx.x; b < kBins; b += kMThreads) gh[b] = 0u;
-}
-
 // grid chunks*segments (1-D), block 256
 __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kMCopies][kBins];
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
   const SegState st = a.states[seg];
   if (st.done) return;
   const int tid = threadIdx.x;
   const int shift = st.shift, wdt = digit_width(shift), nb = 1 << wdt;
-  for (int b = tid; b < nb; b += kMThreads) hist[b] = 0;
-  __syncthreads();
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
-  const float* sc = a.scores + (size_t)seg * a.seg_len;
-  const float* wt = a.weight ? a.weight + (size_t)seg * a.seg_len : nullptr;
-#pragma unroll 8
+  float s[kPerThread], w[kPerThread];
+  msel_load(a, seg, begin, end, stage2 != 0, [&](int i) { return (uint32_t)(i * kMThreads + tid); }, s, w);
+  for (int b = tid; b < kMCopies * kBins; b += kMThreads) (&hist[0][0])[b] = 0;
+  __syncthreads();
+  uint32_t* hc = hist[tid & (kMCopies - 1)];
+#pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const uint32_t f = begin + i * kMThreads + tid;
     if (f < end) {
-      const uint64_t key = make_key(msel_bits(a, st, sc, wt, stage2 != 0, f), f);
+      const uint64_t key = make_key(msel_bits(a, st, s[i], w[i], stage2 != 0, f), f);
       if ((key >> shift) == st.prefix)
-        atomicAdd(&hist[(uint32_t)(key >> (shift - wdt)) & (nb - 1)], 1u);
+        atomicAdd(&hc[(uint32_t)(key >> (shift - wdt)) & (nb - 1)], 1u);
     }
   }
   __syncthreads();
   uint32_t* gh = a.ghist + (size_t)seg * kBins;
-  for (int b = tid; b < nb; b += kMThreads)
-    if (hist[b]) atomicAdd(&gh[b], hist[b]);
+  for (int b = tid; b < nb; b += kMThreads) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int cp = 0; cp < kMCopies; ++cp) v += hist[cp][b];
+    if (v) atomicAdd(gh + b, v);
+  }
 }
 
-// grid segments, block 256: thread t owns bins nb-1-8t .. nb-8-8t (descending)
+// grid segments, block 256: thread t owns bins nb-1-8t .. nb-8-8t
+// (descending); exactly one thread holds the bin where the count of larger
+// keys first reaches need
 __global__ __launch_bounds__(kMThreads) void k_msel_pick(MselArgs a) {
   __shared__ uint32_t sbuf[kMThreads / 64];
   __shared__ uint32_t s_digit, s_above, s_count;
@@ -732,35 +761,6 @@ __device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* sbuf, ui
   return off;
 }
 
-// grid chunks*segments, block 256: per chunk, entries above the bucket and in it
-__global__ __launch_bounds__(kMThreads) void k_msel_count(MselArgs a, int stage2) {
-  __shared__ uint32_t sbuf[kMThreads / 64];
-  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
-  const SegState st = a.states[seg];
-  const int tid = threadIdx.x;
-  uint32_t g, begin, end;
-  msel_chunk(a, c, g, begin, end);
-  const float* sc = a.scores + (size_t)seg * a.seg_len;
-  const float* wt = a.weight ? a.weight + (size_t)seg * a.seg_len : nullptr;
-  uint32_t na = 0, ne = 0;
-#pragma unroll 8
-  for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t f = begin + i * kMThreads + tid;
-    if (f < end) {
-      bool above, eq;
-      msel_class(st, msel_bits(a, st, sc, wt, stage2 != 0, f), f, above, eq);
-      na += above;
-      ne += eq;
-    }
-  }
-  na = block_sum256(na, sbuf);
-  ne = block_sum256(ne, sbuf);
-  if (tid == 0) {
-    a.ccount[((size_t)seg * a.chunks + c) * 2] = na;
-    a.ccount[((size_t)seg * a.chunks + c) * 2 + 1] = ne;
-  }
-}
-
 // grid segments, block 256: per chunk, the bucket entries before it (eqoff)
 // and the members before it (memoff), both in place of the counts; head
 // offsets and window entries
@@ -821,6 +821,35 @@ __global__ __launch_bounds__(kMThreads) void k_msel_offsets(MselArgs a) {
     a.head_offsets[(size_t)seg * (a.groups + 1) + a.groups] = (int32_t)a.budget;
 }
 
+// grid chunks*segments, block 256: per chunk, entries above the bucket and in it
+__global__ __launch_bounds__(kMThreads) void k_msel_count(MselArgs a, int stage2) {
+  __shared__ uint32_t sbuf[kMThreads / 64];
+  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
+  const SegState st = a.states[seg];
+  const int tid = threadIdx.x;
+  uint32_t g, begin, end;
+  msel_chunk(a, c, g, begin, end);
+  float s[kPerThread], w[kPerThread];
+  msel_load(a, seg, begin, end, stage2 != 0, [&](int i) { return (uint32_t)(i * kMThreads + tid); }, s, w);
+  uint32_t na = 0, ne = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const uint32_t f = begin + i * kMThreads + tid;
+    if (f < end) {
+      bool above, eq;
+      msel_class(st, msel_bits(a, st, s[i], w[i], stage2 != 0, f), f, above, eq);
+      na += above;
+      ne += eq;
+    }
+  }
+  na = block_sum256(na, sbuf);
+  ne = block_sum256(ne, sbuf);
+  if (tid == 0) {
+    a.ccount[((size_t)seg * a.chunks + c) * 2] = na;
+    a.ccount[((size_t)seg * a.chunks + c) * 2 + 1] = ne;
+  }
+}
+
 // LDS slot of chunk element e: one pad word per 32, so that a thread
 // reading its own 32 consecutive elements and a wave writing 64
 // consecutive ones both hit distinct banks
@@ -830,7 +859,8 @@ __device__ __forceinline__ uint32_t emit_slot(uint32_t e) { return e + (e >> 5);
 // candidates of the chunk (their key bits staged through LDS from
 // coalesced loads); block scans of the per-thread bucket and member counts
 // give each bucket entry its tie rank and each member its rank, in index
-// order
+// order. The chunk's members take consecutive output slots: they are
+// staged by rank in LDS and stored with coalesced writes.
 __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2) {
   __shared__ uint32_t bits[kChunk + kChunk / 32];
   __shared__ uint32_t sbuf[kMThreads / 64];
@@ -840,31 +870,36 @@ __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2)
   const int tid = threadIdx.x;
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
-  const float* sc = a.scores + (size_t)seg * a.seg_len;
-  const float* wt = a.weight ? a.weight + (size_t)seg * a.seg_len : nullptr;
-#pragma unroll 8
-  for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t e = i * kMThreads + tid;
-    const uint32_t f = begin + e;
-    bits[emit_slot(e)] = f < end ? msel_bits(a, st, sc, wt, stage2 != 0, f) : 0u;
+  {
+    float s[kPerThread], w[kPerThread];
+    msel_load(a, seg, begin, end, stage2 != 0, [&](int i) { return (uint32_t)(i * kMThreads + tid); }, s, w);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const uint32_t e = i * kMThreads + tid;
+      const uint32_t f = begin + e;
+      bits[emit_slot(e)] = f < end ? msel_bits(a, st, s[i], w[i], stage2 != 0, f) : 0u;
+    }
   }
   __syncthreads();
-  uint32_t amask = 0, emask = 0, ne = 0;
+  uint32_t amask = 0, emask = 0, ne = 0, imask = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const uint32_t e = tid * kPerThread + j;
     const uint32_t f = begin + e;
     if (f < end) {
+      const uint32_t b = bits[emit_slot(e)];
       bool above, eq;
-      msel_class(st, bits[emit_slot(e)], f, above, eq);
+      msel_class(st, b, f, above, eq);
       amask |= (uint32_t)above << j;
       emask |= (uint32_t)eq << j;
+      imask |= (uint32_t)(b == kInfBits) << j;
       ne += eq;
     }
   }
   const uint32_t* cc = a.ccount + ((size_t)seg * a.chunks + c) * 2;
+  const uint32_t rank0 = cc[0], eq0 = cc[1];
   uint32_t tot;
-  uint32_t tierank = cc[1] + block_scan256(ne, sbuf, tot);   // bucket entries before this thread's
+  uint32_t tierank = eq0 + block_scan256(ne, sbuf, tot);   // bucket entries before this thread's
   uint32_t mmask = amask;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
@@ -873,19 +908,30 @@ __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2)
       ++tierank;
     }
   }
-  uint32_t rank = cc[0] + block_scan256((uint32_t)__popc(mmask), sbuf, tot);
+  uint32_t count;
+  uint32_t r = block_scan256((uint32_t)__popc(mmask), sbuf, count);   // members before this thread's
+  // staged[r] = position in its head of the chunk's member of rank r, bit
+  // 31 set for a stage-2 member of the two-stage selection (the key bits
+  // are no longer needed: every thread has classified its entries before
+  // the scans' barriers)
+  uint32_t* staged = bits;
+  const uint32_t pos0 = begin - g * a.n_cand + tid * kPerThread;
+  for (uint32_t m = mmask; m != 0; m &= m - 1, ++r) {
+    const uint32_t j = (uint32_t)__builtin_ctz(m);
+    const bool second = stage2 && !((imask >> j) & 1u);
+    staged[r] = (pos0 + j) | (second ? 0x80000000u : 0u);
+  }
+  __syncthreads();
   const SegSpan sp = seg_span(a, (size_t)seg);
   int32_t* out = a.idx + sp.base;
   uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
-  const uint32_t pos0 = begin - g * a.n_cand;
-  for (int j = 0; j < kPerThread; ++j) {
-    if (mmask & (1u << j)) {
-      const int64_t o = (int64_t)rank + (int64_t)g * a.W;
-      if (o < sp.room) {   // k members fit the budget; the room may be cut at the row's end
-        out[o] = (int32_t)(pos0 + tid * kPerThread + j);
-        if (st_out) st_out[o] = (!stage2 || bits[emit_slot(tid * kPerThread + j)] == kInfBits) ? 1 : 2;
-      }
-      ++rank;
+  const int64_t o0 = (int64_t)rank0 + (int64_t)g * a.W;
+  for (uint32_t i = tid; i < count; i += kMThreads) {
+    const int64_t o = o0 + i;
+    if (o < sp.room) {   // k members fit the budget; the room may be cut at the row's end
+      const uint32_t e = staged[i];
+      out[o] = (int32_t)(e & 0x7FFFFFFFu);
+      if (st_out) st_out[o] = (e >> 31) ? 2 : 1;
     }
   }
 }
@@ -944,16 +990,15 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   if (p.budgets) a.head_offsets = head_offsets;
   const long long blocks = (long long)m.chunks * p.segments;
   if (blocks > 0x7fffffffLL || p.segments > 0x7fffffff) return hipErrorInvalidConfiguration;
-  // the global histograms start cleared (a kernel, not a memset, so the
-  // call can be captured in a graph); each pick clears what it read
-  const dim3 gs((p.segments + kMThreads - 1) / kMThreads), gc((unsigned)blocks), gp(p.segments);
-  hipLaunchKernelGGL(k_msel_clear, gp, dim3(kMThreads), 0, st, a);
+  // the global histograms start cleared (by a kernel, not a memset, so
+  // the call can be captured in a graph); each pick clears what it read
+  const dim3 gc((unsigned)blocks), gp(p.segments);
   const int stages = p.two_stage ? 2 : 1;
   for (int stg = 0; stg < stages; ++stg) {
     const int stage2 = stg == 1 ? 1 : 0;
     // the final stage stops after the score bits (ties split in emission)
     const int rounds = stg + 1 < stages ? 6 : 3;
-    hipLaunchKernelGGL(k_msel_init, gs, dim3(kMThreads), 0, st, a, p.segments, stage2);
+    hipLaunchKernelGGL(k_msel_init, gp, dim3(kMThreads), 0, st, a, stage2);
     for (int r = 0; r < rounds; ++r) {
       hipLaunchKernelGGL(k_msel_hist, gc, dim3(kMThreads), 0, st, a, stage2);
       hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);

@@ -262,8 +262,8 @@ def digit_width(shift):
 
 
 def msel_accesses(p, states, ccount, rng, budgets=None):
-    """k_msel_hist, k_msel_pick, k_msel_count, k_msel_offsets, k_msel_emit
-    (select.hip) with arbitrary segment states (shift, need, done) and
+    """k_msel_init, k_msel_hist, k_msel_pick, k_msel_count, k_msel_offsets
+    and k_msel_emit (select.hip) with arbitrary segment states (shift, need, done) and
     arbitrary per-chunk counts. Where a membership test decides a rank, each
     thread's member count is drawn at random within its 32 candidates."""
     acc = Accesses()
@@ -273,6 +273,7 @@ def msel_accesses(p, states, ccount, rng, budgets=None):
         sp = seg_span(p, seg, budgets)
         acc.add("budgets", sp["reads"])
         acc.add("states", [seg])
+        acc.add("ghist", seg * K_BINS + np.arange(K_BINS))       # k_msel_init clears
         # k_msel_hist / k_msel_pick: the digit's bins, whatever the shift
         nb = 1 << digit_width(int(st["shift"]))
         acc.add("ghist", seg * K_BINS + np.arange(nb))
@@ -314,13 +315,14 @@ def msel_accesses(p, states, ccount, rng, budgets=None):
                 acc.add("idx", l * p["stride"] + np.arange(sp["end"], p["stride"], dtype=np.int64))
         elif p["adaptive"]:
             acc.add("head_offsets", [seg * (p["groups"] + 1) + p["groups"]])
-        # k_msel_emit: rank = (arbitrary count) + scan of per-thread members
+        # k_msel_emit: the chunk's members are staged by rank in LDS (at
+        # most kChunk of them) and take slots rank0 + g*W + i, i < count,
+        # with rank0 the chunk's (arbitrary) member offset
         for c in range(chunks):
             g, begin, end = msel_chunk(p, c)
-            per = rng.integers(0, 33, size=M_THREADS)
-            start = _u32(int(_u32(ccount[seg][c, 0])) + np.concatenate([[0], np.cumsum(per)[:-1]]))
-            r = (start[:, None] + np.arange(32)[None, :])[np.arange(32)[None, :] < per[:, None]]
-            o = r + g * W                                # int64: never negative
+            count = int(rng.integers(0, max(0, end - begin) + 1))
+            assert count <= K_CHUNK
+            o = int(_u32(ccount[seg][c, 0])) + g * W + np.arange(count, dtype=np.int64)
             acc.add("idx", sp["base"] + o[o < sp["room"]])
     return acc
 
