@@ -619,8 +619,9 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
                        Rpad, stat);
     hipLaunchKernelGGL((k_gen_colagg<false, true, true>), dim3((unsigned)g2), dim3(512), 0, st, qb,
                        kb, p.H, p.R, p.W, km, p.scale, key_blocks, stat, rawbuf);
-    (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
   }
   if (p.causal)
     hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
@@ -630,6 +631,8 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
     hipLaunchKernelGGL(k_gen_stats<false>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
                        p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
                        o.sp_stride, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   int n_in = 0;
   if (chunked) {
     // the input's own keys, causally: the window rule with n = W = n_in
@@ -640,10 +643,14 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
     hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb,
                        static_cast<const __bf16*>(k_self), p.H, p.R, n_in, kms, alpha,
                        o.row_blocks, 1, kps_self, 1, o.sp_stride, part);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_combine_neg, dim3((Rpad + 255) / 256, p.H, o.Lv), dim3(256), 0, st, part,
                      p.H, p.R, Rpad, o.sp_stride, 1.0f / alpha, chunked ? T : 0, n_in, p.n_prompt,
                      km, stat);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const dim3 grid2((unsigned)g2);
   if (p.causal) {
     if (p.max_agg)
@@ -660,8 +667,9 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
       hipLaunchKernelGGL((k_gen_colagg<false, false>), grid2, dim3(512), 0, st, qb, kb, p.H,
                          p.R, p.W, km, alpha, key_blocks, stat, rawbuf);
   }
-  (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
 }
 
 }  // namespace kvsel

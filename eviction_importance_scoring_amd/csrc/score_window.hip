@@ -545,17 +545,21 @@ hipError_t window_launch(const ScorePlan& p, const WindowLayout& o, const void* 
   const __bf16* kb = static_cast<const __bf16*>(k);
   const float alpha = p.scale * kLog2e;
   dim3 grid(o.blocks, p.H, p.L);
+  // each launch's status is checked before the next one depends on it
   hipLaunchKernelGGL(k_win_stats, grid, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n, alpha,
                      o.blocks, o.kpb, part);
-  (void)combine_launch(part, p.L, p.H, p.R, o.blocks, stat, st);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = combine_launch(part, p.L, p.H, p.R, o.blocks, stat, st);
+  if (e != hipSuccess) return e;
   if (p.max_agg)
     hipLaunchKernelGGL(k_win_colsum<true>, grid, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n,
                        alpha, stat, o.kpb, rawbuf);
   else
     hipLaunchKernelGGL(k_win_colsum<false>, grid, dim3(256), 0, st, qb, kb, p.H, p.R, p.W, p.n,
                        alpha, stat, o.kpb, rawbuf);
-  (void)pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
 }
 
 }  // namespace kvsel

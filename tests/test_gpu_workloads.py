@@ -29,7 +29,7 @@ import eviction_importance_scoring_amd as kv
 import oracle
 import synth
 from harness import (RTOL, assert_logits_close, assert_scores_close, assert_topk_within_band,
-                     oracle_scores_layer, split_heads, to_dev)
+                     logit_error_bound, oracle_scores_layer, split_heads, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -475,10 +475,11 @@ def test_kvzip_many_query_full(name, layer, h):
     k = synth.bf16_to_f64(host[("k", l)][h:h + 1])
     if logit:
         ref = oracle.external_logit_scores(q, k, wl.G, wl.scale)[0]
-        close = assert_logits_close
+        bound = logit_error_bound(q, k, wl.G, wl.scale)     # pool = 1: the same for both
+        assert_logits_close(r[l][h][None], ref[None], bound, "kvzip raw")
+        assert_logits_close(s[l][h][None], ref[None], bound, "kvzip scores")
     else:
         ref = oracle.external_raw_scores(q, k, wl.G, wl.scale, "max", q_chunk=512)[0]
-        close = assert_scores_close
-    close(r[l][h][None], ref[None], "kvzip raw")
-    close(s[l][h][None], ref[None], "kvzip scores")
+        assert_scores_close(r[l][h][None], ref[None], "kvzip raw")
+        assert_scores_close(s[l][h][None], ref[None], "kvzip scores")
     assert_topk_within_band(idx[l][h], ref, wl.budget, "kvzip select", logit)
