@@ -13,11 +13,10 @@
 // no exponential: per key j, scale * max_r <q_r, k_j>.
 // Chunked scoring ([KVzip] §3.4): a "layer" of the grid is a (layer,
 // chunk) pair whose keys are the chunk's m cached keys (a KeyMap says where
-// they sit in the cache). Pass 1 runs twice into two statistics slots per
-// row: over the chunk's cached keys, and causally over the input's own
-// keys (the window rule with n = W = n_in); the combine merges both and
-// gives the rows past a short last chunk's input -inf; pass 2 maxes over
-// the chunk's cached keys.
+// they sit in the cache). Pass 1 folds, per row, the chunk's cached keys
+// and then, in the same workgroup, the input's own keys causally (row r
+// sees own keys 0 .. r % n_in); the combine gives the rows past a short
+// last chunk's input -inf; pass 2 maxes over the chunk's cached keys.
 // Both passes are dense Q K^T contractions on MFMA (32x32x16 bf16, fp32
 // accumulation) built for operand reuse:
 //   pass 1: a workgroup of 8 waves owns 512 rows (a wave: 64 rows, two MFMA
@@ -75,12 +74,17 @@ __device__ __forceinline__ void key_span(const KeyMap& km, int lv, int H, int h,
 constexpr float kHeadroomPow2 = 1.8446744e19f;   // 2^64
 
 // part[lh][sp_off + sp] (of sp_stride slots per row block) for split sp.
-template <bool CAUSAL>
+// SELF (KVzip's chunked scoring): after the grid layer's keys the same
+// workgroup runs on the input's own keys, ks[lv][h][n_self][d], causally
+// (row r sees own keys 0 .. r % n_self), so both key sources fold into one
+// (max, sum) per row and each query block is loaded once.
+template <bool CAUSAL, bool SELF = false>
 __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
                                                    const __bf16* __restrict__ k, int H, int R,
                                                    int W, KeyMap km, float alpha, int row_blocks,
                                                    int splits, int kps, int sp_off, int sp_stride,
-                                                   float2* __restrict__ part) {
+                                                   float2* __restrict__ part,
+                                                   const __bf16* __restrict__ ks, int n_self) {
   __shared__ __align__(16) unsigned char ring[gSlots][gTile * kRowBytes];
   int id = xcd_remap(blockIdx.x, gridDim.x);
   const int rb = id % row_blocks;
@@ -105,30 +109,54 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     vis_end = n - W + top + 1;
   }
   const int j0 = sp * kps, j1 = min(min(n, vis_end), j0 + kps);
-  if (j1 <= j0) {   // a split past every visible key: neutral statistics
+  // SELF: own-key tiles up to the block's last visible own key; self_open:
+  // the own keys every row of the block sees
+  int ntiles2 = 0, self_open = -1;
+  const __bf16* ksh = ks;
+  if constexpr (SELF) {
+    const int r0 = rb * gBlock, r1 = min(R, r0 + gBlock);
+    const bool spans = (r1 - 1) / n_self != r0 / n_self;
+    const int top = spans ? n_self - 1 : (r1 - 1) % n_self;
+    self_open = spans ? 0 : r0 % n_self;
+    ntiles2 = (top + gTile) / gTile;
+    ksh = ks + lh * (size_t)n_self * kHeadDim;
+  }
+  if (j1 <= j0 && (!SELF || ntiles2 == 0)) {   // a split past every visible key: neutral statistics
     const int row = rb * gBlock + threadIdx.x;
     if (row < R) part[(lh * sp_stride + sp_off + sp) * (size_t)R + row] = make_float2(gNegBig, 0.f);
     return;         // every wave returns here: no barrier is left waiting
   }
-  const int ntiles = (j1 - j0 + gTile - 1) / gTile;
+  const int ntiles1 = SELF ? (j1 > j0 ? (j1 - j0 + gTile - 1) / gTile : 0) : (j1 - j0 + gTile - 1) / gTile;
+  const int ntiles = SELF ? ntiles1 + ntiles2 : ntiles1;
 
   const int row0 = rb * gBlock + wave * 64;
   const bool active = row0 < R;
   bf16x8 qb[2][8];
-  int last[2];
+  int last[2], last_self[2] = {-1, -1};
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int row = row0 + nt * 32 + col;
     if (row < R) load_half_row(q + (lh * R + row) * (size_t)kHeadDim, hf, qb[nt]);
     else zero_ops(qb[nt]);
     last[nt] = row < R ? (CAUSAL ? n - W + row % W : n - 1) : -1;   // last visible key
+    if constexpr (SELF) last_self[nt] = row < R ? row % n_self : -1;   // last visible own key
   }
   GenLoader ld;
   ld.init(kHeadDim);
+  // tile t of the workgroup: the layer's keys, then (SELF) the own keys
+  auto issue_tile = [&](int t, unsigned char* slot) {
+    if constexpr (SELF) {
+      if (t >= ntiles1) {
+        ld.issue(ksh, (t - ntiles1) * gTile, n_self, kHeadDim, slot);
+        return;
+      }
+    }
+    ld.issue(kh, j0 + t * gTile, n, kHeadDim, slot);
+  };
   asm volatile("" ::: "memory");
   // the first gSlots-1 tiles (repeating the last one if there are fewer)
 #pragma unroll
-  for (int t = 0; t < gSlots - 1; ++t) ld.issue(kh, j0 + min(t, ntiles - 1) * gTile, n, kHeadDim, ring[t]);
+  for (int t = 0; t < gSlots - 1; ++t) issue_tile(min(t, ntiles - 1), ring[t]);
   // Q is in registers once at most the prologue's loads are in flight; an
   // explicit wait here keeps the compiler from waiting inside the loop
   gen_wait<(gSlots - 1) * gLoads>();
@@ -138,6 +166,24 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
 
   // hide the keys a row does not see (tiles at the causal edge or the split end)
   auto mask = [&](f32x16 (&acc)[2][2], int t) {
+    if constexpr (SELF) {   // the layer's keys, then the own keys (causal)
+      const bool own = t >= ntiles1;
+      const int kt = own ? (t - ntiles1) * gTile : j0 + t * gTile;
+      const int end = own ? n_self : j1;
+      if (kt + gTile - 1 <= (own ? self_open : open_end) && kt + gTile <= end) return;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int lim = own ? last_self[nt] : last[nt];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt + mt * 32 + acc_row(i, lane);
+            if (!(key <= lim && key < end)) acc[mt][nt][i] = neg_inf();
+          }
+      }
+      return;
+    }
     const int kt = j0 + t * gTile;
     if (kt + gTile - 1 <= open_end && kt + gTile <= j1) return;
 #pragma unroll
@@ -190,8 +236,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
   auto begin_tile = [&](int t) -> const unsigned char* {
     gen_wait_tile<gLoads>(t, ntiles);
     gen_barrier();
-    if (t + gSlots - 1 < ntiles)
-      ld.issue(kh, j0 + (t + gSlots - 1) * gTile, n, kHeadDim, ring[(t + gSlots - 1) % gSlots]);
+    if (t + gSlots - 1 < ntiles) issue_tile(t + gSlots - 1, ring[(t + gSlots - 1) % gSlots]);
     // the slot's offset in an opaque vector register: keeps LDS reads from
     // moving across tiles, and each operand address is one add
     int soff = (t % gSlots) * gRowsBytes;
@@ -564,11 +609,11 @@ void twopass_plan(const ScorePlan& p, TwoPassLayout* o) {
   const int row_blocks = (p.R + gBlock - 1) / gBlock;
   int splits, kps, stride;
   if (p.chunk_m > 0) {
-    // chunked: (layer, chunk) pairs fill the GPU; one split over the chunk's
-    // cached keys and one over the input's own keys
+    // chunked: (layer, chunk) pairs fill the GPU; one workgroup per row
+    // block folds the chunk's cached keys and then the input's own keys
     splits = 1;
     kps = (p.chunk_m + gTile - 1) / gTile * gTile;
-    stride = 2;
+    stride = 1;
   } else {
     const long long base = (long long)row_blocks * p.H * p.L;
     // split the keys only when the row blocks alone cannot fill the GPU
@@ -623,29 +668,24 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
     if (e != hipSuccess) return e;
     return pool_launch(rawbuf, p.L, p.H, p.n, p.n_cand, p.pool / 2, scores, st);
   }
-  if (p.causal)
+  // chunked: the input's own keys (rows are [G][n_in], row r sees own keys
+  // 0 .. r % n_in) follow the chunk's cached keys in the same workgroups
+  const int n_in = chunked ? p.n_prompt + p.chunk_m : 0;
+  const __bf16* ksb = static_cast<const __bf16*>(k_self);
+  if (chunked)
+    hipLaunchKernelGGL((k_gen_stats<false, true>), dim3((unsigned)g1), dim3(512), 0, st, qb, kb,
+                       p.H, p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
+                       o.sp_stride, part, ksb, n_in);
+  else if (p.causal)
     hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
                        p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
-                       o.sp_stride, part);
+                       o.sp_stride, part, ksb, 1);
   else
     hipLaunchKernelGGL(k_gen_stats<false>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
                        p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
-                       o.sp_stride, part);
+                       o.sp_stride, part, ksb, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int n_in = 0;
-  if (chunked) {
-    // the input's own keys, causally: the window rule with n = W = n_in
-    // (rows are [G][n_in], row r sees own keys 0 .. r % n_in)
-    n_in = p.n_prompt + p.chunk_m;
-    const KeyMap kms{1, n_in, n_in};
-    const int kps_self = (n_in + gTile - 1) / gTile * gTile;
-    hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb,
-                       static_cast<const __bf16*>(k_self), p.H, p.R, n_in, kms, alpha,
-                       o.row_blocks, 1, kps_self, 1, o.sp_stride, part);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   hipLaunchKernelGGL(k_combine_neg, dim3((Rpad + 255) / 256, p.H, o.Lv), dim3(256), 0, st, part,
                      p.H, p.R, Rpad, o.sp_stride, 1.0f / alpha, chunked ? T : 0, n_in, p.n_prompt,
                      km, stat);
