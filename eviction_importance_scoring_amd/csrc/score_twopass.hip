@@ -19,11 +19,13 @@
 // last chunk's input -inf; pass 2 maxes over the chunk's cached keys.
 // Both passes are dense Q K^T contractions on MFMA (32x32x16 bf16, fp32
 // accumulation) built for operand reuse:
-//   pass 1: a workgroup of 8 waves owns 512 rows (a wave: 64 rows, two MFMA
+//   pass 1: a workgroup of 4 waves owns 256 rows (a wave: 64 rows, two MFMA
 //     N tiles, Q operands in registers) and streams K in 64-key tiles
-//     through an LDS ring shared by the 8 waves. Rows sit on lanes, so the
-//     online max / sum stays in-lane.
-//   pass 2: a workgroup owns 512 keys (a wave: 64 keys in registers) and
+//     through an LDS ring shared by the 4 waves; two workgroups share a CU,
+//     so one computes while the other waits at its tile barrier. Rows sit
+//     on lanes, so the online max / sum stays in-lane.
+//   pass 2: a workgroup owns 256 keys (a wave: 64 keys in registers; two
+//     workgroups share a CU like pass 1's) and
 //     streams Q in 64-row tiles through the ring, each with its 64 c_r.
 //     The accumulators start at -c_r / (log2(e) * scale), so the MFMA
 //     itself subtracts the normaliser and max aggregation costs one max
@@ -78,8 +80,14 @@ constexpr float kHeadroomPow2 = 1.8446744e19f;   // 2^64
 // workgroup runs on the input's own keys, ks[lv][h][n_self][d], causally
 // (row r sees own keys 0 .. r % n_self), so both key sources fold into one
 // (max, sum) per row and each query block is loaded once.
+// Two 4-wave workgroups per CU (256 VGPRs a wave) rather than one of 8
+// waves: the same operand reuse per wave, but each workgroup's tile
+// barriers no longer stall the other's waves.
+constexpr int gStatsWaves = 4;                       // pass-1 waves per workgroup
+constexpr int gStatsBlock = gStatsWaves * 64;         // pass-1 rows per workgroup
+using StatsLoader = RingLoader<gStatsWaves>;
 template <bool CAUSAL, bool SELF = false>
-__global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(gStatsBlock, 2) void k_gen_stats(const __bf16* __restrict__ q,
                                                    const __bf16* __restrict__ k, int H, int R,
                                                    int W, KeyMap km, float alpha, int row_blocks,
                                                    int splits, int kps, int sp_off, int sp_stride,
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
   // own keys have n = W, where this halves the work)
   int vis_end = n;
   if (CAUSAL) {
-    const int r0 = rb * gBlock, r1 = min(R, r0 + gBlock);
+    const int r0 = rb * gStatsBlock, r1 = min(R, r0 + gStatsBlock);
     const int top = (r1 - 1) / W != r0 / W ? W - 1 : (r1 - 1) % W;
     vis_end = n - W + top + 1;
   }
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
   int ntiles2 = 0, self_open = -1;
   const __bf16* ksh = ks;
   if constexpr (SELF) {
-    const int r0 = rb * gBlock, r1 = min(R, r0 + gBlock);
+    const int r0 = rb * gStatsBlock, r1 = min(R, r0 + gStatsBlock);
     const bool spans = (r1 - 1) / n_self != r0 / n_self;
     const int top = spans ? n_self - 1 : (r1 - 1) % n_self;
     self_open = spans ? 0 : r0 % n_self;
@@ -122,14 +130,14 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     ksh = ks + lh * (size_t)n_self * kHeadDim;
   }
   if (j1 <= j0 && (!SELF || ntiles2 == 0)) {   // a split past every visible key: neutral statistics
-    const int row = rb * gBlock + threadIdx.x;
+    const int row = rb * gStatsBlock + threadIdx.x;
     if (row < R) part[(lh * sp_stride + sp_off + sp) * (size_t)R + row] = make_float2(gNegBig, 0.f);
     return;         // every wave returns here: no barrier is left waiting
   }
   const int ntiles1 = SELF ? (j1 > j0 ? (j1 - j0 + gTile - 1) / gTile : 0) : (j1 - j0 + gTile - 1) / gTile;
   const int ntiles = SELF ? ntiles1 + ntiles2 : ntiles1;
 
-  const int row0 = rb * gBlock + wave * 64;
+  const int row0 = rb * gStatsBlock + wave * 64;
   const bool active = row0 < R;
   bf16x8 qb[2][8];
   int last[2], last_self[2] = {-1, -1};
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     last[nt] = row < R ? (CAUSAL ? n - W + row % W : n - 1) : -1;   // last visible key
     if constexpr (SELF) last_self[nt] = row < R ? row % n_self : -1;   // last visible own key
   }
-  GenLoader ld;
+  StatsLoader ld;
   ld.init(kHeadDim);
   // tile t of the workgroup: the layer's keys, then (SELF) the own keys
   auto issue_tile = [&](int t, unsigned char* slot) {
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
   for (int t = 0; t < gSlots - 1; ++t) issue_tile(min(t, ntiles - 1), ring[t]);
   // Q is in registers once at most the prologue's loads are in flight; an
   // explicit wait here keeps the compiler from waiting inside the loop
-  gen_wait<(gSlots - 1) * gLoads>();
+  gen_wait<(gSlots - 1) * StatsLoader::kLoads>();
   // keys every row sees
   const int open_end = CAUSAL ? n - W : n - 1;
   float m[2] = {gNegBig, gNegBig}, s[2] = {0.f, 0.f};
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(512) void k_gen_stats(const __bf16* __restrict__ q,
     }
   };
   auto begin_tile = [&](int t) -> const unsigned char* {
-    gen_wait_tile<gLoads>(t, ntiles);
+    gen_wait_tile<StatsLoader::kLoads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles) issue_tile(t + gSlots - 1, ring[(t + gSlots - 1) % gSlots]);
     // the slot's offset in an opaque vector register: keeps LDS reads from
@@ -378,8 +386,12 @@ __global__ __launch_bounds__(256) void k_logit_stat(int R, int Rpad, float* __re
 // 1-D grid of key_blocks * H * L workgroups, block 512. raw[lh][key].
 // Pipelined like pass 1: the MFMAs of row tile t run beside the aggregation
 // of tile t-1, so the matrix pipe does not wait for the per-tile max / sum.
+// Like pass 1: two 4-wave workgroups per CU.
+constexpr int gColWaves = 4;                          // pass-2 waves per workgroup
+constexpr int gColBlock = gColWaves * 64;             // pass-2 keys per workgroup
+using ColLoader = RingLoader<gColWaves>;
 template <bool CAUSAL, bool MAXAGG, bool LOGIT = false>
-__global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(gColBlock, 2) void k_gen_colagg(const __bf16* __restrict__ q,
                                                     const __bf16* __restrict__ k, int H, int R,
                                                     int W, KeyMap km, float alpha, int key_blocks,
                                                     const float* __restrict__ stat,
@@ -402,7 +414,7 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
   key_span(km, l, H, h, krow0, n);
 
   // this wave's 64 keys: MFMA B operands for the whole kernel
-  const int key0 = kb * gBlock + wave * 64;
+  const int key0 = kb * gColBlock + wave * 64;
   bf16x8 kop[2][8];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -411,7 +423,7 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
     else zero_ops(kop[nt]);
   }
   // a row tile: the Q rows (all waves) and their -c_r / alpha (wave 0)
-  GenLoader ld;
+  ColLoader ld;
   ld.init(kHeadDim);
   auto issue = [&](int t, int slot) {
     ld.issue(qh, t * gTile, R, kHeadDim, ring[slot]);
@@ -423,16 +435,16 @@ __global__ __launch_bounds__(512) void k_gen_colagg(const __bf16* __restrict__ q
 #pragma unroll
   for (int t = 0; t < gSlots - 1; ++t) issue(min(t, ntiles - 1), t);
   // K operands are in registers once at most the prologue's loads remain
-  if (wave == 0) gen_wait<(gSlots - 1) * (gLoads + 1)>();
-  else gen_wait<(gSlots - 1) * gLoads>();
+  if (wave == 0) gen_wait<(gSlots - 1) * (ColLoader::kLoads + 1)>();
+  else gen_wait<(gSlots - 1) * ColLoader::kLoads>();
 
   float agg[2];
   agg[0] = agg[1] = MAXAGG ? neg_inf() : 0.f;
   const bool any_key = key0 < n;
 
   auto begin_tile = [&](int t) -> const unsigned char* {
-    if (wave == 0) gen_wait_tile<gLoads + 1>(t, ntiles);
-    else gen_wait_tile<gLoads>(t, ntiles);
+    if (wave == 0) gen_wait_tile<ColLoader::kLoads + 1>(t, ntiles);
+    else gen_wait_tile<ColLoader::kLoads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
     int soff = (t % gSlots) * gSlotBytes;   // opaque: LDS reads stay inside the tile
@@ -606,7 +618,7 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 void twopass_plan(const ScorePlan& p, TwoPassLayout* o) {
   const int Lv = p.chunk_m > 0 ? p.L * ((p.n + p.chunk_m - 1) / p.chunk_m) : p.L;
-  const int row_blocks = (p.R + gBlock - 1) / gBlock;
+  const int row_blocks = (p.R + gStatsBlock - 1) / gStatsBlock;
   int splits, kps, stride;
   if (p.chunk_m > 0) {
     // chunked: (layer, chunk) pairs fill the GPU; one workgroup per row
@@ -655,14 +667,14 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
   const KeyMap km{T, chunked ? p.chunk_m : p.n, p.n};
   const int kmax = km.m;                      // keys a grid layer holds at most
   const long long g1 = (long long)o.row_blocks * o.splits * p.H * o.Lv;
-  const int key_blocks = (kmax + gBlock - 1) / gBlock;
+  const int key_blocks = (kmax + gColBlock - 1) / gColBlock;
   const long long g2 = (long long)key_blocks * p.H * o.Lv;
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int Rpad = (p.R + gTile - 1) / gTile * gTile;
   if (p.logit) {
     hipLaunchKernelGGL(k_logit_stat, dim3((Rpad + 255) / 256, p.H, o.Lv), dim3(256), 0, st, p.R,
                        Rpad, stat);
-    hipLaunchKernelGGL((k_gen_colagg<false, true, true>), dim3((unsigned)g2), dim3(512), 0, st, qb,
+    hipLaunchKernelGGL((k_gen_colagg<false, true, true>), dim3((unsigned)g2), dim3(gColBlock), 0, st, qb,
                        kb, p.H, p.R, p.W, km, p.scale, key_blocks, stat, rawbuf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -673,15 +685,15 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
   const int n_in = chunked ? p.n_prompt + p.chunk_m : 0;
   const __bf16* ksb = static_cast<const __bf16*>(k_self);
   if (chunked)
-    hipLaunchKernelGGL((k_gen_stats<false, true>), dim3((unsigned)g1), dim3(512), 0, st, qb, kb,
+    hipLaunchKernelGGL((k_gen_stats<false, true>), dim3((unsigned)g1), dim3(gStatsBlock), 0, st, qb, kb,
                        p.H, p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
                        o.sp_stride, part, ksb, n_in);
   else if (p.causal)
-    hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
+    hipLaunchKernelGGL(k_gen_stats<true>, dim3((unsigned)g1), dim3(gStatsBlock), 0, st, qb, kb, p.H,
                        p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
                        o.sp_stride, part, ksb, 1);
   else
-    hipLaunchKernelGGL(k_gen_stats<false>, dim3((unsigned)g1), dim3(512), 0, st, qb, kb, p.H,
+    hipLaunchKernelGGL(k_gen_stats<false>, dim3((unsigned)g1), dim3(gStatsBlock), 0, st, qb, kb, p.H,
                        p.R, p.W, km, alpha, o.row_blocks, o.splits, o.keys_per_split, 0,
                        o.sp_stride, part, ksb, 1);
   hipError_t e = hipGetLastError();
@@ -694,17 +706,17 @@ hipError_t twopass_launch(const ScorePlan& p, const TwoPassLayout& o, const void
   const dim3 grid2((unsigned)g2);
   if (p.causal) {
     if (p.max_agg)
-      hipLaunchKernelGGL((k_gen_colagg<true, true>), grid2, dim3(512), 0, st, qb, kb, p.H, p.R,
+      hipLaunchKernelGGL((k_gen_colagg<true, true>), grid2, dim3(gColBlock), 0, st, qb, kb, p.H, p.R,
                          p.W, km, alpha, key_blocks, stat, rawbuf);
     else
-      hipLaunchKernelGGL((k_gen_colagg<true, false>), grid2, dim3(512), 0, st, qb, kb, p.H,
+      hipLaunchKernelGGL((k_gen_colagg<true, false>), grid2, dim3(gColBlock), 0, st, qb, kb, p.H,
                          p.R, p.W, km, alpha, key_blocks, stat, rawbuf);
   } else {
     if (p.max_agg)
-      hipLaunchKernelGGL((k_gen_colagg<false, true>), grid2, dim3(512), 0, st, qb, kb, p.H,
+      hipLaunchKernelGGL((k_gen_colagg<false, true>), grid2, dim3(gColBlock), 0, st, qb, kb, p.H,
                          p.R, p.W, km, alpha, key_blocks, stat, rawbuf);
     else
-      hipLaunchKernelGGL((k_gen_colagg<false, false>), grid2, dim3(512), 0, st, qb, kb, p.H,
+      hipLaunchKernelGGL((k_gen_colagg<false, false>), grid2, dim3(gColBlock), 0, st, qb, kb, p.H,
                          p.R, p.W, km, alpha, key_blocks, stat, rawbuf);
   }
   e = hipGetLastError();
