@@ -8,8 +8,9 @@
 // per-key |.| sums in registers and never written ([CriticalKV] §D.4 notes
 // the full V W^O would be ~7.8 GB per layer at 7B / 128K).
 //
-// Tiling (the 8-wave LDS ring of kvsel_ring.h): a workgroup owns 512 keys of
-// one (layer, KV head); each wave holds the values of 64 keys (two MFMA
+// Tiling (the LDS ring of kvsel_ring.h, 4 waves, two workgroups per CU): a
+// workgroup owns 256 keys of one (layer, KV head); each wave holds the
+// values of 64 keys (two MFMA
 // N tiles) in registers for the whole kernel. The A operand, W_O^(h,g), is
 // streamed in 64-row tiles (64 of the D output features, 128 columns each,
 // rows H_q*d elements apart in the [D][H_q*d] matrix) through the ring, for
@@ -24,8 +25,14 @@
 
 namespace kvsel {
 
-// 1-D grid of key_blocks * H * L workgroups, block 512.
-__global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__ v,
+// Two 4-wave workgroups per CU: each workgroup's tile barriers do not
+// stall the other's waves.
+constexpr int vWaves = 4;
+constexpr int vBlock = vWaves * 64;                    // keys per workgroup
+using VLoader = RingLoader<vWaves>;
+
+// 1-D grid of key_blocks * H * L workgroups, block vBlock.
+__global__ __launch_bounds__(vBlock, 2) void k_value_weight(const __bf16* __restrict__ v,
                                                       const __bf16* __restrict__ w_o,
                                                       int H, int G, int n, int D, int n_cand,
                                                       int key_blocks,
@@ -45,7 +52,7 @@ __global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__
   const int ntiles = G * dtiles;
 
   // this wave's 64 keys: MFMA B operands for the whole kernel
-  const int key0 = kb * gBlock + wave * 64;
+  const int key0 = kb * vBlock + wave * 64;
   bf16x8 vop[2][8];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -54,7 +61,7 @@ __global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__
     else zero_ops(vop[nt]);
   }
   // tile t: output features [64*dt, 64*dt + 64) of query head h*G + g
-  GenLoader ld;
+  VLoader ld;
   ld.init(stride);
   auto issue = [&](int t, int slot) {
     const int g = t / dtiles, dt = t - g * dtiles;
@@ -64,13 +71,13 @@ __global__ __launch_bounds__(512) void k_value_weight(const __bf16* __restrict__
 #pragma unroll
   for (int t = 0; t < gSlots - 1; ++t) issue(min(t, ntiles - 1), t);
   // values are in registers once at most the prologue's loads remain
-  gen_wait<(gSlots - 1) * gLoads>();
+  gen_wait<(gSlots - 1) * VLoader::kLoads>();
 
   const bool any_key = key0 < n_cand;
   float part[2] = {0.f, 0.f};
 
   auto begin_tile = [&](int t) -> const unsigned char* {
-    gen_wait_tile<gLoads>(t, ntiles);
+    gen_wait_tile<VLoader::kLoads>(t, ntiles);
     gen_barrier();
     if (t + gSlots - 1 < ntiles) issue(t + gSlots - 1, (t + gSlots - 1) % gSlots);
     int soff = (t % gSlots) * gRowsBytes;   // opaque: LDS reads stay inside the tile
@@ -208,7 +215,7 @@ size_t value_weight_ws_bytes(int L, int H, int D, int group_mode) {
 hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int G, int n,
                                int D, int n_cand, int group_mode, float* weight, void* ws,
                                hipStream_t st) {
-  const int key_blocks = (n_cand + gBlock - 1) / gBlock;
+  const int key_blocks = (n_cand + vBlock - 1) / vBlock;
   const long long blocks = (long long)key_blocks * H * L;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const __bf16* proj = static_cast<const __bf16*>(w_o);
@@ -224,7 +231,7 @@ hipError_t value_weight_launch(const void* v, const void* w_o, int L, int H, int
     proj = wsum;
     g_eff = 1;
   }
-  hipLaunchKernelGGL(k_value_weight, dim3((unsigned)blocks), dim3(512), 0, st,
+  hipLaunchKernelGGL(k_value_weight, dim3((unsigned)blocks), dim3(vBlock), 0, st,
                      static_cast<const __bf16*>(v), proj, H, g_eff, n, D, n_cand, key_blocks,
                      weight);
   return hipGetLastError();
