@@ -494,7 +494,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
 //   k_msel_init    per segment: state (prefix, shift, need) for a stage
 //                  (and, for the first, a cleared global histogram)
 //   k_msel_hist    per chunk: histogram of the current digit among the
-//                  candidates that match the prefix (LDS, kMCopies copies),
+//                  candidates that match the prefix (in LDS: four copies on
+//                  a stage's first digit, where keys crowd a few bins; one
+//                  copy after it, where few keys match the prefix),
 //                  added to the segment's global histogram
 //   k_msel_pick    per segment: the bin holding the need-th largest key
 //                  (bins read in descending order), the next state, and a
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
 constexpr int kMThreads = 256;
 constexpr int kChunk = 8192;                       // candidates per chunk
 constexpr int kPerThread = kChunk / kMThreads;     // 32
-constexpr int kMCopies = 4;                        // LDS histogram copies
+constexpr int kMCopies = 4;                        // LDS histogram copies, first digit
 
 struct alignas(16) SegState {
   uint64_t prefix;      // current stage: key prefix above `shift`
@@ -619,8 +621,9 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2)
 }
 
 // grid chunks*segments (1-D), block 256
+template <int COPIES>
 __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2) {
-  __shared__ uint32_t hist[kMCopies][kBins];
+  __shared__ uint32_t hist[COPIES][kBins];
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
   const SegState st = a.states[seg];
   if (st.done) return;
@@ -630,9 +633,11 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
   msel_chunk(a, c, g, begin, end);
   float s[kPerThread], w[kPerThread];
   msel_load(a, seg, begin, end, stage2 != 0, [&](int i) { return (uint32_t)(i * kMThreads + tid); }, s, w);
-  for (int b = tid; b < kMCopies * kBins; b += kMThreads) (&hist[0][0])[b] = 0;
+#pragma unroll
+  for (int cp = 0; cp < COPIES; ++cp)
+    for (int b = tid; b < nb; b += kMThreads) hist[cp][b] = 0;
   __syncthreads();
-  uint32_t* hc = hist[tid & (kMCopies - 1)];
+  uint32_t* hc = hist[tid & (COPIES - 1)];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const uint32_t f = begin + i * kMThreads + tid;
@@ -647,7 +652,7 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
   for (int b = tid; b < nb; b += kMThreads) {
     uint32_t v = 0;
 #pragma unroll
-    for (int cp = 0; cp < kMCopies; ++cp) v += hist[cp][b];
+    for (int cp = 0; cp < COPIES; ++cp) v += hist[cp][b];
     if (v) atomicAdd(gh + b, v);
   }
 }
@@ -1000,7 +1005,10 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
     const int rounds = stg + 1 < stages ? 6 : 3;
     hipLaunchKernelGGL(k_msel_init, gp, dim3(kMThreads), 0, st, a, stage2);
     for (int r = 0; r < rounds; ++r) {
-      hipLaunchKernelGGL(k_msel_hist, gc, dim3(kMThreads), 0, st, a, stage2);
+      if (r == 0)
+        hipLaunchKernelGGL(k_msel_hist<kMCopies>, gc, dim3(kMThreads), 0, st, a, stage2);
+      else
+        hipLaunchKernelGGL(k_msel_hist<1>, gc, dim3(kMThreads), 0, st, a, stage2);
       hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
     }
   }
