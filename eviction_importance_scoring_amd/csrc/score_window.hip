@@ -369,22 +369,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const float ident = MAXAGG ? -__builtin_inff() : 0.f;
 
   // one wave adds the 4 waves' partials of tile tt (written before the
-  // last barrier) in a fixed order
-  auto reduce = [&](int tt) {
+  // last barrier) in a fixed order. In the tile loop the LDS reads are
+  // issued right after the barrier and the sum is stored after the tile's
+  // MFMAs, so the read latency stays off the wave's path to the next
+  // barrier; the buffer is written again only after that barrier.
+  float rp[4];
+  auto reduce_read = [&](int tt) {
+    if (tid >= kTile) return;
+    const float* cb = &sm.colbuf[tt & 1][0][0];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) rp[w] = cb[w * kTile + tid];
+  };
+  auto reduce_store = [&](int tt) {
     if (tid >= kTile) return;
     const int key = j0 + tt * kTile + tid;
-    const float* cb = &sm.colbuf[tt & 1][0][0];
     float v;
-    if (MAXAGG) v = fast_exp2(__builtin_fmaxf(__builtin_fmaxf(cb[tid], cb[kTile + tid]),
-                                              __builtin_fmaxf(cb[2 * kTile + tid], cb[3 * kTile + tid])));
-    else v = (cb[tid] + cb[kTile + tid]) + (cb[2 * kTile + tid] + cb[3 * kTile + tid]);
+    if (MAXAGG) v = fast_exp2(__builtin_fmaxf(__builtin_fmaxf(rp[0], rp[1]), __builtin_fmaxf(rp[2], rp[3])));
+    else v = (rp[0] + rp[1]) + (rp[2] + rp[3]);
     if (key < j1) raw[lh * n + key] = v;
+  };
+  auto reduce = [&](int tt) {
+    reduce_read(tt);
+    reduce_store(tt);
   };
   // tile t-2's sums are stored by wave 0, which loads no ring tiles
   auto begin_tile = [&](int t) -> const unsigned char* {
     wait_ring_w123(t + 1 == ntiles, wave);
     ring_barrier_lds();
-    if (t >= 2) reduce(t - 2);
+    if (t >= 2) reduce_read(t - 2);
     if (t + kSlots - 1 < ntiles)
       ld.issue(kh, j0 + (t + kSlots - 1) * kTile, n, sm.ring[(t + kSlots - 1) % kSlots]);
     // the slot's offset in an opaque vector register: keeps LDS reads from
@@ -455,6 +467,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (t >= 2) reduce_store(t - 2);
     fold_end(pa, t - 1);
   };
 
