@@ -567,17 +567,17 @@ __device__ __forceinline__ void msel_chunk(const MselArgs& a, uint32_t c, uint32
   end = min(begin + (uint32_t)kChunk, (g + 1) * a.n_cand);
 }
 
-// The thread's kPerThread candidates f = begin + e(i) (in range: f < end),
-// all loads issued before the first is used; out-of-range slots read 0.
-template <class Index>
+// The thread's kPerThread candidates f = begin + i * kMThreads + tid (in
+// range: f < end; coalesced), all loads issued before the first is used;
+// out-of-range slots read 0.
 __device__ __forceinline__ void msel_load(const MselArgs& a, uint32_t seg, uint32_t begin,
-                                          uint32_t end, bool stage2, Index e,
-                                          float (&s)[kPerThread], float (&w)[kPerThread]) {
+                                          uint32_t end, bool stage2, float (&s)[kPerThread],
+                                          float (&w)[kPerThread]) {
   const float* sc = a.scores + (size_t)seg * a.seg_len;
   const float* wt = a.weight ? a.weight + (size_t)seg * a.seg_len : nullptr;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t f = begin + e(i);
+    const uint32_t f = begin + i * kMThreads + threadIdx.x;
     s[i] = f < end ? sc[f] : 0.f;
     w[i] = (stage2 && f < end) ? wt[f] : 0.f;
   }
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
   float s[kPerThread], w[kPerThread];
-  msel_load(a, seg, begin, end, stage2 != 0, [&](int i) { return (uint32_t)(i * kMThreads + tid); }, s, w);
+  msel_load(a, seg, begin, end, stage2 != 0, s, w);
 #pragma unroll
   for (int cp = 0; cp < COPIES; ++cp)
     for (int b = tid; b < nb; b += kMThreads) hist[cp][b] = 0;
@@ -835,7 +835,7 @@ __global__ __launch_bounds__(kMThreads) void k_msel_count(MselArgs a, int stage2
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
   float s[kPerThread], w[kPerThread];
-  msel_load(a, seg, begin, end, stage2 != 0, [&](int i) { return (uint32_t)(i * kMThreads + tid); }, s, w);
+  msel_load(a, seg, begin, end, stage2 != 0, s, w);
   uint32_t na = 0, ne = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
@@ -877,7 +877,7 @@ __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2)
   msel_chunk(a, c, g, begin, end);
   {
     float s[kPerThread], w[kPerThread];
-    msel_load(a, seg, begin, end, stage2 != 0, [&](int i) { return (uint32_t)(i * kMThreads + tid); }, s, w);
+    msel_load(a, seg, begin, end, stage2 != 0, s, w);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const uint32_t e = i * kMThreads + tid;

@@ -367,6 +367,7 @@ CHUNKED_CASES = [
     (1, 1, 1, 100, 500, 0, 1),        # m past n: one chunk, no prompt
     (1, 2, 4, 2048, 512, 100, 1),     # an exact multiple
     (1, 1, 3, 700, 64, 200, 5),       # chunks shorter than the prompt
+    (1, 2, 7, 100, 16, 4, 1),         # inputs of 20 rows: a row block spans all 7 group heads
 ]
 
 
