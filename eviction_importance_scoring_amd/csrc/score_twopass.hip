@@ -269,9 +269,19 @@ __global__ __launch_bounds__(gStatsBlock, 2) void k_gen_stats(const __bf16* __re
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
-      tile_step(a[st & 1], qb, st, cur);
-      fold_part(prev, st, ps);
-      __builtin_amdgcn_sched_barrier(0);
+      // each of the step's four MFMAs is followed by two logits of part st
+      // of the previous tile's fold (the sums of fold_part, in its order)
+      const int fnt = st >> 2, fmt = (st >> 1) & 1, fi = (st & 1) * 8;
+      const float off = -m[fnt];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int mt = u & 1, nt = u >> 1;
+        cur[mt][nt] = mfma32(a[st & 1][mt], qb[nt][st], cur[mt][nt]);
+#pragma unroll
+        for (int i = fi + 2 * u; i < fi + 2 * u + 2; ++i)
+          ps[fnt] += fast_exp2(__builtin_fmaf(prev[fmt][fnt][i], alpha, off));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // pin the partial sums here: otherwise the compiler sinks the second
     // row set's folds past the first row set's branch, behind the MFMAs
