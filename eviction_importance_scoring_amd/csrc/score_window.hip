@@ -123,25 +123,11 @@ struct RingLoader {
   }
 };
 
-// Pass 2 leaves wave 0 out of the ring loads: wave 0 stores the finished
-// sums, and a wave's stores share vmcnt with its loads, so a store still in
-// flight would hold up its next ring wait (and with it the barrier). Waves
-// 1..3 load chunks [0,6), [6,11) and [11,16) of each tile's 16 chunks; wave
-// 0 never waits on vmcnt in the loop.
-__device__ __forceinline__ void init_loader_w123(RingLoader<6>& ld, int wave) {
-  if (wave == 0) ld.init(0, 0);
-  else if (wave == 1) ld.init(0, 6);
-  else ld.init(6 + (wave - 2) * 5, 5);
-}
-
-// wait_ring for the pass-2 loaders (wave 0 has no ring loads)
-__device__ __forceinline__ void wait_ring_w123(bool last, int wave) {
-  if (wave == 0) return;
-  if (last) __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-  else if (wave == 1) __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8));
-  else __builtin_amdgcn_s_waitcnt(5 | (7 << 4) | (15 << 8));
-}
-
+// Pass 2 loads the ring like pass 1 (every wave a quarter of each tile).
+// Wave 0 also stores the finished sums, which share vmcnt with its loads;
+// wait_ring stays correct (loads return in order, so at most kLoadsPerTile
+// outstanding operations leave no load of an older tile in flight) and may
+// also wait for a store issued after the newest tile's loads.
 // Before the pass-2 loop every load of the prologue is waited for: with
 // stores in the loop the compiler otherwise re-waits for all loads in
 // flight (vmcnt(0)) at the operands' first use inside the loop.
@@ -360,8 +346,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     crow[i] = r < R ? stat[lh * R + r] : __builtin_inff();
   }
   asm volatile("" ::: "memory");
-  RingLoader<6> ld;
-  init_loader_w123(ld, wave);
+  RingLoader<kLoadsPerTile> ld;
+  ld.init(wave * kLoadsPerTile, kLoadsPerTile);
 #pragma unroll
   for (int t = 0; t < kSlots - 1; ++t) ld.issue(kh, j0 + min(t, ntiles - 1) * kTile, n, sm.ring[t]);
   wait_all();
@@ -392,9 +378,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     reduce_read(tt);
     reduce_store(tt);
   };
-  // tile t-2's sums are stored by wave 0, which loads no ring tiles
+  // tile t-2's sums are read after the barrier and stored by wave 0 after the MFMAs
   auto begin_tile = [&](int t) -> const unsigned char* {
-    wait_ring_w123(t + 1 == ntiles, wave);
+    wait_ring(t + 1 == ntiles);
     ring_barrier_lds();
     if (t >= 2) reduce_read(t - 2);
     if (t + kSlots - 1 < ntiles)
