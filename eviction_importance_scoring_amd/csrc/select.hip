@@ -28,26 +28,28 @@
 // k1 stage-1 members plus the k - k1 best of the rest.
 //
 // Segments of up to kResidentMax candidates are read from HBM once into
-// the LDS of one workgroup; longer ones are spread over many workgroups
-// (below).
+// the registers of one workgroup; longer ones are spread over many
+// workgroups (below).
 //
 // Per-head budget vector ([CriticalKV] §4.1: HeadKV's offline per-head
 // budgets): segments are heads, each with its own budget b (window
 // included, clamped into [W, n]) and so its own k = b - W (and k1); a
 // layer's heads are packed in order into a row of `stride` entries, and
 // entries that would land at or past the row's end are not written.
+#include <type_traits>
+
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
 
 namespace kvsel {
 
 constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kBins = 2048;
-constexpr int kResidentMax = 34816;          // 136 KiB of u32 keys in LDS (< 2^16)
+constexpr int kKPT = 34;                              // keys a thread holds
+constexpr int kResidentMax = kKPT * kSelThreads;      // 34,816 candidates
 constexpr int kMaxGroups = 1024;             // heads per segment
 constexpr uint32_t kInfBits = 0xFF800000u;     // score bits of +inf
-constexpr int kLoadUnroll = 8;              // loads in flight per thread
-constexpr int kMaxPer = 35;                  // candidates a thread emits (odd)
 
 struct SelArgs {
   const float* scores;
@@ -115,34 +117,33 @@ __device__ __forceinline__ void fill_row_tail(int32_t* idx, uint8_t* stage, int6
   }
 }
 
-// The resident select's digit histogram: kHistCopies copies of 16-bit
-// counters, two bins a word (bin 2w in the low half of word w, 2w+1 in the
-// high half). Lane l adds to copy l % kHistCopies, so the lanes of one
-// atomic instruction that hit the same bin (common on the first digit,
-// where keys crowd a few exponent bins) are spread over that many words;
-// copies lie kCopyWords apart, an odd count, so those words sit in
-// different banks. A copy sees at most ceil(len / kHistCopies) keys, which
-// keeps every counter below 2^16.
-constexpr int kHistCopies = 4;
-constexpr int kCopyWords = kBins / 2 + 1;
-static_assert((kResidentMax + kHistCopies * kSelThreads) / kHistCopies < 65536, "16-bit counters");
+// The resident select's digit histogram: kHistCopies copies of 32-bit
+// counters, one bin a word. Lane l adds to copy l % kHistCopies, so the
+// lanes of one atomic instruction that hit the same bin (common on the
+// first digit, where keys crowd a few exponent bins, and wherever
+// max-pooling repeats a score over neighbouring keys, which sit in
+// neighbouring lanes) meet in one word at most four at a time. Copies lie
+// kCopyWords apart (2 mod 32 banks), so one bin's words in different
+// copies sit in different banks, and each thread's pair of bins in a copy
+// is one aligned 8-byte read.
+constexpr int kHistCopies = 16;
+constexpr int kCopyWords = kBins + 2;
+static_assert((kHistCopies * kCopyWords) % 4 == 0, "cleared in 16-byte pieces");
 
-struct alignas(16) SelShared {   // a multiple of 16 bytes: the keys follow it
+struct alignas(16) SelShared {
   uint32_t hist[kHistCopies * kCopyWords];
   uint32_t sbuf[32];
+  uint32_t wcount[2][kSelWaves];        // per wave: members, tied entries
   uint32_t group_start[kMaxGroups];
-  uint64_t prefix;
-  int shift;
-  uint32_t need;
   uint32_t digit, above, dcount;
 };
 
 // Order-preserving 32-bit image of a score: larger value, larger bits.
 __device__ __forceinline__ uint32_t score_bits(float x) {
-  if (x != x) return 0u;                      // NaN: below everything
-  if (x == 0.f) return 0x80000000u;           // -0 and +0 alike
   const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  uint32_t b = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  b = x == 0.f ? 0x80000000u : b;             // -0 and +0 alike
+  return x != x ? 0u : b;                     // NaN: below everything
 }
 
 __device__ __forceinline__ uint64_t make_key(uint32_t bits, uint32_t f) {
@@ -210,61 +211,104 @@ struct SelCut {
   bool done;
 };
 
-// One stage of radix select over the segment's resident key bits, down to
-// stop_shift at most (0: to a single key).
-__device__ SelCut radix_select(SelShared& sm, const uint32_t* bits, uint32_t len, uint32_t k,
-                               int stop_shift) {
+// Candidate i of this thread: f = fbase + 64 i (wave w, lane l: fbase =
+// 64 w kKPT + l), so each key register of a wave covers 64 consecutive
+// candidates.
+__device__ __forceinline__ uint32_t cand(uint32_t fbase, int i) { return fbase + 64u * (uint32_t)i; }
+
+// (key >> shift) >= prefix for key = (bits << 31) | (2^31 - 1 - f), in
+// 32-bit arithmetic
+__device__ __forceinline__ bool key_ge(uint32_t bits, uint32_t f, int shift, uint64_t prefix) {
+  if (shift >= 31) {
+    const uint32_t s = (uint32_t)shift - 31u;   // 0..32
+    const uint32_t top = s >= 32 ? 0u : bits >> s;
+    return (uint64_t)top >= prefix;
+  }
+  const uint32_t pb = (uint32_t)(prefix >> (31 - shift));
+  const uint32_t pi = (uint32_t)prefix & ((1u << (31 - shift)) - 1u);
+  return bits > pb || (bits == pb && ((0x7FFFFFFFu - f) >> shift) >= pi);
+}
+
+// One stage of radix select over the segment's key bits, held in the
+// threads' registers (kb), down to stop_shift at most (0: to a single key).
+// Every thread keeps the same (prefix, shift, need). nvw: registers that
+// hold at least one real candidate in this wave (the rest are skipped).
+// Real candidates past the segment's end in a register that has some hold
+// score bits 0 and indices f >= len: keys below every real key (a NaN
+// score's included), so for 0 < k < len they change neither the k-th key
+// nor which real keys are members; they only add to the lowest buckets'
+// counts, which can make the final stage stop at the score bits with the
+// bucket split by index where it would have been taken whole (the
+// emission counts real keys only, so the members are the same).
+__device__ __forceinline__ SelCut radix_select(SelShared& sm, const uint32_t (&kb)[kKPT],
+                                               uint32_t fbase, uint32_t nvw, uint32_t len,
+                                               uint32_t k, int stop_shift) {
   const int tid = threadIdx.x;
   if (k == 0 || k == len)   // nothing ((key >> 63) >= 1 never holds), or everything
     return SelCut{(k == 0) ? uint64_t(1) : uint64_t(0), 63, 0u, true};
-  if (tid == 0) {
-    sm.prefix = 0;
-    sm.shift = 63;
-    sm.need = k;
-  }
-  __syncthreads();
+  uint64_t prefix = 0;
+  int shift = 63;
+  uint32_t need = k, dcount = 0;
+  // this lane's copy: the atomic's address is one shift-add from the bin
+  uint32_t* hc = sm.hist + (tid & (kHistCopies - 1)) * kCopyWords;
+  __syncthreads();   // the histogram is clear on entry and stays so between rounds
   for (;;) {
-    const uint64_t prefix = sm.prefix;
-    const int shift = sm.shift;
-    const uint32_t need = sm.need;
     const int wdt = digit_width(shift);
-    const int nb = 1 << wdt;
-    for (int w = tid; w < kHistCopies * kCopyWords; w += kSelThreads) sm.hist[w] = 0;
-    __syncthreads();
-    const uint32_t cbase = (uint32_t)(tid & (kHistCopies - 1)) * kCopyWords;
-    if (shift - wdt >= 31 && (len & 3u) == 0) {
-      // the digit lies in the score bits: 32-bit compares on 4 keys a read
-      const uint32_t sh = shift - 31, dsh = shift - wdt - 31, p32 = (uint32_t)prefix;
-      const u32x4* b4 = reinterpret_cast<const u32x4*>(bits);
-      for (uint32_t i = tid; i < (len >> 2); i += kSelThreads) {
-        const u32x4 v = b4[i];
+    const uint32_t nb = 1u << wdt;
+    // opaque per round: keeps the per-key indices from being hoisted out
+    // of the round loop into 34 more registers
+    uint32_t fb = fbase;
+    asm volatile("" : "+v"(fb));
+    // full: every register of the wave holds real candidates (no tests)
+    auto hist = [&](auto full) {
+      constexpr bool kFull = decltype(full)::value;
+      if (shift == 63) {
+        // first digit: every key matches
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if ((uint32_t)((uint64_t)v[c] >> sh) == p32) {   // sh may be 31
-            const uint32_t bin = (v[c] >> dsh) & (nb - 1);
-            atomicAdd(&sm.hist[cbase + (bin >> 1)], 1u << ((bin & 1u) << 4));
-          }
-      }
-    } else {
-      for (uint32_t f = tid; f < len; f += kSelThreads) {
-        const uint64_t key = make_key(bits[f], f);
-        if ((key >> shift) == prefix) {
-          const uint32_t bin = (uint32_t)(key >> (shift - wdt)) & (nb - 1);
-          atomicAdd(&sm.hist[cbase + (bin >> 1)], 1u << ((bin & 1u) << 4));
+        for (int i = 0; i < kKPT; ++i)
+          if (kFull || (uint32_t)i < nvw) atomicAdd(hc + (kb[i] >> 21), 1u);
+      } else if (shift - wdt >= 31) {
+        // the digit lies in the score bits: keys with (bits >> sh) == prefix
+        // are those in [lo, lo + 2^sh)
+        const uint32_t sh = shift - 31, dsh = shift - wdt - 31;
+        const uint32_t lo = (uint32_t)prefix << sh, span = 1u << sh;
+#pragma unroll
+        for (int i = 0; i < kKPT; ++i)
+          if ((kFull || (uint32_t)i < nvw) && kb[i] - lo < span)
+            atomicAdd(hc + __builtin_amdgcn_ubfe(kb[i], dsh, (uint32_t)wdt), 1u);
+      } else {
+        // the digit lies in the index bits: the score bits are all fixed
+        const uint32_t pb = (uint32_t)(prefix >> (31 - shift));
+        const uint32_t pi = (uint32_t)prefix & ((1u << (31 - shift)) - 1u);
+        const uint32_t ish = (uint32_t)shift, dsh = (uint32_t)(shift - wdt);
+#pragma unroll
+        for (int i = 0; i < kKPT; ++i) {
+          const uint32_t ix = 0x7FFFFFFFu - cand(fb, i);
+          if ((kFull || (uint32_t)i < nvw) && kb[i] == pb && (ix >> ish) == pi)
+            atomicAdd(hc + __builtin_amdgcn_ubfe(ix, dsh, (uint32_t)wdt), 1u);
         }
       }
-    }
+    };
+    if (nvw == (uint32_t)kKPT) hist(std::true_type{});
+    else hist(std::false_type{});
     __syncthreads();
     // bins in descending order: thread t holds bins nb-1-2t and nb-2-2t,
-    // the high and low halves of word nb/2-1-t in every copy
-    const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
+    // one aligned pair in every copy, which it clears for the next round
+    // (a round adds to bins below its nb only)
+    const int b0 = (int)nb - 1 - 2 * tid, b1 = b0 - 1;
     uint32_t h0 = 0u, h1 = 0u;
     if (b0 >= 0) {
 #pragma unroll
-      for (int c = 0; c < kHistCopies; ++c) {
-        const uint32_t x = sm.hist[c * kCopyWords + (b0 >> 1)];
-        h0 += x >> 16;
-        h1 += x & 0xFFFFu;
+      for (int c0 = 0; c0 < kHistCopies; c0 += 4) {
+        uint2 x[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const uint2*>(&sm.hist[(c0 + c) * kCopyWords + b1]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          h1 += x[c].x;
+          h0 += x[c].y;
+          *reinterpret_cast<uint2*>(&sm.hist[(c0 + c) * kCopyWords + b1]) = uint2{0u, 0u};
+        }
       }
     }
     uint32_t tot;
@@ -279,197 +323,262 @@ __device__ SelCut radix_select(SelShared& sm, const uint32_t* bits, uint32_t len
       sm.dcount = h1;
     }
     __syncthreads();
-    if (tid == 0) {
-      sm.prefix = (prefix << wdt) | sm.digit;
-      sm.shift = shift - wdt;
-      sm.need = need - sm.above;
-    }
-    __syncthreads();
-    if (sm.need == sm.dcount || sm.shift <= stop_shift) break;
+    prefix = (prefix << wdt) | sm.digit;
+    shift -= wdt;
+    need -= sm.above;
+    dcount = sm.dcount;
+    // sm.digit/above/dcount are written again only after the next round's
+    // histogram barrier, which every thread reaches after these reads
+    if (need == dcount || shift <= stop_shift) break;
   }
-  const SelCut cut{sm.prefix, sm.shift, sm.need, sm.need == sm.dcount || sm.shift == 0};
-  __syncthreads();
-  return cut;
+  return SelCut{prefix, shift, need, need == dcount || shift == 0};
 }
 
-// One workgroup per segment of at most kResidentMax candidates: the key
-// bits are read from HBM once into LDS and every pass runs there.
+// lanes below this one whose bit is set in m, plus base
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m, uint32_t base) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, base));
+}
+
+// One workgroup per segment of at most kResidentMax candidates: every key
+// is read from HBM once into a register of one thread, and each radix
+// round histograms the registers into LDS.
 __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SelShared& sm = *reinterpret_cast<SelShared*>(smem_raw);
-  uint32_t* keys = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SelShared));
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t seg = blockIdx.x;
   const float* sc = a.scores + seg * a.seg_len;
   const float* wt = a.weight ? a.weight + seg * a.seg_len : nullptr;
-  const uint32_t len = a.seg_len;
+  const uint32_t len = a.seg_len;   // >= 1 (the API keeps W < n)
   const SegSpan sp = seg_span(a, seg);
+  const uint32_t fbase = (uint32_t)(wave * kKPT) * 64u + (uint32_t)lane;
+  // the thread's real candidates: i < nv; the wave's: registers i < nvw
+  // hold some (lane 0 has the most), registers i < nvall hold only real ones
+  const uint32_t nv = fbase < len ? min((uint32_t)kKPT, (len - fbase + 63u) / 64u) : 0u;
+  const uint32_t nvw = __builtin_amdgcn_readfirstlane(nv);
+  const uint32_t nvall = __builtin_amdgcn_readlane(nv, 63);
 
-  // every load of a sweep in flight at once (one wait per sweep)
-  if ((len & 3u) == 0) {
-    const u32x4* s4 = reinterpret_cast<const u32x4*>(sc);
-    u32x4* k4 = reinterpret_cast<u32x4*>(keys);
-    const uint32_t n4 = len >> 2;
-    for (uint32_t base = 0; base < n4; base += kLoadUnroll * kSelThreads) {
-      u32x4 v[kLoadUnroll];
+  // every load in flight at once (one wait); each load instruction of a
+  // wave reads 256 contiguous bytes
+  uint32_t kb[kKPT];
+  const uint32_t* sc32 = reinterpret_cast<const uint32_t*>(sc);
+  const uint32_t flast = len - 1u;   // loads past the end repeat the last candidate
 #pragma unroll
-      for (int u = 0; u < kLoadUnroll; ++u) {
-        const uint32_t i = base + u * kSelThreads + tid;
-        v[u] = i < n4 ? __builtin_nontemporal_load(s4 + i) : u32x4{0u, 0u, 0u, 0u};
-      }
+  for (int i = 0; i < kKPT; ++i)
+    kb[i] = (uint32_t)i < nvw ? __builtin_nontemporal_load(sc32 + min(cand(fbase, i), flast)) : 0u;
+  // the histogram starts clear (while the loads are in flight)
+  {
+    u32x4* h4 = reinterpret_cast<u32x4*>(sm.hist);
+    for (int q = tid; q < kHistCopies * kCopyWords / 4; q += kSelThreads) h4[q] = u32x4{0u, 0u, 0u, 0u};
+  }
+  {
+    // an opaque copy of nv keeps the compiler from computing the range
+    // tests once and keeping them (in spilled scalar registers) for later
+    uint32_t nvl = nv;
+    asm volatile("" : "+v"(nvl));
 #pragma unroll
-      for (int u = 0; u < kLoadUnroll; ++u) {
-        const uint32_t i = base + u * kSelThreads + tid;
-        if (i < n4)
-          k4[i] = u32x4{score_bits(__uint_as_float(v[u].x)), score_bits(__uint_as_float(v[u].y)),
-                        score_bits(__uint_as_float(v[u].z)), score_bits(__uint_as_float(v[u].w))};
-      }
-    }
-  } else {
-    for (uint32_t base = 0; base < len; base += kLoadUnroll * kSelThreads) {
-      float v[kLoadUnroll];
-#pragma unroll
-      for (int u = 0; u < kLoadUnroll; ++u) {
-        const uint32_t f = base + u * kSelThreads + tid;
-        v[u] = f < len ? sc[f] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kLoadUnroll; ++u) {
-        const uint32_t f = base + u * kSelThreads + tid;
-        if (f < len) keys[f] = score_bits(v[u]);
-      }
+    for (int i = 0; i < kKPT; ++i) {
+      const uint32_t b = score_bits(__uint_as_float(kb[i]));
+      kb[i] = (uint32_t)i < nvl ? b : 0u;
     }
   }
-  __syncthreads();
 
   // stage 1 (two-stage only), all the way down: stage-1 membership stays a
   // test on the key, which stage 2 turns into +inf
   if (a.two_stage) {
-    const SelCut c1 = radix_select(sm, keys, len, sp.k1, 0);
-    for (uint32_t base = 0; base < len; base += kLoadUnroll * kSelThreads) {
-      float sv[kLoadUnroll], wv[kLoadUnroll];
+    const SelCut c1 = radix_select(sm, kb, fbase, nvw, len, sp.k1, 0);
+    uint32_t nvs = nv;
+    asm volatile("" : "+v"(nvs));
+    constexpr int kParts = 4, kHalf = (kKPT + kParts - 1) / kParts;
 #pragma unroll
-      for (int u = 0; u < kLoadUnroll; ++u) {
-        const uint32_t f = base + u * kSelThreads + tid;
-        sv[u] = f < len ? sc[f] : 0.f;
-        wv[u] = f < len ? wt[f] : 0.f;
+    for (int h = 0; h < kParts; ++h) {
+      float sv[kHalf], wv[kHalf];
+#pragma unroll
+      for (int u = 0; u < kHalf; ++u) {
+        const int i = h * kHalf + u;
+        const uint32_t f = cand(fbase, i);
+        const bool ok = i < kKPT && (uint32_t)i < nvs;
+        sv[u] = ok ? sc[f] : 0.f;
+        wv[u] = ok ? wt[f] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < kLoadUnroll; ++u) {
-        const uint32_t f = base + u * kSelThreads + tid;
-        if (f < len)
-          keys[f] = (make_key(keys[f], f) >> c1.shift) >= c1.prefix
-                        ? kInfBits : stage2_bits(sv[u], wv[u], a.score_norm, a.eps);
+      for (int u = 0; u < kHalf; ++u) {
+        const int i = h * kHalf + u;
+        if (i < kKPT)
+          kb[i] = (uint32_t)i >= nvs ? 0u
+                  : key_ge(kb[i], cand(fbase, i), c1.shift, c1.prefix)
+                      ? kInfBits : stage2_bits(sv[u], wv[u], a.score_norm, a.eps);
       }
     }
-    __syncthreads();
   }
 
-  const SelCut cf = radix_select(sm, keys, len, sp.k, 31);
+  const SelCut cf = radix_select(sm, kb, fbase, nvw, len, sp.k, 31);
 
-  // ---- emission, in index order. Thread t owns the `per` consecutive
-  // candidates from t*per (per odd, so the LDS reads of a wave fall in
-  // distinct banks); block scans give each thread the members (and tied
-  // bucket entries) before its range. Members are staged by rank in LDS
-  // (over the keys, which are no longer needed) and then written out with
-  // coalesced stores.
-  static_assert(((kResidentMax + kSelThreads - 1) / kSelThreads | 1) <= kMaxPer, "one 64-bit mask a thread");
-  const uint32_t per = ((len + kSelThreads - 1) / kSelThreads) | 1u;
-  const uint32_t f0 = min(len, tid * per), f1 = min(len, f0 + per);
-  // (key >> shift) vs prefix on the score bits alone; prefix 1 at shift 63
-  // (select nothing) stays out of reach of every score
-  const uint32_t csh = (uint32_t)cf.shift - 31u;
-  const uint32_t cp = cf.prefix > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)cf.prefix;
-  // every read first (clamped in range), then branch-free tests
-  uint32_t bv[kMaxPer];
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) bv[j] = keys[min(f0 + j, len - 1)];
+  // ---- emission, in index order. A key register of a wave holds 64
+  // consecutive candidates, so a ballot over it orders them; a first sweep
+  // counts each wave's members and tied bucket entries, a scan over the 16
+  // waves gives every wave the counts before it, and a second sweep writes
+  // each member to its output slot (a wave's members of one register go to
+  // consecutive slots).
+  // The select stopped at shift >= 31, so (key >> shift) vs prefix is a
+  // test on the score bits: keys in the bucket are those >= lo, keys above
+  // it those > hi. At shift 63 (k = 0 or k = len) the bucket is nothing
+  // (no key is 0xFFFFFFFF, a NaN image) or everything.
   const bool done = cf.done;
-  uint64_t mmask = 0, emask = 0, imask = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    const bool valid = f0 + j < f1;
-    const uint32_t top = (uint32_t)((uint64_t)bv[j] >> csh);   // the select stopped at shift >= 31
-    const bool eq = top == cp;
-    const bool mem = valid && (top > cp || (done && eq));
-    const bool tie = valid && !done && eq;
-    mmask |= (uint64_t)mem << j;
-    emask |= (uint64_t)tie << j;
-    imask |= (uint64_t)(bv[j] == kInfBits) << j;
+  uint32_t lo, hi;
+  if (cf.shift == 63) {
+    lo = cf.prefix == 0 ? 0u : 0xFFFFFFFFu;
+    hi = 0xFFFFFFFFu;
+  } else {
+    const uint32_t csh = (uint32_t)cf.shift - 31u;            // 0..21
+    const uint64_t top = (cf.prefix + 1) << csh;               // <= 2^32
+    lo = (uint32_t)(cf.prefix << csh);
+    hi = (uint32_t)min(top - 1, (uint64_t)0xFFFFFFFFu);
   }
-  // one scan of (tied entries, members) before each thread's range: the
-  // tied members are the first cf.need tied entries in index order, so the
-  // members before the range are mem_before + min(need, tied_before)
-  uint32_t tot;
-  const uint32_t packed = ((uint32_t)__popcll(emask) << 16) | (uint32_t)__popcll(mmask);
-  const uint32_t before = block_excl_scan(packed, sm.sbuf, tot);   // both sums < 2^16
-  const uint32_t tied_before = before >> 16;
-  const uint32_t need = done ? 0u : cf.need;
-  uint32_t rank = (before & 0xFFFFu) + min(need, tied_before);
-  for (uint64_t e = emask, t = tied_before; e != 0 && t < need; e &= e - 1, ++t)
-    mmask |= e & (~e + 1);
-  // staged[r] = position in its head of the member of rank r, bit 31 set
-  // for a stage-2 member of the two-stage selection
-  uint32_t* staged = keys;
-  if (f0 < f1) {
-    const uint32_t g0 = f0 / a.n_cand, gstart = g0 * a.n_cand;
-    if (gstart == f0) sm.group_start[g0] = rank;   // members before each group
-    for (uint32_t gs = gstart + a.n_cand; gs < f1; gs += a.n_cand)
-      sm.group_start[gs / a.n_cand] = rank + (uint32_t)__popcll(mmask & ((uint64_t(1) << (gs - f0)) - 1));
-    if (a.n_cand >= (uint32_t)kMaxPer) {   // at most one group boundary in the range
-      const uint32_t next = gstart + a.n_cand;
-      uint32_t r = rank;
+  // per register i, as ballots: its members above the bucket (m) and its
+  // entries in the bucket (t), real lanes only; every operation on them
+  // is scalar. kDone: the bucket is taken whole (no tied entries); kFull:
+  // every lane of every register of the wave is real.
+  auto masks = [&](auto dn, auto fl, int i, uint32_t nvx, uint64_t& m, uint64_t& t) {
+    constexpr bool kDone = decltype(dn)::value, kFull = decltype(fl)::value;
+    const uint64_t ge = __ballot(kb[i] >= lo);
+    const uint64_t gt = kDone ? ge : __ballot(kb[i] > hi);
+    const uint64_t rl = kFull || (uint32_t)i < nvall ? ~uint64_t(0) : __ballot((uint32_t)i < nvx);
+    m = gt & rl;
+    t = kDone ? 0 : ge & ~gt & rl;
+  };
+  auto count = [&](auto dn, auto fl, uint32_t nvx, uint32_t& cm, uint32_t& ct) {
 #pragma unroll
-      for (int j = 0; j < kMaxPer; ++j) {
-        if ((mmask >> j) & 1u) {
-          const uint32_t f = f0 + j;
-          const uint32_t pos = f - (f >= next ? next : gstart);
-          const bool second = a.two_stage && !((imask >> j) & 1u);
-          if (r < sp.k) staged[r] = pos | (second ? 0x80000000u : 0u);   // r < k always
-          ++r;
+    for (int i = 0; i < kKPT; ++i)
+      if (decltype(fl)::value || (uint32_t)i < nvw) {
+        uint64_t m, t;
+        masks(dn, fl, i, nvx, m, t);
+        cm += (uint32_t)__popcll(m);
+        ct += (uint32_t)__popcll(t);
+      }
+  };
+  uint32_t cm = 0u, ct = 0u;
+  {
+    uint32_t nva = nv;   // opaque per sweep: the sweeps share no per-key values
+    asm volatile("" : "+v"(nva));
+    const bool full = nvall == (uint32_t)kKPT;
+    if (done) {
+      if (full) count(std::true_type{}, std::true_type{}, nva, cm, ct);
+      else count(std::true_type{}, std::false_type{}, nva, cm, ct);
+    } else {
+      if (full) count(std::false_type{}, std::true_type{}, nva, cm, ct);
+      else count(std::false_type{}, std::false_type{}, nva, cm, ct);
+    }
+  }
+  if (lane == 0) {
+    sm.wcount[0][wave] = cm;
+    sm.wcount[1][wave] = ct;
+  }
+  lds_barrier();
+  uint32_t mb = 0u, tb = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    mb += w < wave ? sm.wcount[0][w] : 0u;
+    tb += w < wave ? sm.wcount[1][w] : 0u;
+  }
+  // the tied members are the first `need` tied entries in index order
+  const uint32_t need = done ? 0u : cf.need;
+  // members before the register's first candidate, tied entries before it
+  uint32_t run = __builtin_amdgcn_readfirstlane(mb + min(need, tb));
+  uint32_t trun = __builtin_amdgcn_readfirstlane(tb);
+  int32_t* out = a.idx + sp.base;
+  uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
+  // slots past lim are never written: r < k always, and a budget row may
+  // cut the segment's room below its budget
+  const uint32_t lim = (uint32_t)min((int64_t)sp.k, sp.room);
+  uint32_t fc = fbase, nvc = nv;
+  asm volatile("" : "+v"(fc), "+v"(nvc));
+  // register i's member ballot, tied members included
+  auto members = [&](auto dn, auto fl, int i) -> uint64_t {
+    uint64_t m, t;
+    masks(dn, fl, i, nvc, m, t);
+    if (!decltype(dn)::value && t) {   // tied entries: the first `need` in index order are members
+      m |= __ballot(__builtin_amdgcn_inverse_ballot_w64(t) && lanes_below(t, trun) < need);
+      trun += (uint32_t)__popcll(t);
+    }
+    return m;
+  };
+  // one head: a member's slot is its rank
+  auto write = [&](auto dn, auto fl) {
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i) {
+      if (!decltype(fl)::value && (uint32_t)i >= nvw) continue;
+      const uint64_t m = members(dn, fl, i);
+      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+        const uint32_t r = lanes_below(m, run);   // members before f, and f's slot
+        if (r < lim) {
+          out[r] = (int32_t)cand(fc, i);
+          if (st_out) st_out[r] = (a.two_stage && kb[i] != kInfBits) ? 2 : 1;
         }
       }
-    } else {
-      uint32_t gs = gstart;
-      for (uint64_t m = mmask; m != 0; m &= m - 1, ++rank) {
-        const uint32_t j = (uint32_t)__builtin_ctzll(m);
-        const uint32_t f = f0 + j;
-        while (f >= gs + a.n_cand) gs += a.n_cand;
-        const bool second = a.two_stage && !((imask >> j) & 1u);
-        if (rank < sp.k) staged[rank] = (f - gs) | (second ? 0x80000000u : 0u);   // rank < k always
+      run += (uint32_t)__popcll(m);
+    }
+  };
+  // several heads (adaptive): group g's members start at slot
+  // group_start[g] + g*W
+  auto write_grouped = [&](auto dn, auto fl) {
+    // group (head) of the lane's candidate: g, and its first candidate gstart
+    uint32_t g = 0u, gstart = 0u;
+    if (fbase < len) {
+      g = fbase / a.n_cand;
+      gstart = g * a.n_cand;
+    }
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i) {
+      if (!decltype(fl)::value && (uint32_t)i >= nvw) continue;
+      const uint64_t m = members(dn, fl, i);
+      const uint32_t f = cand(fc, i);
+      if ((uint32_t)i < nvc) {
+        while (f >= gstart + a.n_cand) {
+          ++g;
+          gstart += a.n_cand;
+        }
+        if (f == gstart) sm.group_start[g] = lanes_below(m, run);
       }
+      if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+        const uint32_t r = lanes_below(m, run);
+        const uint32_t slot = r + g * a.W;   // < 2^31: r < k, g*W <= budget
+        if (r < lim && slot < sp.room) {
+          out[slot] = (int32_t)(f - gstart);
+          if (st_out) st_out[slot] = (a.two_stage && kb[i] != kInfBits) ? 2 : 1;
+        }
+      }
+      run += (uint32_t)__popcll(m);
+    }
+  };
+  {
+    const bool full = nvall == (uint32_t)kKPT;
+    if (a.groups == 1) {
+      if (tid == 0) sm.group_start[0] = 0u;
+      if (done) {
+        if (full) write(std::true_type{}, std::true_type{});
+        else write(std::true_type{}, std::false_type{});
+      } else {
+        if (full) write(std::false_type{}, std::true_type{});
+        else write(std::false_type{}, std::false_type{});
+      }
+    } else {
+      if (done) write_grouped(std::true_type{}, std::false_type{});
+      else write_grouped(std::false_type{}, std::false_type{});
     }
   }
   lds_barrier();
-  // output slot o: group g's members then its W window entries, groups in
-  // order (slot of group g's first member: group_start[g] + g*W)
-  int32_t* out = a.idx + sp.base;
-  uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
-  for (uint32_t o = tid; o < sp.room; o += kSelThreads) {
-    uint32_t g = 0;
-    if (a.groups > 1) {   // last group whose first slot is <= o
-      uint32_t lo = 0, hi = a.groups - 1;
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if (sm.group_start[mid] + mid * a.W <= o) lo = mid; else hi = mid - 1;
-      }
-      g = lo;
+  // each group's W window entries follow its members (slot of group g's
+  // first member: group_start[g] + g*W)
+  for (uint32_t e = tid; e < a.groups * a.W; e += kSelThreads) {
+    const uint32_t gw = a.groups > 1 ? e / a.W : 0u, j = e - gw * a.W;
+    const uint32_t end_g = gw + 1 < a.groups ? sm.group_start[gw + 1] : sp.k;
+    const uint64_t slot = (uint64_t)end_g + (uint64_t)gw * a.W + j;
+    if (slot < (uint64_t)sp.room) {
+      out[slot] = (int32_t)(a.n - a.W + j);
+      if (st_out) st_out[slot] = 0;
     }
-    const uint32_t first = sm.group_start[g];
-    const uint32_t count = (g + 1 < a.groups ? sm.group_start[g + 1] : sp.k) - first;
-    const uint32_t local = o - (first + g * a.W);
-    int32_t v;
-    uint8_t sv;
-    if (local < count) {
-      const uint32_t e = staged[first + local];
-      v = (int32_t)(e & 0x7FFFFFFFu);
-      sv = (e >> 31) ? 2 : 1;
-    } else {
-      v = (int32_t)(a.n - a.W + (local - count));
-      sv = 0;
-    }
-    out[o] = v;
-    if (st_out) st_out[o] = sv;
   }
   if (a.budgets) {
     const size_t l = seg / a.H;
@@ -1019,9 +1128,7 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   return hipGetLastError();
 }
 
-static size_t lds_bytes(uint32_t len) { return sizeof(SelShared) + (size_t)len * sizeof(uint32_t); }
-static_assert(sizeof(SelShared) + (size_t)kResidentMax * sizeof(uint32_t) <= 160 * 1024,
-              "a resident segment and the shared state fit the CU's LDS");
+static_assert(sizeof(SelShared) <= 160 * 1024, "the shared state fits the CU's LDS");
 
 size_t select_ws_bytes(const SelectPlan& p) { return use_multi(p) ? msel_layout(p).bytes : 0; }
 
@@ -1051,7 +1158,7 @@ hipError_t select_launch(const SelectPlan& p, const float* scores, const float* 
   a.alpha = p.alpha;
   if (p.budgets) a.head_offsets = head_offsets;
   if (use_multi(p)) return msel_launch(p, scores, weight, idx, head_offsets, stage, ws, st);
-  const size_t lds = lds_bytes(a.seg_len);
+  const size_t lds = sizeof(SelShared);
   const hipError_t e =
       hipFuncSetAttribute((const void*)k_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
