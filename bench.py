@@ -262,10 +262,20 @@ def main():
         head_sc = torch.empty((wl.L, wl.H_kv), dtype=torch.float32, device=dev)
         budgets = torch.empty((wl.L, wl.H_kv), dtype=torch.int32, device=dev)
 
+    # Where the selection reads every head's raw scores itself (kvsel_select_pool),
+    # the scoring call writes raw scores only and the selection max-pools
+    # them on chip; the head-level, budget-vector, anchor and chunked steps
+    # read pooled scores from the scoring call.
+    pool_in_select = not (wl.chunk or wl.budget_vector or wl.head_keep > 0 or wl.anchor_k)
+    raw = torch.empty((wl.L, wl.H_kv, wl.n), dtype=torch.float32, device=dev) if pool_in_select else None
+
     def score():
         if wl.chunk:
             kv.kvsel_score_chunked(q, k, t["kself"], G=wl.G, m=wl.chunk, n_prompt=wl.n_prompt,
                                    scale=wl.scale, pool=wl.pool, scores=scores)
+        elif pool_in_select:
+            kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
+                           raw=raw, pooled=False)
         else:
             kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
                            scores=scores)
@@ -317,6 +327,11 @@ def main():
                                                    layer_stride=stride, weight=weight,
                                                    score_norm=1.0 / (wl.W * wl.G), eps=wl.eps,
                                                    alpha=wl.alpha)
+        elif pool_in_select:
+            idx, offs, _, _ = kv.kvsel_select_pool(raw, n=wl.n, W=W_kept, budget=wl.budget,
+                                                   pool=wl.pool, adaptive=wl.adaptive,
+                                                   weight=weight, score_norm=1.0 / (wl.W * wl.G),
+                                                   eps=wl.eps, alpha=wl.alpha)
         else:
             idx, offs, _ = kv.kvsel_select(scores, n=wl.n, W=W_kept, budget=wl.budget,
                                            adaptive=wl.adaptive, weight=weight,
@@ -366,9 +381,9 @@ def main():
 
     entries = wl.L * wl.H_kv * wl.n
     # algorithmic bytes of one scoring call: K read once, Q read once,
-    # pooled scores written once
+    # pooled scores (or, when the selection pools, raw scores) written once
     score_bytes = (wl.L * wl.H_kv * wl.n * wl.d * 2 + wl.L * wl.H_q * wl.W * wl.d * 2
-                   + wl.L * wl.H_kv * wl.n_cand * 4)
+                   + wl.L * wl.H_kv * (wl.n if pool_in_select else wl.n_cand) * 4)
     if wl.chunk:   # every chunk's queries and own keys
         score_bytes = (wl.L * wl.H_kv * wl.n * wl.d * 2 + wl.L * wl.T * (wl.H_q + wl.H_kv) * wl.n_in * wl.d * 2
                        + wl.L * wl.H_kv * wl.n_cand * 4)
@@ -390,6 +405,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "L": wl.L, "H_kv": wl.H_kv, "G": wl.G, "d": wl.d,
                    "n": wl.n, "W": wl.W, "q_mode": wl.q_mode, "agg": wl.agg, "pool": wl.pool,
+                   "pooling": "kvsel_select_pool" if pool_in_select else "kvsel_score",
                    "budget": wl.budget, "adaptive": wl.adaptive,
                    **({"chunk": wl.chunk, "n_prompt": wl.n_prompt} if wl.chunk else {}),
                    **({"budget_vector": True, "layer_stride": stride} if wl.budget_vector else {}),

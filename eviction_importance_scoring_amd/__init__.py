@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "lib", "library_path", "KvselError", "kvsel_score", "kvsel_score_chunked", "kvsel_value_weight",
     "kvsel_value_l2_factor", "kvsel_value_weight_l2",
-    "kvsel_select", "kvsel_select_static", "kvsel_static_scratch_bytes", "kvsel_select_budgets", "kvsel_head_score", "kvsel_head_budgets",
+    "kvsel_select", "kvsel_select_pool", "kvsel_select_static", "kvsel_static_scratch_bytes", "kvsel_select_budgets", "kvsel_head_score", "kvsel_head_budgets",
     "kvsel_anchor_select", "kvsel_anchor_assign",
     "kvsel_compact", "kvsel_decode_attention", "kvsel_status_str",
     "kvsel_abi_version",
@@ -56,6 +56,9 @@ _SIGNATURES = {
     "kvsel_select": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                      _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                      _c_size_p, _c_void_p],
+    "kvsel_select_pool": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                          _c_i32, _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p,
+                          _c_void_p, _c_void_p, _c_size_p, _c_void_p],
     "kvsel_select_budgets": [_c_void_p, _c_void_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_void_p,
                              _c_i64, _c_f32, _c_f32, _c_f32, _c_void_p, _c_void_p, _c_void_p,
                              _c_void_p, _c_size_p, _c_void_p],
@@ -170,10 +173,11 @@ def _workspace(nbytes: int, device, workspace=None):
 
 def kvsel_score(q, k, *, G: int, q_mode: int = Q_WINDOW, agg: int = AGG_SUM,
                 scale: float | None = None, pool: int = 7, return_raw: bool = False,
-                scores=None, raw=None, workspace=None):
+                scores=None, raw=None, workspace=None, pooled: bool = True):
     """Pooled attention scores [L][H_kv][n_cand] (and raw [L][H_kv][n]).
 
-    q bf16 [L][H_kv*G][W][d], k bf16 [L][H_kv][n][d]."""
+    q bf16 [L][H_kv*G][W][d], k bf16 [L][H_kv][n][d]. pooled=False: raw
+    scores only (returned as (None, raw)), for kvsel_select_pool."""
     _need(q, torch.bfloat16, "q", 4)
     _need(k, torch.bfloat16, "k", 4)
     L, Hq, W, d = q.shape
@@ -185,8 +189,11 @@ def kvsel_score(q, k, *, G: int, q_mode: int = Q_WINDOW, agg: int = AGG_SUM,
     n_cand = n - W if q_mode == Q_WINDOW else n
     dev = q.device
     _need(k, torch.bfloat16, "k", 4, dev)
-    scores = _out(scores, torch.float32, "scores", (L, H, max(n_cand, 0)), dev)
-    if return_raw or raw is not None:
+    if pooled:
+        scores = _out(scores, torch.float32, "scores", (L, H, max(n_cand, 0)), dev)
+    elif scores is not None:
+        raise ValueError("pooled=False computes no pooled scores")
+    if return_raw or raw is not None or not pooled:
         raw = _out(raw, torch.float32, "raw", (L, H, n), dev)
     nbytes = ctypes.c_size_t(0)
     f = lib().kvsel_score
@@ -316,6 +323,38 @@ def kvsel_select(scores, *, n: int, W: int, budget: int, adaptive: bool = False,
     _check(f(_ptr(scores), _ptr(weight), *args, _ptr(idx), _ptr(offs), _ptr(stage), _ptr(ws),
              ctypes.byref(nbytes), _stream(dev)))
     return idx, offs, stage
+
+
+def kvsel_select_pool(raw, *, n: int, W: int, budget: int, pool: int = 7, adaptive: bool = False,
+                      weight=None, score_norm: float = 1.0, eps: float = 1e-4,
+                      alpha: float = 0.5, return_stage: bool = False, return_pooled: bool = False,
+                      workspace=None):
+    """kvsel_select on raw [L][H_kv][n] scores max-pooled (width `pool`) by
+    the call itself; returns (idx, head_offsets, stage, pooled)."""
+    _need(raw, torch.float32, "raw", 3)
+    dev = raw.device
+    L, H, n_raw = raw.shape
+    if n_raw != n:
+        raise ValueError(f"raw has {n_raw} positions, expected n={n}")
+    if weight is not None:
+        _need(weight, torch.float32, "weight", 3, dev)
+        if tuple(weight.shape) != (L, H, n - W):
+            raise ValueError("weight must be [L][H_kv][n-W]")
+    shape = (L, budget) if adaptive else (L, H, budget)
+    idx = torch.empty(shape, dtype=torch.int32, device=dev)
+    offs = torch.empty((L, H + 1), dtype=torch.int32, device=dev) if adaptive else None
+    stage = torch.empty(shape, dtype=torch.uint8, device=dev) if return_stage else None
+    pooled = torch.empty((L, H, n - W), dtype=torch.float32, device=dev) if return_pooled else None
+    nbytes = ctypes.c_size_t(0)
+    f = lib().kvsel_select_pool
+    args = (int(pool), L, H, n, W, int(budget), int(adaptive), float(score_norm), float(eps),
+            float(alpha))
+    _check(f(None, _ptr(weight), *args, None, None, None, None, None, ctypes.byref(nbytes), None))
+    ws, wsb = _workspace(nbytes.value, dev, workspace)
+    nbytes = ctypes.c_size_t(wsb)
+    _check(f(_ptr(raw), _ptr(weight), *args, _ptr(idx), _ptr(offs), _ptr(stage), _ptr(pooled),
+             _ptr(ws), ctypes.byref(nbytes), _stream(dev)))
+    return idx, offs, stage, pooled
 
 
 def kvsel_select_static(scores, *, n: int, W: int, budget: int, adaptive: bool = False,

@@ -22,6 +22,7 @@ using namespace kvsel;
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
@@ -120,8 +121,9 @@ int32_t kvsel_score(const void* q, const void* k, int32_t L, int32_t H_kv, int32
     *ws_bytes = need;
     return KVSEL_OK;
   }
-  if (!q || !k || !scores) return KVSEL_ERR_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(scores) || !aligned16(ws) ||
+  // scores == NULL: raw only (no pooling), for kvsel_select_pool
+  if (!q || !k || (!scores && !raw)) return KVSEL_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || (scores && !aligned16(scores)) || !aligned16(ws) ||
       (raw && !aligned16(raw)))
     return KVSEL_ERR_ARG;
   if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
@@ -248,6 +250,50 @@ int32_t kvsel_select(const float* scores, const float* weight, int32_t L, int32_
   if (need > 0 && !aligned16(ws)) return KVSEL_ERR_ARG;
   const hipError_t e = select_launch(p, scores, weight, idx, head_offsets, stage, ws,
                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
+}
+
+int32_t kvsel_select_pool(const float* raw, const float* weight, int32_t pool, int32_t L,
+                          int32_t H_kv, int32_t n, int32_t W, int64_t budget, int32_t adaptive,
+                          float score_norm, float eps, float alpha, int32_t* idx,
+                          int32_t* head_offsets, uint8_t* stage, float* pooled, void* ws,
+                          size_t* ws_bytes, void* stream) {
+  if (!ws_bytes) return KVSEL_ERR_ARG;
+  if (pool < 1 || pool % 2 == 0) return KVSEL_ERR_ARG;
+  SelectPlan p;
+  const int32_t rc = select_plan(weight != nullptr, L, H_kv, n, W, budget, adaptive, score_norm,
+                                 eps, alpha, &p);
+  if (rc != KVSEL_OK) return rc;
+  if (pool > 65) return KVSEL_ERR_UNSUPPORTED;
+  // one head's raw row on chip when it fits; else the pooled scores go
+  // through memory (`pooled`, or the workspace) before the selection
+  const int r = pool / 2;
+  const bool on_chip = select_pools_on_chip(p, r);
+  const size_t pooled_ws = on_chip || pooled ? 0 : al256((size_t)L * H_kv * p.n_cand * sizeof(float));
+  const size_t need = pooled_ws + select_ws_bytes(p);
+  if (!ws) {
+    *ws_bytes = need;
+    return KVSEL_OK;
+  }
+  const int32_t rp = select_pointers_ok(p, raw, weight, idx, head_offsets);
+  if (rp != KVSEL_OK) return rp;
+  if (pooled && !aligned16(pooled)) return KVSEL_ERR_ARG;
+  if (*ws_bytes < need) return KVSEL_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return KVSEL_ERR_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (on_chip) {
+    p.pool_r = r;
+    p.in_stride = n;
+    p.pooled = pooled;
+    e = select_launch(p, raw, weight, idx, head_offsets, stage, ws, st);
+  } else {
+    float* ps = pooled ? pooled : static_cast<float*>(ws);
+    e = pool_launch(raw, L, H_kv, n, p.n_cand, r, ps, st);
+    if (e == hipSuccess)
+      e = select_launch(p, ps, weight, idx, head_offsets, stage, static_cast<char*>(ws) + pooled_ws,
+                        st);
+  }
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }
 

@@ -60,7 +60,21 @@ struct SelectPlan {
   const int32_t* budgets = nullptr;   // per-head budgets [L][H] (device), or null
   int64_t stride = 0;     // layer row of idx when budgets are given
   float alpha = 0.f;
+  // On-chip max-pooling (resident segments of one head only): the scores
+  // are raw rows `in_stride` floats apart, pooled with radius pool_r over
+  // each segment's candidates; the pooled scores go to `pooled` if given.
+  int pool_r = 0;
+  int64_t in_stride = 0;  // 0: seg_len
+  float* pooled = nullptr;
 };
+
+// Whether select_launch pools on chip for this plan (else the caller pools).
+bool select_pools_on_chip(const SelectPlan& p, int pool_r);
+
+// scores[lh][j] = max raw[lh][t] over |t - j| <= r, 0 <= t < n_cand (raw
+// rows n apart); scores == nullptr: nothing.
+hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r, float* scores,
+                       hipStream_t st);
 
 size_t select_ws_bytes(const SelectPlan& p);
 int32_t select_plan(bool two_stage, int32_t L, int32_t H_kv, int32_t n, int32_t W, int64_t budget,

@@ -619,6 +619,7 @@ hipError_t combine_launch(const float2* part, int L, int H, int R, int splits, f
 
 hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r, float* scores,
                        hipStream_t st) {
+  if (!scores) return hipSuccess;   // raw scores only
   hipLaunchKernelGGL(k_pool, dim3((n_cand + kPoolSpan - 1) / kPoolSpan, L * H), dim3(256), 0,
                      st, raw, n, n_cand, r, scores);
   return hipGetLastError();

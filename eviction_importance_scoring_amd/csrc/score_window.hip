@@ -531,8 +531,6 @@ void window_plan(const ScorePlan& p, WindowLayout* o) {
 
 hipError_t combine_launch(const float2* part, int L, int H, int R, int splits, float* stat,
                           hipStream_t st);
-hipError_t pool_launch(const float* raw, int L, int H, int n, int n_cand, int r, float* scores,
-                       hipStream_t st);
 
 hipError_t window_launch(const ScorePlan& p, const WindowLayout& o, const void* q, const void* k,
                          float* scores, float* raw, void* ws, hipStream_t st) {

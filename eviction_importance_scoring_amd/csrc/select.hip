@@ -50,18 +50,24 @@ constexpr int kKPT = 34;                              // keys a thread holds
 constexpr int kResidentMax = kKPT * kSelThreads;      // 34,816 candidates
 constexpr int kMaxGroups = 1024;             // heads per segment
 constexpr uint32_t kInfBits = 0xFF800000u;     // score bits of +inf
+constexpr int kMaxPoolR = 3;                 // on-chip max-pooling radius (width 7)
+constexpr int kStagePad = 4;                 // floats before a staged segment
 
 struct SelArgs {
-  const float* scores;
-  const float* weight;
+  const float* scores;      // segment s at scores + s * in_stride
+  const float* weight;      // segment s at weight + s * seg_len
   int32_t* idx;
   int32_t* head_offsets;
   uint8_t* stage;
   const int32_t* budgets;   // [L][H] or null
+  float* pooled;            // resident path with pool_r > 0: pooled scores out, or null
   uint32_t seg_len, n_cand, groups, W, n, H;
   uint32_t k, k1;
   int64_t budget, stride;
+  int64_t in_stride;
   int two_stage;
+  int staged;               // resident path: segments staged by 16-byte loads
+  int pool_r;               // resident path: max-pool radius applied on chip (0..kMaxPoolR)
   float score_norm, eps, alpha;
 };
 
@@ -144,6 +150,13 @@ __device__ __forceinline__ uint32_t score_bits(float x) {
   uint32_t b = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   b = x == 0.f ? 0x80000000u : b;             // -0 and +0 alike
   return x != x ? 0u : b;                     // NaN: below everything
+}
+
+// The score a key's bits stand for (the image of -0 gives +0, of NaN a
+// NaN): the inverse of score_bits wherever the keys' order can tell.
+__device__ __forceinline__ float bits_score(uint32_t b) {
+  const uint32_t u = (b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b;
+  return b == 0u ? __uint_as_float(0x7FC00000u) : __uint_as_float(u);
 }
 
 __device__ __forceinline__ uint64_t make_key(uint32_t bits, uint32_t f) {
@@ -348,7 +361,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t seg = blockIdx.x;
-  const float* sc = a.scores + seg * a.seg_len;
+  const float* sc = a.scores + seg * a.in_stride;
   const float* wt = a.weight ? a.weight + seg * a.seg_len : nullptr;
   const uint32_t len = a.seg_len;   // >= 1 (the API keeps W < n)
   const SegSpan sp = seg_span(a, seg);
@@ -359,15 +372,85 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
   const uint32_t nvw = __builtin_amdgcn_readfirstlane(nv);
   const uint32_t nvall = __builtin_amdgcn_readlane(nv, 63);
 
-  // every load in flight at once (one wait); each load instruction of a
-  // wave reads 256 contiguous bytes
   uint32_t kb[kKPT];
-  const uint32_t* sc32 = reinterpret_cast<const uint32_t*>(sc);
-  const uint32_t flast = len - 1u;   // loads past the end repeat the last candidate
+  if (a.staged) {
+    // The segment goes to LDS (over the histogram, which is not in use yet)
+    // with 16-byte direct-to-LDS loads, 1 KB a wave instruction: the host
+    // checks that the row is 16-byte aligned and that len rounded up to 4
+    // stays inside it. Stage index 4 + f holds candidate f.
+    float* stg = reinterpret_cast<float*>(smem_raw);
+    const uint32_t len4 = (len + 3u) & ~3u;
+#if defined(__HIP_DEVICE_COMPILE__)
+    {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(sc), 0, (int)(len4 * 4u), 0x00020000);
+      const uint32_t chunks = (len4 + 255u) / 256u;   // 1 KB each, <= kResidentMax / 256
+      for (uint32_t c = wave; c < chunks; c += kSelWaves)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(stg + kStagePad + c * 256u), 16,
+            c * 1024u + (uint32_t)lane * 16u, 0, 0, 0);
+    }
+#endif
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);   // vmcnt(0)
+    __syncthreads();
+    if (a.pool_r > 0) {
+      // max-pool over |t - f| <= r, 0 <= t < len: thread t pools the
+      // kKPT consecutive candidates from kKPT * t, reading r more on each
+      // side, then writes them back in place once every thread has read
+      auto pool = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        constexpr int NX = kKPT + 2 * R;
+        const int f0 = tid * kKPT;
+        float x[NX];
 #pragma unroll
-  for (int i = 0; i < kKPT; ++i)
-    kb[i] = (uint32_t)i < nvw ? __builtin_nontemporal_load(sc32 + min(cand(fbase, i), flast)) : 0u;
-  // the histogram starts clear (while the loads are in flight)
+        for (int j = 0; j < NX; ++j) {
+          const int t = f0 - R + j;
+          x[j] = (uint32_t)t < len ? stg[kStagePad + t] : -__builtin_inff();
+        }
+        // in place, ascending (each step reads only entries it has not
+        // rewritten yet): pairs x[j..j+1], then for R > 1 quads x[j..j+3];
+        // the window x[j..j+2R] is the union of two of them
+#pragma unroll
+        for (int j = 0; j + 1 < NX; ++j) x[j] = __builtin_fmaxf(x[j], x[j + 1]);
+        if constexpr (R > 1) {
+#pragma unroll
+          for (int j = 0; j + 3 < NX; ++j) x[j] = __builtin_fmaxf(x[j], x[j + 2]);
+        }
+        constexpr int kSecond = R == 3 ? 3 : 1;   // R = 1: pairs j, j+1; 2: quads j, j+1; 3: quads j, j+3
+#pragma unroll
+        for (int j = 0; j < kKPT; ++j) x[j] = __builtin_fmaxf(x[j], x[j + kSecond]);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kKPT; ++j)
+          if ((uint32_t)(f0 + j) < len) stg[kStagePad + f0 + j] = x[j];
+        __syncthreads();
+      };
+      if (a.pool_r == 1) pool(std::integral_constant<int, 1>{});
+      else if (a.pool_r == 2) pool(std::integral_constant<int, 2>{});
+      else pool(std::integral_constant<int, 3>{});
+    }
+    const uint32_t flast = len - 1u;
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i)
+      kb[i] = (uint32_t)i < nvw ? __float_as_uint(stg[kStagePad + min(cand(fbase, i), flast)]) : 0u;
+    if (a.pooled) {
+      float* po = a.pooled + seg * a.seg_len;
+#pragma unroll
+      for (int i = 0; i < kKPT; ++i)
+        if ((uint32_t)i < nv) po[cand(fbase, i)] = __uint_as_float(kb[i]);
+    }
+    __syncthreads();   // the stage is read: the histogram may take its place
+  } else {
+    // every load in flight at once (one wait); each load instruction of a
+    // wave reads 256 contiguous bytes
+    const uint32_t* sc32 = reinterpret_cast<const uint32_t*>(sc);
+    const uint32_t flast = len - 1u;   // loads past the end repeat the last candidate
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i)
+      kb[i] = (uint32_t)i < nvw ? __builtin_nontemporal_load(sc32 + min(cand(fbase, i), flast)) : 0u;
+  }
+  // the histogram starts clear
   {
     u32x4* h4 = reinterpret_cast<u32x4*>(sm.hist);
     for (int q = tid; q < kHistCopies * kCopyWords / 4; q += kSelThreads) h4[q] = u32x4{0u, 0u, 0u, 0u};
@@ -393,13 +476,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
     constexpr int kParts = 4, kHalf = (kKPT + kParts - 1) / kParts;
 #pragma unroll
     for (int h = 0; h < kParts; ++h) {
-      float sv[kHalf], wv[kHalf];
+      // the score is read back from its key bits (the pooled scores of the
+      // on-chip pooling exist nowhere else); every score the order can
+      // tell apart comes back exactly, and stage2_bits maps the rest (-0
+      // and +0, the NaNs) to the same key
+      float wv[kHalf];
 #pragma unroll
       for (int u = 0; u < kHalf; ++u) {
         const int i = h * kHalf + u;
         const uint32_t f = cand(fbase, i);
         const bool ok = i < kKPT && (uint32_t)i < nvs;
-        sv[u] = ok ? sc[f] : 0.f;
         wv[u] = ok ? wt[f] : 0.f;
       }
 #pragma unroll
@@ -408,7 +494,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
         if (i < kKPT)
           kb[i] = (uint32_t)i >= nvs ? 0u
                   : key_ge(kb[i], cand(fbase, i), c1.shift, c1.prefix)
-                      ? kInfBits : stage2_bits(sv[u], wv[u], a.score_norm, a.eps);
+                      ? kInfBits : stage2_bits(bits_score(kb[i]), wv[u], a.score_norm, a.eps);
       }
     }
   }
@@ -1128,7 +1214,20 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   return hipGetLastError();
 }
 
-static_assert(sizeof(SelShared) <= 160 * 1024, "the shared state fits the CU's LDS");
+constexpr size_t kStageBytes = (kStagePad + (size_t)kResidentMax) * sizeof(float);
+static_assert(sizeof(SelShared) <= 160 * 1024 && kStageBytes <= 160 * 1024,
+              "the shared state and a staged segment fit the CU's LDS");
+
+// A resident segment is staged with 16-byte loads when its rows are
+// 16-byte aligned (the base is: every tensor is) and its length rounded up
+// to 4 stays inside its row.
+static bool stageable(const SelectPlan& p, int64_t in_stride) {
+  return p.seg_len <= kResidentMax && in_stride % 4 == 0 && ((p.seg_len + 3) & ~int64_t(3)) <= in_stride;
+}
+
+bool select_pools_on_chip(const SelectPlan& p, int pool_r) {
+  return !p.adaptive && !p.budgets && pool_r >= 0 && pool_r <= kMaxPoolR && stageable(p, p.n);
+}
 
 size_t select_ws_bytes(const SelectPlan& p) { return use_multi(p) ? msel_layout(p).bytes : 0; }
 
@@ -1157,8 +1256,16 @@ hipError_t select_launch(const SelectPlan& p, const float* scores, const float* 
   a.stride = p.stride;
   a.alpha = p.alpha;
   if (p.budgets) a.head_offsets = head_offsets;
+  a.in_stride = p.in_stride > 0 ? p.in_stride : p.seg_len;
+  a.pool_r = p.pool_r;
+  a.pooled = p.pooled;
+  // raw rows (a stride other than seg_len), on-chip pooling and the pooled
+  // output exist on the staged resident path only
+  if ((a.in_stride != p.seg_len || p.pool_r > 0 || p.pooled) && !select_pools_on_chip(p, p.pool_r))
+    return hipErrorInvalidValue;
   if (use_multi(p)) return msel_launch(p, scores, weight, idx, head_offsets, stage, ws, st);
-  const size_t lds = sizeof(SelShared);
+  a.staged = stageable(p, a.in_stride) ? 1 : 0;
+  const size_t lds = a.staged ? std::max(sizeof(SelShared), kStageBytes) : sizeof(SelShared);
   const hipError_t e =
       hipFuncSetAttribute((const void*)k_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

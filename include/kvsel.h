@@ -23,7 +23,7 @@
  *  - Every argument check runs before anything is launched: a call that
  *    returns non-zero has launched nothing and written nothing.
  *  - Workspace protocol (kvsel_score, kvsel_score_chunked,
- *    kvsel_value_weight, kvsel_select, kvsel_select_budgets,
+ *    kvsel_value_weight, kvsel_select, kvsel_select_pool, kvsel_select_budgets,
  *    kvsel_head_budgets, kvsel_anchor_select, kvsel_anchor_assign,
  *    kvsel_decode_attention): with ws == NULL the
  *    call stores the bytes it needs in *ws_bytes, returns KVSEL_OK and
@@ -94,7 +94,10 @@ enum {
  *   q      bf16 [L][H_kv*G][W][d]
  *   k      bf16 [L][H_kv][n][d]
  *   scores f32  [L][H_kv][n_cand]  pooled scores, n_cand = n-W (window)
- *                                  or n (external)
+ *                                  or n (external); may be NULL when raw is
+ *                                  given: then no pooling is done (the
+ *                                  raw-input selection kvsel_select_pool
+ *                                  pools itself)
  *   raw    f32  [L][H_kv][n]       optional (NULL): pre-pool aggregate over
  *                                  all n keys, window keys included
  *   scale  softmax temperature (the model's 1/sqrt(d)), > 0
@@ -266,6 +269,34 @@ int32_t kvsel_select(const float* scores, const float* weight,
                      float score_norm, float eps, float alpha,
                      int32_t* idx, int32_t* head_offsets, uint8_t* stage,
                      void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * kvsel_select_pool -- kvsel_select on scores it max-pools itself.
+ *
+ * The same selection as kvsel_score(..., pool, scores, raw, ...) followed
+ * by kvsel_select(scores, ...), from the raw aggregates alone: the keys
+ * are raw max-pooled with width `pool` over each head's candidate
+ * positions [0, n-W) (stride 1, centred, neighbours outside [0, n-W)
+ * ignored: [CriticalKV] §3.3, Algorithm 2, steps 4 and 6), then selected
+ * as kvsel_select selects. With a per-head budget (adaptive == 0),
+ * pool <= 7, n a multiple of 4 and n-W <= 34,816, each head's raw row is
+ * read once and pooled on chip: the pooled scores need not pass through
+ * memory. Otherwise the call pools into `pooled`, or its workspace, first.
+ *
+ *   raw     f32 [L][H_kv][n]      kvsel_score's raw output (window keys
+ *                                 included; they are not pooled)
+ *   pool    odd, 1 <= pool <= 65 (else KVSEL_ERR_ARG / _UNSUPPORTED)
+ *   pooled  f32 [L][H_kv][n-W]    optional (NULL): the pooled scores
+ *   weight, idx, head_offsets, stage and every other argument as in
+ *   kvsel_select; the results are those of kvsel_select on the pooled
+ *   scores, bit for bit. Needs a workspace (protocol above).
+ */
+int32_t kvsel_select_pool(const float* raw, const float* weight, int32_t pool,
+                          int32_t L, int32_t H_kv, int32_t n, int32_t W,
+                          int64_t budget, int32_t adaptive,
+                          float score_norm, float eps, float alpha,
+                          int32_t* idx, int32_t* head_offsets, uint8_t* stage,
+                          float* pooled, void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * kvsel_select_static -- kvsel_select without a workspace argument.

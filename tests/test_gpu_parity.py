@@ -213,6 +213,83 @@ def test_select_exact_on_same_fp32_scores(case):
             np.testing.assert_array_equal(offs[l], ro)
 
 
+POOL_SELECT_CASES = [
+    # (L, H, n, W, budget_frac, adaptive, two_stage, alpha, levels, pool)
+    # pooled on chip: per-head budget, pool <= 7, n % 4 == 0, n - W <= 34,816
+    (1, 2, 100, 8, 0.5, False, False, 0.5, 7, 7),
+    (2, 3, 1000, 7, 0.2, False, False, 0.5, 1000000, 7),    # n - W not a multiple of 4
+    (1, 2, 4096, 32, 0.3, False, False, 0.5, 9, 5),
+    (1, 3, 2048, 16, 0.4, False, False, 0.5, 11, 3),
+    (1, 2, 3000, 8, 0.3, False, False, 0.5, 5, 1),          # no pooling, raw rows n apart
+    (2, 2, 2000, 16, 0.3, False, True, 0.5, 30, 7),         # two-stage
+    (1, 2, 500, 4, 0.3, False, True, 0.0, 10, 7),
+    (1, 2, 500, 4, 0.3, False, True, 1.0, 10, 5),
+    (1, 1, 34848, 32, 0.25, False, False, 0.5, 1000, 7),    # the largest resident head
+    (1, 2, 64, 0, 0.5, False, False, 0.5, 3, 7),            # external: no window
+    (1, 2, 64, 32, 1.0, False, False, 0.5, 3, 7),           # keep everything
+    (1, 2, 64, 32, 0.5, False, False, 0.5, 3, 7),           # keep only the window
+    # pooled through memory first
+    (1, 2, 1001, 9, 0.3, False, False, 0.5, 50, 7),         # n % 4 != 0
+    (1, 2, 1000, 8, 0.3, False, False, 0.5, 50, 9),         # pool > 7
+    (1, 4, 3000, 32, 0.4, True, False, 0.5, 50, 7),         # adaptive
+    (1, 1, 50000, 32, 0.1, False, True, 0.5, 1000, 7),      # many workgroups
+]
+
+
+@pytest.mark.parametrize("case", POOL_SELECT_CASES,
+                         ids=lambda c: "L{}H{}n{}W{}b{}a{}t{}al{}lv{}p{}".format(*c))
+def test_select_pool_exact(case):
+    """kvsel_select_pool on raw scores: the oracle's max-pooling then its
+    selection, bit for bit; the window's raw values (made the largest) must
+    neither pool into a candidate nor be selected."""
+    L, H, n, W, frac, adaptive, two_stage, alpha, levels, pool = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    n_cand = n - W
+    raw = _quantised_scores(rng, (L, H, n), levels)
+    raw[..., n_cand:] = 5.0
+    wt = (rng.random((L, H, n_cand)).astype(np.float32) * 3 + 0.01) if two_stage else None
+    groups = H if adaptive else 1
+    budget = max(groups * W, int(np.floor(frac * groups * n)))
+    print(f"[gpu] kvsel_select_pool case={case} budget={budget}", flush=True)
+    idx, offs, stage, pooled = kv.kvsel_select_pool(
+        torch.from_numpy(raw).cuda(), n=n, W=W, budget=budget, pool=pool, adaptive=adaptive,
+        weight=None if wt is None else torch.from_numpy(wt).cuda(), score_norm=1.0 / 128,
+        eps=1e-4, alpha=alpha, return_stage=True, return_pooled=True)
+    torch.cuda.synchronize()
+    idx, stage, pooled = idx.cpu().numpy(), stage.cpu().numpy(), pooled.cpu().numpy()
+    offs = None if offs is None else offs.cpu().numpy()
+    ref_pooled = oracle.maxpool(raw.astype(np.float64), n_cand, pool)
+    np.testing.assert_array_equal(pooled, ref_pooled.astype(np.float32))
+    for l in range(L):
+        ri, ro, rs = oracle.select_layer(ref_pooled[l], budget, W, n, adaptive=adaptive,
+                                         weight=None if wt is None else wt[l].astype(np.float64),
+                                         alpha=float(np.float32(alpha)), score_norm=float(np.float32(1 / 128)),
+                                         eps=float(np.float32(1e-4)), dtype=np.float32)
+        np.testing.assert_array_equal(idx[l], ri)
+        np.testing.assert_array_equal(stage[l], rs)
+        if adaptive:
+            np.testing.assert_array_equal(offs[l], ro)
+
+
+def test_select_pool_matches_score_then_select():
+    """Raw-only scoring followed by kvsel_select_pool gives the same kept
+    entries as pooled scoring followed by kvsel_select, on real scores."""
+    wl = _wl(L=2, H_kv=2, n=2048, W=32)
+    data = gen(wl, seed=3)
+    q, k = to_dev(data["q"]), to_dev(data["k"])
+    scores, raw = kv.kvsel_score(q, k, G=wl.G, pool=wl.pool, return_raw=True)
+    none, raw2 = kv.kvsel_score(q, k, G=wl.G, pool=wl.pool, pooled=False)
+    assert none is None
+    budget = 700
+    idx, _, _ = kv.kvsel_select(scores, n=wl.n, W=wl.W, budget=budget)
+    idx2, _, _, pooled = kv.kvsel_select_pool(raw2, n=wl.n, W=wl.W, budget=budget, pool=wl.pool,
+                                              return_pooled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(raw, raw2)
+    assert torch.equal(pooled, scores)
+    assert torch.equal(idx, idx2)
+
+
 @pytest.mark.parametrize("name", ["f32_tie", "f32_even", "f32_fma"])
 @pytest.mark.parametrize("pad", [0, 40000])
 def test_select_two_stage_f32_hand_examples(name, pad):
