@@ -84,6 +84,14 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x of the lane 32 away (lane l ^ 32) by one v_permlane32_swap, which
+// swaps the upper half of its first operand with the lower half of its
+// second: no LDS round trip (a ds_bpermute's) on the way.
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // Merge two (max, sum-of-exp2) pairs; max may be -inf with sum 0.

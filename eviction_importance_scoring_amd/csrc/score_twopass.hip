@@ -328,7 +328,7 @@ __global__ __launch_bounds__(gStatsBlock, 2) void k_gen_stats(const __bf16* __re
   // the other lane half holds the other 16 keys of every 32-key block
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const float m2 = __shfl_xor(m[nt], 32), s2 = __shfl_xor(s[nt], 32);
+    const float m2 = lane_xor32(m[nt]), s2 = lane_xor32(s[nt]);
     lse_merge(m[nt], s[nt], m2, s2);
     const int row = row0 + nt * 32 + col;
     if (hf == 0 && row < R)
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(gColBlock, 2) void k_gen_colagg(const __bf16* __res
   // the other lane half holds the other 16 rows of every 32-row block
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const float o = __shfl_xor(agg[nt], 32);
+    const float o = lane_xor32(agg[nt]);
     // LOGIT: alpha is the plain scale and the max is the logit itself
     const float tot = LOGIT ? __builtin_fmaxf(agg[nt], o) * alpha
                     : MAXAGG ? fast_exp2(__builtin_fmaxf(agg[nt], o) * alpha) : agg[nt] + o;

@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     fold_all(A, t - 1);
   }
   // the other lane half saw the other 16 keys of every 32-key sub-tile
-  const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(s, 32);
+  const float m2 = lane_xor32(m), s2 = lane_xor32(s);
   lse_merge(m, s, m2, s2);
   if (hf == 0 && row < R) part[(lh * blocks + b) * (size_t)R + row] = make_float2(m, s);
 }
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   auto fold_end = [&](const float (&pa)[kSub], int tt) {
 #pragma unroll
     for (int nt = 0; nt < kSub; ++nt) {
-      const float o = __shfl_xor(pa[nt], 32);
+      const float o = lane_xor32(pa[nt]);
       if (hf == 0)
         sm.colbuf[tt & 1][wave][nt * 32 + col] = MAXAGG ? __builtin_fmaxf(pa[nt], o) : pa[nt] + o;
     }

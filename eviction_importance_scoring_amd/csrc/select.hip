@@ -750,7 +750,7 @@ __device__ __forceinline__ uint32_t msel_bits(const MselArgs& a, const SegState&
                                               float w, bool stage2, uint32_t f) {
   const uint32_t b = score_bits(s);
   if (!stage2) return b;
-  return (make_key(b, f) >> st.s1) >= st.p1 ? kInfBits : stage2_bits(s, w, a.score_norm, a.eps);
+  return key_ge(b, f, st.s1, st.p1) ? kInfBits : stage2_bits(s, w, a.score_norm, a.eps);
 }
 
 // chunk c of a segment: [begin, end) in flat candidate indices
@@ -762,19 +762,48 @@ __device__ __forceinline__ void msel_chunk(const MselArgs& a, uint32_t c, uint32
   end = min(begin + (uint32_t)kChunk, (g + 1) * a.n_cand);
 }
 
-// The thread's kPerThread candidates f = begin + i * kMThreads + tid (in
-// range: f < end; coalesced), all loads issued before the first is used;
-// out-of-range slots read 0.
+// Candidate i of the thread in a chunk starting at `begin`: f = begin +
+// msel_e<VEC>(i). VEC (every chunk 16-byte aligned and a multiple of 4
+// long: n_cand % 4 == 0): four consecutive candidates a 16-byte load,
+// 1 KB a wave; else one a 4-byte load. Either way a wave's loads are
+// contiguous.
+template <bool VEC>
+__device__ __forceinline__ uint32_t msel_e(int i) {
+  if constexpr (VEC)
+    return (uint32_t)(i >> 2) * (4u * kMThreads) + 4u * threadIdx.x + (uint32_t)(i & 3);
+  else
+    return (uint32_t)i * kMThreads + threadIdx.x;
+}
+
+// The thread's kPerThread candidates (in range: f < end), all loads
+// issued before the first is used; out-of-range slots read 0.
+template <bool VEC>
 __device__ __forceinline__ void msel_load(const MselArgs& a, uint32_t seg, uint32_t begin,
                                           uint32_t end, bool stage2, float (&s)[kPerThread],
                                           float (&w)[kPerThread]) {
   const float* sc = a.scores + (size_t)seg * a.seg_len;
   const float* wt = a.weight ? a.weight + (size_t)seg * a.seg_len : nullptr;
+  if constexpr (VEC) {
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t f = begin + i * kMThreads + threadIdx.x;
-    s[i] = f < end ? sc[f] : 0.f;
-    w[i] = (stage2 && f < end) ? wt[f] : 0.f;
+    for (int u = 0; u < kPerThread / 4; ++u) {
+      const uint32_t f = begin + msel_e<true>(4 * u);
+      const bool in = f < end;   // the chunk's length is a multiple of 4
+      const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 x = in ? *reinterpret_cast<const u32x4*>(sc + f) : zero;
+      const u32x4 y = (stage2 && in) ? *reinterpret_cast<const u32x4*>(wt + f) : zero;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s[4 * u + c] = __uint_as_float(x[c]);
+        w[4 * u + c] = __uint_as_float(y[c]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const uint32_t f = begin + msel_e<false>(i);
+      s[i] = f < end ? sc[f] : 0.f;
+      w[i] = (stage2 && f < end) ? wt[f] : 0.f;
+    }
   }
 }
 
@@ -816,7 +845,7 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2)
 }
 
 // grid chunks*segments (1-D), block 256
-template <int COPIES>
+template <int COPIES, bool VEC>
 __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2) {
   __shared__ uint32_t hist[COPIES][kBins];
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
@@ -827,19 +856,36 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
   float s[kPerThread], w[kPerThread];
-  msel_load(a, seg, begin, end, stage2 != 0, s, w);
+  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
 #pragma unroll
   for (int cp = 0; cp < COPIES; ++cp)
     for (int b = tid; b < nb; b += kMThreads) hist[cp][b] = 0;
   __syncthreads();
   uint32_t* hc = hist[tid & (COPIES - 1)];
+  // 32-bit arithmetic on key = (bits << 31) | (2^31 - 1 - f), as in the
+  // resident select
+  const uint32_t mask = (uint32_t)nb - 1u;
+  if (shift - wdt >= 31) {
+    // the digit lies in the score bits: keys in [lo, lo + 2^sh) match
+    const uint32_t sh = shift - 31, dsh = shift - wdt - 31;
+    const uint32_t lo = sh >= 32 ? 0u : (uint32_t)st.prefix << sh;
+    const uint32_t span_m1 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t f = begin + i * kMThreads + tid;
-    if (f < end) {
-      const uint64_t key = make_key(msel_bits(a, st, s[i], w[i], stage2 != 0, f), f);
-      if ((key >> shift) == st.prefix)
-        atomicAdd(&hc[(uint32_t)(key >> (shift - wdt)) & (nb - 1)], 1u);
+    for (int i = 0; i < kPerThread; ++i) {
+      const uint32_t f = begin + msel_e<VEC>(i);
+      const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f);
+      if (f < end && b - lo <= span_m1) atomicAdd(&hc[(b >> dsh) & mask], 1u);
+    }
+  } else {
+    // the digit lies in the index bits: the score bits are all fixed
+    const uint32_t pb = (uint32_t)(st.prefix >> (31 - shift));
+    const uint32_t pi = (uint32_t)st.prefix & ((1u << (31 - shift)) - 1u);
+    const uint32_t ish = (uint32_t)shift, dsh = (uint32_t)(shift - wdt);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const uint32_t f = begin + msel_e<VEC>(i);
+      const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f), ix = 0x7FFFFFFFu - f;
+      if (f < end && b == pb && (ix >> ish) == pi) atomicAdd(&hc[(ix >> dsh) & mask], 1u);
     }
   }
   __syncthreads();
@@ -917,13 +963,12 @@ __global__ __launch_bounds__(kMThreads) void k_msel_pick(MselArgs a) {
 // the first `need` (index order) are members.
 __device__ __forceinline__ void msel_class(const SegState& st, uint32_t bits, uint32_t f,
                                            bool& above, bool& eq) {
-  const uint64_t top = make_key(bits, f) >> st.shift;
   if (st.done) {
-    above = top >= st.prefix;
+    above = key_ge(bits, f, st.shift, st.prefix);
     eq = false;
-  } else {
-    above = top > st.prefix;
-    eq = top == st.prefix;
+  } else {   // shift == 31: the prefix is the bucket's score bits
+    above = bits > (uint32_t)st.prefix;
+    eq = bits == (uint32_t)st.prefix;
   }
 }
 
@@ -1022,6 +1067,7 @@ __global__ __launch_bounds__(kMThreads) void k_msel_offsets(MselArgs a) {
 }
 
 // grid chunks*segments, block 256: per chunk, entries above the bucket and in it
+template <bool VEC>
 __global__ __launch_bounds__(kMThreads) void k_msel_count(MselArgs a, int stage2) {
   __shared__ uint32_t sbuf[kMThreads / 64];
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
@@ -1030,11 +1076,11 @@ __global__ __launch_bounds__(kMThreads) void k_msel_count(MselArgs a, int stage2
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
   float s[kPerThread], w[kPerThread];
-  msel_load(a, seg, begin, end, stage2 != 0, s, w);
+  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
   uint32_t na = 0, ne = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t f = begin + i * kMThreads + tid;
+    const uint32_t f = begin + msel_e<VEC>(i);
     if (f < end) {
       bool above, eq;
       msel_class(st, msel_bits(a, st, s[i], w[i], stage2 != 0, f), f, above, eq);
@@ -1061,6 +1107,7 @@ __device__ __forceinline__ uint32_t emit_slot(uint32_t e) { return e + (e >> 5);
 // give each bucket entry its tie rank and each member its rank, in index
 // order. The chunk's members take consecutive output slots: they are
 // staged by rank in LDS and stored with coalesced writes.
+template <bool VEC>
 __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2) {
   __shared__ uint32_t bits[kChunk + kChunk / 32];
   __shared__ uint32_t sbuf[kMThreads / 64];
@@ -1072,10 +1119,10 @@ __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2)
   msel_chunk(a, c, g, begin, end);
   {
     float s[kPerThread], w[kPerThread];
-    msel_load(a, seg, begin, end, stage2 != 0, s, w);
+    msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const uint32_t e = i * kMThreads + tid;
+      const uint32_t e = msel_e<VEC>(i);
       const uint32_t f = begin + e;
       bits[emit_slot(e)] = f < end ? msel_bits(a, st, s[i], w[i], stage2 != 0, f) : 0u;
     }
@@ -1194,23 +1241,36 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   // the call can be captured in a graph); each pick clears what it read
   const dim3 gc((unsigned)blocks), gp(p.segments);
   const int stages = p.two_stage ? 2 : 1;
+  // 16-byte loads when every chunk starts 16-byte aligned and is a
+  // multiple of 4 long (scores and weights are 16-byte aligned)
+  const bool vec = p.n_cand % 4 == 0;
   for (int stg = 0; stg < stages; ++stg) {
     const int stage2 = stg == 1 ? 1 : 0;
     // the final stage stops after the score bits (ties split in emission)
     const int rounds = stg + 1 < stages ? 6 : 3;
     hipLaunchKernelGGL(k_msel_init, gp, dim3(kMThreads), 0, st, a, stage2);
     for (int r = 0; r < rounds; ++r) {
-      if (r == 0)
-        hipLaunchKernelGGL(k_msel_hist<kMCopies>, gc, dim3(kMThreads), 0, st, a, stage2);
+      if (r == 0 && vec)
+        hipLaunchKernelGGL((k_msel_hist<kMCopies, true>), gc, dim3(kMThreads), 0, st, a, stage2);
+      else if (r == 0)
+        hipLaunchKernelGGL((k_msel_hist<kMCopies, false>), gc, dim3(kMThreads), 0, st, a, stage2);
+      else if (vec)
+        hipLaunchKernelGGL((k_msel_hist<1, true>), gc, dim3(kMThreads), 0, st, a, stage2);
       else
-        hipLaunchKernelGGL(k_msel_hist<1>, gc, dim3(kMThreads), 0, st, a, stage2);
+        hipLaunchKernelGGL((k_msel_hist<1, false>), gc, dim3(kMThreads), 0, st, a, stage2);
       hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
     }
   }
   const int final2 = p.two_stage ? 1 : 0;
-  hipLaunchKernelGGL(k_msel_count, gc, dim3(kMThreads), 0, st, a, final2);
+  if (vec)
+    hipLaunchKernelGGL(k_msel_count<true>, gc, dim3(kMThreads), 0, st, a, final2);
+  else
+    hipLaunchKernelGGL(k_msel_count<false>, gc, dim3(kMThreads), 0, st, a, final2);
   hipLaunchKernelGGL(k_msel_offsets, gp, dim3(kMThreads), 0, st, a);
-  hipLaunchKernelGGL(k_msel_emit, gc, dim3(kMThreads), 0, st, a, final2);
+  if (vec)
+    hipLaunchKernelGGL(k_msel_emit<true>, gc, dim3(kMThreads), 0, st, a, final2);
+  else
+    hipLaunchKernelGGL(k_msel_emit<false>, gc, dim3(kMThreads), 0, st, a, final2);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ constexpr int vBlock = vWaves * 64;                    // keys per workgroup
 using VLoader = RingLoader<vWaves>;
 
 // 1-D grid of key_blocks * H * L workgroups, block vBlock.
-__global__ __launch_bounds__(vBlock, 2) void k_value_weight(const __bf16* __restrict__ v,
+__global__ __launch_bounds__(vBlock, 3) void k_value_weight(const __bf16* __restrict__ v,
                                                       const __bf16* __restrict__ w_o,
                                                       int H, int G, int n, int D, int n_cand,
                                                       int key_blocks,
@@ -105,60 +105,27 @@ __global__ __launch_bounds__(vBlock, 2) void k_value_weight(const __bf16* __rest
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
   };
-  // tile t into cur while tile t-1 (prev) is folded; per-tile partial sums
-  // keep the fp32 additions short
-  auto step = [&](int t, f32x16 (&cur)[2][2], f32x16 (&prev)[2][2]) {
+  // tile t: its MFMAs, then its |.| fold (per-tile partial sums keep the
+  // fp32 additions short). One accumulator set: three workgroups per CU
+  // fit (<= 168 registers), and the other waves' MFMAs cover a wave's fold.
+  f32x16 acc[2][2];
+  for (int t = 0; t < ntiles; ++t) {
     const unsigned char* slot = begin_tile(t);
-    if (!any_key) return;
+    if (!any_key) continue;
     const bool half = half_tile(t);
-    float ps[2] = {0.f, 0.f};
-    zero_acc(cur);
+    zero_acc(acc);
     bf16x8 a[2][2];
     read(slot, 0, half, a[0]);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       if (st + 1 < 8) read(slot, st + 1, half, a[(st + 1) & 1]);
-      tile_step(a[st & 1], vop, st, cur);
-      fold_part(prev, st, ps);
-      __builtin_amdgcn_sched_barrier(0);
+      tile_step(a[st & 1], vop, st, acc);
     }
-    asm volatile("" : "+v"(ps[0]), "+v"(ps[1]));
-    part[0] += ps[0];
-    part[1] += ps[1];
-  };
-  auto fold_all = [&](const f32x16 (&acc)[2][2]) {
     float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; ++c) fold_part(acc, c, ps);
     part[0] += ps[0];
     part[1] += ps[1];
-  };
-
-  f32x16 A[2][2], B[2][2];
-  {
-    const unsigned char* slot = begin_tile(0);
-    if (any_key) {
-      const bool half = half_tile(0);
-      zero_acc(A);
-      bf16x8 a[2][2];
-      read(slot, 0, half, a[0]);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (st + 1 < 8) read(slot, st + 1, half, a[(st + 1) & 1]);
-        tile_step(a[st & 1], vop, st, A);
-      }
-    }
-  }
-  int t = 1;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, B, A);
-    step(t + 1, A, B);
-  }
-  if (t < ntiles) {
-    step(t, B, A);
-    if (any_key) fold_all(B);
-  } else if (any_key) {
-    fold_all(A);
   }
   gen_wait<0>();   // repeats of the last tile (fewer tiles than the prologue's)
   const float inv_g = 1.0f / (float)G;
