@@ -87,7 +87,7 @@ constexpr int gStatsWaves = 4;                       // pass-1 waves per workgro
 constexpr int gStatsBlock = gStatsWaves * 64;         // pass-1 rows per workgroup
 using StatsLoader = RingLoader<gStatsWaves>;
 template <bool CAUSAL, bool SELF = false>
-__global__ __launch_bounds__(gStatsBlock, 2) void k_gen_stats(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(gStatsBlock, 3) void k_gen_stats(const __bf16* __restrict__ q,
                                                    const __bf16* __restrict__ k, int H, int R,
                                                    int W, KeyMap km, float alpha, int row_blocks,
                                                    int splits, int kps, int sp_off, int sp_stride,
@@ -194,13 +194,17 @@ __global__ __launch_bounds__(gStatsBlock, 2) void k_gen_stats(const __bf16* __re
     }
     const int kt = j0 + t * gTile;
     if (kt + gTile - 1 <= open_end && kt + gTile <= j1) return;
+    // opaque key base: keeps the 16 row offsets from being hoisted out of
+    // the tile loop into registers (this branch runs on edge tiles only)
+    int kbase = kt + acc_row(0, lane);
+    asm volatile("" : "+v"(kbase));
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kt + mt * 32 + acc_row(i, lane);
+          const int key = kbase + mt * 32 + (acc_row(i, 0) - acc_row(0, 0));
           if (!(key <= last[nt] && key < j1)) acc[mt][nt][i] = neg_inf();
         }
   };
@@ -288,39 +292,36 @@ __global__ __launch_bounds__(gStatsBlock, 2) void k_gen_stats(const __bf16* __re
     asm volatile("" : "+v"(ps[0]), "+v"(ps[1]));
     fold_end(prev, ps);
   };
-  // fold a tile with no MFMA work beside it
+  // fold a tile with no MFMA work beside it (one part at a time: fewer
+  // exponentials in flight, fewer registers)
   auto fold_all = [&](f32x16 (&acc)[2][2], int t) {
     mask(acc, t);
     float ps[2] = {0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) fold_part(acc, c, ps);
+    for (int c = 0; c < 8; ++c) {
+      fold_part(acc, c, ps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     fold_end(acc, ps);
   };
 
-  f32x16 A[2][2], B[2][2];
-  {
-    const unsigned char* slot = begin_tile(0);
-    if (active) {
-      zero_acc(A);
-      bf16x8 a[2][2];
-      read_step(slot, col, hf, 0, a[0]);
+  // tile t: its MFMAs, then its fold. One accumulator set: three 4-wave
+  // workgroups per CU fit, and the other waves' MFMAs cover a wave's
+  // exponentials (the fold order, and so the sums, are those of the
+  // pipelined step above, which is kept for reference)
+  (void)step;
+  f32x16 acc[2][2];
+  for (int t = 0; t < ntiles; ++t) {
+    const unsigned char* slot = begin_tile(t);
+    if (!active) continue;
+    zero_acc(acc);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
-        tile_step(a[st & 1], qb, st, A);
-      }
+    for (int st = 0; st < 8; ++st) {
+      bf16x8 a[2];
+      read_step(slot, col, hf, st, a);
+      tile_step(a, qb, st, acc);
     }
-  }
-  int t = 1;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, B, A);
-    step(t + 1, A, B);
-  }
-  if (t < ntiles) {
-    step(t, B, A);
-    if (active) fold_all(B, t);
-  } else if (active) {
-    fold_all(A, t - 1);
+    fold_all(acc, t);
   }
   // with fewer tiles than the prologue's loads, repeats of the last tile may
   // still be landing in LDS: let them finish before the workgroup ends
