@@ -402,7 +402,7 @@ constexpr int gColWaves = 4;                          // pass-2 waves per workgr
 constexpr int gColBlock = gColWaves * 64;             // pass-2 keys per workgroup
 using ColLoader = RingLoader<gColWaves>;
 template <bool CAUSAL, bool MAXAGG, bool LOGIT = false>
-__global__ __launch_bounds__(gColBlock, 2) void k_gen_colagg(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(gColBlock, 3) void k_gen_colagg(const __bf16* __restrict__ q,
                                                     const __bf16* __restrict__ k, int H, int R,
                                                     int W, KeyMap km, float alpha, int key_blocks,
                                                     const float* __restrict__ stat,
@@ -530,30 +530,23 @@ __global__ __launch_bounds__(gColBlock, 2) void k_gen_colagg(const __bf16* __res
     for (int c = 0; c < 8; ++c) fold_part(acc, c, agg);
   };
 
-  f32x16 A[2][2], B[2][2];
-  {
-    const unsigned char* slot = begin_tile(0);
-    if (any_key) {
-      init_acc(slot, A);
-      bf16x8 a[2][2];
-      read_step(slot, col, hf, 0, a[0]);
+  // tile t: its MFMAs, then its fold (in the order of the pipelined step
+  // above, kept for reference). One accumulator set: three 4-wave
+  // workgroups per CU fit, and the other waves' MFMAs cover a wave's fold.
+  (void)step;
+  f32x16 acc[2][2];
+  for (int t = 0; t < ntiles; ++t) {
+    const unsigned char* slot = begin_tile(t);
+    if (!any_key) continue;
+    init_acc(slot, acc);
+    bf16x8 a[2][2];
+    read_step(slot, col, hf, 0, a[0]);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
-        tile_step(a[st & 1], kop, st, A);
-      }
+    for (int st = 0; st < 8; ++st) {
+      if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
+      tile_step(a[st & 1], kop, st, acc);
     }
-  }
-  int t = 1;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, B, A);
-    step(t + 1, A, B);
-  }
-  if (t < ntiles) {
-    step(t, B, A);
-    if (any_key) fold_all(B, t);
-  } else if (any_key) {
-    fold_all(A, t - 1);
+    fold_all(acc, t);
   }
   gen_wait<0>();   // repeats of the last tile (fewer tiles than the prologue's)
   // the other lane half holds the other 16 rows of every 32-row block
