@@ -181,6 +181,9 @@ SELECT_CASES = [
     (1, 2, 64, 32, 1.0, False, False, 0.5, 3),            # keep everything
     (1, 2, 64, 32, 0.5, False, False, 0.5, 3),            # keep only the window
     (1, 2, 64, 0, 0.0, False, False, 0.5, 3),             # external: nothing kept
+    # many workgroups with n - W not a multiple of 4 (4-byte loads)
+    (1, 1, 40001, 0, 0.2, False, False, 0.5, 100),
+    (1, 3, 15001, 3, 0.3, True, True, 0.5, 30),
 ]
 
 
