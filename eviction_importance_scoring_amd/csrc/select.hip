@@ -715,8 +715,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
 //
 // Every thread issues all of its kPerThread loads before it uses one: a
 // chunk's workgroup then waits for memory once.
-constexpr int kMThreads = 256;
-constexpr int kChunk = 8192;                       // candidates per chunk
+constexpr int kMThreads = 512;
+constexpr int kChunk = 16384;                      // candidates per chunk
 constexpr int kPerThread = kChunk / kMThreads;     // 32
 constexpr int kMCopies = 4;                        // LDS histogram copies, first digit
 

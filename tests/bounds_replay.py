@@ -193,7 +193,7 @@ def decode_sizes(L, H, G, kept, offs):
 
 # -------------------------------------------------------------- selection ----
 
-SEL_THREADS, M_THREADS, K_CHUNK, K_BINS, K_MAX_GROUPS = 1024, 256, 8192, 2048, 1024
+SEL_THREADS, M_THREADS, K_CHUNK, K_BINS, K_MAX_GROUPS = 1024, 512, 16384, 2048, 1024
 
 
 def _clamp_budget(b, W, n):
