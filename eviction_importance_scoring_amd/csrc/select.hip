@@ -146,10 +146,10 @@ struct alignas(16) SelShared {
 
 // Order-preserving 32-bit image of a score: larger value, larger bits.
 __device__ __forceinline__ uint32_t score_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  uint32_t b = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  b = x == 0.f ? 0x80000000u : b;             // -0 and +0 alike
-  return x != x ? 0u : b;                     // NaN: below everything
+  const float y = x + 0.f;                    // -0 becomes +0 (denormals are kept)
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t b = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // ~u, or u | 2^31
+  return y == y ? b : 0u;                     // NaN: below everything
 }
 
 // The score a key's bits stand for (the image of -0 gives +0, of NaN a
