@@ -229,9 +229,6 @@ def main():
     weight = (torch.empty((wl.L, wl.H_kv, wl.n_cand), dtype=torch.float32, device=dev)
               if wl.value_weight else None)
     ws_s = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-    if not wl.chunk:
-        _, _ = kv.kvsel_score(q, k, G=wl.G, q_mode=mode, agg=agg, scale=wl.scale, pool=wl.pool,
-                              scores=scores)  # sizes the workspace once
     ev = lambda: torch.cuda.Event(enable_timing=True)
     l2 = wl.value_weight and wl.value_norm == "l2"
     factor, ms_factor = None, None
