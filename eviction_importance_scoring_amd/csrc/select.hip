@@ -379,9 +379,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
     // checks that the row is 16-byte aligned and that len rounded up to 4
     // stays inside it. Stage index 4 + f holds candidate f.
     float* stg = reinterpret_cast<float*>(smem_raw);
-    const uint32_t len4 = (len + 3u) & ~3u;
 #if defined(__HIP_DEVICE_COMPILE__)
     {
+      const uint32_t len4 = (len + 3u) & ~3u;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(sc), 0, (int)(len4 * 4u), 0x00020000);
       const uint32_t chunks = (len4 + 255u) / 256u;   // 1 KB each, <= kResidentMax / 256
@@ -685,33 +685,46 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
 //
 // Segments longer than kResidentMax (a whole layer when adaptive, or very
 // long heads) would leave most CUs idle with one workgroup each, so they
-// run the same MSD radix select spread over chunks of kChunk candidates:
-//   k_msel_init    per segment: state (prefix, shift, need) for a stage
+// are spread over chunks of kChunk candidates. Each stage of the selection
+// runs:
+//   k_msel_init    per segment: state (prefix, shift, need) for the stage
 //                  (and, for the first, a cleared global histogram)
-//   k_msel_hist    per chunk: histogram of the current digit among the
-//                  candidates that match the prefix (in LDS: four copies on
-//                  a stage's first digit, where keys crowd a few bins; one
-//                  copy after it, where few keys match the prefix),
-//                  added to the segment's global histogram
-//   k_msel_pick    per segment: the bin holding the need-th largest key
-//                  (bins read in descending order), the next state, and a
-//                  cleared histogram for the next digit
-// A segment whose bucket is taken whole is done and later rounds return at
-// once. The final stage runs only the three rounds of the 31 score bits:
-// if the last bucket (keys with equal score bits b) is not taken whole,
-// its first `need` entries in index order are members (the index part of
-// the key orders equal scores exactly that way), which the emission
-// resolves with a second scan instead of three more rounds over the index
-// bits. Stage 1 of the two-stage selection runs all six rounds, so that
-// its members stay a plain prefix test on the key. Emission:
-//   k_msel_count   per chunk: entries above the bucket, and in it
-//   k_msel_offsets per segment: exclusive scans over its chunks (members
-//                  and bucket entries), head offsets, window entries
-//   k_msel_emit    per chunk: members in index order at their ranks,
-//                  staged in LDS and written with coalesced stores
+//   k_msel_hist    per chunk, twice: histogram of the next 11-bit digit of
+//                  the score bits among the candidates that match the
+//                  prefix (in LDS: four copies on the first digit, where
+//                  keys crowd a few bins), added to the segment's global
+//                  histogram
+//   k_msel_pick    per segment, after each: the bin holding the need-th
+//                  largest key (bins read in descending order), the next
+//                  state, and a cleared histogram for the next digit
+//   k_msel_filter  per chunk: keys above the bucket are members (final
+//                  stage: bits of the chunk's member mask, and its member
+//                  count); keys in it go to the segment's short list
+//                  (score bits and index)
+//   k_msel_finish  per segment: the remaining rounds (the last 10 score
+//                  bits, then the index bits) over the list in LDS, until
+//                  the bucket is taken whole or holds one key. The stage
+//                  ends with an exact threshold key K: its members are the
+//                  keys >= K. In the final stage the listed members are
+//                  added to the mask and the chunk counts.
+// Two digits (22 of the 32 score bits) leave a few dozen keys in the
+// bucket on attention scores: each full pass over the scores is a
+// histogram or the filter, and the rounds below them run on the list. A
+// bucket too long for the list (heavy ties) is narrowed by k_msel_finish
+// itself, one workgroup streaming the segment per round. A segment whose
+// bucket is taken whole after a histogram round is done there: its members
+// are the keys >= prefix << shift, and later kernels of the stage only
+// read that. Stage 2 of the two-stage selection keys the stage-1 members
+// (keys >= K1) as +inf. Emission:
+//   k_msel_offsets per segment: exclusive scans over its chunks' member
+//                  counts, head offsets, window entries
+//   k_msel_emit    per chunk: the members of its mask in index order at
+//                  their ranks, staged in LDS and written with coalesced
+//                  stores
 // Chunks never straddle a head (group), so a group's first chunk offset is
 // the number of members before the group. Every sum runs in a fixed order
-// or over integers: the result is deterministic.
+// or over integers and K is unique (no two keys tie; the list's order
+// does not matter): the result is deterministic.
 //
 // Every thread issues all of its kPerThread loads before it uses one: a
 // chunk's workgroup then waits for memory once.
@@ -719,12 +732,19 @@ constexpr int kMThreads = 512;
 constexpr int kChunk = 16384;                      // candidates per chunk
 constexpr int kPerThread = kChunk / kMThreads;     // 32
 constexpr int kMCopies = 4;                        // LDS histogram copies, first digit
+constexpr int kMaskWords = kChunk / 32;            // a chunk's member mask
+constexpr int kListCap = 1024;                     // bucket entries a segment's list holds
+static_assert(kMaskWords == kMThreads, "k_msel_emit: one mask word a thread");
+static_assert(kBins == 4 * kMThreads, "k_msel_finish: four bins a thread");
 
 struct alignas(16) SegState {
   uint64_t prefix;      // current stage: key prefix above `shift`
-  uint64_t p1;          // stage-1 result (two-stage)
-  int32_t shift, s1;
+  uint64_t thr1;        // two-stage, stage 2: stage-1 members are the keys >= thr1
+  int32_t shift;
   uint32_t need, done;
+  uint32_t count;       // keys in the bucket the last pick chose
+  uint32_t listed;      // entries appended to the segment's list
+  uint32_t pad[3];
 };
 
 struct MselArgs {
@@ -732,7 +752,10 @@ struct MselArgs {
   const float* weight;
   SegState* states;
   uint32_t* ghist;      // [segments][kBins]
-  uint32_t* ccount;     // [segments][chunks][2]: above / in the bucket
+  uint32_t* ccount;     // [segments][chunks]: members, then members before the chunk
+  uint2* list;          // [segments][kListCap]: (score bits, index) of bucket keys
+  uint32_t* mask;       // [segments][chunks][kMaskWords]: final members
+  uint32_t* mask1;      // the same for stage-1 members (two-stage)
   int32_t* idx;
   int32_t* head_offsets;
   uint8_t* stage;
@@ -750,7 +773,7 @@ __device__ __forceinline__ uint32_t msel_bits(const MselArgs& a, const SegState&
                                               float w, bool stage2, uint32_t f) {
   const uint32_t b = score_bits(s);
   if (!stage2) return b;
-  return key_ge(b, f, st.s1, st.p1) ? kInfBits : stage2_bits(s, w, a.score_norm, a.eps);
+  return make_key(b, f) >= st.thr1 ? kInfBits : stage2_bits(s, w, a.score_norm, a.eps);
 }
 
 // chunk c of a segment: [begin, end) in flat candidate indices
@@ -807,10 +830,10 @@ __device__ __forceinline__ void msel_load(const MselArgs& a, uint32_t seg, uint3
   }
 }
 
-// stage 1 (or the single stage): prefix 0 / need k. stage 2: keep the
-// stage-1 result in (p1, s1) first. grid segments, block 256; stage 1 also
-// clears the segment's global histogram (the workspace may hold anything;
-// each pick clears the bins it read).
+// stage 1 (or the single stage): prefix 0 / need k. stage 2: the stage-1
+// threshold first. grid segments; stage 1 also clears the segment's global
+// histogram (the workspace may hold anything; each pick clears the bins
+// it read).
 __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2) {
   const uint32_t seg = blockIdx.x;
   if (!stage2) {
@@ -819,16 +842,13 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2)
   }
   if (threadIdx.x != 0) return;
   SegState& st = a.states[seg];
-  if (stage2) {
-    st.p1 = st.prefix;
-    st.s1 = st.shift;
-  } else {
-    st.p1 = 1;          // no stage-1 members when single-stage
-    st.s1 = 63;
-  }
+  // stage 1 ended with its members the keys >= prefix << shift
+  st.thr1 = stage2 ? st.prefix << st.shift : 0u;
   const SegSpan sp = seg_span(a, (size_t)seg);
   const uint32_t k = (stage2 || sp.k1 == 0xFFFFFFFFu) ? sp.k : sp.k1;
   st.shift = 63;
+  st.count = 0;
+  st.listed = 0;
   if (k == 0) {          // nothing: (key >> 63) >= 1 holds for no key
     st.prefix = 1;
     st.need = 0;
@@ -844,13 +864,14 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2)
   }
 }
 
-// grid chunks*segments (1-D), block 256
+// grid chunks*segments (1-D): the digit below `shift` (63 or 52: both
+// histogram rounds lie in the score bits) among the keys in the bucket
 template <int COPIES, bool VEC>
 __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2) {
   __shared__ uint32_t hist[COPIES][kBins];
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
   const SegState st = a.states[seg];
-  if (st.done) return;
+  if (st.done || st.shift < 52) return;
   const int tid = threadIdx.x;
   const int shift = st.shift, wdt = digit_width(shift), nb = 1 << wdt;
   uint32_t g, begin, end;
@@ -862,31 +883,17 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
     for (int b = tid; b < nb; b += kMThreads) hist[cp][b] = 0;
   __syncthreads();
   uint32_t* hc = hist[tid & (COPIES - 1)];
-  // 32-bit arithmetic on key = (bits << 31) | (2^31 - 1 - f), as in the
-  // resident select
+  // keys (bits << 31) | (2^31 - 1 - f) with (key >> shift) == prefix are
+  // those with bits in [lo, lo + 2^sh)
   const uint32_t mask = (uint32_t)nb - 1u;
-  if (shift - wdt >= 31) {
-    // the digit lies in the score bits: keys in [lo, lo + 2^sh) match
-    const uint32_t sh = shift - 31, dsh = shift - wdt - 31;
-    const uint32_t lo = sh >= 32 ? 0u : (uint32_t)st.prefix << sh;
-    const uint32_t span_m1 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
+  const uint32_t sh = shift - 31, dsh = shift - wdt - 31;
+  const uint32_t lo = sh >= 32 ? 0u : (uint32_t)st.prefix << sh;
+  const uint32_t span_m1 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const uint32_t f = begin + msel_e<VEC>(i);
-      const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f);
-      if (f < end && b - lo <= span_m1) atomicAdd(&hc[(b >> dsh) & mask], 1u);
-    }
-  } else {
-    // the digit lies in the index bits: the score bits are all fixed
-    const uint32_t pb = (uint32_t)(st.prefix >> (31 - shift));
-    const uint32_t pi = (uint32_t)st.prefix & ((1u << (31 - shift)) - 1u);
-    const uint32_t ish = (uint32_t)shift, dsh = (uint32_t)(shift - wdt);
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const uint32_t f = begin + msel_e<VEC>(i);
-      const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f), ix = 0x7FFFFFFFu - f;
-      if (f < end && b == pb && (ix >> ish) == pi) atomicAdd(&hc[(ix >> dsh) & mask], 1u);
-    }
+  for (int i = 0; i < kPerThread; ++i) {
+    const uint32_t f = begin + msel_e<VEC>(i);
+    const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f);
+    if (f < end && b - lo <= span_m1) atomicAdd(&hc[(b >> dsh) & mask], 1u);
   }
   __syncthreads();
   uint32_t* gh = a.ghist + (size_t)seg * kBins;
@@ -898,9 +905,9 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
   }
 }
 
-// grid segments, block 256: thread t owns bins nb-1-8t .. nb-8-8t
-// (descending); exactly one thread holds the bin where the count of larger
-// keys first reaches need
+// grid segments: thread t owns bins nb-1-8t .. nb-8-8t (descending);
+// exactly one thread holds the bin where the count of larger keys first
+// reaches need
 __global__ __launch_bounds__(kMThreads) void k_msel_pick(MselArgs a) {
   __shared__ uint32_t sbuf[kMThreads / 64];
   __shared__ uint32_t s_digit, s_above, s_count;
@@ -952,23 +959,8 @@ __global__ __launch_bounds__(kMThreads) void k_msel_pick(MselArgs a) {
     st.prefix = (st.prefix << wdt) | s_digit;
     st.shift = shift - wdt;
     st.need = need - s_above;
+    st.count = s_count;
     st.done = (st.need == s_count || st.shift == 0) ? 1u : 0u;
-  }
-}
-
-// Membership classes of a key after the rounds: when the segment is done,
-// every key with (key >> shift) >= prefix is a member ("above"); otherwise
-// shift == 31, prefix holds the bucket's score bits, keys with larger score
-// bits are members and keys with equal ones are in the bucket, of which
-// the first `need` (index order) are members.
-__device__ __forceinline__ void msel_class(const SegState& st, uint32_t bits, uint32_t f,
-                                           bool& above, bool& eq) {
-  if (st.done) {
-    above = key_ge(bits, f, st.shift, st.prefix);
-    eq = false;
-  } else {   // shift == 31: the prefix is the bucket's score bits
-    above = bits > (uint32_t)st.prefix;
-    eq = bits == (uint32_t)st.prefix;
   }
 }
 
@@ -984,7 +976,7 @@ __device__ __forceinline__ uint32_t block_sum256(uint32_t v, uint32_t* sbuf) {
   return t;
 }
 
-// exclusive scan over the 256 threads (in thread order); total returned too
+// exclusive scan over the workgroup's threads (in thread order); total returned too
 __device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* sbuf, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -1006,34 +998,232 @@ __device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* sbuf, ui
   return off;
 }
 
-// grid segments, block 256: per chunk, the bucket entries before it (eqoff)
-// and the members before it (memoff), both in place of the counts; head
-// offsets and window entries
+// grid chunks*segments. After the histogram rounds (shift 63, 52 or 41,
+// all in the score bits, so (key >> shift) is bits >> (shift - 31)): the
+// final stage's members above the bucket (all of it when done) go to the
+// chunk's mask and count; the bucket's keys, when they fit the list, to
+// the segment's list.
+template <bool VEC>
+__global__ __launch_bounds__(kMThreads) void k_msel_filter(MselArgs a, int stage2, int final) {
+  __shared__ uint32_t mw[kMaskWords], m1w[kMaskWords];
+  __shared__ uint2 lst[kListCap];
+  __shared__ uint32_t sbuf[kMThreads / 64];
+  __shared__ uint32_t s_n, s_base;
+  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
+  const SegState st = a.states[seg];
+  const bool listing = !st.done && st.count <= (uint32_t)kListCap;
+  if (!final && !listing) return;
+  const int tid = threadIdx.x;
+  uint32_t g, begin, end;
+  msel_chunk(a, c, g, begin, end);
+  float s[kPerThread], w[kPerThread];
+  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
+  mw[tid] = 0u;
+  m1w[tid] = 0u;
+  if (tid == 0) s_n = 0u;
+  __syncthreads();
+  const uint32_t sh = (uint32_t)st.shift - 31u, pref = (uint32_t)st.prefix;
+  uint32_t nmem = 0;
+#pragma unroll
+  for (int u = 0; u < kPerThread / 4; ++u) {
+    // VEC: the four candidates share a mask word (one LDS atomic); else a
+    // wave's 64 candidates are two whole words of its own (a ballot)
+    uint32_t word = 0u, word1 = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * u + q;
+      const uint32_t e = msel_e<VEC>(i), f = begin + e;
+      const bool valid = f < end;
+      const uint32_t b1 = score_bits(s[i]);
+      const bool in1 = valid && stage2 && make_key(b1, f) >= st.thr1;
+      const uint32_t b = !stage2 ? b1 : (in1 ? kInfBits : stage2_bits(s[i], w[i], a.score_norm, a.eps));
+      const uint32_t top = sh >= 32 ? 0u : b >> sh;
+      const bool mem = valid && (top > pref || (st.done && top == pref));
+      nmem += mem;
+      if constexpr (VEC) {
+        word |= (uint32_t)mem << (e & 31);
+        word1 |= (uint32_t)in1 << (e & 31);
+      } else if (final) {
+        const uint64_t bm = __ballot(mem), bm1 = __ballot(in1);
+        if ((tid & 63) == 0) {
+          mw[e >> 5] = (uint32_t)bm;
+          mw[(e >> 5) + 1] = (uint32_t)(bm >> 32);
+          if (stage2) {
+            m1w[e >> 5] = (uint32_t)bm1;
+            m1w[(e >> 5) + 1] = (uint32_t)(bm1 >> 32);
+          }
+        }
+      }
+      if (listing && valid && top == pref) {
+        const uint32_t p = atomicAdd(&s_n, 1u);   // < count <= kListCap
+        if (p < (uint32_t)kListCap) lst[p] = uint2{b, f};
+      }
+    }
+    if constexpr (VEC) {
+      const uint32_t wi = msel_e<true>(4 * u) >> 5;
+      if (final && word) atomicOr(&mw[wi], word);
+      if (final && word1) atomicOr(&m1w[wi], word1);
+    }
+  }
+  __syncthreads();
+  if (final) {
+    const size_t wb = ((size_t)seg * a.chunks + c) * kMaskWords;
+    a.mask[wb + tid] = mw[tid];
+    if (stage2) a.mask1[wb + tid] = m1w[tid];
+    nmem = block_sum256(nmem, sbuf);
+    if (tid == 0) a.ccount[(size_t)seg * a.chunks + c] = nmem;
+  }
+  if (listing) {
+    const uint32_t nl = min(s_n, (uint32_t)kListCap);
+    if (tid == 0 && nl) s_base = atomicAdd(&a.states[seg].listed, nl);
+    __syncthreads();
+    uint2* out = a.list + (size_t)seg * kListCap;
+    for (uint32_t j = tid; j < nl; j += kMThreads)
+      if (s_base + j < (uint32_t)kListCap) out[s_base + j] = lst[j];
+  }
+}
+
+// Final stage: candidate f of the segment is a member (mask bit, chunk count)
+__device__ __forceinline__ void msel_mark(const MselArgs& a, uint32_t seg, uint32_t f) {
+  if (f >= a.seg_len) return;
+  const uint32_t g = f / a.n_cand, pos = f - g * a.n_cand;
+  const uint32_t c = g * a.cpg + pos / kChunk, e = pos % kChunk;
+  const size_t ch = (size_t)seg * a.chunks + c;
+  atomicOr(&a.mask[ch * kMaskWords + (e >> 5)], 1u << (e & 31));
+  atomicAdd(&a.ccount[ch], 1u);
+}
+
+// grid segments: the rounds below the filter's bucket, down to an exact
+// threshold key K (the stage's members are the keys >= K), left in the
+// state as prefix K, shift 0
+__global__ __launch_bounds__(kMThreads) void k_msel_finish(MselArgs a, int stage2, int final) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t lb[kListCap], lf[kListCap];
+  __shared__ uint32_t sbuf[kMThreads / 64];
+  __shared__ uint32_t s_digit, s_above, s_count;
+  const uint32_t seg = blockIdx.x;
+  const SegState st = a.states[seg];
+  if (st.done) return;     // taken whole: the members are the keys >= prefix << shift
+  const int tid = threadIdx.x;
+  const bool listed = st.count <= (uint32_t)kListCap;
+  const uint32_t m = listed ? st.count : 0u;
+  const float* sc = a.scores + (size_t)seg * a.seg_len;
+  const float* wt = stage2 ? a.weight + (size_t)seg * a.seg_len : nullptr;
+  for (uint32_t j = tid; j < m; j += kMThreads) {
+    const uint2 v = a.list[(size_t)seg * kListCap + j];
+    lb[j] = v.x;
+    lf[j] = v.y;
+  }
+  for (int b = tid; b < kBins; b += kMThreads) hist[b] = 0u;
+  __syncthreads();
+  uint64_t prefix = st.prefix;
+  int shift = st.shift;
+  uint32_t need = st.need;
+  for (;;) {
+    const int wdt = digit_width(shift);
+    const int nb = 1 << wdt;
+    const uint32_t dmask = (uint32_t)nb - 1u;
+    if (listed) {
+      for (uint32_t j = tid; j < m; j += kMThreads) {
+        const uint64_t key = make_key(lb[j], lf[j]);
+        if ((key >> shift) == prefix) atomicAdd(&hist[(uint32_t)(key >> (shift - wdt)) & dmask], 1u);
+      }
+    } else {   // the bucket outgrew the list: one workgroup streams the segment
+      for (uint32_t f = tid; f < a.seg_len; f += kMThreads) {
+        const uint64_t key = make_key(msel_bits(a, st, sc[f], wt ? wt[f] : 0.f, stage2 != 0, f), f);
+        if ((key >> shift) == prefix) atomicAdd(&hist[(uint32_t)(key >> (shift - wdt)) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    // bins in descending order, four a thread
+    uint32_t h[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = nb - 1 - 4 * tid - j;
+      h[j] = b >= 0 ? hist[b] : 0u;
+      sum += h[j];
+    }
+    uint32_t tot;
+    const uint32_t above = block_scan256(sum, sbuf, tot);
+    if (above < need && need <= above + sum) {   // exactly one thread
+      uint32_t acc = above;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (acc < need && need <= acc + h[j]) {
+          s_digit = (uint32_t)(nb - 1 - 4 * tid - j);
+          s_above = acc;
+          s_count = h[j];
+        }
+        acc += h[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = nb - 1 - 4 * tid - j;
+      if (b >= 0) hist[b] = 0u;
+    }
+    prefix = (prefix << wdt) | s_digit;
+    shift -= wdt;
+    need -= s_above;
+    const uint32_t dcount = s_count;
+    __syncthreads();   // s_digit/above/count read and the bins cleared before the next round
+    if (need == dcount || shift == 0) break;
+  }
+  const uint64_t K = prefix << shift;
+  if (final) {
+    if (listed) {
+      for (uint32_t j = tid; j < m; j += kMThreads)
+        if (make_key(lb[j], lf[j]) >= K) msel_mark(a, seg, lf[j]);
+    } else {
+      // the bucket's members: keys in it (the filter marked those above)
+      // and >= K, a mask word a thread
+      for (uint32_t c = 0; c < a.chunks; ++c) {
+        uint32_t g, begin, end;
+        msel_chunk(a, c, g, begin, end);
+        uint32_t bits = 0u;
+        for (int j = 0; j < 32; ++j) {
+          const uint32_t f = begin + 32u * tid + j;
+          if (f < end) {
+            const uint64_t key = make_key(msel_bits(a, st, sc[f], wt ? wt[f] : 0.f, stage2 != 0, f), f);
+            if ((key >> st.shift) == st.prefix && key >= K) bits |= 1u << j;
+          }
+        }
+        const size_t ch = (size_t)seg * a.chunks + c;
+        if (bits) atomicOr(&a.mask[ch * kMaskWords + tid], bits);
+        const uint32_t cnt = block_sum256((uint32_t)__popc(bits), sbuf);
+        if (tid == 0 && cnt) atomicAdd(&a.ccount[ch], cnt);
+      }
+    }
+  }
+  if (tid == 0) {
+    SegState& gs = a.states[seg];
+    gs.prefix = K;
+    gs.shift = 0;
+    gs.need = 0;
+    gs.done = 1;
+  }
+}
+
+// grid segments: per chunk, the members before it (in place of its
+// count); head offsets and window entries
 __global__ __launch_bounds__(kMThreads) void k_msel_offsets(MselArgs a) {
   __shared__ uint32_t sbuf[kMThreads / 64];
   __shared__ uint32_t gstart[kMaxGroups];   // members before each group
   const uint32_t seg = blockIdx.x;
-  const SegState st = a.states[seg];
-  const uint32_t need = st.done ? 0u : st.need;
   const int tid = threadIdx.x;
-  uint32_t* cc = a.ccount + (size_t)seg * a.chunks * 2;
-  uint32_t run_eq = 0, run_mem = 0;
+  uint32_t* cc = a.ccount + (size_t)seg * a.chunks;
+  uint32_t run = 0;
   for (uint32_t base = 0; base < a.chunks; base += kMThreads) {
     const uint32_t c = base + tid;
-    const uint32_t na = c < a.chunks ? cc[2 * c] : 0u;
-    const uint32_t ne = c < a.chunks ? cc[2 * c + 1] : 0u;
-    uint32_t tot_eq, tot_mem;
-    const uint32_t eqoff = run_eq + block_scan256(ne, sbuf, tot_eq);
-    // bucket members in this chunk: the part of [eqoff, eqoff + ne) below need
-    const uint32_t tie = eqoff >= need ? 0u : min(ne, need - eqoff);
-    const uint32_t memoff = run_mem + block_scan256(na + tie, sbuf, tot_mem);
+    const uint32_t na = c < a.chunks ? cc[c] : 0u;
+    uint32_t tot;
+    const uint32_t memoff = run + block_scan256(na, sbuf, tot);
     if (c < a.chunks) {
-      cc[2 * c] = memoff;
-      cc[2 * c + 1] = eqoff;
+      cc[c] = memoff;
       if (c % a.cpg == 0) gstart[c / a.cpg] = memoff;
     }
-    run_eq += tot_eq;
-    run_mem += tot_mem;
+    run += tot;
   }
   __syncthreads();
   const SegSpan sp = seg_span(a, (size_t)seg);
@@ -1066,107 +1256,30 @@ __global__ __launch_bounds__(kMThreads) void k_msel_offsets(MselArgs a) {
     a.head_offsets[(size_t)seg * (a.groups + 1) + a.groups] = (int32_t)a.budget;
 }
 
-// grid chunks*segments, block 256: per chunk, entries above the bucket and in it
-template <bool VEC>
-__global__ __launch_bounds__(kMThreads) void k_msel_count(MselArgs a, int stage2) {
+// grid chunks*segments: thread t takes mask word t (the chunk's candidates
+// 32t .. 32t+31); a block scan of the words' member counts gives each
+// member its rank in index order. The chunk's members take consecutive
+// output slots: they are staged by rank in LDS and stored with coalesced
+// writes. Two-stage: stage-1 members are marked 1, the others 2.
+__global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int two_stage) {
+  __shared__ uint32_t staged[kChunk];
   __shared__ uint32_t sbuf[kMThreads / 64];
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
-  const SegState st = a.states[seg];
   const int tid = threadIdx.x;
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
-  float s[kPerThread], w[kPerThread];
-  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
-  uint32_t na = 0, ne = 0;
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t f = begin + msel_e<VEC>(i);
-    if (f < end) {
-      bool above, eq;
-      msel_class(st, msel_bits(a, st, s[i], w[i], stage2 != 0, f), f, above, eq);
-      na += above;
-      ne += eq;
-    }
-  }
-  na = block_sum256(na, sbuf);
-  ne = block_sum256(ne, sbuf);
-  if (tid == 0) {
-    a.ccount[((size_t)seg * a.chunks + c) * 2] = na;
-    a.ccount[((size_t)seg * a.chunks + c) * 2 + 1] = ne;
-  }
-}
-
-// LDS slot of chunk element e: one pad word per 32, so that a thread
-// reading its own 32 consecutive elements and a wave writing 64
-// consecutive ones both hit distinct banks
-__device__ __forceinline__ uint32_t emit_slot(uint32_t e) { return e + (e >> 5); }
-
-// grid chunks*segments, block 256: thread t takes kPerThread consecutive
-// candidates of the chunk (their key bits staged through LDS from
-// coalesced loads); block scans of the per-thread bucket and member counts
-// give each bucket entry its tie rank and each member its rank, in index
-// order. The chunk's members take consecutive output slots: they are
-// staged by rank in LDS and stored with coalesced writes.
-template <bool VEC>
-__global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int stage2) {
-  __shared__ uint32_t bits[kChunk + kChunk / 32];
-  __shared__ uint32_t sbuf[kMThreads / 64];
-  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
-  const SegState st = a.states[seg];
-  const uint32_t need = st.done ? 0u : st.need;
-  const int tid = threadIdx.x;
-  uint32_t g, begin, end;
-  msel_chunk(a, c, g, begin, end);
-  {
-    float s[kPerThread], w[kPerThread];
-    msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const uint32_t e = msel_e<VEC>(i);
-      const uint32_t f = begin + e;
-      bits[emit_slot(e)] = f < end ? msel_bits(a, st, s[i], w[i], stage2 != 0, f) : 0u;
-    }
-  }
-  __syncthreads();
-  uint32_t amask = 0, emask = 0, ne = 0, imask = 0;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const uint32_t e = tid * kPerThread + j;
-    const uint32_t f = begin + e;
-    if (f < end) {
-      const uint32_t b = bits[emit_slot(e)];
-      bool above, eq;
-      msel_class(st, b, f, above, eq);
-      amask |= (uint32_t)above << j;
-      emask |= (uint32_t)eq << j;
-      imask |= (uint32_t)(b == kInfBits) << j;
-      ne += eq;
-    }
-  }
-  const uint32_t* cc = a.ccount + ((size_t)seg * a.chunks + c) * 2;
-  const uint32_t rank0 = cc[0], eq0 = cc[1];
-  uint32_t tot;
-  uint32_t tierank = eq0 + block_scan256(ne, sbuf, tot);   // bucket entries before this thread's
-  uint32_t mmask = amask;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    if (emask & (1u << j)) {
-      if (tierank < need) mmask |= 1u << j;
-      ++tierank;
-    }
-  }
+  const size_t ch = (size_t)seg * a.chunks + c;
+  const uint32_t mm = a.mask[ch * kMaskWords + tid];
+  const uint32_t m1 = two_stage ? a.mask1[ch * kMaskWords + tid] : 0xFFFFFFFFu;
+  const uint32_t rank0 = a.ccount[ch];
   uint32_t count;
-  uint32_t r = block_scan256((uint32_t)__popc(mmask), sbuf, count);   // members before this thread's
+  uint32_t r = block_scan256((uint32_t)__popc(mm), sbuf, count);   // members before this thread's
   // staged[r] = position in its head of the chunk's member of rank r, bit
-  // 31 set for a stage-2 member of the two-stage selection (the key bits
-  // are no longer needed: every thread has classified its entries before
-  // the scans' barriers)
-  uint32_t* staged = bits;
-  const uint32_t pos0 = begin - g * a.n_cand + tid * kPerThread;
-  for (uint32_t m = mmask; m != 0; m &= m - 1, ++r) {
+  // 31 set for a stage-2 member of the two-stage selection
+  const uint32_t pos0 = begin - g * a.n_cand + tid * 32u;
+  for (uint32_t m = mm; m != 0; m &= m - 1, ++r) {
     const uint32_t j = (uint32_t)__builtin_ctz(m);
-    const bool second = stage2 && !((imask >> j) & 1u);
-    staged[r] = (pos0 + j) | (second ? 0x80000000u : 0u);
+    staged[r] = (pos0 + j) | (((m1 >> j) & 1u) ? 0u : 0x80000000u);
   }
   __syncthreads();
   const SegSpan sp = seg_span(a, (size_t)seg);
@@ -1187,7 +1300,7 @@ static size_t al256s(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct MselLayout {
   uint32_t cpg, chunks;
-  size_t states_off, ghist_off, ccount_off, bytes;
+  size_t states_off, ghist_off, ccount_off, list_off, mask_off, mask1_off, bytes;
 };
 
 static MselLayout msel_layout(const SelectPlan& p) {
@@ -1195,10 +1308,14 @@ static MselLayout msel_layout(const SelectPlan& p) {
   const uint32_t groups = p.adaptive ? (uint32_t)p.H : 1u;
   m.cpg = (uint32_t)((p.n_cand + kChunk - 1) / kChunk);
   m.chunks = groups * m.cpg;
+  const size_t chunks = (size_t)p.segments * m.chunks;
   m.states_off = 0;
   m.ghist_off = al256s((size_t)p.segments * sizeof(SegState));
   m.ccount_off = m.ghist_off + al256s((size_t)p.segments * kBins * sizeof(uint32_t));
-  m.bytes = m.ccount_off + al256s((size_t)p.segments * m.chunks * 2 * sizeof(uint32_t));
+  m.list_off = m.ccount_off + al256s(chunks * sizeof(uint32_t));
+  m.mask_off = m.list_off + al256s((size_t)p.segments * kListCap * sizeof(uint2));
+  m.mask1_off = m.mask_off + al256s(chunks * kMaskWords * sizeof(uint32_t));
+  m.bytes = m.mask1_off + (p.two_stage ? al256s(chunks * kMaskWords * sizeof(uint32_t)) : 0);
   return m;
 }
 
@@ -1215,6 +1332,9 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   a.states = reinterpret_cast<SegState*>(w + m.states_off);
   a.ghist = reinterpret_cast<uint32_t*>(w + m.ghist_off);
   a.ccount = reinterpret_cast<uint32_t*>(w + m.ccount_off);
+  a.list = reinterpret_cast<uint2*>(w + m.list_off);
+  a.mask = reinterpret_cast<uint32_t*>(w + m.mask_off);
+  a.mask1 = p.two_stage ? reinterpret_cast<uint32_t*>(w + m.mask1_off) : nullptr;
   a.idx = idx;
   a.head_offsets = p.adaptive ? head_offsets : nullptr;
   a.stage = stage;
@@ -1245,32 +1365,26 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   // multiple of 4 long (scores and weights are 16-byte aligned)
   const bool vec = p.n_cand % 4 == 0;
   for (int stg = 0; stg < stages; ++stg) {
-    const int stage2 = stg == 1 ? 1 : 0;
-    // the final stage stops after the score bits (ties split in emission)
-    const int rounds = stg + 1 < stages ? 6 : 3;
+    const int stage2 = stg == 1 ? 1 : 0, final = stg + 1 == stages ? 1 : 0;
     hipLaunchKernelGGL(k_msel_init, gp, dim3(kMThreads), 0, st, a, stage2);
-    for (int r = 0; r < rounds; ++r) {
-      if (r == 0 && vec)
-        hipLaunchKernelGGL((k_msel_hist<kMCopies, true>), gc, dim3(kMThreads), 0, st, a, stage2);
-      else if (r == 0)
-        hipLaunchKernelGGL((k_msel_hist<kMCopies, false>), gc, dim3(kMThreads), 0, st, a, stage2);
-      else if (vec)
-        hipLaunchKernelGGL((k_msel_hist<1, true>), gc, dim3(kMThreads), 0, st, a, stage2);
-      else
-        hipLaunchKernelGGL((k_msel_hist<1, false>), gc, dim3(kMThreads), 0, st, a, stage2);
-      hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
-    }
+    if (vec)
+      hipLaunchKernelGGL((k_msel_hist<kMCopies, true>), gc, dim3(kMThreads), 0, st, a, stage2);
+    else
+      hipLaunchKernelGGL((k_msel_hist<kMCopies, false>), gc, dim3(kMThreads), 0, st, a, stage2);
+    hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
+    if (vec)
+      hipLaunchKernelGGL((k_msel_hist<1, true>), gc, dim3(kMThreads), 0, st, a, stage2);
+    else
+      hipLaunchKernelGGL((k_msel_hist<1, false>), gc, dim3(kMThreads), 0, st, a, stage2);
+    hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
+    if (vec)
+      hipLaunchKernelGGL(k_msel_filter<true>, gc, dim3(kMThreads), 0, st, a, stage2, final);
+    else
+      hipLaunchKernelGGL(k_msel_filter<false>, gc, dim3(kMThreads), 0, st, a, stage2, final);
+    hipLaunchKernelGGL(k_msel_finish, gp, dim3(kMThreads), 0, st, a, stage2, final);
   }
-  const int final2 = p.two_stage ? 1 : 0;
-  if (vec)
-    hipLaunchKernelGGL(k_msel_count<true>, gc, dim3(kMThreads), 0, st, a, final2);
-  else
-    hipLaunchKernelGGL(k_msel_count<false>, gc, dim3(kMThreads), 0, st, a, final2);
   hipLaunchKernelGGL(k_msel_offsets, gp, dim3(kMThreads), 0, st, a);
-  if (vec)
-    hipLaunchKernelGGL(k_msel_emit<true>, gc, dim3(kMThreads), 0, st, a, final2);
-  else
-    hipLaunchKernelGGL(k_msel_emit<false>, gc, dim3(kMThreads), 0, st, a, final2);
+  hipLaunchKernelGGL(k_msel_emit, gc, dim3(kMThreads), 0, st, a, p.two_stage ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -194,6 +194,7 @@ def decode_sizes(L, H, G, kept, offs):
 # -------------------------------------------------------------- selection ----
 
 SEL_THREADS, M_THREADS, K_CHUNK, K_BINS, K_MAX_GROUPS = 1024, 512, 16384, 2048, 1024
+K_MASK_WORDS, K_LIST_CAP = K_CHUNK // 32, 1024
 
 
 def _clamp_budget(b, W, n):
@@ -261,11 +262,12 @@ def digit_width(shift):
     return 10 if shift == 41 else (9 if shift == 9 else 11)
 
 
-def msel_accesses(p, states, ccount, rng, budgets=None):
-    """k_msel_init, k_msel_hist, k_msel_pick, k_msel_count, k_msel_offsets
-    and k_msel_emit (select.hip) with arbitrary segment states (shift, need, done) and
-    arbitrary per-chunk counts. Where a membership test decides a rank, each
-    thread's member count is drawn at random within its 32 candidates."""
+def msel_accesses(p, states, ccount, rng, budgets=None, lists=None):
+    """k_msel_init, k_msel_hist, k_msel_pick, k_msel_filter, k_msel_finish,
+    k_msel_offsets and k_msel_emit (select.hip) with arbitrary segment
+    states (shift, need, done, count), per-chunk counts and list entries.
+    Where a membership test decides a rank, each thread's member count is
+    drawn at random within its 32 candidates."""
     acc = Accesses()
     S, chunks, W = p["segments"], p["chunks"], p["W"]
     for seg in range(S):
@@ -282,19 +284,43 @@ def msel_accesses(p, states, ccount, rng, budgets=None):
         acc.add("ghist", seg * K_BINS + b[b >= 0])
         for c in range(chunks):
             g, begin, end = msel_chunk(p, c)
-            # k_msel_hist / k_msel_count / k_msel_emit loads: f < end
+            # k_msel_hist / k_msel_filter loads: f < end
             if end > begin:
                 acc.add("scores", seg * p["seg_len"] + np.array([begin, end - 1]))
                 if p["two_stage"]:
                     acc.add("weight", seg * p["seg_len"] + np.array([begin, end - 1]))
-            acc.add("ccount", (seg * chunks + c) * 2 + np.array([0, 1]))
+            # k_msel_filter: the chunk's mask words and count; list slots
+            # base + j (base from an atomic on the state: any uint32) kept
+            # below K_LIST_CAP
+            words = (seg * chunks + c) * K_MASK_WORDS + np.arange(K_MASK_WORDS)
+            acc.add("mask", words)
+            if p["two_stage"]:
+                acc.add("mask1", words)
+            acc.add("ccount", [seg * chunks + c])
+            base = int(rng.integers(0, U32))
+            slot = _u32(base + np.arange(K_LIST_CAP))
+            acc.add("list", seg * K_LIST_CAP + slot[slot < K_LIST_CAP])
+        # k_msel_finish: list entries j < count when count <= K_LIST_CAP,
+        # else the segment streamed (f < seg_len); members marked from the
+        # list's (arbitrary) indices, guarded by f < seg_len
+        m = int(_u32(st.get("count", 0)))
+        if m <= K_LIST_CAP:
+            acc.add("list", seg * K_LIST_CAP + np.arange(m))
+        if p["seg_len"]:
+            acc.add("scores", seg * p["seg_len"] + np.array([0, p["seg_len"] - 1]))
+            if p["two_stage"]:
+                acc.add("weight", seg * p["seg_len"] + np.array([0, p["seg_len"] - 1]))
+        fl = _u32(lists[seg]) if lists is not None else _u32(rng.integers(0, U32, size=64))
+        fl = fl[fl < p["seg_len"]]
+        g = fl // p["n_cand"] if p["n_cand"] else fl * 0
+        pos = fl - g * p["n_cand"]
+        ch = seg * chunks + g * p["cpg"] + pos // K_CHUNK
+        acc.add("ccount", ch)
+        acc.add("mask", ch * K_MASK_WORDS + (pos % K_CHUNK) // 32)
         # k_msel_offsets: scans of arbitrary counts (uint32), group starts
-        cc = ccount[seg]
-        need = 0 if st["done"] else int(st["need"])
-        ne, na = _u32(cc[:, 1]), _u32(cc[:, 0])
-        eqoff = _u32(np.concatenate([[0], np.cumsum(ne)[:-1]]))
-        tie = np.where(eqoff >= need, 0, np.minimum(ne, _u32(need - eqoff)))
-        memoff = _u32(np.concatenate([[0], np.cumsum(_u32(na + tie))[:-1]]))
+        cc = _u32(ccount[seg])
+        memoff = _u32(np.concatenate([[0], np.cumsum(cc)[:-1]]))
+        acc.add("ccount", seg * chunks + np.arange(chunks))
         gidx = np.arange(chunks)[np.arange(chunks) % p["cpg"] == 0] // p["cpg"]
         assert gidx.max(initial=0) < K_MAX_GROUPS
         gstart = memoff[np.arange(chunks) % p["cpg"] == 0]
@@ -315,14 +341,15 @@ def msel_accesses(p, states, ccount, rng, budgets=None):
                 acc.add("idx", l * p["stride"] + np.arange(sp["end"], p["stride"], dtype=np.int64))
         elif p["adaptive"]:
             acc.add("head_offsets", [seg * (p["groups"] + 1) + p["groups"]])
-        # k_msel_emit: the chunk's members are staged by rank in LDS (at
-        # most kChunk of them) and take slots rank0 + g*W + i, i < count,
-        # with rank0 the chunk's (arbitrary) member offset
+        # k_msel_emit: the chunk's members (set bits of its K_MASK_WORDS
+        # words: at most K_CHUNK) are staged by rank in LDS and take slots
+        # rank0 + g*W + i, i < count, with rank0 the chunk's (arbitrary)
+        # member offset
         for c in range(chunks):
             g, begin, end = msel_chunk(p, c)
-            count = int(rng.integers(0, max(0, end - begin) + 1))
-            assert count <= K_CHUNK
-            o = int(_u32(ccount[seg][c, 0])) + g * W + np.arange(count, dtype=np.int64)
+            count = int(rng.integers(0, K_CHUNK + 1))
+            assert count <= K_MASK_WORDS * 32 == K_CHUNK
+            o = int(_u32(ccount[seg][c])) + g * W + np.arange(count, dtype=np.int64)
             acc.add("idx", sp["base"] + o[o < sp["room"]])
     return acc
 
@@ -330,9 +357,12 @@ def msel_accesses(p, states, ccount, rng, budgets=None):
 def select_sizes(p):
     s = {"scores": p["segments"] * p["seg_len"], "budgets": p["L"] * p["H"],
          "states": p["segments"], "ghist": p["segments"] * K_BINS,
-         "ccount": p["segments"] * p.get("chunks", 0) * 2}
+         "ccount": p["segments"] * p.get("chunks", 0),
+         "list": p["segments"] * K_LIST_CAP,
+         "mask": p["segments"] * p.get("chunks", 0) * K_MASK_WORDS}
     if p["two_stage"]:
         s["weight"] = s["scores"]
+        s["mask1"] = s["mask"]
     if p["budgets"] is not None:
         s["idx"] = p["L"] * p["stride"]
         s["head_offsets"] = p["L"] * (p["H"] + 1)

@@ -111,16 +111,21 @@ def test_select_many_workgroups_stays_in_bounds(seed, variant):
         p = _valid_uniform_plan(rng, variant == "adaptive", variant == "two_stage", True)
         budgets = None
     S, C = p["segments"], p["chunks"]
-    # arbitrary segment states and chunk counts (uint32 fields)
+    # arbitrary segment states, chunk counts and list entries (uint32 fields)
     states = [dict(shift=int(rng.integers(I32_MIN, I32_MAX)), need=int(rng.integers(0, 1 << 32)),
-                   done=int(rng.integers(0, 2))) for _ in range(S)]
+                   done=int(rng.integers(0, 2)), count=int(rng.integers(0, 1 << 32)))
+              for _ in range(S)]
     for st in states[: S // 2]:       # and some near the values a select leaves
         st["shift"] = int(rng.choice([63, 52, 41, 31, 20, 9, 0]))
         st["need"] = int(rng.integers(0, p["seg_len"] + 2))
-    ccount = [rng.integers(0, 1 << 32, size=(C, 2), dtype=np.int64) for _ in range(S)]
+        st["count"] = int(rng.integers(0, br.K_LIST_CAP + 2))
+    ccount = [rng.integers(0, 1 << 32, size=C, dtype=np.int64) for _ in range(S)]
     for cc in ccount[: S // 2]:
-        cc[:] = rng.integers(0, br.K_CHUNK + 1, size=(C, 2))
-    acc = br.msel_accesses(p, states, ccount, rng, budgets)
+        cc[:] = rng.integers(0, br.K_CHUNK + 1, size=C)
+    lists = [rng.integers(0, 1 << 32, size=br.K_LIST_CAP, dtype=np.int64) for _ in range(S)]
+    for ls in lists[: S // 2]:
+        ls[:] = rng.integers(0, p["seg_len"] + 2, size=br.K_LIST_CAP)
+    acc = br.msel_accesses(p, states, ccount, rng, budgets, lists)
     acc.check(br.select_sizes(p))
 
 
