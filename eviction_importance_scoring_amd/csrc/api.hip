@@ -266,7 +266,9 @@ int32_t kvsel_select_pool(const float* raw, const float* weight, int32_t pool, i
   if (rc != KVSEL_OK) return rc;
   if (pool > 65) return KVSEL_ERR_UNSUPPORTED;
   // one head's raw row on chip when it fits; else the pooled scores go
-  // through memory (`pooled`, or the workspace) before the selection
+  // through memory (`pooled`, or the workspace): written by the many-
+  // workgroup selection's first pass (radius <= 3), or by the pool kernel
+  // before the selection
   const int r = pool / 2;
   const bool on_chip = select_pools_on_chip(p, r);
   const size_t pooled_ws = on_chip || pooled ? 0 : al256((size_t)L * H_kv * p.n_cand * sizeof(float));
@@ -289,10 +291,16 @@ int32_t kvsel_select_pool(const float* raw, const float* weight, int32_t pool, i
     e = select_launch(p, raw, weight, idx, head_offsets, stage, ws, st);
   } else {
     float* ps = pooled ? pooled : static_cast<float*>(ws);
-    e = pool_launch(raw, L, H_kv, n, p.n_cand, r, ps, st);
-    if (e == hipSuccess)
-      e = select_launch(p, ps, weight, idx, head_offsets, stage, static_cast<char*>(ws) + pooled_ws,
-                        st);
+    void* sws = static_cast<char*>(ws) + pooled_ws;
+    if (select_pools_in_passes(p, r)) {   // pooled in the selection's first pass
+      p.pool_r = r;
+      p.in_stride = n;
+      p.pooled = ps;
+      e = select_launch(p, raw, weight, idx, head_offsets, stage, sws, st);
+    } else {
+      e = pool_launch(raw, L, H_kv, n, p.n_cand, r, ps, st);
+      if (e == hipSuccess) e = select_launch(p, ps, weight, idx, head_offsets, stage, sws, st);
+    }
   }
   return e == hipSuccess ? KVSEL_OK : KVSEL_ERR_HIP;
 }

@@ -60,16 +60,22 @@ struct SelectPlan {
   const int32_t* budgets = nullptr;   // per-head budgets [L][H] (device), or null
   int64_t stride = 0;     // layer row of idx when budgets are given
   float alpha = 0.f;
-  // On-chip max-pooling (resident segments of one head only): the scores
-  // are raw rows `in_stride` floats apart, pooled with radius pool_r over
-  // each segment's candidates; the pooled scores go to `pooled` if given.
+  // Max-pooling in the selection: the scores are raw rows `in_stride`
+  // floats apart, pooled with radius pool_r over each head's candidates.
+  // On chip (resident segments of one head) the pooled scores go to
+  // `pooled` if given; on the many-workgroup path they go to `pooled`.
   int pool_r = 0;
   int64_t in_stride = 0;  // 0: seg_len
   float* pooled = nullptr;
 };
 
-// Whether select_launch pools on chip for this plan (else the caller pools).
+// Whether select_launch pools on chip for this plan (raw rows in, the
+// pooled scores out only if asked).
 bool select_pools_on_chip(const SelectPlan& p, int pool_r);
+// Whether select_launch pools in the first pass of its many-workgroup path
+// (raw rows in; the pooled scores go to SelectPlan::pooled, which is
+// required). Otherwise the caller pools.
+bool select_pools_in_passes(const SelectPlan& p, int pool_r);
 
 // scores[lh][j] = max raw[lh][t] over |t - j| <= r, 0 <= t < n_cand (raw
 // rows n apart); scores == nullptr: nothing.

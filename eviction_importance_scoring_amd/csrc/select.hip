@@ -889,11 +889,28 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
   const uint32_t sh = shift - 31, dsh = shift - wdt - 31;
   const uint32_t lo = sh >= 32 ? 0u : (uint32_t)st.prefix << sh;
   const uint32_t span_m1 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
+  // four candidates at a time (consecutive ones when VEC): when all four
+  // fall in one bin, as neighbouring max-pooled scores mostly do on the
+  // first digit, they add 4 with one atomic
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t f = begin + msel_e<VEC>(i);
-    const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f);
-    if (f < end && b - lo <= span_m1) atomicAdd(&hc[(b >> dsh) & mask], 1u);
+  for (int u = 0; u < kPerThread / 4; ++u) {
+    uint32_t bn[4];
+    bool ok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * u + q;
+      const uint32_t f = begin + msel_e<VEC>(i);
+      const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f);
+      ok[q] = f < end && b - lo <= span_m1;
+      bn[q] = (b >> dsh) & mask;
+    }
+    if (ok[0] && ok[1] && ok[2] && ok[3] && bn[0] == bn[1] && bn[1] == bn[2] && bn[2] == bn[3]) {
+      atomicAdd(&hc[bn[0]], 4u);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (ok[q]) atomicAdd(&hc[bn[q]], 1u);
+    }
   }
   __syncthreads();
   uint32_t* gh = a.ghist + (size_t)seg * kBins;
@@ -902,6 +919,140 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
 #pragma unroll
     for (int cp = 0; cp < COPIES; ++cp) v += hist[cp][b];
     if (v) atomicAdd(gh + b, v);
+  }
+}
+
+// Pooling in the first pass (kvsel_select_pool on raw rows, radius R <=
+// kMaxPoolR): the chunk's raw scores and a halo of kPoolHalo on each side
+// go to LDS (one pad word per 32, so that 64 lanes reading at a stride of
+// 32 or 4 words, and 64 consecutive ones, all hit distinct banks); thread
+// t pools the chunk's candidates 32t .. 32t+31 in the order of the pool
+// kernel (so the pooled bits are the same), histograms their first digit
+// by runs of equal bins along them, and the pooled scores go out to the
+// array the later passes read, through LDS again for coalesced stores.
+constexpr int kPoolHalo = 4;                       // >= kMaxPoolR; keeps 16-byte units
+constexpr int kPoolWin = 32 + 2 * kPoolHalo;       // a thread's window
+__device__ __forceinline__ uint32_t pool_slot(uint32_t x) { return x + (x >> 5); }
+// the last thread's window ends at 32 * 511 + kPoolWin - 1
+constexpr size_t kPoolTileFloats = (size_t)(kChunk - 32 + kPoolWin - 1) + (kChunk - 32 + kPoolWin - 1) / 32 + 1;
+constexpr size_t kPoolTileBytes = (kPoolTileFloats * sizeof(float) + 15) & ~size_t(15);
+constexpr size_t kPoolLdsBytes = kPoolTileBytes + kBins * sizeof(uint32_t);
+constexpr int kPoolLoadsV = ((kChunk + 2 * kPoolHalo) / 4 + kMThreads - 1) / kMThreads;   // 16-byte units
+constexpr int kPoolLoads = (kChunk + 2 * kPoolHalo + kMThreads - 1) / kMThreads;          // 4-byte loads
+
+// grid chunks*segments. raw: row (seg * groups + g) holds group g's
+// candidates, in_stride floats apart. VEC: n_cand and in_stride multiples
+// of 4 (every chunk and its halo in whole 16-byte units).
+template <int R, bool VEC>
+__global__ __launch_bounds__(kMThreads) void k_msel_pool(MselArgs a, const float* raw,
+                                                         int64_t in_stride, float* pooled) {
+  extern __shared__ __align__(16) unsigned char pool_smem[];
+  float* tile = reinterpret_cast<float*>(pool_smem);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(pool_smem + kPoolTileBytes);
+  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
+  const int tid = threadIdx.x;
+  uint32_t g, begin, end;
+  msel_chunk(a, c, g, begin, end);
+  const uint32_t len = end - begin, pos0 = begin - g * a.n_cand;
+  const float* row = raw + ((size_t)seg * a.groups + g) * (size_t)in_stride;
+  const bool do_hist = !a.states[seg].done;
+  // tile x holds candidate pos0 - kPoolHalo + x; -inf outside the candidates
+  const uint32_t nx = len + 2 * kPoolHalo;
+  const float ninf = -__builtin_inff();
+  if constexpr (VEC) {
+    const uint32_t units = nx / 4;
+    u32x4 v[kPoolLoadsV];
+#pragma unroll
+    for (int j = 0; j < kPoolLoadsV; ++j) {
+      const uint32_t q = tid + j * kMThreads;
+      const int64_t p = (int64_t)pos0 - kPoolHalo + 4 * (int64_t)q;
+      const bool in = q < units && p >= 0 && p + 4 <= (int64_t)a.n_cand;
+      const uint32_t ni = __float_as_uint(ninf);
+      v[j] = in ? *reinterpret_cast<const u32x4*>(row + p) : u32x4{ni, ni, ni, ni};
+    }
+#pragma unroll
+    for (int j = 0; j < kPoolLoadsV; ++j) {
+      const uint32_t q = tid + j * kMThreads;
+      if (q < units) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tile[pool_slot(4 * q + i)] = __uint_as_float(v[j][i]);
+      }
+    }
+  } else {
+    float v[kPoolLoads];
+#pragma unroll
+    for (int j = 0; j < kPoolLoads; ++j) {
+      const uint32_t x = tid + j * kMThreads;
+      const int64_t p = (int64_t)pos0 - kPoolHalo + x;
+      v[j] = (x < nx && p >= 0 && p < (int64_t)a.n_cand) ? row[p] : ninf;
+    }
+#pragma unroll
+    for (int j = 0; j < kPoolLoads; ++j) {
+      const uint32_t x = tid + j * kMThreads;
+      if (x < nx) tile[pool_slot(x)] = v[j];
+    }
+  }
+  if (do_hist)
+    for (int b = tid; b < kBins; b += kMThreads) hist[b] = 0u;
+  __syncthreads();
+  // thread t: candidates e = 32t + j, window x = 32t .. 32t + kPoolWin - 1
+  // (reads past nx feed only candidates e >= len)
+  float win[kPoolWin], out[32];
+#pragma unroll
+  for (int j = 0; j < kPoolWin; ++j) win[j] = tile[pool_slot(32u * tid + j)];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    float m = win[j + kPoolHalo];
+#pragma unroll
+    for (int o = 1; o <= R; ++o) m = fmaxf(m, fmaxf(win[j + kPoolHalo - o], win[j + kPoolHalo + o]));
+    out[j] = m;
+  }
+  if (do_hist) {
+    // first digit (score bits >> 21) by runs along the thread's candidates
+    uint32_t cur = 0xFFFFFFFFu, cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (32u * tid + j < len) {
+        const uint32_t bin = score_bits(out[j]) >> 21;
+        if (bin != cur) {
+          if (cnt) atomicAdd(&hist[cur], cnt);
+          cur = bin;
+          cnt = 0;
+        }
+        ++cnt;
+      }
+    }
+    if (cnt) atomicAdd(&hist[cur], cnt);
+  }
+  __syncthreads();   // every window read before the tile takes the pooled scores
+#pragma unroll
+  for (int j = 0; j < 32; ++j) tile[pool_slot(32u * tid + j)] = out[j];
+  __syncthreads();
+  float* dst = pooled + (size_t)seg * a.seg_len + begin;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int u = 0; u < kPerThread / 4; ++u) {
+      const uint32_t e = u * (4u * kMThreads) + 4u * tid;
+      if (e < len) {
+        float4 x;
+        x.x = tile[pool_slot(e)];
+        x.y = tile[pool_slot(e + 1)];
+        x.z = tile[pool_slot(e + 2)];
+        x.w = tile[pool_slot(e + 3)];
+        *reinterpret_cast<float4*>(dst + e) = x;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const uint32_t e = tid + i * kMThreads;
+      if (e < len) dst[e] = tile[pool_slot(e)];
+    }
+  }
+  if (do_hist) {
+    uint32_t* gh = a.ghist + (size_t)seg * kBins;
+    for (int b = tid; b < kBins; b += kMThreads)
+      if (hist[b]) atomicAdd(gh + b, hist[b]);
   }
 }
 
@@ -1321,13 +1472,33 @@ static MselLayout msel_layout(const SelectPlan& p) {
 
 static bool use_multi(const SelectPlan& p) { return p.seg_len > kResidentMax; }
 
+template <int R>
+static hipError_t launch_msel_pool(const MselArgs& a, const float* raw, int64_t in_stride,
+                                   float* pooled, bool vec, dim3 grid, hipStream_t st) {
+  const void* f = vec ? reinterpret_cast<const void*>(&k_msel_pool<R, true>)
+                      : reinterpret_cast<const void*>(&k_msel_pool<R, false>);
+  const hipError_t e =
+      hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPoolLdsBytes);
+  if (e != hipSuccess) return e;
+  if (vec)
+    hipLaunchKernelGGL((k_msel_pool<R, true>), grid, dim3(kMThreads), kPoolLdsBytes, st, a, raw,
+                       in_stride, pooled);
+  else
+    hipLaunchKernelGGL((k_msel_pool<R, false>), grid, dim3(kMThreads), kPoolLdsBytes, st, a, raw,
+                       in_stride, pooled);
+  return hipSuccess;
+}
+
 static hipError_t msel_launch(const SelectPlan& p, const float* scores, const float* weight,
                               int32_t* idx, int32_t* head_offsets, uint8_t* stage, void* ws,
                               hipStream_t st) {
   const MselLayout m = msel_layout(p);
   char* w = static_cast<char*>(ws);
+  // raw rows (kvsel_select_pool): the first pass pools them into
+  // p.pooled, which every later pass reads
+  const bool pool_first = p.pooled != nullptr;
   MselArgs a;
-  a.scores = scores;
+  a.scores = pool_first ? p.pooled : scores;
   a.weight = p.two_stage ? weight : nullptr;
   a.states = reinterpret_cast<SegState*>(w + m.states_off);
   a.ghist = reinterpret_cast<uint32_t*>(w + m.ghist_off);
@@ -1367,10 +1538,21 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   for (int stg = 0; stg < stages; ++stg) {
     const int stage2 = stg == 1 ? 1 : 0, final = stg + 1 == stages ? 1 : 0;
     hipLaunchKernelGGL(k_msel_init, gp, dim3(kMThreads), 0, st, a, stage2);
-    if (vec)
+    if (stg == 0 && pool_first) {
+      const bool pvec = vec && p.in_stride % 4 == 0;
+      hipError_t e;
+      switch (p.pool_r) {
+        case 0: e = launch_msel_pool<0>(a, scores, p.in_stride, p.pooled, pvec, gc, st); break;
+        case 1: e = launch_msel_pool<1>(a, scores, p.in_stride, p.pooled, pvec, gc, st); break;
+        case 2: e = launch_msel_pool<2>(a, scores, p.in_stride, p.pooled, pvec, gc, st); break;
+        default: e = launch_msel_pool<3>(a, scores, p.in_stride, p.pooled, pvec, gc, st); break;
+      }
+      if (e != hipSuccess) return e;
+    } else if (vec) {
       hipLaunchKernelGGL((k_msel_hist<kMCopies, true>), gc, dim3(kMThreads), 0, st, a, stage2);
-    else
+    } else {
       hipLaunchKernelGGL((k_msel_hist<kMCopies, false>), gc, dim3(kMThreads), 0, st, a, stage2);
+    }
     hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
     if (vec)
       hipLaunchKernelGGL((k_msel_hist<1, true>), gc, dim3(kMThreads), 0, st, a, stage2);
@@ -1403,6 +1585,10 @@ bool select_pools_on_chip(const SelectPlan& p, int pool_r) {
   return !p.adaptive && !p.budgets && pool_r >= 0 && pool_r <= kMaxPoolR && stageable(p, p.n);
 }
 
+bool select_pools_in_passes(const SelectPlan& p, int pool_r) {
+  return use_multi(p) && !p.budgets && pool_r >= 0 && pool_r <= kMaxPoolR;
+}
+
 size_t select_ws_bytes(const SelectPlan& p) { return use_multi(p) ? msel_layout(p).bytes : 0; }
 
 hipError_t select_launch(const SelectPlan& p, const float* scores, const float* weight,
@@ -1433,11 +1619,16 @@ hipError_t select_launch(const SelectPlan& p, const float* scores, const float* 
   a.in_stride = p.in_stride > 0 ? p.in_stride : p.seg_len;
   a.pool_r = p.pool_r;
   a.pooled = p.pooled;
-  // raw rows (a stride other than seg_len), on-chip pooling and the pooled
-  // output exist on the staged resident path only
-  if ((a.in_stride != p.seg_len || p.pool_r > 0 || p.pooled) && !select_pools_on_chip(p, p.pool_r))
-    return hipErrorInvalidValue;
-  if (use_multi(p)) return msel_launch(p, scores, weight, idx, head_offsets, stage, ws, st);
+  // raw rows (a stride other than seg_len) and pooling: on chip on the
+  // staged resident path; in the first pass of the many-workgroup path,
+  // into `pooled` (required there)
+  const bool raw_in = a.in_stride != p.seg_len || p.pool_r > 0 || p.pooled;
+  if (use_multi(p)) {
+    if (raw_in && !(select_pools_in_passes(p, p.pool_r) && p.pooled && p.in_stride >= p.n_cand))
+      return hipErrorInvalidValue;
+    return msel_launch(p, scores, weight, idx, head_offsets, stage, ws, st);
+  }
+  if (raw_in && !select_pools_on_chip(p, p.pool_r)) return hipErrorInvalidValue;
   a.staged = stageable(p, a.in_stride) ? 1 : 0;
   const size_t lds = a.staged ? std::max(sizeof(SelShared), kStageBytes) : sizeof(SelShared);
   const hipError_t e =

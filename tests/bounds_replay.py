@@ -354,6 +354,24 @@ def msel_accesses(p, states, ccount, rng, budgets=None, lists=None):
     return acc
 
 
+def msel_pool_accesses(p, in_stride):
+    """k_msel_pool (select.hip): per chunk, raw row (seg * groups + g) read
+    at positions pos0 - halo .. pos0 + len + halo kept inside [0, n_cand)
+    (whole 16-byte units inside it when VEC), the pooled scores written at
+    seg * seg_len + begin + e, e < len."""
+    acc = Accesses()
+    halo = 4
+    for seg in range(p["segments"]):
+        for c in range(p["chunks"]):
+            g, begin, end = msel_chunk(p, c)
+            ln, pos0 = end - begin, begin - g * p["n_cand"]
+            pos = np.arange(pos0 - halo, pos0 + ln + halo, dtype=np.int64)
+            pos = pos[(pos >= 0) & (pos < p["n_cand"])]
+            acc.add("raw", (seg * p["groups"] + g) * in_stride + pos)
+            acc.add("pooled", seg * p["seg_len"] + begin + np.arange(ln, dtype=np.int64))
+    return acc
+
+
 def select_sizes(p):
     s = {"scores": p["segments"] * p["seg_len"], "budgets": p["L"] * p["H"],
          "states": p["segments"], "ghist": p["segments"] * K_BINS,

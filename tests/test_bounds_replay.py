@@ -138,3 +138,12 @@ def test_replay_sees_an_unguarded_access():
     acc.add("kv", pos * vecs)
     with pytest.raises(AssertionError):
         acc.check({"kv": n * vecs})
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("adaptive", [False, True])
+def test_select_pool_first_pass_stays_in_bounds(seed, adaptive):
+    rng = np.random.default_rng(500 + seed + 10 * adaptive)
+    p = _valid_uniform_plan(rng, adaptive, bool(seed % 2), True)
+    acc = br.msel_pool_accesses(p, p["n"])
+    acc.check({"raw": p["L"] * p["H"] * p["n"], "pooled": p["segments"] * p["seg_len"]})

@@ -236,6 +236,14 @@ POOL_SELECT_CASES = [
     (1, 2, 1000, 8, 0.3, False, False, 0.5, 50, 9),         # pool > 7
     (1, 4, 3000, 32, 0.4, True, False, 0.5, 50, 7),         # adaptive
     (1, 1, 50000, 32, 0.1, False, True, 0.5, 1000, 7),      # many workgroups
+    # many workgroups, pooled in the selection's first pass (radius <= 3)
+    (1, 2, 40000, 8, 0.3, True, False, 0.5, 50, 7),         # adaptive
+    (1, 2, 40001, 9, 0.3, True, True, 0.5, 300, 5),         # n % 4 != 0: 4-byte loads
+    (1, 1, 50003, 32, 0.2, False, False, 0.5, 1000, 3),     # n - W odd
+    (1, 1, 40000, 0, 0.2, False, False, 0.5, 1000, 1),      # no window, pool 1 (a copy)
+    (1, 3, 36000, 32, 0.5, False, False, 0.5, 1000000, 7),  # three heads
+    (2, 2, 35000, 32, 0.05, False, True, 1.0, 1000000, 7),  # two layers, two-stage
+    (1, 1, 40000, 16, 0.2, False, True, 0.5, 1000, 9),      # pool 9: the pool kernel first
 ]
 
 
