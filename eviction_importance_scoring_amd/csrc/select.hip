@@ -685,46 +685,46 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a) {
 //
 // Segments longer than kResidentMax (a whole layer when adaptive, or very
 // long heads) would leave most CUs idle with one workgroup each, so they
-// are spread over chunks of kChunk candidates. Each stage of the selection
-// runs:
-//   k_msel_init    per segment: state (prefix, shift, need) for the stage
-//                  (and, for the first, a cleared global histogram)
-//   k_msel_hist    per chunk, twice: histogram of the next 11-bit digit of
-//                  the score bits among the candidates that match the
-//                  prefix (in LDS: four copies on the first digit, where
-//                  keys crowd a few bins), added to the segment's global
-//                  histogram
-//   k_msel_pick    per segment, after each: the bin holding the need-th
-//                  largest key (bins read in descending order), the next
-//                  state, and a cleared histogram for the next digit
-//   k_msel_filter  per chunk: keys above the bucket are members (final
-//                  stage: bits of the chunk's member mask, and its member
-//                  count); keys in it go to the segment's short list
-//                  (score bits and index)
+// are spread over chunks of kChunk candidates. A stage of the selection is
+// four passes over the chunks and one per segment:
+//   round 0        per chunk: histogram of the first 11-bit digit of the
+//                  score bits (k_msel_hist; k_msel_pool when it also
+//                  max-pools the raw scores), added to the segment's global
+//                  histogram of the round
+//   round 1        per chunk: the bin holding the need-th largest key of
+//                  round 0 (every workgroup reads the 2048 bins and finds
+//                  the same one; the chunk-0 workgroup keeps the state),
+//                  then the histogram of the next 11 bits among the keys in
+//                  that bin
+//   k_msel_filter  per chunk: round 1's bin the same way; keys above the
+//                  bucket are members (final stage: bits of the chunk's
+//                  member mask, and its member count); keys in it go to the
+//                  segment's short list (score bits and index)
 //   k_msel_finish  per segment: the remaining rounds (the last 10 score
 //                  bits, then the index bits) over the list in LDS, until
 //                  the bucket is taken whole or holds one key. The stage
 //                  ends with an exact threshold key K: its members are the
 //                  keys >= K. In the final stage the listed members are
-//                  added to the mask and the chunk counts.
+//                  added to the mask and the chunk counts; after stage 1 it
+//                  sets up stage 2.
 // Two digits (22 of the 32 score bits) leave a few dozen keys in the
 // bucket on attention scores: each full pass over the scores is a
 // histogram or the filter, and the rounds below them run on the list. A
 // bucket too long for the list (heavy ties) is narrowed by k_msel_finish
 // itself, one workgroup streaming the segment per round. A segment whose
-// bucket is taken whole after a histogram round is done there: its members
-// are the keys >= prefix << shift, and later kernels of the stage only
-// read that. Stage 2 of the two-stage selection keys the stage-1 members
-// (keys >= K1) as +inf. Emission:
-//   k_msel_offsets per segment: exclusive scans over its chunks' member
-//                  counts, head offsets, window entries
-//   k_msel_emit    per chunk: the members of its mask in index order at
-//                  their ranks, staged in LDS and written with coalesced
-//                  stores
-// Chunks never straddle a head (group), so a group's first chunk offset is
-// the number of members before the group. Every sum runs in a fixed order
-// or over integers and K is unique (no two keys tie; the list's order
-// does not matter): the result is deterministic.
+// bucket is taken whole after a round is done there: its members are the
+// keys >= prefix << shift. Each round's state sits in a slot of its own
+// (0: the stage's start, 1: after round 0, 2: after round 1), written by
+// one workgroup of the kernel that computes it and read by later kernels
+// only, and each round has its own global histogram. Stage 2 of the
+// two-stage selection keys the stage-1 members (keys >= K1) as +inf.
+// Emission (k_msel_emit, per chunk): the members of its mask in index
+// order at their ranks (members before the chunk: a sum over the
+// segment's earlier chunks), staged in LDS and written with coalesced
+// stores; a group's last chunk also writes the group's window entries and
+// the first chunk its head offsets. Chunks never straddle a head (group).
+// Every sum runs in a fixed order or over integers and K is unique (no two
+// keys tie; the list's order does not matter): the result is deterministic.
 //
 // Every thread issues all of its kPerThread loads before it uses one: a
 // chunk's workgroup then waits for memory once.
@@ -734,25 +734,27 @@ constexpr int kPerThread = kChunk / kMThreads;     // 32
 constexpr int kMCopies = 4;                        // LDS histogram copies, first digit
 constexpr int kMaskWords = kChunk / 32;            // a chunk's member mask
 constexpr int kListCap = 1024;                     // bucket entries a segment's list holds
+constexpr int kSlots = 3;                          // states per segment (above)
+constexpr int kHistBufs = 3;                       // global histograms per segment (above)
 static_assert(kMaskWords == kMThreads, "k_msel_emit: one mask word a thread");
-static_assert(kBins == 4 * kMThreads, "k_msel_finish: four bins a thread");
+static_assert(kBins == 4 * kMThreads, "picks: four bins a thread");
 
 struct alignas(16) SegState {
-  uint64_t prefix;      // current stage: key prefix above `shift`
+  uint64_t prefix;      // key prefix above `shift`
   uint64_t thr1;        // two-stage, stage 2: stage-1 members are the keys >= thr1
   int32_t shift;
   uint32_t need, done;
-  uint32_t count;       // keys in the bucket the last pick chose
-  uint32_t listed;      // entries appended to the segment's list
+  uint32_t count;       // keys in the bucket the last round chose
+  uint32_t listed;      // slot 1: entries appended to the segment's list
   uint32_t pad[3];
 };
 
 struct MselArgs {
   const float* scores;
   const float* weight;
-  SegState* states;
-  uint32_t* ghist;      // [segments][kBins]
-  uint32_t* ccount;     // [segments][chunks]: members, then members before the chunk
+  SegState* states;     // [kSlots][segments]
+  uint32_t* ghist;      // [3][segments][kBins]: round 0 of stage 1, round 1, round 0 of stage 2
+  uint32_t* ccount;     // [segments][chunks]: members
   uint2* list;          // [segments][kListCap]: (score bits, index) of bucket keys
   uint32_t* mask;       // [segments][chunks][kMaskWords]: final members
   uint32_t* mask1;      // the same for stage-1 members (two-stage)
@@ -760,11 +762,18 @@ struct MselArgs {
   int32_t* head_offsets;
   uint8_t* stage;
   const int32_t* budgets;   // [L][H] or null
-  uint32_t seg_len, n_cand, groups, W, n, cpg, chunks, H;
+  uint32_t segs, seg_len, n_cand, groups, W, n, cpg, chunks, H;
   uint32_t k, k1;
   int64_t budget, stride;
   float score_norm, eps, alpha;
 };
+
+__device__ __forceinline__ SegState* msel_state(const MselArgs& a, int slot, uint32_t seg) {
+  return a.states + (size_t)slot * a.segs + seg;
+}
+__device__ __forceinline__ uint32_t* msel_ghist(const MselArgs& a, int buf, uint32_t seg) {
+  return a.ghist + ((size_t)buf * a.segs + seg) * kBins;
+}
 
 // Key bits of candidate f for the stage being selected, from its score s
 // and weight w (stage 2 of the two-stage selection: stage-1 members are
@@ -830,25 +839,18 @@ __device__ __forceinline__ void msel_load(const MselArgs& a, uint32_t seg, uint3
   }
 }
 
-// stage 1 (or the single stage): prefix 0 / need k. stage 2: the stage-1
-// threshold first. grid segments; stage 1 also clears the segment's global
-// histogram (the workspace may hold anything; each pick clears the bins
-// it read).
-__global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2) {
-  const uint32_t seg = blockIdx.x;
-  if (!stage2) {
-    uint32_t* gh = a.ghist + (size_t)seg * kBins;
-    for (int b = threadIdx.x; b < kBins; b += kMThreads) gh[b] = 0u;
-  }
-  if (threadIdx.x != 0) return;
-  SegState& st = a.states[seg];
-  // stage 1 ended with its members the keys >= prefix << shift
-  st.thr1 = stage2 ? st.prefix << st.shift : 0u;
+// A stage's start: prefix 0, need k (k1 for stage 1 of the two-stage
+// selection); nothing or everything is done at once.
+__device__ __forceinline__ SegState msel_start(const MselArgs& a, uint32_t seg, bool stage2,
+                                               uint64_t thr1) {
   const SegSpan sp = seg_span(a, (size_t)seg);
   const uint32_t k = (stage2 || sp.k1 == 0xFFFFFFFFu) ? sp.k : sp.k1;
+  SegState st;
+  st.thr1 = thr1;
   st.shift = 63;
   st.count = 0;
   st.listed = 0;
+  st.pad[0] = st.pad[1] = st.pad[2] = 0;
   if (k == 0) {          // nothing: (key >> 63) >= 1 holds for no key
     st.prefix = 1;
     st.need = 0;
@@ -862,36 +864,123 @@ __global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a, int stage2)
     st.need = k;
     st.done = 0;
   }
+  return st;
 }
 
-// grid chunks*segments (1-D): the digit below `shift` (63 or 52: both
-// histogram rounds lie in the score bits) among the keys in the bucket
-template <int COPIES, bool VEC>
-__global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2) {
-  __shared__ uint32_t hist[COPIES][kBins];
-  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
-  const SegState st = a.states[seg];
-  if (st.done || st.shift < 52) return;
+// grid segments: stage 1's (or the single stage's) start, and cleared
+// global histograms (the workspace may hold anything)
+__global__ __launch_bounds__(kMThreads) void k_msel_init(MselArgs a) {
+  const uint32_t seg = blockIdx.x;
+  for (int buf = 0; buf < kHistBufs; ++buf) {
+    uint32_t* gh = msel_ghist(a, buf, seg);
+    for (int b = threadIdx.x; b < kBins; b += kMThreads) gh[b] = 0u;
+  }
+  if (threadIdx.x == 0) *msel_state(a, 0, seg) = msel_start(a, seg, false, 0u);
+}
+
+__device__ __forceinline__ uint32_t block_sum256(uint32_t v, uint32_t* sbuf) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) sbuf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kMThreads / 64; ++w) t += sbuf[w];
+  __syncthreads();
+  return t;
+}
+
+// exclusive scan over the workgroup's threads (in thread order); total returned too
+__device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* sbuf, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sbuf[wave] = x;
+  __syncthreads();
+  uint32_t off = x - v, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kMThreads / 64; ++w) {
+    off += (w < wave) ? sbuf[w] : 0u;
+    tot += sbuf[w];
+  }
+  __syncthreads();
+  total = tot;
+  return off;
+}
+
+// Thread t's four bins of a round's global histogram, in descending bin
+// order (bins 2047-4t .. 2044-4t): loaded before the chunk's scores, so
+// that the pick waits for them only.
+__device__ __forceinline__ void pick_load(const uint32_t* gh, uint32_t (&h)[4]) {
+  const uint32_t* p = gh + (kBins - 4 - 4 * threadIdx.x);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  h[0] = v[3];
+  h[1] = v[2];
+  h[2] = v[1];
+  h[3] = v[0];
+}
+
+// The state after one more 11-bit digit (shift 63 or 52), from the
+// round's histogram: the bin where the count of larger keys first reaches
+// need (exactly one thread holds it). Every thread returns the same state.
+__device__ __forceinline__ SegState msel_pick(SegState st, const uint32_t (&h)[4], uint32_t* sbuf,
+                                              uint32_t* pk) {
+  if (st.done) return st;
   const int tid = threadIdx.x;
-  const int shift = st.shift, wdt = digit_width(shift), nb = 1 << wdt;
-  uint32_t g, begin, end;
-  msel_chunk(a, c, g, begin, end);
-  float s[kPerThread], w[kPerThread];
-  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
+  const uint32_t need = st.need;
+  const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+  uint32_t tot;
+  const uint32_t above = block_scan256(sum, sbuf, tot);
+  if (above < need && need <= above + sum) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (acc < need && need <= acc + h[j]) {
+        pk[0] = (uint32_t)(kBins - 1 - 4 * tid - j);
+        pk[1] = acc;
+        pk[2] = h[j];
+      }
+      acc += h[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t digit = pk[0], ab = pk[1], cnt = pk[2];
+  __syncthreads();   // read by every thread before pk is written again
+  st.prefix = (st.prefix << 11) | digit;
+  st.shift -= 11;
+  st.need = need - ab;
+  st.count = cnt;
+  st.listed = 0;
+  st.done = (st.need == cnt) ? 1u : 0u;
+  return st;
+}
+
+// Histogram of the digit below st.shift (63 or 52: both rounds lie in the
+// score bits) among the keys in the bucket, added to the round's global
+// histogram. Four candidates at a time (consecutive ones when VEC): when
+// all four fall in one bin, as neighbouring max-pooled scores mostly do on
+// the first digit, they add 4 with one atomic.
+template <int COPIES, bool VEC>
+__device__ __forceinline__ void msel_hist_chunk(const MselArgs& a, const SegState& st, bool stage2,
+                                                uint32_t begin, uint32_t end,
+                                                const float (&s)[kPerThread],
+                                                const float (&w)[kPerThread],
+                                                uint32_t (*hist)[kBins], uint32_t* gh) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int cp = 0; cp < COPIES; ++cp)
-    for (int b = tid; b < nb; b += kMThreads) hist[cp][b] = 0;
+    for (int b = tid; b < kBins; b += kMThreads) hist[cp][b] = 0;
   __syncthreads();
   uint32_t* hc = hist[tid & (COPIES - 1)];
   // keys (bits << 31) | (2^31 - 1 - f) with (key >> shift) == prefix are
   // those with bits in [lo, lo + 2^sh)
-  const uint32_t mask = (uint32_t)nb - 1u;
-  const uint32_t sh = shift - 31, dsh = shift - wdt - 31;
+  const uint32_t sh = st.shift - 31, dsh = sh - 11;
   const uint32_t lo = sh >= 32 ? 0u : (uint32_t)st.prefix << sh;
   const uint32_t span_m1 = sh >= 32 ? 0xFFFFFFFFu : (1u << sh) - 1u;
-  // four candidates at a time (consecutive ones when VEC): when all four
-  // fall in one bin, as neighbouring max-pooled scores mostly do on the
-  // first digit, they add 4 with one atomic
 #pragma unroll
   for (int u = 0; u < kPerThread / 4; ++u) {
     uint32_t bn[4];
@@ -900,9 +989,9 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
     for (int q = 0; q < 4; ++q) {
       const int i = 4 * u + q;
       const uint32_t f = begin + msel_e<VEC>(i);
-      const uint32_t b = msel_bits(a, st, s[i], w[i], stage2 != 0, f);
+      const uint32_t b = msel_bits(a, st, s[i], w[i], stage2, f);
       ok[q] = f < end && b - lo <= span_m1;
-      bn[q] = (b >> dsh) & mask;
+      bn[q] = (b >> dsh) & (kBins - 1u);
     }
     if (ok[0] && ok[1] && ok[2] && ok[3] && bn[0] == bn[1] && bn[1] == bn[2] && bn[2] == bn[3]) {
       atomicAdd(&hc[bn[0]], 4u);
@@ -913,13 +1002,51 @@ __global__ __launch_bounds__(kMThreads) void k_msel_hist(MselArgs a, int stage2)
     }
   }
   __syncthreads();
-  uint32_t* gh = a.ghist + (size_t)seg * kBins;
-  for (int b = tid; b < nb; b += kMThreads) {
+  for (int b = tid; b < kBins; b += kMThreads) {
     uint32_t v = 0;
 #pragma unroll
     for (int cp = 0; cp < COPIES; ++cp) v += hist[cp][b];
     if (v) atomicAdd(gh + b, v);
   }
+}
+
+// grid chunks*segments: round 0 of a stage (its start in slot 0). The
+// stage is a template argument so that stage 1 holds no weights (fewer
+// registers, more workgroups per CU).
+template <bool VEC, bool S2>
+__global__ __launch_bounds__(kMThreads) void k_msel_hist0(MselArgs a) {
+  constexpr int stage2 = S2 ? 1 : 0;
+  __shared__ uint32_t hist[kMCopies][kBins];
+  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
+  const SegState st = *msel_state(a, 0, seg);
+  if (st.done) return;
+  uint32_t g, begin, end;
+  msel_chunk(a, c, g, begin, end);
+  float s[kPerThread], w[kPerThread];
+  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
+  msel_hist_chunk<kMCopies, VEC>(a, st, stage2 != 0, begin, end, s, w, hist,
+                                 msel_ghist(a, S2 ? 2 : 0, seg));
+}
+
+// grid chunks*segments: round 1 (round 0's bin picked from its histogram;
+// the chunk-0 workgroup keeps the state in slot 1)
+template <bool VEC, bool S2>
+__global__ __launch_bounds__(kMThreads) void k_msel_hist1(MselArgs a) {
+  constexpr int stage2 = S2 ? 1 : 0;
+  __shared__ uint32_t hist[1][kBins];
+  __shared__ uint32_t sbuf[kMThreads / 64], pk[3];
+  const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
+  const SegState st0 = *msel_state(a, 0, seg);
+  uint32_t h[4];
+  pick_load(msel_ghist(a, S2 ? 2 : 0, seg), h);
+  uint32_t g, begin, end;
+  msel_chunk(a, c, g, begin, end);
+  float s[kPerThread], w[kPerThread];
+  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
+  const SegState st = msel_pick(st0, h, sbuf, pk);
+  if (c == 0 && threadIdx.x == 0) *msel_state(a, 1, seg) = st;
+  if (st.done) return;
+  msel_hist_chunk<1, VEC>(a, st, stage2 != 0, begin, end, s, w, hist, msel_ghist(a, 1, seg));
 }
 
 // Pooling in the first pass (kvsel_select_pool on raw rows, radius R <=
@@ -940,7 +1067,7 @@ constexpr size_t kPoolLdsBytes = kPoolTileBytes + kBins * sizeof(uint32_t);
 constexpr int kPoolLoadsV = ((kChunk + 2 * kPoolHalo) / 4 + kMThreads - 1) / kMThreads;   // 16-byte units
 constexpr int kPoolLoads = (kChunk + 2 * kPoolHalo + kMThreads - 1) / kMThreads;          // 4-byte loads
 
-// grid chunks*segments. raw: row (seg * groups + g) holds group g's
+// grid chunks*segments: round 0 of stage 1. raw: row (seg * groups + g) holds group g's
 // candidates, in_stride floats apart. VEC: n_cand and in_stride multiples
 // of 4 (every chunk and its halo in whole 16-byte units).
 template <int R, bool VEC>
@@ -955,7 +1082,7 @@ __global__ __launch_bounds__(kMThreads) void k_msel_pool(MselArgs a, const float
   msel_chunk(a, c, g, begin, end);
   const uint32_t len = end - begin, pos0 = begin - g * a.n_cand;
   const float* row = raw + ((size_t)seg * a.groups + g) * (size_t)in_stride;
-  const bool do_hist = !a.states[seg].done;
+  const bool do_hist = !msel_state(a, 0, seg)->done;
   // tile x holds candidate pos0 - kPoolHalo + x; -inf outside the candidates
   const uint32_t nx = len + 2 * kPoolHalo;
   const float ninf = -__builtin_inff();
@@ -1050,136 +1177,62 @@ __global__ __launch_bounds__(kMThreads) void k_msel_pool(MselArgs a, const float
     }
   }
   if (do_hist) {
-    uint32_t* gh = a.ghist + (size_t)seg * kBins;
+    uint32_t* gh = msel_ghist(a, 0, seg);
     for (int b = tid; b < kBins; b += kMThreads)
       if (hist[b]) atomicAdd(gh + b, hist[b]);
   }
 }
 
-// grid segments: thread t owns bins nb-1-8t .. nb-8-8t (descending);
-// exactly one thread holds the bin where the count of larger keys first
-// reaches need
-__global__ __launch_bounds__(kMThreads) void k_msel_pick(MselArgs a) {
-  __shared__ uint32_t sbuf[kMThreads / 64];
-  __shared__ uint32_t s_digit, s_above, s_count;
-  const uint32_t seg = blockIdx.x;
-  SegState& st = a.states[seg];
-  if (st.done) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int shift = st.shift, wdt = digit_width(shift), nb = 1 << wdt;
-  const uint32_t need = st.need;
-  uint32_t* gh = a.ghist + (size_t)seg * kBins;
-  uint32_t h[8], sum = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int b = nb - 1 - 8 * tid - j;
-    h[j] = b >= 0 ? gh[b] : 0u;
-    sum += h[j];
-  }
-  // exclusive scan of the per-thread sums (descending bin order)
-  uint32_t x = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sbuf[wave] = x;
-  __syncthreads();
-  uint32_t above = x - sum;
-  for (int w = 0; w < wave; ++w) above += sbuf[w];
-  if (above < need && need <= above + sum) {   // exactly one thread
-    uint32_t acc = above;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (acc < need && need <= acc + h[j]) {
-        s_digit = (uint32_t)(nb - 1 - 8 * tid - j);
-        s_above = acc;
-        s_count = h[j];
-      }
-      acc += h[j];
-    }
-  }
-  __syncthreads();
-  // clear this digit's bins for the next round
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int b = nb - 1 - 8 * tid - j;
-    if (b >= 0) gh[b] = 0u;
-  }
-  if (tid == 0) {
-    st.prefix = (st.prefix << wdt) | s_digit;
-    st.shift = shift - wdt;
-    st.need = need - s_above;
-    st.count = s_count;
-    st.done = (st.need == s_count || st.shift == 0) ? 1u : 0u;
-  }
-}
-
-__device__ __forceinline__ uint32_t block_sum256(uint32_t v, uint32_t* sbuf) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  if ((threadIdx.x & 63) == 0) sbuf[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kMThreads / 64; ++w) t += sbuf[w];
-  __syncthreads();
-  return t;
-}
-
-// exclusive scan over the workgroup's threads (in thread order); total returned too
-__device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t* sbuf, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sbuf[wave] = x;
-  __syncthreads();
-  uint32_t off = x - v, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kMThreads / 64; ++w) {
-    off += (w < wave) ? sbuf[w] : 0u;
-    tot += sbuf[w];
-  }
-  __syncthreads();
-  total = tot;
-  return off;
-}
-
-// grid chunks*segments. After the histogram rounds (shift 63, 52 or 41,
-// all in the score bits, so (key >> shift) is bits >> (shift - 31)): the
-// final stage's members above the bucket (all of it when done) go to the
-// chunk's mask and count; the bucket's keys, when they fit the list, to
-// the segment's list.
-template <bool VEC>
-__global__ __launch_bounds__(kMThreads) void k_msel_filter(MselArgs a, int stage2, int final) {
+// grid chunks*segments: round 1's bin picked from its histogram (the
+// chunk-0 workgroup keeps the state in slot 2). Then the final stage's
+// members above the bucket (all of it when done) go to the chunk's mask
+// and count; the bucket's keys, when they fit the list, to the segment's
+// list. Both rounds stopped at shift 63, 52 or 41, all in the score bits,
+// so (key >> shift) is bits >> (shift - 31).
+//
+// H2 (stage 1 of the two-stage selection): each key's stage-1 membership is
+// known here except in the bucket, so this pass also loads the weights and
+// adds stage 2's first-digit histogram (buffer 2) for the other keys;
+// k_msel_finish adds the bucket's once it has K1.
+template <bool VEC, bool S2, bool H2>
+__global__ __launch_bounds__(kMThreads) void k_msel_filter(MselArgs a, int final) {
+  constexpr int stage2 = S2 ? 1 : 0;
   __shared__ uint32_t mw[kMaskWords], m1w[kMaskWords];
+  __shared__ uint32_t h2[H2 ? kMCopies : 1][kBins];
   __shared__ uint2 lst[kListCap];
-  __shared__ uint32_t sbuf[kMThreads / 64];
+  __shared__ uint32_t sbuf[kMThreads / 64], pk[3];
   __shared__ uint32_t s_n, s_base;
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
-  const SegState st = a.states[seg];
-  const bool listing = !st.done && st.count <= (uint32_t)kListCap;
-  if (!final && !listing) return;
   const int tid = threadIdx.x;
+  const SegState st1 = *msel_state(a, 1, seg);
+  uint32_t h[4];
+  pick_load(msel_ghist(a, 1, seg), h);
   uint32_t g, begin, end;
   msel_chunk(a, c, g, begin, end);
   float s[kPerThread], w[kPerThread];
-  msel_load<VEC>(a, seg, begin, end, stage2 != 0, s, w);
+  msel_load<VEC>(a, seg, begin, end, S2 || H2, s, w);
+  const SegState st = msel_pick(st1, h, sbuf, pk);
+  if (c == 0 && tid == 0) *msel_state(a, 2, seg) = st;
+  const bool listing = !st.done && st.count <= (uint32_t)kListCap;
+  if (!final && !listing && !H2) return;
   mw[tid] = 0u;
   m1w[tid] = 0u;
   if (tid == 0) s_n = 0u;
+  if constexpr (H2) {
+#pragma unroll
+    for (int cp = 0; cp < kMCopies; ++cp)
+      for (int b = tid; b < kBins; b += kMThreads) h2[cp][b] = 0u;
+  }
   __syncthreads();
+  uint32_t* h2c = h2[H2 ? (tid & (kMCopies - 1)) : 0];
   const uint32_t sh = (uint32_t)st.shift - 31u, pref = (uint32_t)st.prefix;
   uint32_t nmem = 0;
 #pragma unroll
   for (int u = 0; u < kPerThread / 4; ++u) {
     // VEC: the four candidates share a mask word (one LDS atomic); else a
     // wave's 64 candidates are two whole words of its own (a ballot)
-    uint32_t word = 0u, word1 = 0u;
+    uint32_t word = 0u, word1 = 0u, bin2[4];
+    bool ok2[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 4 * u + q;
@@ -1209,6 +1262,20 @@ __global__ __launch_bounds__(kMThreads) void k_msel_filter(MselArgs a, int stage
         const uint32_t p = atomicAdd(&s_n, 1u);   // < count <= kListCap
         if (p < (uint32_t)kListCap) lst[p] = uint2{b, f};
       }
+      if constexpr (H2) {   // stage 2's key: stage-1 members +inf
+        ok2[q] = valid && (st.done || top != pref);
+        bin2[q] = (mem ? kInfBits : stage2_bits(s[i], w[i], a.score_norm, a.eps)) >> 21;
+      }
+    }
+    if constexpr (H2) {
+      if (ok2[0] && ok2[1] && ok2[2] && ok2[3] && bin2[0] == bin2[1] && bin2[1] == bin2[2] &&
+          bin2[2] == bin2[3]) {
+        atomicAdd(&h2c[bin2[0]], 4u);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (ok2[q]) atomicAdd(&h2c[bin2[q]], 1u);
+      }
     }
     if constexpr (VEC) {
       const uint32_t wi = msel_e<true>(4 * u) >> 5;
@@ -1217,6 +1284,15 @@ __global__ __launch_bounds__(kMThreads) void k_msel_filter(MselArgs a, int stage
     }
   }
   __syncthreads();
+  if constexpr (H2) {
+    uint32_t* gh = msel_ghist(a, 2, seg);
+    for (int b = tid; b < kBins; b += kMThreads) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int cp = 0; cp < kMCopies; ++cp) v += h2[cp][b];
+      if (v) atomicAdd(gh + b, v);
+    }
+  }
   if (final) {
     const size_t wb = ((size_t)seg * a.chunks + c) * kMaskWords;
     a.mask[wb + tid] = mw[tid];
@@ -1225,8 +1301,9 @@ __global__ __launch_bounds__(kMThreads) void k_msel_filter(MselArgs a, int stage
     if (tid == 0) a.ccount[(size_t)seg * a.chunks + c] = nmem;
   }
   if (listing) {
+    // slot 1 is read-only in this kernel: its count takes the appends
     const uint32_t nl = min(s_n, (uint32_t)kListCap);
-    if (tid == 0 && nl) s_base = atomicAdd(&a.states[seg].listed, nl);
+    if (tid == 0 && nl) s_base = atomicAdd(&msel_state(a, 1, seg)->listed, nl);
     __syncthreads();
     uint2* out = a.list + (size_t)seg * kListCap;
     for (uint32_t j = tid; j < nl; j += kMThreads)
@@ -1244,176 +1321,158 @@ __device__ __forceinline__ void msel_mark(const MselArgs& a, uint32_t seg, uint3
   atomicAdd(&a.ccount[ch], 1u);
 }
 
-// grid segments: the rounds below the filter's bucket, down to an exact
-// threshold key K (the stage's members are the keys >= K), left in the
-// state as prefix K, shift 0
+// grid segments: the rounds below the filter's bucket (state in slot 2),
+// down to an exact threshold key K: the stage's members are the keys >= K.
+// Final stage: the bucket's members go to the masks. Stage 1 of the
+// two-stage selection: the rest of stage 2's first histogram, its start
+// (slot 0) and a cleared round-1 histogram.
 __global__ __launch_bounds__(kMThreads) void k_msel_finish(MselArgs a, int stage2, int final) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t lb[kListCap], lf[kListCap];
   __shared__ uint32_t sbuf[kMThreads / 64];
   __shared__ uint32_t s_digit, s_above, s_count;
   const uint32_t seg = blockIdx.x;
-  const SegState st = a.states[seg];
-  if (st.done) return;     // taken whole: the members are the keys >= prefix << shift
+  const SegState st = *msel_state(a, 2, seg);
   const int tid = threadIdx.x;
-  const bool listed = st.count <= (uint32_t)kListCap;
-  const uint32_t m = listed ? st.count : 0u;
-  const float* sc = a.scores + (size_t)seg * a.seg_len;
-  const float* wt = stage2 ? a.weight + (size_t)seg * a.seg_len : nullptr;
-  for (uint32_t j = tid; j < m; j += kMThreads) {
-    const uint2 v = a.list[(size_t)seg * kListCap + j];
-    lb[j] = v.x;
-    lf[j] = v.y;
-  }
-  for (int b = tid; b < kBins; b += kMThreads) hist[b] = 0u;
-  __syncthreads();
-  uint64_t prefix = st.prefix;
-  int shift = st.shift;
-  uint32_t need = st.need;
-  for (;;) {
-    const int wdt = digit_width(shift);
-    const int nb = 1 << wdt;
-    const uint32_t dmask = (uint32_t)nb - 1u;
-    if (listed) {
-      for (uint32_t j = tid; j < m; j += kMThreads) {
-        const uint64_t key = make_key(lb[j], lf[j]);
-        if ((key >> shift) == prefix) atomicAdd(&hist[(uint32_t)(key >> (shift - wdt)) & dmask], 1u);
-      }
-    } else {   // the bucket outgrew the list: one workgroup streams the segment
-      for (uint32_t f = tid; f < a.seg_len; f += kMThreads) {
-        const uint64_t key = make_key(msel_bits(a, st, sc[f], wt ? wt[f] : 0.f, stage2 != 0, f), f);
-        if ((key >> shift) == prefix) atomicAdd(&hist[(uint32_t)(key >> (shift - wdt)) & dmask], 1u);
-      }
+  uint64_t K = st.prefix << st.shift;   // taken whole: the keys >= prefix << shift
+  if (!st.done) {
+    const bool listed = st.count <= (uint32_t)kListCap;
+    const uint32_t m = listed ? st.count : 0u;
+    const float* sc = a.scores + (size_t)seg * a.seg_len;
+    const float* wt = stage2 ? a.weight + (size_t)seg * a.seg_len : nullptr;
+    for (uint32_t j = tid; j < m; j += kMThreads) {
+      const uint2 v = a.list[(size_t)seg * kListCap + j];
+      lb[j] = v.x;
+      lf[j] = v.y;
     }
+    for (int b = tid; b < kBins; b += kMThreads) hist[b] = 0u;
     __syncthreads();
-    // bins in descending order, four a thread
-    uint32_t h[4], sum = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int b = nb - 1 - 4 * tid - j;
-      h[j] = b >= 0 ? hist[b] : 0u;
-      sum += h[j];
-    }
-    uint32_t tot;
-    const uint32_t above = block_scan256(sum, sbuf, tot);
-    if (above < need && need <= above + sum) {   // exactly one thread
-      uint32_t acc = above;
+    uint64_t prefix = st.prefix;
+    int shift = st.shift;
+    uint32_t need = st.need;
+    for (;;) {
+      const int wdt = digit_width(shift);
+      const int nb = 1 << wdt;
+      const uint32_t dmask = (uint32_t)nb - 1u;
+      if (listed) {
+        for (uint32_t j = tid; j < m; j += kMThreads) {
+          const uint64_t key = make_key(lb[j], lf[j]);
+          if ((key >> shift) == prefix) atomicAdd(&hist[(uint32_t)(key >> (shift - wdt)) & dmask], 1u);
+        }
+      } else {   // the bucket outgrew the list: one workgroup streams the segment
+        for (uint32_t f = tid; f < a.seg_len; f += kMThreads) {
+          const uint64_t key = make_key(msel_bits(a, st, sc[f], wt ? wt[f] : 0.f, stage2 != 0, f), f);
+          if ((key >> shift) == prefix) atomicAdd(&hist[(uint32_t)(key >> (shift - wdt)) & dmask], 1u);
+        }
+      }
+      __syncthreads();
+      // bins in descending order, four a thread
+      uint32_t h[4], sum = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (acc < need && need <= acc + h[j]) {
-          s_digit = (uint32_t)(nb - 1 - 4 * tid - j);
-          s_above = acc;
-          s_count = h[j];
-        }
-        acc += h[j];
+        const int b = nb - 1 - 4 * tid - j;
+        h[j] = b >= 0 ? hist[b] : 0u;
+        sum += h[j];
       }
-    }
-    __syncthreads();
+      uint32_t tot;
+      const uint32_t above = block_scan256(sum, sbuf, tot);
+      if (above < need && need <= above + sum) {   // exactly one thread
+        uint32_t acc = above;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int b = nb - 1 - 4 * tid - j;
-      if (b >= 0) hist[b] = 0u;
-    }
-    prefix = (prefix << wdt) | s_digit;
-    shift -= wdt;
-    need -= s_above;
-    const uint32_t dcount = s_count;
-    __syncthreads();   // s_digit/above/count read and the bins cleared before the next round
-    if (need == dcount || shift == 0) break;
-  }
-  const uint64_t K = prefix << shift;
-  if (final) {
-    if (listed) {
-      for (uint32_t j = tid; j < m; j += kMThreads)
-        if (make_key(lb[j], lf[j]) >= K) msel_mark(a, seg, lf[j]);
-    } else {
-      // the bucket's members: keys in it (the filter marked those above)
-      // and >= K, a mask word a thread
-      for (uint32_t c = 0; c < a.chunks; ++c) {
-        uint32_t g, begin, end;
-        msel_chunk(a, c, g, begin, end);
-        uint32_t bits = 0u;
-        for (int j = 0; j < 32; ++j) {
-          const uint32_t f = begin + 32u * tid + j;
-          if (f < end) {
-            const uint64_t key = make_key(msel_bits(a, st, sc[f], wt ? wt[f] : 0.f, stage2 != 0, f), f);
-            if ((key >> st.shift) == st.prefix && key >= K) bits |= 1u << j;
+        for (int j = 0; j < 4; ++j) {
+          if (acc < need && need <= acc + h[j]) {
+            s_digit = (uint32_t)(nb - 1 - 4 * tid - j);
+            s_above = acc;
+            s_count = h[j];
           }
+          acc += h[j];
         }
-        const size_t ch = (size_t)seg * a.chunks + c;
-        if (bits) atomicOr(&a.mask[ch * kMaskWords + tid], bits);
-        const uint32_t cnt = block_sum256((uint32_t)__popc(bits), sbuf);
-        if (tid == 0 && cnt) atomicAdd(&a.ccount[ch], cnt);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = nb - 1 - 4 * tid - j;
+        if (b >= 0) hist[b] = 0u;
+      }
+      prefix = (prefix << wdt) | s_digit;
+      shift -= wdt;
+      need -= s_above;
+      const uint32_t dcount = s_count;
+      __syncthreads();   // s_digit/above/count read and the bins cleared before the next round
+      if (need == dcount || shift == 0) break;
+    }
+    K = prefix << shift;
+    if (final) {
+      if (listed) {
+        for (uint32_t j = tid; j < m; j += kMThreads)
+          if (make_key(lb[j], lf[j]) >= K) msel_mark(a, seg, lf[j]);
+      } else {
+        // the bucket's members: keys in it (the filter marked those above)
+        // and >= K, a mask word a thread
+        for (uint32_t c = 0; c < a.chunks; ++c) {
+          uint32_t g, begin, end;
+          msel_chunk(a, c, g, begin, end);
+          uint32_t bits = 0u;
+          for (int j = 0; j < 32; ++j) {
+            const uint32_t f = begin + 32u * tid + j;
+            if (f < end) {
+              const uint64_t key = make_key(msel_bits(a, st, sc[f], wt ? wt[f] : 0.f, stage2 != 0, f), f);
+              if ((key >> st.shift) == st.prefix && key >= K) bits |= 1u << j;
+            }
+          }
+          const size_t ch = (size_t)seg * a.chunks + c;
+          if (bits) atomicOr(&a.mask[ch * kMaskWords + tid], bits);
+          const uint32_t cnt = block_sum256((uint32_t)__popc(bits), sbuf);
+          if (tid == 0 && cnt) atomicAdd(&a.ccount[ch], cnt);
+        }
       }
     }
   }
-  if (tid == 0) {
-    SegState& gs = a.states[seg];
-    gs.prefix = K;
-    gs.shift = 0;
-    gs.need = 0;
-    gs.done = 1;
-  }
-}
-
-// grid segments: per chunk, the members before it (in place of its
-// count); head offsets and window entries
-__global__ __launch_bounds__(kMThreads) void k_msel_offsets(MselArgs a) {
-  __shared__ uint32_t sbuf[kMThreads / 64];
-  __shared__ uint32_t gstart[kMaxGroups];   // members before each group
-  const uint32_t seg = blockIdx.x;
-  const int tid = threadIdx.x;
-  uint32_t* cc = a.ccount + (size_t)seg * a.chunks;
-  uint32_t run = 0;
-  for (uint32_t base = 0; base < a.chunks; base += kMThreads) {
-    const uint32_t c = base + tid;
-    const uint32_t na = c < a.chunks ? cc[c] : 0u;
-    uint32_t tot;
-    const uint32_t memoff = run + block_scan256(na, sbuf, tot);
-    if (c < a.chunks) {
-      cc[c] = memoff;
-      if (c % a.cpg == 0) gstart[c / a.cpg] = memoff;
-    }
-    run += tot;
-  }
-  __syncthreads();
-  const SegSpan sp = seg_span(a, (size_t)seg);
-  int32_t* out = a.idx + sp.base;
-  uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
-  for (uint32_t g = 0; g < a.groups; ++g) {
-    const uint32_t end_rank = (g + 1 < a.groups) ? gstart[g + 1] : sp.k;
-    const int64_t end = (int64_t)end_rank + (int64_t)(g + 1) * a.W;
-    for (uint32_t t = tid; t < a.W; t += kMThreads) {
-      const int64_t o = end - a.W + t;
-      if (o >= 0 && o < sp.room) {
-        out[o] = (int32_t)(a.n - a.W + t);
-        if (st_out) st_out[o] = 0;
+  if (!final) {
+    // stage 2's first-digit histogram (buffer 2): the filter added every
+    // key outside the bucket; the bucket's keys are added here, +inf for
+    // the stage-1 members (keys >= K)
+    uint32_t* g2 = msel_ghist(a, 2, seg);
+    const float* sc = a.scores + (size_t)seg * a.seg_len;
+    const float* wt = a.weight + (size_t)seg * a.seg_len;
+    if (!st.done && st.count <= (uint32_t)kListCap) {
+      for (uint32_t j = tid; j < st.count; j += kMThreads) {
+        const uint32_t f = lf[j];
+        if (f < a.seg_len) {
+          const uint32_t b2 = make_key(lb[j], f) >= K
+                                  ? kInfBits
+                                  : stage2_bits(bits_score(lb[j]), wt[f], a.score_norm, a.eps);
+          atomicAdd(&g2[b2 >> 21], 1u);
+        }
+      }
+    } else if (!st.done) {
+      for (uint32_t f = tid; f < a.seg_len; f += kMThreads) {
+        const float x = sc[f];
+        const uint64_t key = make_key(score_bits(x), f);
+        if ((key >> st.shift) == st.prefix) {
+          const uint32_t b2 = key >= K ? kInfBits : stage2_bits(x, wt[f], a.score_norm, a.eps);
+          atomicAdd(&g2[b2 >> 21], 1u);
+        }
       }
     }
-    if (a.head_offsets && !a.budgets && tid == 0)
-      a.head_offsets[(size_t)seg * (a.groups + 1) + g] = (int32_t)(gstart[g] + g * a.W);
+    // round 1's histogram: every stage-1 reader has finished
+    uint32_t* g1 = msel_ghist(a, 1, seg);
+    for (int b = tid; b < kBins; b += kMThreads) g1[b] = 0u;
+    if (tid == 0) *msel_state(a, 0, seg) = msel_start(a, seg, true, K);
   }
-  if (a.budgets) {
-    const size_t l = seg / a.H;
-    const uint32_t h = (uint32_t)(seg - l * a.H);
-    if (tid == 0) a.head_offsets[l * (a.H + 1) + h] = (int32_t)sp.off;
-    if (h + 1 == a.H) {
-      if (tid == 0) a.head_offsets[l * (a.H + 1) + a.H] = (int32_t)sp.end;
-      fill_row_tail(a.idx, a.stage, (int64_t)l * a.stride, sp.end, a.stride, tid, kMThreads);
-    }
-    return;
-  }
-  if (a.head_offsets && tid == 0)
-    a.head_offsets[(size_t)seg * (a.groups + 1) + a.groups] = (int32_t)a.budget;
 }
 
 // grid chunks*segments: thread t takes mask word t (the chunk's candidates
 // 32t .. 32t+31); a block scan of the words' member counts gives each
-// member its rank in index order. The chunk's members take consecutive
-// output slots: they are staged by rank in LDS and stored with coalesced
-// writes. Two-stage: stage-1 members are marked 1, the others 2.
+// member its rank in index order after the members of the segment's
+// earlier chunks. The chunk's members take consecutive output slots: they
+// are staged by rank in LDS and stored with coalesced writes. Two-stage:
+// stage-1 members are marked 1, the others 2. A group's first chunk writes
+// its head offset (budget vector: the segment's first chunk writes the
+// head's and, for a layer's last head, the row tail), its last chunk the
+// group's window entries after its members.
 __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int two_stage) {
-  __shared__ uint32_t staged[kChunk];
+  __shared__ uint16_t staged[kChunk];
   __shared__ uint32_t sbuf[kMThreads / 64];
   const uint32_t seg = blockIdx.x / a.chunks, c = blockIdx.x - seg * a.chunks;
   const int tid = threadIdx.x;
@@ -1422,28 +1481,57 @@ __global__ __launch_bounds__(kMThreads) void k_msel_emit(MselArgs a, int two_sta
   const size_t ch = (size_t)seg * a.chunks + c;
   const uint32_t mm = a.mask[ch * kMaskWords + tid];
   const uint32_t m1 = two_stage ? a.mask1[ch * kMaskWords + tid] : 0xFFFFFFFFu;
-  const uint32_t rank0 = a.ccount[ch];
+  uint32_t part = 0;
+  for (uint32_t j = tid; j < c; j += kMThreads) part += a.ccount[(size_t)seg * a.chunks + j];
+  const uint32_t rank0 = block_sum256(part, sbuf);   // members before the chunk
   uint32_t count;
   uint32_t r = block_scan256((uint32_t)__popc(mm), sbuf, count);   // members before this thread's
-  // staged[r] = position in its head of the chunk's member of rank r, bit
-  // 31 set for a stage-2 member of the two-stage selection
-  const uint32_t pos0 = begin - g * a.n_cand + tid * 32u;
+  // staged[r] = position in the chunk of its member of rank r (< 2^14),
+  // bit 15 set for a stage-2 member of the two-stage selection
+  static_assert(kChunk <= (1 << 15), "chunk positions and the stage bit fit 16 bits");
   for (uint32_t m = mm; m != 0; m &= m - 1, ++r) {
     const uint32_t j = (uint32_t)__builtin_ctz(m);
-    staged[r] = (pos0 + j) | (((m1 >> j) & 1u) ? 0u : 0x80000000u);
+    staged[r] = (uint16_t)((tid * 32u + j) | (((m1 >> j) & 1u) ? 0u : 0x8000u));
   }
   __syncthreads();
   const SegSpan sp = seg_span(a, (size_t)seg);
   int32_t* out = a.idx + sp.base;
   uint8_t* st_out = a.stage ? a.stage + sp.base : nullptr;
   const int64_t o0 = (int64_t)rank0 + (int64_t)g * a.W;
+  const uint32_t pos0 = begin - g * a.n_cand;   // the chunk's first position in its head
   for (uint32_t i = tid; i < count; i += kMThreads) {
     const int64_t o = o0 + i;
     if (o < sp.room) {   // k members fit the budget; the room may be cut at the row's end
       const uint32_t e = staged[i];
-      out[o] = (int32_t)(e & 0x7FFFFFFFu);
-      if (st_out) st_out[o] = (e >> 31) ? 2 : 1;
+      out[o] = (int32_t)(pos0 + (e & 0x7FFFu));
+      if (st_out) st_out[o] = (e >> 15) ? 2 : 1;
     }
+  }
+  const uint32_t cc = c - g * a.cpg;
+  if (cc + 1 == a.cpg) {
+    // the group's window entries, after its members
+    const int64_t wb = (int64_t)rank0 + count + (int64_t)g * a.W;
+    for (uint32_t t = tid; t < a.W; t += kMThreads) {
+      const int64_t o = wb + t;
+      if (o >= 0 && o < sp.room) {
+        out[o] = (int32_t)(a.n - a.W + t);
+        if (st_out) st_out[o] = 0;
+      }
+    }
+  }
+  if (a.budgets) {
+    if (c == 0) {
+      const size_t l = seg / a.H;
+      const uint32_t h = (uint32_t)(seg - l * a.H);
+      if (tid == 0) a.head_offsets[l * (a.H + 1) + h] = (int32_t)sp.off;
+      if (h + 1 == a.H) {
+        if (tid == 0) a.head_offsets[l * (a.H + 1) + a.H] = (int32_t)sp.end;
+        fill_row_tail(a.idx, a.stage, (int64_t)l * a.stride, sp.end, a.stride, tid, kMThreads);
+      }
+    }
+  } else if (a.head_offsets && tid == 0) {
+    if (cc == 0) a.head_offsets[(size_t)seg * (a.groups + 1) + g] = (int32_t)(rank0 + g * a.W);
+    if (c == 0) a.head_offsets[(size_t)seg * (a.groups + 1) + a.groups] = (int32_t)a.budget;
   }
 }
 
@@ -1461,8 +1549,8 @@ static MselLayout msel_layout(const SelectPlan& p) {
   m.chunks = groups * m.cpg;
   const size_t chunks = (size_t)p.segments * m.chunks;
   m.states_off = 0;
-  m.ghist_off = al256s((size_t)p.segments * sizeof(SegState));
-  m.ccount_off = m.ghist_off + al256s((size_t)p.segments * kBins * sizeof(uint32_t));
+  m.ghist_off = al256s((size_t)kSlots * p.segments * sizeof(SegState));
+  m.ccount_off = m.ghist_off + al256s((size_t)kHistBufs * p.segments * kBins * sizeof(uint32_t));
   m.list_off = m.ccount_off + al256s(chunks * sizeof(uint32_t));
   m.mask_off = m.list_off + al256s((size_t)p.segments * kListCap * sizeof(uint2));
   m.mask1_off = m.mask_off + al256s(chunks * kMaskWords * sizeof(uint32_t));
@@ -1471,6 +1559,30 @@ static MselLayout msel_layout(const SelectPlan& p) {
 }
 
 static bool use_multi(const SelectPlan& p) { return p.seg_len > kResidentMax; }
+
+// pass 0: k_msel_hist0, 1: k_msel_hist1, 2: k_msel_filter, for the load
+// width and the stage
+template <int PASS>
+static void launch_msel_passes(bool vec, bool s2, dim3 grid, hipStream_t st, const MselArgs& a,
+                               int final, bool h2 = false) {
+  auto go = [&](auto v, auto t) {
+    constexpr bool V = decltype(v)::value, T = decltype(t)::value;
+    if constexpr (PASS == 0)
+      hipLaunchKernelGGL((k_msel_hist0<V, T>), grid, dim3(kMThreads), 0, st, a);
+    else if constexpr (PASS == 1)
+      hipLaunchKernelGGL((k_msel_hist1<V, T>), grid, dim3(kMThreads), 0, st, a);
+    else if constexpr (T)
+      hipLaunchKernelGGL((k_msel_filter<V, true, false>), grid, dim3(kMThreads), 0, st, a, final);
+    else if (h2)
+      hipLaunchKernelGGL((k_msel_filter<V, false, true>), grid, dim3(kMThreads), 0, st, a, final);
+    else
+      hipLaunchKernelGGL((k_msel_filter<V, false, false>), grid, dim3(kMThreads), 0, st, a, final);
+  };
+  if (vec && s2) go(std::true_type{}, std::true_type{});
+  else if (vec) go(std::true_type{}, std::false_type{});
+  else if (s2) go(std::false_type{}, std::true_type{});
+  else go(std::false_type{}, std::false_type{});
+}
 
 template <int R>
 static hipError_t launch_msel_pool(const MselArgs& a, const float* raw, int64_t in_stride,
@@ -1509,6 +1621,7 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   a.idx = idx;
   a.head_offsets = p.adaptive ? head_offsets : nullptr;
   a.stage = stage;
+  a.segs = (uint32_t)p.segments;
   a.seg_len = (uint32_t)p.seg_len;
   a.n_cand = (uint32_t)p.n_cand;
   a.groups = p.adaptive ? (uint32_t)p.H : 1u;
@@ -1529,15 +1642,16 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
   const long long blocks = (long long)m.chunks * p.segments;
   if (blocks > 0x7fffffffLL || p.segments > 0x7fffffff) return hipErrorInvalidConfiguration;
   // the global histograms start cleared (by a kernel, not a memset, so
-  // the call can be captured in a graph); each pick clears what it read
+  // the call can be captured in a graph); stage 1's finish clears them for
+  // stage 2
   const dim3 gc((unsigned)blocks), gp(p.segments);
   const int stages = p.two_stage ? 2 : 1;
   // 16-byte loads when every chunk starts 16-byte aligned and is a
   // multiple of 4 long (scores and weights are 16-byte aligned)
   const bool vec = p.n_cand % 4 == 0;
+  hipLaunchKernelGGL(k_msel_init, gp, dim3(kMThreads), 0, st, a);
   for (int stg = 0; stg < stages; ++stg) {
     const int stage2 = stg == 1 ? 1 : 0, final = stg + 1 == stages ? 1 : 0;
-    hipLaunchKernelGGL(k_msel_init, gp, dim3(kMThreads), 0, st, a, stage2);
     if (stg == 0 && pool_first) {
       const bool pvec = vec && p.in_stride % 4 == 0;
       hipError_t e;
@@ -1548,24 +1662,13 @@ static hipError_t msel_launch(const SelectPlan& p, const float* scores, const fl
         default: e = launch_msel_pool<3>(a, scores, p.in_stride, p.pooled, pvec, gc, st); break;
       }
       if (e != hipSuccess) return e;
-    } else if (vec) {
-      hipLaunchKernelGGL((k_msel_hist<kMCopies, true>), gc, dim3(kMThreads), 0, st, a, stage2);
-    } else {
-      hipLaunchKernelGGL((k_msel_hist<kMCopies, false>), gc, dim3(kMThreads), 0, st, a, stage2);
-    }
-    hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
-    if (vec)
-      hipLaunchKernelGGL((k_msel_hist<1, true>), gc, dim3(kMThreads), 0, st, a, stage2);
-    else
-      hipLaunchKernelGGL((k_msel_hist<1, false>), gc, dim3(kMThreads), 0, st, a, stage2);
-    hipLaunchKernelGGL(k_msel_pick, gp, dim3(kMThreads), 0, st, a);
-    if (vec)
-      hipLaunchKernelGGL(k_msel_filter<true>, gc, dim3(kMThreads), 0, st, a, stage2, final);
-    else
-      hipLaunchKernelGGL(k_msel_filter<false>, gc, dim3(kMThreads), 0, st, a, stage2, final);
+    } else if (stg == 0) {
+      launch_msel_passes<0>(vec, false, gc, st, a, 0);
+    }   // stage 2's round 0 comes with stage 1's filter and finish
+    launch_msel_passes<1>(vec, stage2 != 0, gc, st, a, 0);
+    launch_msel_passes<2>(vec, stage2 != 0, gc, st, a, final, p.two_stage && stg == 0);
     hipLaunchKernelGGL(k_msel_finish, gp, dim3(kMThreads), 0, st, a, stage2, final);
   }
-  hipLaunchKernelGGL(k_msel_offsets, gp, dim3(kMThreads), 0, st, a);
   hipLaunchKernelGGL(k_msel_emit, gc, dim3(kMThreads), 0, st, a, p.two_stage ? 1 : 0);
   return hipGetLastError();
 }

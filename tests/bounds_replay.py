@@ -194,7 +194,7 @@ def decode_sizes(L, H, G, kept, offs):
 # -------------------------------------------------------------- selection ----
 
 SEL_THREADS, M_THREADS, K_CHUNK, K_BINS, K_MAX_GROUPS = 1024, 512, 16384, 2048, 1024
-K_MASK_WORDS, K_LIST_CAP = K_CHUNK // 32, 1024
+K_MASK_WORDS, K_LIST_CAP, K_SLOTS, K_HIST_BUFS = K_CHUNK // 32, 1024, 3, 3
 
 
 def _clamp_budget(b, W, n):
@@ -263,28 +263,29 @@ def digit_width(shift):
 
 
 def msel_accesses(p, states, ccount, rng, budgets=None, lists=None):
-    """k_msel_init, k_msel_hist, k_msel_pick, k_msel_filter, k_msel_finish,
-    k_msel_offsets and k_msel_emit (select.hip) with arbitrary segment
-    states (shift, need, done, count), per-chunk counts and list entries.
-    Where a membership test decides a rank, each thread's member count is
-    drawn at random within its 32 candidates."""
+    """k_msel_init, k_msel_hist0, k_msel_hist1, k_msel_filter,
+    k_msel_finish and k_msel_emit (select.hip) with arbitrary segment
+    states (count), per-chunk counts and list entries. Where a membership
+    test decides a rank, each thread's member count is drawn at random
+    within its 32 candidates."""
     acc = Accesses()
     S, chunks, W = p["segments"], p["chunks"], p["W"]
     for seg in range(S):
         st = states[seg]
         sp = seg_span(p, seg, budgets)
         acc.add("budgets", sp["reads"])
-        acc.add("states", [seg])
-        acc.add("ghist", seg * K_BINS + np.arange(K_BINS))       # k_msel_init clears
-        # k_msel_hist / k_msel_pick: the digit's bins, whatever the shift
-        nb = 1 << digit_width(int(st["shift"]))
-        acc.add("ghist", seg * K_BINS + np.arange(nb))
-        tid = np.arange(M_THREADS)[:, None]
-        b = nb - 1 - 8 * tid - np.arange(8)[None, :]
-        acc.add("ghist", seg * K_BINS + b[b >= 0])
+        acc.add("states", [slot * S + seg for slot in range(K_SLOTS)])
+        # init clears the three histograms (stage 1's round 0, round 1,
+        # stage 2's round 0), stage 1's finish round 1's; the passes add to
+        # bins masked to K_BINS - 1; the picks read thread t's four bins
+        # K_BINS - 4 - 4t .. K_BINS - 1 - 4t
+        for rnd in range(K_HIST_BUFS):
+            acc.add("ghist", (rnd * S + seg) * K_BINS + np.arange(K_BINS))
+            t = np.arange(M_THREADS)
+            acc.add("ghist", (rnd * S + seg) * K_BINS + (K_BINS - 4 - 4 * t)[:, None] + np.arange(4))
         for c in range(chunks):
             g, begin, end = msel_chunk(p, c)
-            # k_msel_hist / k_msel_filter loads: f < end
+            # hist0 / hist1 / filter loads: f < end
             if end > begin:
                 acc.add("scores", seg * p["seg_len"] + np.array([begin, end - 1]))
                 if p["two_stage"]:
@@ -317,21 +318,29 @@ def msel_accesses(p, states, ccount, rng, budgets=None, lists=None):
         ch = seg * chunks + g * p["cpg"] + pos // K_CHUNK
         acc.add("ccount", ch)
         acc.add("mask", ch * K_MASK_WORDS + (pos % K_CHUNK) // 32)
-        # k_msel_offsets: scans of arbitrary counts (uint32), group starts
+        # k_msel_emit, per chunk: rank0 = the (arbitrary, uint32) counts of
+        # the segment's earlier chunks; its members (set bits of its
+        # K_MASK_WORDS words: at most K_CHUNK) staged by rank in LDS take
+        # slots rank0 + g*W + i, i < count; a group's last chunk writes the
+        # window at rank0 + count + g*W + t, t < W; head offsets
         cc = _u32(ccount[seg])
-        memoff = _u32(np.concatenate([[0], np.cumsum(cc)[:-1]]))
-        acc.add("ccount", seg * chunks + np.arange(chunks))
-        gidx = np.arange(chunks)[np.arange(chunks) % p["cpg"] == 0] // p["cpg"]
-        assert gidx.max(initial=0) < K_MAX_GROUPS
-        gstart = memoff[np.arange(chunks) % p["cpg"] == 0]
-        for g in range(p["groups"]):
-            end_rank = int(gstart[g + 1]) if g + 1 < p["groups"] else int(sp["k"])
-            e = end_rank + (g + 1) * W
-            o = e - W + np.arange(W, dtype=np.int64)
-            o = o[(o >= 0) & (o < sp["room"])]
-            acc.add("idx", sp["base"] + o)
-            if p["adaptive"] and budgets is None:
-                acc.add("head_offsets", [seg * (p["groups"] + 1) + g])
+        for c in range(chunks):
+            g, begin, end = msel_chunk(p, c)
+            acc.add("ccount", seg * chunks + np.arange(c + 1))
+            rank0 = int(_u32(cc[:c].sum()))
+            count = int(rng.integers(0, K_CHUNK + 1))
+            assert count <= K_MASK_WORDS * 32 == K_CHUNK
+            o = rank0 + g * W + np.arange(count, dtype=np.int64)
+            acc.add("idx", sp["base"] + o[o < sp["room"]])
+            if c - g * p["cpg"] + 1 == p["cpg"]:
+                o = rank0 + count + g * W + np.arange(W, dtype=np.int64)
+                acc.add("idx", sp["base"] + o[(o >= 0) & (o < sp["room"])])
+            if budgets is None and p["adaptive"]:
+                if c - g * p["cpg"] == 0:
+                    acc.add("head_offsets", [seg * (p["groups"] + 1) + g])
+                if c == 0:
+                    acc.add("head_offsets", [seg * (p["groups"] + 1) + p["groups"]])
+        assert (np.arange(chunks) // p["cpg"]).max(initial=0) < K_MAX_GROUPS
         if budgets is not None:
             H = p["H"]
             l, h = divmod(seg, H)
@@ -339,18 +348,6 @@ def msel_accesses(p, states, ccount, rng, budgets=None, lists=None):
             if h + 1 == H:
                 acc.add("head_offsets", [l * (H + 1) + H])
                 acc.add("idx", l * p["stride"] + np.arange(sp["end"], p["stride"], dtype=np.int64))
-        elif p["adaptive"]:
-            acc.add("head_offsets", [seg * (p["groups"] + 1) + p["groups"]])
-        # k_msel_emit: the chunk's members (set bits of its K_MASK_WORDS
-        # words: at most K_CHUNK) are staged by rank in LDS and take slots
-        # rank0 + g*W + i, i < count, with rank0 the chunk's (arbitrary)
-        # member offset
-        for c in range(chunks):
-            g, begin, end = msel_chunk(p, c)
-            count = int(rng.integers(0, K_CHUNK + 1))
-            assert count <= K_MASK_WORDS * 32 == K_CHUNK
-            o = int(_u32(ccount[seg][c])) + g * W + np.arange(count, dtype=np.int64)
-            acc.add("idx", sp["base"] + o[o < sp["room"]])
     return acc
 
 
@@ -374,7 +371,7 @@ def msel_pool_accesses(p, in_stride):
 
 def select_sizes(p):
     s = {"scores": p["segments"] * p["seg_len"], "budgets": p["L"] * p["H"],
-         "states": p["segments"], "ghist": p["segments"] * K_BINS,
+         "states": K_SLOTS * p["segments"], "ghist": K_HIST_BUFS * p["segments"] * K_BINS,
          "ccount": p["segments"] * p.get("chunks", 0),
          "list": p["segments"] * K_LIST_CAP,
          "mask": p["segments"] * p.get("chunks", 0) * K_MASK_WORDS}
