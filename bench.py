@@ -429,6 +429,7 @@ def main():
             "select" if not wl.anchor_k else "anchor_select": stats(span(2, 3)),
             "compact" if not wl.anchor_k else "anchor_assign_k": stats(span(3, 4))},
         "scored_selected_entries_per_s": entries / ((ms_score + ms_sel) * 1e-3),
+        "score_source_sha": sha,   # the scoring kernels' sources (SCORE_SOURCES) this line ran on
         "wall_s_timed": wall,
         "timing": ("each step between HIP events on the stream it runs on; a 1 GiB buffer "
                    "overwritten before every step, outside its events" if flush_buf is not None
