@@ -122,17 +122,23 @@ def compact_sizes(L, H, n, vecs, kept, offs):
 
 # -------------------------------------------------------------- k_decode ----
 
-DEC_CHUNK, DEC_REC, HEAD_DIM = 256, 128 + 2, 128
+DEC_REC, HEAD_DIM = 128 + 2, 128
 
 
-def decode_items(H, kept, ragged):
+def dec_chunk(G):
+    """dec_chunk: rows per work item (k_decode_stream for G <= 4, else
+    k_decode_phased)."""
+    return 512 if G <= 4 else 256
+
+
+def decode_items(H, kept, ragged, chunk):
     if ragged:
-        return -(-kept // DEC_CHUNK) + H
+        return -(-kept // chunk) + H
     b = kept // H
-    return H * (-(-b // DEC_CHUNK))
+    return H * (-(-b // chunk))
 
 
-def _dec_prefix(offs, l, H, kept, acc):
+def _dec_prefix(offs, l, H, kept, acc, DEC_CHUNK):
     """dec_prefix: effective offsets (clamped into [0, kept], then the
     running maximum) and the per-head work-item prefix."""
     h = np.arange(H + 1, dtype=np.int64)
@@ -149,15 +155,18 @@ def _dec_prefix(offs, l, H, kept, acc):
 
 
 def decode_accesses(L, H, G, kept, offs):
-    """k_decode (one item of <= 256 kept rows of one head per workgroup) and
-    k_decode_merge (one query head per workgroup), decode.hip. offs: int32
-    [L*(H+1)] (arbitrary) or None (uniform, kept % H == 0)."""
+    """k_decode_stream / k_decode_phased (one item of <= dec_chunk(G) kept
+    rows of one head per workgroup; every row of the item is read, rows past
+    its end clamped to its last) and k_decode_merge (one query head per
+    workgroup), decode.hip. offs: int32 [L*(H+1)] (arbitrary) or None
+    (uniform, kept % H == 0)."""
     acc = Accesses()
     ragged = offs is not None
-    items = decode_items(H, kept, ragged)
+    DEC_CHUNK = dec_chunk(G)
+    items = decode_items(H, kept, ragged, DEC_CHUNK)
     rec = G * DEC_REC
     for l in range(L):
-        eo, pre = _dec_prefix(offs, l, H, kept, acc)
+        eo, pre = _dec_prefix(offs, l, H, kept, acc, DEC_CHUNK)
         its = np.arange(items, dtype=np.int64)
         its = its[its < pre[H]]                    # the others return at once
         if its.size:
@@ -185,7 +194,7 @@ def decode_accesses(L, H, G, kept, offs):
 
 def decode_sizes(L, H, G, kept, offs):
     s = {"kv_rows": L * kept, "q": L * H * G * HEAD_DIM, "out": L * H * G * HEAD_DIM,
-         "part": L * decode_items(H, kept, offs is not None) * G * DEC_REC}
+         "part": L * decode_items(H, kept, offs is not None, dec_chunk(G)) * G * DEC_REC}
     if offs is not None:
         s["offs"] = L * (H + 1)
     return s
