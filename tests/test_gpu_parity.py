@@ -171,7 +171,7 @@ SELECT_CASES = [
     (1, 16, 30, 4, 0.5, True, True, 0.5, 3),              # the same, two-stage
     (1, 1, 50000, 32, 0.1, False, False, 0.5, 1000),      # longer than LDS: many workgroups
     (1, 2, 40000, 32, 0.1, True, True, 0.5, 100000),      # many workgroups, two-stage, adaptive
-    # segments over the LDS size run on many workgroups (chunks of 8192)
+    # segments over the LDS size run on many workgroups (chunks of 16,384)
     (2, 8, 9032, 32, 0.2, True, False, 0.5, 50),          # adaptive, 8 heads, ties
     (1, 3, 20000, 0, 0.3, True, False, 0.5, 5),           # adaptive, no window, heavy ties
     (1, 1, 36000, 16, 1.0, False, False, 0.5, 3),         # keep everything
@@ -184,6 +184,12 @@ SELECT_CASES = [
     # many workgroups with n - W not a multiple of 4 (4-byte loads)
     (1, 1, 40001, 0, 0.2, False, False, 0.5, 100),
     (1, 3, 15001, 3, 0.3, True, True, 0.5, 30),
+    # many workgroups on near-continuous scores: the bucket after two digits
+    # goes to the short list (the tie-heavy cases above outgrow it)
+    (1, 8, 9032, 32, 0.2, True, True, 0.5, 1000000),     # adaptive two-stage, 8 heads
+    (2, 2, 50000, 32, 0.1, False, True, 0.5, 1000000),   # per head, two-stage
+    (1, 1, 40000, 32, 0.00083, False, False, 0.5, 1000000),   # k = 1
+    (1, 1, 40000, 32, 0.99998, False, False, 0.5, 1000000),   # k = n - W - 1
 ]
 
 
@@ -338,6 +344,8 @@ BUDGET_CASES = [
     (1, 4, 50000, 32, False, 0.5, 1000, 0),     # longer than LDS: many workgroups per head
     (1, 2, 40000, 16, True, 0.5, 100, 3),       # many workgroups, two-stage
     (2, 4, 600, 8, False, 0.5, 5, -40),         # rows shorter than layer 0's budgets: truncated
+    (2, 4, 40000, 8, False, 0.5, 1000000, -40), # the same on many workgroups
+    (1, 3, 36000, 32, True, 0.5, 1000000, 2),   # many workgroups, two-stage, short lists
 ]
 
 
