@@ -281,7 +281,10 @@ int32_t kvsel_select(const float* scores, const float* weight,
  * as kvsel_select selects. With a per-head budget (adaptive == 0),
  * pool <= 7, n a multiple of 4 and n-W <= 34,816, each head's raw row is
  * read once and pooled on chip: the pooled scores need not pass through
- * memory. Otherwise the call pools into `pooled`, or its workspace, first.
+ * memory. Otherwise the pooled scores go to `pooled`, or the workspace:
+ * written by the selection's first pass over the raw rows when the
+ * segments are longer than 34,816 candidates and pool <= 7, else by a
+ * pooling pass before the selection.
  *
  *   raw     f32 [L][H_kv][n]      kvsel_score's raw output (window keys
  *                                 included; they are not pooled)
