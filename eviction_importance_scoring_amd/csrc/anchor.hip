@@ -35,6 +35,21 @@ constexpr int kAsBlock = kAsWaves * 64;    // vectors per workgroup
 using AsLoader = RingLoader<kAsWaves>;
 constexpr int kAsLoads = AsLoader::kLoads;
 
+// max of three floats, a quiet NaN operand ignored (IEEE-mode v_max3_f32);
+// as asm so that no canonicalising max is put before each operand.
+__device__ __forceinline__ float max3_nan_skip(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// a.lo * a'.lo + a.hi * a'.hi + c over bf16 pairs, in fp32
+typedef __bf16 bf16x2_a __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float bf16_dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_a, a), __builtin_bit_cast(bf16x2_a, b), c,
+                                         false);
+}
+
 int anchor_kpad(int k) { return (k + gTile - 1) / gTile * gTile; }
 
 // A slot's score is <x, a> * scale. The scale is 1/|a|, or NaN for a zero
@@ -113,9 +128,24 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign(const __bf16* __restri
   for (int t = 0; t < gSlots - 1; ++t) issue(min(t, ntiles - 1), t);
 
   const bool any_key = key0 < n;
-  // best <x, a> / |a| per vector so far, and its slot (gamma = best / |a|)
+  // packed scores as in k_anchor_assign_res: <x, a> / |a| + cx, the low 4
+  // bits replaced by 15 - (accumulator row); best packed value per vector
+  // and its 32-slot half-tile
   float best[2] = {neg_inf(), neg_inf()};
-  int bslot[2] = {0, 0};
+  int bu[2] = {0, 0};
+  float cx[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const u32x4 w = __builtin_bit_cast(u32x4, vop[nt][s8]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = bf16_dot2(w[e], w[e], ss);
+    }
+    ss += __shfl_xor(ss, 32);   // the other half row
+    cx[nt] = __builtin_sqrtf(ss) + 0x1p-100f;
+  }
 
   auto begin_tile = [&](int t) -> const unsigned char* {
     gen_wait_tile<kAsLoads>(t, ntiles);
@@ -140,42 +170,54 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign(const __bf16* __restri
       if (st + 1 < 8) read_step(slot, col, hf, st + 1, a[(st + 1) & 1]);
       tile_step(a[st & 1], vop, st, acc);
     }
-    // anchor rows of this lane, in increasing slot order; rows 4j..4j+3 of
-    // an accumulator are consecutive slots (one 16-byte read each)
+    // half-tile mt of tile t: rows 4j..4j+3 of an accumulator are
+    // consecutive slots (one 16-byte read of their scales)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      float mx[2] = {neg_inf(), neg_inf()};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int s0 = t * gTile + mt * 32 + acc_row(4 * j, lane);
-        const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rinv[s0]);
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(&rinv[t * gTile + mt * 32 + acc_row(4 * j, lane)]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int nt = 0; nt < 2; ++nt) {
+          float p[4];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const float sc = acc[mt][nt][4 * j + u] * r4[u];
-            if (sc > best[nt]) {
-              best[nt] = sc;
-              bslot[nt] = s0 + u;
-            }
+          for (int e = 0; e < 4; ++e) {
+            const float sc = __builtin_fmaf(acc[mt][nt][4 * j + e], r4[e], cx[nt]);
+            p[e] = __uint_as_float((__float_as_uint(sc) & ~15u) | (uint32_t)(15 - (4 * j + e)));
           }
+          mx[nt] = max3_nan_skip(mx[nt], p[0], p[1]);
+          mx[nt] = max3_nan_skip(mx[nt], p[2], p[3]);
+        }
       }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        if (mx[nt] > best[nt]) {
+          best[nt] = mx[nt];
+          bu[nt] = 2 * t + mt;
+        }
+    }
   }
   gen_wait<0>();
+  if (!any_key) return;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
+    const bool found = best[nt] > neg_inf();
+    const int i = 15 - (int)(__float_as_uint(best[nt]) & 15u);
+    int bslot = found ? bu[nt] * 32 + 8 * (i >> 2) + 4 * hf + (i & 3) : 0;
     // the other lane half holds the other 16 anchor rows of every block
     const float ob = __shfl_xor(best[nt], 32);
-    const int os = __shfl_xor(bslot[nt], 32);
-    if (ob > best[nt] || (ob == best[nt] && os < bslot[nt])) {
+    const int os = __shfl_xor(bslot, 32);
+    if (ob > best[nt] || (ob == best[nt] && os < bslot)) {
       best[nt] = ob;
-      bslot[nt] = os;
+      bslot = os;
     }
     const int key = key0 + nt * 32 + col;
     if (hf == 0 && key < n) {
       // <x, a> / <a, a> = (<x, a> / |a|) / |a|; no valid anchor: 0
-      const float g = best[nt] * rinv[bslot[nt]];
-      slot_out[lh * n + key] = bslot[nt];
-      gamma_out[lh * n + key] = best[nt] > neg_inf() ? g : 0.f;
+      const float sc = __uint_as_float(__float_as_uint(best[nt]) & ~15u) - cx[nt];
+      slot_out[lh * n + key] = bslot;
+      gamma_out[lh * n + key] = best[nt] > neg_inf() ? sc * rinv[bslot] : 0.f;
     }
   }
 }
@@ -236,29 +278,44 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
   auto half_op = [&](int u, int st) -> bf16x8 {
     return gen_op(abuf[u >> 1], (u & 1) * 32 + col, hf, st);
   };
-  float best[2];
-  int bslot[2];
-  int bcode[2];   // 8j + e of this half-tile's best row so far, -1 if none
+  // Scores are compared as packed values: the score plus an offset c >= |x|
+  // (so the value is not negative), with its low 4 mantissa bits replaced by
+  // 15 - i for the lane's accumulator row i of the half-tile. Among equal
+  // scores the lower slot (lower i) then holds the larger value, a half-tile
+  // needs one max per two pairs instead of a compare and two selects per
+  // pair, and half-tiles are visited in increasing order with a strict
+  // compare. The truncated bits move a score by less than 2^-19 of 2|x|.
+  float best[2];   // best packed value so far
+  int bu[2];       // its half-tile
+  float mx[2];     // packed maximum of the current half-tile
+  float cx[2];     // offset: |x| (plus 2^-100, so a zero vector's values stay normal)
   // the four scales of rows 4j..4j+3 of half-tile u (consecutive slots)
   auto scales = [&](int u, int j) -> f32x4 {
     return *reinterpret_cast<const f32x4*>(&rinv[u * 32 + acc_row(4 * j, lane)]);
   };
-  // part c of the argmax of half-tile u: slots 32u + 8j + 4hf + e (e < 4),
-  // j = c / 2, of vector set c % 2 (slots rise with j for each set)
+  // part c of the argmax of half-tile u: rows i = 4j + e (e < 4) of vector
+  // set c % 2, j = c / 2; row i is slot 32u + 8j + 4hf + e
   auto arg_part = [&](int u, const f32x16 (&acc)[2], int c, const f32x4& r4) {
     const int j = c >> 1, nt = c & 1;
-    if (j == 0) bcode[nt] = -1;
+    float p[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float sc = acc[nt][4 * j + e] * r4[e];
-      if (sc > best[nt]) {
-        best[nt] = sc;
-        bcode[nt] = 8 * j + e;
-      }
+      const float sc = __builtin_fmaf(acc[nt][4 * j + e], r4[e], cx[nt]);
+      p[e] = __uint_as_float((__float_as_uint(sc) & ~15u) | (uint32_t)(15 - (4 * j + e)));
     }
-    if (j == 3 && bcode[nt] >= 0) bslot[nt] = u * 32 + 4 * hf + bcode[nt];
+    if (j == 0) mx[nt] = neg_inf();
+    mx[nt] = max3_nan_skip(mx[nt], p[0], p[1]);
+    mx[nt] = max3_nan_skip(mx[nt], p[2], p[3]);
+    if (j == 3 && mx[nt] > best[nt]) {
+      best[nt] = mx[nt];
+      bu[nt] = u;
+    }
   };
   // MFMAs of half-tile u into cur, argmax of half-tile u-1 from prev
+  // The scales of the argmax are read one part ahead: r4n holds those of
+  // the next part, across half-tiles too (part 0 of half-tile u is read
+  // during the last part of half-tile u-1's argmax).
+  f32x4 r4n;
   auto half = [&](int u, f32x16 (&cur)[2], const f32x16 (&prev)[2]) {
     bf16x8 op[2];
     f32x4 r4;
@@ -269,7 +326,10 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
         cur[nt] = mfma32(op[st & 1], vcur[nt][st], st == 0 ? zero16() : cur[nt]);
-      if ((st & 1) == 0) r4 = scales(u - 1, st >> 1);   // shared by both vector sets
+      if ((st & 1) == 0) {   // shared by both vector sets
+        r4 = r4n;
+        r4n = st < 6 ? scales(u - 1, (st >> 1) + 1) : scales(u, 0);
+      }
       arg_part(u - 1, prev, st, r4);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -279,8 +339,20 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
     if (b + 1 < b1) load_vecs(b + 1, vnext);   // in flight during this block
     const int key0 = b * kAsBlock + wave * 64;
     best[0] = best[1] = neg_inf();
-    bslot[0] = bslot[1] = 0;
+    bu[0] = bu[1] = 0;
     if (key0 < n) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float ss = 0.f;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const u32x4 w = __builtin_bit_cast(u32x4, vcur[nt][s8]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = bf16_dot2(w[e], w[e], ss);
+        }
+        ss += __shfl_xor(ss, 32);   // the other half row
+        cx[nt] = __builtin_sqrtf(ss) + 0x1p-100f;
+      }
       f32x16 A[2], B[2];
       {
         bf16x8 op[2];
@@ -292,6 +364,7 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
           for (int nt = 0; nt < 2; ++nt)
             A[nt] = mfma32(op[st & 1], vcur[nt][st], st == 0 ? zero16() : A[nt]);
         }
+        r4n = scales(0, 0);
       }
       int u = 1;
       for (; u + 1 < nh; u += 2) {
@@ -307,17 +380,22 @@ __global__ __launch_bounds__(256, 2) void k_anchor_assign_res(const __bf16* __re
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
+        const bool found = best[nt] > neg_inf();
+        const int i = 15 - (int)(__float_as_uint(best[nt]) & 15u);
+        int bslot = found ? bu[nt] * 32 + 8 * (i >> 2) + 4 * hf + (i & 3) : 0;
+        // the other lane half holds the other 16 rows of every half-tile
         const float ob = __shfl_xor(best[nt], 32);
-        const int os = __shfl_xor(bslot[nt], 32);
-        if (ob > best[nt] || (ob == best[nt] && os < bslot[nt])) {
+        const int os = __shfl_xor(bslot, 32);
+        if (ob > best[nt] || (ob == best[nt] && os < bslot)) {
           best[nt] = ob;
-          bslot[nt] = os;
+          bslot = os;
         }
         const int key = key0 + nt * 32 + col;
         if (hf == 0 && key < n) {
-          const float g = best[nt] * rinv[bslot[nt]];
-          slot_out[lh * n + key] = bslot[nt];
-          gamma_out[lh * n + key] = best[nt] > neg_inf() ? g : 0.f;
+          // <x, a> / <a, a> = (<x, a> / |a|) / |a|; no valid anchor: 0
+          const float sc = __uint_as_float(__float_as_uint(best[nt]) & ~15u) - cx[nt];
+          slot_out[lh * n + key] = bslot;
+          gamma_out[lh * n + key] = best[nt] > neg_inf() ? sc * rinv[bslot] : 0.f;
         }
       }
     }

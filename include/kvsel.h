@@ -435,8 +435,12 @@ int32_t kvsel_anchor_select(const float* scores, const float* rand,
  * Equal cosines go to the lower slot; an anchor of zero norm is never
  * chosen; an anchor position is its own slot with gamma = 1. Call once for
  * the keys (the page projects pre-RoPE keys) and once for the values.
- * Dot products are fp32 sums of exact bf16 products, so two anchors whose
- * cosines agree to ~1e-6 may be chosen either way.
+ * Dot products are fp32 sums of exact bf16 products. Scores <x, a>/|a| are
+ * compared after adding |x| (so none is negative) with their last 4
+ * mantissa bits replaced by a code of the slot's row, which makes equal
+ * scores go to the lower slot; two anchors whose cosines agree to within
+ * ~4e-6 may therefore be chosen either way, and gamma carries a relative
+ * error below 4e-6 of |x|/|a|.
  *
  *   x       bf16 [L][H_kv][n][d]
  *   anchors i32  [L][H_kv][k]    positions (kvsel_anchor_select)

@@ -528,6 +528,7 @@ ANCHOR_ASSIGN_CASES = [
     (1, 2, 300, 300),        # every position an anchor
     (1, 1, 777, 1),
     (1, 1, 2100, 130),       # three tiles, ragged vectors
+    (1, 2, 3000, 400),       # more than 256 anchors: the anchor rows stream through the ring
 ]
 
 
