@@ -423,11 +423,14 @@ def main():
                         {"score": ms_score, **({"value_weight": ms_vw} if wl.value_weight else {}),
                          **({"head_score+head_budgets": ms_vw} if keep else {}),
                          "select": ms_sel, "compact": ms_cmp}),
-        "per_call_ms_stats": {
+        "per_call_ms_stats": ({
+            "step": stats(per_step), "score": stats(span(0, 1)),
+            "anchor_select": stats(span(1, 2)), "anchor_assign_k": stats(span(2, 3)),
+            "anchor_assign_v": stats(span(3, 4))} if wl.anchor_k else {
             "step": stats(per_step), "score": stats(span(0, 1)),
             **({"value_weight": stats(span(1, 2))} if wl.value_weight else {}),
-            "select" if not wl.anchor_k else "anchor_select": stats(span(2, 3)),
-            "compact" if not wl.anchor_k else "anchor_assign_k": stats(span(3, 4))},
+            **({"head_score+head_budgets": stats(span(1, 2))} if keep else {}),
+            "select": stats(span(2, 3)), "compact": stats(span(3, 4))}),
         "scored_selected_entries_per_s": entries / ((ms_score + ms_sel) * 1e-3),
         "score_source_sha": sha,   # the scoring kernels' sources (SCORE_SOURCES) this line ran on
         "wall_s_timed": wall,
