@@ -410,3 +410,59 @@ def select_plan(L, H, n, W, budget=0, adaptive=False, two_stage=False, budgets=N
     p["cpg"] = -(-n_cand // K_CHUNK)
     p["chunks"] = groups * p["cpg"]
     return p
+
+
+# ------------------------------------------------------------- anchors ----
+
+AS_TILE, RES_ANCHORS, RES_BLOCKS, AS_BLOCK, MAX_ANCHOR_PAD = 64, 256, 16, 256, 2048
+
+
+def anchor_kpad(k):
+    return (k + AS_TILE - 1) // AS_TILE * AS_TILE
+
+
+def anchor_accesses(L, H, n, k, anchors):
+    """k_anchor_gather, k_anchor_assign_res / k_anchor_assign (the slot a
+    packed score decodes to, for every half-tile, row code and lane half)
+    and k_anchor_self of anchor.hip, with arbitrary anchor positions.
+    Buffers: x [L*H*n] rows, anchors [L*H*k], arows [L*H*kpad] rows,
+    rinv [L*H*kpad], slot and gamma [L*H*n], and the kernels' LDS tables
+    rinv_lds (kResAnchors or kMaxAnchorPad entries)."""
+    acc = Accesses()
+    kpad = anchor_kpad(k)
+    LH = L * H
+    a = np.asarray(anchors, np.int64).reshape(LH, k)
+    lh = np.arange(LH)[:, None]
+    # k_anchor_gather: grid (kpad, L*H); slot s < k reads anchors and, when
+    # the position is inside the head, its row of x; every slot writes its
+    # row of arows and its rinv entry
+    acc.add("anchors", lh * k + np.arange(k)[None, :])
+    valid = (a >= 0) & (a < n)
+    acc.add("x", (lh * n + a)[valid])
+    acc.add("arows", lh * kpad + np.arange(kpad)[None, :])
+    acc.add("rinv", lh * kpad + np.arange(kpad)[None, :])
+    # assignment: vectors of every key block (reads of x guarded by key < n),
+    # the per-slot table copied to LDS, and the decoded slot of every
+    # (half-tile bu, row code, lane half) read back from that table
+    keys = np.arange(n)
+    acc.add("x", (lh * n + keys[None, :]).ravel())
+    table = RES_ANCHORS if kpad <= RES_ANCHORS else MAX_ANCHOR_PAD
+    acc.add("rinv", lh * kpad + np.arange(kpad)[None, :])
+    acc.add("rinv_lds", np.arange(kpad))
+    nh = kpad // 32
+    bu, code, hf = np.meshgrid(np.arange(nh), np.arange(16), np.arange(2), indexing="ij")
+    i = 15 - code
+    slot = bu * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)
+    acc.add("rinv_lds", slot)                 # gamma's scale of the chosen slot
+    # the argmax's scale reads: rows 4j..4j+3 of every half-tile
+    j, e = np.meshgrid(np.arange(4), np.arange(4), indexing="ij")
+    rows = (np.arange(nh)[:, None, None, None] * 32 + 8 * j[None, None] + 4 * np.arange(2)[None, :, None, None]
+            + e[None, None])
+    acc.add("rinv_lds", rows)
+    acc.add("slot", (lh * n + keys[None, :]).ravel())
+    acc.add("gamma", (lh * n + keys[None, :]).ravel())
+    # k_anchor_self: positions inside the head write their slot and gamma
+    acc.add("slot", (lh * n + a)[valid])
+    acc.add("gamma", (lh * n + a)[valid])
+    return acc, {"x": LH * n, "anchors": LH * k, "arows": LH * kpad, "rinv": LH * kpad,
+                 "slot": LH * n, "gamma": LH * n, "rinv_lds": table}

@@ -147,3 +147,19 @@ def test_select_pool_first_pass_stays_in_bounds(seed, adaptive):
     p = _valid_uniform_plan(rng, adaptive, bool(seed % 2), True)
     acc = br.msel_pool_accesses(p, p["n"])
     acc.check({"raw": p["L"] * p["H"] * p["n"], "pooled": p["segments"] * p["seg_len"]})
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_anchor_assign_stays_in_bounds(seed):
+    """Arbitrary anchor positions (outside the head, negative, repeated) and
+    every slot a packed score can decode to stay inside the buffers and the
+    kernels' LDS tables, for anchor counts on both sides of the resident
+    kernel's limit."""
+    rng = np.random.default_rng(seed)
+    L, H = 1, int(rng.integers(1, 4))
+    n = int(rng.integers(1, 3000))
+    k = int(rng.choice([1, 7, 64, 200, 256, 257, 400, min(2048, n)]))
+    k = max(1, min(k, n))
+    anchors = _arbitrary_i32(rng, L * H * k, n)
+    acc, sizes = br.anchor_accesses(L, H, n, k, anchors)
+    acc.check(sizes)
