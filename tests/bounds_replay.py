@@ -1,5 +1,5 @@
 """Host replay of the global-memory index arithmetic of the selection,
-compaction and decoding kernels.
+compaction, decoding and AnchorKV kernels.
 
 Each function below re-states, for every workgroup and thread of a launch,
 the address expressions of one kernel of the HIP library (the kernel named

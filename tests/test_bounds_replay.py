@@ -1,5 +1,5 @@
-"""Every global read and write of the selection, compaction and decoding
-kernels stays inside the buffers the library was given, for arbitrary
+"""Every global read and write of the selection, compaction, decoding and
+AnchorKV kernels stays inside the buffers the library was given, for arbitrary
 contents of the integer buffers those kernels trust (index lists, head
 offsets, budget vectors, the many-workgroup select's segment states and
 chunk counts). The kernels' index arithmetic is replayed on the host
