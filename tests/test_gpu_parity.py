@@ -580,6 +580,38 @@ def test_anchor_assign(case):
                 assert not (s == 3).any() and not (s == 2).any()   # duplicate and zero anchors
 
 
+@pytest.mark.parametrize("k", [8, 300], ids=["resident", "ring"])
+def test_anchor_assign_negative_ties(k):
+    """Vectors whose every cosine is negative, with the least negative one
+    shared by three copies of one anchor (slots 1, 3 and k-2: same lane,
+    other lane half or tile): the lower slot wins the exact tie, as the
+    oracle reads equal cosines."""
+    rng = np.random.default_rng(1000 + k)
+    n, d = 900, 128
+    e0 = np.zeros(d, np.float32)
+    e0[0] = 1.0
+    anchors = np.sort(rng.choice(n, k, replace=False)).astype(np.int32)
+    x = (-5.0 * e0 + 0.02 * rng.standard_normal((n, d))).astype(np.float32)
+    a = (rng.uniform(2.0, 3.0, (k, 1)) * e0 + 0.3 * rng.standard_normal((k, d))).astype(np.float32)
+    a[1] = 0.2 * e0 + 0.3 * rng.standard_normal(d)
+    a[3] = a[1]
+    a[k - 2] = a[1]
+    x[anchors] = a
+    xb = synth.bf16_bits(x[None, None])
+    print(f"[gpu] kvsel_anchor_assign negative ties k={k}", flush=True)
+    slot, gamma = kv.kvsel_anchor_assign(to_dev(xb), torch.from_numpy(anchors[None, None]).cuda())
+    torch.cuda.synchronize()
+    slot = slot.cpu().numpy()[0, 0]
+    xf = synth.bf16_to_f64(xb)[0, 0]
+    A = xf[anchors]
+    cos = (xf @ A.T) / (np.linalg.norm(xf, axis=1)[:, None] * np.linalg.norm(A, axis=1)[None, :])
+    j = np.setdiff1d(np.arange(n), anchors)
+    others = np.delete(cos[j], [1, 3, k - 2], axis=1).max(axis=1)
+    tied = (cos[j, 1] < 0) & (cos[j, 1] - others > 1e-5)
+    assert tied.sum() > n // 2, "the construction should give most vectors a negative tied best"
+    np.testing.assert_array_equal(slot[j][tied], 1)
+
+
 SIGNED_CASES = [
     # (L, H, n, W, frac, adaptive, two_stage)
     (1, 3, 2000, 0, 0.3, False, False),
