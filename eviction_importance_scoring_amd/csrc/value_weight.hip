@@ -8,16 +8,16 @@
 // per-key |.| sums in registers and never written ([CriticalKV] §D.4 notes
 // the full V W^O would be ~7.8 GB per layer at 7B / 128K).
 //
-// Tiling (the LDS ring of kvsel_ring.h, 4 waves, two workgroups per CU): a
-// workgroup owns 256 keys of one (layer, KV head); each wave holds the
-// values of 64 keys (two MFMA
-// N tiles) in registers for the whole kernel. The A operand, W_O^(h,g), is
+// Tiling (the LDS ring of kvsel_ring.h, 4 waves, three workgroups per CU):
+// a workgroup owns 256 keys of one (layer, KV head); each wave holds the
+// values of 64 keys (two MFMA N tiles) in registers for the whole kernel. The A operand, W_O^(h,g), is
 // streamed in 64-row tiles (64 of the D output features, 128 columns each,
 // rows H_q*d elements apart in the [D][H_q*d] matrix) through the ring, for
 // every g: G * ceil(D/64) tiles. Workgroups of one (layer, head) run on one XCD, so
-// the 4 MB slice they all stream stays in that XCD's L2. Software
-// pipelined: the MFMAs of tile t run beside the |.| folding of tile t-1.
-// Every key's sum is accumulated in one lane in a fixed order:
+// the 4 MB slice they all stream stays in that XCD's L2. Each tile's MFMAs
+// run first and its |.| fold after them; a wave's vector work does not run
+// beside its own MFMAs, so the other workgroups' waves keep the matrix unit
+// busy meanwhile. Every key's sum is accumulated in one lane in a fixed order:
 // deterministic, no atomics.
 #include "kvsel_internal.h"
 #include "kvsel_kernels.h"
@@ -25,8 +25,8 @@
 
 namespace kvsel {
 
-// Two 4-wave workgroups per CU: each workgroup's tile barriers do not
-// stall the other's waves.
+// Three 4-wave workgroups per CU: each workgroup's tile barriers do not
+// stall the others' waves.
 constexpr int vWaves = 4;
 constexpr int vBlock = vWaves * 64;                    // keys per workgroup
 using VLoader = RingLoader<vWaves>;
